@@ -1,0 +1,148 @@
+"""Seeded synthetic layers and calibration activations.
+
+Shared by the tests, the benchmark and the oracle's callers: it only draws
+random numbers and rounds them to the storage dtype; it holds none of the
+quantization method's arithmetic.
+
+Every array is reproducible from (seed, layer id, stream id, chunk id) via
+numpy.random.default_rng; large arrays are drawn in row chunks on a thread
+pool.  bf16 values are the round-to-nearest-even bf16 of the fp32 draws
+(torch's CPU cast), returned as fp32 numpy arrays holding exactly those
+values (and, where needed, as torch.bfloat16 tensors).
+
+Workload recipes (weights W [d_out, d_in], activations X [tokens, d_in]):
+  small      W fp32 ~ N(0, 0.02^2), 4 distinct random input columns x20;
+             X fp32 rows z * s, z ~ N(0, 1), per-channel s ~ LogNormal(0, 1).
+  attn_proj  W bf16 ~ N(0, 0.02^2) with 0.1% of entries replaced by
+             0.02 * Student-t(3); X bf16 rows z * s with 8 random channels of
+             s multiplied by 100 (massive activations).
+  mlp        W bf16 ~ N(0, 0.015^2); X as small, in bf16.
+  sparse     W bf16 ~ N(0, 0.01^2) with 0.05% Student-t(3) outliers;
+             X bf16 = |z| * Bernoulli(0.4) * s (60% exact zeros).
+"""
+
+from concurrent.futures import ThreadPoolExecutor
+import os
+
+import numpy as np
+
+SEED = 0
+_CHUNK = 8192
+
+LAYERS = {"small": 1, "attn_proj": 2, "mlp": 3, "sparse": 4, "moe": 5}
+
+
+def rng(layer, stream, chunk=None):
+    key = [SEED, LAYERS.get(layer, layer) if isinstance(layer, str) else layer, stream]
+    if chunk is not None:
+        key.append(chunk)
+    return np.random.default_rng(key)
+
+
+def to_bf16_values(x):
+    """fp32 array -> fp32 array holding the RNE bf16 rounding of each value."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16).float().numpy()
+
+
+def to_bf16_tensor(x):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+
+
+def _threads():
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def channel_scales(layer, k, massive=0):
+    r = rng(layer, 10)
+    s = r.lognormal(0.0, 1.0, size=k).astype(np.float64)
+    if massive:
+        idx = r.choice(k, size=massive, replace=False)
+        s[idx] *= 100.0
+    return s
+
+
+def _x_chunk(layer, c, rows, k, s, kind):
+    r = rng(layer, 11, c)
+    z = r.standard_normal((rows, k), dtype=np.float32)
+    if kind == "sparse":
+        keep = r.random((rows, k), dtype=np.float32) < 0.4
+        z = np.abs(z) * keep
+    return (z * s.astype(np.float32)[None, :]).astype(np.float32)
+
+
+def activations(layer, n, k, massive=0, kind="dense", bf16=True, out=None):
+    """X [n, k] drawn chunk by chunk (chunk c of 8192 rows uses rng(layer, 11, c)).
+
+    Returns an fp32 numpy array (bf16-rounded values when bf16=True).  If out
+    is given (a torch.bfloat16 CPU tensor [n, k]) the bf16 values are written
+    there instead and out is returned.
+    """
+    s = channel_scales(layer, k, massive)
+    nchunks = (n + _CHUNK - 1) // _CHUNK
+    res = None if out is not None else np.empty((n, k), dtype=np.float32)
+
+    def work(c):
+        r0 = c * _CHUNK
+        rows = min(_CHUNK, n - r0)
+        x = _x_chunk(layer, c, rows, k, s, kind)
+        if out is not None:
+            out[r0:r0 + rows] = to_bf16_tensor(x)
+        else:
+            res[r0:r0 + rows] = to_bf16_values(x) if bf16 else x
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(work, range(nchunks)))
+    return out if out is not None else res
+
+
+def weights(layer, m, k, std, outlier_frac=0.0, outlier_cols=0, bf16=True):
+    """W [m, k]: N(0, std^2); optional Student-t(3) outliers and x20 input columns."""
+    r = rng(layer, 20)
+    W = (r.standard_normal((m, k)) * std).astype(np.float64)
+    if outlier_frac:
+        cnt = int(round(outlier_frac * m * k))
+        flat = r.choice(m * k, size=cnt, replace=False)
+        W.reshape(-1)[flat] = std * r.standard_t(3, size=cnt)
+    if outlier_cols:
+        cols = r.choice(k, size=outlier_cols, replace=False)
+        W[:, cols] *= 20.0
+    W = W.astype(np.float32)
+    return to_bf16_values(W) if bf16 else W
+
+
+# ---- named workloads ---------------------------------------------------------
+
+def small_layer(m=256, k=256, n=2048):
+    """Single linear layer, fp32: the oracle-sized case (8 candidates per block)."""
+    W = weights("small", m, k, 0.02, outlier_cols=4, bf16=False)
+    X = activations("small", n, k, bf16=False)
+    return W, X
+
+
+def attn_proj_layer(m=4096, k=4096, n=262144, x_out=None):
+    """Attention-projection-shaped layer, bf16, 16 candidates per block.
+
+    Full size: 4096 x 4096 weights, 262,144 tokens (128 sequences x 2048).
+    Smaller m, k, n give the same recipe at test sizes.
+    """
+    W = weights("attn_proj", m, k, 0.02, outlier_frac=0.001)
+    X = activations("attn_proj", n, k, massive=min(8, k), out=x_out)
+    return W, X
+
+
+def mlp_layer(m, k, n):
+    W = weights("mlp", m, k, 0.015)
+    X = activations("mlp", n, k)
+    return W, X
+
+
+def sparse_layer(m, k, n):
+    W = weights("sparse", m, k, 0.01, outlier_frac=0.0005)
+    X = activations("sparse", n, k, kind="sparse")
+    return W, X

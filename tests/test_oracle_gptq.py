@@ -1,0 +1,274 @@
+"""Pins of the oracle's GPTQ + Schur Replay sweep against mathematics, not itself.
+
+P2  U = I, one candidate: plain round-to-nearest with the absmax scale, checked
+    against an independent RTN built on torch's E4M3 cast and brute-force
+    nearest search; diagonal H with K candidates: brute-force minimum of the
+    H-weighted block error.
+P3  sum_j e_j^2 = dW (H + lam I) dW^T per row (GPTQ's loss identity).
+P4  Schur Replay's per-candidate score equals the increase of the damped
+    least-squares loss once the later columns are re-optimized
+    (numpy.linalg.lstsq on the stacked [X; sqrt(lam) I]), for every row,
+    block and candidate of small layers; the value each column holds when it
+    is quantized equals the least-squares optimum given the committed prefix.
+P5  U^T U = (H + lam I)^-1, U upper with positive diagonal, and U equals the
+    inverse of the index-reversed Cholesky factor (scipy).
+P6  invariances: row permutation, W -> -W, (W, g) -> 2^s (W, g), H -> 4 H.
+P7  H = X^T X against an explicit token loop; E_r = ||X dW_r^T||^2.
+"""
+
+import numpy as np
+import pytest
+import scipy.linalg
+import torch
+
+from oracle import codec, gptq
+
+
+def _layer(m, k, n, seed, outliers=True):
+    r = np.random.default_rng(seed)
+    W = r.normal(0, 0.02, size=(m, k)).astype(np.float32)
+    if outliers:
+        W[:, r.choice(k, 2, replace=False)] *= 20
+    s = r.lognormal(0, 1, size=k)
+    X = (r.normal(size=(n, k)) * s).astype(np.float32)
+    return W, X
+
+
+# ---------------------------------------------------------------- P2
+def _rtn_independent(W, g):
+    """Round-to-nearest NVFP4 with the absmax block scale, built from torch's E4M3 cast."""
+    W64 = W.astype(np.float64)
+    m, k = W.shape
+    blocks = W64.reshape(m, k // 16, 16)
+    amax = np.abs(blocks).max(axis=2)
+    ratio = torch.from_numpy(amax / (6.0 * float(g)))
+    sc = ratio.clamp(max=448.0).to(torch.float8_e4m3fn).view(torch.uint8).numpy().astype(np.int64)
+    sc = np.maximum(sc, 1)   # a non-zero block never uses the zero scale
+    sc = np.where(amax == 0, 0, sc)
+    S = codec.e4m3_decode(sc)[..., None] * float(g)
+    mags = codec.E2M1_MAG
+    dist = np.abs(np.abs(blocks)[..., None] - mags * S[..., None])   # exact for fp32 inputs
+    best = np.argmin(dist, axis=-1)
+    dmin = dist.min(axis=-1, keepdims=True)
+    ties = (dist == dmin)
+    # tie -> even index: choose the even one among tied neighbours
+    even_tie = ties & (np.arange(8) % 2 == 0)
+    has_even = even_tie.any(axis=-1)
+    best = np.where(has_even & (ties.sum(-1) > 1), np.argmax(even_tie, axis=-1), best)
+    sign = ((blocks < 0) & (best > 0)).astype(np.int64)
+    codes = (sign << 3 | best).reshape(m, k)
+    return codes.astype(np.uint8), sc.astype(np.uint8)
+
+
+def test_identity_hessian_one_candidate_is_rtn():
+    W, _ = _layer(32, 256, 8, seed=10)
+    W[3, 16:32] = 0.0                       # an all-zero block
+    g = codec.global_scale(W)
+    res = gptq.sweep(W, np.eye(256), g, 1)
+    codes, sc = _rtn_independent(W, g)
+    assert np.array_equal(res["scales"], sc)
+    assert np.array_equal(res["codes"], codes)
+
+
+def test_diagonal_hessian_picks_min_weighted_block_error():
+    W, _ = _layer(16, 64, 8, seed=11)
+    r = np.random.default_rng(12)
+    h = r.lognormal(0, 1, size=64)
+    H = np.diag(h)
+    U, lam = gptq.hinv_factor(H)
+    g = codec.global_scale(W)
+    K = 8
+    res = gptq.sweep(W, U, g, K)
+    assert np.allclose(U, np.diag(np.diag(U)))
+    for row in range(16):
+        for b in range(4):
+            w = W[row, 16 * b:16 * b + 16].astype(np.float64)
+            hb = h[16 * b:16 * b + 16] + lam
+            cands = gptq.candidate_codes(np.array([np.abs(w).max()]), g, K)[0]
+            errs = []
+            for c in cands:
+                q = codec.dequant_exact(codec.e2m1_encode(w, codec.e4m3_decode(c), g), c, g)
+                errs.append(np.sum(hb * (w - q) ** 2))
+            assert res["scales"][row, b] == cands[int(np.argmin(errs))]
+
+
+# ---------------------------------------------------------------- P3
+def test_loss_identity_sum_e2_equals_damped_quadratic_form():
+    W, X = _layer(24, 128, 512, seed=13)
+    H = gptq.hessian(X)
+    U, lam = gptq.hinv_factor(H)
+    g = codec.global_scale(W)
+    res = gptq.sweep(W, U, g, 8)
+    sc = np.repeat(res["scales"], 16, axis=1)
+    deq = codec.dequant_exact(res["codes"], sc, g)
+    dW = W.astype(np.float64) - deq
+    Hd = H + lam * np.eye(128)
+    quad = np.einsum("rk,kl,rl->r", dW, Hd, dW)
+    assert np.allclose(res["score"], quad, rtol=1e-9, atol=0)
+    assert np.allclose((res["err"] ** 2).sum(1), quad, rtol=1e-9)
+
+
+# ---------------------------------------------------------------- P4
+def _lsq_min(A, b):
+    x, *_ = np.linalg.lstsq(A, b, rcond=None)
+    r = b - A @ x
+    return float(r @ r), x
+
+
+@pytest.mark.parametrize("seed,K", [(14, 4), (15, 8)])
+def test_replay_score_is_compensated_block_error_bruteforce(seed, K):
+    m, k, n = 6, 64, 96
+    W, X = _layer(m, k, n, seed=seed)
+    H = gptq.hessian(X)
+    U, lam = gptq.hinv_factor(H)
+    g = codec.global_scale(W)
+    res = gptq.sweep(W, U, g, K, trace=True)
+    Xt = np.vstack([X.astype(np.float64), np.sqrt(lam) * np.eye(k)])
+    sc = np.repeat(res["scales"], 16, axis=1)
+    deq = codec.dequant_exact(res["codes"], sc, g)
+    for row in range(m):
+        w = W[row].astype(np.float64)
+        y = Xt @ w
+        for b in range(k // 16):
+            c0, c1 = 16 * b, 16 * b + 16
+            qP = deq[row, :c0]
+            base = y - Xt[:, :c0] @ qP
+            L_prefix, vF = _lsq_min(Xt[:, c0:], base)
+            # the committed block's inputs are the continuous optimum given the prefix
+            assert np.allclose(res["vdec"][row, c0], vF[0], rtol=1e-7, atol=1e-12)
+            scores = []
+            for ci in range(K):
+                c = res["cand"][row, b, ci]
+                qb = codec.dequant_exact(res["cand_codes"][row, b, ci], c, g)
+                rhs = base - Xt[:, c0:c1] @ qb
+                if c1 < k:
+                    L_c, _ = _lsq_min(Xt[:, c1:], rhs)
+                else:
+                    L_c = float(rhs @ rhs)
+                scores.append(L_c - L_prefix)
+            scores = np.array(scores)
+            rep = res["cand_score"][row, b]
+            assert np.allclose(rep, scores, rtol=1e-7, atol=1e-9 * abs(L_prefix)), (row, b)
+            assert int(np.argmin(rep)) == int(np.argmin(scores))
+
+
+def test_in_block_rounding_follows_gptq_state():
+    """Each committed column value equals the least-squares optimum given all earlier q."""
+    m, k, n = 4, 32, 80
+    W, X = _layer(m, k, n, seed=16)
+    H = gptq.hessian(X)
+    U, lam = gptq.hinv_factor(H)
+    g = codec.global_scale(W)
+    res = gptq.sweep(W, U, g, 4, trace=True)
+    Xt = np.vstack([X.astype(np.float64), np.sqrt(lam) * np.eye(k)])
+    sc = np.repeat(res["scales"], 16, axis=1)
+    deq = codec.dequant_exact(res["codes"], sc, g)
+    for row in range(m):
+        y = Xt @ W[row].astype(np.float64)
+        for j in range(k):
+            _, v = _lsq_min(Xt[:, j:], y - Xt[:, :j] @ deq[row, :j])
+            assert np.isclose(res["vdec"][row, j], v[0], rtol=1e-7, atol=1e-12), (row, j)
+
+
+# ---------------------------------------------------------------- P5
+def test_factor_identities():
+    _, X = _layer(4, 96, 300, seed=17)
+    H = gptq.hessian(X)
+    U, lam = gptq.hinv_factor(H)
+    Hd = H + lam * np.eye(96)
+    assert lam == pytest.approx(0.01 * np.mean(np.diag(H)), rel=1e-15)
+    assert np.allclose(np.tril(U, -1), 0)
+    assert np.all(np.diag(U) > 0)
+    assert np.allclose(U.T @ U, np.linalg.inv(Hd), rtol=1e-9, atol=1e-12 * np.abs(np.linalg.inv(Hd)).max())
+    J = np.eye(96)[::-1]
+    L = scipy.linalg.cholesky(J @ Hd @ J, lower=True)
+    U2 = scipy.linalg.solve_triangular(J @ L @ J, np.eye(96), lower=False)
+    assert np.allclose(U, U2, rtol=1e-8, atol=1e-12 * np.abs(U).max())
+
+
+def test_factor_rejects_non_pd():
+    H = np.zeros((16, 16))
+    with pytest.raises(np.linalg.LinAlgError):
+        gptq.hinv_factor(H)
+
+
+# ---------------------------------------------------------------- P6
+def test_invariances():
+    W, X = _layer(12, 64, 200, seed=18)
+    H = gptq.hessian(X)
+    U, lam = gptq.hinv_factor(H)
+    g = codec.global_scale(W)
+    base = gptq.sweep(W, U, g, 8)
+    perm = np.random.default_rng(19).permutation(12)
+    p = gptq.sweep(W[perm], U, g, 8)
+    assert np.array_equal(p["codes"], base["codes"][perm])
+    assert np.array_equal(p["scales"], base["scales"][perm])
+    neg = gptq.sweep(-W, U, g, 8)
+    assert np.array_equal(neg["scales"], base["scales"])
+    flip = np.where((base["codes"] & 7) > 0, base["codes"] ^ 8, base["codes"])
+    assert np.array_equal(neg["codes"], flip)
+    s = gptq.sweep(W * 8, U, np.float32(g * 8), 8)
+    assert np.array_equal(s["codes"], base["codes"]) and np.array_equal(s["scales"], base["scales"])
+    U4, lam4 = gptq.hinv_factor(4 * H)
+    assert lam4 == 4 * lam
+    h4 = gptq.sweep(W, U4, g, 8)
+    assert np.array_equal(h4["codes"], base["codes"]) and np.array_equal(h4["scales"], base["scales"])
+    assert np.allclose(h4["score"], 4 * base["score"], rtol=1e-12)
+
+
+# ---------------------------------------------------------------- P7
+def test_hessian_explicit_token_loop():
+    r = np.random.default_rng(20)
+    X = r.normal(size=(7, 5))
+    H = gptq.hessian(X, chunk=3)
+    for i in range(5):
+        for j in range(5):
+            acc = 0.0
+            for t in range(7):
+                acc += X[t, i] * X[t, j]
+            assert H[i, j] == pytest.approx(acc, rel=1e-14, abs=1e-14)
+
+
+def test_weighted_error_equals_output_error():
+    W, X = _layer(8, 64, 128, seed=21)
+    H = gptq.hessian(X)
+    U, _ = gptq.hinv_factor(H)
+    g = codec.global_scale(W)
+    res = gptq.sweep(W, U, g, 8)
+    deq = codec.dequantize(codec.pack_codes(res["codes"]), res["scales"], g)
+    E = gptq.weighted_error(W, deq, H)
+    dW = W.astype(np.float64) - deq.astype(np.float64)
+    out = ((X.astype(np.float64) @ dW.T) ** 2).sum(0)
+    assert np.allclose(E, out, rtol=1e-10)
+
+
+def test_candidate_window_edges():
+    g = np.float32(1.0)
+    c = gptq.candidate_codes(np.array([0.0, 1e-9, 1e9, 6.0]), g, 16)
+    assert list(c[0]) == list(range(1, 17))
+    assert list(c[1]) == list(range(1, 17))
+    assert list(c[2]) == list(range(111, 127))
+    # 6/(6*1) = 1.0 -> code 0x38; window [0x30, 0x3F]
+    assert c[3, 0] == 0x38 - 8 and c[3, -1] == 0x38 + 7
+    c1 = gptq.candidate_codes(np.array([6.0]), g, 1)
+    assert list(c1[0]) == [0x38]
+
+
+def test_gptq_beats_rtn_on_correlated_inputs():
+    W, X = _layer(32, 128, 256, seed=22)
+    r = gptq.quantize_layer(W, X, n_cand=8)
+    g = r["g"]
+    rt = gptq.rtn(W, g, 1)
+    deq = codec.dequantize(codec.pack_codes(rt["codes"]), rt["scales"], g)
+    assert r["row_err"].sum() < gptq.weighted_error(W, deq, r["H"]).sum()
+
+
+def test_fp32_mode_matches_fp64_decisions_on_small_layer():
+    W, X = _layer(32, 128, 512, seed=23)
+    H = gptq.hessian(X)
+    U, _ = gptq.hinv_factor(H)
+    g = codec.global_scale(W)
+    a = gptq.sweep(W, U, g, 8)
+    b = gptq.sweep(W, U, g, 8, dtype=np.float32)
+    assert np.mean(a["codes"] != b["codes"]) <= 1e-3
+    assert np.mean(a["scales"] != b["scales"]) <= 1e-3
