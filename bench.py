@@ -1,0 +1,201 @@
+"""Throughput of NVFP4 GPTQ + Schur Replay layer quantization on one MI355X.
+
+One step = the whole per-layer path on inputs already resident in HBM:
+  H = X^T X (bf16 MFMA)  ->  U with (H + lam I)^-1 = U^T U  ->  global scale
+  ->  GPTQ sweep with Schur Replay (16 candidates per block, lazy batches of
+  128 columns with an fp32 MFMA trailing update)  ->  weighted error
+  tr(dW H dW^T)  ->  dequantized export.
+Workload: attention-projection-shaped layer, W bf16 4096 x 4096, X bf16
+262,144 tokens x 4096 (synthetic, seeded).  Metric: quantized weights per
+second (Mparam/s) including the Hessian.
+
+Prints one JSON line (see the keys below).
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+M, K_IN, N_TOK, N_CAND = 4096, 4096, 262144, 16
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline():
+    """Oracle (NumPy fp64) on a bounded sample of the same workload, scaled to Mparam/s.
+
+    Sample: Hessian over 8,192 of the 262,144 tokens (time scaled x32), the full
+    4096 x 4096 factorization, the sweep + weighted error of 16 of the 4096 rows
+    (time scaled x256).  Layer time = sum of the scaled stage times.
+    """
+    import numpy as np
+    import synth
+    from oracle import codec, gptq
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    W = synth.weights("attn_proj", M, K_IN, 0.02, outlier_frac=0.001)
+    n_s = 8192
+    X = synth.activations("attn_proj", n_s, K_IN, massive=8)
+    t0 = time.perf_counter()
+    H_s = gptq.hessian(X)
+    t_h = (time.perf_counter() - t0) * (N_TOK / n_s)
+    t0 = time.perf_counter()
+    U, lam = gptq.hinv_factor(H_s)
+    t_f = time.perf_counter() - t0
+    rows = 16
+    g = codec.global_scale(W)
+    t0 = time.perf_counter()
+    res = gptq.sweep(W[:rows], U, g, N_CAND)
+    deq = codec.dequantize(codec.pack_codes(res["codes"]), res["scales"], g)
+    gptq.weighted_error(W[:rows], deq, H_s)
+    t_s = (time.perf_counter() - t0) * (M / rows)
+    total = t_h + t_f + t_s
+    return {"value": M * K_IN / total / 1e6, "unit": "Mparam/s", "cores": cores, "kind": "oracle",
+            "sample": f"hessian on {n_s} of {N_TOK} tokens (x{N_TOK // n_s}), full {K_IN}x{K_IN} factor, "
+                      f"sweep+error on {rows} of {M} rows (x{M // rows}); stage seconds "
+                      f"H={t_h:.1f} factor={t_f:.1f} sweep={t_s:.1f}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the per-layer path is a single-GPU workload here "
+              "(rows of W shard across ranks with no exchange; see DESIGN.md). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import post_nvfp4_weight_amd as nvq
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("generating inputs")
+    W = synth.weights("attn_proj", M, K_IN, 0.02, outlier_frac=0.001)
+    Wd = synth.to_bf16_tensor(W).to(dev)
+    Xh = torch.empty(N_TOK, K_IN, dtype=torch.bfloat16, pin_memory=True)
+    synth.activations("attn_proj", N_TOK, K_IN, massive=8, out=Xh)
+    t0 = time.perf_counter()
+    Xd = Xh.to(dev, non_blocking=True)
+    torch.cuda.synchronize()
+    h2d_s = time.perf_counter() - t0
+    del Xh
+    log(f"inputs resident (H2D {h2d_s:.3f} s)")
+
+    lib = nvq.lib
+    stream = nvq._stream
+    P = nvq._ptr
+    H = torch.empty(K_IN, K_IN, dtype=torch.float32, device=dev)
+    U = torch.empty_like(H)
+    lam = torch.empty(1, dtype=torch.float32, device=dev)
+    info = torch.empty(1, dtype=torch.int32, device=dev)
+    g = torch.empty(1, dtype=torch.float32, device=dev)
+    codes = torch.empty(M, K_IN // 2, dtype=torch.uint8, device=dev)
+    scales = torch.empty(M, K_IN // 16, dtype=torch.uint8, device=dev)
+    row_err = torch.empty(M, dtype=torch.float32, device=dev)
+    row_loss = torch.empty(M, dtype=torch.float32, device=dev)
+    deq = torch.empty(M, K_IN, dtype=torch.bfloat16, device=dev)
+    ws_h_n = lib.hessian_workspace_size(N_TOK, K_IN, nvq.NVQ_DTYPE_BF16)
+    ws_f_n = lib.factor_hinv_workspace_size(K_IN)
+    ws_g_n = lib.nvfp4_global_scale_workspace_size(M, K_IN)
+    ws_q_n = lib.gptq_nvfp4_workspace_size(M, K_IN, 0)
+    ws = {n: torch.empty(max(1, b), dtype=torch.uint8, device=dev)
+          for n, b in [("h", ws_h_n), ("f", ws_f_n), ("g", ws_g_n), ("q", ws_q_n)]}
+
+    def chk(name, rc):
+        if rc != 0:
+            raise RuntimeError(f"{name}: {lib.nvq_last_error().decode()}")
+
+    stages = ["hessian", "factor", "gscale", "quantize", "dequant"]
+
+    def step(ev=None):
+        s = stream()
+        if ev: ev[0].record()
+        H.zero_()
+        chk("hessian", lib.hessian_accumulate(P(Xd), nvq.NVQ_DTYPE_BF16, N_TOK, K_IN, K_IN, P(H), P(ws["h"]),
+                                              ws_h_n, s))
+        if ev: ev[1].record()
+        chk("factor", lib.factor_hinv(P(H), K_IN, 0.01, P(U), P(lam), P(info), P(ws["f"]), ws_f_n, s))
+        if ev: ev[2].record()
+        chk("gscale", lib.nvfp4_global_scale(P(Wd), nvq.NVQ_DTYPE_BF16, M, K_IN, K_IN, P(g), P(ws["g"]), ws_g_n, s))
+        if ev: ev[3].record()
+        chk("quantize", lib.gptq_nvfp4_quantize(P(Wd), nvq.NVQ_DTYPE_BF16, M, K_IN, K_IN, P(U), P(H), P(g), N_CAND,
+                                                0, P(codes), P(scales), P(row_err), P(row_loss), P(ws["q"]),
+                                                ws_q_n, s))
+        if ev: ev[4].record()
+        chk("dequant", lib.nvfp4_dequantize(P(codes), P(scales), P(g), M, K_IN, P(deq), nvq.NVQ_DTYPE_BF16, s))
+        if ev: ev[5].record()
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert int(info.item()) == 0, "factorization failed"
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    per_stage = {st: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps for j, st in enumerate(stages)}
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = M * K_IN / (ms_per_step / 1e3) / 1e6
+
+    # The Hessian contraction dominates: algorithmic flops n*k*(k+1) per call.
+    t_h = per_stage["hessian"] / 1e3
+    flops = N_TOK * K_IN * (K_IN + 1)
+    achieved = flops / t_h / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
+
+    # Standalone RTN encode + pack of the same W (the no-update codec path).
+    rtn_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    rtn_ev[0].record()
+    reps = 10
+    for _ in range(reps):
+        chk("rtn", lib.gptq_nvfp4_quantize(P(Wd), nvq.NVQ_DTYPE_BF16, M, K_IN, K_IN, None, None, P(g), 1,
+                                           nvq.FLAG_RTN | nvq.FLAG_NO_ERR, P(codes), P(scales), None, None,
+                                           P(ws["q"]), ws_q_n, stream()))
+    rtn_ev[1].record()
+    torch.cuda.synchronize()
+    rtn_ms = rtn_ev[0].elapsed_time(rtn_ev[1]) / reps
+
+    out = {
+        "metric": "quantized weights/sec (Mparam/s) per layer incl. Hessian",
+        "value": round(value, 1), "unit": "Mparam/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16-mfma/fp32", "data": "synthetic",
+        "config": {"workload": "attention-projection layer W 4096x4096 bf16, X 262144x4096 bf16, 16 scale "
+                               "candidates per 16-block, lazy batch 128",
+                   "d_out": M, "d_in": K_IN, "tokens": N_TOK, "n_cand": N_CAND},
+        "roofline": roofline,
+        "stages_ms": {k: round(v, 3) for k, v in per_stage.items()},
+        "rtn_encode_ms": round(rtn_ms, 4),
+        "h2d_inputs_s": round(h2d_s, 3),
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline")
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

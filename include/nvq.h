@@ -1,0 +1,191 @@
+/*
+ * nvq.h -- C ABI of the NVFP4 GPTQ / Schur Replay weight quantizer for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Method: "Replay the Curvature: Accurate and Scalable NVFP4 Quantization for
+ * Large Language Model Inference" (arXiv 2609.36654), Abstract.  Given a
+ * linear layer's weights W [m x k] (m output rows, k input columns) and
+ * calibration activations X [n x k], the library returns NVFP4 weights --
+ * E2M1 element codes with one E4M3 scale per 16 consecutive weights of a row
+ * -- chosen by a GPTQ column sweep in which each block's scale is selected by
+ * Schur Replay, plus the layer's weighted reconstruction error.
+ *
+ * Conventions shared by every call:
+ *   - Matrices are row-major; leading dimensions (ld*) count elements.
+ *   - Pointers named as device pointers must be device memory of the current
+ *     HIP device; "stream" is a hipStream_t passed as void* (NULL = default
+ *     stream).  Every compute call is asynchronous on that stream: it only
+ *     enqueues kernels, never allocates, frees or synchronizes, and keeps no
+ *     pointer after returning.  Buffers must stay valid until the stream has
+ *     run the work.
+ *   - Callers own every buffer, including workspaces sized by the matching
+ *     *_workspace_size query.  Workspaces must be 256-byte aligned.
+ *   - Return value: NVQ_OK (0) on success, a negative NVQ_ERR_* code when the
+ *     arguments are rejected on the host (nothing is enqueued then), or
+ *     NVQ_ERR_HIP when the HIP runtime reports a launch error.  The reason of
+ *     the last failure on the calling thread is given by nvq_last_error().
+ *   - Calls on different streams may run concurrently when their output and
+ *     workspace buffers do not overlap.
+ */
+#ifndef NVQ_H
+#define NVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------- */
+#define NVQ_OK                 0
+#define NVQ_ERR_NULL          -1  /* a required pointer is NULL                 */
+#define NVQ_ERR_SHAPE         -2  /* a size or leading dimension is invalid     */
+#define NVQ_ERR_DTYPE         -3  /* unsupported dtype code                     */
+#define NVQ_ERR_NCAND         -4  /* candidate count outside [1, 16]            */
+#define NVQ_ERR_WORKSPACE     -5  /* workspace too small or misaligned          */
+#define NVQ_ERR_VALUE         -6  /* a scalar argument is out of range          */
+#define NVQ_ERR_HIP           -7  /* the HIP runtime reported an error          */
+#define NVQ_ERR_ALIGN         -8  /* a pointer is not aligned as required       */
+
+/* ---- element types of W, X and dequantized outputs ------------------------ */
+#define NVQ_DTYPE_F32  0
+#define NVQ_DTYPE_BF16 1
+
+/* ---- flags of gptq_nvfp4_quantize ------------------------------------------ */
+/* Round to nearest without GPTQ updates: U is not read; each block's scale is
+ * the candidate with the least plain squared error (the absmax scale when
+ * n_cand = 1). */
+#define NVQ_FLAG_RTN    1u
+/* Do not compute the weighted error (row_err is not written; H may be NULL). */
+#define NVQ_FLAG_NO_ERR 2u
+
+/*
+ * hessian_accumulate -- second-order state of the layer ("Replay the
+ * Curvature", Abstract: the second-order state of GPTQ), H += X^T X.
+ *
+ *   X      device, [n x ldx] row-major, element type x_dtype (NVQ_DTYPE_BF16
+ *          or NVQ_DTYPE_F32); only the first k columns are read.  bf16 rows
+ *          must start 8-byte aligned (ldx % 4 == 0), fp32 rows 16-byte
+ *          aligned (ldx % 4 == 0).
+ *   n      number of tokens (rows of X), n >= 0; n = 0 leaves H unchanged.
+ *   k      number of input channels, k > 0, k % 16 == 0.
+ *   H      device, fp32 [k x k] row-major.  On entry only the upper triangle
+ *          (j >= i) is read; on return H holds the full symmetric matrix
+ *          (old upper triangle + X^T X, mirrored into the lower triangle).
+ *          Products of bf16 inputs are exact in fp32; sums are fp32 in a
+ *          fixed order, so results are bitwise reproducible.
+ *   ws     device workspace of hessian_workspace_size(n, k, x_dtype) bytes.
+ * Streaming: calling it on consecutive token chunks accumulates into H, so
+ * calibration data can arrive in pieces (the caller tracks the token count).
+ */
+size_t hessian_workspace_size(int64_t n, int64_t k, int x_dtype);
+int hessian_accumulate(const void* X, int x_dtype, int64_t n, int64_t k, int64_t ldx,
+                       float* H, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * factor_hinv -- damped inverse factor used by the GPTQ sweep ("Replay the
+ * Curvature", Abstract: GPTQ, in which quantizing one column updates those
+ * that follow).
+ *
+ *   lambda = damp_rel * mean(diag H); U is the upper-triangular matrix with
+ *   positive diagonal such that (H + lambda I)^-1 = U^T U.
+ *
+ *   H          device fp32 [k x k], symmetric (only the upper triangle is read).
+ *   k          k > 0, k % 16 == 0.
+ *   damp_rel   relative damping, >= 0 and finite (0.01 is the usual value).
+ *   U          device fp32 [k x k] output; entries below the diagonal are set
+ *              to 0.  U must not overlap H.
+ *   lambda_out device, 1 float: lambda.
+ *   info       device, 1 int32: 0 on success; j > 0 if the trailing principal
+ *              submatrix of H + lambda I of order j is not positive definite
+ *              (U then holds no meaningful values).
+ *   ws         device workspace of factor_hinv_workspace_size(k) bytes.
+ * Computed in fp32: a blocked Cholesky factorization of the index-reversed
+ * damped matrix followed by a blocked triangular inverse.
+ */
+size_t factor_hinv_workspace_size(int64_t k);
+int factor_hinv(const float* H, int64_t k, float damp_rel, float* U, float* lambda_out,
+                int32_t* info, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * nvfp4_global_scale -- per-tensor fp32 scale applied on top of the E4M3 block
+ * scales: g = fl32(max|W| / 2688) (2688 = 6 * 448, the largest E2M1 magnitude
+ * times the largest finite E4M3 value), or g = 1 when W is all zero.
+ *
+ *   W      device [m x ldw], element type w_dtype; m, k > 0, ldw >= k.
+ *   g_out  device, 1 float.
+ *   ws     device workspace of nvfp4_global_scale_workspace_size(m, k) bytes.
+ */
+size_t nvfp4_global_scale_workspace_size(int64_t m, int64_t k);
+int nvfp4_global_scale(const void* W, int w_dtype, int64_t m, int64_t k, int64_t ldw,
+                       float* g_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * gptq_nvfp4_quantize -- NVFP4 quantization of W by a GPTQ column sweep with
+ * Schur Replay block-scale selection ("Replay the Curvature", Abstract: each
+ * 16-weight block's E4M3 scale is chosen by reproducing the GPTQ updates it
+ * causes inside the block and scoring the block error left after compensation
+ * from the still-unquantized columns).
+ *
+ * For each row and each 16-column block (natural column order):
+ *   a  = max |w'| over the block's current (updated) weights;
+ *   the candidates are the n_cand consecutive E4M3 codes centred on the code
+ *   nearest to a / (6 g), [c0 - n_cand/2, c0 + ceil(n_cand/2) - 1], shifted to
+ *   lie in [1, 126]; an all-zero block gets scale code 0 and +0 elements;
+ *   each candidate c is replayed: column by column, q_j = nearest E2M1 value
+ *   of w'_j under scale dec(c) * g (ties to even, clipped at 6),
+ *   e_j = (w'_j - q_j) / U_jj, later columns l of the block get
+ *   w'_l -= e_j U_jl; its score is sum_j e_j^2;
+ *   the least score wins (ties: the smaller scale); its codes are stored and
+ *   its errors update every later column of the row: w'_l -= sum_j e_j U_jl.
+ * Later columns receive the updates in lazy batches of 128 columns (an fp32
+ * MFMA GEMM per batch); all working values are fp32.
+ *
+ *   W        device [m x ldw], element type w_dtype (bf16 or fp32); not
+ *            modified.  m > 0, k > 0, k % 16 == 0, ldw >= k, ldw % 4 == 0.
+ *   U        device fp32 [k x k] from factor_hinv (read unless NVQ_FLAG_RTN).
+ *   H        device fp32 [k x k] symmetric (the undamped Hessian), read only
+ *            for the weighted error; may be NULL with NVQ_FLAG_NO_ERR.
+ *   g        device, 1 float: the per-tensor scale (e.g. nvfp4_global_scale).
+ *   n_cand   candidates per block, 1 <= n_cand <= 16.
+ *   codes    device uint8 [m x k/2] output: two E2M1 codes per byte, the even
+ *            column in the low nibble; code = sign << 3 | magnitude index
+ *            (magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6); zero is always +0.
+ *   scales   device uint8 [m x k/16] output: E4M3 (FN) block-scale codes.
+ *   row_err  device fp32 [m] output: E_r = dW_r H dW_r^T with
+ *            dW = W - dequantized W (not written with NVQ_FLAG_NO_ERR).
+ *   row_loss device fp32 [m] output or NULL: sum of the committed e_j^2 of
+ *            the row (the damped loss that the sweep minimizes); 0 for RTN.
+ *   ws       device workspace of gptq_nvfp4_workspace_size(m, k, flags) bytes.
+ */
+size_t gptq_nvfp4_workspace_size(int64_t m, int64_t k, unsigned flags);
+int gptq_nvfp4_quantize(const void* W, int w_dtype, int64_t m, int64_t k, int64_t ldw,
+                        const float* U, const float* H, const float* g, int n_cand,
+                        unsigned flags, uint8_t* codes, uint8_t* scales, float* row_err,
+                        float* row_loss, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * nvfp4_dequantize -- NVFP4 weights back to real values ("Replay the
+ * Curvature", Abstract: E2M1 elements sharing an E4M3 block scale):
+ * out = fl32(e2m1(code) * e4m3(scale) * g), one rounding of the exact product;
+ * for bf16 output that fp32 value is rounded to nearest-even bf16.
+ *
+ *   codes   device uint8 [m x k/2], layout as produced by gptq_nvfp4_quantize.
+ *   scales  device uint8 [m x k/16].
+ *   g       device, 1 float.
+ *   out     device [m x k] of out_dtype (NVQ_DTYPE_F32 or NVQ_DTYPE_BF16).
+ *   m >= 0, k > 0, k % 16 == 0.
+ */
+int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* g, int64_t m,
+                     int64_t k, void* out, int out_dtype, void* stream);
+
+/* Text of a status code; never NULL. */
+const char* nvq_status_string(int status);
+/* Reason of the most recent failing call on this thread ("" if none). */
+const char* nvq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* NVQ_H */

@@ -1,0 +1,182 @@
+"""NVFP4 weight quantization with GPTQ + Schur Replay on AMD Instinct MI355X.
+
+Thin ctypes binding over libnvq.so (C ABI in include/nvq.h).  Every step of
+the quantization runs in the library's HIP kernels; this module only checks
+tensor metadata, allocates outputs and workspaces with torch, and passes raw
+device pointers plus torch's current HIP stream.  There is no CPU fallback:
+importing fails if the library is missing.
+
+Method: "Replay the Curvature: Accurate and Scalable NVFP4 Quantization for
+Large Language Model Inference" (arXiv 2609.36654), Abstract.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnvq.so")
+
+NVQ_DTYPE_F32 = 0
+NVQ_DTYPE_BF16 = 1
+FLAG_RTN = 1
+FLAG_NO_ERR = 2
+
+EXPORTS = [
+    "hessian_workspace_size", "hessian_accumulate",
+    "factor_hinv_workspace_size", "factor_hinv",
+    "nvfp4_global_scale_workspace_size", "nvfp4_global_scale",
+    "gptq_nvfp4_workspace_size", "gptq_nvfp4_quantize",
+    "nvfp4_dequantize", "nvq_status_string", "nvq_last_error",
+]
+
+
+class NvqError(RuntimeError):
+    def __init__(self, fn, status, detail):
+        super().__init__(f"{fn} failed with status {status}: {detail}")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m post_nvfp4_weight_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I64, SZ, I32, F32, U32 = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int,
+                                 ctypes.c_float, ctypes.c_uint)
+    sig = {
+        "hessian_workspace_size": (SZ, [I64, I64, I32]),
+        "hessian_accumulate": (I32, [P, I32, I64, I64, I64, P, P, SZ, P]),
+        "factor_hinv_workspace_size": (SZ, [I64]),
+        "factor_hinv": (I32, [P, I64, F32, P, P, P, P, SZ, P]),
+        "nvfp4_global_scale_workspace_size": (SZ, [I64, I64]),
+        "nvfp4_global_scale": (I32, [P, I32, I64, I64, I64, P, P, SZ, P]),
+        "gptq_nvfp4_workspace_size": (SZ, [I64, I64, U32]),
+        "gptq_nvfp4_quantize": (I32, [P, I32, I64, I64, I64, P, P, P, I32, U32, P, P, P, P, P, SZ, P]),
+        "nvfp4_dequantize": (I32, [P, P, P, I64, I64, P, I32, P]),
+        "nvq_status_string": (ctypes.c_char_p, [I32]),
+        "nvq_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def _check(fn, status):
+    if status != 0:
+        raise NvqError(fn, status, lib.nvq_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return NVQ_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return NVQ_DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _workspace(nbytes, device):
+    if nbytes == 0:
+        return None
+    # torch's caching allocator returns 256-byte aligned blocks (checked by the library).
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def _rows(t, name):
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be a 2-D tensor with unit column stride")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a HIP device")
+    return t.shape[0], t.shape[1], t.stride(0)
+
+
+def hessian_accumulate(X, H=None, ws=None):
+    """H += X^T X (fp32 [k, k], full symmetric on return).  X: [n, k] bf16 or fp32."""
+    n, k, ldx = _rows(X, "X")
+    if H is None:
+        H = torch.zeros(k, k, dtype=torch.float32, device=X.device)
+    need = lib.hessian_workspace_size(n, k, _dtype_code(X))
+    if ws is None or ws.numel() < need:
+        ws = _workspace(need, X.device)
+    _check("hessian_accumulate", lib.hessian_accumulate(_ptr(X), _dtype_code(X), n, k, ldx, _ptr(H), _ptr(ws),
+                                                        need, _stream()))
+    return H
+
+
+def factor_hinv(H, damp_rel=0.01, U=None, ws=None):
+    """Returns (U, lam, info) as device tensors: (H + lam I)^-1 = U^T U, lam = damp_rel * mean(diag H)."""
+    k = H.shape[0]
+    U = torch.empty_like(H) if U is None else U
+    lam = torch.empty(1, dtype=torch.float32, device=H.device)
+    info = torch.empty(1, dtype=torch.int32, device=H.device)
+    need = lib.factor_hinv_workspace_size(k)
+    if ws is None or ws.numel() < need:
+        ws = _workspace(need, H.device)
+    _check("factor_hinv", lib.factor_hinv(_ptr(H), k, float(damp_rel), _ptr(U), _ptr(lam), _ptr(info), _ptr(ws),
+                                          need, _stream()))
+    return U, lam, info
+
+
+def nvfp4_global_scale(W):
+    """Device fp32 scalar tensor g = fl32(max|W| / 2688) (1 for an all-zero W)."""
+    m, k, ldw = _rows(W, "W")
+    g = torch.empty(1, dtype=torch.float32, device=W.device)
+    need = lib.nvfp4_global_scale_workspace_size(m, k)
+    ws = _workspace(need, W.device)
+    _check("nvfp4_global_scale", lib.nvfp4_global_scale(_ptr(W), _dtype_code(W), m, k, ldw, _ptr(g), _ptr(ws),
+                                                        need, _stream()))
+    return g
+
+
+def gptq_nvfp4_quantize(W, U, H, g, n_cand=16, flags=0, ws=None, out=None):
+    """NVFP4 quantization of W [m, k]; returns dict(codes [m, k/2] u8, scales [m, k/16] u8,
+    row_err [m] f32 or None, row_loss [m] f32)."""
+    m, k, ldw = _rows(W, "W")
+    dev = W.device
+    if out is None:
+        out = {
+            "codes": torch.empty(m, k // 2, dtype=torch.uint8, device=dev),
+            "scales": torch.empty(m, k // 16, dtype=torch.uint8, device=dev),
+            "row_err": None if (flags & FLAG_NO_ERR) else torch.empty(m, dtype=torch.float32, device=dev),
+            "row_loss": torch.empty(m, dtype=torch.float32, device=dev),
+        }
+    need = lib.gptq_nvfp4_workspace_size(m, k, flags)
+    if ws is None or ws.numel() < need:
+        ws = _workspace(need, dev)
+    _check("gptq_nvfp4_quantize", lib.gptq_nvfp4_quantize(
+        _ptr(W), _dtype_code(W), m, k, ldw, _ptr(U), _ptr(H), _ptr(g), int(n_cand), int(flags),
+        _ptr(out["codes"]), _ptr(out["scales"]), _ptr(out["row_err"]), _ptr(out["row_loss"]), _ptr(ws), need,
+        _stream()))
+    return out
+
+
+def nvfp4_dequantize(codes, scales, g, out_dtype=torch.float32):
+    m, kh = codes.shape
+    k = kh * 2
+    out = torch.empty(m, k, dtype=out_dtype, device=codes.device)
+    _check("nvfp4_dequantize", lib.nvfp4_dequantize(_ptr(codes), _ptr(scales), _ptr(g), m, k, _ptr(out),
+                                                    _dtype_code(out), _stream()))
+    return out
+
+
+def quantize_layer(W, X, n_cand=16, damp_rel=0.01):
+    """Whole layer: H = X^T X, U, g, the sweep and the weighted error (all on the GPU)."""
+    H = hessian_accumulate(X)
+    U, lam, info = factor_hinv(H, damp_rel)
+    g = nvfp4_global_scale(W)
+    res = gptq_nvfp4_quantize(W, U, H, g, n_cand)
+    res.update(H=H, U=U, lam=lam, info=info, g=g)
+    return res

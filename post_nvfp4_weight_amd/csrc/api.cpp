@@ -1,0 +1,240 @@
+// C ABI of the NVFP4 GPTQ / Schur Replay quantizer: argument validation,
+// workspace carving and kernel sequencing.  See include/nvq.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/nvq.h"
+#include "common.h"
+#include "kernels.h"
+
+using namespace nvq;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return NVQ_OK;
+  return fail(NVQ_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+struct QuantWs {
+  size_t wp, eslab, invd, part, total;
+};
+
+QuantWs quant_ws(int64_t m, int64_t k) {
+  QuantWs w;
+  size_t off = 0;
+  w.wp = off;   off += align_up((size_t)m * k * sizeof(float));
+  w.eslab = off; off += align_up((size_t)m * kBatch * sizeof(float));
+  w.invd = off;  off += align_up((size_t)k * sizeof(float));
+  w.part = off;  off += align_up((size_t)m * ((k + kGemmTile - 1) / kGemmTile) * sizeof(float));
+  w.total = off;
+  return w;
+}
+
+bool dtype_ok(int d) { return d == NVQ_DTYPE_F32 || d == NVQ_DTYPE_BF16; }
+
+}  // namespace
+
+extern "C" {
+
+const char* nvq_status_string(int status) {
+  switch (status) {
+    case NVQ_OK: return "ok";
+    case NVQ_ERR_NULL: return "null pointer";
+    case NVQ_ERR_SHAPE: return "invalid shape";
+    case NVQ_ERR_DTYPE: return "unsupported dtype";
+    case NVQ_ERR_NCAND: return "candidate count outside [1, 16]";
+    case NVQ_ERR_WORKSPACE: return "workspace too small or misaligned";
+    case NVQ_ERR_VALUE: return "invalid scalar argument";
+    case NVQ_ERR_HIP: return "HIP runtime error";
+    case NVQ_ERR_ALIGN: return "misaligned pointer";
+    default: return "unknown status";
+  }
+}
+
+const char* nvq_last_error(void) { return g_last_error.c_str(); }
+
+// ---------------------------------------------------------------------------
+size_t hessian_workspace_size(int64_t n, int64_t k, int x_dtype) {
+  if (n <= 0 || k <= 0) return 0;
+  if (x_dtype == NVQ_DTYPE_BF16) return align_up(syrk_bf16_workspace(n, k));
+  return 0;
+}
+
+int hessian_accumulate(const void* X, int x_dtype, int64_t n, int64_t k, int64_t ldx, float* H, void* ws,
+                       size_t ws_bytes, void* stream) {
+  if (!H) return fail(NVQ_ERR_NULL, "hessian_accumulate: H is NULL");
+  if (!dtype_ok(x_dtype)) return fail(NVQ_ERR_DTYPE, "hessian_accumulate: x_dtype %d", x_dtype);
+  if (n < 0 || k <= 0 || k % 16 != 0 || ldx < k || ldx % 4 != 0)
+    return fail(NVQ_ERR_SHAPE, "hessian_accumulate: n=%lld k=%lld ldx=%lld (need n>=0, k>0, k%%16==0, ldx>=k, ldx%%4==0)",
+                (long long)n, (long long)k, (long long)ldx);
+  if (n == 0) return NVQ_OK;
+  if (!X) return fail(NVQ_ERR_NULL, "hessian_accumulate: X is NULL");
+  if (!aligned(H, 16)) return fail(NVQ_ERR_ALIGN, "hessian_accumulate: H must be 16-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  if (x_dtype == NVQ_DTYPE_BF16) {
+    if (!aligned(X, 8)) return fail(NVQ_ERR_ALIGN, "hessian_accumulate: bf16 X must be 8-byte aligned");
+    size_t need = hessian_workspace_size(n, k, x_dtype);
+    if (need && (!ws || ws_bytes < need || !aligned(ws, kAlign)))
+      return fail(NVQ_ERR_WORKSPACE, "hessian_accumulate: workspace needs %zu bytes (256-aligned), got %zu", need,
+                  ws_bytes);
+    return hip_status(syrk_bf16((const uint16_t*)X, n, k, ldx, H, ws, s), "hessian_accumulate");
+  }
+  if (!aligned(X, 16)) return fail(NVQ_ERR_ALIGN, "hessian_accumulate: fp32 X must be 16-byte aligned");
+  hipError_t e = symmetrize_from_upper(H, k, s);
+  if (e == hipSuccess) {
+    GemmArgs a{};
+    a.A = (const float*)X; a.lda = ldx;   // stored [n x k] = op(A)^T
+    a.B = (const float*)X; a.ldb = ldx;
+    a.C = H; a.ldc = k;
+    a.M = k; a.N = k; a.K = n; a.batch = 1; a.alpha = 1.0f; a.beta = 1.0f;
+    e = gemm_f32(a, true, false, false, kEpiAxpby, s);
+  }
+  if (e == hipSuccess) e = symmetrize_from_upper(H, k, s);
+  return hip_status(e, "hessian_accumulate");
+}
+
+// ---------------------------------------------------------------------------
+size_t factor_hinv_workspace_size(int64_t k) { return k > 0 ? align_up(factor_workspace(k)) : 0; }
+
+int factor_hinv(const float* H, int64_t k, float damp_rel, float* U, float* lambda_out, int32_t* info, void* ws,
+                size_t ws_bytes, void* stream) {
+  if (!H || !U || !lambda_out || !info) return fail(NVQ_ERR_NULL, "factor_hinv: H, U, lambda_out and info are required");
+  if (k <= 0 || k % 16 != 0) return fail(NVQ_ERR_SHAPE, "factor_hinv: k=%lld (need k>0, k%%16==0)", (long long)k);
+  if (!(damp_rel >= 0.0f) || !std::isfinite(damp_rel))
+    return fail(NVQ_ERR_VALUE, "factor_hinv: damp_rel must be finite and >= 0");
+  if (H == U) return fail(NVQ_ERR_VALUE, "factor_hinv: U must not overlap H");
+  if (!aligned(H, 16) || !aligned(U, 16)) return fail(NVQ_ERR_ALIGN, "factor_hinv: H and U must be 16-byte aligned");
+  size_t need = factor_hinv_workspace_size(k);
+  if (!ws || ws_bytes < need || !aligned(ws, kAlign))
+    return fail(NVQ_ERR_WORKSPACE, "factor_hinv: workspace needs %zu bytes (256-aligned), got %zu", need, ws_bytes);
+  return hip_status(factor_hinv_launch(H, k, damp_rel, U, lambda_out, info, ws, (hipStream_t)stream), "factor_hinv");
+}
+
+// ---------------------------------------------------------------------------
+size_t nvfp4_global_scale_workspace_size(int64_t m, int64_t k) {
+  return (m > 0 && k > 0) ? align_up((size_t)global_scale_parts(m, k) * sizeof(float)) : 0;
+}
+
+int nvfp4_global_scale(const void* W, int w_dtype, int64_t m, int64_t k, int64_t ldw, float* g_out, void* ws,
+                       size_t ws_bytes, void* stream) {
+  if (!W || !g_out) return fail(NVQ_ERR_NULL, "nvfp4_global_scale: W and g_out are required");
+  if (!dtype_ok(w_dtype)) return fail(NVQ_ERR_DTYPE, "nvfp4_global_scale: w_dtype %d", w_dtype);
+  if (m <= 0 || k <= 0 || ldw < k) return fail(NVQ_ERR_SHAPE, "nvfp4_global_scale: m=%lld k=%lld ldw=%lld",
+                                               (long long)m, (long long)k, (long long)ldw);
+  size_t need = nvfp4_global_scale_workspace_size(m, k);
+  if (!ws || ws_bytes < need || !aligned(ws, kAlign))
+    return fail(NVQ_ERR_WORKSPACE, "nvfp4_global_scale: workspace needs %zu bytes, got %zu", need, ws_bytes);
+  return hip_status(global_scale_launch(W, w_dtype == NVQ_DTYPE_BF16, m, k, ldw, g_out, (float*)ws,
+                                        global_scale_parts(m, k), (hipStream_t)stream),
+                    "nvfp4_global_scale");
+}
+
+// ---------------------------------------------------------------------------
+size_t gptq_nvfp4_workspace_size(int64_t m, int64_t k, unsigned flags) {
+  (void)flags;
+  if (m <= 0 || k <= 0) return 0;
+  return quant_ws(m, k).total;
+}
+
+int gptq_nvfp4_quantize(const void* W, int w_dtype, int64_t m, int64_t k, int64_t ldw, const float* U,
+                        const float* H, const float* g, int n_cand, unsigned flags, uint8_t* codes, uint8_t* scales,
+                        float* row_err, float* row_loss, void* ws, size_t ws_bytes, void* stream) {
+  const bool rtn = flags & NVQ_FLAG_RTN;
+  const bool want_err = !(flags & NVQ_FLAG_NO_ERR);
+  if (flags & ~(NVQ_FLAG_RTN | NVQ_FLAG_NO_ERR)) return fail(NVQ_ERR_VALUE, "gptq_nvfp4_quantize: unknown flags 0x%x", flags);
+  if (!W || !g || !codes || !scales) return fail(NVQ_ERR_NULL, "gptq_nvfp4_quantize: W, g, codes and scales are required");
+  if (!rtn && !U) return fail(NVQ_ERR_NULL, "gptq_nvfp4_quantize: U is required without NVQ_FLAG_RTN");
+  if (want_err && (!H || !row_err)) return fail(NVQ_ERR_NULL, "gptq_nvfp4_quantize: H and row_err are required unless NVQ_FLAG_NO_ERR");
+  if (!dtype_ok(w_dtype)) return fail(NVQ_ERR_DTYPE, "gptq_nvfp4_quantize: w_dtype %d", w_dtype);
+  if (m <= 0 || k <= 0 || k % 16 != 0 || ldw < k || ldw % 4 != 0)
+    return fail(NVQ_ERR_SHAPE, "gptq_nvfp4_quantize: m=%lld k=%lld ldw=%lld (need m>0, k>0, k%%16==0, ldw>=k, ldw%%4==0)",
+                (long long)m, (long long)k, (long long)ldw);
+  if (n_cand < 1 || n_cand > 16) return fail(NVQ_ERR_NCAND, "gptq_nvfp4_quantize: n_cand=%d", n_cand);
+  if (!aligned(codes, 8)) return fail(NVQ_ERR_ALIGN, "gptq_nvfp4_quantize: codes must be 8-byte aligned");
+  if ((U && !aligned(U, 16)) || (H && !aligned(H, 16)))
+    return fail(NVQ_ERR_ALIGN, "gptq_nvfp4_quantize: U and H must be 16-byte aligned");
+  QuantWs L = quant_ws(m, k);
+  if (!ws || ws_bytes < L.total || !aligned(ws, kAlign))
+    return fail(NVQ_ERR_WORKSPACE, "gptq_nvfp4_quantize: workspace needs %zu bytes (256-aligned), got %zu", L.total,
+                ws_bytes);
+  hipStream_t s = (hipStream_t)stream;
+  char* base = (char*)ws;
+  float* Wp = (float*)(base + L.wp);
+  float* Eslab = (float*)(base + L.eslab);
+  float* invd = (float*)(base + L.invd);
+  float* part = (float*)(base + L.part);
+  const int bf = w_dtype == NVQ_DTYPE_BF16;
+  hipError_t e = hipSuccess;
+
+  if (rtn) {
+    e = rtn_launch(W, bf, m, k, ldw, g, n_cand, codes, scales, row_loss, s);
+  } else {
+    e = inv_diag_launch(U, k, invd, s);
+    if (e == hipSuccess) e = load_working_copy(W, bf, m, k, ldw, Wp, s);
+    if (e == hipSuccess && row_loss) e = fill_f32(row_loss, m, 0.0f, s);
+    for (int64_t i1 = 0; e == hipSuccess && i1 < k; i1 += kBatch) {
+      const int ncols = (int)std::min<int64_t>(kBatch, k - i1);
+      e = sweep_batch_launch(Wp, U, invd, g, m, k, (int)i1, ncols, n_cand, codes, scales, Eslab, row_loss, s);
+      const int64_t i2 = i1 + ncols;
+      if (e == hipSuccess && i2 < k) {
+        GemmArgs a{};
+        a.A = Eslab; a.lda = kBatch;
+        a.B = U + i1 * k + i2; a.ldb = k;
+        a.C = Wp + i2; a.ldc = k;
+        a.M = m; a.N = k - i2; a.K = ncols; a.batch = 1; a.alpha = -1.0f; a.beta = 1.0f;
+        e = gemm_f32(a, false, false, false, kEpiAxpby, s);
+      }
+    }
+  }
+  if (e == hipSuccess && want_err) {
+    e = delta_w_launch(W, bf, m, k, ldw, codes, scales, g, Wp, s);
+    if (e == hipSuccess) {
+      GemmArgs a{};
+      a.A = Wp; a.lda = k;
+      a.B = H; a.ldb = k;
+      a.D = Wp; a.ldd = k;
+      a.P = part; a.ldp = (k + kGemmTile - 1) / kGemmTile;
+      a.M = m; a.N = k; a.K = k; a.batch = 1; a.alpha = 1.0f; a.beta = 0.0f;
+      e = gemm_f32(a, false, false, false, kEpiRowDot, s);
+    }
+    if (e == hipSuccess) e = row_sum_launch(part, m, (k + kGemmTile - 1) / kGemmTile, row_err, s);
+  }
+  return hip_status(e, "gptq_nvfp4_quantize");
+}
+
+// ---------------------------------------------------------------------------
+int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* g, int64_t m, int64_t k, void* out,
+                     int out_dtype, void* stream) {
+  if (m < 0 || k <= 0 || k % 16 != 0) return fail(NVQ_ERR_SHAPE, "nvfp4_dequantize: m=%lld k=%lld", (long long)m,
+                                                  (long long)k);
+  if (!dtype_ok(out_dtype)) return fail(NVQ_ERR_DTYPE, "nvfp4_dequantize: out_dtype %d", out_dtype);
+  if (m == 0) return NVQ_OK;
+  if (!codes || !scales || !g || !out) return fail(NVQ_ERR_NULL, "nvfp4_dequantize: null argument");
+  if (!aligned(codes, 8) || !aligned(out, 16)) return fail(NVQ_ERR_ALIGN, "nvfp4_dequantize: codes need 8-byte and out 16-byte alignment");
+  return hip_status(dequant_launch(codes, scales, g, m, k, out, out_dtype == NVQ_DTYPE_BF16, (hipStream_t)stream),
+                    "nvfp4_dequantize");
+}
+
+}  // extern "C"

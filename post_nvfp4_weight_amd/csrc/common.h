@@ -1,0 +1,106 @@
+// Shared device helpers of the NVFP4 quantizer (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvq {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kBlock = 16;       // weights per E4M3 scale
+constexpr int kBatch = 128;      // lazy-batch width of the GPTQ sweep
+constexpr int kE4m3MaxCode = 0x7E;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 bits (inputs are finite here).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// ---------------------------------------------------------------------------
+// NVFP4 codec.  E4M3 (FN): bias 7, exponent field 0 is subnormal (m * 2^-9),
+// 0x7E = 448 is the largest finite value.  E2M1 magnitudes by index:
+// 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+//
+// Every rounding decision compares a magnitude |w| with t * s * g, where t is
+// a midpoint of one of the grids (at most 7 significant bits together with
+// s) and g the fp32 tensor scale.  t * s is exact in fp32, and the sign of
+// fmaf(-(t * s), g, |w|) is the sign of the exact difference, so decisions are
+// those of exact real arithmetic (denormals must not be flushed).
+// ---------------------------------------------------------------------------
+
+// Value of a non-negative E4M3 code 0..126 (exact).
+__device__ __forceinline__ float e4m3_value(int c) {
+  int e = c >> 3, m = c & 7;
+  return e == 0 ? (float)m * 0x1p-9f : __uint_as_float((uint32_t)(e + 120) << 23 | (uint32_t)m << 20);
+}
+
+// Code of the E4M3 value nearest to the real quotient a / (6 g), ties to the
+// even code, saturating at 0x7E.  a >= 0.  Binary search over the 126
+// midpoints m_i = (v_i + v_{i+1}) / 2; a passes midpoint i when a > 6 m_i g,
+// or a >= 6 m_i g when i is odd (the tie then rounds up to the even code i+1).
+__device__ __forceinline__ int e4m3_code_of_ratio(float a, float g) {
+  int lo = 0, hi = kE4m3MaxCode;           // answer in [lo, hi]
+#pragma unroll
+  for (int it = 0; it < 7; ++it) {
+    int mid = (lo + hi) >> 1;              // test midpoint between mid and mid+1
+    if (lo >= hi) break;
+    float six_m = 3.0f * (e4m3_value(mid) + e4m3_value(mid + 1));   // 6 * m_i, exact
+    float d = fmaf(-six_m, g, a);
+    bool pass = (mid & 1) ? (d >= 0.0f) : (d > 0.0f);
+    if (pass) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+// Magnitude index (0..7) of the E2M1 value nearest to |w| / (s g), ties to the
+// even index, clipped at 6.  aw = |w|, s = E4M3 block-scale value.
+__device__ __forceinline__ int e2m1_index(float aw, float s, float g) {
+  int idx = 0;
+  idx += fmaf(-0.25f * s, g, aw) > 0.0f;
+  idx += fmaf(-0.75f * s, g, aw) >= 0.0f;
+  idx += fmaf(-1.25f * s, g, aw) > 0.0f;
+  idx += fmaf(-1.75f * s, g, aw) >= 0.0f;
+  idx += fmaf(-2.50f * s, g, aw) > 0.0f;
+  idx += fmaf(-3.50f * s, g, aw) >= 0.0f;
+  idx += fmaf(-5.00f * s, g, aw) > 0.0f;
+  return idx;
+}
+
+// Twice the E2M1 magnitude of index idx: 0,1,2,3,4,6,8,12 packed in nibbles.
+__device__ __forceinline__ float e2m1_twice_mag(int idx) {
+  return (float)((0xC8643210u >> (4 * idx)) & 0xFu);
+}
+
+// Signed dequantized value fl32(e2m1 * s * g): the first product is exact.
+__device__ __forceinline__ float e2m1_dequant(int code4, float s, float g) {
+  float m = e2m1_twice_mag(code4 & 7) * 0.5f * s;
+  float v = m * g;
+  return (code4 & 8) ? -v : v;
+}
+
+// 4-bit code of w under scale s * g (zero is +0).
+__device__ __forceinline__ int e2m1_encode(float w, float s, float g) {
+  int idx = e2m1_index(fabsf(w), s, g);
+  return (idx != 0 && w < 0.0f) ? (idx | 8) : idx;
+}
+
+// First of the n_cand consecutive candidate codes around c0, inside [1, 126].
+__device__ __forceinline__ int candidate_lo(int c0, int n_cand) {
+  int lo = c0 - (n_cand >> 1);
+  lo = lo < 1 ? 1 : lo;
+  int top = kE4m3MaxCode - n_cand + 1;
+  return lo > top ? top : lo;
+}
+
+}  // namespace nvq

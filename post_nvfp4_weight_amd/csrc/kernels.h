@@ -1,0 +1,65 @@
+// Internal launchers (host side) of the gfx950 kernels.  Every launcher
+// enqueues on `s` and returns the hipGetLastError() of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace nvq {
+
+// ---- fp32 MFMA GEMM: C = alpha * op(A) op(B) + beta * C ---------------------
+enum GemmEpi { kEpiAxpby = 0, kEpiRowDot = 1 };
+
+struct GemmArgs {
+  const float* A; const float* B; float* C;
+  const float* D;       // row-dot epilogue: the matrix multiplied into op(A)op(B)
+  float* P;             // row-dot epilogue: partial sums [M x ldp]
+  int64_t M, N, K;
+  int64_t lda, ldb, ldc, ldd, ldp;
+  int64_t sA, sB, sC;   // batch strides (elements)
+  int batch;
+  float alpha, beta;
+};
+// trans_a: A is stored [K x M]; trans_b: B is stored [N x K].  lower: skip
+// 128x128 tiles that lie entirely above the diagonal (square C only).
+// Requires M, N, K, leading dimensions and offsets to be multiples of 4 and
+// 16-byte aligned matrix starts.
+hipError_t gemm_f32(const GemmArgs& a, bool trans_a, bool trans_b, bool lower, GemmEpi epi,
+                    hipStream_t s);
+constexpr int kGemmTile = 128;
+
+// ---- Hessian -------------------------------------------------------------
+size_t syrk_bf16_workspace(int64_t n, int64_t k);
+hipError_t syrk_bf16(const uint16_t* X, int64_t n, int64_t k, int64_t ldx, float* H, void* ws,
+                     hipStream_t s);
+hipError_t symmetrize_from_upper(float* H, int64_t k, hipStream_t s);
+
+// ---- factor ----------------------------------------------------------------
+size_t factor_workspace(int64_t k);
+hipError_t factor_hinv_launch(const float* H, int64_t k, float damp_rel, float* U,
+                              float* lambda_out, int32_t* info, void* ws, hipStream_t s);
+
+// ---- codec / sweep -----------------------------------------------------------
+hipError_t global_scale_launch(const void* W, int bf16, int64_t m, int64_t k, int64_t ldw,
+                               float* g, float* partial, int nparts, hipStream_t s);
+int global_scale_parts(int64_t m, int64_t k);
+hipError_t dequant_launch(const uint8_t* codes, const uint8_t* scales, const float* g,
+                          int64_t m, int64_t k, void* out, int out_bf16, hipStream_t s);
+hipError_t rtn_launch(const void* W, int bf16, int64_t m, int64_t k, int64_t ldw,
+                      const float* g, int n_cand, uint8_t* codes, uint8_t* scales,
+                      float* row_loss, hipStream_t s);
+hipError_t load_working_copy(const void* W, int bf16, int64_t m, int64_t k, int64_t ldw,
+                             float* Wp, hipStream_t s);
+hipError_t inv_diag_launch(const float* U, int64_t k, float* invd, hipStream_t s);
+hipError_t sweep_batch_launch(float* Wp, const float* U, const float* invd, const float* g,
+                              int64_t m, int64_t k, int i1, int ncols, int n_cand,
+                              uint8_t* codes, uint8_t* scales, float* Eslab, float* row_loss,
+                              hipStream_t s);
+hipError_t delta_w_launch(const void* W, int bf16, int64_t m, int64_t k, int64_t ldw,
+                          const uint8_t* codes, const uint8_t* scales, const float* g,
+                          float* dW, hipStream_t s);
+hipError_t row_sum_launch(const float* P, int64_t m, int64_t nparts, float* out, hipStream_t s);
+hipError_t fill_f32(float* p, int64_t n, float v, hipStream_t s);
+
+}  // namespace nvq

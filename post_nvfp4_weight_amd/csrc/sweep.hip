@@ -1,0 +1,430 @@
+// GPTQ column sweep with Schur Replay block-scale selection, and the NVFP4
+// streaming kernels (global scale, round-to-nearest encode, dequantization).
+//
+// Sweep mapping.  Output rows are independent; inside a row the 16-column
+// blocks are processed in order.  One lane per (row, candidate): a row's G
+// candidate lanes (G = next power of two >= n_cand) replay the block in
+// registers, each with its own scale, reduce their scores with cross-lane
+// shuffles (ties to the lower candidate), and the winner publishes its codes,
+// scale and errors.  A workgroup owns ROWS rows of one 128-column lazy batch:
+// the rows' batch slab and the transposed 128x128 diagonal block of U live in
+// LDS, the 16x16 in-block factor entries are wave-uniform (scalar loads), and
+// after each block the row's G lanes update the later columns of the batch.
+// Columns beyond the batch are updated afterwards by one fp32 MFMA GEMM with
+// the batch's error slab.
+#include "common.h"
+#include "kernels.h"
+
+namespace nvq {
+
+namespace {
+
+template <int BF16>
+__device__ __forceinline__ float load_w(const void* W, int64_t idx) {
+  if (BF16) return bf16_bits_to_f32(((const uint16_t*)W)[idx]);
+  return ((const float*)W)[idx];
+}
+
+// ---- global scale --------------------------------------------------------------
+template <int BF16>
+__global__ __launch_bounds__(256) void amax_kernel(const void* __restrict__ W, int64_t m, int64_t k,
+                                                   int64_t ldw, float* __restrict__ partial) {
+  __shared__ float red[256];
+  float a = 0.0f;
+  const int64_t total = m * k;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+    int64_t r = e / k, c = e % k;
+    a = fmaxf(a, fabsf(load_w<BF16>(W, r * ldw + c)));
+  }
+  red[threadIdx.x] = a;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + w]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) partial[blockIdx.x] = red[0];
+}
+
+__global__ __launch_bounds__(256) void gscale_finish_kernel(const float* __restrict__ partial, int nparts,
+                                                            float* __restrict__ g) {
+  __shared__ float red[256];
+  float a = 0.0f;
+  for (int i = threadIdx.x; i < nparts; i += 256) a = fmaxf(a, partial[i]);
+  red[threadIdx.x] = a;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + w]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    float amax = red[0];
+    // fl32(amax / 2688): the fp64 quotient rounded to fp32 is the correctly
+    // rounded fp32 quotient (no fp32 midpoint lies within fp64 rounding of it).
+    *g = amax > 0.0f ? (float)((double)amax / 2688.0) : 1.0f;
+  }
+}
+
+// ---- dequantization ---------------------------------------------------------------
+template <int OUT_BF16>
+__global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ codes,
+                                                      const uint8_t* __restrict__ scales,
+                                                      const float* __restrict__ gptr, int64_t m, int64_t k,
+                                                      void* __restrict__ out) {
+  const int64_t nblk = m * (k / kBlock);
+  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (b >= nblk) return;
+  const float g = *gptr;
+  const float s = e4m3_value(scales[b] & 0x7F);
+  const bool neg_scale = scales[b] & 0x80;
+  u32x2 c = *(const u32x2*)(codes + b * 8);
+  float v[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    int code = (c[j >> 3] >> (4 * (j & 7))) & 0xF;
+    float x = e2m1_dequant(code, s, g);
+    v[j] = neg_scale ? -x : x;
+  }
+  if (OUT_BF16) {
+    u32x4 o[2];
+#pragma unroll
+    for (int w = 0; w < 8; ++w)
+      o[w >> 2][w & 3] = (uint32_t)f32_to_bf16_bits(v[2 * w]) | ((uint32_t)f32_to_bf16_bits(v[2 * w + 1]) << 16);
+    u32x4* dst = (u32x4*)((uint16_t*)out + b * 16);
+    dst[0] = o[0];
+    dst[1] = o[1];
+  } else {
+    f32x4* dst = (f32x4*)((float*)out + b * 16);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dst[q] = f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+  }
+}
+
+// ---- round to nearest (no GPTQ updates) ------------------------------------------
+// One thread per (row, block).  Candidate scores are sum_j (w_j - q_j)^2 with
+// separately rounded products and sums in column order.
+template <int BF16>
+__global__ __launch_bounds__(256) void rtn_kernel(const void* __restrict__ W, int64_t m, int64_t k, int64_t ldw,
+                                                  const float* __restrict__ gptr, int n_cand,
+                                                  uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  const int64_t nbk = k / kBlock;
+  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (b >= m * nbk) return;
+  const int64_t row = b / nbk, blk = b % nbk;
+  const float g = *gptr;
+  float w[16];
+  float a = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    w[j] = load_w<BF16>(W, row * ldw + blk * 16 + j);
+    a = fmaxf(a, fabsf(w[j]));
+  }
+  int best_c = 0;
+  uint32_t best_lo = 0, best_hi = 0;
+  if (a > 0.0f) {
+    const int lo = candidate_lo(e4m3_code_of_ratio(a, g), n_cand);
+    float best = __builtin_inff();
+    for (int ci = 0; ci < n_cand; ++ci) {
+      const int c = lo + ci;
+      const float s = e4m3_value(c);
+      float score = 0.0f;
+      uint32_t plo = 0, phi = 0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        int code = e2m1_encode(w[j], s, g);
+        float e = __fsub_rn(w[j], e2m1_dequant(code, s, g));
+        score = __fadd_rn(score, __fmul_rn(e, e));
+        if (j < 8) plo |= (uint32_t)code << (4 * j); else phi |= (uint32_t)code << (4 * (j - 8));
+      }
+      if (score < best) { best = score; best_c = c; best_lo = plo; best_hi = phi; }
+    }
+  }
+  *(u32x2*)(codes + row * (k / 2) + blk * 8) = u32x2{best_lo, best_hi};
+  scales[row * nbk + blk] = (uint8_t)best_c;
+}
+
+// ---- sweep helpers ------------------------------------------------------------------
+template <int BF16>
+__global__ void load_working_kernel(const void* __restrict__ W, int64_t m, int64_t k, int64_t ldw,
+                                    float* __restrict__ Wp) {
+  int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e >= m * k) return;
+  int64_t r = e / k, c = e % k;  // k % 4 == 0: the 4 elements share a row
+  f32x4 v;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) v[q] = load_w<BF16>(W, r * ldw + c + q);
+  *(f32x4*)(Wp + e) = v;
+}
+
+__global__ void inv_diag_kernel(const float* __restrict__ U, int64_t k, float* __restrict__ invd) {
+  int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (j < k) invd[j] = 1.0f / U[j * k + j];
+}
+
+// dW = W - dequant(codes, scales, g) as fp32 [m x k].
+template <int BF16>
+__global__ __launch_bounds__(256) void delta_w_kernel(const void* __restrict__ W, int64_t m, int64_t k,
+                                                      int64_t ldw, const uint8_t* __restrict__ codes,
+                                                      const uint8_t* __restrict__ scales,
+                                                      const float* __restrict__ gptr, float* __restrict__ dW) {
+  const int64_t nbk = k / kBlock;
+  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (b >= m * nbk) return;
+  const int64_t row = b / nbk, blk = b % nbk;
+  const float g = *gptr;
+  const float s = e4m3_value(scales[b] & 0x7F);
+  u32x2 c = *(const u32x2*)(codes + b * 8);
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    int code = (c[j >> 3] >> (4 * (j & 7))) & 0xF;
+    dW[row * k + blk * 16 + j] = load_w<BF16>(W, row * ldw + blk * 16 + j) - e2m1_dequant(code, s, g);
+  }
+}
+
+__global__ void row_sum_kernel(const float* __restrict__ P, int64_t m, int64_t np, float* __restrict__ out) {
+  int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (r >= m) return;
+  float s = 0.0f;
+  for (int64_t t = 0; t < np; ++t) s += P[r * np + t];
+  out[r] = s;
+}
+
+__global__ void fill_kernel(float* p, int64_t n, float v) {
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// ---- the sweep of one lazy batch ---------------------------------------------------------
+constexpr int UT_LD = kBatch + 4;
+
+template <int G>
+struct SweepCfg {
+  static constexpr int ROWS = (64 / G) > 16 ? (64 / G) : 16;
+  static constexpr int THREADS = ROWS * G;
+};
+
+template <int G>
+__global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
+    float* __restrict__ Wp, const float* __restrict__ U, const float* __restrict__ invd,
+    const float* __restrict__ gptr, int64_t m, int64_t k, int i1, int ncols, int n_cand,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ Eslab,
+    float* __restrict__ row_loss) {
+  constexpr int ROWS = SweepCfg<G>::ROWS;
+  constexpr int NT = SweepCfg<G>::THREADS;
+  __shared__ __attribute__((aligned(16))) float Ut[kBatch * UT_LD];   // Ut[c][r] = U[i1+r][i1+c]
+  __shared__ __attribute__((aligned(16))) float slab[ROWS][kBatch];
+  __shared__ __attribute__((aligned(16))) float eb_s[ROWS][16];
+
+  const int tid = threadIdx.x;
+  const int rl = tid / G, ci = tid % G;
+  const int64_t row = (int64_t)blockIdx.x * ROWS + rl;
+  const bool row_ok = row < m;
+  const float g = *gptr;
+
+  for (int e = tid; e < kBatch * kBatch; e += NT) {
+    int r = e / kBatch, c = e % kBatch;
+    float v = 0.0f;
+    if (r < ncols && c < ncols && r <= c) v = U[(int64_t)(i1 + r) * k + i1 + c];
+    Ut[c * UT_LD + r] = v;
+  }
+  for (int e = tid; e < ROWS * kBatch; e += NT) {
+    int r = e / kBatch, c = e % kBatch;
+    int64_t gr = (int64_t)blockIdx.x * ROWS + r;
+    slab[r][c] = (gr < m && c < ncols) ? Wp[gr * k + i1 + c] : 0.0f;
+  }
+  __syncthreads();
+
+  float loss = 0.0f;
+  const int nblk = ncols / kBlock;
+  for (int b = 0; b < nblk; ++b) {
+    const int c0 = b * kBlock;
+    float v[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      f32x4 t = *(const f32x4*)&slab[rl][c0 + 4 * q];
+      v[4 * q] = t[0]; v[4 * q + 1] = t[1]; v[4 * q + 2] = t[2]; v[4 * q + 3] = t[3];
+    }
+    float a = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) a = fmaxf(a, fabsf(v[j]));
+
+    float e[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) e[j] = 0.0f;
+    uint32_t plo = 0, phi = 0;
+    int cand = 0;
+    float score = __builtin_inff();
+    if (a > 0.0f) {
+      const int lo = candidate_lo(e4m3_code_of_ratio(a, g), n_cand);
+      cand = lo + (ci < n_cand ? ci : 0);
+      const float s = e4m3_value(cand);
+      const float* Ub = U + (int64_t)(i1 + c0) * k + (i1 + c0);
+      const float* id = invd + i1 + c0;
+      float sc = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int code = e2m1_encode(v[j], s, g);
+        const float ej = (v[j] - e2m1_dequant(code, s, g)) * id[j];
+        sc = fmaf(ej, ej, sc);
+#pragma unroll
+        for (int l = j + 1; l < 16; ++l) v[l] = fmaf(-ej, Ub[(int64_t)j * k + l], v[l]);
+        e[j] = ej;
+        if (j < 8) plo |= (uint32_t)code << (4 * j); else phi |= (uint32_t)code << (4 * (j - 8));
+      }
+      if (ci < n_cand) score = sc;
+    }
+    // Arg-min over the row's G lanes; ties to the lower candidate index.
+    float bs = score;
+    int bi = ci;
+#pragma unroll
+    for (int off = 1; off < G; off <<= 1) {
+      float so = __shfl_xor(bs, off, G);
+      int io = __shfl_xor(bi, off, G);
+      if (so < bs || (so == bs && io < bi)) { bs = so; bi = io; }
+    }
+    if (ci == bi && row_ok) {
+      *(f32x4*)&eb_s[rl][0] = f32x4{e[0], e[1], e[2], e[3]};
+      *(f32x4*)&eb_s[rl][4] = f32x4{e[4], e[5], e[6], e[7]};
+      *(f32x4*)&eb_s[rl][8] = f32x4{e[8], e[9], e[10], e[11]};
+      *(f32x4*)&eb_s[rl][12] = f32x4{e[12], e[13], e[14], e[15]};
+      const int64_t gb = (i1 + c0) / kBlock;
+      *(u32x2*)(codes + row * (k / 2) + gb * 8) = u32x2{plo, phi};
+      scales[row * (k / kBlock) + gb] = (uint8_t)cand;
+      f32x4* es = (f32x4*)(Eslab + row * kBatch + c0);
+      es[0] = f32x4{e[0], e[1], e[2], e[3]};
+      es[1] = f32x4{e[4], e[5], e[6], e[7]};
+      es[2] = f32x4{e[8], e[9], e[10], e[11]};
+      es[3] = f32x4{e[12], e[13], e[14], e[15]};
+      if (a > 0.0f) loss += bs;
+    }
+    __syncthreads();
+    // Update the later columns of the batch: w'_l -= sum_j e_j U[c0+j][l].
+    if (row_ok && c0 + kBlock < ncols) {
+      float eb[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        f32x4 t = *(const f32x4*)&eb_s[rl][4 * q];
+        eb[4 * q] = t[0]; eb[4 * q + 1] = t[1]; eb[4 * q + 2] = t[2]; eb[4 * q + 3] = t[3];
+      }
+      for (int cc = c0 + kBlock + ci; cc < ncols; cc += G) {
+        float acc = slab[rl][cc];
+        const float* ut = &Ut[cc * UT_LD + c0];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          f32x4 u4 = *(const f32x4*)(ut + 4 * q);
+          acc = fmaf(-eb[4 * q + 0], u4[0], acc);
+          acc = fmaf(-eb[4 * q + 1], u4[1], acc);
+          acc = fmaf(-eb[4 * q + 2], u4[2], acc);
+          acc = fmaf(-eb[4 * q + 3], u4[3], acc);
+        }
+        slab[rl][cc] = acc;
+      }
+    }
+    __syncthreads();
+  }
+  // Per-row loss: the winners' scores are spread over the row's lanes.
+#pragma unroll
+  for (int off = 1; off < G; off <<= 1) loss += __shfl_xor(loss, off, G);
+  if (ci == 0 && row_ok && row_loss) row_loss[row] += loss;
+}
+
+template <int G>
+hipError_t sweep_launch_g(float* Wp, const float* U, const float* invd, const float* g, int64_t m, int64_t k,
+                          int i1, int ncols, int n_cand, uint8_t* codes, uint8_t* scales, float* Eslab,
+                          float* row_loss, hipStream_t s) {
+  constexpr int ROWS = SweepCfg<G>::ROWS;
+  dim3 grid((unsigned)((m + ROWS - 1) / ROWS));
+  hipLaunchKernelGGL(sweep_batch_kernel<G>, grid, dim3(SweepCfg<G>::THREADS), 0, s, Wp, U, invd, g, m, k, i1,
+                     ncols, n_cand, codes, scales, Eslab, row_loss);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int global_scale_parts(int64_t m, int64_t k) {
+  int64_t blocks = (m * k + 256 * 16 - 1) / (256 * 16);
+  if (blocks > 1024) blocks = 1024;
+  return (int)(blocks < 1 ? 1 : blocks);
+}
+
+hipError_t global_scale_launch(const void* W, int bf16, int64_t m, int64_t k, int64_t ldw, float* g,
+                               float* partial, int nparts, hipStream_t s) {
+  if (bf16)
+    hipLaunchKernelGGL(amax_kernel<1>, dim3(nparts), dim3(256), 0, s, W, m, k, ldw, partial);
+  else
+    hipLaunchKernelGGL(amax_kernel<0>, dim3(nparts), dim3(256), 0, s, W, m, k, ldw, partial);
+  hipLaunchKernelGGL(gscale_finish_kernel, dim3(1), dim3(256), 0, s, partial, nparts, g);
+  return hipGetLastError();
+}
+
+hipError_t dequant_launch(const uint8_t* codes, const uint8_t* scales, const float* g, int64_t m, int64_t k,
+                          void* out, int out_bf16, hipStream_t s) {
+  int64_t nblk = m * (k / kBlock);
+  if (nblk == 0) return hipSuccess;
+  dim3 grid((unsigned)((nblk + 255) / 256));
+  if (out_bf16)
+    hipLaunchKernelGGL(dequant_kernel<1>, grid, dim3(256), 0, s, codes, scales, g, m, k, out);
+  else
+    hipLaunchKernelGGL(dequant_kernel<0>, grid, dim3(256), 0, s, codes, scales, g, m, k, out);
+  return hipGetLastError();
+}
+
+hipError_t rtn_launch(const void* W, int bf16, int64_t m, int64_t k, int64_t ldw, const float* g, int n_cand,
+                      uint8_t* codes, uint8_t* scales, float* row_loss, hipStream_t s) {
+  int64_t nblk = m * (k / kBlock);
+  dim3 grid((unsigned)((nblk + 255) / 256));
+  if (bf16)
+    hipLaunchKernelGGL(rtn_kernel<1>, grid, dim3(256), 0, s, W, m, k, ldw, g, n_cand, codes, scales);
+  else
+    hipLaunchKernelGGL(rtn_kernel<0>, grid, dim3(256), 0, s, W, m, k, ldw, g, n_cand, codes, scales);
+  if (row_loss) hipLaunchKernelGGL(fill_kernel, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, s, row_loss, m, 0.0f);
+  return hipGetLastError();
+}
+
+hipError_t load_working_copy(const void* W, int bf16, int64_t m, int64_t k, int64_t ldw, float* Wp,
+                             hipStream_t s) {
+  dim3 grid((unsigned)((m * k / 4 + 255) / 256));
+  if (bf16)
+    hipLaunchKernelGGL(load_working_kernel<1>, grid, dim3(256), 0, s, W, m, k, ldw, Wp);
+  else
+    hipLaunchKernelGGL(load_working_kernel<0>, grid, dim3(256), 0, s, W, m, k, ldw, Wp);
+  return hipGetLastError();
+}
+
+hipError_t inv_diag_launch(const float* U, int64_t k, float* invd, hipStream_t s) {
+  hipLaunchKernelGGL(inv_diag_kernel, dim3((unsigned)((k + 255) / 256)), dim3(256), 0, s, U, k, invd);
+  return hipGetLastError();
+}
+
+hipError_t sweep_batch_launch(float* Wp, const float* U, const float* invd, const float* g, int64_t m, int64_t k,
+                              int i1, int ncols, int n_cand, uint8_t* codes, uint8_t* scales, float* Eslab,
+                              float* row_loss, hipStream_t s) {
+  if (n_cand <= 1) return sweep_launch_g<1>(Wp, U, invd, g, m, k, i1, ncols, n_cand, codes, scales, Eslab, row_loss, s);
+  if (n_cand <= 2) return sweep_launch_g<2>(Wp, U, invd, g, m, k, i1, ncols, n_cand, codes, scales, Eslab, row_loss, s);
+  if (n_cand <= 4) return sweep_launch_g<4>(Wp, U, invd, g, m, k, i1, ncols, n_cand, codes, scales, Eslab, row_loss, s);
+  if (n_cand <= 8) return sweep_launch_g<8>(Wp, U, invd, g, m, k, i1, ncols, n_cand, codes, scales, Eslab, row_loss, s);
+  return sweep_launch_g<16>(Wp, U, invd, g, m, k, i1, ncols, n_cand, codes, scales, Eslab, row_loss, s);
+}
+
+hipError_t delta_w_launch(const void* W, int bf16, int64_t m, int64_t k, int64_t ldw, const uint8_t* codes,
+                          const uint8_t* scales, const float* g, float* dW, hipStream_t s) {
+  int64_t nblk = m * (k / kBlock);
+  dim3 grid((unsigned)((nblk + 255) / 256));
+  if (bf16)
+    hipLaunchKernelGGL(delta_w_kernel<1>, grid, dim3(256), 0, s, W, m, k, ldw, codes, scales, g, dW);
+  else
+    hipLaunchKernelGGL(delta_w_kernel<0>, grid, dim3(256), 0, s, W, m, k, ldw, codes, scales, g, dW);
+  return hipGetLastError();
+}
+
+hipError_t row_sum_launch(const float* P, int64_t m, int64_t np, float* out, hipStream_t s) {
+  hipLaunchKernelGGL(row_sum_kernel, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, s, P, m, np, out);
+  return hipGetLastError();
+}
+
+hipError_t fill_f32(float* p, int64_t n, float v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n, v);
+  return hipGetLastError();
+}
+
+}  // namespace nvq

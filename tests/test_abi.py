@@ -1,0 +1,79 @@
+"""The C-ABI library loads, exports every function declared in include/nvq.h, and
+rejects bad arguments on the host (no GPU work is enqueued by these calls)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvq.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\**\s*([a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ["hessian_accumulate", "factor_hinv", "gptq_nvfp4_quantize", "nvfp4_dequantize",
+              "nvfp4_global_scale", "nvq_status_string", "nvq_last_error"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    import post_nvfp4_weight_amd as nvq
+    lib = ctypes.CDLL(nvq.LIB_PATH)
+    missing = [n for n in _declared() if not hasattr(lib, n)]
+    assert not missing, missing
+    assert sorted(nvq.EXPORTS) == _declared()
+
+
+def test_host_validation_rejects_bad_arguments():
+    import post_nvfp4_weight_amd as nvq
+    lib = nvq.lib
+    P = ctypes.c_void_p
+    fake = P(4096)   # never dereferenced: validation fails first
+    # k not a multiple of 16
+    assert lib.hessian_accumulate(fake, 1, 10, 24, 24, fake, None, 0, None) == -2
+    # H missing
+    assert lib.hessian_accumulate(fake, 1, 10, 32, 32, None, None, 0, None) == -1
+    # unknown dtype
+    assert lib.hessian_accumulate(fake, 7, 10, 32, 32, fake, None, 0, None) == -3
+    assert b"x_dtype" in lib.nvq_last_error()
+    # n = 0 is a no-op
+    assert lib.hessian_accumulate(None, 1, 0, 32, 32, fake, None, 0, None) == 0
+    # candidate count out of range
+    rc = lib.gptq_nvfp4_quantize(fake, 1, 16, 32, 32, fake, fake, fake, 17, 0, fake, fake, fake, None,
+                                 fake, 1 << 30, None)
+    assert rc == -4
+    # workspace too small
+    rc = lib.gptq_nvfp4_quantize(fake, 1, 16, 32, 32, fake, fake, fake, 16, 0, fake, fake, fake, None,
+                                 P(1 << 20), 16, None)
+    assert rc == -5
+    # U required without the RTN flag
+    rc = lib.gptq_nvfp4_quantize(fake, 1, 16, 32, 32, None, fake, fake, 16, 0, fake, fake, fake, None,
+                                 fake, 1 << 30, None)
+    assert rc == -1
+    # factor: negative damping, overlapping U
+    assert lib.factor_hinv(fake, 32, ctypes.c_float(-1.0), P(8192), fake, fake, fake, 1 << 30, None) == -6
+    assert lib.factor_hinv(fake, 32, ctypes.c_float(0.01), fake, fake, fake, fake, 1 << 30, None) == -6
+    # dequantize: bad k, bad dtype, empty is fine
+    assert lib.nvfp4_dequantize(fake, fake, fake, 4, 8, fake, 0, None) == -2
+    assert lib.nvfp4_dequantize(fake, fake, fake, 4, 32, fake, 5, None) == -3
+    assert lib.nvfp4_dequantize(None, None, None, 0, 32, None, 0, None) == 0
+    for s in (0, -1, -2, -3, -4, -5, -6, -7, -8, 99):
+        assert lib.nvq_status_string(s)
+
+
+def test_workspace_queries_are_consistent():
+    import post_nvfp4_weight_amd as nvq
+    lib = nvq.lib
+    assert lib.gptq_nvfp4_workspace_size(4096, 4096, 0) >= 4096 * 4096 * 4
+    assert lib.factor_hinv_workspace_size(4096) >= 2 * 4096 * 4096 * 4
+    assert lib.gptq_nvfp4_workspace_size(0, 16, 0) == 0
+    assert lib.nvfp4_global_scale_workspace_size(16, 16) > 0
