@@ -65,9 +65,9 @@ extern "C" {
  * Curvature", Abstract: the second-order state of GPTQ), H += X^T X.
  *
  *   X      device, [n x ldx] row-major, element type x_dtype (NVQ_DTYPE_BF16
- *          or NVQ_DTYPE_F32); only the first k columns are read.  bf16 rows
- *          must start 8-byte aligned (ldx % 4 == 0), fp32 rows 16-byte
- *          aligned (ldx % 4 == 0).
+ *          or NVQ_DTYPE_F32); only the first k columns are used.  Rows must
+ *          start 16-byte aligned: X itself 16-byte aligned and ldx % 8 == 0
+ *          for bf16, ldx % 4 == 0 for fp32.
  *   n      number of tokens (rows of X), n >= 0; n = 0 leaves H unchanged.
  *   k      number of input channels, k > 0, k % 16 == 0.
  *   H      device, fp32 [k x k] row-major.  On entry only the upper triangle

@@ -1,6 +1,7 @@
 """Build libnvq.so (gfx950) in-tree with hipcc.
 
-Usage: python -m post_nvfp4_weight_amd.build   (or build() from Python)
+Usage: python post_nvfp4_weight_amd/build.py   (run by path: importing the
+package loads the library it builds)
 """
 
 import os

@@ -94,7 +94,8 @@ int hessian_accumulate(const void* X, int x_dtype, int64_t n, int64_t k, int64_t
   if (!aligned(H, 16)) return fail(NVQ_ERR_ALIGN, "hessian_accumulate: H must be 16-byte aligned");
   hipStream_t s = (hipStream_t)stream;
   if (x_dtype == NVQ_DTYPE_BF16) {
-    if (!aligned(X, 8)) return fail(NVQ_ERR_ALIGN, "hessian_accumulate: bf16 X must be 8-byte aligned");
+    if (!aligned(X, 16)) return fail(NVQ_ERR_ALIGN, "hessian_accumulate: bf16 X must be 16-byte aligned");
+    if (ldx % 8 != 0) return fail(NVQ_ERR_SHAPE, "hessian_accumulate: bf16 rows must be 16-byte aligned (ldx %% 8 == 0)");
     size_t need = hessian_workspace_size(n, k, x_dtype);
     if (need && (!ws || ws_bytes < need || !aligned(ws, kAlign)))
       return fail(NVQ_ERR_WORKSPACE, "hessian_accumulate: workspace needs %zu bytes (256-aligned), got %zu", need,

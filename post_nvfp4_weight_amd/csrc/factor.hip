@@ -49,66 +49,79 @@ __global__ void flip_damp_kernel(const float* __restrict__ H, int64_t k, const f
 }
 
 // Factor the 64x64 diagonal block at p in place (lower L), write its inverse
-// into Linv's diagonal block and into Dinv [64 x 64].  Sets *info (once) on a
-// non-positive pivot: info = p + j + 1 is the order of the failing leading
-// minor of A, i.e. of the failing trailing minor of H + lam I.
-__global__ __launch_bounds__(256) void potf2_inv_kernel(float* __restrict__ A, int64_t k, int64_t p,
-                                                        float* __restrict__ Linv, float* __restrict__ Dinv,
-                                                        int32_t* __restrict__ info) {
-  __shared__ float S[NB][NB + 1];
-  __shared__ float X[NB][NB + 1];
-  __shared__ int bad;
-  const int tid = threadIdx.x;
+// into Linv's diagonal block and into Dinv [64 x 64].  One wave; lane l keeps
+// column l of the block in registers.  Cholesky step j: lane j scales its
+// column and publishes it in LDS, every lane l > j subtracts L[l][j] times it.
+// The inverse is then solved column by column (lane c: L x = e_c) against an
+// LDS copy of L, one row per step.  Sets *info (once) on a non-positive pivot:
+// info = p + j + 1 is the order of the failing leading minor of A, i.e. of the
+// failing trailing minor of H + lam I.
+__global__ __launch_bounds__(64) void potf2_inv_kernel(float* __restrict__ A, int64_t k, int64_t p,
+                                                       float* __restrict__ Linv, float* __restrict__ Dinv,
+                                                       int32_t* __restrict__ info) {
+  __shared__ __attribute__((aligned(16))) float colj[NB];
+  __shared__ __attribute__((aligned(16))) float Ls[NB][NB + 4];
+  const int lane = threadIdx.x;
   const int nb = (int)min((int64_t)NB, k - p);
-  if (tid == 0) bad = 0;
-  for (int e = tid; e < NB * NB; e += 256) {
-    int r = e / NB, c = e % NB;
+  float c[NB];   // column `lane`: c[i] = A[i][lane] (lower part meaningful)
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
     float v = 0.0f;
-    if (r < nb && c < nb && c <= r) v = A[(p + r) * k + p + c];
-    else if (r == c) v = 1.0f;  // pad beyond k with identity
-    S[r][c] = v;
-    X[r][c] = (r == c) ? 1.0f : 0.0f;
+    if (i < nb && lane < nb && lane <= i) v = A[(p + i) * k + p + lane];
+    else if (i == lane) v = 1.0f;   // pad beyond k with identity
+    c[i] = v;
   }
-  __syncthreads();
-  // Cholesky, column by column.
+  bool bad = false;
+#pragma unroll
   for (int j = 0; j < NB; ++j) {
-    float d = S[j][j];
-    __syncthreads();
+    float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c[j]), j));
     if (!(d > 0.0f)) {
-      if (tid == 0 && !bad) {
-        bad = 1;
-        if (*info == 0 && j < nb) *info = (int32_t)(p + j + 1);
-      }
+      if (!bad && j < nb && lane == 0 && *info == 0) *info = (int32_t)(p + j + 1);
+      bad = true;
       d = 1.0f;
     }
-    float sd = sqrtf(d);
-    for (int i = j + tid; i < NB; i += 256) S[i][j] = (i == j) ? sd : S[i][j] / sd;
+    const float sd = sqrtf(d), rs = 1.0f / sd;
+    if (lane == j) {
+      c[j] = sd;
+#pragma unroll
+      for (int i = j + 1; i < NB; ++i) {
+        c[i] *= rs;
+        colj[i] = c[i];
+      }
+    }
     __syncthreads();
-    for (int e = tid; e < NB * NB; e += 256) {
-      int i = e / NB, l = e % NB;
-      if (l > j && i >= l) S[i][l] = fmaf(-S[i][j], S[l][j], S[i][l]);
+    if (lane > j) {
+      const float cl = colj[lane];
+#pragma unroll
+      for (int i = j + 1; i < NB; ++i) c[i] = fmaf(-colj[i], cl, c[i]);
     }
     __syncthreads();
   }
-  // Inverse by forward substitution, one row of the inverse per step:
-  // X[j] = R[j] / L[j][j], then R[i] -= L[i][j] X[j] for i > j (R starts as I).
-  for (int j = 0; j < NB; ++j) {
-    float dinv = 1.0f / S[j][j];
-    for (int c = tid; c <= j; c += 256) X[j][c] *= dinv;
-    __syncthreads();
-    for (int e = tid; e < NB * NB; e += 256) {
-      int i = e / NB, c = e % NB;
-      if (i > j && c <= j) X[i][c] = fmaf(-S[i][j], X[j][c], X[i][c]);
+#pragma unroll
+  for (int i = 0; i < NB; ++i) Ls[i][lane] = (lane <= i) ? c[i] : 0.0f;
+  __syncthreads();
+  // Column `lane` of L^-1 (x reuses c's registers).
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    __builtin_amdgcn_sched_barrier(0);
+    float a0 = (i == lane) ? 1.0f : 0.0f, a1 = 0.0f;
+#pragma unroll
+    for (int l = 0; l + 1 < i; l += 2) {
+      a0 = fmaf(-Ls[i][l], c[l], a0);
+      a1 = fmaf(-Ls[i][l + 1], c[l + 1], a1);
     }
-    __syncthreads();
+    if (i & 1) a0 = fmaf(-Ls[i][i - 1], c[i - 1], a0);
+    c[i] = (a0 + a1) / Ls[i][i];
   }
-  for (int e = tid; e < NB * NB; e += 256) {
-    int r = e / NB, c = e % NB;
-    if (r < nb && c < nb) {
-      if (c <= r) A[(p + r) * k + p + c] = S[r][c];
-      Linv[(p + r) * k + p + c] = (c <= r) ? X[r][c] : 0.0f;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const float xv = (lane <= i) ? c[i] : 0.0f;   // L^-1[i][lane]
+    if (i < nb && lane < nb) {
+      if (lane <= i) A[(p + i) * k + p + lane] = Ls[i][lane];
+      Linv[(p + i) * k + p + lane] = xv;
     }
-    Dinv[r * NB + c] = (c <= r) ? X[r][c] : 0.0f;
+    Dinv[i * NB + lane] = xv;
   }
 }
 
@@ -148,7 +161,7 @@ hipError_t factor_hinv_launch(const float* H, int64_t k, float damp_rel, float* 
   if (e != hipSuccess) return e;
 
   for (int64_t p = 0; p < k; p += NB) {
-    hipLaunchKernelGGL(potf2_inv_kernel, dim3(1), dim3(256), 0, s, A, k, p, Linv, Dinv, info);
+    hipLaunchKernelGGL(potf2_inv_kernel, dim3(1), dim3(64), 0, s, A, k, p, Linv, Dinv, info);
     int64_t rest = k - p - NB;
     if (rest <= 0) break;
     // Panel below the block: A21 := A21 * Dinv^T (in place; one tile column).

@@ -2,8 +2,8 @@
 //
 // One 256-thread workgroup computes a 128x128 tile of C; its four waves hold
 // 64x64 sub-tiles as 2x2 MFMA 32x32 accumulators.  K is consumed in chunks of
-// 16 staged through LDS (A transposed so both operands are read as
-// [k][row/col] with one float per lane per MFMA).  Used for the GPTQ trailing
+// 32 staged through two LDS buffers (the next chunk is loaded into registers
+// while the current one is multiplied).  Used for the GPTQ trailing
 // update, the Cholesky panel/trailing updates, the triangular inverse and the
 // weighted error (row-dot epilogue).
 #include "common.h"
@@ -13,14 +13,65 @@ namespace nvq {
 
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 16, PAD = 4;
+constexpr int BM = 128, BN = 128, BK = 32;
+// LDS layouts.  An operand whose k index is contiguous in memory is kept as
+// [row][BK + 1] (scalar stores; the odd stride makes both the stores and the
+// MFMA reads of 32 consecutive rows conflict free); one whose row index is
+// contiguous is kept as [BK][128 + 4] (16-byte stores, conflict-free reads).
+constexpr int KSTRIDE = BK + 1;           // [row][k] layout
+constexpr int RSTRIDE = 128 + 4;          // [k][row] layout
+constexpr int OPER_FLOATS = 128 * KSTRIDE > BK * RSTRIDE ? 128 * KSTRIDE : BK * RSTRIDE;
+
+// Global -> registers for one operand tile of 128 rows x BK k-values.
+// kmajor: element (r, kk) at src[r * ld + kk] (k contiguous); otherwise at
+// src[kk * ld + r] (rows contiguous).  Each thread moves 4 float4.
+template <bool KMAJOR>
+__device__ __forceinline__ void load_tile(const float* __restrict__ src, int64_t ld, int64_t r0, int64_t nrows,
+                                          int64_t k0, int64_t K, int tid, f32x4 (&v)[4]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    int e = q * 256 + tid;
+    v[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (KMAJOR) {
+      int r = e >> 3, kk = (e & 7) * 4;            // 8 lanes cover 32 k of a row
+      int64_t gr = r0 + r, gk = k0 + kk;
+      if (gr < nrows && gk < K) v[q] = *(const f32x4*)(src + gr * ld + gk);
+    } else {
+      int kk = e >> 5, r = (e & 31) * 4;           // 32 lanes cover 128 rows of a k
+      int64_t gr = r0 + r, gk = k0 + kk;
+      if (gr < nrows && gk < K) v[q] = *(const f32x4*)(src + gk * ld + gr);
+    }
+  }
+}
+
+template <bool KMAJOR>
+__device__ __forceinline__ void store_tile(float* dst, int tid, const f32x4 (&v)[4]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    int e = q * 256 + tid;
+    if (KMAJOR) {
+      int r = e >> 3, kk = (e & 7) * 4;
+      float* d = dst + r * KSTRIDE + kk;
+      d[0] = v[q][0]; d[1] = v[q][1]; d[2] = v[q][2]; d[3] = v[q][3];
+    } else {
+      int kk = e >> 5, r = (e & 31) * 4;
+      *(f32x4*)(dst + kk * RSTRIDE + r) = v[q];
+    }
+  }
+}
+
+template <bool KMAJOR>
+__device__ __forceinline__ float read_operand(const float* tile, int row, int kk) {
+  return KMAJOR ? tile[row * KSTRIDE + kk] : tile[kk * RSTRIDE + row];
+}
 
 template <bool TA, bool TB, bool LOWER, int EPI>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
   if (LOWER && blockIdx.x > blockIdx.y) return;
-  __shared__ __attribute__((aligned(16))) float As[BK][BM + PAD];
-  __shared__ __attribute__((aligned(16))) float Bs[BK][BN + PAD];
-  __shared__ float red[BM][33];
+  // [buffer][A | B] operand tiles; reused by the row-dot epilogue.
+  __shared__ __attribute__((aligned(16))) float smem[2 * 2 * OPER_FLOATS];
+  constexpr bool AK = !TA;   // A stored [M][K]: k contiguous
+  constexpr bool BKM = TB;   // B stored [N][K]: k contiguous
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -39,65 +90,30 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  for (int64_t k0 = 0; k0 < p.K; k0 += BK) {
-    // ---- stage A tile (logical A'[i][kk], i in [m0, m0+128), kk in [k0, k0+16))
-    if (!TA) {
-      int i = tid >> 1, kk = (tid & 1) * 8;
-      int64_t gi = m0 + i;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        int64_t gk = k0 + kk + 4 * h;
-        f32x4 v = {0.f, 0.f, 0.f, 0.f};
-        if (gi < p.M && gk < p.K) v = *(const f32x4*)(A + gi * p.lda + gk);
-        As[kk + 4 * h + 0][i] = v[0];
-        As[kk + 4 * h + 1][i] = v[1];
-        As[kk + 4 * h + 2][i] = v[2];
-        As[kk + 4 * h + 3][i] = v[3];
-      }
-    } else {
-      int kk = tid >> 4, i = (tid & 15) * 8;
-      int64_t gk = k0 + kk;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        int64_t gi = m0 + i + 4 * h;
-        f32x4 v = {0.f, 0.f, 0.f, 0.f};
-        if (gi < p.M && gk < p.K) v = *(const f32x4*)(A + gk * p.lda + gi);
-        *(f32x4*)&As[kk][i + 4 * h] = v;
-      }
+  f32x4 ra[4], rb[4];
+  const int64_t nk = (p.K + BK - 1) / BK;
+  if (nk > 0) {
+    load_tile<AK>(A, p.lda, m0, p.M, 0, p.K, tid, ra);
+    load_tile<BKM>(B, p.ldb, n0, p.N, 0, p.K, tid, rb);
+    store_tile<AK>(smem, tid, ra);
+    store_tile<BKM>(smem + OPER_FLOATS, tid, rb);
+  }
+  __syncthreads();
+  for (int64_t c = 0; c < nk; ++c) {
+    const int cur = (int)(c & 1);
+    if (c + 1 < nk) {
+      load_tile<AK>(A, p.lda, m0, p.M, (c + 1) * BK, p.K, tid, ra);
+      load_tile<BKM>(B, p.ldb, n0, p.N, (c + 1) * BK, p.K, tid, rb);
     }
-    // ---- stage B tile (logical B'[kk][j])
-    if (!TB) {
-      int kk = tid >> 4, j = (tid & 15) * 8;
-      int64_t gk = k0 + kk;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        int64_t gj = n0 + j + 4 * h;
-        f32x4 v = {0.f, 0.f, 0.f, 0.f};
-        if (gj < p.N && gk < p.K) v = *(const f32x4*)(B + gk * p.ldb + gj);
-        *(f32x4*)&Bs[kk][j + 4 * h] = v;
-      }
-    } else {
-      int j = tid >> 1, kk = (tid & 1) * 8;
-      int64_t gj = n0 + j;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        int64_t gk = k0 + kk + 4 * h;
-        f32x4 v = {0.f, 0.f, 0.f, 0.f};
-        if (gj < p.N && gk < p.K) v = *(const f32x4*)(B + gj * p.ldb + gk);
-        Bs[kk + 4 * h + 0][j] = v[0];
-        Bs[kk + 4 * h + 1][j] = v[1];
-        Bs[kk + 4 * h + 2][j] = v[2];
-        Bs[kk + 4 * h + 3][j] = v[3];
-      }
-    }
-    __syncthreads();
+    const float* As = smem + cur * 2 * OPER_FLOATS;
+    const float* Bs = As + OPER_FLOATS;
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 2) {
       float a[2], b[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        a[t] = As[kk + (lane >> 5)][wr * 64 + t * 32 + (lane & 31)];
-        b[t] = Bs[kk + (lane >> 5)][wc * 64 + t * 32 + (lane & 31)];
+        a[t] = read_operand<AK>(As, wr * 64 + t * 32 + (lane & 31), kk + (lane >> 5));
+        b[t] = read_operand<BKM>(Bs, wc * 64 + t * 32 + (lane & 31), kk + (lane >> 5));
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -105,29 +121,40 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j], 0, 0, 0);
     }
+    if (c + 1 < nk) {
+      float* nxt = smem + (cur ^ 1) * 2 * OPER_FLOATS;
+      store_tile<AK>(nxt, tid, ra);
+      store_tile<BKM>(nxt + OPER_FLOATS, tid, rb);
+    }
     __syncthreads();
   }
 
   // Accumulator layout of a 32x32 MFMA tile: lane l, register r holds
   // row 8*(r/4) + 4*(l/32) + r%4, column l%32.
   if (EPI == kEpiAxpby) {
+    // Per 32x32 tile: read its 16 C values per lane, then store them (the
+    // compiler cannot prove that a store does not feed a later load, so
+    // interleaving them would serialize every load behind a store).
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        int64_t gj = n0 + wc * 64 + j * 32 + (lane & 31);
+        const int64_t gj = n0 + wc * 64 + j * 32 + (lane & 31);
+        float old[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           int64_t gi = m0 + wr * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          if (gi < p.M && gj < p.N) {
-            float v = p.alpha * acc[i][j][r];
-            if (p.beta != 0.0f) v = fmaf(p.beta, C[gi * p.ldc + gj], v);
-            C[gi * p.ldc + gj] = v;
-          }
+          old[r] = (p.beta != 0.0f && gi < p.M && gj < p.N) ? C[gi * p.ldc + gj] : 0.0f;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          int64_t gi = m0 + wr * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          if (gi < p.M && gj < p.N) C[gi * p.ldc + gj] = fmaf(p.beta, old[r], p.alpha * acc[i][j][r]);
         }
       }
   } else {
     // Row-dot: P[row, tile] = sum over the tile's columns of alpha*acc*D.
+    float (*red)[33] = (float (*)[33])smem;   // [128][33], operand tiles are dead here
     float part[2][16];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -142,7 +169,6 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
         }
         part[i][r] = s;
       }
-    // Each (row, wc) has 32 lanes of partials: write them and sum in a fixed order.
     for (int half = 0; half < 2; ++half) {
       if (wc == half) {
 #pragma unroll
@@ -158,7 +184,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
     }
     if (tid < BM) {
       float s = 0.0f;
-      for (int c = 0; c < 32; ++c) s += red[tid][c];
+      for (int c2 = 0; c2 < 32; ++c2) s += red[tid][c2];
       int64_t gi = m0 + tid;
       if (gi < p.M) p.P[gi * p.ldp + blockIdx.x] = s;
     }

@@ -10,15 +10,16 @@
 // the token range is split, partial tiles go to the workspace, and a second
 // kernel sums the splits in a fixed order, so results are reproducible.
 //
-// Operand staging.  X is row-major [tokens][channels] but an MFMA operand
-// needs 8 consecutive tokens of one channel per lane, so every 64-token stage
-// is transposed on the way into LDS: each thread loads 8 tokens x 4 channels
-// with 8-byte loads (coalesced along channels), regroups them with v_perm into
-// four 16-byte channel fragments and stores those into [channel][token] rows.
-// Rows are 128 bytes with the 16-byte slot index rotated by a function of the
-// channel, which keeps both the fragment stores and the MFMA operand reads
-// free of bank conflicts.  Two LDS buffers alternate so the global loads of
-// stage s+1 are in flight while stage s is multiplied.
+// Operand staging.  X is row-major [tokens][channels]; an MFMA operand needs
+// 8 consecutive tokens of one channel per lane.  Tokens are streamed in
+// 32-token stages through a ring of six LDS buffers filled by buffer loads
+// that write LDS directly (no registers, no per-load address arithmetic; the
+// buffer bound returns zeros past the last token).  The tile keeps X's layout,
+// [token][channel], and operands are fetched with ds_read_b64_tr_b16: within
+// each 16-lane group, lane j addresses token T + j/4, channels C + 4(j%4),
+// and lane i receives channel C + i for tokens T..T+3.  16-byte chunks of a
+// row are XOR-swizzled by the row index so that the transposed reads of 32
+// lanes hit 64 distinct banks.
 #include "common.h"
 #include "kernels.h"
 
@@ -26,11 +27,23 @@ namespace nvq {
 
 namespace {
 
-constexpr int ST = 64;        // tokens per stage
+constexpr int ST = 32;        // tokens per stage
+constexpr int NS = 6;         // ring depth (stages in flight + the one being multiplied)
 constexpr int TM = 128;       // rows (channels) of a job tile
 constexpr int SLOT_FLOATS = 128 * 256;
 
-__device__ __forceinline__ int rot(int c) { return (c + (c >> 3)) & 7; }
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+#define LDS_AS __attribute__((address_space(3)))
+
+// Physical 16-byte chunk of logical chunk p in tile row r, and its inverse.
+// g(p) = p ^ ((p & 2) << 2) moves chunk bit 1 into bit 3 (an involution);
+// the row index then XORs bits 1..3.
+__device__ __forceinline__ int swz(int p, int r) { return (p ^ ((p & 2) << 2)) ^ (2 * (r & 7)); }
+__device__ __forceinline__ int unswz(int pc, int r) {
+  const int y = pc ^ (2 * (r & 7));
+  return y ^ ((y & 2) << 2);
+}
 
 // (I, J) of pair job p: block row I, first block column J (covers J, J+1).
 __device__ __forceinline__ void pair_job(int p, int nb, int& I, int& J) {
@@ -44,13 +57,62 @@ __device__ __forceinline__ void pair_job(int p, int nb, int& I, int& J) {
 
 template <bool WIDE>
 struct Cfg {
-  static constexpr int TN = WIDE ? 256 : 128;              // columns of the job tile
-  static constexpr int UNITS = (TM / 4) * 8 + (TN / 4) * 8; // (quad, token-group) units
-  static constexpr int UPT = UNITS / 256;                    // units per thread
-  static constexpr int A_WORDS = TM * 32;                    // u32 words per stage
-  static constexpr int B_WORDS = TN * 32;
-  static constexpr int NJ = TN / 64;                         // 32-col MFMA tiles per wave
+  static constexpr int TN = WIDE ? 256 : 128;          // columns of the job tile
+  static constexpr int A_ROWB = TM * 2, B_ROWB = TN * 2; // bytes per token row
+  static constexpr int A_BYTES = ST * A_ROWB, B_BYTES = ST * B_ROWB;
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  static constexpr int INSTR = STAGE_BYTES / 1024;        // 1 KB direct-to-LDS loads per stage
+  static constexpr int PER_WAVE = INSTR / 4;
+  static constexpr int NJ = TN / 64;                      // 32-col MFMA tiles per wave
 };
+
+// Enqueue one stage's direct-to-LDS loads: the lane's 16-byte chunks of the
+// stage's token rows (voff: byte offsets from src) into the buffer at dst.
+// Offsets at or past nrec bytes read as zero.
+template <int PER_WAVE>
+__device__ __forceinline__ void issue_loads(char* dst, const void* src, int nrec, const uint32_t (&voff)[PER_WAVE],
+                                            const int (&ldsoff)[PER_WAVE]) {
+#if __HIP_DEVICE_COMPILE__   // buffer resources exist only in device code
+  __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, nrec, 0x00020000);
+#pragma unroll
+  for (int q = 0; q < PER_WAVE; ++q)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(dst + ldsoff[q]), 16, voff[q], 0, 0, 0);
+#endif
+}
+
+// One pipeline step: enqueue the direct-to-LDS loads of a later stage into
+// `dst` and multiply the stage already resident in `buf`.  The two slots never
+// overlap, which the restrict qualifiers state; the completion of the loads is
+// tracked by explicit vmcnt waits and a barrier in the caller, so the compiler
+// need not wait on them before the operand reads here.
+template <int NJ, int PER_WAVE, int A_ROWB, int B_ROWB>
+__device__ __forceinline__ void stage_step(char* __restrict__ dst, bool issue, const void* src, int nrec,
+                                           const uint32_t (&voff)[PER_WAVE], const int (&ldsoff)[PER_WAVE],
+                                           const char* __restrict__ buf, const int (&aoff)[2][2],
+                                           const int (&boff)[NJ][2], f32x16 (&acc)[2][NJ]) {
+  if (issue) issue_loads<PER_WAVE>(dst, src, nrec, voff, ldsoff);
+#pragma unroll
+  for (int kk = 0; kk < ST / 16; ++kk) {
+    bf16x8 a[2], b[NJ];
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(buf + aoff[f][0] + kk * 16 * A_ROWB));
+      s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(buf + aoff[f][1] + kk * 16 * A_ROWB));
+      a[f] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+#pragma unroll
+    for (int f = 0; f < NJ; ++f) {
+      s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(buf + boff[f][0] + kk * 16 * B_ROWB));
+      s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(buf + boff[f][1] + kk * 16 * B_ROWB));
+      b[f] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int f = 0; f < NJ; ++f)
+        acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[f], acc[i][f], 0, 0, 0);
+  }
+}
 
 template <bool WIDE>
 __global__ __launch_bounds__(256) void syrk_bf16_kernel(const uint16_t* __restrict__ X, int64_t n,
@@ -58,8 +120,7 @@ __global__ __launch_bounds__(256) void syrk_bf16_kernel(const uint16_t* __restri
                                                         float* __restrict__ partial, int nsplit,
                                                         int64_t split_tokens, int slot_base) {
   using C = Cfg<WIDE>;
-  extern __shared__ __attribute__((aligned(16))) uint32_t lds[];
-  constexpr int STAGE_WORDS = C::A_WORDS + C::B_WORDS;   // [A rows | B rows] per buffer
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
 
   const int nb = (int)((k + 127) / 128);
   int I, J;
@@ -72,117 +133,111 @@ __global__ __launch_bounds__(256) void syrk_bf16_kernel(const uint16_t* __restri
   const int64_t rowc0 = (int64_t)I * 128, colc0 = (int64_t)J * 128;
   const int64_t t_begin = (int64_t)blockIdx.y * split_tokens;
   const int64_t t_end = min(n, t_begin + split_tokens);
+  const int nstages = t_end > t_begin ? (int)((t_end - t_begin + ST - 1) / ST) : 0;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1;
 
-  // Per-unit source description (constant over stages).
-  int u_is_b[C::UPT], u_quad[C::UPT], u_tg[C::UPT];
-  const uint16_t* u_src[C::UPT];
-  bool u_chan_ok[C::UPT];
+  // This lane's source offset (bytes from the stage's first token row) for
+  // each of the wave's load instructions, and the LDS chunk it fills.
+  uint32_t voff[C::PER_WAVE];
+  int ldsoff[C::PER_WAVE];
 #pragma unroll
-  for (int u = 0; u < C::UPT; ++u) {
-    int gu = u * 256 + tid;
-    int isb = gu >= 256;
-    int lu = isb ? gu - 256 : gu;
-    int nq = isb ? C::TN / 4 : TM / 4;
-    u_is_b[u] = isb;
-    u_quad[u] = lu % nq;
-    u_tg[u] = lu / nq;
-    int64_t ch = (isb ? colc0 : rowc0) + 4 * u_quad[u];
-    u_chan_ok[u] = ch < k;
-    u_src[u] = X + ch;
+  for (int q = 0; q < C::PER_WAVE; ++q) {
+    const int ins = wave + 4 * q;                       // instruction index in the stage
+    const int off = ins * 1024 + lane * 16;             // byte offset in the stage buffer
+    const bool is_b = off >= C::A_BYTES;
+    const int toff = is_b ? off - C::A_BYTES : off;
+    const int rowb = is_b ? C::B_ROWB : C::A_ROWB;
+    const int r = toff / rowb, pc = (toff % rowb) / 16;
+    const int p = unswz(pc, r);                         // logical chunk: channels 8p..8p+7
+    const int64_t ch = (is_b ? colc0 : rowc0) + 8 * p;
+    voff[q] = (uint32_t)(r * ldx * 2 + ch * 2);
+    ldsoff[q] = ins * 1024;
   }
-
-  u32x2 pre[C::UPT][8];
-  auto load_stage = [&](int64_t t0) {
+  // Per-lane LDS byte offsets of the transposed operand reads, for each
+  // fragment f and half h (tokens 4h..4h+3 of the lane group's 8), k-step 0.
+  const int g = lane >> 4, j = lane & 15;
+  int aoff[2][2], boff[C::NJ][2];
 #pragma unroll
-    for (int u = 0; u < C::UPT; ++u)
+  for (int h = 0; h < 2; ++h) {
+    const int r = 8 * (g >> 1) + 4 * h + (j >> 2);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        int64_t t = t0 + u_tg[u] * 8 + i;
-        u32x2 v = {0u, 0u};
-        if (u_chan_ok[u] && t < t_end) v = *(const u32x2*)(u_src[u] + t * ldx);
-        pre[u][i] = v;
-      }
-  };
-  auto store_stage = [&](int buf) {
-#pragma unroll
-    for (int u = 0; u < C::UPT; ++u) {
-      uint32_t* base = lds + buf * STAGE_WORDS + (u_is_b[u] ? C::A_WORDS : 0);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        // channel c of the quad: low (c even) or high (c odd) half of word c/2
-        const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-        u32x4 f;
-#pragma unroll
-        for (int w = 0; w < 4; ++w)
-          f[w] = __builtin_amdgcn_perm(pre[u][2 * w + 1][c >> 1], pre[u][2 * w][c >> 1], sel);
-        int row = 4 * u_quad[u] + c;
-        int slot = (u_tg[u] + rot(row)) & 7;
-        *(u32x4*)(base + row * 32 + slot * 4) = f;
-      }
+    for (int f = 0; f < 2; ++f) {
+      const int ch = wr * 64 + f * 32 + 16 * (g & 1) + 4 * (j & 3);
+      aoff[f][h] = r * C::A_ROWB + swz(ch >> 3, r) * 16 + 8 * (j & 1);
     }
-  };
+#pragma unroll
+    for (int f = 0; f < C::NJ; ++f) {
+      const int ch = wc * (C::TN / 2) + f * 32 + 16 * (g & 1) + 4 * (j & 3);
+      boff[f][h] = C::A_BYTES + r * C::B_ROWB + swz(ch >> 3, r) * 16 + 8 * (j & 1);
+    }
+  }
 
   f32x16 acc[2][C::NJ];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int j = 0; j < C::NJ; ++j)
+    for (int f = 0; f < C::NJ; ++f)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+      for (int r = 0; r < 16; ++r) acc[i][f][r] = 0.0f;
 
-  const int nstages = (int)((t_end - t_begin + ST - 1) / ST);
-  if (nstages > 0) {
-    load_stage(t_begin);
-    store_stage(0);
+  for (int s = 0; s < NS - 1 && s < nstages; ++s) {
+    const int64_t t0 = t_begin + (int64_t)s * ST;
+    issue_loads<C::PER_WAVE>(lds + (s % NS) * C::STAGE_BYTES, (const void*)(X + t0 * ldx),
+                             (int)min((t_end - t0) * ldx * 2, (int64_t)0x7FFFFFF0), voff, ldsoff);
   }
-  __syncthreads();
   for (int s = 0; s < nstages; ++s) {
-    const int cur = s & 1;
-    if (s + 1 < nstages) load_stage(t_begin + (int64_t)(s + 1) * ST);
-    const uint32_t* A = lds + cur * STAGE_WORDS;
-    const uint32_t* B = A + C::A_WORDS;
-#pragma unroll
-    for (int kk = 0; kk < ST / 16; ++kk) {
-      const int tg = 2 * kk + (lane >> 5);
-      bf16x8 a[2], b[C::NJ];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        int row = wr * 64 + i * 32 + (lane & 31);
-        u32x4 w = *(const u32x4*)(A + row * 32 + ((tg + rot(row)) & 7) * 4);
-        a[i] = __builtin_bit_cast(bf16x8, w);
-      }
-#pragma unroll
-      for (int j = 0; j < C::NJ; ++j) {
-        int row = wc * (C::TN / 2) + j * 32 + (lane & 31);
-        u32x4 w = *(const u32x4*)(B + row * 32 + ((tg + rot(row)) & 7) * 4);
-        b[j] = __builtin_bit_cast(bf16x8, w);
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < C::NJ; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    // Wait until this wave's loads of stage s have landed (later stages may
+    // stay in flight), then make every wave's loads visible.
+    const int ahead = min(NS - 2, nstages - 1 - s);     // stages issued after s
+    switch (ahead * C::PER_WAVE) {
+#define NVQ_WAIT(N) case N: __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14)); break;
+      NVQ_WAIT(0) NVQ_WAIT(4) NVQ_WAIT(6) NVQ_WAIT(8) NVQ_WAIT(12) NVQ_WAIT(16) NVQ_WAIT(18) NVQ_WAIT(24)
+#undef NVQ_WAIT
+      default: __builtin_amdgcn_s_waitcnt(0); break;
     }
-    if (s + 1 < nstages) store_stage(cur ^ 1);
-    __syncthreads();
+    // Plain workgroup barrier (the memory clobber keeps the compiler from
+    // moving LDS accesses across it).  __syncthreads() would add a release
+    // fence that drains the loads of the stages still in flight.
+    asm volatile("s_barrier" ::: "memory");
+    const int sn = s + NS - 1;
+    const bool issue = sn < nstages;
+    const int64_t t0 = t_begin + (int64_t)sn * ST;
+    const int64_t rem = issue ? (t_end - t0) * ldx * 2 : 0;
+    stage_step<C::NJ, C::PER_WAVE, C::A_ROWB, C::B_ROWB>(lds + (sn % NS) * C::STAGE_BYTES, issue,
+                                                        (const void*)(X + (issue ? t0 : t_begin) * ldx),
+                                                        (int)min(rem, (int64_t)0x7FFFFFF0), voff, ldsoff,
+                                                        lds + (s % NS) * C::STAGE_BYTES, aoff, boff, acc);
   }
 
   // Epilogue.  Accumulator element (lane l, register r) of a 32x32 tile is at
   // row 8*(r/4) + 4*(l/32) + r%4, column l%32.
   if (nsplit == 1) {
+    // Read the old upper-triangle values first, then store (stores to H would
+    // otherwise serialize the loads behind them).
+    float old[2][C::NJ][16];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < C::NJ; ++j) {
-        int64_t gj = colc0 + wc * (C::TN / 2) + j * 32 + (lane & 31);
+      for (int f = 0; f < C::NJ; ++f) {
+        int64_t gj = colc0 + wc * (C::TN / 2) + f * 32 + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          int64_t gi = rowc0 + wr * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          old[i][f][r] = (gi < k && gj < k && gi <= gj) ? H[gi * k + gj] : 0.0f;
+        }
+      }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int f = 0; f < C::NJ; ++f) {
+        int64_t gj = colc0 + wc * (C::TN / 2) + f * 32 + (lane & 31);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           int64_t gi = rowc0 + wr * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
           if (gi < k && gj < k && gi <= gj) {
-            float v = H[gi * k + gj] + acc[i][j][r];
+            float v = old[i][f][r] + acc[i][f][r];
             H[gi * k + gj] = v;
             if (gi != gj) H[gj * k + gi] = v;
           }
@@ -193,12 +248,12 @@ __global__ __launch_bounds__(256) void syrk_bf16_kernel(const uint16_t* __restri
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < C::NJ; ++j) {
-        int col = wc * (C::TN / 2) + j * 32 + (lane & 31);
+      for (int f = 0; f < C::NJ; ++f) {
+        int col = wc * (C::TN / 2) + f * 32 + (lane & 31);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           int row = wr * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          P[row * 256 + col] = acc[i][j][r];
+          P[row * 256 + col] = acc[i][f][r];
         }
       }
   }
@@ -290,8 +345,8 @@ hipError_t syrk_bf16(const uint16_t* X, int64_t n, int64_t k, int64_t ldx, float
   if (n <= 0) return hipSuccess;
   SyrkPlan p = plan(n, k, num_cus());
   float* partial = (float*)ws;
-  const size_t lds_wide = 2 * (Cfg<true>::A_WORDS + Cfg<true>::B_WORDS) * sizeof(uint32_t);
-  const size_t lds_narrow = 2 * (Cfg<false>::A_WORDS + Cfg<false>::B_WORDS) * sizeof(uint32_t);
+  const size_t lds_wide = (size_t)NS * Cfg<true>::STAGE_BYTES;
+  const size_t lds_narrow = (size_t)NS * Cfg<false>::STAGE_BYTES;
   static bool attr = false;
   if (!attr) {
     (void)hipFuncSetAttribute((const void*)syrk_bf16_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
