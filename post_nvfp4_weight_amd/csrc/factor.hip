@@ -50,78 +50,120 @@ __global__ void flip_damp_kernel(const float* __restrict__ H, int64_t k, const f
 
 // Factor the 64x64 diagonal block at p in place (lower L), write its inverse
 // into Linv's diagonal block and into Dinv [64 x 64].  One wave; lane l keeps
-// column l of the block in registers.  Cholesky step j: lane j scales its
-// column and publishes it in LDS, every lane l > j subtracts L[l][j] times it.
-// The inverse is then solved column by column (lane c: L x = e_c) against an
-// LDS copy of L, one row per step.  Sets *info (once) on a non-positive pivot:
-// info = p + j + 1 is the order of the failing leading minor of A, i.e. of the
-// failing trailing minor of H + lam I.
+// column l of the whole symmetric block in registers (c[i] = S[i][l]).  At
+// step j the trailing block loses the rank-1 term S[:,j] S[j,:] / S[j][j]:
+// lane l's multiplier S[l][j] / S[j][j] is its own c[j] (symmetry) and the
+// broadcast S[i][j] comes from lane j by readlane, so a step needs no LDS and
+// no barrier; columns are scaled by 1/sqrt(pivot) once at the end.  The
+// inverse is then solved column by column (lane c: L x = e_c).  Sets *info
+// (once) on a non-positive pivot: info = p + j + 1 is the order of the failing
+// leading minor of A, i.e. of the failing trailing minor of H + lam I.
 __global__ __launch_bounds__(64) void potf2_inv_kernel(float* __restrict__ A, int64_t k, int64_t p,
                                                        float* __restrict__ Linv, float* __restrict__ Dinv,
                                                        int32_t* __restrict__ info) {
-  __shared__ __attribute__((aligned(16))) float colj[NB];
-  __shared__ __attribute__((aligned(16))) float Ls[NB][NB + 4];
   const int lane = threadIdx.x;
   const int nb = (int)min((int64_t)NB, k - p);
-  float c[NB];   // column `lane`: c[i] = A[i][lane] (lower part meaningful)
+  float c[NB];   // column `lane` of the symmetric block (only the lower part of A is stored)
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
+    const int r = i > lane ? i : lane, q = i > lane ? lane : i;
     float v = 0.0f;
-    if (i < nb && lane < nb && lane <= i) v = A[(p + i) * k + p + lane];
+    if (r < nb) v = A[(p + r) * k + p + q];
     else if (i == lane) v = 1.0f;   // pad beyond k with identity
     c[i] = v;
   }
   bool bad = false;
+  float piv = 1.0f;   // this lane's pivot S[lane][lane] at its step
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
+    __builtin_amdgcn_sched_barrier(0);   // keep each step's broadcasts within the step
     float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c[j]), j));
     if (!(d > 0.0f)) {
       if (!bad && j < nb && lane == 0 && *info == 0) *info = (int32_t)(p + j + 1);
       bad = true;
       d = 1.0f;
     }
-    const float sd = sqrtf(d), rs = 1.0f / sd;
-    if (lane == j) {
-      c[j] = sd;
+    if (lane == j) piv = d;
+    const float m = (lane > j) ? c[j] / d : 0.0f;
 #pragma unroll
-      for (int i = j + 1; i < NB; ++i) {
-        c[i] *= rs;
-        colj[i] = c[i];
-      }
+    for (int i = j + 1; i < NB; ++i) {
+      const float sij = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c[i]), j));
+      c[i] = fmaf(-sij, m, c[i]);
     }
-    __syncthreads();
-    if (lane > j) {
-      const float cl = colj[lane];
+  }
+  // L[i][lane] = c[i] / sqrt(piv) below the diagonal, sqrt(piv) on it.
+  const float sd = sqrtf(piv), rs = 1.0f / sd;
 #pragma unroll
-      for (int i = j + 1; i < NB; ++i) c[i] = fmaf(-colj[i], cl, c[i]);
-    }
-    __syncthreads();
+  for (int i = 0; i < NB; ++i) c[i] = (i > lane) ? c[i] * rs : (i == lane ? sd : 0.0f);
+  // Rows of L to registers (lane = row) through LDS, then L^-1 by forward
+  // elimination on [L | I]: after step j, row j of the unscaled inverse is
+  // final and rows below subtract L[i][j] / L[j][j] times it; each row is
+  // divided by its diagonal at the end.  Row j is broadcast by readlane.
+  __shared__ float Ls[NB][NB + 1];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) Ls[i][lane] = c[i];
+  __syncthreads();
+  float lrow[NB], x[NB];
+#pragma unroll
+  for (int q = 0; q < NB; ++q) {
+    lrow[q] = Ls[lane][q];
+    x[q] = (q == lane) ? 1.0f : 0.0f;
   }
 #pragma unroll
-  for (int i = 0; i < NB; ++i) Ls[i][lane] = (lane <= i) ? c[i] : 0.0f;
-  __syncthreads();
-  // Column `lane` of L^-1 (x reuses c's registers).
+  for (int j = 0; j < NB; ++j) {
+    const float ljj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lrow[j]), j));
+    const float f = (lane > j) ? lrow[j] / ljj : 0.0f;
 #pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    __builtin_amdgcn_sched_barrier(0);
-    float a0 = (i == lane) ? 1.0f : 0.0f, a1 = 0.0f;
-#pragma unroll
-    for (int l = 0; l + 1 < i; l += 2) {
-      a0 = fmaf(-Ls[i][l], c[l], a0);
-      a1 = fmaf(-Ls[i][l + 1], c[l + 1], a1);
+    for (int q = 0; q <= j; ++q) {
+      const float xj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x[q]), j));
+      x[q] = fmaf(-f, xj, x[q]);
     }
-    if (i & 1) a0 = fmaf(-Ls[i][i - 1], c[i - 1], a0);
-    c[i] = (a0 + a1) / Ls[i][i];
   }
+  const float rdiag = rs;   // 1 / L[lane][lane]
+#pragma unroll
+  for (int q = 0; q < NB; ++q) x[q] = (q <= lane) ? x[q] * rdiag : 0.0f;
+  // Transpose the inverse back through LDS so that stores are row-coalesced.
   __syncthreads();
 #pragma unroll
+  for (int q = 0; q < NB; ++q) Ls[lane][q] = x[q];
+  __syncthreads();
+  // Row-major writes: lane = column.
+#pragma unroll
   for (int i = 0; i < NB; ++i) {
-    const float xv = (lane <= i) ? c[i] : 0.0f;   // L^-1[i][lane]
+    const float xv = Ls[i][lane];
     if (i < nb && lane < nb) {
-      if (lane <= i) A[(p + i) * k + p + lane] = Ls[i][lane];
+      if (lane <= i) A[(p + i) * k + p + lane] = c[i];
       Linv[(p + i) * k + p + lane] = xv;
     }
     Dinv[i * NB + lane] = xv;
+  }
+}
+
+// Panel solve below a factored diagonal block: A21 := A21 * Dinv^T, where
+// Dinv = L11^-1 (64 x 64, lower).  Rows are independent: a workgroup takes 16
+// rows; thread t computes 4 of the 16 x 64 outputs.
+__global__ __launch_bounds__(256) void panel_solve_kernel(float* __restrict__ A, int64_t k, int64_t p,
+                                                          int64_t rows, const float* __restrict__ Dinv) {
+  __shared__ float D[NB][NB + 1];
+  __shared__ float R[16][NB + 1];
+  const int tid = threadIdx.x;
+  const int64_t r0 = (int64_t)blockIdx.x * 16;
+  for (int e = tid; e < NB * NB; e += 256) D[e / NB][e % NB] = Dinv[e];
+  for (int e = tid; e < 16 * NB; e += 256) {
+    const int r = e / NB, c = e % NB;
+    R[r][c] = (r0 + r < rows) ? A[(p + NB + r0 + r) * k + p + c] : 0.0f;
+  }
+  __syncthreads();
+  const int r = tid >> 4, cb = tid & 15;
+  float out[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int l = 0; l < NB; ++l) {
+    const float a = R[r][l];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) out[q] = fmaf(a, D[cb + 16 * q][l], out[q]);
+  }
+  if (r0 + r < rows) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) A[(p + NB + r0 + r) * k + p + cb + 16 * q] = out[q];
   }
 }
 
@@ -164,14 +206,8 @@ hipError_t factor_hinv_launch(const float* H, int64_t k, float damp_rel, float* 
     hipLaunchKernelGGL(potf2_inv_kernel, dim3(1), dim3(64), 0, s, A, k, p, Linv, Dinv, info);
     int64_t rest = k - p - NB;
     if (rest <= 0) break;
-    // Panel below the block: A21 := A21 * Dinv^T (in place; one tile column).
-    GemmArgs t{};
-    t.A = A + (p + NB) * k + p; t.lda = k;
-    t.B = Dinv; t.ldb = NB;
-    t.C = A + (p + NB) * k + p; t.ldc = k;
-    t.M = rest; t.N = NB; t.K = NB; t.batch = 1; t.alpha = 1.0f; t.beta = 0.0f;
-    e = gemm_f32(t, false, true, false, kEpiAxpby, s);
-    if (e != hipSuccess) return e;
+    // Panel below the block: A21 := A21 * Dinv^T.
+    hipLaunchKernelGGL(panel_solve_kernel, dim3((unsigned)((rest + 15) / 16)), dim3(256), 0, s, A, k, p, rest, Dinv);
     // Trailing update: A22 -= A21 A21^T (lower tiles).
     GemmArgs u{};
     u.A = A + (p + NB) * k + p; u.lda = k;

@@ -45,9 +45,10 @@ __device__ __forceinline__ void load_tile(const float* __restrict__ src, int64_t
 }
 
 template <bool KMAJOR>
-__device__ __forceinline__ void store_tile(float* dst, int tid, const f32x4 (&v)[4]) {
+__device__ __forceinline__ void store_tile(float* dst, int tid, f32x4 (&v)[4], float scale = 1.0f) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
+    if (scale != 1.0f) v[q] = v[q] * scale;
     int e = q * 256 + tid;
     if (KMAJOR) {
       int r = e >> 3, kk = (e & 7) * 4;
@@ -82,20 +83,37 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
   const float* B = p.B + z * p.sB;
   float* C = p.C + z * p.sC;
 
+  // Accumulator layout of a 32x32 MFMA tile: lane l, register r holds
+  // row 8*(r/4) + 4*(l/32) + r%4, column l%32.  With beta != 0 the tile of C
+  // is loaded into the accumulators up front (its latency overlaps the first
+  // operand loads) and alpha is applied to A on its way into LDS, so the
+  // epilogue only stores: C = beta*C + (alpha*A) op(B).
   f32x16 acc[2][2];
+  const bool load_c = EPI == kEpiAxpby && p.beta != 0.0f;
+  // Wave-uniform base of this wave's 64x64 sub-tile of C plus a 32-bit lane
+  // offset; a whole tile inside C needs no per-element bounds checks.
+  const int64_t wrow0 = m0 + wr * 64, wcol0 = n0 + wc * 64;
+  float* Cw = C + wrow0 * p.ldc + wcol0;
+  const int lane_off = 4 * (lane >> 5) * (int)p.ldc + (lane & 31);
+  const bool full = wrow0 + 64 <= p.M && wcol0 + 64 <= p.N;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+      for (int r = 0; r < 16; ++r) {
+        const int row = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3), col = j * 32 + (lane & 31);
+        const bool ok = full || (wrow0 + row < p.M && wcol0 + col < p.N);
+        acc[i][j][r] = (load_c && ok) ? p.beta * Cw[(i * 32 + 8 * (r >> 2) + (r & 3)) * p.ldc + j * 32 + lane_off] : 0.0f;
+      }
+  const float alpha_a = EPI == kEpiAxpby ? p.alpha : 1.0f;
 
   f32x4 ra[4], rb[4];
   const int64_t nk = (p.K + BK - 1) / BK;
   if (nk > 0) {
     load_tile<AK>(A, p.lda, m0, p.M, 0, p.K, tid, ra);
     load_tile<BKM>(B, p.ldb, n0, p.N, 0, p.K, tid, rb);
-    store_tile<AK>(smem, tid, ra);
+    store_tile<AK>(smem, tid, ra, alpha_a);
     store_tile<BKM>(smem + OPER_FLOATS, tid, rb);
   }
   __syncthreads();
@@ -123,35 +141,23 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
     }
     if (c + 1 < nk) {
       float* nxt = smem + (cur ^ 1) * 2 * OPER_FLOATS;
-      store_tile<AK>(nxt, tid, ra);
+      store_tile<AK>(nxt, tid, ra, alpha_a);
       store_tile<BKM>(nxt + OPER_FLOATS, tid, rb);
     }
     __syncthreads();
   }
 
-  // Accumulator layout of a 32x32 MFMA tile: lane l, register r holds
-  // row 8*(r/4) + 4*(l/32) + r%4, column l%32.
   if (EPI == kEpiAxpby) {
-    // Per 32x32 tile: read its 16 C values per lane, then store them (the
-    // compiler cannot prove that a store does not feed a later load, so
-    // interleaving them would serialize every load behind a store).
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int64_t gj = n0 + wc * 64 + j * 32 + (lane & 31);
-        float old[16];
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          int64_t gi = m0 + wr * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          old[r] = (p.beta != 0.0f && gi < p.M && gj < p.N) ? C[gi * p.ldc + gj] : 0.0f;
+          const int row = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3), col = j * 32 + (lane & 31);
+          if (full || (wrow0 + row < p.M && wcol0 + col < p.N))
+            Cw[(i * 32 + 8 * (r >> 2) + (r & 3)) * p.ldc + j * 32 + lane_off] = acc[i][j][r];
         }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          int64_t gi = m0 + wr * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          if (gi < p.M && gj < p.N) C[gi * p.ldc + gj] = fmaf(p.beta, old[r], p.alpha * acc[i][j][r]);
-        }
-      }
   } else {
     // Row-dot: P[row, tile] = sum over the tile's columns of alpha*acc*D.
     float (*red)[33] = (float (*)[33])smem;   // [128][33], operand tiles are dead here

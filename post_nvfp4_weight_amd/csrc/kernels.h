@@ -8,7 +8,8 @@
 
 namespace nvq {
 
-// ---- fp32 MFMA GEMM: C = alpha * op(A) op(B) + beta * C ---------------------
+// ---- fp32 MFMA GEMM: C = (alpha * op(A)) op(B) + beta * C --------------------
+// (alpha scales the A operand before the product: exact when alpha = +-1.)
 enum GemmEpi { kEpiAxpby = 0, kEpiRowDot = 1 };
 
 struct GemmArgs {

@@ -4,14 +4,14 @@
 // Sweep mapping.  Output rows are independent; inside a row the 16-column
 // blocks are processed in order.  One lane per (row, candidate): a row's G
 // candidate lanes (G = next power of two >= n_cand) replay the block in
-// registers, each with its own scale, reduce their scores with cross-lane
-// shuffles (ties to the lower candidate), and the winner publishes its codes,
-// scale and errors.  A workgroup owns ROWS rows of one 128-column lazy batch:
-// the rows' batch slab and the transposed 128x128 diagonal block of U live in
-// LDS, the 16x16 in-block factor entries are wave-uniform (scalar loads), and
-// after each block the row's G lanes update the later columns of the batch.
-// Columns beyond the batch are updated afterwards by one fp32 MFMA GEMM with
-// the batch's error slab.
+// registers, each with its own scale, reduce their scores with DPP lane
+// permutations (ties to the lower candidate), and the winner publishes its
+// codes, scale and errors.  A workgroup owns ROWS rows of one 128-column lazy
+// batch: the rows' batch slab, the transposed 128x128 diagonal block of U, its
+// eight 16x16 diagonal blocks and 1/U_jj live in LDS (the in-block factor
+// entries are read as wave-wide broadcasts), and after each block the row's G
+// lanes update the later columns of the batch.  Columns beyond the batch are
+// updated afterwards by one fp32 MFMA GEMM with the batch's error slab.
 #include "common.h"
 #include "kernels.h"
 
@@ -202,6 +202,40 @@ struct SweepCfg {
   static constexpr int THREADS = ROWS * G;
 };
 
+// One butterfly step of the candidate arg-min inside groups of G lanes
+// (ties to the lower candidate index).  DPP moves within 16-lane rows.
+template <int CTRL>
+__device__ __forceinline__ void argmin_step(float& s, int& i) {
+  const float so = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s), CTRL, 0xF, 0xF, false));
+  const int io = __builtin_amdgcn_mov_dpp(i, CTRL, 0xF, 0xF, false);
+  if (so < s || (so == s && io < i)) { s = so; i = io; }
+}
+template <int CTRL>
+__device__ __forceinline__ float sum_step(float s) {
+  return s + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s), CTRL, 0xF, 0xF, false));
+}
+// Lane pairings: xor 1 and xor 2 (quad_perm), then 8-lane and 16-lane mirrors.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+template <int G>
+__device__ __forceinline__ void group_argmin(float& s, int& i) {
+  if (G >= 2) argmin_step<kDppXor1>(s, i);
+  if (G >= 4) argmin_step<kDppXor2>(s, i);
+  if (G >= 8) argmin_step<kDppHalfMirror>(s, i);
+  if (G >= 16) argmin_step<kDppMirror>(s, i);
+}
+template <int G>
+__device__ __forceinline__ float group_sum(float s) {
+  if (G >= 2) s = sum_step<kDppXor1>(s);
+  if (G >= 4) s = sum_step<kDppXor2>(s);
+  if (G >= 8) s = sum_step<kDppHalfMirror>(s);
+  if (G >= 16) s = sum_step<kDppMirror>(s);
+  return s;
+}
+
+// A row's G candidate lanes always lie in one wave, so after the initial
+// loads the block loop needs no workgroup barrier: a wave's LDS accesses are
+// executed in program order.
 template <int G>
 __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
     float* __restrict__ Wp, const float* __restrict__ U, const float* __restrict__ invd,
@@ -210,7 +244,9 @@ __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
     float* __restrict__ row_loss) {
   constexpr int ROWS = SweepCfg<G>::ROWS;
   constexpr int NT = SweepCfg<G>::THREADS;
-  __shared__ __attribute__((aligned(16))) float Ut[kBatch * UT_LD];   // Ut[c][r] = U[i1+r][i1+c]
+  __shared__ __attribute__((aligned(16))) float Ut[kBatch * UT_LD];      // Ut[c][r] = U[i1+r][i1+c]
+  __shared__ __attribute__((aligned(16))) float Ud[kBatch / kBlock][kBlock][kBlock];  // diagonal 16x16 blocks
+  __shared__ __attribute__((aligned(16))) float id_s[kBatch];
   __shared__ __attribute__((aligned(16))) float slab[ROWS][kBatch];
   __shared__ __attribute__((aligned(16))) float eb_s[ROWS][16];
 
@@ -221,14 +257,16 @@ __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
   const float g = *gptr;
 
   for (int e = tid; e < kBatch * kBatch; e += NT) {
-    int r = e / kBatch, c = e % kBatch;
+    const int r = e / kBatch, c = e % kBatch;
     float v = 0.0f;
     if (r < ncols && c < ncols && r <= c) v = U[(int64_t)(i1 + r) * k + i1 + c];
     Ut[c * UT_LD + r] = v;
+    if ((r >> 4) == (c >> 4)) Ud[r >> 4][r & 15][c & 15] = v;
   }
+  for (int e = tid; e < kBatch; e += NT) id_s[e] = e < ncols ? invd[i1 + e] : 0.0f;
   for (int e = tid; e < ROWS * kBatch; e += NT) {
-    int r = e / kBatch, c = e % kBatch;
-    int64_t gr = (int64_t)blockIdx.x * ROWS + r;
+    const int r = e / kBatch, c = e % kBatch;
+    const int64_t gr = (int64_t)blockIdx.x * ROWS + r;
     slab[r][c] = (gr < m && c < ncols) ? Wp[gr * k + i1 + c] : 0.0f;
   }
   __syncthreads();
@@ -257,30 +295,30 @@ __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
       const int lo = candidate_lo(e4m3_code_of_ratio(a, g), n_cand);
       cand = lo + (ci < n_cand ? ci : 0);
       const float s = e4m3_value(cand);
-      const float* Ub = U + (int64_t)(i1 + c0) * k + (i1 + c0);
-      const float* id = invd + i1 + c0;
       float sc = 0.0f;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int code = e2m1_encode(v[j], s, g);
-        const float ej = (v[j] - e2m1_dequant(code, s, g)) * id[j];
+        const float ej = (v[j] - e2m1_dequant(code, s, g)) * id_s[c0 + j];
         sc = fmaf(ej, ej, sc);
+        if (j + 1 < 16) {
+          float urow[16];
 #pragma unroll
-        for (int l = j + 1; l < 16; ++l) v[l] = fmaf(-ej, Ub[(int64_t)j * k + l], v[l]);
+          for (int q = 0; q < 4; ++q) {
+            f32x4 t = *(const f32x4*)&Ud[b][j][4 * q];
+            urow[4 * q] = t[0]; urow[4 * q + 1] = t[1]; urow[4 * q + 2] = t[2]; urow[4 * q + 3] = t[3];
+          }
+#pragma unroll
+          for (int l = j + 1; l < 16; ++l) v[l] = fmaf(-ej, urow[l], v[l]);
+        }
         e[j] = ej;
         if (j < 8) plo |= (uint32_t)code << (4 * j); else phi |= (uint32_t)code << (4 * (j - 8));
       }
       if (ci < n_cand) score = sc;
     }
-    // Arg-min over the row's G lanes; ties to the lower candidate index.
     float bs = score;
     int bi = ci;
-#pragma unroll
-    for (int off = 1; off < G; off <<= 1) {
-      float so = __shfl_xor(bs, off, G);
-      int io = __shfl_xor(bi, off, G);
-      if (so < bs || (so == bs && io < bi)) { bs = so; bi = io; }
-    }
+    group_argmin<G>(bs, bi);
     if (ci == bi && row_ok) {
       *(f32x4*)&eb_s[rl][0] = f32x4{e[0], e[1], e[2], e[3]};
       *(f32x4*)&eb_s[rl][4] = f32x4{e[4], e[5], e[6], e[7]};
@@ -296,7 +334,6 @@ __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
       es[3] = f32x4{e[12], e[13], e[14], e[15]};
       if (a > 0.0f) loss += bs;
     }
-    __syncthreads();
     // Update the later columns of the batch: w'_l -= sum_j e_j U[c0+j][l].
     if (row_ok && c0 + kBlock < ncols) {
       float eb[16];
@@ -319,11 +356,9 @@ __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
         slab[rl][cc] = acc;
       }
     }
-    __syncthreads();
   }
   // Per-row loss: the winners' scores are spread over the row's lanes.
-#pragma unroll
-  for (int off = 1; off < G; off <<= 1) loss += __shfl_xor(loss, off, G);
+  loss = group_sum<G>(loss);
   if (ci == 0 && row_ok && row_loss) row_loss[row] += loss;
 }
 
