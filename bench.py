@@ -24,6 +24,15 @@ sys.path.insert(0, ROOT)
 M, K_IN, N_TOK, N_CAND = 4096, 4096, 262144, 16
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
+WORKLOAD = ("attention-projection layer W 4096x4096 bf16, X 262144x4096 bf16, 16 scale candidates per "
+            "16-block, lazy batch 128")
+
+# HBM traffic of the Hessian call, from rocprofv3 FETCH_SIZE / WRITE_SIZE passes
+# over this script, scaled by what the same counters read for the untimed
+# device copy of CAL_COPY_BYTES that main() runs after the timed steps.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hessian_accumulate_attn_proj_4096x4096_n262144_hbm_traffic.json")
+HESSIAN_SOURCES = [os.path.join(ROOT, "post_nvfp4_weight_amd", "csrc", f) for f in ("syrk.hip", "common.h")]
+CAL_COPY_BYTES = 512 << 20
 
 
 def log(*a):
@@ -67,13 +76,73 @@ def cpu_baseline():
                       f"H={t_h:.1f} factor={t_f:.1f} sweep={t_s:.1f}"}
 
 
+def hessian_source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for f in HESSIAN_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic():
+    """Measured HBM bytes per Hessian call, or None if absent or taken on other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            d = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_digest") != hessian_source_digest() or d.get("workload") != WORKLOAD:
+        return None
+    return d.get("hbm_bytes_per_call")
+
+
+def summarize_pmc(fetch_csv, write_csv):
+    """Per-call HBM bytes of hessian_accumulate from two rocprofv3 --pmc CSVs -> TRAFFIC_FILE."""
+    import csv
+
+    def per_dispatch(path, counter):
+        d = {}
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter:
+                    e = d.setdefault(r["Dispatch_Id"], [r["Kernel_Name"], 0.0])
+                    e[1] += float(r["Counter_Value"])
+        return list(d.values())
+
+    out = {"kernel": "hessian_accumulate (syrk_main_kernel + syrk_single_kernel + syrk_reduce_kernel)",
+           "workload": WORKLOAD, "source_digest": hessian_source_digest(), "unit": "bytes per call",
+           "calibration_copy_bytes": CAL_COPY_BYTES}
+    total = 0.0
+    for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = per_dispatch(path, name)
+        calls = sum(1 for n, _ in rows if "syrk_main_kernel" in n)
+        kib = sum(v for n, v in rows if "syrk_" in n) / max(1, calls)
+        copies = [v for n, v in rows if "bitwise_not" in n]
+        if not calls or not copies:
+            raise SystemExit(f"{path}: no Hessian or calibration-copy dispatches with {name}")
+        factor = (CAL_COPY_BYTES / 1024.0) / max(copies)
+        out[name] = {"kib_per_call": round(kib, 1), "copy_kib": round(max(copies), 1),
+                     "scale": round(factor, 4), "bytes_per_call": round(kib * 1024.0 * factor)}
+        total += kib * 1024.0 * factor
+    out["hbm_bytes_per_call"] = round(total)
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the Hessian's measured HBM traffic from two rocprofv3 --pmc CSVs and exit")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: the per-layer path is a single-GPU workload here "
               "(rows of W shard across ranks with no exchange; see DESIGN.md). Use --gpus 1.", file=sys.stderr)
@@ -125,8 +194,8 @@ def main():
 
     def step(ev=None):
         s = stream()
-        if ev: ev[0].record()
         H.zero_()
+        if ev: ev[0].record()
         chk("hessian", lib.hessian_accumulate(P(Xd), nvq.NVQ_DTYPE_BF16, N_TOK, K_IN, K_IN, P(H), P(ws["h"]),
                                               ws_h_n, s))
         if ev: ev[1].record()
@@ -164,7 +233,8 @@ def main():
     flops = N_TOK * K_IN * (K_IN + 1)
     achieved = flops / t_h / 1e12
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": load_traffic(),
+                "kernel": "hessian_accumulate", "ms_per_call": round(per_stage["hessian"], 4)}
 
     # Standalone RTN encode + pack of the same W (the no-update codec path).
     rtn_ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
@@ -178,13 +248,18 @@ def main():
     torch.cuda.synchronize()
     rtn_ms = rtn_ev[0].elapsed_time(rtn_ev[1]) / reps
 
+    # Untimed streaming kernel of known size (reads and writes CAL_COPY_BYTES):
+    # the calibration dispatch for rocprofv3's HBM byte counters (see summarize_pmc).
+    cal = torch.bitwise_not(Xd.view(torch.int32).reshape(-1)[:CAL_COPY_BYTES // 4])
+    torch.cuda.synchronize()
+    del cal
+
     out = {
         "metric": "quantized weights/sec (Mparam/s) per layer incl. Hessian",
         "value": round(value, 1), "unit": "Mparam/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16-mfma/fp32", "data": "synthetic",
-        "config": {"workload": "attention-projection layer W 4096x4096 bf16, X 262144x4096 bf16, 16 scale "
-                               "candidates per 16-block, lazy batch 128",
+        "config": {"workload": WORKLOAD,
                    "d_out": M, "d_in": K_IN, "tokens": N_TOK, "n_cand": N_CAND},
         "roofline": roofline,
         "stages_ms": {k: round(v, 3) for k, v in per_stage.items()},

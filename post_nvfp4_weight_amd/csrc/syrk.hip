@@ -10,12 +10,15 @@
 //   single  128x128: the bottom-right diagonal 128-block of a diagonal
 //           256-block (waves 64x64).
 // A quad moves 512 channels per token for 65536 products, a strip 384 for
-// 32768: the big tile halves the load traffic per flop.  Quads over half of
-// the tokens and strips over all of them are the same amount of work, so the
-// first launch runs both side by side (for a 4096-channel layer: 240 quad
-// halves + 16 strips = 256 equal items); the small singles follow, split over
-// tokens.  Split tiles write partial sums to the workspace, summed in a
-// fixed order by a second kernel, so results are reproducible.
+// 32768: the big tile halves the load traffic per flop.  The first launch
+// runs quads and strip pairs (two strips one after the other: the same work
+// as a quad), split over token ranges until there is an item per CU (for a
+// 4096-channel layer: 2 ranges x (120 quads + 8 strip pairs) = 256 items).
+// Items are ordered so that each XCD holds one token range and a compact
+// group of tiles, which keeps most operand reads inside its L2.  The small
+// singles follow in a second launch, split over tokens.  Split tiles write
+// partial sums to the workspace, summed in a fixed order by a reduction
+// kernel, so results are reproducible.
 //
 // Operand staging.  X is row-major [tokens][channels]; an MFMA operand needs
 // 8 consecutive tokens of one channel per lane.  Tokens are streamed in
@@ -27,6 +30,8 @@
 // and lane i receives channel C + i for tokens T..T+3.  16-byte chunks of a
 // row are XOR-swizzled by the row index so that the transposed reads of 32
 // lanes hit 64 distinct banks.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -81,40 +86,113 @@ __device__ __forceinline__ void issue_loads(char* dst, const void* src, int nrec
 #endif
 }
 
-// One pipeline step: enqueue the direct-to-LDS loads of a later stage into
-// `dst` and multiply the stage already resident in `buf`.  The two slots never
-// overlap, which the restrict qualifiers state; the completion of the loads is
-// tracked by explicit vmcnt waits and a barrier in the caller, so the compiler
-// need not wait on them before the operand reads here.
+// Operand fragments of k-step kk (16 tokens) of the stage in buf.
 template <int TM, int TN>
-__device__ __forceinline__ void stage_step(char* __restrict__ dst, bool issue, const void* src, int nrec,
-                                           const uint32_t (&voff)[Tile<TM, TN>::PER_WAVE],
-                                           const int (&ldsoff)[Tile<TM, TN>::PER_WAVE], const char* __restrict__ buf,
-                                           const int (&aoff)[Tile<TM, TN>::NI][2],
-                                           const int (&boff)[Tile<TM, TN>::NJ][2],
-                                           f32x16 (&acc)[Tile<TM, TN>::NI][Tile<TM, TN>::NJ]) {
+__device__ __forceinline__ void read_frags(const char* buf, int kk, const int (&aoff)[Tile<TM, TN>::NI][2],
+                                           const int (&boff)[Tile<TM, TN>::NJ][2], bf16x8 (&a)[Tile<TM, TN>::NI],
+                                           bf16x8 (&b)[Tile<TM, TN>::NJ]) {
   using T = Tile<TM, TN>;
-  if (issue) issue_loads<T::PER_WAVE>(dst, src, nrec, voff, ldsoff);
 #pragma unroll
-  for (int kk = 0; kk < ST / 16; ++kk) {
-    bf16x8 a[T::NI], b[T::NJ];
+  for (int f = 0; f < T::NI; ++f) {
+    s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(buf + aoff[f][0] + kk * 16 * T::A_ROWB));
+    s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(buf + aoff[f][1] + kk * 16 * T::A_ROWB));
+    a[f] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
 #pragma unroll
-    for (int f = 0; f < T::NI; ++f) {
-      s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(buf + aoff[f][0] + kk * 16 * T::A_ROWB));
-      s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(buf + aoff[f][1] + kk * 16 * T::A_ROWB));
-      a[f] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  for (int f = 0; f < T::NJ; ++f) {
+    s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(buf + boff[f][0] + kk * 16 * T::B_ROWB));
+    s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(buf + boff[f][1] + kk * 16 * T::B_ROWB));
+    b[f] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+}
+
+template <int TM, int TN>
+__device__ __forceinline__ void mfma_block(const bf16x8 (&a)[Tile<TM, TN>::NI], const bf16x8 (&b)[Tile<TM, TN>::NJ],
+                                           f32x16 (&acc)[Tile<TM, TN>::NI][Tile<TM, TN>::NJ]) {
+#pragma unroll
+  for (int i = 0; i < Tile<TM, TN>::NI; ++i)
+#pragma unroll
+    for (int f = 0; f < Tile<TM, TN>::NJ; ++f)
+      acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[f], acc[i][f], 0, 0, 0);
+}
+
+// Fragment f of k-step kk of the stage in buf: f < NI is A fragment f,
+// otherwise B fragment f - NI.
+template <int TM, int TN>
+__device__ __forceinline__ void read_one(const char* buf, int kk, int f, const int (&aoff)[Tile<TM, TN>::NI][2],
+                                         const int (&boff)[Tile<TM, TN>::NJ][2], bf16x8 (&a)[Tile<TM, TN>::NI],
+                                         bf16x8 (&b)[Tile<TM, TN>::NJ]) {
+  using T = Tile<TM, TN>;
+  if (f < T::NI) {
+    s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(buf + aoff[f][0] + kk * 16 * T::A_ROWB));
+    s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(buf + aoff[f][1] + kk * 16 * T::A_ROWB));
+    a[f] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  } else {
+    const int g = f - T::NI;
+    s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(buf + boff[g][0] + kk * 16 * T::B_ROWB));
+    s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(buf + boff[g][1] + kk * 16 * T::B_ROWB));
+    b[g] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+}
+
+// One stage's direct-to-LDS load q of this wave (see issue_loads).
+__device__ __forceinline__ void issue_load_one(char* dst, const void* src, int nrec, uint32_t voff, int ldsoff) {
+#if __HIP_DEVICE_COMPILE__
+  __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)src, (short)0, nrec, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(dst + ldsoff), 16, voff, 0, 0, 0);
+#endif
+}
+
+// One pipeline step over stage s, whose LDS slot is `slot`; on entry (a0, b0)
+// hold the operand fragments of its first k-step.  First half: the products
+// of the first k-step, interleaved with the reads of the second k-step's
+// fragments (one fragment per product, early in the half).  Then the wave
+// waits for those reads and for its own loads of stage s+1 (vmcnt <= WAIT)
+// and joins the workgroup barrier: every wave's loads of stage s+1 have
+// landed and every wave is done reading stage s.  Second half: the products
+// of the second k-step, interleaved with the refill of `slot` (direct-to-LDS
+// loads of stage s+NS, zero-length past the end, so every step issues the
+// same number of loads) and the reads of stage s+1's first fragments (from
+// `nxt` into (a0, b0)).  Scheduling fences keep this order, so the matrix
+// cores are never left waiting behind a burst of memory instructions.
+// `slot` and `nxt` are distinct, which the restrict qualifiers state: the
+// compiler then need not wait on the loads in flight before operand reads.
+template <int TM, int TN, int WAIT, bool has_next>
+__device__ __forceinline__ void pipe_step(char* __restrict__ slot, const char* __restrict__ nxt,
+                                          const void* src, int nrec, const uint32_t (&voff)[Tile<TM, TN>::PER_WAVE],
+                                          const int (&ldsoff)[Tile<TM, TN>::PER_WAVE],
+                                          const int (&aoff)[Tile<TM, TN>::NI][2],
+                                          const int (&boff)[Tile<TM, TN>::NJ][2], bf16x8 (&a0)[Tile<TM, TN>::NI],
+                                          bf16x8 (&b0)[Tile<TM, TN>::NJ],
+                                          f32x16 (&acc)[Tile<TM, TN>::NI][Tile<TM, TN>::NJ]) {
+  using T = Tile<TM, TN>;
+  static_assert(ST == 32, "two k-steps per stage");
+  constexpr int NM = T::NI * T::NJ, NF = T::NI + T::NJ, NL = T::PER_WAVE;
+  constexpr int N1 = NM > NF ? NM : NF;
+  constexpr int N2 = N1 > NL ? N1 : NL;
+  bf16x8 a1[T::NI], b1[T::NJ];
+#pragma unroll
+  for (int m = 0; m < N1; ++m) {
+    if (m < NF) read_one<TM, TN>(slot, 1, m, aoff, boff, a1, b1);
+    if (m < NM) acc[m / T::NJ][m % T::NJ] =
+        __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[m / T::NJ], b0[m % T::NJ], acc[m / T::NJ][m % T::NJ], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if constexpr (has_next) {
+    constexpr int w = WAIT;
+    __builtin_amdgcn_s_waitcnt((w & 15) | (7 << 4) | (0 << 8) | ((w >> 4) << 14));
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int m = 0; m < N2; ++m) {
+    if constexpr (has_next) {
+      if (m < NL) issue_load_one(slot, src, nrec, voff[m], ldsoff[m]);
+      if (m < NF) read_one<TM, TN>(nxt, 0, m, aoff, boff, a0, b0);
     }
-#pragma unroll
-    for (int f = 0; f < T::NJ; ++f) {
-      s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(buf + boff[f][0] + kk * 16 * T::B_ROWB));
-      s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(buf + boff[f][1] + kk * 16 * T::B_ROWB));
-      b[f] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    }
-#pragma unroll
-    for (int i = 0; i < T::NI; ++i)
-#pragma unroll
-      for (int f = 0; f < T::NJ; ++f)
-        acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[f], acc[i][f], 0, 0, 0);
+    if (m < NM) acc[m / T::NJ][m % T::NJ] =
+        __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[m / T::NJ], b1[m % T::NJ], acc[m / T::NJ][m % T::NJ], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -149,6 +227,14 @@ __device__ __forceinline__ void tile_job(char* lds, const uint16_t* __restrict__
     voff[q] = (uint32_t)(r * ldx * 2 + ch * 2);
     ldsoff[q] = ins * 1024;
   }
+  // Byte bound of the buffer that starts at stage `st` (0 past the end).
+  auto stage_nrec = [&](int st) -> int {
+    const int64_t t0 = t_begin + (int64_t)st * ST;
+    return st < nstages ? (int)min((t_end - t0) * ldx * 2, (int64_t)0x7FFFFFF0) : 0;
+  };
+  auto stage_src = [&](int st) -> const void* {
+    return (const void*)(X + (st < nstages ? t_begin + (int64_t)st * ST : t_begin) * ldx);
+  };
 
   // Per-lane LDS byte offsets of the transposed operand reads, for each
   // fragment f and half h (tokens 4h..4h+3 of the lane group's 8), k-step 0.
@@ -177,33 +263,29 @@ __device__ __forceinline__ void tile_job(char* lds, const uint16_t* __restrict__
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][f][r] = 0.0f;
 
-  for (int s = 0; s < NS - 1 && s < nstages; ++s) {
-    const int64_t t0 = t_begin + (int64_t)s * ST;
-    issue_loads<T::PER_WAVE>(lds + (s % NS) * T::STAGE_BYTES, (const void*)(X + t0 * ldx),
-                             (int)min((t_end - t0) * ldx * 2, (int64_t)0x7FFFFFF0), voff, ldsoff);
-  }
-  // Steady state: NS-2 later stages stay in flight while stage s is used.
+  // Prologue: fill every slot (zero-length loads past the end), then read
+  // stage 0's first fragments (the compiler also waits here for the other
+  // prologue loads).
+  for (int s = 0; s < NS; ++s)
+    issue_loads<T::PER_WAVE>(lds + s * T::STAGE_BYTES, stage_src(s), stage_nrec(s), voff, ldsoff);
+  bf16x8 a0[T::NI], b0[T::NJ];
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+  asm volatile("s_barrier" ::: "memory");
+  read_frags<TM, TN>(lds, 0, aoff, boff, a0, b0);
+  // Every step issues one stage of loads, so while the wave waits for stage
+  // s+1 the loads of stages s+2..s+NS-1 are the ones it leaves in flight.
   constexpr int kWait = (NS - 2) * T::PER_WAVE;
-  static_assert(kWait < 64, "vmcnt range");
-  auto step = [&](int s, bool steady) {
-    // Wait until this wave's loads of stage s have landed, then make every
-    // wave's loads visible with a plain workgroup barrier (the memory clobber
-    // keeps the compiler from moving LDS accesses across it; __syncthreads()
-    // would add a release fence that drains the stages still in flight).
-    if (steady) __builtin_amdgcn_s_waitcnt((kWait & 15) | (7 << 4) | (15 << 8) | ((kWait >> 4) << 14));
-    else __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
-    asm volatile("s_barrier" ::: "memory");
-    const int sn = s + NS - 1;
-    const bool issue = sn < nstages;
-    const int64_t t0 = t_begin + (int64_t)sn * ST;
-    const int64_t rem = issue ? (t_end - t0) * ldx * 2 : 0;
-    stage_step<TM, TN>(lds + (sn % NS) * T::STAGE_BYTES, issue, (const void*)(X + (issue ? t0 : t_begin) * ldx),
-                       (int)min(rem, (int64_t)0x7FFFFFF0), voff, ldsoff, lds + (s % NS) * T::STAGE_BYTES, aoff,
-                       boff, acc);
-  };
-  int s = 0;
-  for (; s + NS - 2 < nstages; ++s) step(s, true);    // stages s+1..s+NS-2 exist
-  for (; s < nstages; ++s) step(s, false);            // drain: wait for everything
+  static_assert(NS >= 2 && kWait < 64, "ring depth");
+  for (int s = 0; s + 1 < nstages; ++s) {
+    const int sn = s + NS;
+    pipe_step<TM, TN, kWait, true>(lds + (s % NS) * T::STAGE_BYTES, lds + ((s + 1) % NS) * T::STAGE_BYTES,
+                                   stage_src(sn), stage_nrec(sn), voff, ldsoff, aoff, boff, a0, b0, acc);
+  }
+  if (nstages > 0) {
+    const int s = nstages - 1;
+    pipe_step<TM, TN, kWait, false>(lds + (s % NS) * T::STAGE_BYTES, lds, stage_src(s), 0, voff, ldsoff, aoff, boff,
+                                    a0, b0, acc);
+  }
 
   // Epilogue.  Accumulator element (lane l, register r) of a 32x32 tile is at
   // row 8*(r/4) + 4*(l/32) + r%4, column l%32.
@@ -246,35 +328,85 @@ __device__ __forceinline__ void tile_job(char* lds, const uint16_t* __restrict__
   }
 }
 
-// Quad q (a < b over 256-blocks, row-major) -> (a, b).
-__device__ __forceinline__ void quad_coords(int q, int nb2, int& a, int& b) {
-  for (a = 0; a < nb2; ++a) {
-    const int cnt = nb2 - 1 - a;
-    if (q < cnt) { b = a + 1 + q; return; }
-    q -= cnt;
+// Order of the first launch's items within one token range.  256-blocks are
+// grouped into super-blocks of SB; for each super-block A in turn come the
+// quads inside A (row-major), then A's strips in pairs (2p, 2p+1), then the
+// quads of A against each later super-block B (row-major over A x B).  Runs
+// of consecutive items therefore touch few distinct 256-channel segments:
+// for a 4096-channel layer, each run of 32 items reads 8 or 12 of the 16.
+// Returns kind 0 (quad a < b), 1 (strip pair a, b; b = -1 if a is alone) or
+// -1 past the end.
+constexpr int SB = 8;
+__host__ __device__ inline void item_coords(int r, int nb2, int& kind, int& a, int& b) {
+  const int nsb = (nb2 + SB - 1) / SB;
+  for (int A = 0; A < nsb; ++A) {
+    const int a0 = A * SB, na = min(SB, nb2 - a0);
+    const int nq = na * (na - 1) / 2, np = (na + 1) / 2;
+    if (r < nq) {
+      int aa = 0;
+      while (r >= na - 1 - aa) { r -= na - 1 - aa; ++aa; }
+      kind = 0; a = a0 + aa; b = a0 + aa + 1 + r;
+      return;
+    }
+    r -= nq;
+    if (r < np) {
+      kind = 1; a = a0 + 2 * r; b = a + 1 < a0 + na ? a + 1 : -1;
+      return;
+    }
+    r -= np;
+    for (int B = A + 1; B < nsb; ++B) {
+      const int b0 = B * SB, nbb = min(SB, nb2 - b0);
+      if (r < na * nbb) {
+        kind = 0; a = a0 + r / nbb; b = b0 + r % nbb;
+        return;
+      }
+      r -= na * nbb;
+    }
   }
-  a = b = 0;
+  kind = -1; a = b = 0;
 }
 
-// Launch 1: items [0, nquad * qsplit) are quad token-splits (split-major: the
-// quads of token range 0 first), the next nb2 items are strips (all tokens).
+int items_per_range(int nb2) {
+  int nsp = 0;
+  for (int a0 = 0; a0 < nb2; a0 += SB) nsp += (min(SB, nb2 - a0) + 1) / 2;
+  return nb2 * (nb2 - 1) / 2 + nsp;
+}
+
+// Workgroups are dealt to the XCDs round-robin by id (id % 8).  Give each
+// XCD a contiguous run of logical items, so the items sharing an XCD's L2
+// share a token range and channel segments.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_logical(int id, int G) {
+  const int per = G / kXcds, rem = G % kXcds, x = id % kXcds, i = id / kXcds;
+  return (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + i;
+}
+
+// Launch 1: G = qsplit * per_range items; logical item L covers token range
+// L / per_range and item L % per_range of the order above.  A quad over one
+// range and a strip pair over one range are equal work.  With qsplit > 1 the
+// item's partial sums go to slot L (a strip pair's two 128x256 strips fill
+// the two halves of the slot).
 __global__ __launch_bounds__(256) void syrk_main_kernel(const uint16_t* __restrict__ X, int64_t n, int64_t k,
                                                         int64_t ldx, float* __restrict__ H,
-                                                        float* __restrict__ partial, int nquad, int qsplit,
+                                                        float* __restrict__ partial, int per_range, int qsplit,
                                                         int64_t qtokens) {
   extern __shared__ __attribute__((aligned(1024))) char lds[];
   const int nb2 = (int)((k + QUAD - 1) / QUAD);
-  const int item = blockIdx.x;
-  if (item < nquad * qsplit) {
-    const int sp = item / nquad, q = item % nquad;
-    int a, b;
-    quad_coords(q, nb2, a, b);
-    const int64_t t0 = (int64_t)sp * qtokens;
-    float* P = qsplit > 1 ? partial + (size_t)item * kSlotFloats : nullptr;
-    tile_job<QUAD, QUAD>(lds, X, k, ldx, (int64_t)a * QUAD, (int64_t)b * QUAD, t0, min(n, t0 + qtokens), H, P);
-  } else {
-    const int a = item - nquad * qsplit;
-    tile_job<HALF, QUAD>(lds, X, k, ldx, (int64_t)a * QUAD, (int64_t)a * QUAD, 0, n, H, nullptr);
+  const int L = xcd_logical(blockIdx.x, gridDim.x);
+  const int sp = L / per_range;
+  int kind, a, b;
+  item_coords(L % per_range, nb2, kind, a, b);
+  const int64_t t0 = (int64_t)sp * qtokens, t1 = min(n, t0 + qtokens);
+  float* P = qsplit > 1 ? partial + (size_t)L * kSlotFloats : nullptr;
+  if (kind == 0) {
+    tile_job<QUAD, QUAD>(lds, X, k, ldx, (int64_t)a * QUAD, (int64_t)b * QUAD, t0, t1, H, P);
+  } else if (kind == 1) {
+    tile_job<HALF, QUAD>(lds, X, k, ldx, (int64_t)a * QUAD, (int64_t)a * QUAD, t0, t1, H, P);
+    if (b >= 0) {
+      __syncthreads();   // the LDS ring is reused
+      tile_job<HALF, QUAD>(lds, X, k, ldx, (int64_t)b * QUAD, (int64_t)b * QUAD, t0, t1, H,
+                           P ? P + HALF * QUAD : nullptr);
+    }
   }
 }
 
@@ -292,33 +424,44 @@ __global__ __launch_bounds__(256) void syrk_single_kernel(const uint16_t* __rest
   tile_job<HALF, HALF>(lds, X, k, ldx, c0, c0, t0, min(n, t0 + stokens), H, P);
 }
 
-// Sum the token splits of a tile in split order and add into H (upper
-// triangle + mirror).  Partial slot of split sp of tile t:
-// slot_base + sp * sstride + t * tstride.
-__global__ __launch_bounds__(256) void syrk_reduce_kernel(int64_t k, float* __restrict__ H,
-                                                          const float* __restrict__ partial, int kind, int nsplit,
-                                                          size_t slot_base, size_t sstride, size_t tstride) {
-  const int nb2 = (int)((k + QUAD - 1) / QUAD);
-  int64_t r0, c0;
-  int TM, TN;
-  if (kind == 0) {
-    int a, b;
-    quad_coords(blockIdx.x, nb2, a, b);
-    r0 = (int64_t)a * QUAD; c0 = (int64_t)b * QUAD; TM = QUAD; TN = QUAD;
-  } else {
-    r0 = c0 = (int64_t)blockIdx.x * QUAD + HALF; TM = HALF; TN = HALF;
-  }
-  const float* P = partial + (slot_base + (size_t)blockIdx.x * tstride) * kSlotFloats;
+// Sum the token splits in split order and add into H (upper triangle +
+// mirror).  kind 0: blockIdx.x is item r of the first launch's order, whose
+// split sp sits in slot sp * per_range + r.  kind 1: blockIdx.x is single a,
+// whose split sp sits in slot slot_base + a * nsplit + sp.
+__device__ __forceinline__ void reduce_block(int64_t k, float* __restrict__ H, const float* __restrict__ P,
+                                             size_t sstride, int nsplit, int64_t r0, int64_t c0, int TM, int TN) {
   const int rows_per = TM / gridDim.y;
   for (int e = threadIdx.x; e < rows_per * TN; e += 256) {
     const int row = blockIdx.y * rows_per + e / TN, col = e % TN;
     const int64_t gi = r0 + row, gj = c0 + col;
     if (gi >= k || gj >= k || gi > gj) continue;
     float s = 0.0f;
-    for (int sp = 0; sp < nsplit; ++sp) s += P[(size_t)sp * sstride * kSlotFloats + row * TN + col];
+    for (int sp = 0; sp < nsplit; ++sp) s += P[(size_t)sp * sstride + row * TN + col];
     const float v = H[gi * k + gj] + s;
     H[gi * k + gj] = v;
     if (gi != gj) H[gj * k + gi] = v;
+  }
+}
+
+__global__ __launch_bounds__(256) void syrk_reduce_kernel(int64_t k, float* __restrict__ H,
+                                                          const float* __restrict__ partial, int kind, int nsplit,
+                                                          int per_range, size_t slot_base) {
+  const int nb2 = (int)((k + QUAD - 1) / QUAD);
+  if (kind == 0) {
+    int ik, a, b;
+    item_coords(blockIdx.x, nb2, ik, a, b);
+    const float* P = partial + (size_t)blockIdx.x * kSlotFloats;
+    const size_t sstride = (size_t)per_range * kSlotFloats;
+    if (ik == 0) {
+      reduce_block(k, H, P, sstride, nsplit, (int64_t)a * QUAD, (int64_t)b * QUAD, QUAD, QUAD);
+    } else if (ik == 1) {
+      reduce_block(k, H, P, sstride, nsplit, (int64_t)a * QUAD, (int64_t)a * QUAD, HALF, QUAD);
+      if (b >= 0) reduce_block(k, H, P + HALF * QUAD, sstride, nsplit, (int64_t)b * QUAD, (int64_t)b * QUAD, HALF, QUAD);
+    }
+  } else {
+    const int64_t c0 = (int64_t)blockIdx.x * QUAD + HALF;
+    const float* P = partial + (slot_base + (size_t)blockIdx.x * nsplit) * kSlotFloats;
+    reduce_block(k, H, P, kSlotFloats, nsplit, c0, c0, HALF, HALF);
   }
 }
 
@@ -328,7 +471,7 @@ __global__ void symmetrize_kernel(float* H, int64_t k) {
 }
 
 struct SyrkPlan {
-  int nb2, nquad, qsplit, nsingle, ssplit;
+  int nb2, per_range, qsplit, nsingle, ssplit;
   int64_t qtokens, stokens;
   size_t slots;
 };
@@ -347,17 +490,17 @@ int num_cus() {
 SyrkPlan plan(int64_t n, int64_t k, int cus) {
   SyrkPlan p;
   p.nb2 = (int)((k + QUAD - 1) / QUAD);
-  p.nquad = p.nb2 * (p.nb2 - 1) / 2;
+  p.per_range = items_per_range(p.nb2);
   p.nsingle = 0;
   for (int a = 0; a < p.nb2; ++a)
     if ((int64_t)a * QUAD + HALF < k) ++p.nsingle;
   int64_t nstages = (n + ST - 1) / ST;
   if (nstages < 1) nstages = 1;
-  // A quad over half the tokens and a strip are equal work.  Split the quads
-  // over tokens while the first launch would not give every CU an item.
+  // Split the first launch's items over token ranges while they would not
+  // give every CU an item.
   p.qsplit = 1;
-  if (p.nquad > 0 && p.nquad + p.nb2 < cus) {
-    int64_t s = (cus - p.nb2 + p.nquad - 1) / p.nquad;
+  if (p.per_range < cus) {
+    int64_t s = (cus + p.per_range - 1) / p.per_range;
     if (s > nstages) s = nstages;
     p.qsplit = (int)(s < 1 ? 1 : s);
   }
@@ -369,7 +512,7 @@ SyrkPlan plan(int64_t n, int64_t k, int cus) {
   }
   p.qtokens = ((nstages + p.qsplit - 1) / p.qsplit) * ST;
   p.stokens = ((nstages + p.ssplit - 1) / p.ssplit) * ST;
-  p.slots = (p.qsplit > 1 ? (size_t)p.nquad * p.qsplit : 0) + (p.ssplit > 1 ? (size_t)p.nsingle * p.ssplit : 0);
+  p.slots = (p.qsplit > 1 ? (size_t)p.per_range * p.qsplit : 0) + (p.ssplit > 1 ? (size_t)p.nsingle * p.ssplit : 0);
   return p;
 }
 
@@ -397,22 +540,21 @@ hipError_t syrk_bf16(const uint16_t* X, int64_t n, int64_t k, int64_t ldx, float
                               (int)lds_single);
     attr = true;
   }
-  const int items = p.nquad * p.qsplit + p.nb2;
-  hipLaunchKernelGGL(syrk_main_kernel, dim3(items), dim3(256), lds_main, s, X, n, k, ldx, H, partial, p.nquad,
+  const int items = p.per_range * p.qsplit;
+  hipLaunchKernelGGL(syrk_main_kernel, dim3(items), dim3(256), lds_main, s, X, n, k, ldx, H, partial, p.per_range,
                      p.qsplit, p.qtokens);
   size_t slot = 0;
   if (p.qsplit > 1) {
-    // split sp of quad q sits in slot sp * nquad + q
-    hipLaunchKernelGGL(syrk_reduce_kernel, dim3(p.nquad, 16), dim3(256), 0, s, k, H, partial, 0, p.qsplit, (size_t)0,
-                       (size_t)p.nquad, (size_t)1);
-    slot += (size_t)p.nquad * p.qsplit;
+    hipLaunchKernelGGL(syrk_reduce_kernel, dim3(p.per_range, 16), dim3(256), 0, s, k, H, partial, 0, p.qsplit,
+                       p.per_range, (size_t)0);
+    slot += (size_t)p.per_range * p.qsplit;
   }
   if (p.nsingle > 0) {
     hipLaunchKernelGGL(syrk_single_kernel, dim3(p.nsingle, p.ssplit), dim3(256), lds_single, s, X, n, k, ldx, H,
                        partial, p.ssplit, p.stokens, slot);
     if (p.ssplit > 1)
-      hipLaunchKernelGGL(syrk_reduce_kernel, dim3(p.nsingle, 8), dim3(256), 0, s, k, H, partial, 1, p.ssplit, slot,
-                         (size_t)1, (size_t)p.ssplit);
+      hipLaunchKernelGGL(syrk_reduce_kernel, dim3(p.nsingle, 8), dim3(256), 0, s, k, H, partial, 1, p.ssplit, 0,
+                         slot);
   }
   return hipGetLastError();
 }

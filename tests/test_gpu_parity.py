@@ -100,7 +100,7 @@ def _hessian_check(H_gpu, X, n):
     assert np.all(np.abs(H_gpu - ref) <= bound + 1e-30)
 
 
-@pytest.mark.parametrize("n,k", [(3000, 400), (700, 256), (64, 128), (5000, 1024)])
+@pytest.mark.parametrize("n,k", [(3000, 400), (700, 256), (64, 128), (5000, 1024), (1500, 2320), (777, 4096)])
 def test_hessian_bf16(nvq, n, k):
     X = synth.activations("attn_proj", n, k, massive=4)
     Xt = synth.to_bf16_tensor(X).to(DEV)
