@@ -25,7 +25,7 @@ def build(verbose=False, jobs=None):
     """Compile every source for gfx950 and link libnvq.so; raises on failure."""
     build_dir = os.path.join(HERE, "_build")
     os.makedirs(build_dir, exist_ok=True)
-    common = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}", "-I", os.path.join(ROOT, "include"),
+    common = ["-O3", "-fPIC", "-std=c++20", f"--offload-arch={ARCH}", "-I", os.path.join(ROOT, "include"),
               "-Wno-unused-result"]
     # Device code: no packed-fp32 instruction selection.
     device_flags = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -3,12 +3,15 @@
 // With J the index reversal, A = J (H + lam I) J = L L^T (lower Cholesky), and
 // R = J L J is upper with H + lam I = R R^T, so U = R^-1 = J L^-1 J.  The
 // library therefore factors the reversed matrix with a right-looking blocked
-// Cholesky (64-column panels: a one-workgroup panel factorization that also
-// inverts the 64x64 diagonal block, a GEMM for the panel below it and a
-// lower-triangular GEMM for the trailing update), inverts L by recursive
-// doubling (at each level, for every pair of adjacent diagonal blocks,
-// X21 = -L22^-1 L21 L11^-1 with two batched GEMMs) and finally writes
-// U[i][j] = L^-1[k-1-i][k-1-j].  Everything is fp32.
+// Cholesky (64-column panels: one launch factors the diagonal block and
+// solves the panel below it, one launch applies the lower-triangular
+// trailing update), inverts the 64x64 diagonal blocks of L in one batched
+// launch, completes L^-1 by recursive doubling (at each level, for every pair
+// of adjacent diagonal blocks, X21 = -L22^-1 L21 L11^-1 with two batched
+// GEMMs) and finally writes U[i][j] = L^-1[k-1-i][k-1-j].  Everything is
+// fp32.
+#include <utility>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -48,123 +51,276 @@ __global__ void flip_damp_kernel(const float* __restrict__ H, int64_t k, const f
   A[i * k + j] = v;
 }
 
-// Factor the 64x64 diagonal block at p in place (lower L), write its inverse
-// into Linv's diagonal block and into Dinv [64 x 64].  One wave; lane l keeps
-// column l of the whole symmetric block in registers (c[i] = S[i][l]).  At
-// step j the trailing block loses the rank-1 term S[:,j] S[j,:] / S[j][j]:
-// lane l's multiplier S[l][j] / S[j][j] is its own c[j] (symmetry) and the
-// broadcast S[i][j] comes from lane j by readlane, so a step needs no LDS and
-// no barrier; columns are scaled by 1/sqrt(pivot) once at the end.  The
-// inverse is then solved column by column (lane c: L x = e_c).  Sets *info
-// (once) on a non-positive pivot: info = p + j + 1 is the order of the failing
-// leading minor of A, i.e. of the failing trailing minor of H + lam I.
-__global__ __launch_bounds__(64) void potf2_inv_kernel(float* __restrict__ A, int64_t k, int64_t p,
-                                                       float* __restrict__ Linv, float* __restrict__ Dinv,
-                                                       int32_t* __restrict__ info) {
-  const int lane = threadIdx.x;
+// Lane n of each row of 16 lanes, broadcast to the row (DPP row_newbcast).
+template <int N>
+__device__ __forceinline__ float row_bcast(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + N, 0xF, 0xF, false));
+}
+
+// Cholesky factor (lower) and inverse of a 16 x 16 SPD block held as columns:
+// lane l (of each row of 16 lanes) enters with c[i] = S[i][l] and leaves with
+// c[i] = L[i][l] and x[i] = L^-1[i][l].  Column j's entries come to every
+// lane by row broadcast.  A non-positive pivot j is replaced by 1 and
+// reported in bad (the first such j), so the arithmetic stays finite.
+template <int J>
+__device__ __forceinline__ void chol16_step(float (&c)[16], int l, float& piv, int& bad) {
+  float d = row_bcast<J>(c[J]);
+  if (!(d > 0.0f)) {
+    if (bad < 0) bad = J;
+    d = 1.0f;
+  }
+  if (l == J) piv = d;
+  const float negm = (l > J) ? -(c[J] * __builtin_amdgcn_rcpf(d)) : 0.0f;
+#pragma unroll
+  for (int i = J + 1; i < 16; ++i) c[i] = fmaf(row_bcast<J>(c[i]), negm, c[i]);
+}
+template <int I>
+__device__ __forceinline__ void inv16_row(const float (&c)[16], float (&x)[16], int l, float rs) {
+  float acc = (I == l) ? 1.0f : 0.0f;
+  if constexpr (I > 0) {
+    [&]<int... M>(std::integer_sequence<int, M...>) {
+      ((acc = fmaf(-row_bcast<M>(c[I]), x[M], acc)), ...);
+    }(std::make_integer_sequence<int, I>{});
+  }
+  x[I] = acc * row_bcast<I>(rs);
+}
+__device__ __forceinline__ void chol_inv16(float (&c)[16], float (&x)[16], int l, int& bad) {
+  float piv = 1.0f;
+  [&]<int... J>(std::integer_sequence<int, J...>) {
+    (chol16_step<J>(c, l, piv, bad), ...);
+  }(std::make_integer_sequence<int, 16>{});
+  const float rs = __builtin_amdgcn_rsqf(piv), sd = piv * rs;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) c[i] = (i > l) ? c[i] * rs : (i == l ? sd : 0.0f);
+  [&]<int... I>(std::integer_sequence<int, I...>) {
+    (inv16_row<I>(c, x, l, rs), ...);
+  }(std::make_integer_sequence<int, 16>{});
+}
+
+// Panel p of the blocked Cholesky factorization (columns p .. p+nb-1 of the
+// lower factor).  Every workgroup factors the nb x nb diagonal block itself
+// (identical arithmetic, so identical results) and then solves its own 64
+// rows of the panel below it: L21 = A21 L11^-T.  Inside the workgroup the
+// block is factored in 16-column steps: one wave factors and inverts the
+// 16 x 16 diagonal sub-block in registers, then all waves apply the inverse
+// to the rows below it (the block's own rows and the panel rows) and subtract
+// the step's contribution from the columns to its right, each thread on a
+// 4 x 4 register tile.  Workgroup 0 stores L11 and, on a non-positive pivot,
+// sets *info (once) to the order of the failing leading minor of the
+// reversed matrix, i.e. of the failing trailing minor of H + lam I.
+constexpr int SP = NB + 1;   // LDS row stride of 64-wide blocks
+__global__ __launch_bounds__(256) void panel_kernel(float* __restrict__ A, int64_t k, int64_t p,
+                                                    int32_t* __restrict__ info) {
+  // Rows 0..63: the diagonal block (lower part; -> L11); rows 64..127: this
+  // workgroup's panel rows (-> L21 rows).
+  __shared__ float V[2 * NB][SP];
+  __shared__ float Li[16][17];   // inverse of the current 16 x 16 diagonal sub-block
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nb = (int)min((int64_t)NB, k - p);
-  float c[NB];   // column `lane` of the symmetric block (only the lower part of A is stored)
+  const int64_t r0 = (int64_t)blockIdx.x * NB;
+  const int rows = (int)max((int64_t)0, min((int64_t)NB, k - p - nb - r0));
+  // All loads first (16-byte, clamped to valid rows), then the LDS writes.
+  f32x4 ld[8];
 #pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    const int r = i > lane ? i : lane, q = i > lane ? lane : i;
-    float v = 0.0f;
-    if (r < nb) v = A[(p + r) * k + p + q];
-    else if (i == lane) v = 1.0f;   // pad beyond k with identity
-    c[i] = v;
+  for (int q = 0; q < 8; ++q) {
+    const int e = tid + 256 * (q & 3), i = e >> 4, j4 = (e & 15) * 4;
+    const int64_t row = q < 4 ? p + min(i, nb - 1) : p + nb + r0 + min(i, max(rows - 1, 0));
+    ld[q] = (q < 4 || rows > 0) ? *(const f32x4*)(A + row * k + p + j4) : f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  bool bad = false;
-  float piv = 1.0f;   // this lane's pivot S[lane][lane] at its step
 #pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    __builtin_amdgcn_sched_barrier(0);   // keep each step's broadcasts within the step
-    float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c[j]), j));
-    if (!(d > 0.0f)) {
-      if (!bad && j < nb && lane == 0 && *info == 0) *info = (int32_t)(p + j + 1);
-      bad = true;
-      d = 1.0f;
-    }
-    if (lane == j) piv = d;
-    const float m = (lane > j) ? c[j] / d : 0.0f;
+  for (int q = 0; q < 8; ++q) {
+    const int e = tid + 256 * (q & 3), i = e >> 4, j4 = (e & 15) * 4;
 #pragma unroll
-    for (int i = j + 1; i < NB; ++i) {
-      const float sij = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(c[i]), j));
-      c[i] = fmaf(-sij, m, c[i]);
+    for (int u = 0; u < 4; ++u) {
+      const int j = j4 + u;
+      float v;
+      if (q < 4) v = (i < nb && j < nb) ? (j <= i ? ld[q][u] : 0.0f) : (i == j ? 1.0f : 0.0f);
+      else v = (i < rows && j < nb) ? ld[q][u] : 0.0f;
+      V[q < 4 ? i : NB + i][j] = v;
     }
   }
-  // L[i][lane] = c[i] / sqrt(piv) below the diagonal, sqrt(piv) on it.
-  const float sd = sqrtf(piv), rs = 1.0f / sd;
-#pragma unroll
-  for (int i = 0; i < NB; ++i) c[i] = (i > lane) ? c[i] * rs : (i == lane ? sd : 0.0f);
-  // Rows of L to registers (lane = row) through LDS, then L^-1 by forward
-  // elimination on [L | I]: after step j, row j of the unscaled inverse is
-  // final and rows below subtract L[i][j] / L[j][j] times it; each row is
-  // divided by its diagonal at the end.  Row j is broadcast by readlane.
-  __shared__ float Ls[NB][NB + 1];
-#pragma unroll
-  for (int i = 0; i < NB; ++i) Ls[i][lane] = c[i];
   __syncthreads();
-  float lrow[NB], x[NB];
+  int first_bad = 0;
+  for (int b = 0; b < NB / 16; ++b) {
+    const int o = 16 * b;
+    if (wave == 0) {
+      const int l = lane & 15;
+      float c[16], x[16];
 #pragma unroll
-  for (int q = 0; q < NB; ++q) {
-    lrow[q] = Ls[lane][q];
-    x[q] = (q == lane) ? 1.0f : 0.0f;
-  }
+      for (int i = 0; i < 16; ++i) c[i] = i >= l ? V[o + i][o + l] : V[o + l][o + i];
+      int bad = -1;
+      chol_inv16(c, x, l, bad);
+      if (bad >= 0 && first_bad == 0 && o + bad < nb) first_bad = (int)(p + o + bad + 1);
+      if (lane < 16) {
 #pragma unroll
-  for (int j = 0; j < NB; ++j) {
-    const float ljj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lrow[j]), j));
-    const float f = (lane > j) ? lrow[j] / ljj : 0.0f;
-#pragma unroll
-    for (int q = 0; q <= j; ++q) {
-      const float xj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x[q]), j));
-      x[q] = fmaf(-f, xj, x[q]);
+        for (int i = 0; i < 16; ++i) {
+          if (i >= lane) V[o + i][o + lane] = c[i];
+          Li[i][lane] = x[i];
+        }
+      }
     }
-  }
-  const float rdiag = rs;   // 1 / L[lane][lane]
+    __syncthreads();
+    // Rows below the sub-block: V rows o+16 .. 127 (the block's rows, then the
+    // panel rows).  Columns o..o+15 := V * Li^T on 4 x 4 tiles.
+    const int rbase = o + 16, nrow = 2 * NB - rbase, nS = NB - rbase;
+    const int ntile_b = (nrow / 4) * 4;
+    float outb[2][4][4];
 #pragma unroll
-  for (int q = 0; q < NB; ++q) x[q] = (q <= lane) ? x[q] * rdiag : 0.0f;
-  // Transpose the inverse back through LDS so that stores are row-coalesced.
-  __syncthreads();
+    for (int q = 0; q < 2; ++q) {
+      const int t = tid + 256 * q;
+      if (t < ntile_b) {
+        const int r = rbase + 4 * (t >> 2), c0 = 4 * (t & 3);
+        float a[4][16];
 #pragma unroll
-  for (int q = 0; q < NB; ++q) Ls[lane][q] = x[q];
-  __syncthreads();
-  // Row-major writes: lane = column.
+        for (int ri = 0; ri < 4; ++ri)
 #pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    const float xv = Ls[i][lane];
-    if (i < nb && lane < nb) {
-      if (lane <= i) A[(p + i) * k + p + lane] = c[i];
-      Linv[(p + i) * k + p + lane] = xv;
+          for (int m = 0; m < 16; ++m) a[ri][m] = (m < c0 + 4) ? V[r + ri][o + m] : 0.0f;
+#pragma unroll
+        for (int cj = 0; cj < 4; ++cj) {
+          float li[16];
+#pragma unroll
+          for (int m = 0; m < 16; ++m) li[m] = (m <= c0 + cj) ? Li[c0 + cj][m] : 0.0f;
+#pragma unroll
+          for (int ri = 0; ri < 4; ++ri) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int m = 0; m < 16; ++m) acc = fmaf(a[ri][m], li[m], acc);
+            outb[q][ri][cj] = acc;
+          }
+        }
+      }
     }
-    Dinv[i * NB + lane] = xv;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int t = tid + 256 * q;
+      if (t < ntile_b) {
+        const int r = rbase + 4 * (t >> 2), c0 = 4 * (t & 3);
+#pragma unroll
+        for (int ri = 0; ri < 4; ++ri)
+#pragma unroll
+          for (int cj = 0; cj < 4; ++cj) V[r + ri][o + c0 + cj] = outb[q][ri][cj];
+      }
+    }
+    __syncthreads();
+    // Columns right of the step (rbase .. 63): V[r][j] -= V[r][o:o+16] . L[j][o:o+16]
+    // for every row below, on 4 x 4 tiles (entries above the diagonal of the
+    // block are computed too and never read).
+    if (nS > 0) {
+      const int ncg = nS / 4, ntile_c = (nrow / 4) * ncg;
+      for (int t = tid; t < ntile_c; t += 256) {
+        const int r = rbase + 4 * (t / ncg), j0 = rbase + 4 * (t % ncg);
+        float a[4][16], w[4][16];
+#pragma unroll
+        for (int ri = 0; ri < 4; ++ri)
+#pragma unroll
+          for (int m = 0; m < 16; ++m) {
+            a[ri][m] = V[r + ri][o + m];
+            w[ri][m] = V[j0 + ri][o + m];
+          }
+#pragma unroll
+        for (int ri = 0; ri < 4; ++ri)
+#pragma unroll
+          for (int cj = 0; cj < 4; ++cj) {
+            float acc = V[r + ri][j0 + cj];
+#pragma unroll
+            for (int m = 0; m < 16; ++m) acc = fmaf(-a[ri][m], w[cj][m], acc);
+            V[r + ri][j0 + cj] = acc;
+          }
+      }
+    }
+    __syncthreads();
+  }
+  // 16-byte stores; the diagonal block's upper triangle is written as zeros.
+  if (blockIdx.x == 0 && tid == 0 && first_bad != 0 && *info == 0) *info = first_bad;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int e = tid + 256 * (q & 3), i = e >> 4, j4 = (e & 15) * 4;
+    if (q < 4 ? (blockIdx.x != 0 || i >= nb) : i >= rows) continue;
+    f32x4 v;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = (q < 4 && j4 + u > i) ? 0.0f : V[q < 4 ? i : NB + i][j4 + u];
+    *(f32x4*)(A + (q < 4 ? p + i : p + nb + r0 + i) * k + p + j4) = v;
   }
 }
 
-// Panel solve below a factored diagonal block: A21 := A21 * Dinv^T, where
-// Dinv = L11^-1 (64 x 64, lower).  Rows are independent: a workgroup takes 16
-// rows; thread t computes 4 of the 16 x 64 outputs.
-__global__ __launch_bounds__(256) void panel_solve_kernel(float* __restrict__ A, int64_t k, int64_t p,
-                                                          int64_t rows, const float* __restrict__ Dinv) {
-  __shared__ float D[NB][NB + 1];
-  __shared__ float R[16][NB + 1];
-  const int tid = threadIdx.x;
-  const int64_t r0 = (int64_t)blockIdx.x * 16;
-  for (int e = tid; e < NB * NB; e += 256) D[e / NB][e % NB] = Dinv[e];
-  for (int e = tid; e < 16 * NB; e += 256) {
-    const int r = e / NB, c = e % NB;
-    R[r][c] = (r0 + r < rows) ? A[(p + NB + r0 + r) * k + p + c] : 0.0f;
+// Trailing update after panel p: C -= P P^T on the lower triangle, where P
+// is the panel's L21 (rest x 64, at A + (p+64) k + p) and C the trailing
+// block (rest x rest, at A + (p+64)(k+1)).  One workgroup per 64 x 64 lower
+// tile; each wave holds a 32 x 32 quadrant in MFMA accumulators initialized
+// from C, and multiplies -P_i by P_j^T (v_mfma_f32_32x32x2f32, K = 64).
+constexpr int UP = NB + 2;   // LDS row stride: a lane's (row, k) reads hit 64 distinct banks
+__global__ __launch_bounds__(256) void chol_update_kernel(float* __restrict__ A, int64_t k, int64_t p,
+                                                          int64_t rest) {
+  __shared__ float Pi[NB][UP], Pj[NB][UP];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // Tile t -> (ti, tj), tj <= ti, row-major over the lower triangle of tiles.
+  const int64_t t = blockIdx.x;
+  int64_t ti = (int64_t)((sqrt(8.0 * (double)t + 1.0) - 1.0) * 0.5);
+  while (ti * (ti + 1) / 2 > t) --ti;
+  while ((ti + 1) * (ti + 2) / 2 <= t) ++ti;
+  const int64_t tj = t - ti * (ti + 1) / 2;
+  const float* P = A + (p + NB) * k + p;
+  float* C = A + (p + NB) * k + p + NB;
+  for (int e = tid; e < NB * NB / 4; e += 256) {
+    const int r = e / (NB / 4), c4 = (e % (NB / 4)) * 4;
+    const int64_t gi = ti * NB + r, gj = tj * NB + r;
+    f32x4 vi = gi < rest ? *(const f32x4*)(P + gi * k + c4) : f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 vj = gj < rest ? *(const f32x4*)(P + gj * k + c4) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) { Pi[r][c4 + q] = -vi[q]; Pj[r][c4 + q] = vj[q]; }
+  }
+  const int wr = wave >> 1, wc = wave & 1;
+  const int64_t col = tj * NB + wc * 32 + (lane & 31);
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int64_t row = ti * NB + wr * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+    acc[r] = (row < rest && col < rest && col <= row) ? C[row * k + col] : 0.0f;
   }
   __syncthreads();
-  const int r = tid >> 4, cb = tid & 15;
-  float out[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int l = 0; l < NB; ++l) {
-    const float a = R[r][l];
+  const float* pa = &Pi[wr * 32 + (lane & 31)][lane >> 5];
+  const float* pb = &Pj[wc * 32 + (lane & 31)][lane >> 5];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) out[q] = fmaf(a, D[cb + 16 * q][l], out[q]);
-  }
-  if (r0 + r < rows) {
+  for (int kk = 0; kk < NB; kk += 2) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(pa[kk], pb[kk], acc, 0, 0, 0);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) A[(p + NB + r0 + r) * k + p + cb + 16 * q] = out[q];
+  for (int r = 0; r < 16; ++r) {
+    const int64_t row = ti * NB + wr * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+    if (row < rest && col < rest && col <= row) C[row * k + col] = acc[r];
   }
+}
+
+// Inverses of the diagonal 64-blocks of L (one wave each) into Linv: lane c
+// keeps column c of the block and solves L x = e_c by forward substitution;
+// row i of L comes to every lane by readlane.
+__global__ __launch_bounds__(64) void diag_inv_kernel(const float* __restrict__ A, int64_t k,
+                                                      float* __restrict__ Linv) {
+  const int lane = threadIdx.x;
+  const int64_t p = (int64_t)blockIdx.x * NB;
+  const int nb = (int)min((int64_t)NB, k - p);
+  float c[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    float v = (i == lane) ? 1.0f : 0.0f;
+    if (i < nb && lane < nb && lane <= i) v = A[(p + i) * k + p + lane];
+    c[i] = v;
+  }
+  float inv_own = 0.0f;   // 1 / L[lane][lane]
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+    if (i == lane) inv_own = 1.0f / c[i];
+  float x[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    float acc = (i == lane) ? 1.0f : 0.0f;
+#pragma unroll
+    for (int m = 0; m < i; ++m)
+      acc = fmaf(-__int_as_float(__builtin_amdgcn_readlane(__float_as_int(c[i]), m)), x[m], acc);
+    x[i] = acc * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(inv_own), i));
+  }
+#pragma unroll
+  for (int i = 0; i < NB; ++i)
+    if (i < nb && lane < nb) Linv[(p + i) * k + p + lane] = x[i];
 }
 
 // U[i][j] = Linv[k-1-i][k-1-j] for j >= i, 0 below the diagonal.
@@ -182,8 +338,8 @@ __global__ void zero_kernel(float* p, int64_t n) {
 }  // namespace
 
 size_t factor_workspace(int64_t k) {
-  // A (k^2), Linv (k^2), T (k^2 / 2), Dinv (64^2), lam (64 floats)
-  return ((size_t)k * k * 2 + (size_t)k * k / 2 + NB * NB + 64) * sizeof(float);
+  // A (k^2), Linv (k^2), T (k^2 / 2), lam (64 floats)
+  return ((size_t)k * k * 2 + (size_t)k * k / 2 + 64) * sizeof(float);
 }
 
 hipError_t factor_hinv_launch(const float* H, int64_t k, float damp_rel, float* U, float* lambda_out,
@@ -191,8 +347,7 @@ hipError_t factor_hinv_launch(const float* H, int64_t k, float damp_rel, float* 
   float* A = (float*)ws;
   float* Linv = A + (size_t)k * k;
   float* T = Linv + (size_t)k * k;
-  float* Dinv = T + (size_t)k * k / 2;
-  float* lam = Dinv + NB * NB;
+  float* lam = T + (size_t)k * k / 2;
 
   hipLaunchKernelGGL(damping_kernel, dim3(1), dim3(256), 0, s, H, k, damp_rel, lam, lambda_out, info);
   hipLaunchKernelGGL(zero_kernel, dim3((unsigned)(((size_t)k * k + 255) / 256)), dim3(256), 0, s, Linv,
@@ -203,20 +358,16 @@ hipError_t factor_hinv_launch(const float* H, int64_t k, float damp_rel, float* 
   if (e != hipSuccess) return e;
 
   for (int64_t p = 0; p < k; p += NB) {
-    hipLaunchKernelGGL(potf2_inv_kernel, dim3(1), dim3(64), 0, s, A, k, p, Linv, Dinv, info);
-    int64_t rest = k - p - NB;
+    const int64_t rest = k - p - NB;
+    const unsigned groups = rest > 0 ? (unsigned)((rest + NB - 1) / NB) : 1u;
+    hipLaunchKernelGGL(panel_kernel, dim3(groups), dim3(256), 0, s, A, k, p, info);
     if (rest <= 0) break;
-    // Panel below the block: A21 := A21 * Dinv^T.
-    hipLaunchKernelGGL(panel_solve_kernel, dim3((unsigned)((rest + 15) / 16)), dim3(256), 0, s, A, k, p, rest, Dinv);
-    // Trailing update: A22 -= A21 A21^T (lower tiles).
-    GemmArgs u{};
-    u.A = A + (p + NB) * k + p; u.lda = k;
-    u.B = A + (p + NB) * k + p; u.ldb = k;
-    u.C = A + (p + NB) * k + p + NB; u.ldc = k;
-    u.M = rest; u.N = rest; u.K = NB; u.batch = 1; u.alpha = -1.0f; u.beta = 1.0f;
-    e = gemm_f32(u, false, true, true, kEpiAxpby, s);
-    if (e != hipSuccess) return e;
+    const int64_t tiles = (rest + NB - 1) / NB;
+    hipLaunchKernelGGL(chol_update_kernel, dim3((unsigned)(tiles * (tiles + 1) / 2)), dim3(256), 0, s, A, k, p, rest);
   }
+  hipLaunchKernelGGL(diag_inv_kernel, dim3((unsigned)((k + NB - 1) / NB)), dim3(64), 0, s, A, k, Linv);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
 
   // Triangular inverse by recursive doubling over diagonal blocks of size bs.
   for (int64_t bs = NB; bs < k; bs *= 2) {
