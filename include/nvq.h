@@ -139,8 +139,11 @@ int nvfp4_global_scale(const void* W, int w_dtype, int64_t m, int64_t k, int64_t
  *   w'_l -= e_j U_jl; its score is sum_j e_j^2;
  *   the least score wins (ties: the smaller scale); its codes are stored and
  *   its errors update every later column of the row: w'_l -= sum_j e_j U_jl.
- * Later columns receive the updates in lazy batches of 128 columns (an fp32
- * MFMA GEMM per batch); all working values are fp32.
+ * Later columns receive the updates lazily: the errors of each 128-column
+ * batch update the rest of its 512-column block at once, and the columns past
+ * a finished 512-column block receive that block's errors together (fp32
+ * MFMA GEMMs; the same sums as eager updates in another order); all working
+ * values are fp32.
  *
  *   W        device [m x ldw], element type w_dtype (bf16 or fp32); not
  *            modified.  m > 0, k > 0, k % 16 == 0, ldw >= k, ldw % 4 == 0.

@@ -45,7 +45,7 @@ QuantWs quant_ws(int64_t m, int64_t k) {
   QuantWs w;
   size_t off = 0;
   w.wp = off;   off += align_up((size_t)m * k * sizeof(float));
-  w.eslab = off; off += align_up((size_t)m * kBatch * sizeof(float));
+  w.eslab = off; off += align_up((size_t)m * kSuperBatch * sizeof(float));
   w.invd = off;  off += align_up((size_t)k * sizeof(float));
   w.part = off;  off += align_up((size_t)m * ((k + kGemmTile - 1) / kGemmTile) * sizeof(float));
   w.total = off;
@@ -195,18 +195,27 @@ int gptq_nvfp4_quantize(const void* W, int w_dtype, int64_t m, int64_t k, int64_
     e = inv_diag_launch(U, k, invd, s);
     if (e == hipSuccess) e = load_working_copy(W, bf, m, k, ldw, Wp, s);
     if (e == hipSuccess && row_loss) e = fill_f32(row_loss, m, 0.0f, s);
-    for (int64_t i1 = 0; e == hipSuccess && i1 < k; i1 += kBatch) {
-      const int ncols = (int)std::min<int64_t>(kBatch, k - i1);
-      e = sweep_batch_launch(Wp, U, invd, g, m, k, (int)i1, ncols, n_cand, codes, scales, Eslab, row_loss, s);
-      const int64_t i2 = i1 + ncols;
-      if (e == hipSuccess && i2 < k) {
-        GemmArgs a{};
-        a.A = Eslab; a.lda = kBatch;
-        a.B = U + i1 * k + i2; a.ldb = k;
-        a.C = Wp + i2; a.ldc = k;
-        a.M = m; a.N = k - i2; a.K = ncols; a.batch = 1; a.alpha = -1.0f; a.beta = 1.0f;
-        e = gemm_f32(a, false, false, false, kEpiAxpby, s);
+    // Two-level lazy updates (the same sums as eager GPTQ updates, in another
+    // order): a batch's errors update the rest of its 512-column block at
+    // once, and the later columns receive the whole block's errors together.
+    auto rank_update = [&](const float* Eb, int64_t r0, int64_t c0, int64_t kk, int64_t ncol) {
+      GemmArgs a{};
+      a.A = Eb; a.lda = kSuperBatch;
+      a.B = U + r0 * k + c0; a.ldb = k;
+      a.C = Wp + c0; a.ldc = k;
+      a.M = m; a.N = ncol; a.K = kk; a.batch = 1; a.alpha = -1.0f; a.beta = 1.0f;
+      return gemm_f32(a, false, false, false, kEpiAxpby, s);
+    };
+    for (int64_t s0 = 0; e == hipSuccess && s0 < k; s0 += kSuperBatch) {
+      const int64_t s1 = std::min<int64_t>(k, s0 + kSuperBatch);
+      for (int64_t i1 = s0; e == hipSuccess && i1 < s1; i1 += kBatch) {
+        const int ncols = (int)std::min<int64_t>(kBatch, s1 - i1);
+        e = sweep_batch_launch(Wp, U, invd, g, m, k, (int)i1, ncols, n_cand, codes, scales, Eslab + (i1 - s0),
+                               kSuperBatch, row_loss, s);
+        const int64_t i2 = i1 + ncols;
+        if (e == hipSuccess && i2 < s1) e = rank_update(Eslab + (i1 - s0), i1, i2, ncols, s1 - i2);
       }
+      if (e == hipSuccess && s1 < k) e = rank_update(Eslab, s0, s1, s1 - s0, k - s1);
     }
   }
   if (e == hipSuccess && want_err) {

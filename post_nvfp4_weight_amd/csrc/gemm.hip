@@ -31,15 +31,18 @@ __device__ __forceinline__ void load_tile(const float* __restrict__ src, int64_t
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     int e = q * 256 + tid;
-    v[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Unconditional loads from clamped addresses (so that all of them are
+    // in flight together), zeroed outside the matrix afterwards.
     if (KMAJOR) {
       int r = e >> 3, kk = (e & 7) * 4;            // 8 lanes cover 32 k of a row
       int64_t gr = r0 + r, gk = k0 + kk;
-      if (gr < nrows && gk < K) v[q] = *(const f32x4*)(src + gr * ld + gk);
+      const f32x4 t = *(const f32x4*)(src + min(gr, nrows - 1) * ld + min(gk, K - 4));
+      v[q] = (gr < nrows && gk < K) ? t : f32x4{0.f, 0.f, 0.f, 0.f};
     } else {
       int kk = e >> 5, r = (e & 31) * 4;           // 32 lanes cover 128 rows of a k
       int64_t gr = r0 + r, gk = k0 + kk;
-      if (gr < nrows && gk < K) v[q] = *(const f32x4*)(src + gk * ld + gr);
+      const f32x4 t = *(const f32x4*)(src + min(gk, K - 1) * ld + min(gr, nrows - 4));
+      v[q] = (gr < nrows && gk < K) ? t : f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
 }
@@ -96,16 +99,35 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
   float* Cw = C + wrow0 * p.ldc + wcol0;
   const int lane_off = 4 * (lane >> 5) * (int)p.ldc + (lane & 31);
   const bool full = wrow0 + 64 <= p.M && wcol0 + 64 <= p.N;
+  // Unconditional loads (clamped addresses at the matrix edge), so that all
+  // 64 are in flight together.
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3), col = j * 32 + (lane & 31);
-        const bool ok = full || (wrow0 + row < p.M && wcol0 + col < p.N);
-        acc[i][j][r] = (load_c && ok) ? p.beta * Cw[(i * 32 + 8 * (r >> 2) + (r & 3)) * p.ldc + j * 32 + lane_off] : 0.0f;
-      }
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  if (load_c && full) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          acc[i][j][r] = p.beta * Cw[(i * 32 + 8 * (r >> 2) + (r & 3)) * p.ldc + j * 32 + lane_off];
+  } else if (load_c) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t gr = wrow0 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int64_t gc = wcol0 + j * 32 + (lane & 31);
+          const float v = C[min(gr, p.M - 1) * p.ldc + min(gc, p.N - 1)];
+          acc[i][j][r] = (gr < p.M && gc < p.N) ? p.beta * v : 0.0f;
+        }
+  }
   const float alpha_a = EPI == kEpiAxpby ? p.alpha : 1.0f;
 
   f32x4 ra[4], rb[4];

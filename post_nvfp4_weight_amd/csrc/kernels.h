@@ -55,8 +55,12 @@ hipError_t load_working_copy(const void* W, int bf16, int64_t m, int64_t k, int6
 hipError_t inv_diag_launch(const float* U, int64_t k, float* invd, hipStream_t s);
 hipError_t sweep_batch_launch(float* Wp, const float* U, const float* invd, const float* g,
                               int64_t m, int64_t k, int i1, int ncols, int n_cand,
-                              uint8_t* codes, uint8_t* scales, float* Eslab, float* row_loss,
+                              uint8_t* codes, uint8_t* scales, float* Eslab, int64_t lde, float* row_loss,
                               hipStream_t s);
+// Columns of the two-level lazy update: each 128-column batch updates the
+// rest of its 512-column block; each finished block updates every later
+// column with its whole error slab (m x 512).
+constexpr int kSuperBatch = 512;
 hipError_t delta_w_launch(const void* W, int bf16, int64_t m, int64_t k, int64_t ldw,
                           const uint8_t* codes, const uint8_t* scales, const float* g,
                           float* dW, hipStream_t s);

@@ -240,7 +240,7 @@ template <int G>
 __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
     float* __restrict__ Wp, const float* __restrict__ U, const float* __restrict__ invd,
     const float* __restrict__ gptr, int64_t m, int64_t k, int i1, int ncols, int n_cand,
-    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ Eslab,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ Eslab, int64_t lde,
     float* __restrict__ row_loss) {
   constexpr int ROWS = SweepCfg<G>::ROWS;
   constexpr int NT = SweepCfg<G>::THREADS;
@@ -327,7 +327,7 @@ __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
       const int64_t gb = (i1 + c0) / kBlock;
       *(u32x2*)(codes + row * (k / 2) + gb * 8) = u32x2{plo, phi};
       scales[row * (k / kBlock) + gb] = (uint8_t)cand;
-      f32x4* es = (f32x4*)(Eslab + row * kBatch + c0);
+      f32x4* es = (f32x4*)(Eslab + row * lde + c0);
       es[0] = f32x4{e[0], e[1], e[2], e[3]};
       es[1] = f32x4{e[4], e[5], e[6], e[7]};
       es[2] = f32x4{e[8], e[9], e[10], e[11]};
@@ -365,11 +365,11 @@ __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
 template <int G>
 hipError_t sweep_launch_g(float* Wp, const float* U, const float* invd, const float* g, int64_t m, int64_t k,
                           int i1, int ncols, int n_cand, uint8_t* codes, uint8_t* scales, float* Eslab,
-                          float* row_loss, hipStream_t s) {
+                          int64_t lde, float* row_loss, hipStream_t s) {
   constexpr int ROWS = SweepCfg<G>::ROWS;
   dim3 grid((unsigned)((m + ROWS - 1) / ROWS));
   hipLaunchKernelGGL(sweep_batch_kernel<G>, grid, dim3(SweepCfg<G>::THREADS), 0, s, Wp, U, invd, g, m, k, i1,
-                     ncols, n_cand, codes, scales, Eslab, row_loss);
+                     ncols, n_cand, codes, scales, Eslab, lde, row_loss);
   return hipGetLastError();
 }
 
@@ -432,12 +432,12 @@ hipError_t inv_diag_launch(const float* U, int64_t k, float* invd, hipStream_t s
 
 hipError_t sweep_batch_launch(float* Wp, const float* U, const float* invd, const float* g, int64_t m, int64_t k,
                               int i1, int ncols, int n_cand, uint8_t* codes, uint8_t* scales, float* Eslab,
-                              float* row_loss, hipStream_t s) {
-  if (n_cand <= 1) return sweep_launch_g<1>(Wp, U, invd, g, m, k, i1, ncols, n_cand, codes, scales, Eslab, row_loss, s);
-  if (n_cand <= 2) return sweep_launch_g<2>(Wp, U, invd, g, m, k, i1, ncols, n_cand, codes, scales, Eslab, row_loss, s);
-  if (n_cand <= 4) return sweep_launch_g<4>(Wp, U, invd, g, m, k, i1, ncols, n_cand, codes, scales, Eslab, row_loss, s);
-  if (n_cand <= 8) return sweep_launch_g<8>(Wp, U, invd, g, m, k, i1, ncols, n_cand, codes, scales, Eslab, row_loss, s);
-  return sweep_launch_g<16>(Wp, U, invd, g, m, k, i1, ncols, n_cand, codes, scales, Eslab, row_loss, s);
+                              int64_t lde, float* row_loss, hipStream_t s) {
+  if (n_cand <= 1) return sweep_launch_g<1>(Wp, U, invd, g, m, k, i1, ncols, n_cand, codes, scales, Eslab, lde, row_loss, s);
+  if (n_cand <= 2) return sweep_launch_g<2>(Wp, U, invd, g, m, k, i1, ncols, n_cand, codes, scales, Eslab, lde, row_loss, s);
+  if (n_cand <= 4) return sweep_launch_g<4>(Wp, U, invd, g, m, k, i1, ncols, n_cand, codes, scales, Eslab, lde, row_loss, s);
+  if (n_cand <= 8) return sweep_launch_g<8>(Wp, U, invd, g, m, k, i1, ncols, n_cand, codes, scales, Eslab, lde, row_loss, s);
+  return sweep_launch_g<16>(Wp, U, invd, g, m, k, i1, ncols, n_cand, codes, scales, Eslab, lde, row_loss, s);
 }
 
 hipError_t delta_w_launch(const void* W, int bf16, int64_t m, int64_t k, int64_t ldw, const uint8_t* codes,
