@@ -226,7 +226,8 @@ int gptq_nvfp4_quantize(const void* W, int w_dtype, int64_t m, int64_t k, int64_
       a.B = H; a.ldb = k;
       a.D = Wp; a.ldd = k;
       a.P = part; a.ldp = (k + kGemmTile - 1) / kGemmTile;
-      a.M = m; a.N = k; a.K = k; a.batch = 1; a.alpha = 1.0f; a.beta = 0.0f;
+      // dW H dW^T = dW H' dW^T with H' = 2 triu(H, 1) + diag(H): half the products.
+      a.M = m; a.N = k; a.K = k; a.batch = 1; a.alpha = 1.0f; a.beta = 0.0f; a.kmode = kGemmKSymUpperB;
       e = gemm_f32(a, false, false, false, kEpiRowDot, s);
     }
     if (e == hipSuccess) e = row_sum_launch(part, m, (k + kGemmTile - 1) / kGemmTile, row_err, s);

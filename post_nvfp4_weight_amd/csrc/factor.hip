@@ -380,7 +380,7 @@ hipError_t factor_hinv_launch(const float* H, int64_t k, float damp_rel, float* 
       a.C = T; a.ldc = n1;
       a.M = n2; a.N = n1; a.K = n1; a.batch = batch;
       a.sA = 2 * bs * k + 2 * bs; a.sB = 2 * bs * k + 2 * bs; a.sC = n1 * n2;
-      a.alpha = 1.0f; a.beta = 0.0f;
+      a.alpha = 1.0f; a.beta = 0.0f; a.kmode = kGemmKLowerB;   // L11^-1 is lower triangular
       hipError_t err = gemm_f32(a, false, false, false, kEpiAxpby, s);
       if (err != hipSuccess) return err;
       // X21 = -L22^-1 * T   (n2 x n1), written into Linv
@@ -390,7 +390,7 @@ hipError_t factor_hinv_launch(const float* H, int64_t k, float damp_rel, float* 
       b.C = Linv + (base + bs) * k + base; b.ldc = k;
       b.M = n2; b.N = n1; b.K = n2; b.batch = batch;
       b.sA = 2 * bs * k + 2 * bs; b.sB = n1 * n2; b.sC = 2 * bs * k + 2 * bs;
-      b.alpha = -1.0f; b.beta = 0.0f;
+      b.alpha = -1.0f; b.beta = 0.0f; b.kmode = kGemmKLowerA;  // L22^-1 is lower triangular
       return gemm_f32(b, false, false, false, kEpiAxpby, s);
     };
     if (full > 0) {

@@ -47,6 +47,21 @@ __device__ __forceinline__ void load_tile(const float* __restrict__ src, int64_t
   }
 }
 
+// B' = 2 triu(B, 1) + diag(B) on a B tile (k-index k0 + kk, column n0 + r).
+template <bool KMAJOR>
+__device__ __forceinline__ void sym_upper(f32x4 (&v)[4], int tid, int64_t k0, int64_t n0) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = q * 256 + tid;
+    const int r = KMAJOR ? e >> 3 : (e & 31) * 4, kk = KMAJOR ? (e & 7) * 4 : e >> 5;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t kg = k0 + kk + (KMAJOR ? u : 0), jg = n0 + r + (KMAJOR ? 0 : u);
+      v[q][u] *= kg < jg ? 2.0f : (kg == jg ? 1.0f : 0.0f);
+    }
+  }
+}
+
 template <bool KMAJOR>
 __device__ __forceinline__ void store_tile(float* dst, int tid, f32x4 (&v)[4], float scale = 1.0f) {
 #pragma unroll
@@ -71,7 +86,16 @@ __device__ __forceinline__ float read_operand(const float* tile, int row, int kk
 
 template <bool TA, bool TB, bool LOWER, int EPI>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
-  if (LOWER && blockIdx.x > blockIdx.y) return;
+  // Tile of this workgroup.  With a triangular k range the tiles differ in
+  // length: they are dealt out longest first, so that the last ones to start
+  // are short.
+  const int nt = (int)gridDim.x, mt = (int)gridDim.y;
+  const int lin = (int)blockIdx.y * nt + (int)blockIdx.x;
+  int tn = (int)blockIdx.x, tm = (int)blockIdx.y;
+  if (p.kmode == kGemmKSymUpperB) { tn = nt - 1 - lin / mt; tm = lin % mt; }
+  else if (p.kmode == kGemmKLowerB) { tn = lin / mt; tm = lin % mt; }
+  else if (p.kmode == kGemmKLowerA) { tm = mt - 1 - lin / nt; tn = lin % nt; }
+  if (LOWER && tn > tm) return;
   // [buffer][A | B] operand tiles; reused by the row-dot epilogue.
   __shared__ __attribute__((aligned(16))) float smem[2 * 2 * OPER_FLOATS];
   constexpr bool AK = !TA;   // A stored [M][K]: k contiguous
@@ -80,7 +104,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1;
-  const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
+  const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int64_t z = blockIdx.z;
   const float* A = p.A + z * p.sA;
   const float* B = p.B + z * p.sB;
@@ -130,17 +154,25 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
   }
   const float alpha_a = EPI == kEpiAxpby ? p.alpha : 1.0f;
 
+  // The chunks of k this tile needs (all of them unless a triangular operand
+  // makes the rest zero).
+  int64_t klo = 0, khi = p.K;
+  if (p.kmode == kGemmKLowerA) khi = min(p.K, m0 + BM);
+  if (p.kmode == kGemmKLowerB) klo = n0;
+  if (p.kmode == kGemmKSymUpperB) khi = min(p.K, n0 + BN);
+  const int64_t c0 = klo / BK, nk = (khi + BK - 1) / BK;
+  const bool sym = p.kmode == kGemmKSymUpperB;
   f32x4 ra[4], rb[4];
-  const int64_t nk = (p.K + BK - 1) / BK;
-  if (nk > 0) {
-    load_tile<AK>(A, p.lda, m0, p.M, 0, p.K, tid, ra);
-    load_tile<BKM>(B, p.ldb, n0, p.N, 0, p.K, tid, rb);
+  if (c0 < nk) {
+    load_tile<AK>(A, p.lda, m0, p.M, c0 * BK, p.K, tid, ra);
+    load_tile<BKM>(B, p.ldb, n0, p.N, c0 * BK, p.K, tid, rb);
+    if (sym) sym_upper<BKM>(rb, tid, c0 * BK, n0);
     store_tile<AK>(smem, tid, ra, alpha_a);
     store_tile<BKM>(smem + OPER_FLOATS, tid, rb);
   }
   __syncthreads();
-  for (int64_t c = 0; c < nk; ++c) {
-    const int cur = (int)(c & 1);
+  for (int64_t c = c0; c < nk; ++c) {
+    const int cur = (int)((c - c0) & 1);
     if (c + 1 < nk) {
       load_tile<AK>(A, p.lda, m0, p.M, (c + 1) * BK, p.K, tid, ra);
       load_tile<BKM>(B, p.ldb, n0, p.N, (c + 1) * BK, p.K, tid, rb);
@@ -163,6 +195,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
     }
     if (c + 1 < nk) {
       float* nxt = smem + (cur ^ 1) * 2 * OPER_FLOATS;
+      if (sym) sym_upper<BKM>(rb, tid, (c + 1) * BK, n0);
       store_tile<AK>(nxt, tid, ra, alpha_a);
       store_tile<BKM>(nxt + OPER_FLOATS, tid, rb);
     }
@@ -183,6 +216,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
   } else {
     // Row-dot: P[row, tile] = sum over the tile's columns of alpha*acc*D.
     float (*red)[33] = (float (*)[33])smem;   // [128][33], operand tiles are dead here
+    // Unconditional loads of D (clamped at the matrix edge), all in flight
+    // together.
     float part[2][16];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -193,7 +228,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           int64_t gj = n0 + wc * 64 + j * 32 + (lane & 31);
-          if (gi < p.M && gj < p.N) s = fmaf(p.alpha * acc[i][j][r], p.D[gi * p.ldd + gj], s);
+          const float d = p.D[min(gi, p.M - 1) * p.ldd + min(gj, p.N - 1)];
+          s = fmaf(p.alpha * acc[i][j][r], (gi < p.M && gj < p.N) ? d : 0.0f, s);
         }
         part[i][r] = s;
       }
@@ -214,7 +250,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
       float s = 0.0f;
       for (int c2 = 0; c2 < 32; ++c2) s += red[tid][c2];
       int64_t gi = m0 + tid;
-      if (gi < p.M) p.P[gi * p.ldp + blockIdx.x] = s;
+      if (gi < p.M) p.P[gi * p.ldp + tn] = s;
     }
   }
 }

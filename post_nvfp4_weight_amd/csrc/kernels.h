@@ -21,7 +21,14 @@ struct GemmArgs {
   int64_t sA, sB, sC;   // batch strides (elements)
   int batch;
   float alpha, beta;
+  int kmode;            // GemmK: which part of the k range each output tile needs
 };
+// kmode: kGemmKFull; kGemmKLowerA (A lower triangular: row tile i needs
+// k < its last row); kGemmKLowerB (B lower triangular: column tile j needs
+// k >= its first column); kGemmKSymUpperB (B symmetric, used as its upper
+// triangle with the off-diagonal entries doubled: column tile j needs
+// k < its last column; for x^T B x = x^T B' x with B' = 2 triu(B, 1) + diag(B)).
+enum GemmK { kGemmKFull = 0, kGemmKLowerA = 1, kGemmKLowerB = 2, kGemmKSymUpperB = 3 };
 // trans_a: A is stored [K x M]; trans_b: B is stored [N x K].  lower: skip
 // 128x128 tiles that lie entirely above the diagonal (square C only).
 // Requires M, N, K, leading dimensions and offsets to be multiples of 4 and
