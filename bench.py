@@ -110,7 +110,13 @@ def summarize_pmc(fetch_csv, write_csv):
                     e[1] += float(r["Counter_Value"])
         return list(d.values())
 
-    out = {"kernel": "hessian_accumulate (syrk_main_kernel + syrk_single_kernel + syrk_reduce_kernel)",
+    out = {"commands": ["rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmcf -o fetch -- "
+                        "python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline",
+                        "rocprofv3 --pmc WRITE_SIZE --output-format csv -d gpurun_out/pmcw -o write -- "
+                        "python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline",
+                        "python3 bench.py --summarize-pmc gpurun_out/pmcf/fetch_counter_collection.csv "
+                        "gpurun_out/pmcw/write_counter_collection.csv"],
+           "kernel": "hessian_accumulate (syrk_main_kernel + syrk_single_kernel + syrk_reduce_kernel)",
            "workload": WORKLOAD, "source_digest": hessian_source_digest(), "unit": "bytes per call",
            "calibration_copy_bytes": CAL_COPY_BYTES}
     total = 0.0
