@@ -125,7 +125,8 @@ __global__ __launch_bounds__(256) void panel_kernel(float* __restrict__ A, int64
   for (int q = 0; q < 8; ++q) {
     const int e = tid + 256 * (q & 3), i = e >> 4, j4 = (e & 15) * 4;
     const int64_t row = q < 4 ? p + min(i, nb - 1) : p + nb + r0 + min(i, max(rows - 1, 0));
-    ld[q] = (q < 4 || rows > 0) ? *(const f32x4*)(A + row * k + p + j4) : f32x4{0.f, 0.f, 0.f, 0.f};
+    // nb is a multiple of 16: a 4-column group lies wholly inside or past it.
+    ld[q] = (q < 4 || rows > 0) ? *(const f32x4*)(A + row * k + p + min(j4, nb - 4)) : f32x4{0.f, 0.f, 0.f, 0.f};
   }
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
@@ -236,7 +237,7 @@ __global__ __launch_bounds__(256) void panel_kernel(float* __restrict__ A, int64
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
     const int e = tid + 256 * (q & 3), i = e >> 4, j4 = (e & 15) * 4;
-    if (q < 4 ? (blockIdx.x != 0 || i >= nb) : i >= rows) continue;
+    if ((q < 4 ? (blockIdx.x != 0 || i >= nb) : i >= rows) || j4 >= nb) continue;
     f32x4 v;
 #pragma unroll
     for (int u = 0; u < 4; ++u) v[u] = (q < 4 && j4 + u > i) ? 0.0f : V[q < 4 ? i : NB + i][j4 + u];
