@@ -84,6 +84,35 @@ int hessian_accumulate(const void* X, int x_dtype, int64_t n, int64_t k, int64_t
                        float* H, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * hessian_accumulate_grouped -- one Hessian per group of token rows, for a
+ * mixture-of-experts layer in which every expert is a linear layer of its own
+ * that sees only the tokens routed to it ("Replay the Curvature", Abstract:
+ * the second-order state of each layer's GPTQ solve; its MoE evaluation model
+ * routes each token to a few experts).  For every group e:
+ *   H[e] += X[tok_idx[j]]^T X[tok_idx[j]] summed over j in [grp_off[e], grp_off[e+1]).
+ *
+ *   X        device [n x ldx], element type x_dtype, as for hessian_accumulate
+ *            (16-byte aligned; ldx % 8 == 0 for bf16, % 4 for fp32).
+ *   n        number of token rows of X.
+ *   tok_idx  device int32 [grp_off[G]]: the token row of every assignment,
+ *            grouped by expert.  Values outside [0, n) are clamped into it
+ *            (no out-of-bounds read); the caller guarantees they lie inside.
+ *   grp_off  HOST int64 [G + 1]: grp_off[0] = 0, non-decreasing; group e owns
+ *            entries grp_off[e] .. grp_off[e+1]-1 of tok_idx (empty groups are
+ *            skipped).  Read during the call only.
+ *   G        number of groups, G > 0.
+ *   H        device fp32 [G][k][k]; each H[e] as in hessian_accumulate (upper
+ *            triangle read, full symmetric matrix written).
+ *   ws       device workspace of hessian_grouped_workspace_size(grp_off, G, k,
+ *            x_dtype) bytes: the largest group's gathered rows plus the
+ *            Hessian workspace for that many tokens.
+ * Groups are processed in order on the stream (gather, then the contraction).
+ */
+size_t hessian_grouped_workspace_size(const int64_t* grp_off, int64_t G, int64_t k, int x_dtype);
+int hessian_accumulate_grouped(const void* X, int x_dtype, int64_t n, int64_t k, int64_t ldx, const int32_t* tok_idx,
+                               const int64_t* grp_off, int64_t G, float* H, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * factor_hinv -- damped inverse factor used by the GPTQ sweep ("Replay the
  * Curvature", Abstract: GPTQ, in which quantizing one column updates those
  * that follow).
@@ -107,6 +136,19 @@ int hessian_accumulate(const void* X, int x_dtype, int64_t n, int64_t k, int64_t
 size_t factor_hinv_workspace_size(int64_t k);
 int factor_hinv(const float* H, int64_t k, float damp_rel, float* U, float* lambda_out,
                 int32_t* info, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * factor_hinv_batched -- factor_hinv of `batch` matrices (one per expert of a
+ * mixture-of-experts layer), one after the other on the stream:
+ * H + e*stride_h -> U + e*stride_u, lambda_out[e], info[e].
+ * Strides count floats, are >= k*k and multiples of 4; the U and H ranges
+ * must not overlap.  ws: factor_hinv_workspace_size(k) bytes (reused).
+ * batch = 0 is a no-op.  Arguments are checked as for factor_hinv; the first
+ * failing element's status is returned (elements before it are enqueued).
+ */
+int factor_hinv_batched(const float* H, int64_t k, int64_t batch, int64_t stride_h, float damp_rel, float* U,
+                        int64_t stride_u, float* lambda_out, int32_t* info, void* ws, size_t ws_bytes,
+                        void* stream);
 
 /*
  * nvfp4_global_scale -- per-tensor fp32 scale applied on top of the E4M3 block
@@ -167,6 +209,23 @@ int gptq_nvfp4_quantize(const void* W, int w_dtype, int64_t m, int64_t k, int64_
                         const float* U, const float* H, const float* g, int n_cand,
                         unsigned flags, uint8_t* codes, uint8_t* scales, float* row_err,
                         float* row_loss, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * gptq_nvfp4_quantize_batched -- gptq_nvfp4_quantize of `batch` weight
+ * matrices of equal shape (the experts of a mixture-of-experts layer), one
+ * after the other on the stream.  Element e reads W + e*stride_w (elements of
+ * w_dtype), U + e*stride_u, H + e*stride_h (floats; U and H are not read when
+ * the flags say so) and g[e], and writes codes + e*m*(k/2),
+ * scales + e*m*(k/16), row_err + e*m and row_loss + e*m.  Strides: stride_w
+ * >= m*ldw; stride_u and stride_h >= k*k and multiples of 4.  ws:
+ * gptq_nvfp4_workspace_size(m, k, flags) bytes (reused).  batch = 0 is a
+ * no-op; arguments are checked as for gptq_nvfp4_quantize.
+ */
+int gptq_nvfp4_quantize_batched(const void* W, int w_dtype, int64_t batch, int64_t m, int64_t k, int64_t ldw,
+                                int64_t stride_w, const float* U, int64_t stride_u, const float* H,
+                                int64_t stride_h, const float* g, int n_cand, unsigned flags, uint8_t* codes,
+                                uint8_t* scales, float* row_err, float* row_loss, void* ws, size_t ws_bytes,
+                                void* stream);
 
 /*
  * nvfp4_dequantize -- NVFP4 weights back to real values ("Replay the

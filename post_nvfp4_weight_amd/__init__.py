@@ -25,9 +25,10 @@ FLAG_NO_ERR = 2
 
 EXPORTS = [
     "hessian_workspace_size", "hessian_accumulate",
-    "factor_hinv_workspace_size", "factor_hinv",
+    "hessian_grouped_workspace_size", "hessian_accumulate_grouped",
+    "factor_hinv_workspace_size", "factor_hinv", "factor_hinv_batched",
     "nvfp4_global_scale_workspace_size", "nvfp4_global_scale",
-    "gptq_nvfp4_workspace_size", "gptq_nvfp4_quantize",
+    "gptq_nvfp4_workspace_size", "gptq_nvfp4_quantize", "gptq_nvfp4_quantize_batched",
     "nvfp4_dequantize", "nvq_status_string", "nvq_last_error",
 ]
 
@@ -47,6 +48,11 @@ def _load():
     sig = {
         "hessian_workspace_size": (SZ, [I64, I64, I32]),
         "hessian_accumulate": (I32, [P, I32, I64, I64, I64, P, P, SZ, P]),
+        "hessian_grouped_workspace_size": (SZ, [P, I64, I64, I32]),
+        "hessian_accumulate_grouped": (I32, [P, I32, I64, I64, I64, P, P, I64, P, P, SZ, P]),
+        "factor_hinv_batched": (I32, [P, I64, I64, I64, F32, P, I64, P, P, P, SZ, P]),
+        "gptq_nvfp4_quantize_batched": (I32, [P, I32, I64, I64, I64, I64, I64, P, I64, P, I64, P, I32, U32, P, P,
+                                               P, P, P, SZ, P]),
         "factor_hinv_workspace_size": (SZ, [I64]),
         "factor_hinv": (I32, [P, I64, F32, P, P, P, P, SZ, P]),
         "nvfp4_global_scale_workspace_size": (SZ, [I64, I64]),
@@ -169,6 +175,58 @@ def nvfp4_dequantize(codes, scales, g, out_dtype=torch.float32):
     out = torch.empty(m, k, dtype=out_dtype, device=codes.device)
     _check("nvfp4_dequantize", lib.nvfp4_dequantize(_ptr(codes), _ptr(scales), _ptr(g), m, k, _ptr(out),
                                                     _dtype_code(out), _stream()))
+    return out
+
+
+def hessian_accumulate_grouped(X, tok_idx, grp_off, H=None):
+    """Per-group H[e] += X[idx_e]^T X[idx_e]; tok_idx: device int32 [total], grp_off: host sequence [G+1]."""
+    import numpy as np
+    n, k, ldx = _rows(X, "X")
+    off = np.ascontiguousarray(np.asarray(grp_off, dtype=np.int64))
+    G = len(off) - 1
+    if H is None:
+        H = torch.zeros(G, k, k, dtype=torch.float32, device=X.device)
+    offp = off.ctypes.data_as(ctypes.c_void_p)
+    need = lib.hessian_grouped_workspace_size(offp, G, k, _dtype_code(X))
+    ws = _workspace(need, X.device)
+    idx = tok_idx if tok_idx.dtype == torch.int32 else tok_idx.to(torch.int32)
+    _check("hessian_accumulate_grouped", lib.hessian_accumulate_grouped(
+        _ptr(X), _dtype_code(X), n, k, ldx, _ptr(idx), offp, G, _ptr(H), _ptr(ws), need, _stream()))
+    return H
+
+
+def factor_hinv_batched(H, damp_rel=0.01):
+    """H: [B, k, k] -> (U [B, k, k], lam [B], info [B]) as device tensors."""
+    B, k = H.shape[0], H.shape[1]
+    U = torch.empty_like(H)
+    lam = torch.empty(B, dtype=torch.float32, device=H.device)
+    info = torch.empty(B, dtype=torch.int32, device=H.device)
+    need = lib.factor_hinv_workspace_size(k)
+    ws = _workspace(need, H.device)
+    _check("factor_hinv_batched", lib.factor_hinv_batched(_ptr(H), k, B, H.stride(0), float(damp_rel), _ptr(U),
+                                                          U.stride(0), _ptr(lam), _ptr(info), _ptr(ws), need,
+                                                          _stream()))
+    return U, lam, info
+
+
+def gptq_nvfp4_quantize_batched(W, U, H, g, n_cand=16, flags=0):
+    """W: [B, m, k]; U, H: [B, k, k] (or None as the flags allow); g: device fp32 [B]."""
+    B, m, k = W.shape
+    dev = W.device
+    if W.stride(2) != 1:
+        raise ValueError("W must have unit column stride")
+    out = {
+        "codes": torch.empty(B, m, k // 2, dtype=torch.uint8, device=dev),
+        "scales": torch.empty(B, m, k // 16, dtype=torch.uint8, device=dev),
+        "row_err": None if (flags & FLAG_NO_ERR) else torch.empty(B, m, dtype=torch.float32, device=dev),
+        "row_loss": torch.empty(B, m, dtype=torch.float32, device=dev),
+    }
+    need = lib.gptq_nvfp4_workspace_size(m, k, flags)
+    ws = _workspace(need, dev)
+    _check("gptq_nvfp4_quantize_batched", lib.gptq_nvfp4_quantize_batched(
+        _ptr(W), _dtype_code(W), B, m, k, W.stride(1), W.stride(0), _ptr(U), 0 if U is None else U.stride(0),
+        _ptr(H), 0 if H is None else H.stride(0), _ptr(g), int(n_cand), int(flags), _ptr(out["codes"]),
+        _ptr(out["scales"]), _ptr(out["row_err"]), _ptr(out["row_loss"]), _ptr(ws), need, _stream()))
     return out
 
 

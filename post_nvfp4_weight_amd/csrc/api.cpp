@@ -54,55 +54,9 @@ QuantWs quant_ws(int64_t m, int64_t k) {
 
 bool dtype_ok(int d) { return d == NVQ_DTYPE_F32 || d == NVQ_DTYPE_BF16; }
 
-}  // namespace
-
-extern "C" {
-
-const char* nvq_status_string(int status) {
-  switch (status) {
-    case NVQ_OK: return "ok";
-    case NVQ_ERR_NULL: return "null pointer";
-    case NVQ_ERR_SHAPE: return "invalid shape";
-    case NVQ_ERR_DTYPE: return "unsupported dtype";
-    case NVQ_ERR_NCAND: return "candidate count outside [1, 16]";
-    case NVQ_ERR_WORKSPACE: return "workspace too small or misaligned";
-    case NVQ_ERR_VALUE: return "invalid scalar argument";
-    case NVQ_ERR_HIP: return "HIP runtime error";
-    case NVQ_ERR_ALIGN: return "misaligned pointer";
-    default: return "unknown status";
-  }
-}
-
-const char* nvq_last_error(void) { return g_last_error.c_str(); }
-
-// ---------------------------------------------------------------------------
-size_t hessian_workspace_size(int64_t n, int64_t k, int x_dtype) {
-  if (n <= 0 || k <= 0) return 0;
-  if (x_dtype == NVQ_DTYPE_BF16) return align_up(syrk_bf16_workspace(n, k));
-  return 0;
-}
-
-int hessian_accumulate(const void* X, int x_dtype, int64_t n, int64_t k, int64_t ldx, float* H, void* ws,
-                       size_t ws_bytes, void* stream) {
-  if (!H) return fail(NVQ_ERR_NULL, "hessian_accumulate: H is NULL");
-  if (!dtype_ok(x_dtype)) return fail(NVQ_ERR_DTYPE, "hessian_accumulate: x_dtype %d", x_dtype);
-  if (n < 0 || k <= 0 || k % 16 != 0 || ldx < k || ldx % 4 != 0)
-    return fail(NVQ_ERR_SHAPE, "hessian_accumulate: n=%lld k=%lld ldx=%lld (need n>=0, k>0, k%%16==0, ldx>=k, ldx%%4==0)",
-                (long long)n, (long long)k, (long long)ldx);
-  if (n == 0) return NVQ_OK;
-  if (!X) return fail(NVQ_ERR_NULL, "hessian_accumulate: X is NULL");
-  if (!aligned(H, 16)) return fail(NVQ_ERR_ALIGN, "hessian_accumulate: H must be 16-byte aligned");
-  hipStream_t s = (hipStream_t)stream;
-  if (x_dtype == NVQ_DTYPE_BF16) {
-    if (!aligned(X, 16)) return fail(NVQ_ERR_ALIGN, "hessian_accumulate: bf16 X must be 16-byte aligned");
-    if (ldx % 8 != 0) return fail(NVQ_ERR_SHAPE, "hessian_accumulate: bf16 rows must be 16-byte aligned (ldx %% 8 == 0)");
-    size_t need = hessian_workspace_size(n, k, x_dtype);
-    if (need && (!ws || ws_bytes < need || !aligned(ws, kAlign)))
-      return fail(NVQ_ERR_WORKSPACE, "hessian_accumulate: workspace needs %zu bytes (256-aligned), got %zu", need,
-                  ws_bytes);
-    return hip_status(syrk_bf16((const uint16_t*)X, n, k, ldx, H, ws, s), "hessian_accumulate");
-  }
-  if (!aligned(X, 16)) return fail(NVQ_ERR_ALIGN, "hessian_accumulate: fp32 X must be 16-byte aligned");
+hipError_t hessian_run(const void* X, int x_dtype, int64_t n, int64_t k, int64_t ldx, float* H, void* ws,
+                       hipStream_t s) {
+  if (x_dtype == NVQ_DTYPE_BF16) return syrk_bf16((const uint16_t*)X, n, k, ldx, H, ws, s);
   hipError_t e = symmetrize_from_upper(H, k, s);
   if (e == hipSuccess) {
     GemmArgs a{};
@@ -113,75 +67,49 @@ int hessian_accumulate(const void* X, int x_dtype, int64_t n, int64_t k, int64_t
     e = gemm_f32(a, true, false, false, kEpiAxpby, s);
   }
   if (e == hipSuccess) e = symmetrize_from_upper(H, k, s);
-  return hip_status(e, "hessian_accumulate");
+  return e;
 }
 
-// ---------------------------------------------------------------------------
-size_t factor_hinv_workspace_size(int64_t k) { return k > 0 ? align_up(factor_workspace(k)) : 0; }
-
-int factor_hinv(const float* H, int64_t k, float damp_rel, float* U, float* lambda_out, int32_t* info, void* ws,
-                size_t ws_bytes, void* stream) {
-  if (!H || !U || !lambda_out || !info) return fail(NVQ_ERR_NULL, "factor_hinv: H, U, lambda_out and info are required");
-  if (k <= 0 || k % 16 != 0) return fail(NVQ_ERR_SHAPE, "factor_hinv: k=%lld (need k>0, k%%16==0)", (long long)k);
-  if (!(damp_rel >= 0.0f) || !std::isfinite(damp_rel))
-    return fail(NVQ_ERR_VALUE, "factor_hinv: damp_rel must be finite and >= 0");
-  if (H == U) return fail(NVQ_ERR_VALUE, "factor_hinv: U must not overlap H");
-  if (!aligned(H, 16) || !aligned(U, 16)) return fail(NVQ_ERR_ALIGN, "factor_hinv: H and U must be 16-byte aligned");
-  size_t need = factor_hinv_workspace_size(k);
-  if (!ws || ws_bytes < need || !aligned(ws, kAlign))
-    return fail(NVQ_ERR_WORKSPACE, "factor_hinv: workspace needs %zu bytes (256-aligned), got %zu", need, ws_bytes);
-  return hip_status(factor_hinv_launch(H, k, damp_rel, U, lambda_out, info, ws, (hipStream_t)stream), "factor_hinv");
+// fail() with the entry point's name in front of the message.
+int failp(int code, const char* fn, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = std::string(fn) + ": " + buf;
+  return code;
 }
 
-// ---------------------------------------------------------------------------
-size_t nvfp4_global_scale_workspace_size(int64_t m, int64_t k) {
-  return (m > 0 && k > 0) ? align_up((size_t)global_scale_parts(m, k) * sizeof(float)) : 0;
-}
-
-int nvfp4_global_scale(const void* W, int w_dtype, int64_t m, int64_t k, int64_t ldw, float* g_out, void* ws,
-                       size_t ws_bytes, void* stream) {
-  if (!W || !g_out) return fail(NVQ_ERR_NULL, "nvfp4_global_scale: W and g_out are required");
-  if (!dtype_ok(w_dtype)) return fail(NVQ_ERR_DTYPE, "nvfp4_global_scale: w_dtype %d", w_dtype);
-  if (m <= 0 || k <= 0 || ldw < k) return fail(NVQ_ERR_SHAPE, "nvfp4_global_scale: m=%lld k=%lld ldw=%lld",
-                                               (long long)m, (long long)k, (long long)ldw);
-  size_t need = nvfp4_global_scale_workspace_size(m, k);
-  if (!ws || ws_bytes < need || !aligned(ws, kAlign))
-    return fail(NVQ_ERR_WORKSPACE, "nvfp4_global_scale: workspace needs %zu bytes, got %zu", need, ws_bytes);
-  return hip_status(global_scale_launch(W, w_dtype == NVQ_DTYPE_BF16, m, k, ldw, g_out, (float*)ws,
-                                        global_scale_parts(m, k), (hipStream_t)stream),
-                    "nvfp4_global_scale");
-}
-
-// ---------------------------------------------------------------------------
-size_t gptq_nvfp4_workspace_size(int64_t m, int64_t k, unsigned flags) {
-  (void)flags;
-  if (m <= 0 || k <= 0) return 0;
-  return quant_ws(m, k).total;
-}
-
-int gptq_nvfp4_quantize(const void* W, int w_dtype, int64_t m, int64_t k, int64_t ldw, const float* U,
-                        const float* H, const float* g, int n_cand, unsigned flags, uint8_t* codes, uint8_t* scales,
-                        float* row_err, float* row_loss, void* ws, size_t ws_bytes, void* stream) {
+int quant_check(const char* fn, const void* W, int w_dtype, int64_t m, int64_t k, int64_t ldw, const float* U,
+                const float* H, const float* g, int n_cand, unsigned flags, const uint8_t* codes,
+                const uint8_t* scales, const float* row_err, const void* ws, size_t ws_bytes) {
   const bool rtn = flags & NVQ_FLAG_RTN;
   const bool want_err = !(flags & NVQ_FLAG_NO_ERR);
-  if (flags & ~(NVQ_FLAG_RTN | NVQ_FLAG_NO_ERR)) return fail(NVQ_ERR_VALUE, "gptq_nvfp4_quantize: unknown flags 0x%x", flags);
-  if (!W || !g || !codes || !scales) return fail(NVQ_ERR_NULL, "gptq_nvfp4_quantize: W, g, codes and scales are required");
-  if (!rtn && !U) return fail(NVQ_ERR_NULL, "gptq_nvfp4_quantize: U is required without NVQ_FLAG_RTN");
-  if (want_err && (!H || !row_err)) return fail(NVQ_ERR_NULL, "gptq_nvfp4_quantize: H and row_err are required unless NVQ_FLAG_NO_ERR");
-  if (!dtype_ok(w_dtype)) return fail(NVQ_ERR_DTYPE, "gptq_nvfp4_quantize: w_dtype %d", w_dtype);
+  if (flags & ~(NVQ_FLAG_RTN | NVQ_FLAG_NO_ERR)) return failp(NVQ_ERR_VALUE, fn, "unknown flags 0x%x", flags);
+  if (!W || !g || !codes || !scales) return failp(NVQ_ERR_NULL, fn, "W, g, codes and scales are required");
+  if (!rtn && !U) return failp(NVQ_ERR_NULL, fn, "U is required without NVQ_FLAG_RTN");
+  if (want_err && (!H || !row_err)) return failp(NVQ_ERR_NULL, fn, "H and row_err are required unless NVQ_FLAG_NO_ERR");
+  if (!dtype_ok(w_dtype)) return failp(NVQ_ERR_DTYPE, fn, "w_dtype %d", w_dtype);
   if (m <= 0 || k <= 0 || k % 16 != 0 || ldw < k || ldw % 4 != 0)
-    return fail(NVQ_ERR_SHAPE, "gptq_nvfp4_quantize: m=%lld k=%lld ldw=%lld (need m>0, k>0, k%%16==0, ldw>=k, ldw%%4==0)",
-                (long long)m, (long long)k, (long long)ldw);
-  if (n_cand < 1 || n_cand > 16) return fail(NVQ_ERR_NCAND, "gptq_nvfp4_quantize: n_cand=%d", n_cand);
-  if (!aligned(codes, 8)) return fail(NVQ_ERR_ALIGN, "gptq_nvfp4_quantize: codes must be 8-byte aligned");
-  if ((U && !aligned(U, 16)) || (H && !aligned(H, 16)))
-    return fail(NVQ_ERR_ALIGN, "gptq_nvfp4_quantize: U and H must be 16-byte aligned");
+    return failp(NVQ_ERR_SHAPE, fn, "m=%lld k=%lld ldw=%lld (need m>0, k>0, k%%16==0, ldw>=k, ldw%%4==0)",
+                 (long long)m, (long long)k, (long long)ldw);
+  if (n_cand < 1 || n_cand > 16) return failp(NVQ_ERR_NCAND, fn, "n_cand=%d", n_cand);
+  if (!aligned(codes, 8)) return failp(NVQ_ERR_ALIGN, fn, "codes must be 8-byte aligned");
+  if ((U && !aligned(U, 16)) || (H && !aligned(H, 16))) return failp(NVQ_ERR_ALIGN, fn, "U and H must be 16-byte aligned");
   QuantWs L = quant_ws(m, k);
   if (!ws || ws_bytes < L.total || !aligned(ws, kAlign))
-    return fail(NVQ_ERR_WORKSPACE, "gptq_nvfp4_quantize: workspace needs %zu bytes (256-aligned), got %zu", L.total,
-                ws_bytes);
-  hipStream_t s = (hipStream_t)stream;
-  char* base = (char*)ws;
+    return failp(NVQ_ERR_WORKSPACE, fn, "workspace needs %zu bytes (256-aligned), got %zu", L.total, ws_bytes);
+  return NVQ_OK;
+}
+
+// The quantization of one weight matrix (arguments already checked).
+hipError_t quant_run(const void* W, int w_dtype, int64_t m, int64_t k, int64_t ldw, const float* U, const float* H,
+                     const float* g, int n_cand, unsigned flags, uint8_t* codes, uint8_t* scales, float* row_err,
+                     float* row_loss, char* base, hipStream_t s) {
+  const bool rtn = flags & NVQ_FLAG_RTN;
+  const bool want_err = !(flags & NVQ_FLAG_NO_ERR);
+  QuantWs L = quant_ws(m, k);
   float* Wp = (float*)(base + L.wp);
   float* Eslab = (float*)(base + L.eslab);
   float* invd = (float*)(base + L.invd);
@@ -232,7 +160,195 @@ int gptq_nvfp4_quantize(const void* W, int w_dtype, int64_t m, int64_t k, int64_
     }
     if (e == hipSuccess) e = row_sum_launch(part, m, (k + kGemmTile - 1) / kGemmTile, row_err, s);
   }
-  return hip_status(e, "gptq_nvfp4_quantize");
+  return e;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* nvq_status_string(int status) {
+  switch (status) {
+    case NVQ_OK: return "ok";
+    case NVQ_ERR_NULL: return "null pointer";
+    case NVQ_ERR_SHAPE: return "invalid shape";
+    case NVQ_ERR_DTYPE: return "unsupported dtype";
+    case NVQ_ERR_NCAND: return "candidate count outside [1, 16]";
+    case NVQ_ERR_WORKSPACE: return "workspace too small or misaligned";
+    case NVQ_ERR_VALUE: return "invalid scalar argument";
+    case NVQ_ERR_HIP: return "HIP runtime error";
+    case NVQ_ERR_ALIGN: return "misaligned pointer";
+    default: return "unknown status";
+  }
+}
+
+const char* nvq_last_error(void) { return g_last_error.c_str(); }
+
+// ---------------------------------------------------------------------------
+size_t hessian_workspace_size(int64_t n, int64_t k, int x_dtype) {
+  if (n <= 0 || k <= 0) return 0;
+  if (x_dtype == NVQ_DTYPE_BF16) return align_up(syrk_bf16_workspace(n, k));
+  return 0;
+}
+
+int hessian_accumulate(const void* X, int x_dtype, int64_t n, int64_t k, int64_t ldx, float* H, void* ws,
+                       size_t ws_bytes, void* stream) {
+  if (!H) return fail(NVQ_ERR_NULL, "hessian_accumulate: H is NULL");
+  if (!dtype_ok(x_dtype)) return fail(NVQ_ERR_DTYPE, "hessian_accumulate: x_dtype %d", x_dtype);
+  if (n < 0 || k <= 0 || k % 16 != 0 || ldx < k || ldx % 4 != 0)
+    return fail(NVQ_ERR_SHAPE, "hessian_accumulate: n=%lld k=%lld ldx=%lld (need n>=0, k>0, k%%16==0, ldx>=k, ldx%%4==0)",
+                (long long)n, (long long)k, (long long)ldx);
+  if (n == 0) return NVQ_OK;
+  if (!X) return fail(NVQ_ERR_NULL, "hessian_accumulate: X is NULL");
+  if (!aligned(H, 16)) return fail(NVQ_ERR_ALIGN, "hessian_accumulate: H must be 16-byte aligned");
+  if (!aligned(X, 16)) return fail(NVQ_ERR_ALIGN, "hessian_accumulate: X must be 16-byte aligned");
+  if (x_dtype == NVQ_DTYPE_BF16 && ldx % 8 != 0)
+    return fail(NVQ_ERR_SHAPE, "hessian_accumulate: bf16 rows must be 16-byte aligned (ldx %% 8 == 0)");
+  size_t need = hessian_workspace_size(n, k, x_dtype);
+  if (need && (!ws || ws_bytes < need || !aligned(ws, kAlign)))
+    return fail(NVQ_ERR_WORKSPACE, "hessian_accumulate: workspace needs %zu bytes (256-aligned), got %zu", need,
+                ws_bytes);
+  return hip_status(hessian_run(X, x_dtype, n, k, ldx, H, ws, (hipStream_t)stream), "hessian_accumulate");
+}
+
+size_t hessian_grouped_workspace_size(const int64_t* grp_off, int64_t G, int64_t k, int x_dtype) {
+  if (!grp_off || G <= 0 || k <= 0 || !dtype_ok(x_dtype)) return 0;
+  int64_t nmax = 0;
+  for (int64_t e = 0; e < G; ++e) nmax = std::max<int64_t>(nmax, grp_off[e + 1] - grp_off[e]);
+  if (nmax <= 0) return 0;
+  const size_t esize = x_dtype == NVQ_DTYPE_BF16 ? 2 : 4;
+  return align_up((size_t)nmax * k * esize) + hessian_workspace_size(nmax, k, x_dtype);
+}
+
+int hessian_accumulate_grouped(const void* X, int x_dtype, int64_t n, int64_t k, int64_t ldx, const int32_t* tok_idx,
+                               const int64_t* grp_off, int64_t G, float* H, void* ws, size_t ws_bytes, void* stream) {
+  if (!H || !grp_off) return fail(NVQ_ERR_NULL, "hessian_accumulate_grouped: H and grp_off are required");
+  if (!dtype_ok(x_dtype)) return fail(NVQ_ERR_DTYPE, "hessian_accumulate_grouped: x_dtype %d", x_dtype);
+  if (G <= 0 || n < 0 || k <= 0 || k % 16 != 0 || ldx < k || ldx % (x_dtype == NVQ_DTYPE_BF16 ? 8 : 4) != 0)
+    return fail(NVQ_ERR_SHAPE, "hessian_accumulate_grouped: G=%lld n=%lld k=%lld ldx=%lld", (long long)G,
+                (long long)n, (long long)k, (long long)ldx);
+  if (grp_off[0] != 0) return fail(NVQ_ERR_VALUE, "hessian_accumulate_grouped: grp_off[0] must be 0");
+  for (int64_t e = 0; e < G; ++e)
+    if (grp_off[e + 1] < grp_off[e])
+      return fail(NVQ_ERR_VALUE, "hessian_accumulate_grouped: grp_off must be non-decreasing (group %lld)", (long long)e);
+  if (grp_off[G] == 0) return NVQ_OK;
+  if (n == 0) return fail(NVQ_ERR_SHAPE, "hessian_accumulate_grouped: assignments given but n = 0");
+  if (!X || !tok_idx) return fail(NVQ_ERR_NULL, "hessian_accumulate_grouped: X and tok_idx are required");
+  if (!aligned(H, 16) || !aligned(X, 16)) return fail(NVQ_ERR_ALIGN, "hessian_accumulate_grouped: X and H must be 16-byte aligned");
+  const size_t need = hessian_grouped_workspace_size(grp_off, G, k, x_dtype);
+  if (!ws || ws_bytes < need || !aligned(ws, kAlign))
+    return fail(NVQ_ERR_WORKSPACE, "hessian_accumulate_grouped: workspace needs %zu bytes (256-aligned), got %zu", need,
+                ws_bytes);
+  hipStream_t s = (hipStream_t)stream;
+  const int esize = x_dtype == NVQ_DTYPE_BF16 ? 2 : 4;
+  int64_t nmax = 0;
+  for (int64_t e = 0; e < G; ++e) nmax = std::max<int64_t>(nmax, grp_off[e + 1] - grp_off[e]);
+  char* rows = (char*)ws;
+  void* hws = rows + align_up((size_t)nmax * k * esize);
+  hipError_t err = hipSuccess;
+  for (int64_t e = 0; err == hipSuccess && e < G; ++e) {
+    const int64_t ne = grp_off[e + 1] - grp_off[e];
+    if (ne == 0) continue;
+    err = gather_rows(X, esize, ldx, tok_idx + grp_off[e], n, ne, k, rows, s);
+    if (err == hipSuccess) err = hessian_run(rows, x_dtype, ne, k, k, H + (size_t)e * k * k, hws, s);
+  }
+  return hip_status(err, "hessian_accumulate_grouped");
+}
+
+// ---------------------------------------------------------------------------
+size_t factor_hinv_workspace_size(int64_t k) { return k > 0 ? align_up(factor_workspace(k)) : 0; }
+
+int factor_hinv(const float* H, int64_t k, float damp_rel, float* U, float* lambda_out, int32_t* info, void* ws,
+                size_t ws_bytes, void* stream) {
+  if (!H || !U || !lambda_out || !info) return fail(NVQ_ERR_NULL, "factor_hinv: H, U, lambda_out and info are required");
+  if (k <= 0 || k % 16 != 0) return fail(NVQ_ERR_SHAPE, "factor_hinv: k=%lld (need k>0, k%%16==0)", (long long)k);
+  if (!(damp_rel >= 0.0f) || !std::isfinite(damp_rel))
+    return fail(NVQ_ERR_VALUE, "factor_hinv: damp_rel must be finite and >= 0");
+  if (H == U) return fail(NVQ_ERR_VALUE, "factor_hinv: U must not overlap H");
+  if (!aligned(H, 16) || !aligned(U, 16)) return fail(NVQ_ERR_ALIGN, "factor_hinv: H and U must be 16-byte aligned");
+  size_t need = factor_hinv_workspace_size(k);
+  if (!ws || ws_bytes < need || !aligned(ws, kAlign))
+    return fail(NVQ_ERR_WORKSPACE, "factor_hinv: workspace needs %zu bytes (256-aligned), got %zu", need, ws_bytes);
+  return hip_status(factor_hinv_launch(H, k, damp_rel, U, lambda_out, info, ws, (hipStream_t)stream), "factor_hinv");
+}
+
+int factor_hinv_batched(const float* H, int64_t k, int64_t batch, int64_t stride_h, float damp_rel, float* U,
+                        int64_t stride_u, float* lambda_out, int32_t* info, void* ws, size_t ws_bytes, void* stream) {
+  if (batch < 0) return fail(NVQ_ERR_SHAPE, "factor_hinv_batched: batch=%lld", (long long)batch);
+  if (batch == 0) return NVQ_OK;
+  if (stride_h < k * k || stride_u < k * k || stride_h % 4 != 0 || stride_u % 4 != 0)
+    return fail(NVQ_ERR_SHAPE, "factor_hinv_batched: strides must be >= k*k and multiples of 4");
+  if (H && U && (const float*)U < H + (size_t)stride_h * batch && H < (const float*)U + (size_t)stride_u * batch)
+    return fail(NVQ_ERR_VALUE, "factor_hinv_batched: U must not overlap H");
+  for (int64_t e = 0; e < batch; ++e) {
+    const int rc = factor_hinv(H ? H + (size_t)e * stride_h : nullptr, k, damp_rel,
+                               U ? U + (size_t)e * stride_u : nullptr, lambda_out ? lambda_out + e : nullptr,
+                               info ? info + e : nullptr, ws, ws_bytes, stream);
+    if (rc != NVQ_OK) return rc;
+  }
+  return NVQ_OK;
+}
+
+// ---------------------------------------------------------------------------
+size_t nvfp4_global_scale_workspace_size(int64_t m, int64_t k) {
+  return (m > 0 && k > 0) ? align_up((size_t)global_scale_parts(m, k) * sizeof(float)) : 0;
+}
+
+int nvfp4_global_scale(const void* W, int w_dtype, int64_t m, int64_t k, int64_t ldw, float* g_out, void* ws,
+                       size_t ws_bytes, void* stream) {
+  if (!W || !g_out) return fail(NVQ_ERR_NULL, "nvfp4_global_scale: W and g_out are required");
+  if (!dtype_ok(w_dtype)) return fail(NVQ_ERR_DTYPE, "nvfp4_global_scale: w_dtype %d", w_dtype);
+  if (m <= 0 || k <= 0 || ldw < k) return fail(NVQ_ERR_SHAPE, "nvfp4_global_scale: m=%lld k=%lld ldw=%lld",
+                                               (long long)m, (long long)k, (long long)ldw);
+  size_t need = nvfp4_global_scale_workspace_size(m, k);
+  if (!ws || ws_bytes < need || !aligned(ws, kAlign))
+    return fail(NVQ_ERR_WORKSPACE, "nvfp4_global_scale: workspace needs %zu bytes, got %zu", need, ws_bytes);
+  return hip_status(global_scale_launch(W, w_dtype == NVQ_DTYPE_BF16, m, k, ldw, g_out, (float*)ws,
+                                        global_scale_parts(m, k), (hipStream_t)stream),
+                    "nvfp4_global_scale");
+}
+
+// ---------------------------------------------------------------------------
+size_t gptq_nvfp4_workspace_size(int64_t m, int64_t k, unsigned flags) {
+  (void)flags;
+  if (m <= 0 || k <= 0) return 0;
+  return quant_ws(m, k).total;
+}
+
+int gptq_nvfp4_quantize(const void* W, int w_dtype, int64_t m, int64_t k, int64_t ldw, const float* U,
+                        const float* H, const float* g, int n_cand, unsigned flags, uint8_t* codes, uint8_t* scales,
+                        float* row_err, float* row_loss, void* ws, size_t ws_bytes, void* stream) {
+  const int rc = quant_check("gptq_nvfp4_quantize", W, w_dtype, m, k, ldw, U, H, g, n_cand, flags, codes, scales,
+                             row_err, ws, ws_bytes);
+  if (rc != NVQ_OK) return rc;
+  return hip_status(quant_run(W, w_dtype, m, k, ldw, U, H, g, n_cand, flags, codes, scales, row_err, row_loss,
+                              (char*)ws, (hipStream_t)stream),
+                    "gptq_nvfp4_quantize");
+}
+
+int gptq_nvfp4_quantize_batched(const void* W, int w_dtype, int64_t batch, int64_t m, int64_t k, int64_t ldw,
+                                int64_t stride_w, const float* U, int64_t stride_u, const float* H, int64_t stride_h,
+                                const float* g, int n_cand, unsigned flags, uint8_t* codes, uint8_t* scales,
+                                float* row_err, float* row_loss, void* ws, size_t ws_bytes, void* stream) {
+  if (batch < 0) return fail(NVQ_ERR_SHAPE, "gptq_nvfp4_quantize_batched: batch=%lld", (long long)batch);
+  if (batch == 0) return NVQ_OK;
+  const int rc = quant_check("gptq_nvfp4_quantize_batched", W, w_dtype, m, k, ldw, U, H, g, n_cand, flags, codes,
+                             scales, row_err, ws, ws_bytes);
+  if (rc != NVQ_OK) return rc;
+  const bool rtn = flags & NVQ_FLAG_RTN, want_err = !(flags & NVQ_FLAG_NO_ERR);
+  if (stride_w < m * ldw || (!rtn && (stride_u < k * k || stride_u % 4 != 0)) ||
+      (want_err && (stride_h < k * k || stride_h % 4 != 0)))
+    return fail(NVQ_ERR_SHAPE, "gptq_nvfp4_quantize_batched: strides must cover one element (W: m*ldw, U and H: k*k, "
+                               "multiples of 4)");
+  const size_t es = w_dtype == NVQ_DTYPE_BF16 ? 2 : 4;
+  hipError_t err = hipSuccess;
+  for (int64_t e = 0; err == hipSuccess && e < batch; ++e)
+    err = quant_run((const char*)W + (size_t)e * stride_w * es, w_dtype, m, k, ldw,
+                    U ? U + (size_t)e * stride_u : nullptr, H ? H + (size_t)e * stride_h : nullptr, g + e, n_cand,
+                    flags, codes + (size_t)e * m * (k / 2), scales + (size_t)e * m * (k / kBlock),
+                    row_err ? row_err + (size_t)e * m : nullptr, row_loss ? row_loss + (size_t)e * m : nullptr,
+                    (char*)ws, (hipStream_t)stream);
+  return hip_status(err, "gptq_nvfp4_quantize_batched");
 }
 
 // ---------------------------------------------------------------------------

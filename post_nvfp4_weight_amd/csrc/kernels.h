@@ -42,6 +42,9 @@ size_t syrk_bf16_workspace(int64_t n, int64_t k);
 hipError_t syrk_bf16(const uint16_t* X, int64_t n, int64_t k, int64_t ldx, float* H, void* ws,
                      hipStream_t s);
 hipError_t symmetrize_from_upper(float* H, int64_t k, hipStream_t s);
+// out[t] = row clamp(idx[t], 0, nsrc-1) of X (rows of k elements of esize bytes, ld ldx).
+hipError_t gather_rows(const void* X, int esize, int64_t ldx, const int32_t* idx, int64_t nsrc, int64_t n,
+                       int64_t k, void* out, hipStream_t s);
 
 // ---- factor ----------------------------------------------------------------
 size_t factor_workspace(int64_t k);

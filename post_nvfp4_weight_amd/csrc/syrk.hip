@@ -559,6 +559,28 @@ hipError_t syrk_bf16(const uint16_t* X, int64_t n, int64_t k, int64_t ldx, float
   return hipGetLastError();
 }
 
+// Row gather for grouped Hessians: out[t][0:k] = X[clamp(idx[t])][0:k],
+// in 16-byte pieces (rows of k * esize bytes, a multiple of 16).
+__global__ __launch_bounds__(256) void gather_rows_kernel(const char* __restrict__ X, int64_t row_bytes_src,
+                                                          const int32_t* __restrict__ idx, int64_t nsrc, int64_t n,
+                                                          int64_t pieces, char* __restrict__ out) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= n * pieces) return;
+  const int64_t t = e / pieces, c = e % pieces;
+  int64_t r = idx[t];
+  r = r < 0 ? 0 : (r >= nsrc ? nsrc - 1 : r);
+  *(u32x4*)(out + (t * pieces + c) * 16) = *(const u32x4*)(X + r * row_bytes_src + c * 16);
+}
+
+hipError_t gather_rows(const void* X, int esize, int64_t ldx, const int32_t* idx, int64_t nsrc, int64_t n,
+                       int64_t k, void* out, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t pieces = k * esize / 16;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)((n * pieces + 255) / 256)), dim3(256), 0, s,
+                     (const char*)X, ldx * esize, idx, nsrc, n, pieces, (char*)out);
+  return hipGetLastError();
+}
+
 hipError_t symmetrize_from_upper(float* H, int64_t k, hipStream_t s) {
   hipLaunchKernelGGL(symmetrize_kernel, dim3((unsigned)((k + 255) / 256), (unsigned)k), dim3(256), 0, s, H, k);
   return hipGetLastError();

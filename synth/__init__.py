@@ -19,6 +19,10 @@ Workload recipes (weights W [d_out, d_in], activations X [tokens, d_in]):
   mlp        W bf16 ~ N(0, 0.015^2); X as small, in bf16.
   sparse     W bf16 ~ N(0, 0.01^2) with 0.05% Student-t(3) outliers;
              X bf16 = |z| * Bernoulli(0.4) * s (60% exact zeros).
+  moe        per expert W bf16 ~ N(0, 0.02^2); X as small, in bf16; every
+             token routed to top_k distinct experts drawn without replacement
+             with probability proportional to rank^-1.1 (Zipf popularity),
+             by the Gumbel top-k trick.
 """
 
 from concurrent.futures import ThreadPoolExecutor
@@ -146,3 +150,36 @@ def sparse_layer(m, k, n):
     W = weights("sparse", m, k, 0.01, outlier_frac=0.0005)
     X = activations("sparse", n, k, kind="sparse")
     return W, X
+
+
+def moe_routing(n_tokens, n_experts, top_k, zipf=1.1, layer="moe"):
+    """Token -> expert assignments, grouped by expert.
+
+    Expert e has popularity rank perm[e] + 1 (a seeded permutation) and
+    weight (rank)^-zipf.  Each token draws top_k distinct experts without
+    replacement with probability proportional to the weights: the top_k
+    largest of log(weight) + Gumbel noise.  Returns (tok_idx int32 [n*top_k]
+    sorted by expert then token, grp_off int64 [n_experts + 1]).
+    """
+    r = rng(layer, 30)
+    rank = r.permutation(n_experts) + 1
+    logw = (-zipf * np.log(rank.astype(np.float64))).astype(np.float32)
+    experts = np.empty((n_tokens, top_k), dtype=np.int32)
+    for c0 in range(0, n_tokens, _CHUNK):
+        rows = min(_CHUNK, n_tokens - c0)
+        gum = rng(layer, 31, c0 // _CHUNK).gumbel(size=(rows, n_experts)).astype(np.float32)
+        experts[c0:c0 + rows] = np.argpartition(-(logw[None, :] + gum), top_k - 1, axis=1)[:, :top_k]
+    tok = np.repeat(np.arange(n_tokens, dtype=np.int64), top_k)
+    ex = experts.reshape(-1).astype(np.int64)
+    order = np.lexsort((tok, ex))
+    counts = np.bincount(ex, minlength=n_experts)
+    grp_off = np.zeros(n_experts + 1, dtype=np.int64)
+    grp_off[1:] = np.cumsum(counts)
+    return tok[order].astype(np.int32), grp_off
+
+
+def moe_expert_weights(expert, m, k, std=0.02, layer="moe"):
+    """W [m, k] of one expert (gate and up stacked along m), bf16 values."""
+    r = rng(layer, 40, expert)
+    W = (r.standard_normal((m, k)) * std).astype(np.float32)
+    return to_bf16_values(W)

@@ -66,6 +66,22 @@ def test_host_validation_rejects_bad_arguments():
     assert lib.nvfp4_dequantize(fake, fake, fake, 4, 8, fake, 0, None) == -2
     assert lib.nvfp4_dequantize(fake, fake, fake, 4, 32, fake, 5, None) == -3
     assert lib.nvfp4_dequantize(None, None, None, 0, 32, None, 0, None) == 0
+    # grouped Hessian: offsets must start at 0 and not decrease; G > 0
+    off = (ctypes.c_int64 * 4)(0, 5, 3, 9)
+    assert lib.hessian_accumulate_grouped(fake, 1, 10, 32, 32, fake, off, 3, fake, fake, 1 << 30, None) == -6
+    off = (ctypes.c_int64 * 3)(1, 5, 9)
+    assert lib.hessian_accumulate_grouped(fake, 1, 10, 32, 32, fake, off, 2, fake, fake, 1 << 30, None) == -6
+    assert lib.hessian_accumulate_grouped(fake, 1, 10, 32, 32, fake, off, 0, fake, fake, 1 << 30, None) == -2
+    off = (ctypes.c_int64 * 3)(0, 0, 0)   # no assignments: a no-op
+    assert lib.hessian_accumulate_grouped(None, 1, 0, 32, 32, None, off, 2, fake, None, 0, None) == 0
+    # batched factor / quantize: empty batch is a no-op, strides must cover an element
+    assert lib.factor_hinv_batched(None, 32, 0, 1024, ctypes.c_float(0.01), None, 1024, None, None, None, 0,
+                                   None) == 0
+    assert lib.factor_hinv_batched(fake, 32, 2, 100, ctypes.c_float(0.01), P(1 << 24), 1024, fake, fake, fake,
+                                   1 << 30, None) == -2
+    rc = lib.gptq_nvfp4_quantize_batched(fake, 1, 2, 16, 32, 32, 100, fake, 1024, fake, 1024, fake, 16, 0,
+                                         fake, fake, fake, None, fake, 1 << 30, None)
+    assert rc == -2
     for s in (0, -1, -2, -3, -4, -5, -6, -7, -8, 99):
         assert lib.nvq_status_string(s)
 
@@ -77,3 +93,6 @@ def test_workspace_queries_are_consistent():
     assert lib.factor_hinv_workspace_size(4096) >= 2 * 4096 * 4096 * 4
     assert lib.gptq_nvfp4_workspace_size(0, 16, 0) == 0
     assert lib.nvfp4_global_scale_workspace_size(16, 16) > 0
+    off = (ctypes.c_int64 * 4)(0, 100, 100, 350)
+    need = lib.hessian_grouped_workspace_size(off, 3, 256, 1)
+    assert need >= 250 * 256 * 2 + lib.hessian_workspace_size(250, 256, 1)
