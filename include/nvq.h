@@ -59,6 +59,13 @@ extern "C" {
 #define NVQ_FLAG_RTN    1u
 /* Do not compute the weighted error (row_err is not written; H may be NULL). */
 #define NVQ_FLAG_NO_ERR 2u
+/* fp64 working precision for the sweep: working weights, errors, scores and
+ * the lazy updates are fp64 (U and H are read as fp32 inputs; the weighted
+ * error is computed as without the flag).  For layers whose Hessian spans
+ * many orders of magnitude, where fp32 rounding alone moves more than 0.1%
+ * of the decisions of the exact computation.  Needs a larger workspace
+ * (gptq_nvfp4_workspace_size with the same flags).  Ignored with RTN. */
+#define NVQ_FLAG_FP64   4u
 
 /*
  * hessian_accumulate -- second-order state of the layer ("Replay the
@@ -185,7 +192,7 @@ int nvfp4_global_scale(const void* W, int w_dtype, int64_t m, int64_t k, int64_t
  * batch update the rest of its 512-column block at once, and the columns past
  * a finished 512-column block receive that block's errors together (fp32
  * MFMA GEMMs; the same sums as eager updates in another order); all working
- * values are fp32.
+ * values are fp32 (fp64 with NVQ_FLAG_FP64).
  *
  *   W        device [m x ldw], element type w_dtype (bf16 or fp32); not
  *            modified.  m > 0, k > 0, k % 16 == 0, ldw >= k, ldw % 4 == 0.

@@ -22,6 +22,7 @@ NVQ_DTYPE_F32 = 0
 NVQ_DTYPE_BF16 = 1
 FLAG_RTN = 1
 FLAG_NO_ERR = 2
+FLAG_FP64 = 4
 
 EXPORTS = [
     "hessian_workspace_size", "hessian_accumulate",
@@ -230,11 +231,11 @@ def gptq_nvfp4_quantize_batched(W, U, H, g, n_cand=16, flags=0):
     return out
 
 
-def quantize_layer(W, X, n_cand=16, damp_rel=0.01):
+def quantize_layer(W, X, n_cand=16, damp_rel=0.01, flags=0):
     """Whole layer: H = X^T X, U, g, the sweep and the weighted error (all on the GPU)."""
     H = hessian_accumulate(X)
     U, lam, info = factor_hinv(H, damp_rel)
     g = nvfp4_global_scale(W)
-    res = gptq_nvfp4_quantize(W, U, H, g, n_cand)
+    res = gptq_nvfp4_quantize(W, U, H, g, n_cand, flags)
     res.update(H=H, U=U, lam=lam, info=info, g=g)
     return res

@@ -41,11 +41,12 @@ struct QuantWs {
   size_t wp, eslab, invd, part, total;
 };
 
-QuantWs quant_ws(int64_t m, int64_t k) {
+QuantWs quant_ws(int64_t m, int64_t k, bool f64) {
   QuantWs w;
+  const size_t es = f64 ? sizeof(double) : sizeof(float);
   size_t off = 0;
-  w.wp = off;   off += align_up((size_t)m * k * sizeof(float));
-  w.eslab = off; off += align_up((size_t)m * kSuperBatch * sizeof(float));
+  w.wp = off;   off += align_up((size_t)m * k * es);
+  w.eslab = off; off += align_up((size_t)m * kSuperBatch * es);
   w.invd = off;  off += align_up((size_t)k * sizeof(float));
   w.part = off;  off += align_up((size_t)m * ((k + kGemmTile - 1) / kGemmTile) * sizeof(float));
   w.total = off;
@@ -86,7 +87,7 @@ int quant_check(const char* fn, const void* W, int w_dtype, int64_t m, int64_t k
                 const uint8_t* scales, const float* row_err, const void* ws, size_t ws_bytes) {
   const bool rtn = flags & NVQ_FLAG_RTN;
   const bool want_err = !(flags & NVQ_FLAG_NO_ERR);
-  if (flags & ~(NVQ_FLAG_RTN | NVQ_FLAG_NO_ERR)) return failp(NVQ_ERR_VALUE, fn, "unknown flags 0x%x", flags);
+  if (flags & ~(NVQ_FLAG_RTN | NVQ_FLAG_NO_ERR | NVQ_FLAG_FP64)) return failp(NVQ_ERR_VALUE, fn, "unknown flags 0x%x", flags);
   if (!W || !g || !codes || !scales) return failp(NVQ_ERR_NULL, fn, "W, g, codes and scales are required");
   if (!rtn && !U) return failp(NVQ_ERR_NULL, fn, "U is required without NVQ_FLAG_RTN");
   if (want_err && (!H || !row_err)) return failp(NVQ_ERR_NULL, fn, "H and row_err are required unless NVQ_FLAG_NO_ERR");
@@ -97,7 +98,7 @@ int quant_check(const char* fn, const void* W, int w_dtype, int64_t m, int64_t k
   if (n_cand < 1 || n_cand > 16) return failp(NVQ_ERR_NCAND, fn, "n_cand=%d", n_cand);
   if (!aligned(codes, 8)) return failp(NVQ_ERR_ALIGN, fn, "codes must be 8-byte aligned");
   if ((U && !aligned(U, 16)) || (H && !aligned(H, 16))) return failp(NVQ_ERR_ALIGN, fn, "U and H must be 16-byte aligned");
-  QuantWs L = quant_ws(m, k);
+  QuantWs L = quant_ws(m, k, (flags & NVQ_FLAG_FP64) && !rtn);
   if (!ws || ws_bytes < L.total || !aligned(ws, kAlign))
     return failp(NVQ_ERR_WORKSPACE, fn, "workspace needs %zu bytes (256-aligned), got %zu", L.total, ws_bytes);
   return NVQ_OK;
@@ -109,7 +110,8 @@ hipError_t quant_run(const void* W, int w_dtype, int64_t m, int64_t k, int64_t l
                      float* row_loss, char* base, hipStream_t s) {
   const bool rtn = flags & NVQ_FLAG_RTN;
   const bool want_err = !(flags & NVQ_FLAG_NO_ERR);
-  QuantWs L = quant_ws(m, k);
+  const bool f64 = (flags & NVQ_FLAG_FP64) && !rtn;
+  QuantWs L = quant_ws(m, k, f64);
   float* Wp = (float*)(base + L.wp);
   float* Eslab = (float*)(base + L.eslab);
   float* invd = (float*)(base + L.invd);
@@ -119,6 +121,25 @@ hipError_t quant_run(const void* W, int w_dtype, int64_t m, int64_t k, int64_t l
 
   if (rtn) {
     e = rtn_launch(W, bf, m, k, ldw, g, n_cand, codes, scales, row_loss, s);
+  } else if (f64) {
+    // The same sweep and two-level updates with fp64 working weights and errors.
+    double* Wd = (double*)(base + L.wp);
+    double* Ed = (double*)(base + L.eslab);
+    e = load_working_copy_f64(W, bf, m, k, ldw, Wd, s);
+    if (e == hipSuccess && row_loss) e = fill_f32(row_loss, m, 0.0f, s);
+    for (int64_t s0 = 0; e == hipSuccess && s0 < k; s0 += kSuperBatch) {
+      const int64_t s1 = std::min<int64_t>(k, s0 + kSuperBatch);
+      for (int64_t i1 = s0; e == hipSuccess && i1 < s1; i1 += kBatch) {
+        const int ncols = (int)std::min<int64_t>(kBatch, s1 - i1);
+        e = sweep_batch_launch_f64(Wd, U, g, m, k, (int)i1, ncols, n_cand, codes, scales, Ed + (i1 - s0),
+                                   kSuperBatch, row_loss, s);
+        const int64_t i2 = i1 + ncols;
+        if (e == hipSuccess && i2 < s1)
+          e = rank_update_f64(Ed + (i1 - s0), kSuperBatch, U + i1 * k + i2, k, Wd + i2, k, m, s1 - i2, ncols, s);
+      }
+      if (e == hipSuccess && s1 < k)
+        e = rank_update_f64(Ed, kSuperBatch, U + s0 * k + s1, k, Wd + s1, k, m, k - s1, s1 - s0, s);
+    }
   } else {
     e = inv_diag_launch(U, k, invd, s);
     if (e == hipSuccess) e = load_working_copy(W, bf, m, k, ldw, Wp, s);
@@ -310,9 +331,8 @@ int nvfp4_global_scale(const void* W, int w_dtype, int64_t m, int64_t k, int64_t
 
 // ---------------------------------------------------------------------------
 size_t gptq_nvfp4_workspace_size(int64_t m, int64_t k, unsigned flags) {
-  (void)flags;
   if (m <= 0 || k <= 0) return 0;
-  return quant_ws(m, k).total;
+  return quant_ws(m, k, (flags & NVQ_FLAG_FP64) && !(flags & NVQ_FLAG_RTN)).total;
 }
 
 int gptq_nvfp4_quantize(const void* W, int w_dtype, int64_t m, int64_t k, int64_t ldw, const float* U,

@@ -11,6 +11,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+typedef double f64x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBlock = 16;       // weights per E4M3 scale
 constexpr int kBatch = 128;      // lazy-batch width of the GPTQ sweep
@@ -93,6 +95,42 @@ __device__ __forceinline__ float e2m1_dequant(int code4, float s, float g) {
 __device__ __forceinline__ int e2m1_encode(float w, float s, float g) {
   int idx = e2m1_index(fabsf(w), s, g);
   return (idx != 0 && w < 0.0f) ? (idx | 8) : idx;
+}
+
+// fp64 working values: every threshold t * s * g (t * s at most 7 significant
+// bits, g 24) is exact in fp64, so plain comparisons are exact.
+__device__ __forceinline__ int e4m3_code_of_ratio(double a, float g) {
+  int lo = 0, hi = kE4m3MaxCode;
+#pragma unroll
+  for (int it = 0; it < 7; ++it) {
+    int mid = (lo + hi) >> 1;
+    if (lo >= hi) break;
+    double thr = (double)(3.0f * (e4m3_value(mid) + e4m3_value(mid + 1))) * (double)g;
+    bool pass = (mid & 1) ? (a >= thr) : (a > thr);
+    if (pass) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+__device__ __forceinline__ int e2m1_index(double aw, float s, float g) {
+  const double sg = (double)s * (double)g;
+  int idx = 0;
+  idx += aw > 0.25 * sg;
+  idx += aw >= 0.75 * sg;
+  idx += aw > 1.25 * sg;
+  idx += aw >= 1.75 * sg;
+  idx += aw > 2.50 * sg;
+  idx += aw >= 3.50 * sg;
+  idx += aw > 5.00 * sg;
+  return idx;
+}
+__device__ __forceinline__ int e2m1_encode(double w, float s, float g) {
+  int idx = e2m1_index(fabs(w), s, g);
+  return (idx != 0 && w < 0.0) ? (idx | 8) : idx;
+}
+// Exact signed value e2m1 * s * g in fp64.
+__device__ __forceinline__ double e2m1_dequant_f64(int code4, float s, float g) {
+  double v = (double)(e2m1_twice_mag(code4 & 7) * 0.5f * s) * (double)g;
+  return (code4 & 8) ? -v : v;
 }
 
 // First of the n_cand consecutive candidate codes around c0, inside [1, 126].

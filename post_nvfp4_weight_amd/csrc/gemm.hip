@@ -262,7 +262,88 @@ hipError_t launch(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---- fp64 rank update: C -= A B with A, C fp64 and B fp32 (widened) ------------
+// 64 x 64 tiles, 4 waves of 32 x 32 (2 x 2 v_mfma_f64_16x16x4f64 tiles), k in
+// chunks of 16.  MFMA f64 16x16x4: lane l supplies A[l%16][l/16] and
+// B[l/16][l%16]; result register r of lane l is row l/16 + 4r, column l%16.
+constexpr int F64_T = 64, F64_BK = 16;
+__global__ __launch_bounds__(256) void rank_update_f64_kernel(const double* __restrict__ A, int64_t lda,
+                                                              const float* __restrict__ B, int64_t ldb,
+                                                              double* __restrict__ C, int64_t ldc, int64_t M,
+                                                              int64_t N, int64_t K) {
+  __shared__ double As[F64_T][F64_BK + 1];   // -A tile, [row][k]
+  __shared__ double Bs[F64_BK][F64_T + 1];   // B tile, [k][column]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+  const int64_t m0 = (int64_t)blockIdx.y * F64_T, n0 = (int64_t)blockIdx.x * F64_T;
+  f64x4 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t row = m0 + wr * 32 + 16 * i + (lane >> 4) + 4 * r;
+        const int64_t col = n0 + wc * 32 + 16 * j + (lane & 15);
+        const double v = C[min(row, M - 1) * ldc + min(col, N - 1)];
+        acc[i][j][r] = (row < M && col < N) ? v : 0.0;
+      }
+  for (int64_t k0 = 0; k0 < K; k0 += F64_BK) {
+    double av[4];
+    float bv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = tid + 256 * q;
+      const int64_t gr = m0 + (e >> 4), gk = k0 + (e & 15);
+      const double x = A[min(gr, M - 1) * lda + min(gk, K - 1)];
+      av[q] = (gr < M && gk < K) ? -x : 0.0;
+      const int64_t gk2 = k0 + (e >> 6), gc = n0 + (e & 63);
+      const float y = B[min(gk2, K - 1) * ldb + min(gc, N - 1)];
+      bv[q] = (gk2 < K && gc < N) ? y : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = tid + 256 * q;
+      As[e >> 4][e & 15] = av[q];
+      Bs[e >> 6][e & 63] = (double)bv[q];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < F64_BK; kk += 4) {
+      double a[2], b[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        a[t] = As[wr * 32 + 16 * t + (lane & 15)][kk + (lane >> 4)];
+        b[t] = Bs[kk + (lane >> 4)][wc * 32 + 16 * t + (lane & 15)];
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t row = m0 + wr * 32 + 16 * i + (lane >> 4) + 4 * r;
+        const int64_t col = n0 + wc * 32 + 16 * j + (lane & 15);
+        if (row < M && col < N) C[row * ldc + col] = acc[i][j][r];
+      }
+}
+
 }  // namespace
+
+hipError_t rank_update_f64(const double* A, int64_t lda, const float* B, int64_t ldb, double* C, int64_t ldc,
+                           int64_t M, int64_t N, int64_t K, hipStream_t s) {
+  if (M <= 0 || N <= 0 || K <= 0) return hipSuccess;
+  dim3 grid((unsigned)((N + F64_T - 1) / F64_T), (unsigned)((M + F64_T - 1) / F64_T));
+  hipLaunchKernelGGL(rank_update_f64_kernel, grid, dim3(256), 0, s, A, lda, B, ldb, C, ldc, M, N, K);
+  return hipGetLastError();
+}
 
 hipError_t gemm_f32(const GemmArgs& a, bool ta, bool tb, bool lower, GemmEpi epi, hipStream_t s) {
   if (a.M <= 0 || a.N <= 0 || a.batch <= 0) return hipSuccess;

@@ -36,6 +36,9 @@ enum GemmK { kGemmKFull = 0, kGemmKLowerA = 1, kGemmKLowerB = 2, kGemmKSymUpperB
 hipError_t gemm_f32(const GemmArgs& a, bool trans_a, bool trans_b, bool lower, GemmEpi epi,
                     hipStream_t s);
 constexpr int kGemmTile = 128;
+// C -= A B with A [M x K] and C [M x N] fp64, B [K x N] fp32 (all row-major).
+hipError_t rank_update_f64(const double* A, int64_t lda, const float* B, int64_t ldb, double* C, int64_t ldc,
+                           int64_t M, int64_t N, int64_t K, hipStream_t s);
 
 // ---- Hessian -------------------------------------------------------------
 size_t syrk_bf16_workspace(int64_t n, int64_t k);
@@ -67,6 +70,12 @@ hipError_t sweep_batch_launch(float* Wp, const float* U, const float* invd, cons
                               int64_t m, int64_t k, int i1, int ncols, int n_cand,
                               uint8_t* codes, uint8_t* scales, float* Eslab, int64_t lde, float* row_loss,
                               hipStream_t s);
+// The same sweep with fp64 working weights and errors (U read as fp32).
+hipError_t sweep_batch_launch_f64(double* Wp, const float* U, const float* g, int64_t m, int64_t k, int i1,
+                                  int ncols, int n_cand, uint8_t* codes, uint8_t* scales, double* Eslab, int64_t lde,
+                                  float* row_loss, hipStream_t s);
+hipError_t load_working_copy_f64(const void* W, int bf16, int64_t m, int64_t k, int64_t ldw, double* Wp,
+                                 hipStream_t s);
 // Columns of the two-level lazy update: each 128-column batch updates the
 // rest of its 512-column block; each finished block updates every later
 // column with its whole error slab (m x 512).

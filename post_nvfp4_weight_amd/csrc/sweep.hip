@@ -144,6 +144,14 @@ __global__ __launch_bounds__(256) void rtn_kernel(const void* __restrict__ W, in
 
 // ---- sweep helpers ------------------------------------------------------------------
 template <int BF16>
+__global__ void load_working_f64_kernel(const void* __restrict__ W, int64_t m, int64_t k, int64_t ldw,
+                                        double* __restrict__ Wp) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= m * k) return;
+  Wp[e] = (double)load_w<BF16>(W, (e / k) * ldw + e % k);
+}
+
+template <int BF16>
 __global__ void load_working_kernel(const void* __restrict__ W, int64_t m, int64_t k, int64_t ldw,
                                     float* __restrict__ Wp) {
   int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
@@ -217,15 +225,34 @@ __device__ __forceinline__ float sum_step(float s) {
 // Lane pairings: xor 1 and xor 2 (quad_perm), then 8-lane and 16-lane mirrors.
 constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
 
-template <int G>
-__device__ __forceinline__ void group_argmin(float& s, int& i) {
+// fp64 values move as two 32-bit halves.
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const uint64_t u = __double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)u, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(u >> 32), CTRL, 0xF, 0xF, false);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+template <int CTRL>
+__device__ __forceinline__ void argmin_step(double& s, int& i) {
+  const double so = dpp_f64<CTRL>(s);
+  const int io = __builtin_amdgcn_mov_dpp(i, CTRL, 0xF, 0xF, false);
+  if (so < s || (so == s && io < i)) { s = so; i = io; }
+}
+template <int CTRL>
+__device__ __forceinline__ double sum_step(double s) {
+  return s + dpp_f64<CTRL>(s);
+}
+
+template <int G, typename T>
+__device__ __forceinline__ void group_argmin(T& s, int& i) {
   if (G >= 2) argmin_step<kDppXor1>(s, i);
   if (G >= 4) argmin_step<kDppXor2>(s, i);
   if (G >= 8) argmin_step<kDppHalfMirror>(s, i);
   if (G >= 16) argmin_step<kDppMirror>(s, i);
 }
-template <int G>
-__device__ __forceinline__ float group_sum(float s) {
+template <int G, typename T>
+__device__ __forceinline__ T group_sum(T s) {
   if (G >= 2) s = sum_step<kDppXor1>(s);
   if (G >= 4) s = sum_step<kDppXor2>(s);
   if (G >= 8) s = sum_step<kDppHalfMirror>(s);
@@ -235,20 +262,31 @@ __device__ __forceinline__ float group_sum(float s) {
 
 // A row's G candidate lanes always lie in one wave, so after the initial
 // loads the block loop needs no workgroup barrier: a wave's LDS accesses are
-// executed in program order.
-template <int G>
+// executed in program order.  T is the working precision (fp32, or fp64 for
+// layers whose Hessian spreads over many orders of magnitude); U stays fp32
+// (its values are exact inputs) and is widened where it is used.  In fp32 the
+// error of a column is (w' - q) times the rounded 1/U_jj; in fp64 it is the
+// quotient (w' - q) / U_jj.
+template <typename T>
+__device__ __forceinline__ void load16(const T* p, T (&v)[16]) {
+#pragma unroll
+  for (int q = 0; q < 16; ++q) v[q] = p[q];
+}
+
+template <int G, typename T>
 __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
-    float* __restrict__ Wp, const float* __restrict__ U, const float* __restrict__ invd,
+    T* __restrict__ Wp, const float* __restrict__ U, const float* __restrict__ invd,
     const float* __restrict__ gptr, int64_t m, int64_t k, int i1, int ncols, int n_cand,
-    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ Eslab, int64_t lde,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, T* __restrict__ Eslab, int64_t lde,
     float* __restrict__ row_loss) {
+  constexpr bool F64 = sizeof(T) == 8;
   constexpr int ROWS = SweepCfg<G>::ROWS;
   constexpr int NT = SweepCfg<G>::THREADS;
   __shared__ __attribute__((aligned(16))) float Ut[kBatch * UT_LD];      // Ut[c][r] = U[i1+r][i1+c]
   __shared__ __attribute__((aligned(16))) float Ud[kBatch / kBlock][kBlock][kBlock];  // diagonal 16x16 blocks
   __shared__ __attribute__((aligned(16))) float id_s[kBatch];
-  __shared__ __attribute__((aligned(16))) float slab[ROWS][kBatch];
-  __shared__ __attribute__((aligned(16))) float eb_s[ROWS][16];
+  __shared__ __attribute__((aligned(16))) T slab[ROWS][kBatch];
+  __shared__ __attribute__((aligned(16))) T eb_s[ROWS][16];
 
   const int tid = threadIdx.x;
   const int rl = tid / G, ci = tid % G;
@@ -267,40 +305,46 @@ __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
   for (int e = tid; e < ROWS * kBatch; e += NT) {
     const int r = e / kBatch, c = e % kBatch;
     const int64_t gr = (int64_t)blockIdx.x * ROWS + r;
-    slab[r][c] = (gr < m && c < ncols) ? Wp[gr * k + i1 + c] : 0.0f;
+    slab[r][c] = (gr < m && c < ncols) ? Wp[gr * k + i1 + c] : T(0);
   }
   __syncthreads();
 
-  float loss = 0.0f;
+  T loss = 0;
   const int nblk = ncols / kBlock;
   for (int b = 0; b < nblk; ++b) {
     const int c0 = b * kBlock;
-    float v[16];
+    T v[16];
+    if constexpr (F64) {
+      load16(&slab[rl][c0], v);
+    } else {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      f32x4 t = *(const f32x4*)&slab[rl][c0 + 4 * q];
-      v[4 * q] = t[0]; v[4 * q + 1] = t[1]; v[4 * q + 2] = t[2]; v[4 * q + 3] = t[3];
+      for (int q = 0; q < 4; ++q) {
+        f32x4 t = *(const f32x4*)&slab[rl][c0 + 4 * q];
+        v[4 * q] = t[0]; v[4 * q + 1] = t[1]; v[4 * q + 2] = t[2]; v[4 * q + 3] = t[3];
+      }
     }
-    float a = 0.0f;
+    T a = 0;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) a = fmaxf(a, fabsf(v[j]));
+    for (int j = 0; j < 16; ++j) a = fmax(a, fabs(v[j]));
 
-    float e[16];
+    T e[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) e[j] = 0.0f;
+    for (int j = 0; j < 16; ++j) e[j] = 0;
     uint32_t plo = 0, phi = 0;
     int cand = 0;
-    float score = __builtin_inff();
-    if (a > 0.0f) {
+    T score = F64 ? T(__builtin_inf()) : T(__builtin_inff());
+    if (a > T(0)) {
       const int lo = candidate_lo(e4m3_code_of_ratio(a, g), n_cand);
       cand = lo + (ci < n_cand ? ci : 0);
       const float s = e4m3_value(cand);
-      float sc = 0.0f;
+      T sc = 0;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
         const int code = e2m1_encode(v[j], s, g);
-        const float ej = (v[j] - e2m1_dequant(code, s, g)) * id_s[c0 + j];
-        sc = fmaf(ej, ej, sc);
+        T ej;
+        if constexpr (F64) ej = (v[j] - e2m1_dequant_f64(code, s, g)) / (T)Ud[b][j][j];
+        else ej = (v[j] - e2m1_dequant(code, s, g)) * id_s[c0 + j];
+        sc = fma(ej, ej, sc);
         if (j + 1 < 16) {
           float urow[16];
 #pragma unroll
@@ -309,49 +353,41 @@ __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
             urow[4 * q] = t[0]; urow[4 * q + 1] = t[1]; urow[4 * q + 2] = t[2]; urow[4 * q + 3] = t[3];
           }
 #pragma unroll
-          for (int l = j + 1; l < 16; ++l) v[l] = fmaf(-ej, urow[l], v[l]);
+          for (int l = j + 1; l < 16; ++l) v[l] = fma(-ej, (T)urow[l], v[l]);
         }
         e[j] = ej;
         if (j < 8) plo |= (uint32_t)code << (4 * j); else phi |= (uint32_t)code << (4 * (j - 8));
       }
       if (ci < n_cand) score = sc;
     }
-    float bs = score;
+    T bs = score;
     int bi = ci;
     group_argmin<G>(bs, bi);
     if (ci == bi && row_ok) {
-      *(f32x4*)&eb_s[rl][0] = f32x4{e[0], e[1], e[2], e[3]};
-      *(f32x4*)&eb_s[rl][4] = f32x4{e[4], e[5], e[6], e[7]};
-      *(f32x4*)&eb_s[rl][8] = f32x4{e[8], e[9], e[10], e[11]};
-      *(f32x4*)&eb_s[rl][12] = f32x4{e[12], e[13], e[14], e[15]};
+#pragma unroll
+      for (int j = 0; j < 16; ++j) eb_s[rl][j] = e[j];
       const int64_t gb = (i1 + c0) / kBlock;
       *(u32x2*)(codes + row * (k / 2) + gb * 8) = u32x2{plo, phi};
       scales[row * (k / kBlock) + gb] = (uint8_t)cand;
-      f32x4* es = (f32x4*)(Eslab + row * lde + c0);
-      es[0] = f32x4{e[0], e[1], e[2], e[3]};
-      es[1] = f32x4{e[4], e[5], e[6], e[7]};
-      es[2] = f32x4{e[8], e[9], e[10], e[11]};
-      es[3] = f32x4{e[12], e[13], e[14], e[15]};
-      if (a > 0.0f) loss += bs;
+      T* es = Eslab + row * lde + c0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) es[j] = e[j];
+      if (a > T(0)) loss += bs;
     }
     // Update the later columns of the batch: w'_l -= sum_j e_j U[c0+j][l].
     if (row_ok && c0 + kBlock < ncols) {
-      float eb[16];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        f32x4 t = *(const f32x4*)&eb_s[rl][4 * q];
-        eb[4 * q] = t[0]; eb[4 * q + 1] = t[1]; eb[4 * q + 2] = t[2]; eb[4 * q + 3] = t[3];
-      }
+      T eb[16];
+      load16(&eb_s[rl][0], eb);
       for (int cc = c0 + kBlock + ci; cc < ncols; cc += G) {
-        float acc = slab[rl][cc];
+        T acc = slab[rl][cc];
         const float* ut = &Ut[cc * UT_LD + c0];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           f32x4 u4 = *(const f32x4*)(ut + 4 * q);
-          acc = fmaf(-eb[4 * q + 0], u4[0], acc);
-          acc = fmaf(-eb[4 * q + 1], u4[1], acc);
-          acc = fmaf(-eb[4 * q + 2], u4[2], acc);
-          acc = fmaf(-eb[4 * q + 3], u4[3], acc);
+          acc = fma(-eb[4 * q + 0], (T)u4[0], acc);
+          acc = fma(-eb[4 * q + 1], (T)u4[1], acc);
+          acc = fma(-eb[4 * q + 2], (T)u4[2], acc);
+          acc = fma(-eb[4 * q + 3], (T)u4[3], acc);
         }
         slab[rl][cc] = acc;
       }
@@ -359,18 +395,28 @@ __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
   }
   // Per-row loss: the winners' scores are spread over the row's lanes.
   loss = group_sum<G>(loss);
-  if (ci == 0 && row_ok && row_loss) row_loss[row] += loss;
+  if (ci == 0 && row_ok && row_loss) row_loss[row] += (float)loss;
 }
 
-template <int G>
-hipError_t sweep_launch_g(float* Wp, const float* U, const float* invd, const float* g, int64_t m, int64_t k,
-                          int i1, int ncols, int n_cand, uint8_t* codes, uint8_t* scales, float* Eslab,
+template <int G, typename T>
+hipError_t sweep_launch_g(T* Wp, const float* U, const float* invd, const float* g, int64_t m, int64_t k,
+                          int i1, int ncols, int n_cand, uint8_t* codes, uint8_t* scales, T* Eslab,
                           int64_t lde, float* row_loss, hipStream_t s) {
   constexpr int ROWS = SweepCfg<G>::ROWS;
   dim3 grid((unsigned)((m + ROWS - 1) / ROWS));
-  hipLaunchKernelGGL(sweep_batch_kernel<G>, grid, dim3(SweepCfg<G>::THREADS), 0, s, Wp, U, invd, g, m, k, i1,
-                     ncols, n_cand, codes, scales, Eslab, lde, row_loss);
+  hipLaunchKernelGGL((sweep_batch_kernel<G, T>), grid, dim3(SweepCfg<G>::THREADS), 0, s, Wp, U, invd, g, m, k,
+                     i1, ncols, n_cand, codes, scales, Eslab, lde, row_loss);
   return hipGetLastError();
+}
+template <typename T>
+hipError_t sweep_launch_t(T* Wp, const float* U, const float* invd, const float* g, int64_t m, int64_t k, int i1,
+                          int ncols, int n_cand, uint8_t* codes, uint8_t* scales, T* Eslab, int64_t lde,
+                          float* row_loss, hipStream_t s) {
+  if (n_cand <= 1) return sweep_launch_g<1>(Wp, U, invd, g, m, k, i1, ncols, n_cand, codes, scales, Eslab, lde, row_loss, s);
+  if (n_cand <= 2) return sweep_launch_g<2>(Wp, U, invd, g, m, k, i1, ncols, n_cand, codes, scales, Eslab, lde, row_loss, s);
+  if (n_cand <= 4) return sweep_launch_g<4>(Wp, U, invd, g, m, k, i1, ncols, n_cand, codes, scales, Eslab, lde, row_loss, s);
+  if (n_cand <= 8) return sweep_launch_g<8>(Wp, U, invd, g, m, k, i1, ncols, n_cand, codes, scales, Eslab, lde, row_loss, s);
+  return sweep_launch_g<16>(Wp, U, invd, g, m, k, i1, ncols, n_cand, codes, scales, Eslab, lde, row_loss, s);
 }
 
 }  // namespace
@@ -430,14 +476,25 @@ hipError_t inv_diag_launch(const float* U, int64_t k, float* invd, hipStream_t s
   return hipGetLastError();
 }
 
+hipError_t load_working_copy_f64(const void* W, int bf16, int64_t m, int64_t k, int64_t ldw, double* Wp,
+                                 hipStream_t s) {
+  dim3 grid((unsigned)((m * k + 255) / 256));
+  if (bf16)
+    hipLaunchKernelGGL(load_working_f64_kernel<1>, grid, dim3(256), 0, s, W, m, k, ldw, Wp);
+  else
+    hipLaunchKernelGGL(load_working_f64_kernel<0>, grid, dim3(256), 0, s, W, m, k, ldw, Wp);
+  return hipGetLastError();
+}
+
 hipError_t sweep_batch_launch(float* Wp, const float* U, const float* invd, const float* g, int64_t m, int64_t k,
                               int i1, int ncols, int n_cand, uint8_t* codes, uint8_t* scales, float* Eslab,
                               int64_t lde, float* row_loss, hipStream_t s) {
-  if (n_cand <= 1) return sweep_launch_g<1>(Wp, U, invd, g, m, k, i1, ncols, n_cand, codes, scales, Eslab, lde, row_loss, s);
-  if (n_cand <= 2) return sweep_launch_g<2>(Wp, U, invd, g, m, k, i1, ncols, n_cand, codes, scales, Eslab, lde, row_loss, s);
-  if (n_cand <= 4) return sweep_launch_g<4>(Wp, U, invd, g, m, k, i1, ncols, n_cand, codes, scales, Eslab, lde, row_loss, s);
-  if (n_cand <= 8) return sweep_launch_g<8>(Wp, U, invd, g, m, k, i1, ncols, n_cand, codes, scales, Eslab, lde, row_loss, s);
-  return sweep_launch_g<16>(Wp, U, invd, g, m, k, i1, ncols, n_cand, codes, scales, Eslab, lde, row_loss, s);
+  return sweep_launch_t<float>(Wp, U, invd, g, m, k, i1, ncols, n_cand, codes, scales, Eslab, lde, row_loss, s);
+}
+hipError_t sweep_batch_launch_f64(double* Wp, const float* U, const float* g, int64_t m, int64_t k, int i1,
+                                  int ncols, int n_cand, uint8_t* codes, uint8_t* scales, double* Eslab, int64_t lde,
+                                  float* row_loss, hipStream_t s) {
+  return sweep_launch_t<double>(Wp, U, U, g, m, k, i1, ncols, n_cand, codes, scales, Eslab, lde, row_loss, s);
 }
 
 hipError_t delta_w_launch(const void* W, int bf16, int64_t m, int64_t k, int64_t ldw, const uint8_t* codes,

@@ -187,6 +187,26 @@ def test_sweep_matches_oracle(nvq, m, k, n, K):
     assert np.allclose(loss, ref64["score"], rtol=1e-3)
 
 
+@pytest.mark.parametrize("m,k,n", [(200, 384, 3000), (64, 1040, 4096)])
+def test_sweep_fp64_working_precision_matches_fp64_oracle(nvq, m, k, n):
+    W, X = synth.attn_proj_layer(m, k, n)
+    H = gptq.hessian(X)
+    Uref, _ = gptq.hinv_factor(H)
+    g = codec.global_scale(W)
+    U32 = Uref.astype(np.float32)
+    out = nvq.gptq_nvfp4_quantize(_to_dev(W, torch.bfloat16), _to_dev(U32), _to_dev(H.astype(np.float32)),
+                                  _to_dev(np.array([g])), 16, nvq.FLAG_FP64)
+    codes = codec.unpack_codes(out["codes"].cpu().numpy())
+    scales = out["scales"].cpu().numpy()
+    ref = gptq.sweep(W, U32, g, 16)   # fp64 arithmetic on the same fp32 U
+    assert _mismatch(codes, ref["codes"]) <= 1e-4
+    assert _mismatch(scales, ref["scales"]) <= 1e-4
+    assert np.allclose(out["row_loss"].cpu().numpy(), ref["score"], rtol=1e-5)
+    deq = codec.dequantize(codec.pack_codes(codes), scales, g)
+    E_own = gptq.weighted_error(W, deq, H)
+    assert np.allclose(out["row_err"].cpu().numpy().astype(np.float64), E_own, rtol=1e-4, atol=1e-6 * E_own.max())
+
+
 def test_identity_hessian_one_candidate_is_rtn(nvq):
     W = synth.weights("attn_proj", 48, 384, 0.02, outlier_frac=0.01)
     g = codec.global_scale(W)
