@@ -104,6 +104,59 @@ int quant_check(const char* fn, const void* W, int w_dtype, int64_t m, int64_t k
   return NVQ_OK;
 }
 
+// Weighted error of output columns [c0, c1) given dW for every column < c1:
+// dW H' dW^T restricted to those columns, H' = 2 triu(H, 1) + diag(H), into
+// the per-column-tile partial sums.
+hipError_t error_tiles(const float* H, float* dW, float* part, int64_t m, int64_t k, int64_t c0, int64_t c1,
+                       hipStream_t s) {
+  GemmArgs a{};
+  a.A = dW; a.lda = k;
+  a.B = H + c0; a.ldb = k;
+  a.D = dW + c0; a.ldd = k;
+  a.P = part + c0 / kGemmTile; a.ldp = (k + kGemmTile - 1) / kGemmTile;
+  a.M = m; a.N = c1 - c0; a.K = c1; a.batch = 1; a.alpha = 1.0f; a.beta = 0.0f;
+  a.kmode = kGemmKSymUpperB; a.noff = c0;
+  return gemm_f32(a, false, false, false, kEpiRowDot, s);
+}
+
+hipError_t weighted_error_all(const void* W, int bf, int64_t m, int64_t k, int64_t ldw, const float* H,
+                              const float* g, const uint8_t* codes, const uint8_t* scales, float* row_err, float* dW,
+                              float* part, hipStream_t s) {
+  hipError_t e = delta_w_launch(W, bf, m, k, ldw, codes, scales, g, dW, s);
+  if (e == hipSuccess) e = error_tiles(H, dW, part, m, k, 0, k, s);
+  if (e == hipSuccess) e = row_sum_launch(part, m, (k + kGemmTile - 1) / kGemmTile, row_err, s);
+  return e;
+}
+
+// The fp32 sweep with two-level lazy updates (the same sums as eager GPTQ
+// updates, in another order): a batch's errors update the rest of its
+// 512-column block at once, and a finished block's error slab updates every
+// later column.
+hipError_t sweep_f32(int64_t m, int64_t k, const float* U, const float* g, int n_cand, uint8_t* codes,
+                     uint8_t* scales, float* row_loss, float* Wp, float* Eslab, const float* invd, hipStream_t s) {
+  auto rank_update = [&](const float* Eb, int64_t r0, int64_t c0, int64_t kk, int64_t ncol) {
+    GemmArgs a{};
+    a.A = Eb; a.lda = kSuperBatch;
+    a.B = U + r0 * k + c0; a.ldb = k;
+    a.C = Wp + c0; a.ldc = k;
+    a.M = m; a.N = ncol; a.K = kk; a.batch = 1; a.alpha = -1.0f; a.beta = 1.0f;
+    return gemm_f32(a, false, false, false, kEpiAxpby, s);
+  };
+  hipError_t e = hipSuccess;
+  for (int64_t s0 = 0; e == hipSuccess && s0 < k; s0 += kSuperBatch) {
+    const int64_t s1 = std::min<int64_t>(k, s0 + kSuperBatch);
+    for (int64_t i1 = s0; e == hipSuccess && i1 < s1; i1 += kBatch) {
+      const int ncols = (int)std::min<int64_t>(kBatch, s1 - i1);
+      e = sweep_batch_launch(Wp, U, invd, g, m, k, (int)i1, ncols, n_cand, codes, scales, Eslab + (i1 - s0),
+                             kSuperBatch, row_loss, s);
+      const int64_t i2 = i1 + ncols;
+      if (e == hipSuccess && i2 < s1) e = rank_update(Eslab + (i1 - s0), i1, i2, ncols, s1 - i2);
+    }
+    if (e == hipSuccess && s1 < k) e = rank_update(Eslab, s0, s1, s1 - s0, k - s1);
+  }
+  return e;
+}
+
 // The quantization of one weight matrix (arguments already checked).
 hipError_t quant_run(const void* W, int w_dtype, int64_t m, int64_t k, int64_t ldw, const float* U, const float* H,
                      const float* g, int n_cand, unsigned flags, uint8_t* codes, uint8_t* scales, float* row_err,
@@ -144,43 +197,9 @@ hipError_t quant_run(const void* W, int w_dtype, int64_t m, int64_t k, int64_t l
     e = inv_diag_launch(U, k, invd, s);
     if (e == hipSuccess) e = load_working_copy(W, bf, m, k, ldw, Wp, s);
     if (e == hipSuccess && row_loss) e = fill_f32(row_loss, m, 0.0f, s);
-    // Two-level lazy updates (the same sums as eager GPTQ updates, in another
-    // order): a batch's errors update the rest of its 512-column block at
-    // once, and the later columns receive the whole block's errors together.
-    auto rank_update = [&](const float* Eb, int64_t r0, int64_t c0, int64_t kk, int64_t ncol) {
-      GemmArgs a{};
-      a.A = Eb; a.lda = kSuperBatch;
-      a.B = U + r0 * k + c0; a.ldb = k;
-      a.C = Wp + c0; a.ldc = k;
-      a.M = m; a.N = ncol; a.K = kk; a.batch = 1; a.alpha = -1.0f; a.beta = 1.0f;
-      return gemm_f32(a, false, false, false, kEpiAxpby, s);
-    };
-    for (int64_t s0 = 0; e == hipSuccess && s0 < k; s0 += kSuperBatch) {
-      const int64_t s1 = std::min<int64_t>(k, s0 + kSuperBatch);
-      for (int64_t i1 = s0; e == hipSuccess && i1 < s1; i1 += kBatch) {
-        const int ncols = (int)std::min<int64_t>(kBatch, s1 - i1);
-        e = sweep_batch_launch(Wp, U, invd, g, m, k, (int)i1, ncols, n_cand, codes, scales, Eslab + (i1 - s0),
-                               kSuperBatch, row_loss, s);
-        const int64_t i2 = i1 + ncols;
-        if (e == hipSuccess && i2 < s1) e = rank_update(Eslab + (i1 - s0), i1, i2, ncols, s1 - i2);
-      }
-      if (e == hipSuccess && s1 < k) e = rank_update(Eslab, s0, s1, s1 - s0, k - s1);
-    }
+    if (e == hipSuccess) e = sweep_f32(m, k, U, g, n_cand, codes, scales, row_loss, Wp, Eslab, invd, s);
   }
-  if (e == hipSuccess && want_err) {
-    e = delta_w_launch(W, bf, m, k, ldw, codes, scales, g, Wp, s);
-    if (e == hipSuccess) {
-      GemmArgs a{};
-      a.A = Wp; a.lda = k;
-      a.B = H; a.ldb = k;
-      a.D = Wp; a.ldd = k;
-      a.P = part; a.ldp = (k + kGemmTile - 1) / kGemmTile;
-      // dW H dW^T = dW H' dW^T with H' = 2 triu(H, 1) + diag(H): half the products.
-      a.M = m; a.N = k; a.K = k; a.batch = 1; a.alpha = 1.0f; a.beta = 0.0f; a.kmode = kGemmKSymUpperB;
-      e = gemm_f32(a, false, false, false, kEpiRowDot, s);
-    }
-    if (e == hipSuccess) e = row_sum_launch(part, m, (k + kGemmTile - 1) / kGemmTile, row_err, s);
-  }
+  if (e == hipSuccess && want_err) e = weighted_error_all(W, bf, m, k, ldw, H, g, codes, scales, row_err, Wp, part, s);
   return e;
 }
 

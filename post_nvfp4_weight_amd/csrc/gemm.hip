@@ -158,15 +158,15 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
   // makes the rest zero).
   int64_t klo = 0, khi = p.K;
   if (p.kmode == kGemmKLowerA) khi = min(p.K, m0 + BM);
-  if (p.kmode == kGemmKLowerB) klo = n0;
-  if (p.kmode == kGemmKSymUpperB) khi = min(p.K, n0 + BN);
+  if (p.kmode == kGemmKLowerB) klo = p.noff + n0;
+  if (p.kmode == kGemmKSymUpperB) khi = min(p.K, p.noff + n0 + BN);
   const int64_t c0 = klo / BK, nk = (khi + BK - 1) / BK;
   const bool sym = p.kmode == kGemmKSymUpperB;
   f32x4 ra[4], rb[4];
   if (c0 < nk) {
     load_tile<AK>(A, p.lda, m0, p.M, c0 * BK, p.K, tid, ra);
     load_tile<BKM>(B, p.ldb, n0, p.N, c0 * BK, p.K, tid, rb);
-    if (sym) sym_upper<BKM>(rb, tid, c0 * BK, n0);
+    if (sym) sym_upper<BKM>(rb, tid, c0 * BK, p.noff + n0);
     store_tile<AK>(smem, tid, ra, alpha_a);
     store_tile<BKM>(smem + OPER_FLOATS, tid, rb);
   }
@@ -195,7 +195,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
     }
     if (c + 1 < nk) {
       float* nxt = smem + (cur ^ 1) * 2 * OPER_FLOATS;
-      if (sym) sym_upper<BKM>(rb, tid, (c + 1) * BK, n0);
+      if (sym) sym_upper<BKM>(rb, tid, (c + 1) * BK, p.noff + n0);
       store_tile<AK>(nxt, tid, ra, alpha_a);
       store_tile<BKM>(nxt + OPER_FLOATS, tid, rb);
     }

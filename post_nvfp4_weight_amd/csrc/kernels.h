@@ -22,6 +22,7 @@ struct GemmArgs {
   int batch;
   float alpha, beta;
   int kmode;            // GemmK: which part of the k range each output tile needs
+  int64_t noff;         // column of C (and of B) 0 within the whole matrix, for kmode's triangle
 };
 // kmode: kGemmKFull; kGemmKLowerA (A lower triangular: row tile i needs
 // k < its last row); kGemmKLowerB (B lower triangular: column tile j needs
@@ -82,7 +83,7 @@ hipError_t load_working_copy_f64(const void* W, int bf16, int64_t m, int64_t k, 
 constexpr int kSuperBatch = 512;
 hipError_t delta_w_launch(const void* W, int bf16, int64_t m, int64_t k, int64_t ldw,
                           const uint8_t* codes, const uint8_t* scales, const float* g,
-                          float* dW, hipStream_t s);
+                          float* dW, hipStream_t s, int64_t c0 = 0, int64_t c1 = -1);
 hipError_t row_sum_launch(const float* P, int64_t m, int64_t nparts, float* out, hipStream_t s);
 hipError_t fill_f32(float* p, int64_t n, float v, hipStream_t s);
 

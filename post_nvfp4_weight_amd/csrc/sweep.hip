@@ -173,11 +173,12 @@ template <int BF16>
 __global__ __launch_bounds__(256) void delta_w_kernel(const void* __restrict__ W, int64_t m, int64_t k,
                                                       int64_t ldw, const uint8_t* __restrict__ codes,
                                                       const uint8_t* __restrict__ scales,
-                                                      const float* __restrict__ gptr, float* __restrict__ dW) {
+                                                      const float* __restrict__ gptr, float* __restrict__ dW,
+                                                      int64_t blk0, int64_t nblk) {
   const int64_t nbk = k / kBlock;
-  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (b >= m * nbk) return;
-  const int64_t row = b / nbk, blk = b % nbk;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= m * nblk) return;
+  const int64_t row = t / nblk, blk = blk0 + t % nblk, b = row * nbk + blk;
   const float g = *gptr;
   const float s = e4m3_value(scales[b] & 0x7F);
   u32x2 c = *(const u32x2*)(codes + b * 8);
@@ -294,18 +295,73 @@ __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
   const bool row_ok = row < m;
   const float g = *gptr;
 
-  for (int e = tid; e < kBatch * kBatch; e += NT) {
-    const int r = e / kBatch, c = e % kBatch;
-    float v = 0.0f;
-    if (r < ncols && c < ncols && r <= c) v = U[(int64_t)(i1 + r) * k + i1 + c];
-    Ut[c * UT_LD + r] = v;
-    if ((r >> 4) == (c >> 4)) Ud[r >> 4][r & 15][c & 15] = v;
+  // Staging: Ut[c][r] = U[i1+r][i1+c] for r <= c < ncols (0 elsewhere), the
+  // diagonal 16x16 blocks, 1/U_jj and the rows' slab of W'.  Every load is a
+  // 16-byte vector at a clamped (always valid) address and the loads of a
+  // chunk are all issued before its LDS writes.  ncols is a multiple of 16.
+  constexpr int Q = kBatch / 4;                       // float4 per tile row
+  constexpr int UCH = (kBatch * Q) / NT < 16 ? (kBatch * Q) / NT : 16;
+  constexpr int VT = 16 / sizeof(T);                  // slab elements per vector
+  constexpr int SV = ROWS * kBatch / VT;              // slab vectors
+  constexpr int SCH = SV / NT < 8 ? SV / NT : 8;
+  static_assert((kBatch * Q) % (NT * UCH) == 0 && SV % (NT * SCH) == 0, "staging chunks");
+  typedef T tvec __attribute__((ext_vector_type(VT)));
+  const int64_t row0 = (int64_t)blockIdx.x * ROWS;
+  constexpr int IDN = (kBatch + NT - 1) / NT;
+  float idv[IDN];
+#pragma unroll
+  for (int j = 0; j < IDN; ++j) idv[j] = invd[i1 + min(tid + j * NT, ncols - 1)];
+  auto slab_load = [&](int base, tvec (&w)[SCH]) {
+#pragma unroll
+    for (int it = 0; it < SCH; ++it) {
+      const int idx = base + it * NT + tid;
+      const int64_t gr = min(row0 + idx / (kBatch / VT), m - 1);
+      const int c = min((idx % (kBatch / VT)) * VT, ncols - VT);
+      w[it] = *(const tvec*)(Wp + gr * k + i1 + c);
+    }
+  };
+  auto slab_store = [&](int base, const tvec (&w)[SCH]) {
+#pragma unroll
+    for (int it = 0; it < SCH; ++it) {
+      const int idx = base + it * NT + tid;
+      const int r = idx / (kBatch / VT), c = (idx % (kBatch / VT)) * VT;
+      const bool ok = row0 + r < m && c < ncols;
+      tvec v;
+#pragma unroll
+      for (int t = 0; t < VT; ++t) v[t] = ok ? w[it][t] : T(0);
+      *(tvec*)&slab[r][c] = v;
+    }
+  };
+  tvec w0[SCH];
+  slab_load(0, w0);
+  for (int base = 0; base < kBatch * Q; base += NT * UCH) {
+    f32x4 u[UCH];
+#pragma unroll
+    for (int it = 0; it < UCH; ++it) {
+      const int idx = base + it * NT + tid;
+      const int r = min(idx / Q, ncols - 1), c = min((idx % Q) * 4, ncols - 4);
+      u[it] = *(const f32x4*)(U + (int64_t)(i1 + r) * k + i1 + c);
+    }
+    if (base == 0) slab_store(0, w0);
+#pragma unroll
+    for (int it = 0; it < UCH; ++it) {
+      const int idx = base + it * NT + tid;
+      const int r = idx / Q, c = (idx % Q) * 4;
+      f32x4 v;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) v[t] = (r < ncols && c + t < ncols && r <= c + t) ? u[it][t] : 0.0f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) Ut[(c + t) * UT_LD + r] = v[t];
+      if ((r >> 4) == (c >> 4)) *(f32x4*)&Ud[r >> 4][r & 15][c & 15] = v;
+    }
   }
-  for (int e = tid; e < kBatch; e += NT) id_s[e] = e < ncols ? invd[i1 + e] : 0.0f;
-  for (int e = tid; e < ROWS * kBatch; e += NT) {
-    const int r = e / kBatch, c = e % kBatch;
-    const int64_t gr = (int64_t)blockIdx.x * ROWS + r;
-    slab[r][c] = (gr < m && c < ncols) ? Wp[gr * k + i1 + c] : T(0);
+#pragma unroll
+  for (int j = 0; j < IDN; ++j)
+    if (tid + j * NT < kBatch) id_s[tid + j * NT] = tid + j * NT < ncols ? idv[j] : 0.0f;
+  for (int base = NT * SCH; base < SV; base += NT * SCH) {
+    tvec w[SCH];
+    slab_load(base, w);
+    slab_store(base, w);
   }
   __syncthreads();
 
@@ -498,13 +554,15 @@ hipError_t sweep_batch_launch_f64(double* Wp, const float* U, const float* g, in
 }
 
 hipError_t delta_w_launch(const void* W, int bf16, int64_t m, int64_t k, int64_t ldw, const uint8_t* codes,
-                          const uint8_t* scales, const float* g, float* dW, hipStream_t s) {
-  int64_t nblk = m * (k / kBlock);
-  dim3 grid((unsigned)((nblk + 255) / 256));
+                          const uint8_t* scales, const float* g, float* dW, hipStream_t s, int64_t c0, int64_t c1) {
+  if (c1 < 0) c1 = k;
+  const int64_t blk0 = c0 / kBlock, nblk = (c1 - c0) / kBlock;
+  if (m <= 0 || nblk <= 0) return hipSuccess;
+  dim3 grid((unsigned)((m * nblk + 255) / 256));
   if (bf16)
-    hipLaunchKernelGGL(delta_w_kernel<1>, grid, dim3(256), 0, s, W, m, k, ldw, codes, scales, g, dW);
+    hipLaunchKernelGGL(delta_w_kernel<1>, grid, dim3(256), 0, s, W, m, k, ldw, codes, scales, g, dW, blk0, nblk);
   else
-    hipLaunchKernelGGL(delta_w_kernel<0>, grid, dim3(256), 0, s, W, m, k, ldw, codes, scales, g, dW);
+    hipLaunchKernelGGL(delta_w_kernel<0>, grid, dim3(256), 0, s, W, m, k, ldw, codes, scales, g, dW, blk0, nblk);
   return hipGetLastError();
 }
 
