@@ -286,7 +286,8 @@ __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
   __shared__ __attribute__((aligned(16))) float Ut[kBatch * UT_LD];      // Ut[c][r] = U[i1+r][i1+c]
   __shared__ __attribute__((aligned(16))) float Ud[kBatch / kBlock][kBlock][kBlock];  // diagonal 16x16 blocks
   __shared__ __attribute__((aligned(16))) float id_s[kBatch];
-  __shared__ __attribute__((aligned(16))) T slab[ROWS][kBatch];
+  // Rows padded by 64 bytes: the four rows a wave touches fall on distinct banks.
+  __shared__ __attribute__((aligned(16))) T slab[ROWS][kBatch + 64 / sizeof(T)];
   __shared__ __attribute__((aligned(16))) T eb_s[ROWS][16];
 
   const int tid = threadIdx.x;
@@ -299,12 +300,17 @@ __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
   // diagonal 16x16 blocks, 1/U_jj and the rows' slab of W'.  Every load is a
   // 16-byte vector at a clamped (always valid) address and the loads of a
   // chunk are all issued before its LDS writes.  ncols is a multiple of 16.
-  constexpr int Q = kBatch / 4;                       // float4 per tile row
-  constexpr int UCH = (kBatch * Q) / NT < 16 ? (kBatch * Q) / NT : 16;
+  // U is staged by 16x16 tiles on or above the diagonal (the kernel reads
+  // no other part): one wave-instruction loads a tile as 16 rows x 4 float4,
+  // so the transposed LDS writes of its 64 lanes hit 64 distinct banks.
+  constexpr int NW = NT / 64;                         // waves
+  constexpr int NTILE = (kBatch / 16) * (kBatch / 16 + 1) / 2;
+  constexpr int UCH = NTILE / NW < 9 ? NTILE / NW : 9;   // tiles per wave in flight
+  static_assert(NTILE % (NW * UCH) == 0, "tile chunks");
   constexpr int VT = 16 / sizeof(T);                  // slab elements per vector
   constexpr int SV = ROWS * kBatch / VT;              // slab vectors
   constexpr int SCH = SV / NT < 8 ? SV / NT : 8;
-  static_assert((kBatch * Q) % (NT * UCH) == 0 && SV % (NT * SCH) == 0, "staging chunks");
+  static_assert(SV % (NT * SCH) == 0, "slab chunks");
   typedef T tvec __attribute__((ext_vector_type(VT)));
   const int64_t row0 = (int64_t)blockIdx.x * ROWS;
   constexpr int IDN = (kBatch + NT - 1) / NT;
@@ -334,25 +340,30 @@ __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
   };
   tvec w0[SCH];
   slab_load(0, w0);
-  for (int base = 0; base < kBatch * Q; base += NT * UCH) {
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
+  for (int base = 0; base < NTILE; base += NW * UCH) {
     f32x4 u[UCH];
+    int tr[UCH], tc[UCH];
 #pragma unroll
     for (int it = 0; it < UCH; ++it) {
-      const int idx = base + it * NT + tid;
-      const int r = min(idx / Q, ncols - 1), c = min((idx % Q) * 4, ncols - 4);
+      // upper-triangle tile q -> (tile row, tile column), row-major
+      int q = base + it * NW + wave, t_r = 0, len = kBatch / 16;
+      while (q >= len) { q -= len; ++t_r; --len; }
+      tr[it] = t_r; tc[it] = t_r + q;
+      const int r = min(tr[it] * 16 + lane % 16, ncols - 1);
+      const int c = min(tc[it] * 16 + (lane / 16) * 4, ncols - 4);
       u[it] = *(const f32x4*)(U + (int64_t)(i1 + r) * k + i1 + c);
     }
     if (base == 0) slab_store(0, w0);
 #pragma unroll
     for (int it = 0; it < UCH; ++it) {
-      const int idx = base + it * NT + tid;
-      const int r = idx / Q, c = (idx % Q) * 4;
+      const int r = tr[it] * 16 + lane % 16, c = tc[it] * 16 + (lane / 16) * 4;
       f32x4 v;
 #pragma unroll
       for (int t = 0; t < 4; ++t) v[t] = (r < ncols && c + t < ncols && r <= c + t) ? u[it][t] : 0.0f;
 #pragma unroll
       for (int t = 0; t < 4; ++t) Ut[(c + t) * UT_LD + r] = v[t];
-      if ((r >> 4) == (c >> 4)) *(f32x4*)&Ud[r >> 4][r & 15][c & 15] = v;
+      if (tr[it] == tc[it]) *(f32x4*)&Ud[tr[it]][r & 15][c & 15] = v;
     }
   }
 #pragma unroll

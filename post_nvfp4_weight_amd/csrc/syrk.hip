@@ -424,44 +424,113 @@ __global__ __launch_bounds__(256) void syrk_single_kernel(const uint16_t* __rest
   tile_job<HALF, HALF>(lds, X, k, ldx, c0, c0, t0, min(n, t0 + stokens), H, P);
 }
 
-// Sum the token splits in split order and add into H (upper triangle +
-// mirror).  kind 0: blockIdx.x is item r of the first launch's order, whose
-// split sp sits in slot sp * per_range + r.  kind 1: blockIdx.x is single a,
-// whose split sp sits in slot slot_base + a * nsplit + sp.
-__device__ __forceinline__ void reduce_block(int64_t k, float* __restrict__ H, const float* __restrict__ P,
-                                             size_t sstride, int nsplit, int64_t r0, int64_t c0, int TM, int TN) {
-  const int rows_per = TM / gridDim.y;
-  for (int e = threadIdx.x; e < rows_per * TN; e += 256) {
-    const int row = blockIdx.y * rows_per + e / TN, col = e % TN;
-    const int64_t gi = r0 + row, gj = c0 + col;
-    if (gi >= k || gj >= k || gi > gj) continue;
-    float s = 0.0f;
-    for (int sp = 0; sp < nsplit; ++sp) s += P[(size_t)sp * sstride + row * TN + col];
-    const float v = H[gi * k + gj] + s;
-    H[gi * k + gj] = v;
-    if (gi != gj) H[gj * k + gi] = v;
+// Sum the token splits of one 64x64 piece of a tile in split order, add the
+// sum into H's upper triangle and write the mirror.  The piece is at rows r0,
+// columns c0 of H; its split sp is at P + sp * sstride with row stride ldp.
+// H and P move in 16-byte vectors; the mirror goes through an LDS transpose
+// so that it is written by rows too.  k % 16 == 0, so a vector is wholly
+// inside or outside H.
+constexpr int PIECE = 64;
+__device__ __forceinline__ void reduce_piece(int64_t k, float* __restrict__ H, const float* __restrict__ P,
+                                             size_t sstride, int nsplit, int ldp, int64_t r0, int64_t c0) {
+  if (r0 >= k || c0 >= k || r0 >= c0 + PIECE) return;   // outside H, or wholly below the diagonal
+  __shared__ float tr[PIECE][PIECE + 1];
+  const int tid = threadIdx.x;
+  const bool offdiag = r0 + PIECE <= c0;
+  f32x4 s[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) s[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  int sp = 0;
+  for (; sp + 2 <= nsplit; sp += 2) {
+    f32x4 v[2][4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int e = q * 256 + tid, row = e >> 4, c4 = (e & 15) * 4;
+        v[u][q] = *(const f32x4*)(P + (size_t)(sp + u) * sstride + (size_t)row * ldp + c4);
+      }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) s[q] += v[u][q];
+  }
+  if (sp < nsplit) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = q * 256 + tid, row = e >> 4, c4 = (e & 15) * 4;
+      s[q] += *(const f32x4*)(P + (size_t)sp * sstride + (size_t)row * ldp + c4);
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = q * 256 + tid, row = e >> 4, c4 = (e & 15) * 4;
+    const int64_t gi = r0 + row, gj = c0 + c4;
+    const bool in = gi < k && gj < k;
+    const f32x4 h = *(const f32x4*)(H + min(gi, k - 1) * k + min(gj, k - 4));
+    const f32x4 v = h + s[q];
+    if (in) {
+      if (offdiag) {
+        *(f32x4*)(H + gi * k + gj) = v;
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (gi <= gj + u) H[gi * k + gj + u] = v[u];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) tr[row][c4 + u] = v[u];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    // mirror row c0 + a, columns r0 + b4 .. r0 + b4 + 3
+    const int e = q * 256 + tid, a = e >> 4, b4 = (e & 15) * 4;
+    const int64_t mi = c0 + a, mj = r0 + b4;
+    if (mi >= k || mj >= k) continue;
+    f32x4 v;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = tr[b4 + u][a];
+    if (offdiag) {
+      *(f32x4*)(H + mi * k + mj) = v;
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (mj + u < mi) H[mi * k + mj + u] = v[u];
+    }
   }
 }
 
+// kind 0: blockIdx.x is item r of the first launch's order, whose split sp
+// sits in slot sp * per_range + r; blockIdx.y (0..15) is a 64x64 piece (a
+// quad's 4x4, or a strip pair's two 2x4).  kind 1: blockIdx.x is single a,
+// whose split sp sits in slot slot_base + a * nsplit + sp; blockIdx.y (0..3)
+// is a piece of its 2x2.
 __global__ __launch_bounds__(256) void syrk_reduce_kernel(int64_t k, float* __restrict__ H,
                                                           const float* __restrict__ partial, int kind, int nsplit,
                                                           int per_range, size_t slot_base) {
   const int nb2 = (int)((k + QUAD - 1) / QUAD);
+  const int y = blockIdx.y;
   if (kind == 0) {
     int ik, a, b;
     item_coords(blockIdx.x, nb2, ik, a, b);
     const float* P = partial + (size_t)blockIdx.x * kSlotFloats;
     const size_t sstride = (size_t)per_range * kSlotFloats;
+    const int pr = (y & 7) / 4, pc = y % 4;
     if (ik == 0) {
-      reduce_block(k, H, P, sstride, nsplit, (int64_t)a * QUAD, (int64_t)b * QUAD, QUAD, QUAD);
+      reduce_piece(k, H, P + (size_t)(y / 4) * PIECE * QUAD + pc * PIECE, sstride, nsplit, QUAD,
+                   (int64_t)a * QUAD + (y / 4) * PIECE, (int64_t)b * QUAD + pc * PIECE);
     } else if (ik == 1) {
-      reduce_block(k, H, P, sstride, nsplit, (int64_t)a * QUAD, (int64_t)a * QUAD, HALF, QUAD);
-      if (b >= 0) reduce_block(k, H, P + HALF * QUAD, sstride, nsplit, (int64_t)b * QUAD, (int64_t)b * QUAD, HALF, QUAD);
+      const int d = y < 8 ? a : b;
+      if (d >= 0)
+        reduce_piece(k, H, P + (y < 8 ? 0 : (size_t)HALF * QUAD) + (size_t)pr * PIECE * QUAD + pc * PIECE, sstride,
+                     nsplit, QUAD, (int64_t)d * QUAD + pr * PIECE, (int64_t)d * QUAD + pc * PIECE);
     }
   } else {
     const int64_t c0 = (int64_t)blockIdx.x * QUAD + HALF;
     const float* P = partial + (slot_base + (size_t)blockIdx.x * nsplit) * kSlotFloats;
-    reduce_block(k, H, P, kSlotFloats, nsplit, c0, c0, HALF, HALF);
+    reduce_piece(k, H, P + (size_t)(y / 2) * PIECE * HALF + (y % 2) * PIECE, kSlotFloats, nsplit, HALF,
+                 c0 + (y / 2) * PIECE, c0 + (y % 2) * PIECE);
   }
 }
 
@@ -553,7 +622,7 @@ hipError_t syrk_bf16(const uint16_t* X, int64_t n, int64_t k, int64_t ldx, float
     hipLaunchKernelGGL(syrk_single_kernel, dim3(p.nsingle, p.ssplit), dim3(256), lds_single, s, X, n, k, ldx, H,
                        partial, p.ssplit, p.stokens, slot);
     if (p.ssplit > 1)
-      hipLaunchKernelGGL(syrk_reduce_kernel, dim3(p.nsingle, 8), dim3(256), 0, s, k, H, partial, 1, p.ssplit, 0,
+      hipLaunchKernelGGL(syrk_reduce_kernel, dim3(p.nsingle, 4), dim3(256), 0, s, k, H, partial, 1, p.ssplit, 0,
                          slot);
   }
   return hipGetLastError();
