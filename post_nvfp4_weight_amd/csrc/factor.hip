@@ -51,49 +51,40 @@ __global__ void flip_damp_kernel(const float* __restrict__ H, int64_t k, const f
   A[i * k + j] = v;
 }
 
-// Lane n of each row of 16 lanes, broadcast to the row (DPP row_newbcast).
+// Lane n of each row of 16 lanes, broadcast to the row (DPP row_newbcast;
+// every lane's source is valid, so no old value is needed and the move can
+// fold into the instruction that uses it).
 template <int N>
 __device__ __forceinline__ float row_bcast(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + N, 0xF, 0xF, false));
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x150 + N, 0xF, 0xF, false));
 }
 
-// Cholesky factor (lower) and inverse of a 16 x 16 SPD block held as columns:
-// lane l (of each row of 16 lanes) enters with c[i] = S[i][l] and leaves with
-// c[i] = L[i][l] and x[i] = L^-1[i][l].  Column j's entries come to every
-// lane by row broadcast.  A non-positive pivot j is replaced by 1 and
-// reported in bad (the first such j), so the arithmetic stays finite.
+// Cholesky factor of a 16 x 16 SPD block S held as columns: lane l (of each
+// row of 16 lanes, lf = l as a float) enters with c[i] = S[i][l] and leaves
+// with c[i] = the Schur-complemented column l, so that L[i][l] = c[i] *
+// rsv[l] for i >= l; rsv[j] = 1 / L[j][j] (the same in every lane).  Column
+// j comes to every lane by row broadcast; lanes l <= j, whose columns are
+// final, have their multiplier scaled by 0 (no per-lane comparisons).  A
+// non-positive pivot j is replaced by 1 and reported in bad (the first such
+// j), so the arithmetic stays finite.
 template <int J>
-__device__ __forceinline__ void chol16_step(float (&c)[16], int l, float& piv, int& bad) {
-  float d = row_bcast<J>(c[J]);
-  if (!(d > 0.0f)) {
-    if (bad < 0) bad = J;
-    d = 1.0f;
-  }
-  if (l == J) piv = d;
-  const float negm = (l > J) ? -(c[J] * __builtin_amdgcn_rcpf(d)) : 0.0f;
+__device__ __forceinline__ void chol16_step(float (&c)[16], float lf, float (&rsv)[16], int& bad) {
+  float bc[16];
 #pragma unroll
-  for (int i = J + 1; i < 16; ++i) c[i] = fmaf(row_bcast<J>(c[i]), negm, c[i]);
+  for (int i = J; i < 16; ++i) bc[i] = row_bcast<J>(c[i]);
+  float d = bc[J];
+  const bool ok = d > 0.0f;
+  bad = (!ok && bad < 0) ? J : bad;
+  d = ok ? d : 1.0f;
+  rsv[J] = __builtin_amdgcn_rsqf(d);
+  const float act = __builtin_amdgcn_fmed3f(lf - (float)J, 0.0f, 1.0f);   // 1 for l > J, else 0
+  const float negm = -(c[J] * __builtin_amdgcn_rcpf(d)) * act;
+#pragma unroll
+  for (int i = J + 1; i < 16; ++i) c[i] = fmaf(bc[i], negm, c[i]);
 }
-template <int I>
-__device__ __forceinline__ void inv16_row(const float (&c)[16], float (&x)[16], int l, float rs) {
-  float acc = (I == l) ? 1.0f : 0.0f;
-  if constexpr (I > 0) {
-    [&]<int... M>(std::integer_sequence<int, M...>) {
-      ((acc = fmaf(-row_bcast<M>(c[I]), x[M], acc)), ...);
-    }(std::make_integer_sequence<int, I>{});
-  }
-  x[I] = acc * row_bcast<I>(rs);
-}
-__device__ __forceinline__ void chol_inv16(float (&c)[16], float (&x)[16], int l, int& bad) {
-  float piv = 1.0f;
+__device__ __forceinline__ void chol16(float (&c)[16], float lf, float (&rsv)[16], int& bad) {
   [&]<int... J>(std::integer_sequence<int, J...>) {
-    (chol16_step<J>(c, l, piv, bad), ...);
-  }(std::make_integer_sequence<int, 16>{});
-  const float rs = __builtin_amdgcn_rsqf(piv), sd = piv * rs;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) c[i] = (i > l) ? c[i] * rs : (i == l ? sd : 0.0f);
-  [&]<int... I>(std::integer_sequence<int, I...>) {
-    (inv16_row<I>(c, x, l, rs), ...);
+    (chol16_step<J>(c, lf, rsv, bad), ...);
   }(std::make_integer_sequence<int, 16>{});
 }
 
@@ -102,20 +93,26 @@ __device__ __forceinline__ void chol_inv16(float (&c)[16], float (&x)[16], int l
 // (identical arithmetic, so identical results) and then solves its own 64
 // rows of the panel below it: L21 = A21 L11^-T.  Inside the workgroup the
 // block is factored in 16-column steps: one wave factors and inverts the
-// 16 x 16 diagonal sub-block in registers, then all waves apply the inverse
-// to the rows below it (the block's own rows and the panel rows) and subtract
-// the step's contribution from the columns to its right, each thread on a
-// 4 x 4 register tile.  Workgroup 0 stores L11 and, on a non-positive pivot,
-// sets *info (once) to the order of the failing leading minor of the
-// reversed matrix, i.e. of the failing trailing minor of H + lam I.
-constexpr int SP = NB + 1;   // LDS row stride of 64-wide blocks
+// 16 x 16 diagonal sub-block in registers; then the rows below it (the
+// block's own rows and the panel rows) are multiplied by the inverse's
+// transpose, and the step's contribution is subtracted from the columns to
+// its right, both as 16 x 16 tiles on the matrix cores
+// (v_mfma_f32_16x16x4f32, one tile per wave at a time).  Workgroup 0 stores
+// L11 and, on a non-positive pivot, sets *info (once) to the order of the
+// failing leading minor of the reversed matrix, i.e. of the failing trailing
+// minor of H + lam I.
+//
+// 16x16x4 operand layout: lane l supplies A[l % 16][l / 16] and
+// B[l / 16][l % 16]; accumulator register r of lane l is D[4 (l / 16) + r][l % 16].
+constexpr int SP = NB + 4;   // LDS row stride: the tiles' operand and accumulator accesses are conflict free
 __global__ __launch_bounds__(256) void panel_kernel(float* __restrict__ A, int64_t k, int64_t p,
                                                     int32_t* __restrict__ info) {
   // Rows 0..63: the diagonal block (lower part; -> L11); rows 64..127: this
   // workgroup's panel rows (-> L21 rows).
-  __shared__ float V[2 * NB][SP];
+  __shared__ __attribute__((aligned(16))) float V[2 * NB][SP];
   __shared__ float Li[16][17];   // inverse of the current 16 x 16 diagonal sub-block
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, lq = lane >> 4;
   const int nb = (int)min((int64_t)NB, k - p);
   const int64_t r0 = (int64_t)blockIdx.x * NB;
   const int rows = (int)max((int64_t)0, min((int64_t)NB, k - p - nb - r0));
@@ -131,103 +128,107 @@ __global__ __launch_bounds__(256) void panel_kernel(float* __restrict__ A, int64
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
     const int e = tid + 256 * (q & 3), i = e >> 4, j4 = (e & 15) * 4;
+    f32x4 v;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int j = j4 + u;
-      float v;
-      if (q < 4) v = (i < nb && j < nb) ? (j <= i ? ld[q][u] : 0.0f) : (i == j ? 1.0f : 0.0f);
-      else v = (i < rows && j < nb) ? ld[q][u] : 0.0f;
-      V[q < 4 ? i : NB + i][j] = v;
+      if (q < 4) v[u] = (i < nb && j < nb) ? (j <= i ? ld[q][u] : 0.0f) : (i == j ? 1.0f : 0.0f);
+      else v[u] = (i < rows && j < nb) ? ld[q][u] : 0.0f;
     }
+    *(f32x4*)&V[q < 4 ? i : NB + i][j4] = v;
   }
   __syncthreads();
   int first_bad = 0;
+  // Wave 0 factors and inverts sub-block o (16 x 16 at rows/columns o).
+  auto factor_sub = [&](int o) {
+    // The lane index is made opaque here, so that the compiler forms what
+    // depends on it where it is used.
+    int lo = l16;
+    asm volatile("" : "+v"(lo));
+    const float lf = (float)lo;
+    float c[16], rsv[16], x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) c[i] = V[o + max(i, lo)][o + min(i, lo)];
+    int bad = -1;
+    chol16(c, lf, rsv, bad);
+    if (bad >= 0 && first_bad == 0 && o + bad < nb) first_bad = (int)(p + o + bad + 1);
+    // Lane l's scale 1 / L[l][l], through LDS (column 16 of Li is spare).
+    if (lane == 0) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) Li[j][16] = rsv[j];
+    }
+    const float rsl = Li[lo][16];
+    // L into V (entries above the diagonal get values that nothing reads).
+    if (lane < 16) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) V[o + i][o + lane] = c[i] * rsl;
+    }
+    // Column l of L^-1 by forward substitution over L's rows in V (the same
+    // addresses in every lane): x[I] = (delta(I, l) - sum_{M<I} L[I][M] x[M]) / L[I][I].
+#pragma unroll
+    for (int I = 0; I < 16; ++I) {
+      const float dl = lf - (float)I;
+      float acc = fmaxf(fmaf(-dl, dl, 1.0f), 0.0f);   // delta(I, l)
+#pragma unroll
+      for (int M = 0; M < I; ++M) acc = fmaf(-V[o + I][o + M], x[M], acc);
+      x[I] = acc * rsv[I];
+    }
+    if (lane < 16) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) Li[i][lane] = x[i];
+    }
+  };
+  if (wave == 0) factor_sub(0);
+  __syncthreads();
   for (int b = 0; b < NB / 16; ++b) {
     const int o = 16 * b;
-    if (wave == 0) {
-      const int l = lane & 15;
-      float c[16], x[16];
+    // Rows below the sub-block (o+16 .. 127): columns o..o+15 := V Li^T.
+    const int nrt = (2 * NB - o - 16) / 16;
+    for (int t = wave; t < nrt; t += 4) {
+      const int t0 = o + 16 + 16 * t;
+      float av[4], bv[4];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) c[i] = i >= l ? V[o + i][o + l] : V[o + l][o + i];
-      int bad = -1;
-      chol_inv16(c, x, l, bad);
-      if (bad >= 0 && first_bad == 0 && o + bad < nb) first_bad = (int)(p + o + bad + 1);
-      if (lane < 16) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          if (i >= lane) V[o + i][o + lane] = c[i];
-          Li[i][lane] = x[i];
-        }
+      for (int kk = 0; kk < 4; ++kk) {
+        av[kk] = V[t0 + l16][o + 4 * kk + lq];
+        bv[kk] = Li[l16][4 * kk + lq];
       }
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[kk], bv[kk], acc, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) V[t0 + 4 * lq + r][o + l16] = acc[r];
     }
     __syncthreads();
-    // Rows below the sub-block: V rows o+16 .. 127 (the block's rows, then the
-    // panel rows).  Columns o..o+15 := V * Li^T on 4 x 4 tiles.
-    const int rbase = o + 16, nrow = 2 * NB - rbase, nS = NB - rbase;
-    const int ntile_b = (nrow / 4) * 4;
-    float outb[2][4][4];
+    // Columns right of the step (o+16 .. 63), every row below:
+    // V[r][j] -= V[r][o:o+16] . V[j][o:o+16].  Tiles wholly above the
+    // diagonal of the block are never read and are skipped.  Wave 0 updates
+    // the next diagonal sub-block (tile 0) and goes on to factor it while
+    // waves 1-3 update the other tiles.
+    const int nct = (NB - o - 16) / 16;
+    auto c_tile = [&](int t) {
+      const int ti = t / nct, tj = t % nct;
+      const int t0 = o + 16 + 16 * ti, j0 = o + 16 + 16 * tj;
+      if (t0 < j0) return;
+      float av[4], bv[4];
+      f32x4 acc;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int t = tid + 256 * q;
-      if (t < ntile_b) {
-        const int r = rbase + 4 * (t >> 2), c0 = 4 * (t & 3);
-        float a[4][16];
+      for (int r = 0; r < 4; ++r) acc[r] = V[t0 + 4 * lq + r][j0 + l16];
 #pragma unroll
-        for (int ri = 0; ri < 4; ++ri)
-#pragma unroll
-          for (int m = 0; m < 16; ++m) a[ri][m] = (m < c0 + 4) ? V[r + ri][o + m] : 0.0f;
-#pragma unroll
-        for (int cj = 0; cj < 4; ++cj) {
-          float li[16];
-#pragma unroll
-          for (int m = 0; m < 16; ++m) li[m] = (m <= c0 + cj) ? Li[c0 + cj][m] : 0.0f;
-#pragma unroll
-          for (int ri = 0; ri < 4; ++ri) {
-            float acc = 0.0f;
-#pragma unroll
-            for (int m = 0; m < 16; ++m) acc = fmaf(a[ri][m], li[m], acc);
-            outb[q][ri][cj] = acc;
-          }
-        }
+      for (int kk = 0; kk < 4; ++kk) {
+        av[kk] = -V[t0 + l16][o + 4 * kk + lq];
+        bv[kk] = V[j0 + l16][o + 4 * kk + lq];
       }
-    }
-    __syncthreads();
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int t = tid + 256 * q;
-      if (t < ntile_b) {
-        const int r = rbase + 4 * (t >> 2), c0 = 4 * (t & 3);
+      for (int kk = 0; kk < 4; ++kk) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[kk], bv[kk], acc, 0, 0, 0);
 #pragma unroll
-        for (int ri = 0; ri < 4; ++ri)
-#pragma unroll
-          for (int cj = 0; cj < 4; ++cj) V[r + ri][o + c0 + cj] = outb[q][ri][cj];
-      }
-    }
-    __syncthreads();
-    // Columns right of the step (rbase .. 63): V[r][j] -= V[r][o:o+16] . L[j][o:o+16]
-    // for every row below, on 4 x 4 tiles (entries above the diagonal of the
-    // block are computed too and never read).
-    if (nS > 0) {
-      const int ncg = nS / 4, ntile_c = (nrow / 4) * ncg;
-      for (int t = tid; t < ntile_c; t += 256) {
-        const int r = rbase + 4 * (t / ncg), j0 = rbase + 4 * (t % ncg);
-        float a[4][16], w[4][16];
-#pragma unroll
-        for (int ri = 0; ri < 4; ++ri)
-#pragma unroll
-          for (int m = 0; m < 16; ++m) {
-            a[ri][m] = V[r + ri][o + m];
-            w[ri][m] = V[j0 + ri][o + m];
-          }
-#pragma unroll
-        for (int ri = 0; ri < 4; ++ri)
-#pragma unroll
-          for (int cj = 0; cj < 4; ++cj) {
-            float acc = V[r + ri][j0 + cj];
-#pragma unroll
-            for (int m = 0; m < 16; ++m) acc = fmaf(-a[ri][m], w[cj][m], acc);
-            V[r + ri][j0 + cj] = acc;
-          }
+      for (int r = 0; r < 4; ++r) V[t0 + 4 * lq + r][j0 + l16] = acc[r];
+    };
+    if (nct > 0) {
+      if (wave == 0) {
+        c_tile(0);
+        factor_sub(o + 16);
+      } else {
+        for (int t = wave; t < nrt * nct; t += 3) c_tile(t);
       }
     }
     __syncthreads();
@@ -238,9 +239,10 @@ __global__ __launch_bounds__(256) void panel_kernel(float* __restrict__ A, int64
   for (int q = 0; q < 8; ++q) {
     const int e = tid + 256 * (q & 3), i = e >> 4, j4 = (e & 15) * 4;
     if ((q < 4 ? (blockIdx.x != 0 || i >= nb) : i >= rows) || j4 >= nb) continue;
-    f32x4 v;
+    f32x4 v = *(const f32x4*)&V[q < 4 ? i : NB + i][j4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = (q < 4 && j4 + u > i) ? 0.0f : V[q < 4 ? i : NB + i][j4 + u];
+    for (int u = 0; u < 4; ++u)
+      if (q < 4 && j4 + u > i) v[u] = 0.0f;
     *(f32x4*)(A + (q < 4 ? p + i : p + nb + r0 + i) * k + p + j4) = v;
   }
 }
@@ -263,13 +265,13 @@ __global__ __launch_bounds__(256) void chol_update_kernel(float* __restrict__ A,
   const int64_t tj = t - ti * (ti + 1) / 2;
   const float* P = A + (p + NB) * k + p;
   float* C = A + (p + NB) * k + p + NB;
-  for (int e = tid; e < NB * NB / 4; e += 256) {
-    const int r = e / (NB / 4), c4 = (e % (NB / 4)) * 4;
-    const int64_t gi = ti * NB + r, gj = tj * NB + r;
-    f32x4 vi = gi < rest ? *(const f32x4*)(P + gi * k + c4) : f32x4{0.f, 0.f, 0.f, 0.f};
-    f32x4 vj = gj < rest ? *(const f32x4*)(P + gj * k + c4) : f32x4{0.f, 0.f, 0.f, 0.f};
+  // All panel loads in flight together (clamped rows), then the LDS writes.
+  f32x4 vi[4], vj[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) { Pi[r][c4 + q] = -vi[q]; Pj[r][c4 + q] = vj[q]; }
+  for (int q = 0; q < 4; ++q) {
+    const int e = q * 256 + tid, r = e / (NB / 4), c4 = (e % (NB / 4)) * 4;
+    vi[q] = *(const f32x4*)(P + min(ti * NB + r, rest - 1) * k + c4);
+    vj[q] = *(const f32x4*)(P + min(tj * NB + r, rest - 1) * k + c4);
   }
   const int wr = wave >> 1, wc = wave & 1;
   const int64_t col = tj * NB + wc * 32 + (lane & 31);
@@ -279,11 +281,31 @@ __global__ __launch_bounds__(256) void chol_update_kernel(float* __restrict__ A,
     const int64_t row = ti * NB + wr * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
     acc[r] = (row < rest && col < rest && col <= row) ? C[row * k + col] : 0.0f;
   }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = q * 256 + tid, r = e / (NB / 4), c4 = (e % (NB / 4)) * 4;
+    const bool oki = ti * NB + r < rest, okj = tj * NB + r < rest;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) { Pi[r][c4 + u] = oki ? -vi[q][u] : 0.0f; Pj[r][c4 + u] = okj ? vj[q][u] : 0.0f; }
+  }
   __syncthreads();
   const float* pa = &Pi[wr * 32 + (lane & 31)][lane >> 5];
   const float* pb = &Pj[wc * 32 + (lane & 31)][lane >> 5];
+  // Operands of the next 16 k-values are read while the current 8 MFMAs run.
+  float a8[2][8], b8[2][8];
 #pragma unroll
-  for (int kk = 0; kk < NB; kk += 2) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(pa[kk], pb[kk], acc, 0, 0, 0);
+  for (int u = 0; u < 8; ++u) { a8[0][u] = pa[2 * u]; b8[0][u] = pb[2 * u]; }
+#pragma unroll
+  for (int h = 0; h < NB / 16; ++h) {
+    if (h + 1 < NB / 16) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) { a8[(h + 1) & 1][u] = pa[16 * (h + 1) + 2 * u]; b8[(h + 1) & 1][u] = pb[16 * (h + 1) + 2 * u]; }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a8[h & 1][u], b8[h & 1][u], acc, 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int64_t row = ti * NB + wr * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
