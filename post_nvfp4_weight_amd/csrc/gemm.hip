@@ -1,7 +1,9 @@
 // fp32 GEMM on CDNA4 matrix cores (v_mfma_f32_32x32x2_f32).
 //
 // One 256-thread workgroup computes a 128x128 tile of C; its four waves hold
-// 64x64 sub-tiles as 2x2 MFMA 32x32 accumulators.  K is consumed in chunks of
+// 64x64 sub-tiles as 2x2 MFMA 32x32 accumulators.  Launches that would give
+// fewer than two such tiles per CU use 64x64 tiles (one 32x32 accumulator
+// per wave) instead.  K is consumed in chunks of
 // 32 staged through two LDS buffers (the next chunk is loaded into registers
 // while the current one is multiplied).  Used for the GPTQ trailing
 // update, the Cholesky panel/trailing updates, the triangular inverse and the
@@ -13,23 +15,29 @@ namespace nvq {
 
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 32;
+constexpr int BK = 32;
 // LDS layouts.  An operand whose k index is contiguous in memory is kept as
 // [row][BK + 1] (scalar stores; the odd stride makes both the stores and the
 // MFMA reads of 32 consecutive rows conflict free); one whose row index is
-// contiguous is kept as [BK][128 + 4] (16-byte stores, conflict-free reads).
+// contiguous is kept as [BK][T + 4] (16-byte stores, conflict-free reads).
+// T is the tile edge: 128, or 64 for launches that would otherwise leave
+// most CUs idle.
 constexpr int KSTRIDE = BK + 1;           // [row][k] layout
-constexpr int RSTRIDE = 128 + 4;          // [k][row] layout
-constexpr int OPER_FLOATS = 128 * KSTRIDE > BK * RSTRIDE ? 128 * KSTRIDE : BK * RSTRIDE;
+template <int T> struct TileCfg {
+  static constexpr int RSTRIDE = T + 4;                       // [k][row] layout
+  static constexpr int OPER = T * KSTRIDE > BK * RSTRIDE ? T * KSTRIDE : BK * RSTRIDE;
+  static constexpr int LQ = T * BK / 4 / 256;                  // float4 per thread per operand tile
+  static constexpr int NI = T / 64;                            // 32x32 accumulators per wave per dimension
+};
 
-// Global -> registers for one operand tile of 128 rows x BK k-values.
+// Global -> registers for one operand tile of T rows x BK k-values.
 // kmajor: element (r, kk) at src[r * ld + kk] (k contiguous); otherwise at
-// src[kk * ld + r] (rows contiguous).  Each thread moves 4 float4.
-template <bool KMAJOR>
+// src[kk * ld + r] (rows contiguous).
+template <int T, bool KMAJOR>
 __device__ __forceinline__ void load_tile(const float* __restrict__ src, int64_t ld, int64_t r0, int64_t nrows,
-                                          int64_t k0, int64_t K, int tid, f32x4 (&v)[4]) {
+                                          int64_t k0, int64_t K, int tid, f32x4 (&v)[TileCfg<T>::LQ]) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < TileCfg<T>::LQ; ++q) {
     int e = q * 256 + tid;
     // Unconditional loads from clamped addresses (so that all of them are
     // in flight together), zeroed outside the matrix afterwards.
@@ -39,7 +47,7 @@ __device__ __forceinline__ void load_tile(const float* __restrict__ src, int64_t
       const f32x4 t = *(const f32x4*)(src + min(gr, nrows - 1) * ld + min(gk, K - 4));
       v[q] = (gr < nrows && gk < K) ? t : f32x4{0.f, 0.f, 0.f, 0.f};
     } else {
-      int kk = e >> 5, r = (e & 31) * 4;           // 32 lanes cover 128 rows of a k
+      int kk = e / (T / 4), r = (e % (T / 4)) * 4;   // T/4 lanes cover the T rows of a k
       int64_t gr = r0 + r, gk = k0 + kk;
       const f32x4 t = *(const f32x4*)(src + min(gk, K - 1) * ld + min(gr, nrows - 4));
       v[q] = (gr < nrows && gk < K) ? t : f32x4{0.f, 0.f, 0.f, 0.f};
@@ -48,12 +56,12 @@ __device__ __forceinline__ void load_tile(const float* __restrict__ src, int64_t
 }
 
 // B' = 2 triu(B, 1) + diag(B) on a B tile (k-index k0 + kk, column n0 + r).
-template <bool KMAJOR>
-__device__ __forceinline__ void sym_upper(f32x4 (&v)[4], int tid, int64_t k0, int64_t n0) {
+template <int T, bool KMAJOR>
+__device__ __forceinline__ void sym_upper(f32x4 (&v)[TileCfg<T>::LQ], int tid, int64_t k0, int64_t n0) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < TileCfg<T>::LQ; ++q) {
     const int e = q * 256 + tid;
-    const int r = KMAJOR ? e >> 3 : (e & 31) * 4, kk = KMAJOR ? (e & 7) * 4 : e >> 5;
+    const int r = KMAJOR ? e >> 3 : (e % (T / 4)) * 4, kk = KMAJOR ? (e & 7) * 4 : e / (T / 4);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int64_t kg = k0 + kk + (KMAJOR ? u : 0), jg = n0 + r + (KMAJOR ? 0 : u);
@@ -62,10 +70,10 @@ __device__ __forceinline__ void sym_upper(f32x4 (&v)[4], int tid, int64_t k0, in
   }
 }
 
-template <bool KMAJOR>
-__device__ __forceinline__ void store_tile(float* dst, int tid, f32x4 (&v)[4], float scale = 1.0f) {
+template <int T, bool KMAJOR>
+__device__ __forceinline__ void store_tile(float* dst, int tid, f32x4 (&v)[TileCfg<T>::LQ], float scale = 1.0f) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < TileCfg<T>::LQ; ++q) {
     if (scale != 1.0f) v[q] = v[q] * scale;
     int e = q * 256 + tid;
     if (KMAJOR) {
@@ -73,19 +81,20 @@ __device__ __forceinline__ void store_tile(float* dst, int tid, f32x4 (&v)[4], f
       float* d = dst + r * KSTRIDE + kk;
       d[0] = v[q][0]; d[1] = v[q][1]; d[2] = v[q][2]; d[3] = v[q][3];
     } else {
-      int kk = e >> 5, r = (e & 31) * 4;
-      *(f32x4*)(dst + kk * RSTRIDE + r) = v[q];
+      int kk = e / (T / 4), r = (e % (T / 4)) * 4;
+      *(f32x4*)(dst + kk * TileCfg<T>::RSTRIDE + r) = v[q];
     }
   }
 }
 
-template <bool KMAJOR>
+template <int T, bool KMAJOR>
 __device__ __forceinline__ float read_operand(const float* tile, int row, int kk) {
-  return KMAJOR ? tile[row * KSTRIDE + kk] : tile[kk * RSTRIDE + row];
+  return KMAJOR ? tile[row * KSTRIDE + kk] : tile[kk * TileCfg<T>::RSTRIDE + row];
 }
 
-template <bool TA, bool TB, bool LOWER, int EPI>
+template <int T, bool TA, bool TB, bool LOWER, int EPI>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
+  constexpr int BM = T, BN = T, WT = T / 2, NI = TileCfg<T>::NI, OPER = TileCfg<T>::OPER, LQ = TileCfg<T>::LQ;
   // Tile of this workgroup.  With a triangular k range the tiles differ in
   // length: they are dealt out longest first, so that the last ones to start
   // are short.
@@ -97,7 +106,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
   else if (p.kmode == kGemmKLowerA) { tm = mt - 1 - lin / nt; tn = lin % nt; }
   if (LOWER && tn > tm) return;
   // [buffer][A | B] operand tiles; reused by the row-dot epilogue.
-  __shared__ __attribute__((aligned(16))) float smem[2 * 2 * OPER_FLOATS];
+  __shared__ __attribute__((aligned(16))) float smem[2 * 2 * OPER];
   constexpr bool AK = !TA;   // A stored [M][K]: k contiguous
   constexpr bool BKM = TB;   // B stored [N][K]: k contiguous
 
@@ -115,35 +124,35 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
   // is loaded into the accumulators up front (its latency overlaps the first
   // operand loads) and alpha is applied to A on its way into LDS, so the
   // epilogue only stores: C = beta*C + (alpha*A) op(B).
-  f32x16 acc[2][2];
+  f32x16 acc[NI][NI];
   const bool load_c = EPI == kEpiAxpby && p.beta != 0.0f;
-  // Wave-uniform base of this wave's 64x64 sub-tile of C plus a 32-bit lane
+  // Wave-uniform base of this wave's WT x WT sub-tile of C plus a 32-bit lane
   // offset; a whole tile inside C needs no per-element bounds checks.
-  const int64_t wrow0 = m0 + wr * 64, wcol0 = n0 + wc * 64;
+  const int64_t wrow0 = m0 + wr * WT, wcol0 = n0 + wc * WT;
   float* Cw = C + wrow0 * p.ldc + wcol0;
   const int lane_off = 4 * (lane >> 5) * (int)p.ldc + (lane & 31);
-  const bool full = wrow0 + 64 <= p.M && wcol0 + 64 <= p.N;
+  const bool full = wrow0 + WT <= p.M && wcol0 + WT <= p.N;
   // Unconditional loads (clamped addresses at the matrix edge), so that all
-  // 64 are in flight together.
+  // of them are in flight together.
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NI; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
   if (load_c && full) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < NI; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           acc[i][j][r] = p.beta * Cw[(i * 32 + 8 * (r >> 2) + (r & 3)) * p.ldc + j * 32 + lane_off];
   } else if (load_c) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < NI; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int64_t gr = wrow0 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
@@ -162,51 +171,51 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
   if (p.kmode == kGemmKSymUpperB) khi = min(p.K, p.noff + n0 + BN);
   const int64_t c0 = klo / BK, nk = (khi + BK - 1) / BK;
   const bool sym = p.kmode == kGemmKSymUpperB;
-  f32x4 ra[4], rb[4];
+  f32x4 ra[LQ], rb[LQ];
   if (c0 < nk) {
-    load_tile<AK>(A, p.lda, m0, p.M, c0 * BK, p.K, tid, ra);
-    load_tile<BKM>(B, p.ldb, n0, p.N, c0 * BK, p.K, tid, rb);
-    if (sym) sym_upper<BKM>(rb, tid, c0 * BK, p.noff + n0);
-    store_tile<AK>(smem, tid, ra, alpha_a);
-    store_tile<BKM>(smem + OPER_FLOATS, tid, rb);
+    load_tile<T, AK>(A, p.lda, m0, p.M, c0 * BK, p.K, tid, ra);
+    load_tile<T, BKM>(B, p.ldb, n0, p.N, c0 * BK, p.K, tid, rb);
+    if (sym) sym_upper<T, BKM>(rb, tid, c0 * BK, p.noff + n0);
+    store_tile<T, AK>(smem, tid, ra, alpha_a);
+    store_tile<T, BKM>(smem + OPER, tid, rb);
   }
   __syncthreads();
   for (int64_t c = c0; c < nk; ++c) {
     const int cur = (int)((c - c0) & 1);
     if (c + 1 < nk) {
-      load_tile<AK>(A, p.lda, m0, p.M, (c + 1) * BK, p.K, tid, ra);
-      load_tile<BKM>(B, p.ldb, n0, p.N, (c + 1) * BK, p.K, tid, rb);
+      load_tile<T, AK>(A, p.lda, m0, p.M, (c + 1) * BK, p.K, tid, ra);
+      load_tile<T, BKM>(B, p.ldb, n0, p.N, (c + 1) * BK, p.K, tid, rb);
     }
-    const float* As = smem + cur * 2 * OPER_FLOATS;
-    const float* Bs = As + OPER_FLOATS;
+    const float* As = smem + cur * 2 * OPER;
+    const float* Bs = As + OPER;
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 2) {
-      float a[2], b[2];
+      float a[NI], b[NI];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        a[t] = read_operand<AK>(As, wr * 64 + t * 32 + (lane & 31), kk + (lane >> 5));
-        b[t] = read_operand<BKM>(Bs, wc * 64 + t * 32 + (lane & 31), kk + (lane >> 5));
+      for (int t = 0; t < NI; ++t) {
+        a[t] = read_operand<T, AK>(As, wr * WT + t * 32 + (lane & 31), kk + (lane >> 5));
+        b[t] = read_operand<T, BKM>(Bs, wc * WT + t * 32 + (lane & 31), kk + (lane >> 5));
       }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < NI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < NI; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j], 0, 0, 0);
     }
     if (c + 1 < nk) {
-      float* nxt = smem + (cur ^ 1) * 2 * OPER_FLOATS;
-      if (sym) sym_upper<BKM>(rb, tid, (c + 1) * BK, p.noff + n0);
-      store_tile<AK>(nxt, tid, ra, alpha_a);
-      store_tile<BKM>(nxt + OPER_FLOATS, tid, rb);
+      float* nxt = smem + (cur ^ 1) * 2 * OPER;
+      if (sym) sym_upper<T, BKM>(rb, tid, (c + 1) * BK, p.noff + n0);
+      store_tile<T, AK>(nxt, tid, ra, alpha_a);
+      store_tile<T, BKM>(nxt + OPER, tid, rb);
     }
     __syncthreads();
   }
 
   if (EPI == kEpiAxpby) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < NI; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3), col = j * 32 + (lane & 31);
@@ -215,19 +224,19 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
         }
   } else {
     // Row-dot: P[row, tile] = sum over the tile's columns of alpha*acc*D.
-    float (*red)[33] = (float (*)[33])smem;   // [128][33], operand tiles are dead here
+    float (*red)[33] = (float (*)[33])smem;   // [T][33], operand tiles are dead here
     // Unconditional loads of D (clamped at the matrix edge), all in flight
     // together.
-    float part[2][16];
+    float part[NI][16];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        int64_t gi = m0 + wr * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        int64_t gi = m0 + wr * WT + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         float s = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          int64_t gj = n0 + wc * 64 + j * 32 + (lane & 31);
+        for (int j = 0; j < NI; ++j) {
+          int64_t gj = n0 + wc * WT + j * 32 + (lane & 31);
           const float d = p.D[min(gi, p.M - 1) * p.ldd + min(gj, p.N - 1)];
           s = fmaf(p.alpha * acc[i][j][r], (gi < p.M && gj < p.N) ? d : 0.0f, s);
         }
@@ -236,10 +245,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
     for (int half = 0; half < 2; ++half) {
       if (wc == half) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < NI; ++i)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            int row = wr * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            int row = wr * WT + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
             float prev = half ? red[row][lane & 31] : 0.0f;
             red[row][lane & 31] = prev + part[i][r];
           }
@@ -255,11 +264,31 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
   }
 }
 
+int gemm_num_cus() {
+  static int cus = 0;
+  if (!cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+  }
+  return cus;
+}
+
+template <int T, bool TA, bool TB, bool LOWER, int EPI>
+hipError_t launch_t(const GemmArgs& a, hipStream_t s) {
+  dim3 grid((unsigned)((a.N + T - 1) / T), (unsigned)((a.M + T - 1) / T), (unsigned)a.batch);
+  hipLaunchKernelGGL((gemm_f32_kernel<T, TA, TB, LOWER, EPI>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// 64-wide tiles when 128-wide ones would give fewer than two per CU (the
+// row-dot keeps 128: its partial sums are laid out per 128 columns).
 template <bool TA, bool TB, bool LOWER, int EPI>
 hipError_t launch(const GemmArgs& a, hipStream_t s) {
-  dim3 grid((unsigned)((a.N + BN - 1) / BN), (unsigned)((a.M + BM - 1) / BM), (unsigned)a.batch);
-  hipLaunchKernelGGL((gemm_f32_kernel<TA, TB, LOWER, EPI>), grid, dim3(256), 0, s, a);
-  return hipGetLastError();
+  const int64_t tiles128 = ((a.N + 127) / 128) * ((a.M + 127) / 128) * a.batch;
+  if (EPI == kEpiAxpby && tiles128 < 2 * gemm_num_cus()) return launch_t<64, TA, TB, LOWER, EPI>(a, s);
+  return launch_t<128, TA, TB, LOWER, EPI>(a, s);
 }
 
 // ---- fp64 rank update: C -= A B with A, C fp64 and B fp32 (widened) ------------
