@@ -1,4 +1,6 @@
-// fp32 GEMM on CDNA4 matrix cores (v_mfma_f32_32x32x2_f32).
+// fp32 GEMMs on CDNA4 matrix cores: v_mfma_f32_32x32x2_f32, and for large
+// non-transposed products the bf16 matrix cores with operands split into
+// three bf16 parts (gemm_x6_kernel below).
 //
 // One 256-thread workgroup computes a 128x128 tile of C; its four waves hold
 // 64x64 sub-tiles as 2x2 MFMA 32x32 accumulators.  Launches that would give
@@ -264,6 +266,235 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
   }
 }
 
+// ---- fp32 GEMM on the bf16 matrix cores (v_mfma_f32_32x32x16_bf16) -----------------
+// Each fp32 operand x is split into three bf16 parts, x = x1 + x2 + x3 with
+// x1 = bf16(x), x2 = bf16(x - x1), x3 = bf16(x - x1 - x2) (the differences
+// are exact in fp32), and a product is the sum of the six part products whose
+// orders add up to at most four: x1y1, x1y2, x2y1, x1y3, x2y2, x3y1.  The
+// dropped terms are below 2^-24 of |x y|; bf16 products are exact in fp32 and
+// accumulate in fp32, so the result has fp32 accuracy at 6/16 of the fp32
+// matrix-core time.  A is [M][K] (k contiguous) and B is [K][N]; tiles are
+// 128 x 128, four waves of 64 x 64, k in chunks of 32.  In LDS every part is
+// kept [row][k] (k contiguous, rows padded to 40 elements), so that an MFMA
+// operand (8 consecutive k of one row or column) is one 16-byte read; B is
+// transposed on its way in, each thread turning a 4 x 4 block.
+constexpr int X6_T = 128, X6_LD = BK + 8;                 // bf16 row stride of a part
+constexpr int X6_PART = X6_T * X6_LD;                     // bf16 elements of one part
+constexpr int X6_BUF = 6 * X6_PART;                       // A parts, then B parts
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// Two values -> their three bf16 parts, each pair packed as one 32-bit word
+// (first value in the low half).
+__device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& h, uint32_t& m, uint32_t& l) {
+  h = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{x0, x1}, bf16x2));
+  const float r0 = x0 - __uint_as_float(h << 16), r1 = x1 - __uint_as_float(h & 0xFFFF0000u);
+  m = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{r0, r1}, bf16x2));
+  const float s0 = r0 - __uint_as_float(m << 16), s1 = r1 - __uint_as_float(m & 0xFFFF0000u);
+  l = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{s0, s1}, bf16x2));
+}
+// Four consecutive-k values of one row -> 8 bytes at element offset off of
+// each of the three parts.
+__device__ __forceinline__ void put4(uint16_t* base, int off, const f32x4& v) {
+  uint32_t h0, m0, l0, h1, m1, l1;
+  split_pair(v[0], v[1], h0, m0, l0);
+  split_pair(v[2], v[3], h1, m1, l1);
+  *(u32x2*)(base + off) = u32x2{h0, h1};
+  *(u32x2*)(base + X6_PART + off) = u32x2{m0, m1};
+  *(u32x2*)(base + 2 * X6_PART + off) = u32x2{l0, l1};
+}
+// B is stored transposed, [column][k]; its 16-byte k chunks are XOR-swizzled
+// by (column / 16) % 4, which spreads the transposing writes over the banks.
+__device__ __forceinline__ int x6_boff(int n, int k) { return n * X6_LD + ((((k >> 3) ^ (n >> 4)) & 3) << 3) + (k & 7); }
+
+template <int EPI>
+__global__ __launch_bounds__(256) void gemm_x6_kernel(GemmArgs p) {
+  constexpr int WT = X6_T / 2;
+  const int nt = (int)gridDim.x, mt = (int)gridDim.y;
+  const int lin = (int)blockIdx.y * nt + (int)blockIdx.x;
+  int tn = (int)blockIdx.x, tm = (int)blockIdx.y;
+  if (p.kmode == kGemmKSymUpperB) { tn = nt - 1 - lin / mt; tm = lin % mt; }
+  else if (p.kmode == kGemmKLowerB) { tn = lin / mt; tm = lin % mt; }
+  else if (p.kmode == kGemmKLowerA) { tm = mt - 1 - lin / nt; tn = lin % nt; }
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * X6_BUF];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+  const int64_t m0 = (int64_t)tm * X6_T, n0 = (int64_t)tn * X6_T;
+  const int64_t z = blockIdx.z;
+  const float* A = p.A + z * p.sA;
+  const float* B = p.B + z * p.sB;
+  float* C = p.C + z * p.sC;
+
+  f32x16 acc[2][2];
+  const bool load_c = EPI == kEpiAxpby && p.beta != 0.0f;
+  const int64_t wrow0 = m0 + wr * WT, wcol0 = n0 + wc * WT;
+  float* Cw = C + wrow0 * p.ldc + wcol0;
+  const int lane_off = 4 * (lane >> 5) * (int)p.ldc + (lane & 31);
+  const bool full = wrow0 + WT <= p.M && wcol0 + WT <= p.N;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  if (load_c && full) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          acc[i][j][r] = p.beta * Cw[(i * 32 + 8 * (r >> 2) + (r & 3)) * p.ldc + j * 32 + lane_off];
+  } else if (load_c) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int64_t gr = wrow0 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int64_t gc = wcol0 + j * 32 + (lane & 31);
+          const float v = C[min(gr, p.M - 1) * p.ldc + min(gc, p.N - 1)];
+          acc[i][j][r] = (gr < p.M && gc < p.N) ? p.beta * v : 0.0f;
+        }
+  }
+  const float alpha_a = EPI == kEpiAxpby ? p.alpha : 1.0f;
+
+  int64_t klo = 0, khi = p.K;
+  if (p.kmode == kGemmKLowerA) khi = min(p.K, m0 + X6_T);
+  if (p.kmode == kGemmKLowerB) klo = p.noff + n0;
+  if (p.kmode == kGemmKSymUpperB) khi = min(p.K, p.noff + n0 + X6_T);
+  const int64_t c0 = klo / BK, nk = (khi + BK - 1) / BK;
+  const bool sym = p.kmode == kGemmKSymUpperB;
+
+  // Loads of one chunk: A rows (4 float4 along k per thread), B as a 4 x 4
+  // block (4 k x 4 columns) per thread, raw from clamped addresses so that
+  // all eight are in flight while the previous chunk is multiplied; masking,
+  // alpha and the symmetric weights are applied when the chunk is stored.
+  const int bk = (tid >> 5) * 4, bn = (tid & 31) * 4;
+  auto load_chunk = [&](int64_t k0, f32x4 (&ra)[4], f32x4 (&rb)[4]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = q * 256 + tid, r = e >> 3, kk = (e & 7) * 4;
+      ra[q] = *(const f32x4*)(A + min(m0 + r, p.M - 1) * p.lda + min(k0 + kk, p.K - 4));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rb[i] = *(const f32x4*)(B + min(k0 + bk + i, p.K - 1) * p.ldb + min(n0 + bn, p.N - 4));
+  };
+  auto store_chunk = [&](uint16_t* buf, int64_t k0, const f32x4 (&ra)[4], const f32x4 (&rb)[4]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = q * 256 + tid, r = e >> 3, kk = (e & 7) * 4;
+      const bool ok = m0 + r < p.M && k0 + kk < p.K;
+      put4(buf, r * X6_LD + kk, ok ? ra[q] * alpha_a : f32x4{0.f, 0.f, 0.f, 0.f});
+    }
+    f32x4 v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t gk = k0 + bk + i, gn = n0 + bn;
+      v[i] = (gk < p.K && gn < p.N) ? rb[i] : f32x4{0.f, 0.f, 0.f, 0.f};
+      if (sym) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int64_t jg = p.noff + gn + u;
+          v[i][u] *= gk < jg ? 2.0f : (gk == jg ? 1.0f : 0.0f);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) put4(buf + 3 * X6_PART, x6_boff(bn + j, bk), f32x4{v[0][j], v[1][j], v[2][j], v[3][j]});
+  };
+
+  f32x4 ra[4], rb[4];
+  if (c0 < nk) {
+    load_chunk(c0 * BK, ra, rb);
+    store_chunk(smem, c0 * BK, ra, rb);
+  }
+  __syncthreads();
+  // Lane l reads rows (l % 32) and k offset 8 (l / 32) of each 32-row block.
+  const int arow = wr * WT + (lane & 31), brow = wc * WT + (lane & 31), koff = 8 * (lane >> 5);
+  constexpr int PA[6] = {2, 1, 0, 1, 0, 0}, PB[6] = {0, 1, 2, 0, 1, 0};   // part products, smallest first
+  for (int64_t c = c0; c < nk; ++c) {
+    const int cur = (int)((c - c0) & 1);
+    if (c + 1 < nk) load_chunk((c + 1) * BK, ra, rb);
+    const uint16_t* As = smem + cur * X6_BUF;
+    const uint16_t* Bs = As + 3 * X6_PART;
+#pragma unroll
+    for (int ks = 0; ks < BK; ks += 16) {
+      bf16x8 a[3][2], b[3][2];
+#pragma unroll
+      for (int pt = 0; pt < 3; ++pt)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          a[pt][t] = *(const bf16x8*)(As + pt * X6_PART + (arow + 32 * t) * X6_LD + ks + koff);
+          b[pt][t] = *(const bf16x8*)(Bs + pt * X6_PART + x6_boff(brow + 32 * t, ks + koff));
+        }
+      // The four accumulators take turns, so that no MFMA waits for the one
+      // before it.
+#pragma unroll
+      for (int pp = 0; pp < 6; ++pp)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[PA[pp]][i], b[PB[pp]][j], acc[i][j], 0, 0, 0);
+    }
+    if (c + 1 < nk) store_chunk(smem + (cur ^ 1) * X6_BUF, (c + 1) * BK, ra, rb);
+    __syncthreads();
+  }
+
+  if (EPI == kEpiAxpby) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3), col = j * 32 + (lane & 31);
+          if (full || (wrow0 + row < p.M && wcol0 + col < p.N))
+            Cw[(i * 32 + 8 * (r >> 2) + (r & 3)) * p.ldc + j * 32 + lane_off] = acc[i][j][r];
+        }
+  } else {
+    float (*red)[33] = (float (*)[33])smem;   // [128][33], operand tiles are dead here
+    float part[2][16];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        int64_t gi = m0 + wr * WT + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        float sacc = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          int64_t gj = n0 + wc * WT + j * 32 + (lane & 31);
+          const float d = p.D[min(gi, p.M - 1) * p.ldd + min(gj, p.N - 1)];
+          sacc = fmaf(p.alpha * acc[i][j][r], (gi < p.M && gj < p.N) ? d : 0.0f, sacc);
+        }
+        part[i][r] = sacc;
+      }
+    for (int half = 0; half < 2; ++half) {
+      if (wc == half) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            int row = wr * WT + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            float prev = half ? red[row][lane & 31] : 0.0f;
+            red[row][lane & 31] = prev + part[i][r];
+          }
+      }
+      __syncthreads();
+    }
+    if (tid < X6_T) {
+      float sacc = 0.0f;
+      for (int c2 = 0; c2 < 32; ++c2) sacc += red[tid][c2];
+      int64_t gi = m0 + tid;
+      if (gi < p.M) p.P[gi * p.ldp + tn] = sacc;
+    }
+  }
+}
+
 int gemm_num_cus() {
   static int cus = 0;
   if (!cus) {
@@ -282,12 +513,18 @@ hipError_t launch_t(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// 64-wide tiles when 128-wide ones would give fewer than two per CU (the
-// row-dot keeps 128: its partial sums are laid out per 128 columns).
+// 64-wide fp32 tiles when 128-wide ones would give fewer than two per CU (the
+// row-dot keeps 128: its partial sums are laid out per 128 columns);
+// otherwise the split-bf16 kernel for A [M][K] times B [K][N].
 template <bool TA, bool TB, bool LOWER, int EPI>
 hipError_t launch(const GemmArgs& a, hipStream_t s) {
   const int64_t tiles128 = ((a.N + 127) / 128) * ((a.M + 127) / 128) * a.batch;
   if (EPI == kEpiAxpby && tiles128 < 2 * gemm_num_cus()) return launch_t<64, TA, TB, LOWER, EPI>(a, s);
+  if (!TA && !TB && !LOWER) {
+    dim3 grid((unsigned)((a.N + X6_T - 1) / X6_T), (unsigned)((a.M + X6_T - 1) / X6_T), (unsigned)a.batch);
+    hipLaunchKernelGGL((gemm_x6_kernel<EPI>), grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   return launch_t<128, TA, TB, LOWER, EPI>(a, s);
 }
 
