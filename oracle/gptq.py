@@ -94,11 +94,18 @@ def candidate_codes(absmax, g, n_cand):
     return lo[..., None] + np.arange(n_cand)
 
 
-def sweep(W, U, g, n_cand, dtype=np.float64, trace=False):
+def sweep(W, U, g, n_cand, dtype=np.float64, trace=False, select="replay"):
     """GPTQ column sweep over 16-weight blocks with Schur Replay scale selection.
 
     W: [m, k] weights (any real dtype; read exactly).  U: [k, k] upper factor.
     g: per-tensor scale.  n_cand: candidates per block (1..16).
+    select: "replay" (Schur Replay: the candidate whose replayed block errors
+    have the smallest sum_j e_j^2), or "independent" (the baseline the pages
+    set out to fix, scoring a block on its own: the candidate whose plain
+    squared rounding error sum_j (v_j - q_j)^2 over the block's weights at the
+    block start, each rounded with no in-block updates, is smallest).  Either
+    way the chosen candidate's block is then committed with its replayed GPTQ
+    updates.
 
     Returns dict with
       codes  uint8 [m, k]      4-bit element codes (unpacked),
@@ -106,7 +113,8 @@ def sweep(W, U, g, n_cand, dtype=np.float64, trace=False):
       err    [m, k]            GPTQ errors e_j of the committed choice,
       score  [m]               sum_j e_j^2 (the damped loss of the sweep).
     With trace=True it also holds, per row and block, the candidate codes
-    ("cand" [m, k/16, K]), their replay scores ("cand_score"), the element
+    ("cand" [m, k/16, K]), the scores the choice was made on ("cand_score":
+    replay scores, or the independent ones with select="independent"), the element
     codes each candidate chose ("cand_codes" [m, k/16, K, 16]) and the value
     of each column when it was quantized ("vdec" [m, k]).
     Updates are applied eagerly after each block (identical mathematics to
@@ -138,6 +146,15 @@ def sweep(W, U, g, n_cand, dtype=np.float64, trace=False):
         sval = codec.e4m3_decode(cand)                            # exact
         V = np.repeat(vb[:, None, :], n_cand, axis=1).copy()      # [m, K, 16]
         score = np.zeros((m, n_cand), dtype=dtype)
+        if select == "independent":
+            indep = np.zeros((m, n_cand), dtype=dtype)
+            for j in range(BLOCK):
+                v0 = V[:, :, j]
+                q0 = codec.dequant_exact(codec.e2m1_encode(v0, sval, g), cand, g).astype(dtype)
+                dj = (v0 - q0).astype(dtype)
+                indep = (indep + dj * dj).astype(dtype)
+        elif select != "replay":
+            raise ValueError(f"select must be 'replay' or 'independent', got {select!r}")
         E = np.zeros((m, n_cand, BLOCK), dtype=dtype)
         C = np.zeros((m, n_cand, BLOCK), dtype=np.uint8)
         VD = np.zeros((m, n_cand, BLOCK), dtype=dtype)
@@ -152,7 +169,7 @@ def sweep(W, U, g, n_cand, dtype=np.float64, trace=False):
                 V[:, :, j + 1:] -= ej[:, :, None] * Ub[j, j + 1:]
             E[:, :, j] = ej
             C[:, :, j] = cj
-        best = np.argmin(score, axis=1)                           # first minimum
+        best = np.argmin(score if select == "replay" else indep, axis=1)   # first minimum
         rows = np.arange(m)
         eb = E[rows, best]
         cb = C[rows, best]
@@ -163,7 +180,7 @@ def sweep(W, U, g, n_cand, dtype=np.float64, trace=False):
         sb[zero] = 0
         if trace:
             tr_cand[:, beta] = cand
-            tr_score[:, beta] = score
+            tr_score[:, beta] = score if select == "replay" else indep
             tr_codes[:, beta] = C
             vdec[:, c0:c1] = VD[rows, best]
         codes[:, c0:c1] = cb

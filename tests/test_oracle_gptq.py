@@ -272,3 +272,72 @@ def test_fp32_mode_matches_fp64_decisions_on_small_layer():
     b = gptq.sweep(W, U, g, 8, dtype=np.float32)
     assert np.mean(a["codes"] != b["codes"]) <= 1e-3
     assert np.mean(a["scales"] != b["scales"]) <= 1e-3
+
+
+# ------------------------------------------- block-independent scale selection
+def _block_min_mse_scale(v, g, K):
+    """Brute force: the candidate with the smallest plain squared rounding error of block v."""
+    cands = gptq.candidate_codes(np.array([np.abs(v).max()]), g, K)[0]
+    errs = [np.sum((v - codec.dequant_exact(codec.e2m1_encode(v, codec.e4m3_decode(c), g), c, g)) ** 2)
+            for c in cands]
+    return cands[int(np.argmin(errs))]
+
+
+def test_independent_select_with_identity_u_is_min_mse_rtn():
+    # U = I: no in-block updates, so the replay score and the independent
+    # squared error are the same numbers; both pick the brute-force
+    # minimum-MSE scale of each block.
+    W, _ = _layer(16, 128, 8, seed=30)
+    g = codec.global_scale(W)
+    a = gptq.sweep(W, np.eye(128), g, 8)
+    b = gptq.sweep(W, np.eye(128), g, 8, select="independent")
+    assert np.array_equal(a["codes"], b["codes"]) and np.array_equal(a["scales"], b["scales"])
+    for row in range(16):
+        for blk in range(8):
+            v = W[row, 16 * blk:16 * blk + 16].astype(np.float64)
+            assert b["scales"][row, blk] == _block_min_mse_scale(v, g, 8)
+
+
+def test_independent_select_scores_block_start_weights():
+    # Correlated H: each block's scale is the brute-force minimum-MSE scale of
+    # the block's weights at the block start, rebuilt here from W and the
+    # committed errors (w' = w - e_prev U_prev); the committed codes are the
+    # chosen candidate's replay, the same codes the replay sweep traced for
+    # that candidate.
+    W, X = _layer(12, 96, 400, seed=32)
+    H = gptq.hessian(X)
+    U, _ = gptq.hinv_factor(H)
+    g = codec.global_scale(W)
+    K = 8
+    res = gptq.sweep(W, U, g, K, select="independent", trace=True)
+    err = res["err"].astype(np.float64)
+    for blk in range(6):
+        c0, c1 = 16 * blk, 16 * blk + 16
+        start = W[:, c0:c1].astype(np.float64) - err[:, :c0] @ U[:c0, c0:c1]
+        for row in range(12):
+            s = _block_min_mse_scale(start[row], g, K)
+            assert res["scales"][row, blk] == s, (row, blk)
+            kk = int(np.nonzero(res["cand"][row, blk] == s)[0][0])
+            assert np.array_equal(res["codes"][row, c0:c1], res["cand_codes"][row, blk, kk])
+
+
+def test_replay_selection_lowers_loss_against_independent():
+    # The pages' claim behind Schur Replay: scoring a block on its own
+    # misjudges what it leaves after compensation.  On correlated inputs the
+    # replay choice gives the lower damped loss and weighted error.
+    W, X = _layer(48, 256, 768, seed=31)
+    H = gptq.hessian(X)
+    U, _ = gptq.hinv_factor(H)
+    g = codec.global_scale(W)
+    rep = gptq.sweep(W, U, g, 16)
+    ind = gptq.sweep(W, U, g, 16, select="independent")
+    assert np.mean(rep["scales"] != ind["scales"]) > 0.05
+    assert rep["score"].sum() < ind["score"].sum()
+    e_rep = gptq.weighted_error(W, codec.dequantize(codec.pack_codes(rep["codes"]), rep["scales"], g), H)
+    e_ind = gptq.weighted_error(W, codec.dequantize(codec.pack_codes(ind["codes"]), ind["scales"], g), H)
+    assert e_rep.sum() < e_ind.sum()
+
+
+def test_select_rejects_unknown_rule():
+    with pytest.raises(ValueError):
+        gptq.sweep(np.zeros((1, 16)), np.eye(16), 1.0, 1, select="mse")
