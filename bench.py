@@ -137,6 +137,24 @@ def summarize_pmc(fetch_csv, write_csv):
     print(json.dumps(out))
 
 
+def ablation(nvq, Wd, Xd):
+    """Total weighted error sum_r dW_r H dW_r^T of the benchmarked layer under
+    each scale-selection configuration, all on the GPU."""
+    res = nvq.quantize_layer(Wd, Xd, n_cand=N_CAND)
+    U, H, g = res["U"], res["H"], res["g"]
+    E = {
+        "rtn_absmax": nvq.gptq_nvfp4_quantize(Wd, None, H, g, 1, nvq.FLAG_RTN)["row_err"],
+        "gptq_absmax": nvq.gptq_nvfp4_quantize(Wd, U, H, g, 1)["row_err"],
+        "gptq_block_independent": nvq.gptq_nvfp4_quantize(Wd, U, H, g, N_CAND, nvq.FLAG_INDEP)["row_err"],
+        "gptq_schur_replay": res["row_err"],
+    }
+    E = {k: float(v.double().sum()) for k, v in E.items()}
+    ref = E["gptq_schur_replay"]
+    print(json.dumps({"ablation": "block-scale selection", "workload": WORKLOAD, "n_cand": N_CAND,
+                      "E_total": E, "E_relative_to_schur_replay": {k: round(v / ref, 4) for k, v in E.items()},
+                      "data": "synthetic"}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -145,6 +163,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the Hessian's measured HBM traffic from two rocprofv3 --pmc CSVs and exit")
+    ap.add_argument("--ablation", action="store_true",
+                    help="instead of timing, print the layer's total weighted error under four scale-selection "
+                         "configurations (RTN absmax, GPTQ absmax, GPTQ block-independent, GPTQ Schur Replay)")
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
@@ -171,6 +192,9 @@ def main():
     h2d_s = time.perf_counter() - t0
     del Xh
     log(f"inputs resident (H2D {h2d_s:.3f} s)")
+    if args.ablation:
+        ablation(nvq, Wd, Xd)
+        return
 
     lib = nvq.lib
     stream = nvq._stream

@@ -66,6 +66,15 @@ extern "C" {
  * of the decisions of the exact computation.  Needs a larger workspace
  * (gptq_nvfp4_workspace_size with the same flags).  Ignored with RTN. */
 #define NVQ_FLAG_FP64   4u
+/* Block-independent scale selection, the baseline that Schur Replay corrects
+ * ("Replay the Curvature", Abstract: scoring blocks independently can
+ * misestimate their final error): each candidate is scored by the plain
+ * squared rounding error sum_j (w'_j - q_j)^2 of the block's weights at the
+ * block start, every element rounded on its own with no in-block updates; the
+ * least score wins (ties: the smaller scale) and that candidate's block is
+ * committed with its replayed GPTQ updates as usual.  For the scale-selection
+ * ablation; ignored with RTN. */
+#define NVQ_FLAG_INDEP  8u
 
 /*
  * hessian_accumulate -- second-order state of the layer ("Replay the

@@ -23,6 +23,7 @@ NVQ_DTYPE_BF16 = 1
 FLAG_RTN = 1
 FLAG_NO_ERR = 2
 FLAG_FP64 = 4
+FLAG_INDEP = 8
 
 EXPORTS = [
     "hessian_workspace_size", "hessian_accumulate",

@@ -87,7 +87,8 @@ int quant_check(const char* fn, const void* W, int w_dtype, int64_t m, int64_t k
                 const uint8_t* scales, const float* row_err, const void* ws, size_t ws_bytes) {
   const bool rtn = flags & NVQ_FLAG_RTN;
   const bool want_err = !(flags & NVQ_FLAG_NO_ERR);
-  if (flags & ~(NVQ_FLAG_RTN | NVQ_FLAG_NO_ERR | NVQ_FLAG_FP64)) return failp(NVQ_ERR_VALUE, fn, "unknown flags 0x%x", flags);
+  if (flags & ~(NVQ_FLAG_RTN | NVQ_FLAG_NO_ERR | NVQ_FLAG_FP64 | NVQ_FLAG_INDEP))
+    return failp(NVQ_ERR_VALUE, fn, "unknown flags 0x%x", flags);
   if (!W || !g || !codes || !scales) return failp(NVQ_ERR_NULL, fn, "W, g, codes and scales are required");
   if (!rtn && !U) return failp(NVQ_ERR_NULL, fn, "U is required without NVQ_FLAG_RTN");
   if (want_err && (!H || !row_err)) return failp(NVQ_ERR_NULL, fn, "H and row_err are required unless NVQ_FLAG_NO_ERR");
@@ -132,7 +133,7 @@ hipError_t weighted_error_all(const void* W, int bf, int64_t m, int64_t k, int64
 // updates, in another order): a batch's errors update the rest of its
 // 512-column block at once, and a finished block's error slab updates every
 // later column.
-hipError_t sweep_f32(int64_t m, int64_t k, const float* U, const float* g, int n_cand, uint8_t* codes,
+hipError_t sweep_f32(int64_t m, int64_t k, const float* U, const float* g, int n_cand, bool indep, uint8_t* codes,
                      uint8_t* scales, float* row_loss, float* Wp, float* Eslab, const float* invd, hipStream_t s) {
   auto rank_update = [&](const float* Eb, int64_t r0, int64_t c0, int64_t kk, int64_t ncol) {
     GemmArgs a{};
@@ -147,7 +148,7 @@ hipError_t sweep_f32(int64_t m, int64_t k, const float* U, const float* g, int n
     const int64_t s1 = std::min<int64_t>(k, s0 + kSuperBatch);
     for (int64_t i1 = s0; e == hipSuccess && i1 < s1; i1 += kBatch) {
       const int ncols = (int)std::min<int64_t>(kBatch, s1 - i1);
-      e = sweep_batch_launch(Wp, U, invd, g, m, k, (int)i1, ncols, n_cand, codes, scales, Eslab + (i1 - s0),
+      e = sweep_batch_launch(Wp, U, invd, g, m, k, (int)i1, ncols, n_cand, indep, codes, scales, Eslab + (i1 - s0),
                              kSuperBatch, row_loss, s);
       const int64_t i2 = i1 + ncols;
       if (e == hipSuccess && i2 < s1) e = rank_update(Eslab + (i1 - s0), i1, i2, ncols, s1 - i2);
@@ -164,6 +165,7 @@ hipError_t quant_run(const void* W, int w_dtype, int64_t m, int64_t k, int64_t l
   const bool rtn = flags & NVQ_FLAG_RTN;
   const bool want_err = !(flags & NVQ_FLAG_NO_ERR);
   const bool f64 = (flags & NVQ_FLAG_FP64) && !rtn;
+  const bool indep = flags & NVQ_FLAG_INDEP;
   QuantWs L = quant_ws(m, k, f64);
   float* Wp = (float*)(base + L.wp);
   float* Eslab = (float*)(base + L.eslab);
@@ -184,7 +186,7 @@ hipError_t quant_run(const void* W, int w_dtype, int64_t m, int64_t k, int64_t l
       const int64_t s1 = std::min<int64_t>(k, s0 + kSuperBatch);
       for (int64_t i1 = s0; e == hipSuccess && i1 < s1; i1 += kBatch) {
         const int ncols = (int)std::min<int64_t>(kBatch, s1 - i1);
-        e = sweep_batch_launch_f64(Wd, U, g, m, k, (int)i1, ncols, n_cand, codes, scales, Ed + (i1 - s0),
+        e = sweep_batch_launch_f64(Wd, U, g, m, k, (int)i1, ncols, n_cand, indep, codes, scales, Ed + (i1 - s0),
                                    kSuperBatch, row_loss, s);
         const int64_t i2 = i1 + ncols;
         if (e == hipSuccess && i2 < s1)
@@ -197,7 +199,7 @@ hipError_t quant_run(const void* W, int w_dtype, int64_t m, int64_t k, int64_t l
     e = inv_diag_launch(U, k, invd, s);
     if (e == hipSuccess) e = load_working_copy(W, bf, m, k, ldw, Wp, s);
     if (e == hipSuccess && row_loss) e = fill_f32(row_loss, m, 0.0f, s);
-    if (e == hipSuccess) e = sweep_f32(m, k, U, g, n_cand, codes, scales, row_loss, Wp, Eslab, invd, s);
+    if (e == hipSuccess) e = sweep_f32(m, k, U, g, n_cand, indep, codes, scales, row_loss, Wp, Eslab, invd, s);
   }
   if (e == hipSuccess && want_err) e = weighted_error_all(W, bf, m, k, ldw, H, g, codes, scales, row_err, Wp, part, s);
   return e;

@@ -67,14 +67,16 @@ hipError_t rtn_launch(const void* W, int bf16, int64_t m, int64_t k, int64_t ldw
 hipError_t load_working_copy(const void* W, int bf16, int64_t m, int64_t k, int64_t ldw,
                              float* Wp, hipStream_t s);
 hipError_t inv_diag_launch(const float* U, int64_t k, float* invd, hipStream_t s);
+// indep: choose each block's scale by the block-independent squared rounding
+// error instead of the replay score (the committed block is still replayed).
 hipError_t sweep_batch_launch(float* Wp, const float* U, const float* invd, const float* g,
-                              int64_t m, int64_t k, int i1, int ncols, int n_cand,
+                              int64_t m, int64_t k, int i1, int ncols, int n_cand, bool indep,
                               uint8_t* codes, uint8_t* scales, float* Eslab, int64_t lde, float* row_loss,
                               hipStream_t s);
 // The same sweep with fp64 working weights and errors (U read as fp32).
 hipError_t sweep_batch_launch_f64(double* Wp, const float* U, const float* g, int64_t m, int64_t k, int i1,
-                                  int ncols, int n_cand, uint8_t* codes, uint8_t* scales, double* Eslab, int64_t lde,
-                                  float* row_loss, hipStream_t s);
+                                  int ncols, int n_cand, bool indep, uint8_t* codes, uint8_t* scales, double* Eslab,
+                                  int64_t lde, float* row_loss, hipStream_t s);
 hipError_t load_working_copy_f64(const void* W, int bf16, int64_t m, int64_t k, int64_t ldw, double* Wp,
                                  hipStream_t s);
 // Columns of the two-level lazy update: each 128-column batch updates the

@@ -274,7 +274,7 @@ __device__ __forceinline__ void load16(const T* p, T (&v)[16]) {
   for (int q = 0; q < 16; ++q) v[q] = p[q];
 }
 
-template <int G, typename T>
+template <int G, typename T, bool INDEP>
 __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
     T* __restrict__ Wp, const float* __restrict__ U, const float* __restrict__ invd,
     const float* __restrict__ gptr, int64_t m, int64_t k, int i1, int ncols, int n_cand,
@@ -400,10 +400,23 @@ __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
     uint32_t plo = 0, phi = 0;
     int cand = 0;
     T score = F64 ? T(__builtin_inf()) : T(__builtin_inff());
+    T rsc = 0;   // this candidate's replay score (its damped loss)
     if (a > T(0)) {
       const int lo = candidate_lo(e4m3_code_of_ratio(a, g), n_cand);
       cand = lo + (ci < n_cand ? ci : 0);
       const float s = e4m3_value(cand);
+      // Block-independent selection: the plain squared rounding error of the
+      // block's weights at the block start, each rounded on its own.
+      T isc = 0;
+      if constexpr (INDEP) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          T dj;
+          if constexpr (F64) dj = v[j] - e2m1_dequant_f64(e2m1_encode(v[j], s, g), s, g);
+          else dj = v[j] - e2m1_dequant(e2m1_encode(v[j], s, g), s, g);
+          isc = fma(dj, dj, isc);
+        }
+      }
       T sc = 0;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
@@ -425,7 +438,8 @@ __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
         e[j] = ej;
         if (j < 8) plo |= (uint32_t)code << (4 * j); else phi |= (uint32_t)code << (4 * (j - 8));
       }
-      if (ci < n_cand) score = sc;
+      rsc = sc;
+      if (ci < n_cand) score = INDEP ? isc : sc;
     }
     T bs = score;
     int bi = ci;
@@ -439,7 +453,7 @@ __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
       T* es = Eslab + row * lde + c0;
 #pragma unroll
       for (int j = 0; j < 16; ++j) es[j] = e[j];
-      if (a > T(0)) loss += bs;
+      if (a > T(0)) loss += rsc;
     }
     // Update the later columns of the batch: w'_l -= sum_j e_j U[c0+j][l].
     if (row_ok && c0 + kBlock < ncols) {
@@ -467,23 +481,27 @@ __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
 
 template <int G, typename T>
 hipError_t sweep_launch_g(T* Wp, const float* U, const float* invd, const float* g, int64_t m, int64_t k,
-                          int i1, int ncols, int n_cand, uint8_t* codes, uint8_t* scales, T* Eslab,
+                          int i1, int ncols, int n_cand, bool indep, uint8_t* codes, uint8_t* scales, T* Eslab,
                           int64_t lde, float* row_loss, hipStream_t s) {
   constexpr int ROWS = SweepCfg<G>::ROWS;
   dim3 grid((unsigned)((m + ROWS - 1) / ROWS));
-  hipLaunchKernelGGL((sweep_batch_kernel<G, T>), grid, dim3(SweepCfg<G>::THREADS), 0, s, Wp, U, invd, g, m, k,
-                     i1, ncols, n_cand, codes, scales, Eslab, lde, row_loss);
+  if (indep)
+    hipLaunchKernelGGL((sweep_batch_kernel<G, T, true>), grid, dim3(SweepCfg<G>::THREADS), 0, s, Wp, U, invd, g, m,
+                       k, i1, ncols, n_cand, codes, scales, Eslab, lde, row_loss);
+  else
+    hipLaunchKernelGGL((sweep_batch_kernel<G, T, false>), grid, dim3(SweepCfg<G>::THREADS), 0, s, Wp, U, invd, g, m,
+                       k, i1, ncols, n_cand, codes, scales, Eslab, lde, row_loss);
   return hipGetLastError();
 }
 template <typename T>
 hipError_t sweep_launch_t(T* Wp, const float* U, const float* invd, const float* g, int64_t m, int64_t k, int i1,
-                          int ncols, int n_cand, uint8_t* codes, uint8_t* scales, T* Eslab, int64_t lde,
+                          int ncols, int n_cand, bool indep, uint8_t* codes, uint8_t* scales, T* Eslab, int64_t lde,
                           float* row_loss, hipStream_t s) {
-  if (n_cand <= 1) return sweep_launch_g<1>(Wp, U, invd, g, m, k, i1, ncols, n_cand, codes, scales, Eslab, lde, row_loss, s);
-  if (n_cand <= 2) return sweep_launch_g<2>(Wp, U, invd, g, m, k, i1, ncols, n_cand, codes, scales, Eslab, lde, row_loss, s);
-  if (n_cand <= 4) return sweep_launch_g<4>(Wp, U, invd, g, m, k, i1, ncols, n_cand, codes, scales, Eslab, lde, row_loss, s);
-  if (n_cand <= 8) return sweep_launch_g<8>(Wp, U, invd, g, m, k, i1, ncols, n_cand, codes, scales, Eslab, lde, row_loss, s);
-  return sweep_launch_g<16>(Wp, U, invd, g, m, k, i1, ncols, n_cand, codes, scales, Eslab, lde, row_loss, s);
+  if (n_cand <= 1) return sweep_launch_g<1>(Wp, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s);
+  if (n_cand <= 2) return sweep_launch_g<2>(Wp, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s);
+  if (n_cand <= 4) return sweep_launch_g<4>(Wp, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s);
+  if (n_cand <= 8) return sweep_launch_g<8>(Wp, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s);
+  return sweep_launch_g<16>(Wp, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s);
 }
 
 }  // namespace
@@ -554,14 +572,14 @@ hipError_t load_working_copy_f64(const void* W, int bf16, int64_t m, int64_t k, 
 }
 
 hipError_t sweep_batch_launch(float* Wp, const float* U, const float* invd, const float* g, int64_t m, int64_t k,
-                              int i1, int ncols, int n_cand, uint8_t* codes, uint8_t* scales, float* Eslab,
-                              int64_t lde, float* row_loss, hipStream_t s) {
-  return sweep_launch_t<float>(Wp, U, invd, g, m, k, i1, ncols, n_cand, codes, scales, Eslab, lde, row_loss, s);
+                              int i1, int ncols, int n_cand, bool indep, uint8_t* codes, uint8_t* scales,
+                              float* Eslab, int64_t lde, float* row_loss, hipStream_t s) {
+  return sweep_launch_t<float>(Wp, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s);
 }
 hipError_t sweep_batch_launch_f64(double* Wp, const float* U, const float* g, int64_t m, int64_t k, int i1,
-                                  int ncols, int n_cand, uint8_t* codes, uint8_t* scales, double* Eslab, int64_t lde,
-                                  float* row_loss, hipStream_t s) {
-  return sweep_launch_t<double>(Wp, U, U, g, m, k, i1, ncols, n_cand, codes, scales, Eslab, lde, row_loss, s);
+                                  int ncols, int n_cand, bool indep, uint8_t* codes, uint8_t* scales, double* Eslab,
+                                  int64_t lde, float* row_loss, hipStream_t s) {
+  return sweep_launch_t<double>(Wp, U, U, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s);
 }
 
 hipError_t delta_w_launch(const void* W, int bf16, int64_t m, int64_t k, int64_t ldw, const uint8_t* codes,
