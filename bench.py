@@ -137,6 +137,39 @@ def summarize_pmc(fetch_csv, write_csv):
     print(json.dumps(out))
 
 
+def streamed(nvq, Xh, dev):
+    """Hessian of the benchmarked layer's X (2 GiB bf16) from host memory, in
+    32768-token chunks, PCIe copies overlapped with the accumulation; against
+    X resident in HBM."""
+    import torch
+    chunk = 32768
+    Xd = Xh.to(dev)
+    H = torch.zeros(K_IN, K_IN, dtype=torch.float32, device=dev)
+
+    def timed(fn, reps=3):
+        fn()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t) / reps * 1e3
+
+    ms_dev = timed(lambda: nvq.hessian_accumulate(Xd, H))
+    del Xd
+    Xpage = Xh.clone()   # pageable copy; Xh is pinned
+    ms_pin = timed(lambda: nvq.hessian_accumulate_host(Xh, H, chunk=chunk))
+    ms_page = timed(lambda: nvq.hessian_accumulate_host(Xpage, H, chunk=chunk))
+    gb = Xh.numel() * 2 / 1e9
+    print(json.dumps({"streamed_hessian": WORKLOAD, "chunk_tokens": chunk, "x_gb": round(gb, 3),
+                      "ms_x_in_hbm": round(ms_dev, 3), "ms_x_pinned_host": round(ms_pin, 3),
+                      "ms_x_pageable_host": round(ms_page, 3),
+                      "host_to_device_gbs_pinned": round(gb / ms_pin * 1e3, 1),
+                      "host_to_device_gbs_pageable": round(gb / ms_page * 1e3, 1),
+                      "device_bytes_streamed": int(nvq.lib.hessian_host_workspace_size(chunk, K_IN, 1)),
+                      "data": "synthetic"}))
+
+
 def ablation(nvq, Wd, Xd):
     """Total weighted error sum_r dW_r H dW_r^T of the benchmarked layer under
     each scale-selection configuration, all on the GPU."""
@@ -163,6 +196,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the Hessian's measured HBM traffic from two rocprofv3 --pmc CSVs and exit")
+    ap.add_argument("--streamed", action="store_true",
+                    help="instead of the layer step, time the Hessian with X in host memory (pinned and "
+                         "pageable), streamed to the device in chunks, against X resident in HBM")
     ap.add_argument("--ablation", action="store_true",
                     help="instead of timing, print the layer's total weighted error under four scale-selection "
                          "configurations (RTN absmax, GPTQ absmax, GPTQ block-independent, GPTQ Schur Replay)")
@@ -186,6 +222,9 @@ def main():
     Wd = synth.to_bf16_tensor(W).to(dev)
     Xh = torch.empty(N_TOK, K_IN, dtype=torch.bfloat16, pin_memory=True)
     synth.activations("attn_proj", N_TOK, K_IN, massive=8, out=Xh)
+    if args.streamed:
+        streamed(nvq, Xh, dev)
+        return
     t0 = time.perf_counter()
     Xd = Xh.to(dev, non_blocking=True)
     torch.cuda.synchronize()

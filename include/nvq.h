@@ -100,6 +100,40 @@ int hessian_accumulate(const void* X, int x_dtype, int64_t n, int64_t k, int64_t
                        float* H, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * hessian_accumulate_host -- the same H += X^T X with X resident in host
+ * memory ("Replay the Curvature", Abstract: calibration activations are
+ * tiered across device, host and disk, and only the active layer is kept on
+ * the device).  X is streamed to the device in chunks of `chunk` tokens
+ * through two device buffers: chunk i+1 is copied (on copy_stream) while
+ * chunk i is accumulated (on stream), ordered by events.  The result equals
+ * calling hessian_accumulate on the chunks in order.
+ *
+ *   X_host   host [n x ldx], element type x_dtype: pinned (hipHostMalloc) or
+ *            pageable (e.g. a memory-mapped file).  Without staging it must
+ *            stay valid until copy_stream's work is done; pageable memory is
+ *            then copied synchronously by the runtime.
+ *   n, k     tokens and channels; n >= 0, k > 0, k % 16 == 0; ldx >= k.
+ *   H        device fp32 [k x k], accumulated in place.
+ *   chunk    tokens per chunk, > 0.
+ *   ws       device workspace of hessian_host_workspace_size(chunk, k, x_dtype)
+ *            bytes (two chunk buffers and the Hessian workspace), 256-aligned.
+ *   staging  NULL, or pinned host memory of hessian_host_staging_size(chunk,
+ *            k, x_dtype) bytes: pageable chunks are then copied into it by
+ *            host threads and sent asynchronously; the call returns once the
+ *            staging buffers have been read (the accumulation itself is still
+ *            asynchronous on stream).
+ *   stream, copy_stream  compute and copy streams (default priority); a NULL
+ *            copy_stream means stream (no overlap).
+ * The device memory used is H plus two chunks plus the Hessian workspace,
+ * whatever n is.
+ */
+size_t hessian_host_workspace_size(int64_t chunk, int64_t k, int x_dtype);
+size_t hessian_host_staging_size(int64_t chunk, int64_t k, int x_dtype);
+int hessian_accumulate_host(const void* X_host, int x_dtype, int64_t n, int64_t k, int64_t ldx, float* H,
+                            int64_t chunk, void* ws, size_t ws_bytes, void* staging, size_t staging_bytes,
+                            void* stream, void* copy_stream);
+
+/*
  * hessian_accumulate_grouped -- one Hessian per group of token rows, for a
  * mixture-of-experts layer in which every expert is a linear layer of its own
  * that sees only the tokens routed to it ("Replay the Curvature", Abstract:

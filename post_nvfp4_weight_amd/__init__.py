@@ -28,6 +28,7 @@ FLAG_INDEP = 8
 EXPORTS = [
     "hessian_workspace_size", "hessian_accumulate",
     "hessian_grouped_workspace_size", "hessian_accumulate_grouped",
+    "hessian_host_workspace_size", "hessian_host_staging_size", "hessian_accumulate_host",
     "factor_hinv_workspace_size", "factor_hinv", "factor_hinv_batched",
     "nvfp4_global_scale_workspace_size", "nvfp4_global_scale",
     "gptq_nvfp4_workspace_size", "gptq_nvfp4_quantize", "gptq_nvfp4_quantize_batched",
@@ -51,6 +52,9 @@ def _load():
         "hessian_workspace_size": (SZ, [I64, I64, I32]),
         "hessian_accumulate": (I32, [P, I32, I64, I64, I64, P, P, SZ, P]),
         "hessian_grouped_workspace_size": (SZ, [P, I64, I64, I32]),
+        "hessian_host_workspace_size": (SZ, [I64, I64, I32]),
+        "hessian_host_staging_size": (SZ, [I64, I64, I32]),
+        "hessian_accumulate_host": (I32, [P, I32, I64, I64, I64, P, I64, P, SZ, P, SZ, P, P]),
         "hessian_accumulate_grouped": (I32, [P, I32, I64, I64, I64, P, P, I64, P, P, SZ, P]),
         "factor_hinv_batched": (I32, [P, I64, I64, I64, F32, P, I64, P, P, P, SZ, P]),
         "gptq_nvfp4_quantize_batched": (I32, [P, I32, I64, I64, I64, I64, I64, P, I64, P, I64, P, I32, U32, P, P,
@@ -121,6 +125,58 @@ def hessian_accumulate(X, H=None, ws=None):
         ws = _workspace(need, X.device)
     _check("hessian_accumulate", lib.hessian_accumulate(_ptr(X), _dtype_code(X), n, k, ldx, _ptr(H), _ptr(ws),
                                                         need, _stream()))
+    return H
+
+
+_copy_streams = {}
+
+
+def hessian_accumulate_host(X, H=None, chunk=32768, staging=True, device="cuda:0"):
+    """H += X^T X with X in host memory, streamed to the device in chunks.
+
+    X: a CPU torch tensor (bf16 or fp32, pinned or not) or a NumPy array whose
+    rows are contiguous: uint16 holding bf16 bits, or float32 (a np.memmap of
+    a file on disk works).  Pageable X goes through pinned staging buffers
+    (staging=True); the copies run on a library copy stream of default
+    priority, overlapped with the accumulation on the current stream.
+    """
+    if isinstance(X, torch.Tensor):
+        if X.device.type != "cpu" or X.dim() != 2 or X.stride(1) != 1:
+            raise ValueError("X must be a 2-D CPU tensor with contiguous rows")
+        code = _dtype_code(X)
+        ptr, ldx, pinned = X.data_ptr(), X.stride(0), X.is_pinned()
+    else:
+        import numpy as np
+        X = np.asarray(X) if not isinstance(X, np.ndarray) else X
+        if X.ndim != 2 or X.strides[1] != X.itemsize:
+            raise ValueError("X must be 2-D with contiguous rows")
+        if X.dtype == np.uint16:
+            code = NVQ_DTYPE_BF16
+        elif X.dtype == np.float32:
+            code = NVQ_DTYPE_F32
+        else:
+            raise ValueError("NumPy X must be uint16 (bf16 bits) or float32")
+        ptr, ldx, pinned = X.ctypes.data, X.strides[0] // X.itemsize, False
+    n, k = X.shape
+    dev = torch.device(device)
+    if H is None:
+        H = torch.zeros(k, k, dtype=torch.float32, device=dev)
+    need = lib.hessian_host_workspace_size(chunk, k, code)
+    ws = _workspace(need, dev)
+    stg, stg_n = None, 0
+    if staging and not pinned:
+        stg_n = lib.hessian_host_staging_size(chunk, k, code)
+        stg = torch.empty(max(1, stg_n), dtype=torch.uint8, pin_memory=True)
+    if dev not in _copy_streams:
+        _copy_streams[dev] = torch.cuda.Stream(device=dev)
+    cs = _copy_streams[dev]
+    cur = torch.cuda.current_stream(dev)
+    cs.wait_stream(cur)   # H and the workspace are ready before the first copy
+    _check("hessian_accumulate_host",
+           lib.hessian_accumulate_host(ctypes.c_void_p(ptr), code, n, k, ldx, _ptr(H), chunk, _ptr(ws), need,
+                                       _ptr(stg), stg_n, ctypes.c_void_p(cur.cuda_stream),
+                                       ctypes.c_void_p(cs.cuda_stream)))
+    ws.record_stream(cs)
     return H
 
 

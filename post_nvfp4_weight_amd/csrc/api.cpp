@@ -6,7 +6,10 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstring>
 #include <string>
+#include <thread>
+#include <vector>
 
 #include "../../include/nvq.h"
 #include "common.h"
@@ -251,6 +254,104 @@ int hessian_accumulate(const void* X, int x_dtype, int64_t n, int64_t k, int64_t
     return fail(NVQ_ERR_WORKSPACE, "hessian_accumulate: workspace needs %zu bytes (256-aligned), got %zu", need,
                 ws_bytes);
   return hip_status(hessian_run(X, x_dtype, n, k, ldx, H, ws, (hipStream_t)stream), "hessian_accumulate");
+}
+
+// ---- Hessian over host-resident activations ---------------------------------
+namespace {
+size_t host_chunk_bytes(int64_t chunk, int64_t k, int x_dtype) {
+  return align_up((size_t)chunk * k * (x_dtype == NVQ_DTYPE_BF16 ? 2 : 4));
+}
+// Rows [r0, r0 + rows) of a host matrix with row stride ld into a dense buffer.
+void copy_rows_host(char* dst, const char* src, int64_t rows, int64_t row_bytes, int64_t ld_bytes) {
+  auto part = [&](int64_t a, int64_t b) {
+    if (ld_bytes == row_bytes) {
+      std::memcpy(dst + a * row_bytes, src + a * ld_bytes, (size_t)((b - a) * row_bytes));
+    } else {
+      for (int64_t r = a; r < b; ++r) std::memcpy(dst + r * row_bytes, src + r * ld_bytes, (size_t)row_bytes);
+    }
+  };
+  const int64_t bytes = rows * row_bytes;
+  const int nt = bytes >= (64ll << 20) ? 8 : (bytes >= (8ll << 20) ? 4 : 1);
+  if (nt == 1) { part(0, rows); return; }
+  std::vector<std::thread> th;
+  for (int t = 0; t < nt; ++t) th.emplace_back(part, rows * t / nt, rows * (t + 1) / nt);
+  for (auto& x : th) x.join();
+}
+}  // namespace
+
+size_t hessian_host_workspace_size(int64_t chunk, int64_t k, int x_dtype) {
+  if (chunk <= 0 || k <= 0 || !dtype_ok(x_dtype)) return 0;
+  return 2 * host_chunk_bytes(chunk, k, x_dtype) + hessian_workspace_size(chunk, k, x_dtype);
+}
+size_t hessian_host_staging_size(int64_t chunk, int64_t k, int x_dtype) {
+  if (chunk <= 0 || k <= 0 || !dtype_ok(x_dtype)) return 0;
+  return 2 * host_chunk_bytes(chunk, k, x_dtype);
+}
+
+int hessian_accumulate_host(const void* X_host, int x_dtype, int64_t n, int64_t k, int64_t ldx, float* H,
+                            int64_t chunk, void* ws, size_t ws_bytes, void* staging, size_t staging_bytes,
+                            void* stream, void* copy_stream) {
+  const char* fn = "hessian_accumulate_host";
+  if (!H) return failp(NVQ_ERR_NULL, fn, "H is NULL");
+  if (!dtype_ok(x_dtype)) return failp(NVQ_ERR_DTYPE, fn, "x_dtype %d", x_dtype);
+  if (n < 0 || k <= 0 || k % 16 != 0 || ldx < k)
+    return failp(NVQ_ERR_SHAPE, fn, "n=%lld k=%lld ldx=%lld (need n>=0, k>0, k%%16==0, ldx>=k)", (long long)n,
+                 (long long)k, (long long)ldx);
+  if (chunk <= 0) return failp(NVQ_ERR_SHAPE, fn, "chunk=%lld (need > 0)", (long long)chunk);
+  if (n == 0) return NVQ_OK;
+  if (!X_host) return failp(NVQ_ERR_NULL, fn, "X_host is NULL");
+  if (!aligned(H, 16)) return failp(NVQ_ERR_ALIGN, fn, "H must be 16-byte aligned");
+  const size_t need = hessian_host_workspace_size(chunk, k, x_dtype);
+  if (!ws || ws_bytes < need || !aligned(ws, kAlign))
+    return failp(NVQ_ERR_WORKSPACE, fn, "workspace needs %zu bytes (256-aligned), got %zu", need, ws_bytes);
+  const size_t sneed = hessian_host_staging_size(chunk, k, x_dtype);
+  if (staging && staging_bytes < sneed)
+    return failp(NVQ_ERR_WORKSPACE, fn, "staging needs %zu bytes, got %zu", sneed, staging_bytes);
+
+  const int64_t es = x_dtype == NVQ_DTYPE_BF16 ? 2 : 4;
+  const size_t cb = host_chunk_bytes(chunk, k, x_dtype);
+  char* dev[2] = {(char*)ws, (char*)ws + cb};
+  void* hws = (char*)ws + 2 * cb;
+  char* stg[2] = {(char*)staging, staging ? (char*)staging + cb : nullptr};
+  hipStream_t s = (hipStream_t)stream, cs = copy_stream ? (hipStream_t)copy_stream : s;
+  hipEvent_t copied[2] = {nullptr, nullptr}, used[2] = {nullptr, nullptr};
+  hipError_t e = hipSuccess;
+  for (int b = 0; b < 2 && e == hipSuccess; ++b) {
+    e = hipEventCreateWithFlags(&copied[b], hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&used[b], hipEventDisableTiming);
+  }
+  const char* src = (const char*)X_host;
+  for (int64_t t0 = 0, i = 0; e == hipSuccess && t0 < n; t0 += chunk, ++i) {
+    const int b = (int)(i & 1);
+    const int64_t rows = std::min<int64_t>(chunk, n - t0);
+    const char* from = src + t0 * ldx * es;
+    int64_t from_ld = ldx * es;
+    if (stg[0]) {
+      // The copy out of this staging buffer two chunks ago must be done.
+      if (i >= 2) e = hipEventSynchronize(copied[b]);
+      if (e != hipSuccess) break;
+      copy_rows_host(stg[b], from, rows, k * es, ldx * es);
+      from = stg[b];
+      from_ld = k * es;
+    }
+    // The device buffer's previous chunk must have been consumed.
+    if (i >= 2) e = hipStreamWaitEvent(cs, used[b], 0);
+    if (e == hipSuccess)
+      e = hipMemcpy2DAsync(dev[b], (size_t)(k * es), from, (size_t)from_ld, (size_t)(k * es), (size_t)rows,
+                           hipMemcpyHostToDevice, cs);
+    if (e == hipSuccess) e = hipEventRecord(copied[b], cs);
+    if (e == hipSuccess) e = hipStreamWaitEvent(s, copied[b], 0);
+    if (e == hipSuccess) e = hessian_run(dev[b], x_dtype, rows, k, k, H, hws, s);
+    if (e == hipSuccess) e = hipEventRecord(used[b], s);
+  }
+  // With staging, return only once the staging buffers have been read, so the
+  // caller may reuse them at once.
+  for (int b = 0; b < 2 && stg[0] && e == hipSuccess; ++b) e = hipEventSynchronize(copied[b]);
+  for (int b = 0; b < 2; ++b) {
+    if (copied[b]) (void)hipEventDestroy(copied[b]);
+    if (used[b]) (void)hipEventDestroy(used[b]);
+  }
+  return hip_status(e, fn);
 }
 
 size_t hessian_grouped_workspace_size(const int64_t* grp_off, int64_t G, int64_t k, int x_dtype) {

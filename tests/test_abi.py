@@ -82,6 +82,14 @@ def test_host_validation_rejects_bad_arguments():
     rc = lib.gptq_nvfp4_quantize_batched(fake, 1, 2, 16, 32, 32, 100, fake, 1024, fake, 1024, fake, 16, 0,
                                          fake, fake, fake, None, fake, 1 << 30, None)
     assert rc == -2
+    # Hessian over host memory: chunk, shape, H, workspace and staging checks; n = 0 is a no-op
+    assert lib.hessian_accumulate_host(fake, 1, 10, 32, 32, fake, 0, fake, 1 << 30, None, 0, None, None) == -2
+    assert lib.hessian_accumulate_host(fake, 1, 10, 24, 24, fake, 8, fake, 1 << 30, None, 0, None, None) == -2
+    assert lib.hessian_accumulate_host(fake, 1, 10, 32, 32, None, 8, fake, 1 << 30, None, 0, None, None) == -1
+    assert lib.hessian_accumulate_host(None, 1, 0, 32, 32, fake, 8, None, 0, None, 0, None, None) == 0
+    assert lib.hessian_accumulate_host(fake, 1, 10, 32, 32, fake, 8, P(1 << 20), 16, None, 0, None, None) == -5
+    assert lib.hessian_accumulate_host(fake, 1, 10, 32, 32, fake, 8, P(1 << 20), 1 << 30, fake, 16, None,
+                                       None) == -5
     for s in (0, -1, -2, -3, -4, -5, -6, -7, -8, 99):
         assert lib.nvq_status_string(s)
 
@@ -96,3 +104,8 @@ def test_workspace_queries_are_consistent():
     off = (ctypes.c_int64 * 4)(0, 100, 100, 350)
     need = lib.hessian_grouped_workspace_size(off, 3, 256, 1)
     assert need >= 250 * 256 * 2 + lib.hessian_workspace_size(250, 256, 1)
+    # host streaming: two chunk buffers plus the Hessian workspace of one chunk; two pinned chunks
+    ws = lib.hessian_host_workspace_size(1000, 256, 1)
+    assert ws >= 2 * 1000 * 256 * 2 + lib.hessian_workspace_size(1000, 256, 1)
+    assert lib.hessian_host_staging_size(1000, 256, 1) >= 2 * 1000 * 256 * 2
+    assert lib.hessian_host_staging_size(1000, 256, 0) >= 2 * 1000 * 256 * 4
