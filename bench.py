@@ -170,6 +170,37 @@ def streamed(nvq, Xh, dev):
                       "data": "synthetic"}))
 
 
+def consumer_bench(nvq, Wd, Xd):
+    """nvfp4_gemm (Y = X dequant(W)^T) on the benchmarked layer after quantization,
+    for several token counts, against torch's bf16 GEMM on the dequantized weights."""
+    import torch
+    res = nvq.quantize_layer(Wd, Xd, n_cand=N_CAND)
+    codes, scales, g = res["codes"], res["scales"], res["g"]
+    Wdq = nvq.nvfp4_dequantize(codes, scales, g, torch.bfloat16)
+    out = []
+    for T in (16, 256, 2048, 8192):
+        X = Xd[:T].contiguous()
+
+        def timed(fn, reps=20):
+            fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / reps
+
+        ms = timed(lambda: nvq.nvfp4_gemm(X, codes, scales, g))
+        ms_bf16 = timed(lambda: torch.matmul(X, Wdq.t()))
+        flops = 2.0 * T * M * K_IN
+        wbytes = M * K_IN * 0.5625
+        out.append({"tokens": T, "ms": round(ms, 4), "tflops": round(flops / ms / 1e9, 1),
+                    "weight_gbs": round(wbytes / ms / 1e6, 1), "ms_torch_bf16_dense": round(ms_bf16, 4)})
+    print(json.dumps({"consumer": "nvfp4 weight-only GEMM, " + WORKLOAD, "results": out, "data": "synthetic"}))
+
+
 def ablation(nvq, Wd, Xd):
     """Total weighted error sum_r dW_r H dW_r^T of the benchmarked layer under
     each scale-selection configuration, all on the GPU."""
@@ -199,6 +230,8 @@ def main():
     ap.add_argument("--streamed", action="store_true",
                     help="instead of the layer step, time the Hessian with X in host memory (pinned and "
                          "pageable), streamed to the device in chunks, against X resident in HBM")
+    ap.add_argument("--consumer", action="store_true",
+                    help="instead of the layer step, time the NVFP4 weight-only GEMM on the quantized layer")
     ap.add_argument("--ablation", action="store_true",
                     help="instead of timing, print the layer's total weighted error under four scale-selection "
                          "configurations (RTN absmax, GPTQ absmax, GPTQ block-independent, GPTQ Schur Replay)")
@@ -233,6 +266,9 @@ def main():
     log(f"inputs resident (H2D {h2d_s:.3f} s)")
     if args.ablation:
         ablation(nvq, Wd, Xd)
+        return
+    if args.consumer:
+        consumer_bench(nvq, Wd, Xd)
         return
 
     lib = nvq.lib

@@ -292,6 +292,23 @@ int gptq_nvfp4_quantize_batched(const void* W, int w_dtype, int64_t batch, int64
 int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* g, int64_t m,
                      int64_t k, void* out, int out_dtype, void* stream);
 
+/*
+ * nvfp4_gemm -- a consumer of the exported weights ("Replay the Curvature",
+ * Abstract: the quantized layer is exported in NVFP4 for use): the
+ * weight-only product Y = X dequant(W)^T with bf16 activations.
+ * Computed as Y = g (X Q^T) with Q = e2m1 * e4m3 exact in bf16, on the bf16
+ * matrix cores with fp32 accumulation (within 2^-24 per product of
+ * X fl32(Q g)^T).
+ *
+ *   X       device bf16 [T x ldx]; T >= 0, k > 0, k % 16 == 0, ldx >= k,
+ *           ldx % 8 == 0; 16-byte aligned.
+ *   codes, scales, g   the layer as written by gptq_nvfp4_quantize: codes
+ *           [m x k/2] (8-byte aligned), scales [m x k/16], g 1 float (device).
+ *   Y       device [T x ldy] of y_dtype (fp32 or bf16, RNE), ldy >= m.
+ */
+int nvfp4_gemm(const void* X, int x_dtype, int64_t T, int64_t k, int64_t ldx, const uint8_t* codes,
+               const uint8_t* scales, const float* g, int64_t m, void* Y, int y_dtype, int64_t ldy, void* stream);
+
 /* Text of a status code; never NULL. */
 const char* nvq_status_string(int status);
 /* Reason of the most recent failing call on this thread ("" if none). */

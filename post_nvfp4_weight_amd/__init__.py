@@ -32,7 +32,7 @@ EXPORTS = [
     "factor_hinv_workspace_size", "factor_hinv", "factor_hinv_batched",
     "nvfp4_global_scale_workspace_size", "nvfp4_global_scale",
     "gptq_nvfp4_workspace_size", "gptq_nvfp4_quantize", "gptq_nvfp4_quantize_batched",
-    "nvfp4_dequantize", "nvq_status_string", "nvq_last_error",
+    "nvfp4_dequantize", "nvfp4_gemm", "nvq_status_string", "nvq_last_error",
 ]
 
 
@@ -66,6 +66,7 @@ def _load():
         "gptq_nvfp4_workspace_size": (SZ, [I64, I64, U32]),
         "gptq_nvfp4_quantize": (I32, [P, I32, I64, I64, I64, P, P, P, I32, U32, P, P, P, P, P, SZ, P]),
         "nvfp4_dequantize": (I32, [P, P, P, I64, I64, P, I32, P]),
+        "nvfp4_gemm": (I32, [P, I32, I64, I64, I64, P, P, P, I64, P, I32, I64, P]),
         "nvq_status_string": (ctypes.c_char_p, [I32]),
         "nvq_last_error": (ctypes.c_char_p, []),
     }
@@ -126,6 +127,17 @@ def hessian_accumulate(X, H=None, ws=None):
     _check("hessian_accumulate", lib.hessian_accumulate(_ptr(X), _dtype_code(X), n, k, ldx, _ptr(H), _ptr(ws),
                                                         need, _stream()))
     return H
+
+
+def nvfp4_gemm(X, codes, scales, g, out_dtype=torch.float32, Y=None):
+    """Y = X dequant(W)^T for bf16 activations X [T, k] and NVFP4 weights (codes [m, k/2], scales [m, k/16], g)."""
+    T, k, ldx = _rows(X, "X")
+    m = codes.shape[0]
+    if Y is None:
+        Y = torch.empty(T, m, dtype=out_dtype, device=X.device)
+    _check("nvfp4_gemm", lib.nvfp4_gemm(_ptr(X), _dtype_code(X), T, k, ldx, _ptr(codes), _ptr(scales), _ptr(g), m,
+                                        _ptr(Y), _dtype_code(Y), Y.stride(0), _stream()))
+    return Y
 
 
 _copy_streams = {}

@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libnvq.so")
-SOURCES = ["api.cpp", "gemm.hip", "syrk.hip", "factor.hip", "sweep.hip"]
+SOURCES = ["api.cpp", "gemm.hip", "syrk.hip", "factor.hip", "sweep.hip", "consumer.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

@@ -354,6 +354,23 @@ int hessian_accumulate_host(const void* X_host, int x_dtype, int64_t n, int64_t 
   return hip_status(e, fn);
 }
 
+// ---- consumer: NVFP4 weight-only GEMM ------------------------------------------
+int nvfp4_gemm(const void* X, int x_dtype, int64_t T, int64_t k, int64_t ldx, const uint8_t* codes,
+               const uint8_t* scales, const float* g, int64_t m, void* Y, int y_dtype, int64_t ldy, void* stream) {
+  const char* fn = "nvfp4_gemm";
+  if (x_dtype != NVQ_DTYPE_BF16) return failp(NVQ_ERR_DTYPE, fn, "x_dtype %d (activations must be bf16)", x_dtype);
+  if (!dtype_ok(y_dtype)) return failp(NVQ_ERR_DTYPE, fn, "y_dtype %d", y_dtype);
+  if (T < 0 || m < 0 || k <= 0 || k % 16 != 0 || ldx < k || ldx % 8 != 0 || ldy < m)
+    return failp(NVQ_ERR_SHAPE, fn, "T=%lld m=%lld k=%lld ldx=%lld ldy=%lld (need k%%16==0, ldx>=k, ldx%%8==0, ldy>=m)",
+                 (long long)T, (long long)m, (long long)k, (long long)ldx, (long long)ldy);
+  if (T == 0 || m == 0) return NVQ_OK;
+  if (!X || !codes || !scales || !g || !Y) return failp(NVQ_ERR_NULL, fn, "X, codes, scales, g and Y are required");
+  if (!aligned(X, 16)) return failp(NVQ_ERR_ALIGN, fn, "X must be 16-byte aligned");
+  if (!aligned(codes, 8)) return failp(NVQ_ERR_ALIGN, fn, "codes must be 8-byte aligned");
+  return hip_status(nvfp4_gemm_launch((const uint16_t*)X, T, k, ldx, codes, scales, g, m, Y,
+                                      y_dtype == NVQ_DTYPE_BF16, ldy, (hipStream_t)stream), fn);
+}
+
 size_t hessian_grouped_workspace_size(const int64_t* grp_off, int64_t G, int64_t k, int x_dtype) {
   if (!grp_off || G <= 0 || k <= 0 || !dtype_ok(x_dtype)) return 0;
   int64_t nmax = 0;
