@@ -305,9 +305,15 @@ int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* g
  *   codes, scales, g   the layer as written by gptq_nvfp4_quantize: codes
  *           [m x k/2] (8-byte aligned), scales [m x k/16], g 1 float (device).
  *   Y       device [T x ldy] of y_dtype (fp32 or bf16, RNE), ldy >= m.
+ *   ws      device workspace of nvfp4_gemm_workspace_size(T, k, m) bytes
+ *           (256-aligned; may be NULL when that is 0): for few tokens k is
+ *           split over workgroups and the fp32 partial sums are added in
+ *           split order, so results do not depend on timing.
  */
+size_t nvfp4_gemm_workspace_size(int64_t T, int64_t k, int64_t m);
 int nvfp4_gemm(const void* X, int x_dtype, int64_t T, int64_t k, int64_t ldx, const uint8_t* codes,
-               const uint8_t* scales, const float* g, int64_t m, void* Y, int y_dtype, int64_t ldy, void* stream);
+               const uint8_t* scales, const float* g, int64_t m, void* Y, int y_dtype, int64_t ldy, void* ws,
+               size_t ws_bytes, void* stream);
 
 /* Text of a status code; never NULL. */
 const char* nvq_status_string(int status);

@@ -32,7 +32,7 @@ EXPORTS = [
     "factor_hinv_workspace_size", "factor_hinv", "factor_hinv_batched",
     "nvfp4_global_scale_workspace_size", "nvfp4_global_scale",
     "gptq_nvfp4_workspace_size", "gptq_nvfp4_quantize", "gptq_nvfp4_quantize_batched",
-    "nvfp4_dequantize", "nvfp4_gemm", "nvq_status_string", "nvq_last_error",
+    "nvfp4_dequantize", "nvfp4_gemm_workspace_size", "nvfp4_gemm", "nvq_status_string", "nvq_last_error",
 ]
 
 
@@ -66,7 +66,8 @@ def _load():
         "gptq_nvfp4_workspace_size": (SZ, [I64, I64, U32]),
         "gptq_nvfp4_quantize": (I32, [P, I32, I64, I64, I64, P, P, P, I32, U32, P, P, P, P, P, SZ, P]),
         "nvfp4_dequantize": (I32, [P, P, P, I64, I64, P, I32, P]),
-        "nvfp4_gemm": (I32, [P, I32, I64, I64, I64, P, P, P, I64, P, I32, I64, P]),
+        "nvfp4_gemm_workspace_size": (SZ, [I64, I64, I64]),
+        "nvfp4_gemm": (I32, [P, I32, I64, I64, I64, P, P, P, I64, P, I32, I64, P, SZ, P]),
         "nvq_status_string": (ctypes.c_char_p, [I32]),
         "nvq_last_error": (ctypes.c_char_p, []),
     }
@@ -135,8 +136,10 @@ def nvfp4_gemm(X, codes, scales, g, out_dtype=torch.float32, Y=None):
     m = codes.shape[0]
     if Y is None:
         Y = torch.empty(T, m, dtype=out_dtype, device=X.device)
+    need = lib.nvfp4_gemm_workspace_size(T, k, m)
+    ws = _workspace(need, X.device) if need else None
     _check("nvfp4_gemm", lib.nvfp4_gemm(_ptr(X), _dtype_code(X), T, k, ldx, _ptr(codes), _ptr(scales), _ptr(g), m,
-                                        _ptr(Y), _dtype_code(Y), Y.stride(0), _stream()))
+                                        _ptr(Y), _dtype_code(Y), Y.stride(0), _ptr(ws), need, _stream()))
     return Y
 
 

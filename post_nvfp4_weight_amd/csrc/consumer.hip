@@ -13,6 +13,8 @@
 // steps of 64 (four NVFP4 blocks); both operands are kept [row][k] in LDS
 // (k contiguous, rows padded to 72 elements) and double-buffered; the next
 // step's loads are in flight while the current step is multiplied.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -34,12 +36,14 @@ __device__ __forceinline__ uint32_t dq_pair(uint32_t c2, float hs) {
   return p | ((c0 & 8) << 12) | ((c1 & 8) << 28);   // sign bits of the two bf16 halves
 }
 
-template <bool OUT_BF16>
+// OUT: 0 fp32 Y, 1 bf16 Y, 2 fp32 partial sums of k-split blockIdx.z (no g)
+// at P + z * T * m.  ksplit: k per split (a multiple of CK).
+template <int OUT>
 __global__ __launch_bounds__(256) void nvfp4_gemm_kernel(const uint16_t* __restrict__ X, int64_t T, int64_t k,
                                                          int64_t ldx, const uint8_t* __restrict__ codes,
                                                          const uint8_t* __restrict__ scales,
                                                          const float* __restrict__ gptr, int64_t m,
-                                                         void* __restrict__ Y, int64_t ldy) {
+                                                         void* __restrict__ Y, int64_t ldy, int64_t ksplit) {
   __shared__ __attribute__((aligned(16))) uint16_t smem[2 * CBUF];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1;
@@ -94,17 +98,18 @@ __global__ __launch_bounds__(256) void nvfp4_gemm_kernel(const uint16_t* __restr
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int64_t nsteps = (k + CK - 1) / CK;
+  const int64_t kbeg = (int64_t)blockIdx.z * ksplit, kend = min(k, kbeg + ksplit);
+  const int64_t nsteps = (kend - kbeg + CK - 1) / CK;
   u32x4 xv[4];
   u32x2 cv[2];
   uint32_t sv[2];
-  load(0, xv, cv, sv);
-  store(smem, 0, xv, cv, sv);
+  load(kbeg, xv, cv, sv);
+  store(smem, kbeg, xv, cv, sv);
   __syncthreads();
   const int arow = wr * 64 + (lane & 31), brow = wc * 64 + (lane & 31), koff = 8 * (lane >> 5);
   for (int64_t st = 0; st < nsteps; ++st) {
     const int cur = (int)(st & 1);
-    if (st + 1 < nsteps) load((st + 1) * CK, xv, cv, sv);
+    if (st + 1 < nsteps) load(kbeg + (st + 1) * CK, xv, cv, sv);
     const uint16_t* Xs = smem + cur * CBUF;
     const uint16_t* Qs = Xs + CT * CLD;
 #pragma unroll
@@ -120,12 +125,13 @@ __global__ __launch_bounds__(256) void nvfp4_gemm_kernel(const uint16_t* __restr
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
     }
-    if (st + 1 < nsteps) store(smem + (cur ^ 1) * CBUF, (st + 1) * CK, xv, cv, sv);
+    if (st + 1 < nsteps) store(smem + (cur ^ 1) * CBUF, kbeg + (st + 1) * CK, xv, cv, sv);
     __syncthreads();
   }
 
   // Accumulator layout: lane l, register r -> row 8 (r/4) + 4 (l/32) + r%4, column l%32.
-  const float g = *gptr;
+  const float g = OUT == 2 ? 1.0f : *gptr;
+  float* P = (float*)Y + (OUT == 2 ? (int64_t)blockIdx.z * T * m : 0);
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -136,23 +142,78 @@ __global__ __launch_bounds__(256) void nvfp4_gemm_kernel(const uint16_t* __restr
         const int64_t col = o0 + wc * 64 + j * 32 + (lane & 31);
         if (row < T && col < m) {
           const float v = acc[i][j][r] * g;
-          if (OUT_BF16) ((__bf16*)Y)[row * ldy + col] = (__bf16)v;
-          else ((float*)Y)[row * ldy + col] = v;
+          if (OUT == 1) ((__bf16*)Y)[row * ldy + col] = (__bf16)v;
+          else if (OUT == 0) ((float*)Y)[row * ldy + col] = v;
+          else P[row * m + col] = v;
         }
       }
 }
 
+// Y = g * (sum of the splits in split order).
+template <bool OUT_BF16>
+__global__ void nvfp4_gemm_reduce_kernel(const float* __restrict__ P, int nsplit, int64_t T, int64_t m,
+                                         const float* __restrict__ gptr, void* __restrict__ Y, int64_t ldy) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= T * m) return;
+  float s = 0.0f;
+  for (int z = 0; z < nsplit; ++z) s += P[(int64_t)z * T * m + e];
+  const float v = s * *gptr;
+  const int64_t row = e / m, col = e % m;
+  if (OUT_BF16) ((__bf16*)Y)[row * ldy + col] = (__bf16)v;
+  else ((float*)Y)[row * ldy + col] = v;
+}
+
+int num_cus_consumer() {
+  static int cus = 0;
+  if (!cus) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+  }
+  return cus;
+}
+
+// k splits so that the launch has about two workgroups per CU (at most 16,
+// and each split at least one k step).
+int nvfp4_gemm_splits(int64_t T, int64_t k, int64_t m) {
+  const int64_t tiles = ((m + CT - 1) / CT) * ((T + CT - 1) / CT);
+  const int64_t steps = (k + CK - 1) / CK;
+  int64_t sp = (2 * num_cus_consumer() + tiles - 1) / tiles;
+  sp = std::min<int64_t>(std::min<int64_t>(sp, 16), steps);
+  return (int)std::max<int64_t>(sp, 1);
+}
+
 }  // namespace
+
+size_t nvfp4_gemm_workspace(int64_t T, int64_t k, int64_t m) {
+  if (T <= 0 || m <= 0 || k <= 0) return 0;
+  const int sp = nvfp4_gemm_splits(T, k, m);
+  return sp > 1 ? (size_t)sp * T * m * sizeof(float) : 0;
+}
 
 hipError_t nvfp4_gemm_launch(const uint16_t* X, int64_t T, int64_t k, int64_t ldx, const uint8_t* codes,
                              const uint8_t* scales, const float* g, int64_t m, void* Y, int out_bf16, int64_t ldy,
-                             hipStream_t s) {
+                             float* ws, hipStream_t s) {
   if (T <= 0 || m <= 0) return hipSuccess;
-  dim3 grid((unsigned)((m + CT - 1) / CT), (unsigned)((T + CT - 1) / CT));
-  if (out_bf16)
-    hipLaunchKernelGGL(nvfp4_gemm_kernel<true>, grid, dim3(256), 0, s, X, T, k, ldx, codes, scales, g, m, Y, ldy);
-  else
-    hipLaunchKernelGGL(nvfp4_gemm_kernel<false>, grid, dim3(256), 0, s, X, T, k, ldx, codes, scales, g, m, Y, ldy);
+  const int sp = nvfp4_gemm_splits(T, k, m);
+  const int64_t steps = (k + CK - 1) / CK;
+  const int64_t ksplit = ((steps + sp - 1) / sp) * CK;
+  const int nz = (int)((k + ksplit - 1) / ksplit);
+  dim3 grid((unsigned)((m + CT - 1) / CT), (unsigned)((T + CT - 1) / CT), (unsigned)nz);
+  if (nz > 1) {
+    hipLaunchKernelGGL(nvfp4_gemm_kernel<2>, grid, dim3(256), 0, s, X, T, k, ldx, codes, scales, g, m, (void*)ws,
+                       ldy, ksplit);
+    const dim3 rg((unsigned)((T * m + 255) / 256));
+    if (out_bf16)
+      hipLaunchKernelGGL(nvfp4_gemm_reduce_kernel<true>, rg, dim3(256), 0, s, ws, nz, T, m, g, Y, ldy);
+    else
+      hipLaunchKernelGGL(nvfp4_gemm_reduce_kernel<false>, rg, dim3(256), 0, s, ws, nz, T, m, g, Y, ldy);
+  } else if (out_bf16) {
+    hipLaunchKernelGGL(nvfp4_gemm_kernel<1>, grid, dim3(256), 0, s, X, T, k, ldx, codes, scales, g, m, Y, ldy, ksplit);
+  } else {
+    hipLaunchKernelGGL(nvfp4_gemm_kernel<0>, grid, dim3(256), 0, s, X, T, k, ldx, codes, scales, g, m, Y, ldy, ksplit);
+  }
   return hipGetLastError();
 }
 

@@ -91,8 +91,10 @@ hipError_t fill_f32(float* p, int64_t n, float v, hipStream_t s);
 
 // NVFP4 weight-only GEMM: Y [T x m] = g (X Q^T), X bf16 [T x k] (row stride ldx),
 // Q = e2m1 * e4m3 from codes [m x k/2] and scales [m x k/16]; Y fp32 or bf16 (row stride ldy).
+// Small token counts split k over workspace partials (nvfp4_gemm_workspace bytes, 0 if unsplit).
+size_t nvfp4_gemm_workspace(int64_t T, int64_t k, int64_t m);
 hipError_t nvfp4_gemm_launch(const uint16_t* X, int64_t T, int64_t k, int64_t ldx, const uint8_t* codes,
                              const uint8_t* scales, const float* g, int64_t m, void* Y, int out_bf16, int64_t ldy,
-                             hipStream_t s);
+                             float* ws, hipStream_t s);
 
 }  // namespace nvq
