@@ -133,6 +133,42 @@ __device__ __forceinline__ double e2m1_dequant_f64(int code4, float s, float g) 
   return (code4 & 8) ? -v : v;
 }
 
+// ---- the same decisions with shorter dependency chains (the sweep's inner loop) ----
+// Whether a passes the midpoint between E4M3 codes i and i+1 (the binary
+// search's test above); never past the last code.
+// (Branch-free: i <= 126, and e4m3_value is defined on 127.)
+__device__ __forceinline__ bool e4m3_passes(float a, float g, int i) {
+  const float d = fmaf(-3.0f * (e4m3_value(i) + e4m3_value(i + 1)), g, a);
+  return i < kE4m3MaxCode && ((i & 1) ? d >= 0.0f : d > 0.0f);
+}
+__device__ __forceinline__ bool e4m3_passes(double a, float g, int i) {
+  const double thr = (double)(3.0f * (e4m3_value(i) + e4m3_value(i + 1))) * (double)g;
+  return i < kE4m3MaxCode && ((i & 1) ? a >= thr : a > thr);
+}
+// E4M3 code whose value is at or just below q >= 0, from q's bits (q may be
+// approximate or infinite; clamped to [0, 126]).
+__device__ __forceinline__ int e4m3_code_below(float q) {
+  int c;
+  if (q < 0x1p-6f) {
+    c = (int)(q * 512.0f);
+  } else {
+    const uint32_t u = __float_as_uint(q);
+    c = ((int)(u >> 23) - 120) * 8 + (int)((u >> 20) & 7);
+  }
+  return min(max(c, 0), kE4m3MaxCode);
+}
+// The code e4m3_code_of_ratio returns, located by an approximate quotient
+// (r6g ~ 1 / (6 g), a few ulps off): the grid floor of the exact quotient is
+// within one code of the approximate quotient's (grid steps are >= 1/16
+// relative), and the nearest code is that floor or the next one, so the true
+// code lies in [lo, lo + 3] for lo = below - 1.  Every midpoint under lo is
+// passed and none past lo + 2; the three in between are tested exactly.
+template <typename T>
+__device__ __forceinline__ int e4m3_code_of_ratio_fast(T a, float g, float r6g) {
+  const int lo = max(e4m3_code_below((float)a * r6g) - 1, 0);
+  return lo + (int)e4m3_passes(a, g, lo) + (int)e4m3_passes(a, g, lo + 1) + (int)e4m3_passes(a, g, lo + 2);
+}
+
 // First of the n_cand consecutive candidate codes around c0, inside [1, 126].
 __device__ __forceinline__ int candidate_lo(int c0, int n_cand) {
   int lo = c0 - (n_cand >> 1);

@@ -295,6 +295,7 @@ __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
   const int64_t row = (int64_t)blockIdx.x * ROWS + rl;
   const bool row_ok = row < m;
   const float g = *gptr;
+  const float r6g = 1.0f / (6.0f * g);   // only locates the candidate window's centre
 
   // Staging: Ut[c][r] = U[i1+r][i1+c] for r <= c < ncols (0 elsewhere), the
   // diagonal 16x16 blocks, 1/U_jj and the rows' slab of W'.  Every load is a
@@ -402,7 +403,7 @@ __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
     T score = F64 ? T(__builtin_inf()) : T(__builtin_inff());
     T rsc = 0;   // this candidate's replay score (its damped loss)
     if (a > T(0)) {
-      const int lo = candidate_lo(e4m3_code_of_ratio(a, g), n_cand);
+      const int lo = candidate_lo(e4m3_code_of_ratio_fast(a, g, r6g), n_cand);
       cand = lo + (ci < n_cand ? ci : 0);
       const float s = e4m3_value(cand);
       // Block-independent selection: the plain squared rounding error of the
