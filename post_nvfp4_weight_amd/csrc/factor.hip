@@ -59,16 +59,20 @@ __device__ __forceinline__ float row_bcast(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x150 + N, 0xF, 0xF, false));
 }
 
-// Cholesky factor of a 16 x 16 SPD block S held as columns: lane l (of each
-// row of 16 lanes, lf = l as a float) enters with c[i] = S[i][l] and leaves
-// with c[i] = the Schur-complemented column l, so that L[i][l] = c[i] *
-// rsv[l] for i >= l; rsv[j] = 1 / L[j][j] (the same in every lane).  Column
-// j comes to every lane by row broadcast; lanes l <= j, whose columns are
-// final, have their multiplier scaled by 0 (no per-lane comparisons).  A
-// non-positive pivot j is replaced by 1 and reported in bad (the first such
-// j), so the arithmetic stays finite.
+// Cholesky factor of a 16 x 16 SPD block S held as columns, and the inverse
+// of the factor: lane l (of each row of 16 lanes, lf = l as a float) enters
+// with c[i] = S[i][l] and x[i] = delta(i, l), and leaves with c[i] = the
+// Schur-complemented column l, so that L[i][l] = c[i] * rsv[l] for i >= l,
+// rsv[j] = 1 / L[j][j] (the same in every lane), and x = column l of L^-1.
+// Column j comes to every lane by row broadcast; lanes l <= j, whose columns
+// are final, have their multiplier scaled by 0 (no per-lane comparisons).
+// The same broadcast column gives L[i][j] = bc[i] * rsv[j], with which step j
+// finishes x[j] = x[j] / L[j][j] and removes its term from the later x[i]
+// (forward substitution by columns: the updates of one step are independent).
+// A non-positive pivot j is replaced by 1 and reported in bad (the first
+// such j), so the arithmetic stays finite.
 template <int J>
-__device__ __forceinline__ void chol16_step(float (&c)[16], float lf, float (&rsv)[16], int& bad) {
+__device__ __forceinline__ void chol16_step(float (&c)[16], float (&x)[16], float lf, float (&rsv)[16], int& bad) {
   float bc[16];
 #pragma unroll
   for (int i = J; i < 16; ++i) bc[i] = row_bcast<J>(c[i]);
@@ -81,10 +85,14 @@ __device__ __forceinline__ void chol16_step(float (&c)[16], float lf, float (&rs
   const float negm = -(c[J] * __builtin_amdgcn_rcpf(d)) * act;
 #pragma unroll
   for (int i = J + 1; i < 16; ++i) c[i] = fmaf(bc[i], negm, c[i]);
+  x[J] *= rsv[J];
+  const float t = -(x[J] * rsv[J]);   // -x[J] / L[J][J]
+#pragma unroll
+  for (int i = J + 1; i < 16; ++i) x[i] = fmaf(bc[i], t, x[i]);
 }
-__device__ __forceinline__ void chol16(float (&c)[16], float lf, float (&rsv)[16], int& bad) {
+__device__ __forceinline__ void chol16(float (&c)[16], float (&x)[16], float lf, float (&rsv)[16], int& bad) {
   [&]<int... J>(std::integer_sequence<int, J...>) {
-    (chol16_step<J>(c, lf, rsv, bad), ...);
+    (chol16_step<J>(c, x, lf, rsv, bad), ...);
   }(std::make_integer_sequence<int, 16>{});
 }
 
@@ -148,9 +156,13 @@ __global__ __launch_bounds__(256) void panel_kernel(float* __restrict__ A, int64
     const float lf = (float)lo;
     float c[16], rsv[16], x[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) c[i] = V[o + max(i, lo)][o + min(i, lo)];
+    for (int i = 0; i < 16; ++i) {
+      c[i] = V[o + max(i, lo)][o + min(i, lo)];
+      const float dl = lf - (float)i;
+      x[i] = fmaxf(fmaf(-dl, dl, 1.0f), 0.0f);   // delta(i, l)
+    }
     int bad = -1;
-    chol16(c, lf, rsv, bad);
+    chol16(c, x, lf, rsv, bad);
     if (bad >= 0 && first_bad == 0 && o + bad < nb) first_bad = (int)(p + o + bad + 1);
     // Lane l's scale 1 / L[l][l], through LDS (column 16 of Li is spare).
     if (lane == 0) {
@@ -162,16 +174,6 @@ __global__ __launch_bounds__(256) void panel_kernel(float* __restrict__ A, int64
     if (lane < 16) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) V[o + i][o + lane] = c[i] * rsl;
-    }
-    // Column l of L^-1 by forward substitution over L's rows in V (the same
-    // addresses in every lane): x[I] = (delta(I, l) - sum_{M<I} L[I][M] x[M]) / L[I][I].
-#pragma unroll
-    for (int I = 0; I < 16; ++I) {
-      const float dl = lf - (float)I;
-      float acc = fmaxf(fmaf(-dl, dl, 1.0f), 0.0f);   // delta(I, l)
-#pragma unroll
-      for (int M = 0; M < I; ++M) acc = fmaf(-V[o + I][o + M], x[M], acc);
-      x[I] = acc * rsv[I];
     }
     if (lane < 16) {
 #pragma unroll
