@@ -374,75 +374,162 @@ __global__ __launch_bounds__(256) void gemm_x6_kernel(GemmArgs p) {
   // all eight are in flight while the previous chunk is multiplied; masking,
   // alpha and the symmetric weights are applied when the chunk is stored.
   const int bk = (tid >> 5) * 4, bn = (tid & 31) * 4;
+  auto load_a = [&](int64_t k0, f32x4 (&ra)[4], int q) {
+    const int e = q * 256 + tid, r = e >> 3, kk = (e & 7) * 4;
+    ra[q] = *(const f32x4*)(A + min(m0 + r, p.M - 1) * p.lda + min(k0 + kk, p.K - 4));
+  };
+  auto load_b = [&](int64_t k0, f32x4 (&rb)[4], int i) {
+    rb[i] = *(const f32x4*)(B + min(k0 + bk + i, p.K - 1) * p.ldb + min(n0 + bn, p.N - 4));
+  };
   auto load_chunk = [&](int64_t k0, f32x4 (&ra)[4], f32x4 (&rb)[4]) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = q * 256 + tid, r = e >> 3, kk = (e & 7) * 4;
-      ra[q] = *(const f32x4*)(A + min(m0 + r, p.M - 1) * p.lda + min(k0 + kk, p.K - 4));
-    }
+    for (int q = 0; q < 4; ++q) load_a(k0, ra, q);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) rb[i] = *(const f32x4*)(B + min(k0 + bk + i, p.K - 1) * p.ldb + min(n0 + bn, p.N - 4));
+    for (int i = 0; i < 4; ++i) load_b(k0, rb, i);
   };
-  auto store_chunk = [&](uint16_t* buf, int64_t k0, const f32x4 (&ra)[4], const f32x4 (&rb)[4]) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = q * 256 + tid, r = e >> 3, kk = (e & 7) * 4;
-      const bool ok = m0 + r < p.M && k0 + kk < p.K;
+  // Piece idx of storing a loaded chunk into LDS as three bf16 parts:
+  // pieces 0..3 are A's row chunks q = idx, pieces 4..7 B's columns
+  // bn + idx - 4 (four k values each).  Indices fit in 32 bits.
+  const int sm0 = (int)m0, sn0 = (int)n0, sM = (int)p.M, sN = (int)p.N, sK = (int)p.K, snoff = (int)p.noff;
+  auto store_piece = [&](uint16_t* buf, int k0, const f32x4 (&ra)[4], const f32x4 (&rb)[4], int idx) {
+    if (idx < 4) {
+      const int q = idx, e = q * 256 + tid, r = e >> 3, kk = (e & 7) * 4;
+      const bool ok = sm0 + r < sM && k0 + kk < sK;
       put4(buf, r * X6_LD + kk, ok ? ra[q] * alpha_a : f32x4{0.f, 0.f, 0.f, 0.f});
+    } else {
+      const int j = idx - 4, gn = sn0 + bn;
+      f32x4 v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int gk = k0 + bk + i;
+        float x = (gk < sK && gn < sN) ? rb[i][j] : 0.0f;
+        if (sym) {
+          const int jg = snoff + gn + j;
+          x *= gk < jg ? 2.0f : (gk == jg ? 1.0f : 0.0f);
+        }
+        v[i] = x;
+      }
+      put4(buf + 3 * X6_PART, x6_boff(bn + j, bk), v);
     }
-    f32x4 v[4];
+  };
+  auto store_chunk = [&](uint16_t* buf, int k0, const f32x4 (&ra)[4], const f32x4 (&rb)[4]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t gk = k0 + bk + i, gn = n0 + bn;
-      v[i] = (gk < p.K && gn < p.N) ? rb[i] : f32x4{0.f, 0.f, 0.f, 0.f};
-      if (sym) {
+    for (int idx = 0; idx < 8; ++idx) store_piece(buf, k0, ra, rb, idx);
+  };
+  // Stage st (0..5) of piece idx, the same arithmetic as store_piece spread
+  // over six calls: the input, its high parts, the first residual, the
+  // middle parts (and the high store), the low parts, the last two stores.
+  auto store_stage = [&](uint16_t* buf, int k0, const f32x4 (&ra)[4], const f32x4 (&rb)[4], int idx, int st,
+                         f32x4& v, uint32_t& h0, uint32_t& h1, uint32_t& mm0, uint32_t& mm1, float (&r)[4]) {
+    uint16_t* base;
+    int off;
+    if (idx < 4) {
+      const int e = idx * 256 + tid;
+      base = buf; off = (e >> 3) * X6_LD + (e & 7) * 4;
+    } else {
+      base = buf + 3 * X6_PART; off = x6_boff(bn + idx - 4, bk);
+    }
+    if (st == 0) {
+      if (idx < 4) {
+        const int q = idx, e = q * 256 + tid, rr = e >> 3, kk = (e & 7) * 4;
+        const bool ok = sm0 + rr < sM && k0 + kk < sK;
+        v = ok ? ra[q] * alpha_a : f32x4{0.f, 0.f, 0.f, 0.f};
+      } else {
+        const int j = idx - 4, gn = sn0 + bn;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int64_t jg = p.noff + gn + u;
-          v[i][u] *= gk < jg ? 2.0f : (gk == jg ? 1.0f : 0.0f);
+        for (int i = 0; i < 4; ++i) {
+          const int gk = k0 + bk + i;
+          float x = (gk < sK && gn < sN) ? rb[i][j] : 0.0f;
+          if (sym) {
+            const int jg = snoff + gn + j;
+            x *= gk < jg ? 2.0f : (gk == jg ? 1.0f : 0.0f);
+          }
+          v[i] = x;
         }
       }
+    } else if (st == 1) {
+      h0 = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{v[0], v[1]}, bf16x2));
+      h1 = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{v[2], v[3]}, bf16x2));
+    } else if (st == 2) {
+      r[0] = v[0] - __uint_as_float(h0 << 16); r[1] = v[1] - __uint_as_float(h0 & 0xFFFF0000u);
+      r[2] = v[2] - __uint_as_float(h1 << 16); r[3] = v[3] - __uint_as_float(h1 & 0xFFFF0000u);
+    } else if (st == 3) {
+      mm0 = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{r[0], r[1]}, bf16x2));
+      mm1 = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{r[2], r[3]}, bf16x2));
+      *(u32x2*)(base + off) = u32x2{h0, h1};
+    } else if (st == 4) {
+      r[0] -= __uint_as_float(mm0 << 16); r[1] -= __uint_as_float(mm0 & 0xFFFF0000u);
+      r[2] -= __uint_as_float(mm1 << 16); r[3] -= __uint_as_float(mm1 & 0xFFFF0000u);
+      h0 = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{r[0], r[1]}, bf16x2));   // low parts
+      h1 = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{r[2], r[3]}, bf16x2));
+    } else {
+      *(u32x2*)(base + X6_PART + off) = u32x2{mm0, mm1};
+      *(u32x2*)(base + 2 * X6_PART + off) = u32x2{h0, h1};
     }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) put4(buf + 3 * X6_PART, x6_boff(bn + j, bk), f32x4{v[0][j], v[1][j], v[2][j], v[3][j]});
   };
 
-  f32x4 ra[4], rb[4];
-  if (c0 < nk) {
-    load_chunk(c0 * BK, ra, rb);
-    store_chunk(smem, c0 * BK, ra, rb);
-  }
+  // Two register sets of raw chunks: while chunk c is multiplied, chunk c+1
+  // (loaded two steps earlier) is split into the other LDS buffer, in eight
+  // pieces placed among the products, and then the loads of chunk c+3 take
+  // its registers.  Loads past the end read clamped addresses and stores past
+  // the end go to the idle buffer, so no step branches.
+  f32x4 ra0[4], rb0[4], ra1[4], rb1[4];
+  load_chunk(c0 * BK, ra0, rb0);
+  store_chunk(smem, (int)(c0 * BK), ra0, rb0);
+  load_chunk((c0 + 1) * BK, ra0, rb0);
+  load_chunk((c0 + 2) * BK, ra1, rb1);
   __syncthreads();
   // Lane l reads rows (l % 32) and k offset 8 (l / 32) of each 32-row block.
   const int arow = wr * WT + (lane & 31), brow = wc * WT + (lane & 31), koff = 8 * (lane >> 5);
   constexpr int PA[6] = {2, 1, 0, 1, 0, 0}, PB[6] = {0, 1, 2, 0, 1, 0};   // part products, smallest first
-  for (int64_t c = c0; c < nk; ++c) {
-    const int cur = (int)((c - c0) & 1);
-    if (c + 1 < nk) load_chunk((c + 1) * BK, ra, rb);
-    const uint16_t* As = smem + cur * X6_BUF;
+  static_assert(BK == 32, "two 16-deep k-steps per chunk");
+  // As (the buffer being multiplied) and nbuf (the idle one) are distinct,
+  // which the restrict qualifiers state: the stores into nbuf need not wait
+  // for the fragment reads from As.
+  auto body = [&](const uint16_t* __restrict__ As, uint16_t* __restrict__ nbuf, int64_t c, f32x4 (&ra)[4],
+                  f32x4 (&rb)[4]) {
     const uint16_t* Bs = As + 3 * X6_PART;
+    const int kn = (int)((c + 1) * BK);
+    bf16x8 a[2][3][2], b[2][3][2];   // [k-step][part][32-row block]
+    auto read = [&](int h, int f) {   // fragment f (0..11) of k-step h
+      const int pt = f >> 2, t = (f >> 1) & 1, ks = 16 * h;
+      if (f & 1) b[h][pt][t] = *(const bf16x8*)(Bs + pt * X6_PART + x6_boff(brow + 32 * t, ks + koff));
+      else a[h][pt][t] = *(const bf16x8*)(As + pt * X6_PART + (arow + 32 * t) * X6_LD + ks + koff);
+    };
 #pragma unroll
-    for (int ks = 0; ks < BK; ks += 16) {
-      bf16x8 a[3][2], b[3][2];
+    for (int f = 0; f < 12; ++f) read(0, f);
+    // Per k-step: 24 products (the four accumulators take turns, so that no
+    // MFMA waits for the one before it).  Behind each product comes one stage
+    // of the next chunk's store (6 stages for each of its 8 pieces, a few
+    // vector instructions each, which run while the MFMA does); the first
+    // k-step also reads the second one's fragments, and each load of chunk
+    // c+3 follows the stage that last reads the registers it fills (A's row
+    // chunk q: piece q's first stage; B's rows: piece 7's).
+    f32x4 sv;
+    uint32_t sh0, sh1, sm0_, sm1_;
+    float sr[4];
 #pragma unroll
-      for (int pt = 0; pt < 3; ++pt)
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          a[pt][t] = *(const bf16x8*)(As + pt * X6_PART + (arow + 32 * t) * X6_LD + ks + koff);
-          b[pt][t] = *(const bf16x8*)(Bs + pt * X6_PART + x6_boff(brow + 32 * t, ks + koff));
-        }
-      // The four accumulators take turns, so that no MFMA waits for the one
-      // before it.
-#pragma unroll
-      for (int pp = 0; pp < 6; ++pp)
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[PA[pp]][i], b[PB[pp]][j], acc[i][j], 0, 0, 0);
-    }
-    if (c + 1 < nk) store_chunk(smem + (cur ^ 1) * X6_BUF, (c + 1) * BK, ra, rb);
+      for (int m = 0; m < 24; ++m) {
+        const int pp = m >> 2, i = (m >> 1) & 1, j = m & 1;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[h][PA[pp]][i], b[h][PB[pp]][j], acc[i][j], 0, 0, 0);
+        if (h == 0 && m < 12) read(1, m);
+        const int g = 24 * h + m;
+        store_stage(nbuf, kn, ra, rb, g / 6, g % 6, sv, sh0, sh1, sm0_, sm1_, sr);
+        if (g % 6 == 1 && g < 24) load_a((c + 3) * BK, ra, g / 6);
+        if (g >= 43 && g < 47) load_b((c + 3) * BK, rb, g - 43);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  };
+  auto step = [&](int64_t c, f32x4 (&ra)[4], f32x4 (&rb)[4]) {
+    const int cur = (int)((c - c0) & 1);
+    body(smem + cur * X6_BUF, smem + (cur ^ 1) * X6_BUF, c, ra, rb);
     __syncthreads();
+  };
+  for (int64_t c = c0; c < nk; c += 2) {
+    step(c, ra0, rb0);
+    if (c + 1 < nk) step(c + 1, ra1, rb1);
   }
 
   if (EPI == kEpiAxpby) {
