@@ -600,13 +600,14 @@ hipError_t launch_t(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// 64-wide fp32 tiles when 128-wide ones would give fewer than two per CU (the
-// row-dot keeps 128: its partial sums are laid out per 128 columns);
-// otherwise the split-bf16 kernel for A [M][K] times B [K][N].
+// 64-wide fp32 tiles when 128-wide ones would give fewer than one per two CUs
+// (the row-dot keeps 128: its partial sums are laid out per 128 columns);
+// otherwise the split-bf16 kernel for A [M][K] times B [K][N].  Measured on
+// the 4096-column layer: the crossover between 1/4 and 1 tile per CU.
 template <bool TA, bool TB, bool LOWER, int EPI>
 hipError_t launch(const GemmArgs& a, hipStream_t s) {
   const int64_t tiles128 = ((a.N + 127) / 128) * ((a.M + 127) / 128) * a.batch;
-  if (EPI == kEpiAxpby && tiles128 < 2 * gemm_num_cus()) return launch_t<64, TA, TB, LOWER, EPI>(a, s);
+  if (EPI == kEpiAxpby && 2 * tiles128 < gemm_num_cus()) return launch_t<64, TA, TB, LOWER, EPI>(a, s);
   if (!TA && !TB && !LOWER) {
     dim3 grid((unsigned)((a.N + X6_T - 1) / X6_T), (unsigned)((a.M + X6_T - 1) / X6_T), (unsigned)a.batch);
     hipLaunchKernelGGL((gemm_x6_kernel<EPI>), grid, dim3(256), 0, s, a);
