@@ -20,6 +20,7 @@ namespace nvq {
 namespace {
 
 constexpr int NB = 64;
+constexpr int SW = 8 * NB;   // super-panel width of the trailing updates
 
 __global__ __launch_bounds__(256) void damping_kernel(const float* __restrict__ H, int64_t k, float damp_rel,
                                                       float* __restrict__ lam_ws, float* __restrict__ lam_out,
@@ -249,32 +250,38 @@ __global__ __launch_bounds__(256) void panel_kernel(float* __restrict__ A, int64
   }
 }
 
-// Trailing update after panel p: C -= P P^T on the lower triangle, where P
-// is the panel's L21 (rest x 64, at A + (p+64) k + p) and C the trailing
-// block (rest x rest, at A + (p+64)(k+1)).  One workgroup per 64 x 64 lower
+// Trailing update by the kw panel columns starting at column p: C -= P P^T
+// on the lower triangle, where P is those columns' L21 (rest x kw, at
+// A + (p+kw) k + p) and C the block right of and below them (rest x rest, at
+// A + (p+kw)(k+1)).  With lim < 0 every lower tile is updated; otherwise only
+// the tiles in the first lim 64-column blocks of C (grid lim x tiles; the
+// workgroups of tiles above the diagonal exit).  One workgroup per 64 x 64
 // tile; each wave holds a 32 x 32 quadrant in MFMA accumulators initialized
-// from C, and multiplies -P_i by P_j^T (v_mfma_f32_32x32x2f32, K = 64).
+// from C, and multiplies -P_i by P_j^T (v_mfma_f32_32x32x2f32) in chunks of
+// 64 columns, in column order, so that C is read and written once for all kw
+// columns and every element sees the same sums in the same order as kw / 64
+// separate updates.
 constexpr int UP = NB + 2;   // LDS row stride: a lane's (row, k) reads hit 64 distinct banks
 __global__ __launch_bounds__(256) void chol_update_kernel(float* __restrict__ A, int64_t k, int64_t p,
-                                                          int64_t rest) {
+                                                          int64_t rest, int kw, int lim) {
   __shared__ float Pi[NB][UP], Pj[NB][UP];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // Tile t -> (ti, tj), tj <= ti, row-major over the lower triangle of tiles.
   const int64_t t = blockIdx.x;
-  int64_t ti = (int64_t)((sqrt(8.0 * (double)t + 1.0) - 1.0) * 0.5);
-  while (ti * (ti + 1) / 2 > t) --ti;
-  while ((ti + 1) * (ti + 2) / 2 <= t) ++ti;
-  const int64_t tj = t - ti * (ti + 1) / 2;
-  const float* P = A + (p + NB) * k + p;
-  float* C = A + (p + NB) * k + p + NB;
-  // All panel loads in flight together (clamped rows), then the LDS writes.
-  f32x4 vi[4], vj[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = q * 256 + tid, r = e / (NB / 4), c4 = (e % (NB / 4)) * 4;
-    vi[q] = *(const f32x4*)(P + min(ti * NB + r, rest - 1) * k + c4);
-    vj[q] = *(const f32x4*)(P + min(tj * NB + r, rest - 1) * k + c4);
+  int64_t ti, tj;
+  if (lim < 0) {
+    // Tile t -> (ti, tj), tj <= ti, row-major over the lower triangle of tiles.
+    ti = (int64_t)((sqrt(8.0 * (double)t + 1.0) - 1.0) * 0.5);
+    while (ti * (ti + 1) / 2 > t) --ti;
+    while ((ti + 1) * (ti + 2) / 2 <= t) ++ti;
+    tj = t - ti * (ti + 1) / 2;
+  } else {
+    const int64_t nt = (rest + NB - 1) / NB;
+    tj = t / nt;
+    ti = t % nt;
+    if (ti < tj) return;
   }
+  const float* P = A + (p + kw) * k + p;
+  float* C = A + (p + kw) * k + p + kw;
   const int wr = wave >> 1, wc = wave & 1;
   const int64_t col = tj * NB + wc * 32 + (lane & 31);
   f32x16 acc;
@@ -283,30 +290,41 @@ __global__ __launch_bounds__(256) void chol_update_kernel(float* __restrict__ A,
     const int64_t row = ti * NB + wr * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
     acc[r] = (row < rest && col < rest && col <= row) ? C[row * k + col] : 0.0f;
   }
+  for (int kc = 0; kc < kw; kc += NB) {
+    // All panel loads in flight together (clamped rows), then the LDS writes.
+    f32x4 vi[4], vj[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = q * 256 + tid, r = e / (NB / 4), c4 = (e % (NB / 4)) * 4;
-    const bool oki = ti * NB + r < rest, okj = tj * NB + r < rest;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) { Pi[r][c4 + u] = oki ? -vi[q][u] : 0.0f; Pj[r][c4 + u] = okj ? vj[q][u] : 0.0f; }
-  }
-  __syncthreads();
-  const float* pa = &Pi[wr * 32 + (lane & 31)][lane >> 5];
-  const float* pb = &Pj[wc * 32 + (lane & 31)][lane >> 5];
-  // Operands of the next 16 k-values are read while the current 8 MFMAs run.
-  float a8[2][8], b8[2][8];
-#pragma unroll
-  for (int u = 0; u < 8; ++u) { a8[0][u] = pa[2 * u]; b8[0][u] = pb[2 * u]; }
-#pragma unroll
-  for (int h = 0; h < NB / 16; ++h) {
-    if (h + 1 < NB / 16) {
-#pragma unroll
-      for (int u = 0; u < 8; ++u) { a8[(h + 1) & 1][u] = pa[16 * (h + 1) + 2 * u]; b8[(h + 1) & 1][u] = pb[16 * (h + 1) + 2 * u]; }
+    for (int q = 0; q < 4; ++q) {
+      const int e = q * 256 + tid, r = e / (NB / 4), c4 = (e % (NB / 4)) * 4;
+      vi[q] = *(const f32x4*)(P + min(ti * NB + r, rest - 1) * k + kc + c4);
+      vj[q] = *(const f32x4*)(P + min(tj * NB + r, rest - 1) * k + kc + c4);
     }
-    __builtin_amdgcn_sched_barrier(0);
+    if (kc > 0) __syncthreads();   // every wave is done with the previous chunk
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a8[h & 1][u], b8[h & 1][u], acc, 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
+    for (int q = 0; q < 4; ++q) {
+      const int e = q * 256 + tid, r = e / (NB / 4), c4 = (e % (NB / 4)) * 4;
+      const bool oki = ti * NB + r < rest, okj = tj * NB + r < rest;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) { Pi[r][c4 + u] = oki ? -vi[q][u] : 0.0f; Pj[r][c4 + u] = okj ? vj[q][u] : 0.0f; }
+    }
+    __syncthreads();
+    const float* pa = &Pi[wr * 32 + (lane & 31)][lane >> 5];
+    const float* pb = &Pj[wc * 32 + (lane & 31)][lane >> 5];
+    // Operands of the next 16 k-values are read while the current 8 MFMAs run.
+    float a8[2][8], b8[2][8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) { a8[0][u] = pa[2 * u]; b8[0][u] = pb[2 * u]; }
+#pragma unroll
+    for (int h = 0; h < NB / 16; ++h) {
+      if (h + 1 < NB / 16) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) { a8[(h + 1) & 1][u] = pa[16 * (h + 1) + 2 * u]; b8[(h + 1) & 1][u] = pb[16 * (h + 1) + 2 * u]; }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a8[h & 1][u], b8[h & 1][u], acc, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
@@ -382,13 +400,26 @@ hipError_t factor_hinv_launch(const float* H, int64_t k, float damp_rel, float* 
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
+  // Panels are grouped in super-panels of SW columns.  After each panel only
+  // the rest of its super-panel is updated (the columns the next panels
+  // factor); the columns right of the super-panel take all of its panels in
+  // one update after its last panel, so they are read and written once per
+  // SW columns instead of once per panel.
   for (int64_t p = 0; p < k; p += NB) {
     const int64_t rest = k - p - NB;
     const unsigned groups = rest > 0 ? (unsigned)((rest + NB - 1) / NB) : 1u;
     hipLaunchKernelGGL(panel_kernel, dim3(groups), dim3(256), 0, s, A, k, p, info);
     if (rest <= 0) break;
-    const int64_t tiles = (rest + NB - 1) / NB;
-    hipLaunchKernelGGL(chol_update_kernel, dim3((unsigned)(tiles * (tiles + 1) / 2)), dim3(256), 0, s, A, k, p, rest);
+    const int64_t s0 = p / SW * SW, send = min(s0 + SW, k);
+    if (p + NB < send) {
+      const int64_t tiles = (rest + NB - 1) / NB, lim = (send - p - NB + NB - 1) / NB;
+      hipLaunchKernelGGL(chol_update_kernel, dim3((unsigned)(lim * tiles)), dim3(256), 0, s, A, k, p, rest, NB,
+                         (int)lim);
+    } else if (send < k) {
+      const int64_t rest2 = k - send, tiles = (rest2 + NB - 1) / NB;
+      hipLaunchKernelGGL(chol_update_kernel, dim3((unsigned)(tiles * (tiles + 1) / 2)), dim3(256), 0, s, A, k, s0,
+                         rest2, (int)(send - s0), -1);
+    }
   }
   hipLaunchKernelGGL(diag_inv_kernel, dim3((unsigned)((k + NB - 1) / NB)), dim3(64), 0, s, A, k, Linv);
   e = hipGetLastError();
