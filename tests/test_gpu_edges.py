@@ -121,10 +121,12 @@ def test_ragged_shapes_sweep(nvq, m, k, K):
     assert np.allclose(E_gpu, E_own, rtol=1e-4, atol=1e-6 * max(E_own.max(), 1e-30))
 
 
-def test_factor_ragged_last_panel(nvq):
-    # k = 208: the last 64-column panel holds 16 columns.
-    k = 208
-    X = synth.activations("small", 1500, k, bf16=False)
+@pytest.mark.parametrize("k", [208, 592, 1104])
+def test_factor_ragged_last_panel(nvq, k):
+    # The last 64-column panel holds 16 columns; 592 and 1104 also end in a
+    # partial 512-column super-panel after one or two full ones (each full
+    # one's columns to the right are updated once, by all its panels).
+    X = synth.activations("small", max(1500, 2 * k), k, bf16=False)
     H = gptq.hessian(X)
     U, lam, info = nvq.factor_hinv(_to_dev(H.astype(np.float32)))
     assert int(info.item()) == 0
