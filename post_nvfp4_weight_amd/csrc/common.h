@@ -168,6 +168,13 @@ __device__ __forceinline__ int e4m3_code_of_ratio_fast(T a, float g, float r6g) 
   const int lo = max(e4m3_code_below((float)a * r6g) - 1, 0);
   return lo + (int)e4m3_passes(a, g, lo) + (int)e4m3_passes(a, g, lo + 1) + (int)e4m3_passes(a, g, lo + 2);
 }
+// The quotient above is only that close while 1 / (6 g) is a finite normal
+// float; below this g (weights under ~1e-35) the binary search is used.
+constexpr float kFastRatioMinG = 0x1p-120f;
+template <typename T>
+__device__ __forceinline__ int e4m3_code_of_ratio_any(T a, float g, float r6g) {
+  return g >= kFastRatioMinG ? e4m3_code_of_ratio_fast(a, g, r6g) : e4m3_code_of_ratio(a, g);
+}
 
 // First of the n_cand consecutive candidate codes around c0, inside [1, 126].
 __device__ __forceinline__ int candidate_lo(int c0, int n_cand) {

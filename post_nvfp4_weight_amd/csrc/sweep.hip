@@ -26,15 +26,35 @@ __device__ __forceinline__ float load_w(const void* W, int64_t idx) {
 }
 
 // ---- global scale --------------------------------------------------------------
+// Rows are dealt to the workgroups in turn and each row's columns to the
+// threads; with vec (W 16-byte aligned, ldw and k multiples of 8 values) a
+// thread reads 8 consecutive values at a time.
 template <int BF16>
 __global__ __launch_bounds__(256) void amax_kernel(const void* __restrict__ W, int64_t m, int64_t k,
-                                                   int64_t ldw, float* __restrict__ partial) {
+                                                   int64_t ldw, float* __restrict__ partial, bool vec) {
   __shared__ float red[256];
   float a = 0.0f;
-  const int64_t total = m * k;
-  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
-    int64_t r = e / k, c = e % k;
-    a = fmaxf(a, fabsf(load_w<BF16>(W, r * ldw + c)));
+  for (int64_t r = blockIdx.x; r < m; r += gridDim.x) {
+    if (vec) {
+      for (int64_t c = (int64_t)threadIdx.x * 8; c < k; c += 256 * 8) {
+        if (BF16) {
+          const u32x4 u = *(const u32x4*)((const uint16_t*)W + r * ldw + c);
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            a = fmaxf(a, fmaxf(fabsf(__uint_as_float(u[q] << 16)), fabsf(__uint_as_float(u[q] & 0xFFFF0000u))));
+        } else {
+          const f32x4* src = (const f32x4*)((const float*)W + r * ldw + c);
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const f32x4 u = src[h];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) a = fmaxf(a, fabsf(u[q]));
+          }
+        }
+      }
+    } else {
+      for (int64_t c = threadIdx.x; c < k; c += 256) a = fmaxf(a, fabsf(load_w<BF16>(W, r * ldw + c)));
+    }
   }
   red[threadIdx.x] = a;
   __syncthreads();
@@ -70,58 +90,84 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
                                                       const uint8_t* __restrict__ scales,
                                                       const float* __restrict__ gptr, int64_t m, int64_t k,
                                                       void* __restrict__ out) {
-  const int64_t nblk = m * (k / kBlock);
-  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (b >= nblk) return;
+  // One thread per half block (8 weights: 4 bytes of codes, 16 bytes of bf16
+  // out), so that a wave's loads and stores are contiguous.
+  const int64_t nhalf = m * (k / kBlock) * 2;
+  const int64_t hb = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (hb >= nhalf) return;
   const float g = *gptr;
-  const float s = e4m3_value(scales[b] & 0x7F);
-  const bool neg_scale = scales[b] & 0x80;
-  u32x2 c = *(const u32x2*)(codes + b * 8);
-  float v[16];
+  const uint8_t sc = scales[hb >> 1];
+  const float s = e4m3_value(sc & 0x7F);
+  const bool neg_scale = sc & 0x80;
+  const uint32_t c = *(const uint32_t*)(codes + hb * 4);
+  float v[8];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    int code = (c[j >> 3] >> (4 * (j & 7))) & 0xF;
-    float x = e2m1_dequant(code, s, g);
+  for (int j = 0; j < 8; ++j) {
+    const float x = e2m1_dequant((int)((c >> (4 * j)) & 0xF), s, g);
     v[j] = neg_scale ? -x : x;
   }
   if (OUT_BF16) {
-    u32x4 o[2];
+    u32x4 o;
 #pragma unroll
-    for (int w = 0; w < 8; ++w)
-      o[w >> 2][w & 3] = (uint32_t)f32_to_bf16_bits(v[2 * w]) | ((uint32_t)f32_to_bf16_bits(v[2 * w + 1]) << 16);
-    u32x4* dst = (u32x4*)((uint16_t*)out + b * 16);
-    dst[0] = o[0];
-    dst[1] = o[1];
+    for (int w = 0; w < 4; ++w)
+      o[w] = (uint32_t)f32_to_bf16_bits(v[2 * w]) | ((uint32_t)f32_to_bf16_bits(v[2 * w + 1]) << 16);
+    *(u32x4*)((uint16_t*)out + hb * 8) = o;
   } else {
-    f32x4* dst = (f32x4*)((float*)out + b * 16);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) dst[q] = f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+    f32x4* dst = (f32x4*)((float*)out + hb * 8);
+    dst[0] = f32x4{v[0], v[1], v[2], v[3]};
+    dst[1] = f32x4{v[4], v[5], v[6], v[7]};
   }
 }
 
 // ---- round to nearest (no GPTQ updates) ------------------------------------------
 // One thread per (row, block).  Candidate scores are sum_j (w_j - q_j)^2 with
 // separately rounded products and sums in column order.
+// vec: every block starts 16-byte aligned (W aligned, ldw a multiple of 8
+// bf16 or 4 fp32 values), so it is read with 16-byte loads.
 template <int BF16>
 __global__ __launch_bounds__(256) void rtn_kernel(const void* __restrict__ W, int64_t m, int64_t k, int64_t ldw,
                                                   const float* __restrict__ gptr, int n_cand,
-                                                  uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+                                                  uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                  bool vec) {
   const int64_t nbk = k / kBlock;
   const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (b >= m * nbk) return;
   const int64_t row = b / nbk, blk = b % nbk;
   const float g = *gptr;
   float w[16];
+  const int64_t base = row * ldw + blk * 16;
+  if (vec) {
+    if (BF16) {
+      const u32x4* src = (const u32x4*)((const uint16_t*)W + base);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const u32x4 u = src[h];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          w[8 * h + 2 * q] = __uint_as_float(u[q] << 16);
+          w[8 * h + 2 * q + 1] = __uint_as_float(u[q] & 0xFFFF0000u);
+        }
+      }
+    } else {
+      const f32x4* src = (const f32x4*)((const float*)W + base);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 u = src[q];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) w[4 * q + t] = u[t];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) w[j] = load_w<BF16>(W, base + j);
+  }
   float a = 0.0f;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    w[j] = load_w<BF16>(W, row * ldw + blk * 16 + j);
-    a = fmaxf(a, fabsf(w[j]));
-  }
+  for (int j = 0; j < 16; ++j) a = fmaxf(a, fabsf(w[j]));
   int best_c = 0;
   uint32_t best_lo = 0, best_hi = 0;
   if (a > 0.0f) {
-    const int lo = candidate_lo(e4m3_code_of_ratio(a, g), n_cand);
+    const int lo = candidate_lo(e4m3_code_of_ratio_any(a, g, 1.0f / (6.0f * g)), n_cand);
     float best = __builtin_inff();
     for (int ci = 0; ci < n_cand; ++ci) {
       const int c = lo + ci;
@@ -403,7 +449,7 @@ __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
     T score = F64 ? T(__builtin_inf()) : T(__builtin_inff());
     T rsc = 0;   // this candidate's replay score (its damped loss)
     if (a > T(0)) {
-      const int lo = candidate_lo(e4m3_code_of_ratio_fast(a, g, r6g), n_cand);
+      const int lo = candidate_lo(e4m3_code_of_ratio_any(a, g, r6g), n_cand);
       cand = lo + (ci < n_cand ? ci : 0);
       const float s = e4m3_value(cand);
       // Block-independent selection: the plain squared rounding error of the
@@ -508,17 +554,19 @@ hipError_t sweep_launch_t(T* Wp, const float* U, const float* invd, const float*
 }  // namespace
 
 int global_scale_parts(int64_t m, int64_t k) {
-  int64_t blocks = (m * k + 256 * 16 - 1) / (256 * 16);
+  (void)k;
+  int64_t blocks = m;   // one or more rows per workgroup
   if (blocks > 1024) blocks = 1024;
   return (int)(blocks < 1 ? 1 : blocks);
 }
 
 hipError_t global_scale_launch(const void* W, int bf16, int64_t m, int64_t k, int64_t ldw, float* g,
                                float* partial, int nparts, hipStream_t s) {
+  const bool vec = ((uintptr_t)W % 16 == 0) && (ldw % 8 == 0) && (k % 8 == 0);
   if (bf16)
-    hipLaunchKernelGGL(amax_kernel<1>, dim3(nparts), dim3(256), 0, s, W, m, k, ldw, partial);
+    hipLaunchKernelGGL(amax_kernel<1>, dim3(nparts), dim3(256), 0, s, W, m, k, ldw, partial, vec);
   else
-    hipLaunchKernelGGL(amax_kernel<0>, dim3(nparts), dim3(256), 0, s, W, m, k, ldw, partial);
+    hipLaunchKernelGGL(amax_kernel<0>, dim3(nparts), dim3(256), 0, s, W, m, k, ldw, partial, vec);
   hipLaunchKernelGGL(gscale_finish_kernel, dim3(1), dim3(256), 0, s, partial, nparts, g);
   return hipGetLastError();
 }
@@ -527,7 +575,7 @@ hipError_t dequant_launch(const uint8_t* codes, const uint8_t* scales, const flo
                           void* out, int out_bf16, hipStream_t s) {
   int64_t nblk = m * (k / kBlock);
   if (nblk == 0) return hipSuccess;
-  dim3 grid((unsigned)((nblk + 255) / 256));
+  dim3 grid((unsigned)((2 * nblk + 255) / 256));
   if (out_bf16)
     hipLaunchKernelGGL(dequant_kernel<1>, grid, dim3(256), 0, s, codes, scales, g, m, k, out);
   else
@@ -539,10 +587,11 @@ hipError_t rtn_launch(const void* W, int bf16, int64_t m, int64_t k, int64_t ldw
                       uint8_t* codes, uint8_t* scales, float* row_loss, hipStream_t s) {
   int64_t nblk = m * (k / kBlock);
   dim3 grid((unsigned)((nblk + 255) / 256));
+  const bool vec = ((uintptr_t)W % 16 == 0) && (ldw % (bf16 ? 8 : 4) == 0);
   if (bf16)
-    hipLaunchKernelGGL(rtn_kernel<1>, grid, dim3(256), 0, s, W, m, k, ldw, g, n_cand, codes, scales);
+    hipLaunchKernelGGL(rtn_kernel<1>, grid, dim3(256), 0, s, W, m, k, ldw, g, n_cand, codes, scales, vec);
   else
-    hipLaunchKernelGGL(rtn_kernel<0>, grid, dim3(256), 0, s, W, m, k, ldw, g, n_cand, codes, scales);
+    hipLaunchKernelGGL(rtn_kernel<0>, grid, dim3(256), 0, s, W, m, k, ldw, g, n_cand, codes, scales, vec);
   if (row_loss) hipLaunchKernelGGL(fill_kernel, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, s, row_loss, m, 0.0f);
   return hipGetLastError();
 }

@@ -141,3 +141,36 @@ def test_factor_singular_without_damping_reports_order(nvq):
     H = gptq.hessian(X).astype(np.float32)
     _, _, info = nvq.factor_hinv(_to_dev(H), damp_rel=0.0)
     assert 0 < int(info.item()) <= k
+
+
+@pytest.mark.parametrize("scale", [1e-36, 1e12])
+def test_extreme_magnitudes_rtn_bit_exact(nvq, scale):
+    # Weights near 1e-36 give a subnormal global scale g (the candidate window
+    # is then found by the exact search rather than from 1 / (6 g), which
+    # overflows); weights near 1e12 give a large one.  Scales and codes must
+    # still match the oracle bit for bit.
+    W = synth.weights("attn_proj", 48, 256, 0.02, outlier_frac=0.01, bf16=False)
+    W = (W.astype(np.float64) * scale).astype(np.float32)
+    g = codec.global_scale(W)
+    ref = gptq.sweep(W, np.eye(256), g, 8, dtype=np.float32)
+    out = nvq.gptq_nvfp4_quantize(_to_dev(W), None, None, _to_dev(np.array([g], dtype=np.float32)), 8,
+                                  nvq.FLAG_RTN | nvq.FLAG_NO_ERR)
+    assert np.array_equal(out["scales"].cpu().numpy(), ref["scales"])
+    assert np.array_equal(out["codes"].cpu().numpy(), codec.pack_codes(ref["codes"]))
+
+
+def test_tiny_magnitudes_sweep(nvq):
+    # The GPTQ sweep with a subnormal global scale (weights near 1e-36).
+    m, k = 32, 256
+    W = synth.weights("attn_proj", m, k, 0.02, outlier_frac=0.01, bf16=False)
+    W = (W.astype(np.float64) * 1e-36).astype(np.float32)
+    X = synth.activations("attn_proj", 2048, k, massive=4)
+    H = gptq.hessian(X)
+    U, _ = gptq.hinv_factor(H)
+    g = codec.global_scale(W)
+    assert g < 2.0 ** -120
+    out = nvq.gptq_nvfp4_quantize(_to_dev(W), _to_dev(U.astype(np.float32)), _to_dev(H.astype(np.float32)),
+                                  _to_dev(np.array([g], dtype=np.float32)), 16, nvq.FLAG_NO_ERR)
+    ref = gptq.sweep(W, U.astype(np.float32), g, 16, dtype=np.float32)
+    assert _mismatch(codec.unpack_codes(out["codes"].cpu().numpy()), ref["codes"]) <= 1e-3
+    assert _mismatch(out["scales"].cpu().numpy(), ref["scales"]) <= 1e-3

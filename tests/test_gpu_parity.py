@@ -69,6 +69,21 @@ def test_global_scale_bit_exact(nvq, dtype):
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("m,k,pad", [(3000, 4096, 0), (7, 13, 3), (33, 40, 1), (2, 24, 8)])
+def test_global_scale_shapes_and_strides(nvq, dtype, m, k, pad):
+    # More rows than workgroups, k not a multiple of 8, and rows padded by
+    # pad values (odd strides take the element-wise path).  The maximum is
+    # planted in the last row's last column.
+    W = synth.weights("attn_proj", m, k, 0.02, outlier_frac=0.001, bf16=(dtype == torch.bfloat16))
+    W[m - 1, k - 1] = -4.0 * np.abs(W).max()
+    full = np.zeros((m, k + pad), dtype=np.float32)
+    full[:, :k] = W
+    Wd = _to_dev(full, dtype)[:, :k]
+    g = nvq.nvfp4_global_scale(Wd).item()
+    assert np.float32(g) == codec.global_scale(W)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_rtn_one_candidate_bit_exact(nvq, dtype):
     W = synth.weights("attn_proj", 96, 512, 0.02, outlier_frac=0.01, bf16=(dtype == torch.bfloat16))
     W[5, 32:48] = 0.0
