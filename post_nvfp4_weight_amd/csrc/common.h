@@ -133,6 +133,16 @@ __device__ __forceinline__ double e2m1_dequant_f64(int code4, float s, float g) 
   return (code4 & 8) ? -v : v;
 }
 
+// Workgroup barrier for LDS double buffering: waits for this wave's LDS
+// (and scalar) operations only, then joins the barrier, so every wave's LDS
+// writes before it are visible to every wave after it, while global loads
+// issued ahead stay in flight (__syncthreads would wait for those too).  The
+// memory clobber keeps the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt 63 and expcnt 7 (no wait)
+  asm volatile("s_barrier" ::: "memory");
+}
+
 // ---- the same decisions with shorter dependency chains (the sweep's inner loop) ----
 // Whether a passes the midpoint between E4M3 codes i and i+1 (the binary
 // search's test above); never past the last code.

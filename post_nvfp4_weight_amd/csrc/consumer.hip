@@ -28,12 +28,30 @@ constexpr int CBUF = 2 * CT * CLD;   // bf16 elements of one buffer: X tile, the
 typedef float f32x2c __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2c __attribute__((ext_vector_type(2)));
 
-// Two codes (low nibble first) under block scale value s -> packed bf16 pair of e2m1 * s.
-__device__ __forceinline__ uint32_t dq_pair(uint32_t c2, float hs) {
-  const uint32_t c0 = c2 & 0xF, c1 = (c2 >> 4) & 0xF;
-  const float m0 = e2m1_twice_mag((int)(c0 & 7)) * hs, m1 = e2m1_twice_mag((int)(c1 & 7)) * hs;
-  const uint32_t p = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2c{m0, m1}, bf16x2c));
-  return p | ((c0 & 8) << 12) | ((c1 & 8) << 28);   // sign bits of the two bf16 halves
+// Byte B of word (two codes, low nibble first) under block scale value s ->
+// packed bf16 pair of e2m1 * s.  The E2M1 decode is the hardware's FP4
+// conversion at scale 1 (its scale operand applies only a power of two, so
+// the E4M3 scale is multiplied in fp32; the product has at most 6
+// significant bits and is exact, as is its bf16 conversion).
+// E4M3 value of code c (0..126) without branches: (m + 8 min(e, 1)) 2^(max(e, 1) - 10)
+// for c = 8 e + m, which is m 2^-9 for e = 0 and (1 + m/8) 2^(e-7) otherwise.
+__device__ __forceinline__ float scale_value(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15, m = c & 7;
+  return (float)(m + 8 * min(e, 1u)) * __uint_as_float((max(e, 1u) + 117) << 23);
+}
+
+template <int B>
+__device__ __forceinline__ uint32_t dq_byte(uint32_t word, float s) {
+  const f32x2c v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, B);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2c{v.x * s, v.y * s}, bf16x2c));
+}
+__device__ __forceinline__ uint32_t dq_byte(uint32_t word, float s, int b) {   // b known after unrolling
+  switch (b) {
+    case 0: return dq_byte<0>(word, s);
+    case 1: return dq_byte<1>(word, s);
+    case 2: return dq_byte<2>(word, s);
+    default: return dq_byte<3>(word, s);
+  }
 }
 
 // OUT: 0 fp32 Y, 1 bf16 Y, 2 fp32 partial sums of k-split blockIdx.z (no g)
@@ -78,12 +96,13 @@ __global__ __launch_bounds__(256) void nvfp4_gemm_kernel(const uint16_t* __restr
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
       const bool ok = o0 + wrow < m && k0 + 32 * wh + 16 * b < k;
-      const float hs = 0.5f * e4m3_value((int)(sv[b] & 0x7F));
+      const float sb = scale_value(sv[b] & 0x7F);
+      const uint32_t keep = ok ? ~0u : 0u;   // a mask, so that nothing branches
       u32x4 lo, hi;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        lo[j] = ok ? dq_pair((cv[b][0] >> (8 * j)) & 0xFF, hs) : 0u;
-        hi[j] = ok ? dq_pair((cv[b][1] >> (8 * j)) & 0xFF, hs) : 0u;
+        lo[j] = dq_byte(cv[b][0], sb, j) & keep;
+        hi[j] = dq_byte(cv[b][1], sb, j) & keep;
       }
       *(u32x4*)(qb + wrow * CLD + 32 * wh + 16 * b) = lo;
       *(u32x4*)(qb + wrow * CLD + 32 * wh + 16 * b + 8) = hi;
@@ -163,6 +182,152 @@ __global__ void nvfp4_gemm_reduce_kernel(const float* __restrict__ P, int nsplit
   else ((float*)Y)[row * ldy + col] = v;
 }
 
+// ---- many tokens: 256 x 256 tiles ----------------------------------------------
+// 256 (tokens) x 256 (output channels) per workgroup, four waves of 128 x 128
+// (16 accumulators of 32 x 32), k in steps of 32.  A wave reads 8 operand
+// fragments per 16 products, half the LDS reads per product of the 64 x 64
+// wave tiles above.  While a step is multiplied, the next one (loaded two
+// steps earlier into one of two register sets) is stored into the other LDS
+// buffer in small pieces placed between the products (codes expanded to
+// bf16 on the way), and the loads of the step after it are issued.
+constexpr int BT = 256, BK = 32, BLD = BK + 8;
+constexpr int BBUF = 2 * BT * BLD;   // bf16 elements of one buffer: X tile, then Q tile
+
+template <int OUT>   // 0 fp32 Y, 1 bf16 Y
+__global__ __launch_bounds__(256) void nvfp4_gemm_big_kernel(const uint16_t* __restrict__ X, int64_t T, int64_t k,
+                                                             int64_t ldx, const uint8_t* __restrict__ codes,
+                                                             const uint8_t* __restrict__ scales,
+                                                             const float* __restrict__ gptr, int64_t m,
+                                                             void* __restrict__ Y, int64_t ldy) {
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * BBUF];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+  const int64_t t0 = (int64_t)blockIdx.y * BT, o0 = (int64_t)blockIdx.x * BT;
+  const int64_t kb = k / 16;
+  const int64_t nsteps = (k + BK - 1) / BK;
+
+  // Per step and thread: 4 x 16 bytes of X (row (q*256 + tid) / 4, 8 values
+  // at ((q*256 + tid) % 4) * 8) and the two blocks of codes and scales of
+  // weight row tid.  Addresses are clamped, so that every load is valid.
+  // The four X rows share the column offset c8; row pointers are formed once.
+  const int c8 = (tid & 3) * 8;
+  const uint16_t* xrow[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) xrow[q] = X + min(t0 + ((q * 256 + tid) >> 2), T - 1) * ldx + c8;
+  const int64_t wrow = min(o0 + tid, m - 1);
+  const uint8_t* crow = codes + wrow * (k / 2);
+  const uint8_t* srow = scales + wrow * kb;
+  const int kx = (int)(k - 8 - c8), kb1 = (int)(kb - 1);
+  auto load = [&](int64_t k0, u32x4 (&xv)[4], u32x2 (&cv)[2], uint32_t (&sv)[2]) {
+    const int k0i = (int)k0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) xv[q] = *(const u32x4*)(xrow[q] + min(k0i, kx));
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int blk = min(k0i / 16 + b, kb1);
+      cv[b] = *(const u32x2*)(crow + blk * 8);
+      sv[b] = srow[blk];
+    }
+  };
+  // Piece p (0..11) of storing a loaded step into buf: 0..3 the X chunks q,
+  // 4..11 the weight row's 8-code halves (block (p-4)/4... two halves per
+  // block, each two calls: the first expands 4 codes, the second 4 more and
+  // stores the 16 bytes).
+  auto store_piece = [&](uint16_t* buf, int64_t k0, const u32x4 (&xv)[4], const u32x2 (&cv)[2],
+                         const uint32_t (&sv)[2], int p, u32x4& qv) {
+    if (p < 4) {
+      const int r = (p * 256 + tid) >> 2;
+      const bool ok = t0 + r < T && k0 + c8 < k;
+      *(u32x4*)(buf + r * BLD + c8) = ok ? xv[p] : u32x4{0u, 0u, 0u, 0u};
+    } else {
+      const int u = p - 4, b = u >> 2, h = (u >> 1) & 1, part = u & 1;
+      const bool ok = o0 + tid < m && k0 + 16 * b < k;
+      const float sb = scale_value(sv[b] & 0x7F);
+      const uint32_t keep = ok ? ~0u : 0u;   // a mask, so that nothing branches
+      const uint32_t word = cv[b][h];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int jj = 2 * part + j;
+        qv[jj] = dq_byte(word, sb, jj) & keep;
+      }
+      if (part == 1) *(u32x4*)(buf + BT * BLD + tid * BLD + 16 * b + 8 * h) = qv;
+    }
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  u32x4 xv0[4], xv1[4], qv;
+  u32x2 cv0[2], cv1[2];
+  uint32_t sv0[2], sv1[2];
+  load(0, xv0, cv0, sv0);
+#pragma unroll
+  for (int p = 0; p < 12; ++p) store_piece(smem, 0, xv0, cv0, sv0, p, qv);
+  load(BK, xv0, cv0, sv0);
+  load(2 * BK, xv1, cv1, sv1);
+  __syncthreads();
+
+  const int arow = wr * 128 + (lane & 31), brow = wc * 128 + (lane & 31), koff = 8 * (lane >> 5);
+  auto body = [&](const uint16_t* __restrict__ Xs, uint16_t* __restrict__ nbuf, int64_t st, u32x4 (&xv)[4],
+                  u32x2 (&cv)[2], uint32_t (&sv)[2]) {
+    const uint16_t* Qs = Xs + BT * BLD;
+    const int64_t kn = (st + 1) * BK;
+    bf16x8 a[2][4], b[2][4];
+    auto read = [&](int h, int f) {
+      if (f < 4) a[h][f] = *(const bf16x8*)(Xs + (arow + 32 * f) * BLD + 16 * h + koff);
+      else b[h][f - 4] = *(const bf16x8*)(Qs + (brow + 32 * (f - 4)) * BLD + 16 * h + koff);
+    };
+#pragma unroll
+    for (int f = 0; f < 8; ++f) read(0, f);
+    // 32 products per step (two k-steps of 16); behind product g: the second
+    // k-step's fragment g (g < 8), store piece g - 4 (4 <= g < 16) and, once
+    // the register set's last reader has run, the loads of step st+3 into it
+    // (g == 20).
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int mm = 0; mm < 16; ++mm) {
+        const int g = 16 * h + mm, i = mm >> 2, j = mm & 3;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[h][i], b[h][j], acc[i][j], 0, 0, 0);
+        if (g < 8) read(1, g);
+        if (g >= 4 && g < 16) store_piece(nbuf, kn, xv, cv, sv, g - 4, qv);
+        if (g == 20) load((st + 3) * BK, xv, cv, sv);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+  };
+  // Steps go in pairs with no branch between them (a join would make the
+  // compiler copy the accumulators): with an odd step count the last pair's
+  // second step multiplies the zeros stored for the step past the end.
+  for (int64_t st = 0; st < nsteps; st += 2) {
+    body(smem + 0, smem + BBUF, st, xv0, cv0, sv0);
+    lds_barrier();
+    body(smem + BBUF, smem + 0, st + 1, xv1, cv1, sv1);
+    lds_barrier();
+  }
+
+  // Accumulator layout: lane l, register r -> row 8 (r/4) + 4 (l/32) + r%4, column l%32.
+  const float g = *gptr;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = t0 + wr * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int64_t col = o0 + wc * 128 + j * 32 + (lane & 31);
+        if (row < T && col < m) {
+          const float v = acc[i][j][r] * g;
+          if (OUT == 1) ((__bf16*)Y)[row * ldy + col] = (__bf16)v;
+          else ((float*)Y)[row * ldy + col] = v;
+        }
+      }
+}
+
 int num_cus_consumer() {
   static int cus = 0;
   if (!cus) {
@@ -196,6 +361,15 @@ hipError_t nvfp4_gemm_launch(const uint16_t* X, int64_t T, int64_t k, int64_t ld
                              const uint8_t* scales, const float* g, int64_t m, void* Y, int out_bf16, int64_t ldy,
                              float* ws, hipStream_t s) {
   if (T <= 0 || m <= 0) return hipSuccess;
+  if (((T + BT - 1) / BT) * ((m + BT - 1) / BT) >= num_cus_consumer()) {
+    // Enough 256 x 256 tiles for every CU: the large-tile kernel, no k split.
+    dim3 grid((unsigned)((m + BT - 1) / BT), (unsigned)((T + BT - 1) / BT));
+    if (out_bf16)
+      hipLaunchKernelGGL(nvfp4_gemm_big_kernel<1>, grid, dim3(256), 0, s, X, T, k, ldx, codes, scales, g, m, Y, ldy);
+    else
+      hipLaunchKernelGGL(nvfp4_gemm_big_kernel<0>, grid, dim3(256), 0, s, X, T, k, ldx, codes, scales, g, m, Y, ldy);
+    return hipGetLastError();
+  }
   const int sp = nvfp4_gemm_splits(T, k, m);
   const int64_t steps = (k + CK - 1) / CK;
   const int64_t ksplit = ((steps + sp - 1) / sp) * CK;

@@ -525,7 +525,7 @@ __global__ __launch_bounds__(256) void gemm_x6_kernel(GemmArgs p) {
   auto step = [&](int64_t c, f32x4 (&ra)[4], f32x4 (&rb)[4]) {
     const int cur = (int)((c - c0) & 1);
     body(smem + cur * X6_BUF, smem + (cur ^ 1) * X6_BUF, c, ra, rb);
-    __syncthreads();
+    lds_barrier();
   };
   for (int64_t c = c0; c < nk; c += 2) {
     step(c, ra0, rb0);

@@ -39,7 +39,11 @@ def _layer(m, k, T, seed):
     return X, packed, scales, g
 
 
-@pytest.mark.parametrize("T,m,k", [(1, 64, 16), (37, 100, 48), (300, 256, 1024), (129, 130, 2064), (512, 512, 4096)])
+# The last two cases have a 256 x 256 tile per CU and take the many-token
+# kernel: one aligned, one ragged in T and m with an odd number of 32-deep k
+# steps (k = 528).
+@pytest.mark.parametrize("T,m,k", [(1, 64, 16), (37, 100, 48), (300, 256, 1024), (129, 130, 2064), (512, 512, 4096),
+                                   (4096, 4096, 512), (4000, 4100, 528)])
 def test_gemm_matches_oracle(nvq, T, m, k):
     X, packed, scales, g = _layer(m, k, T, seed=T)
     Xd = synth.to_bf16_tensor(X).to(DEV)
@@ -73,5 +77,18 @@ def test_gemm_after_library_quantization(nvq):
     X = Xc[:T]
     Y = nvq.nvfp4_gemm(synth.to_bf16_tensor(X).to(DEV), res["codes"], res["scales"], res["g"]).cpu().numpy()
     packed, scales, g = res["codes"].cpu().numpy(), res["scales"].cpu().numpy(), np.float32(res["g"].item())
+    ref = consumer.weight_only_matmul(X, packed, scales, g)
+    assert np.all(np.abs(Y - ref) <= _bound(X, packed, scales, g) + 1e-30)
+
+
+def test_gemm_many_tokens_strided(nvq):
+    # The many-token kernel with activation rows padded (ldx > k).
+    T, m, k = 4096, 4096, 256
+    X, packed, scales, g = _layer(m, k, T, seed=11)
+    wide = torch.zeros(T, k + 40, dtype=torch.bfloat16)
+    wide[:, :k] = synth.to_bf16_tensor(X)
+    Xd = wide.to(DEV)[:, :k]
+    Y = nvq.nvfp4_gemm(Xd, torch.from_numpy(packed).to(DEV), torch.from_numpy(scales).to(DEV),
+                       torch.tensor([g], dtype=torch.float32, device=DEV)).cpu().numpy()
     ref = consumer.weight_only_matmul(X, packed, scales, g)
     assert np.all(np.abs(Y - ref) <= _bound(X, packed, scales, g) + 1e-30)
