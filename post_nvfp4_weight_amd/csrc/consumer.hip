@@ -184,14 +184,22 @@ __global__ void nvfp4_gemm_reduce_kernel(const float* __restrict__ P, int nsplit
 
 // ---- many tokens: 256 x 256 tiles ----------------------------------------------
 // 256 (tokens) x 256 (output channels) per workgroup, four waves of 128 x 128
-// (16 accumulators of 32 x 32), k in steps of 32.  A wave reads 8 operand
-// fragments per 16 products, half the LDS reads per product of the 64 x 64
-// wave tiles above.  While a step is multiplied, the next one (loaded two
-// steps earlier into one of two register sets) is stored into the other LDS
-// buffer in small pieces placed between the products (codes expanded to
-// bf16 on the way), and the loads of the step after it are issued.
+// (16 accumulators of 32 x 32), k in steps of 32 (k a multiple of 32).  A wave
+// reads 8 operand fragments per 16 products, half the LDS reads per product
+// of the 64 x 64 wave tiles above.
+//
+// X goes to LDS by direct-to-LDS buffer loads, issued two steps ahead into a
+// ring of three X buffers: 256 rows of 64 bytes, 16-byte chunks XOR-swizzled
+// by (row / 2) % 4, so that the 8 lanes of each fragment-read group hit
+// distinct banks.  Rows past T read as zeros (the buffer bound).  The codes
+// and scales of a step are loaded into registers three steps ahead (two
+// register sets) and expanded to bf16 into one of two Q buffers, in small
+// pieces placed between the products.
 constexpr int BT = 256, BK = 32, BLD = BK + 8;
-constexpr int BBUF = 2 * BT * BLD;   // bf16 elements of one buffer: X tile, then Q tile
+constexpr int BXBUF = BT * BK;     // bf16 elements of one X buffer (64-byte rows, no padding)
+constexpr int BQBUF = BT * BLD;    // bf16 elements of one Q buffer (rows padded to 80 bytes)
+
+__device__ __forceinline__ int bswz(int row, int c) { return c ^ ((row >> 1) & 3); }
 
 template <int OUT>   // 0 fp32 Y, 1 bf16 Y
 __global__ __launch_bounds__(256) void nvfp4_gemm_big_kernel(const uint16_t* __restrict__ X, int64_t T, int64_t k,
@@ -199,59 +207,66 @@ __global__ __launch_bounds__(256) void nvfp4_gemm_big_kernel(const uint16_t* __r
                                                              const uint8_t* __restrict__ scales,
                                                              const float* __restrict__ gptr, int64_t m,
                                                              void* __restrict__ Y, int64_t ldy) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * BBUF];
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[3 * BXBUF + 2 * BQBUF];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1;
   const int64_t t0 = (int64_t)blockIdx.y * BT, o0 = (int64_t)blockIdx.x * BT;
   const int64_t kb = k / 16;
-  const int64_t nsteps = (k + BK - 1) / BK;
+  const int64_t nsteps = k / BK;
+  uint16_t* const xbuf = smem;
+  uint16_t* const qbuf = smem + 3 * BXBUF;
 
-  // Per step and thread: 4 x 16 bytes of X (row (q*256 + tid) / 4, 8 values
-  // at ((q*256 + tid) % 4) * 8) and the two blocks of codes and scales of
-  // weight row tid.  Addresses are clamped, so that every load is valid.
-  // The four X rows share the column offset c8; row pointers are formed once.
-  const int c8 = (tid & 3) * 8;
-  const uint16_t* xrow[4];
+  // Direct-to-LDS loads: this wave's instruction q fills bytes [1024 i, 1024 (i+1))
+  // of an X buffer, i = wave + 4 q: rows 16 i + lane / 4, physical chunk lane % 4.
+  uint32_t voff[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) xrow[q] = X + min(t0 + ((q * 256 + tid) >> 2), T - 1) * ldx + c8;
+  for (int q = 0; q < 4; ++q) {
+    const int i = wave + 4 * q, row = 16 * i + (lane >> 2);
+    voff[q] = (uint32_t)(row * ldx * 2 + bswz(row, lane & 3) * 16);
+  }
+  const int64_t rows_left = T - t0;
+  auto issue_x = [&](int64_t st) {   // step st into its ring buffer; zero-length past the end
+#if __HIP_DEVICE_COMPILE__
+    const int64_t kk = st < nsteps ? st * BK : 0;
+    const int nrec = st < nsteps ? (int)min(rows_left * ldx * 2 - kk * 2, (int64_t)0x7FFFFFF0) : 0;
+    __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(X + t0 * ldx + kk), (short)0, nrec, 0x00020000);
+    char* dst = (char*)(xbuf + ((int)st % 3) * BXBUF);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(dst + (wave + 4 * q) * 1024),
+                                               16, voff[q], 0, 0, 0);
+#endif
+  };
+
+  // Codes and scales of weight row tid: two blocks per step (clamped, so
+  // that every load is valid).
   const int64_t wrow = min(o0 + tid, m - 1);
   const uint8_t* crow = codes + wrow * (k / 2);
   const uint8_t* srow = scales + wrow * kb;
-  const int kx = (int)(k - 8 - c8), kb1 = (int)(kb - 1);
-  auto load = [&](int64_t k0, u32x4 (&xv)[4], u32x2 (&cv)[2], uint32_t (&sv)[2]) {
-    const int k0i = (int)k0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) xv[q] = *(const u32x4*)(xrow[q] + min(k0i, kx));
+  const int kb1 = (int)(kb - 1);
+  auto load_q = [&](int64_t st, u32x2 (&cv)[2], uint32_t (&sv)[2]) {
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      const int blk = min(k0i / 16 + b, kb1);
+      const int blk = min((int)(st * 2) + b, kb1);
       cv[b] = *(const u32x2*)(crow + blk * 8);
       sv[b] = srow[blk];
     }
   };
-  // Piece p (0..11) of storing a loaded step into buf: 0..3 the X chunks q,
-  // 4..11 the weight row's 8-code halves (block (p-4)/4... two halves per
-  // block, each two calls: the first expands 4 codes, the second 4 more and
-  // stores the 16 bytes).
-  auto store_piece = [&](uint16_t* buf, int64_t k0, const u32x4 (&xv)[4], const u32x2 (&cv)[2],
-                         const uint32_t (&sv)[2], int p, u32x4& qv) {
-    if (p < 4) {
-      const int r = (p * 256 + tid) >> 2;
-      const bool ok = t0 + r < T && k0 + c8 < k;
-      *(u32x4*)(buf + r * BLD + c8) = ok ? xv[p] : u32x4{0u, 0u, 0u, 0u};
-    } else {
-      const int u = p - 4, b = u >> 2, h = (u >> 1) & 1, part = u & 1;
-      const bool ok = o0 + tid < m && k0 + 16 * b < k;
-      const float sb = scale_value(sv[b] & 0x7F);
-      const uint32_t keep = ok ? ~0u : 0u;   // a mask, so that nothing branches
-      const uint32_t word = cv[b][h];
+  // Piece p (0..7) of expanding step st's codes into Q buffer buf: block p / 4,
+  // 8-code half (p / 2) % 2; the first piece of a half expands 4 codes, the
+  // second 4 more and stores the 16 bytes.
+  auto q_piece = [&](uint16_t* buf, int64_t st, const u32x2 (&cv)[2], const uint32_t (&sv)[2], int p, u32x4& qv) {
+    const int b = p >> 2, h = (p >> 1) & 1, part = p & 1;
+    const uint32_t keep = (o0 + tid < m && st < nsteps) ? ~0u : 0u;   // a mask, so that nothing branches
+    const float sb = scale_value(sv[b] & 0x7F);
+    const uint32_t word = cv[b][h];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int jj = 2 * part + j;
-        qv[jj] = dq_byte(word, sb, jj) & keep;
-      }
-      if (part == 1) *(u32x4*)(buf + BT * BLD + tid * BLD + 16 * b + 8 * h) = qv;
+    for (int j = 0; j < 2; ++j) {
+      const int jj = 2 * part + j;
+      qv[jj] = dq_byte(word, sb, jj) & keep;
     }
+    if (part == 1) *(u32x4*)(buf + tid * BLD + 16 * b + 8 * h) = qv;
   };
 
   f32x16 acc[4][4];
@@ -262,32 +277,39 @@ __global__ __launch_bounds__(256) void nvfp4_gemm_big_kernel(const uint16_t* __r
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  u32x4 xv0[4], xv1[4], qv;
   u32x2 cv0[2], cv1[2];
   uint32_t sv0[2], sv1[2];
-  load(0, xv0, cv0, sv0);
+  u32x4 qv;
+  issue_x(0);
+  issue_x(1);
+  load_q(0, cv0, sv0);
 #pragma unroll
-  for (int p = 0; p < 12; ++p) store_piece(smem, 0, xv0, cv0, sv0, p, qv);
-  load(BK, xv0, cv0, sv0);
-  load(2 * BK, xv1, cv1, sv1);
-  __syncthreads();
+  for (int p = 0; p < 8; ++p) q_piece(qbuf, 0, cv0, sv0, p, qv);
+  load_q(1, cv0, sv0);
+  load_q(2, cv1, sv1);
+  __syncthreads();   // waits for every load so far, X steps 0 and 1 included
 
-  const int arow = wr * 128 + (lane & 31), brow = wc * 128 + (lane & 31), koff = 8 * (lane >> 5);
-  auto body = [&](const uint16_t* __restrict__ Xs, uint16_t* __restrict__ nbuf, int64_t st, u32x4 (&xv)[4],
-                  u32x2 (&cv)[2], uint32_t (&sv)[2]) {
-    const uint16_t* Qs = Xs + BT * BLD;
-    const int64_t kn = (st + 1) * BK;
+  const int arow = wr * 128 + (lane & 31), brow = wc * 128 + (lane & 31), kc = lane >> 5;
+  // Per step st: 4 loads of X step st+2 (first), 4 loads of codes step st+3
+  // (product 20).  At the end, X step st+1 must have landed: after it were
+  // issued the codes of st+2, X of st+2 and the codes of st+3, 12 loads.
+  auto body = [&](const uint16_t* __restrict__ Xs, const uint16_t* __restrict__ Qs, uint16_t* __restrict__ nq,
+                  int64_t st, u32x2 (&cv)[2], uint32_t (&sv)[2]) {
     bf16x8 a[2][4], b[2][4];
     auto read = [&](int h, int f) {
-      if (f < 4) a[h][f] = *(const bf16x8*)(Xs + (arow + 32 * f) * BLD + 16 * h + koff);
-      else b[h][f - 4] = *(const bf16x8*)(Qs + (brow + 32 * (f - 4)) * BLD + 16 * h + koff);
+      if (f < 4) {
+        const int r = arow + 32 * f;
+        a[h][f] = *(const bf16x8*)(Xs + r * BK + bswz(r, 2 * h + kc) * 8);
+      } else {
+        b[h][f - 4] = *(const bf16x8*)(Qs + (brow + 32 * (f - 4)) * BLD + 16 * h + 8 * kc);
+      }
     };
 #pragma unroll
     for (int f = 0; f < 8; ++f) read(0, f);
-    // 32 products per step (two k-steps of 16); behind product g: the second
-    // k-step's fragment g (g < 8), store piece g - 4 (4 <= g < 16) and, once
-    // the register set's last reader has run, the loads of step st+3 into it
-    // (g == 20).
+    // Behind product g: the second k-step's fragment g (g < 8), the X loads
+    // of step st+2 (g < 4, one per product), codes piece g - 4 (4 <= g < 12)
+    // and, once its register set's last reader has run, the codes of step
+    // st+3 (g == 20).
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -295,19 +317,21 @@ __global__ __launch_bounds__(256) void nvfp4_gemm_big_kernel(const uint16_t* __r
         const int g = 16 * h + mm, i = mm >> 2, j = mm & 3;
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[h][i], b[h][j], acc[i][j], 0, 0, 0);
         if (g < 8) read(1, g);
-        if (g >= 4 && g < 16) store_piece(nbuf, kn, xv, cv, sv, g - 4, qv);
-        if (g == 20) load((st + 3) * BK, xv, cv, sv);
+        if (g == 0) issue_x(st + 2);
+        if (g >= 4 && g < 12) q_piece(nq, st + 1, cv, sv, g - 4, qv);
+        if (g == 20) load_q(st + 3, cv, sv);
         __builtin_amdgcn_sched_barrier(0);
       }
+    __builtin_amdgcn_s_waitcnt(12 | (7 << 4) | (0 << 8));   // vmcnt(12), lgkmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
   };
   // Steps go in pairs with no branch between them (a join would make the
   // compiler copy the accumulators): with an odd step count the last pair's
-  // second step multiplies the zeros stored for the step past the end.
+  // second step multiplies zeros (its X rows read past the end as zeros and
+  // its codes are masked).
   for (int64_t st = 0; st < nsteps; st += 2) {
-    body(smem + 0, smem + BBUF, st, xv0, cv0, sv0);
-    lds_barrier();
-    body(smem + BBUF, smem + 0, st + 1, xv1, cv1, sv1);
-    lds_barrier();
+    body(xbuf + ((int)st % 3) * BXBUF, qbuf, qbuf + BQBUF, st, cv0, sv0);
+    body(xbuf + ((int)st + 1) % 3 * BXBUF, qbuf + BQBUF, qbuf, st + 1, cv1, sv1);
   }
 
   // Accumulator layout: lane l, register r -> row 8 (r/4) + 4 (l/32) + r%4, column l%32.
@@ -361,7 +385,7 @@ hipError_t nvfp4_gemm_launch(const uint16_t* X, int64_t T, int64_t k, int64_t ld
                              const uint8_t* scales, const float* g, int64_t m, void* Y, int out_bf16, int64_t ldy,
                              float* ws, hipStream_t s) {
   if (T <= 0 || m <= 0) return hipSuccess;
-  if (((T + BT - 1) / BT) * ((m + BT - 1) / BT) >= num_cus_consumer()) {
+  if (k % BK == 0 && ((T + BT - 1) / BT) * ((m + BT - 1) / BT) >= num_cus_consumer()) {
     // Enough 256 x 256 tiles for every CU: the large-tile kernel, no k split.
     dim3 grid((unsigned)((m + BT - 1) / BT), (unsigned)((T + BT - 1) / BT));
     if (out_bf16)
