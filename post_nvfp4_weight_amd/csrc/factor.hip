@@ -334,32 +334,33 @@ __global__ __launch_bounds__(256) void chol_update_kernel(float* __restrict__ A,
 }
 
 // Inverses of the diagonal 64-blocks of L (one wave each) into Linv: lane c
-// keeps column c of the block and solves L x = e_c by forward substitution;
-// row i of L comes to every lane by readlane.
+// solves L x = e_c by forward substitution (column c of the inverse), with
+// the block in LDS so that row i of L reaches every lane as broadcast reads
+// (the same address in every lane), four values at a time.
 __global__ __launch_bounds__(64) void diag_inv_kernel(const float* __restrict__ A, int64_t k,
                                                       float* __restrict__ Linv) {
+  __shared__ __attribute__((aligned(16))) float Ls[NB][NB];
   const int lane = threadIdx.x;
   const int64_t p = (int64_t)blockIdx.x * NB;
   const int nb = (int)min((int64_t)NB, k - p);
-  float c[NB];
-#pragma unroll
+  // L's lower part; the identity outside nb.
+#pragma unroll 8
   for (int i = 0; i < NB; ++i) {
     float v = (i == lane) ? 1.0f : 0.0f;
     if (i < nb && lane < nb && lane <= i) v = A[(p + i) * k + p + lane];
-    c[i] = v;
+    Ls[i][lane] = v;
   }
-  float inv_own = 0.0f;   // 1 / L[lane][lane]
-#pragma unroll
-  for (int i = 0; i < NB; ++i)
-    if (i == lane) inv_own = 1.0f / c[i];
+  __syncthreads();
   float x[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
     float acc = (i == lane) ? 1.0f : 0.0f;
 #pragma unroll
-    for (int m = 0; m < i; ++m)
-      acc = fmaf(-__int_as_float(__builtin_amdgcn_readlane(__float_as_int(c[i]), m)), x[m], acc);
-    x[i] = acc * __int_as_float(__builtin_amdgcn_readlane(__float_as_int(inv_own), i));
+    for (int m = 0; m < i; ++m) acc = fmaf(-Ls[i][m], x[m], acc);
+    x[i] = acc * (1.0f / Ls[i][i]);
+    // Row by row: x[i] is formed here (not sunk to its stores, which would
+    // keep every value read alive), and later rows' reads stay below.
+    asm volatile("" : "+v"(x[i]) :: "memory");
   }
 #pragma unroll
   for (int i = 0; i < NB; ++i)
