@@ -333,6 +333,9 @@ __global__ __launch_bounds__(256) void nvfp4_gemm_big_kernel(const uint16_t* __r
     body(xbuf + ((int)st % 3) * BXBUF, qbuf, qbuf + BQBUF, st, cv0, sv0);
     body(xbuf + ((int)st + 1) % 3 * BXBUF, qbuf + BQBUF, qbuf, st + 1, cv1, sv1);
   }
+  // The direct-to-LDS loads issued for steps past the end still write LDS
+  // (zeros): none may be in flight once the workgroup's LDS is released.
+  __builtin_amdgcn_s_waitcnt(0);
 
   // Accumulator layout: lane l, register r -> row 8 (r/4) + 4 (l/32) + r%4, column l%32.
   const float g = *gptr;

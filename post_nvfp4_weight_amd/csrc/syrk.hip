@@ -287,6 +287,11 @@ __device__ __forceinline__ void tile_job(char* lds, const uint16_t* __restrict__
                                     a0, b0, acc);
   }
 
+  // The zero-length loads issued for stages past the end write LDS too: wait
+  // for them, so that none is in flight once the workgroup's LDS is reused
+  // (the next tile job) or released.
+  __builtin_amdgcn_s_waitcnt(0);
+
   // Epilogue.  Accumulator element (lane l, register r) of a 32x32 tile is at
   // row 8*(r/4) + 4*(l/32) + r%4, column l%32.
   if (P == nullptr) {
