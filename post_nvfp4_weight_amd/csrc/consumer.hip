@@ -239,19 +239,21 @@ __global__ __launch_bounds__(256) void nvfp4_gemm_big_kernel(const uint16_t* __r
 #endif
   };
 
-  // Codes and scales of weight row tid: two blocks per step (clamped, so
-  // that every load is valid).
+  // Codes and scales of weight row tid: the two blocks of a step are 16
+  // aligned bytes of codes and 2 of scales (k is a multiple of 32); steps
+  // past the end are clamped, so that every load is valid.
   const int64_t wrow = min(o0 + tid, m - 1);
   const uint8_t* crow = codes + wrow * (k / 2);
   const uint8_t* srow = scales + wrow * kb;
-  const int kb1 = (int)(kb - 1);
+  const int last = (int)(nsteps - 1);
   auto load_q = [&](int64_t st, u32x2 (&cv)[2], uint32_t (&sv)[2]) {
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int blk = min((int)(st * 2) + b, kb1);
-      cv[b] = *(const u32x2*)(crow + blk * 8);
-      sv[b] = srow[blk];
-    }
+    const int s2 = min((int)st, last);
+    const u32x4 c = *(const u32x4*)(crow + s2 * 16);
+    const uint32_t sc = *(const uint16_t*)(srow + s2 * 2);
+    cv[0] = u32x2{c[0], c[1]};
+    cv[1] = u32x2{c[2], c[3]};
+    sv[0] = sc & 0xFF;
+    sv[1] = sc >> 8;
   };
   // Piece p (0..7) of expanding step st's codes into Q buffer buf: block p / 4,
   // 8-code half (p / 2) % 2; the first piece of a half expands 4 codes, the
@@ -388,8 +390,10 @@ hipError_t nvfp4_gemm_launch(const uint16_t* X, int64_t T, int64_t k, int64_t ld
                              const uint8_t* scales, const float* g, int64_t m, void* Y, int out_bf16, int64_t ldy,
                              float* ws, hipStream_t s) {
   if (T <= 0 || m <= 0) return hipSuccess;
-  if (k % BK == 0 && ((T + BT - 1) / BT) * ((m + BT - 1) / BT) >= num_cus_consumer()) {
-    // Enough 256 x 256 tiles for every CU: the large-tile kernel, no k split.
+  if (k % BK == 0 && (uintptr_t)codes % 16 == 0 && (uintptr_t)scales % 2 == 0 &&
+      ((T + BT - 1) / BT) * ((m + BT - 1) / BT) >= num_cus_consumer()) {
+    // Enough 256 x 256 tiles for every CU (k a multiple of 32, codes 16-byte and
+    // scales 2-byte aligned): the large-tile kernel, no k split.
     dim3 grid((unsigned)((m + BT - 1) / BT), (unsigned)((T + BT - 1) / BT));
     if (out_bf16)
       hipLaunchKernelGGL(nvfp4_gemm_big_kernel<1>, grid, dim3(256), 0, s, X, T, k, ldx, codes, scales, g, m, Y, ldy);
