@@ -47,6 +47,11 @@ namespace {
 #endif
 constexpr int ST = NVQ_SYRK_ST;   // tokens per stage
 constexpr int NS = NVQ_SYRK_NS;   // ring depth (stages in flight + the one being multiplied)
+#ifndef NVQ_SYRK_HEAD16
+#define NVQ_SYRK_HEAD16 13
+#endif
+constexpr int HEAD16 = NVQ_SYRK_HEAD16;   // sixteenths of a token range a strip pair covers in the first launch
+constexpr int TSPLIT = 4;                 // tail pieces per (range, strip pair)
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 #define LDS_AS __attribute__((address_space(3)))
@@ -371,10 +376,43 @@ __host__ __device__ inline void item_coords(int r, int nb2, int& kind, int& a, i
   kind = -1; a = b = 0;
 }
 
-int items_per_range(int nb2) {
+__host__ __device__ inline int items_per_range(int nb2) {
   int nsp = 0;
   for (int a0 = 0; a0 < nb2; a0 += SB) nsp += (min(SB, nb2 - a0) + 1) / 2;
   return nb2 * (nb2 - 1) / 2 + nsp;
+}
+__host__ __device__ inline int pairs_per_range(int nb2) { return items_per_range(nb2) - nb2 * (nb2 - 1) / 2; }
+
+// Strip-pair tails.  With token splits every first-launch item covers one
+// token range, but a strip pair moves 1.5 times the bytes per product of a
+// quad and would finish last.  So it covers only the first `head` tokens of
+// its range there, and the rest of the range is cut into tsplit pieces that
+// run in the second launch beside the singles (npairs == 0: no tails).
+struct TailArgs {
+  int npairs;        // strip-pair items per range
+  int tsplit;        // pieces per (range, pair)
+  int64_t head;      // tokens of a range covered by the first launch
+  int64_t ttokens;   // tokens per piece
+  int64_t base;      // first partial slot of the pieces, ordered by (range, pair, piece)
+};
+// Item index (within a range) of the p-th strip pair, and the pair number of item r.
+__device__ inline int pair_item(int p, int nb2) {
+  const int per = items_per_range(nb2);
+  for (int r = 0, q = 0; r < per; ++r) {
+    int kind, a, b;
+    item_coords(r, nb2, kind, a, b);
+    if (kind == 1 && q++ == p) return r;
+  }
+  return 0;
+}
+__device__ inline int pair_of_item(int r, int nb2) {
+  int q = 0;
+  for (int i = 0; i < r; ++i) {
+    int kind, a, b;
+    item_coords(i, nb2, kind, a, b);
+    q += kind == 1;
+  }
+  return q;
 }
 
 // Workgroups are dealt to the XCDs round-robin by id (id % 8).  Give each
@@ -394,7 +432,7 @@ __device__ __forceinline__ int xcd_logical(int id, int G) {
 __global__ __launch_bounds__(256) void syrk_main_kernel(const uint16_t* __restrict__ X, int64_t n, int64_t k,
                                                         int64_t ldx, float* __restrict__ H,
                                                         float* __restrict__ partial, int per_range, int qsplit,
-                                                        int64_t qtokens) {
+                                                        int64_t qtokens, TailArgs tail) {
   extern __shared__ __attribute__((aligned(1024))) char lds[];
   const int nb2 = (int)((k + QUAD - 1) / QUAD);
   const int L = xcd_logical(blockIdx.x, gridDim.x);
@@ -406,38 +444,64 @@ __global__ __launch_bounds__(256) void syrk_main_kernel(const uint16_t* __restri
   if (kind == 0) {
     tile_job<QUAD, QUAD>(lds, X, k, ldx, (int64_t)a * QUAD, (int64_t)b * QUAD, t0, t1, H, P);
   } else if (kind == 1) {
-    tile_job<HALF, QUAD>(lds, X, k, ldx, (int64_t)a * QUAD, (int64_t)a * QUAD, t0, t1, H, P);
+    const int64_t te = tail.npairs > 0 ? min(t1, t0 + tail.head) : t1;   // the rest is tail work
+    tile_job<HALF, QUAD>(lds, X, k, ldx, (int64_t)a * QUAD, (int64_t)a * QUAD, t0, te, H, P);
     if (b >= 0) {
       __syncthreads();   // the LDS ring is reused
-      tile_job<HALF, QUAD>(lds, X, k, ldx, (int64_t)b * QUAD, (int64_t)b * QUAD, t0, t1, H,
+      tile_job<HALF, QUAD>(lds, X, k, ldx, (int64_t)b * QUAD, (int64_t)b * QUAD, t0, te, H,
                            P ? P + HALF * QUAD : nullptr);
     }
   }
 }
 
 // Launch 2: singles (bottom-right diagonal 128-block of 256-block a), split
-// over tokens when they are too few to fill the device.
+// over tokens when they are too few to fill the device (workgroups
+// 0 .. nsingle * nsplit - 1), then the strip-pair tail pieces.
 __global__ __launch_bounds__(256) void syrk_single_kernel(const uint16_t* __restrict__ X, int64_t n, int64_t k,
                                                           int64_t ldx, float* __restrict__ H,
-                                                          float* __restrict__ partial, int nsplit,
-                                                          int64_t stokens, size_t slot_base) {
+                                                          float* __restrict__ partial, int nsingle, int nsplit,
+                                                          int64_t stokens, size_t slot_base, int64_t qtokens,
+                                                          TailArgs tail) {
   extern __shared__ __attribute__((aligned(1024))) char lds[];
-  const int a = blockIdx.x;
-  const int64_t c0 = (int64_t)a * QUAD + HALF;
-  const int64_t t0 = (int64_t)blockIdx.y * stokens;
-  float* P = nsplit > 1 ? partial + (slot_base + (size_t)blockIdx.x * nsplit + blockIdx.y) * kSlotFloats : nullptr;
-  tile_job<HALF, HALF>(lds, X, k, ldx, c0, c0, t0, min(n, t0 + stokens), H, P);
+  const int id = blockIdx.x, nsi = nsingle * nsplit;
+  if (id < nsi) {
+    const int a = id / nsplit, sp = id % nsplit;
+    const int64_t c0 = (int64_t)a * QUAD + HALF;
+    const int64_t t0 = (int64_t)sp * stokens;
+    float* P = nsplit > 1 ? partial + (slot_base + (size_t)a * nsplit + sp) * kSlotFloats : nullptr;
+    tile_job<HALF, HALF>(lds, X, k, ldx, c0, c0, t0, min(n, t0 + stokens), H, P);
+    return;
+  }
+  // Tail piece u: token range sp, strip pair p, piece t (an empty token range
+  // stores zeros).
+  const int u = id - nsi;
+  const int sp = u / (tail.npairs * tail.tsplit), p = (u / tail.tsplit) % tail.npairs, t = u % tail.tsplit;
+  const int nb2 = (int)((k + QUAD - 1) / QUAD);
+  int kind, a, b;
+  item_coords(pair_item(p, nb2), nb2, kind, a, b);
+  const int64_t r1 = min(n, (int64_t)sp * qtokens + qtokens);
+  const int64_t ts = min(r1, (int64_t)sp * qtokens + tail.head + (int64_t)t * tail.ttokens);
+  const int64_t te = min(r1, ts + tail.ttokens);
+  float* P = partial + ((size_t)tail.base + u) * kSlotFloats;
+  tile_job<HALF, QUAD>(lds, X, k, ldx, (int64_t)a * QUAD, (int64_t)a * QUAD, ts, te, H, P);
+  if (b >= 0) {
+    __syncthreads();   // the LDS ring is reused
+    tile_job<HALF, QUAD>(lds, X, k, ldx, (int64_t)b * QUAD, (int64_t)b * QUAD, ts, te, H, P + HALF * QUAD);
+  }
 }
 
 // Sum the token splits of one 64x64 piece of a tile in split order, add the
 // sum into H's upper triangle and write the mirror.  The piece is at rows r0,
-// columns c0 of H; its split sp is at P + sp * sstride with row stride ldp.
-// H and P move in 16-byte vectors; the mirror goes through an LDS transpose
-// so that it is written by rows too.  k % 16 == 0, so a vector is wholly
-// inside or outside H.
+// columns c0 of H; its split sp is at P + sp * sstride with row stride ldp;
+// then come n2 more partial sums (strip-pair tail pieces), the j-th at
+// P2 + (j / inner2) * ostride2 + (j % inner2) * istride2.  H and P move in
+// 16-byte vectors; the mirror goes through an LDS transpose so that it is
+// written by rows too.  k % 16 == 0, so a vector is wholly inside or outside H.
 constexpr int PIECE = 64;
 __device__ __forceinline__ void reduce_piece(int64_t k, float* __restrict__ H, const float* __restrict__ P,
-                                             size_t sstride, int nsplit, int ldp, int64_t r0, int64_t c0) {
+                                             size_t sstride, int nsplit, int ldp, int64_t r0, int64_t c0,
+                                             const float* __restrict__ P2 = nullptr, int n2 = 0, int inner2 = 1,
+                                             size_t ostride2 = 0, size_t istride2 = 0) {
   if (r0 >= k || c0 >= k || r0 >= c0 + PIECE) return;   // outside H, or wholly below the diagonal
   __shared__ float tr[PIECE][PIECE + 1];
   const int tid = threadIdx.x;
@@ -465,6 +529,14 @@ __device__ __forceinline__ void reduce_piece(int64_t k, float* __restrict__ H, c
     for (int q = 0; q < 4; ++q) {
       const int e = q * 256 + tid, row = e >> 4, c4 = (e & 15) * 4;
       s[q] += *(const f32x4*)(P + (size_t)sp * sstride + (size_t)row * ldp + c4);
+    }
+  }
+  for (int j = 0; j < n2; ++j) {
+    const float* Q = P2 + (size_t)(j / inner2) * ostride2 + (size_t)(j % inner2) * istride2;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = q * 256 + tid, row = e >> 4, c4 = (e & 15) * 4;
+      s[q] += *(const f32x4*)(Q + (size_t)row * ldp + c4);
     }
   }
 #pragma unroll
@@ -513,7 +585,7 @@ __device__ __forceinline__ void reduce_piece(int64_t k, float* __restrict__ H, c
 // is a piece of its 2x2.
 __global__ __launch_bounds__(256) void syrk_reduce_kernel(int64_t k, float* __restrict__ H,
                                                           const float* __restrict__ partial, int kind, int nsplit,
-                                                          int per_range, size_t slot_base) {
+                                                          int per_range, size_t slot_base, TailArgs tail) {
   const int nb2 = (int)((k + QUAD - 1) / QUAD);
   const int y = blockIdx.y;
   if (kind == 0) {
@@ -527,9 +599,17 @@ __global__ __launch_bounds__(256) void syrk_reduce_kernel(int64_t k, float* __re
                    (int64_t)a * QUAD + (y / 4) * PIECE, (int64_t)b * QUAD + pc * PIECE);
     } else if (ik == 1) {
       const int d = y < 8 ? a : b;
+      const size_t off = (y < 8 ? 0 : (size_t)HALF * QUAD) + (size_t)pr * PIECE * QUAD + pc * PIECE;
+      const float* P2 = nullptr;
+      int n2 = 0;
+      if (tail.npairs > 0) {   // then the pair's tail pieces, by range and piece
+        P2 = partial + ((size_t)tail.base + (size_t)pair_of_item(blockIdx.x, nb2) * tail.tsplit) * kSlotFloats + off;
+        n2 = nsplit * tail.tsplit;
+      }
       if (d >= 0)
-        reduce_piece(k, H, P + (y < 8 ? 0 : (size_t)HALF * QUAD) + (size_t)pr * PIECE * QUAD + pc * PIECE, sstride,
-                     nsplit, QUAD, (int64_t)d * QUAD + pr * PIECE, (int64_t)d * QUAD + pc * PIECE);
+        reduce_piece(k, H, P + off, sstride, nsplit, QUAD, (int64_t)d * QUAD + pr * PIECE,
+                     (int64_t)d * QUAD + pc * PIECE, P2, n2, tail.tsplit,
+                     (size_t)tail.npairs * tail.tsplit * kSlotFloats, kSlotFloats);
     }
   } else {
     const int64_t c0 = (int64_t)blockIdx.x * QUAD + HALF;
@@ -547,6 +627,7 @@ __global__ void symmetrize_kernel(float* H, int64_t k) {
 struct SyrkPlan {
   int nb2, per_range, qsplit, nsingle, ssplit;
   int64_t qtokens, stokens;
+  TailArgs tail;
   size_t slots;
 };
 
@@ -578,15 +659,31 @@ SyrkPlan plan(int64_t n, int64_t k, int cus) {
     if (s > nstages) s = nstages;
     p.qsplit = (int)(s < 1 ? 1 : s);
   }
+  p.qtokens = ((nstages + p.qsplit - 1) / p.qsplit) * ST;
+  // Strip-pair tails (only with token splits, whose partial sums the tails
+  // join): the pairs keep HEAD16/16 of each range, whole stages, when the
+  // pieces leave at least half the device to the singles.
+  p.tail = TailArgs{0, 1, 0, 0, 0};
+  if (p.qsplit > 1) {
+    const int npairs = pairs_per_range(p.nb2);
+    const int64_t head = p.qtokens * HEAD16 / 16 / ST * ST;
+    if (npairs > 0 && head > 0 && head < p.qtokens && (int64_t)npairs * p.qsplit * TSPLIT <= cus / 2) {
+      const int64_t per = (p.qtokens - head + TSPLIT - 1) / TSPLIT;
+      p.tail = TailArgs{npairs, TSPLIT, head, (per + ST - 1) / ST * ST, (int64_t)p.per_range * p.qsplit};
+    }
+  }
+  const int tail_items = p.tail.npairs * p.qsplit * p.tail.tsplit;
   p.ssplit = 1;
-  if (p.nsingle > 0 && p.nsingle < cus) {
-    int64_t s = cus / p.nsingle;
+  if (p.nsingle > 0 && p.nsingle < cus - tail_items) {
+    int64_t s = (cus - tail_items) / p.nsingle;
     if (s > nstages) s = nstages;
     p.ssplit = (int)(s < 1 ? 1 : s);
   }
-  p.qtokens = ((nstages + p.qsplit - 1) / p.qsplit) * ST;
   p.stokens = ((nstages + p.ssplit - 1) / p.ssplit) * ST;
-  p.slots = (p.qsplit > 1 ? (size_t)p.per_range * p.qsplit : 0) + (p.ssplit > 1 ? (size_t)p.nsingle * p.ssplit : 0);
+  // Slots: first-launch items, then the singles' splits, then the tail pieces.
+  p.slots = (p.qsplit > 1 ? (size_t)p.per_range * p.qsplit : 0) + (p.ssplit > 1 ? (size_t)p.nsingle * p.ssplit : 0) +
+            (size_t)tail_items;
+  if (tail_items > 0) p.tail.base = (int64_t)(p.slots - tail_items);
   return p;
 }
 
@@ -605,7 +702,9 @@ hipError_t syrk_bf16(const uint16_t* X, int64_t n, int64_t k, int64_t ldx, float
                                  ? Tile<QUAD, QUAD>::STAGE_BYTES
                                  : Tile<HALF, QUAD>::STAGE_BYTES;
   const size_t lds_main = (size_t)NS * main_stage;
-  const size_t lds_single = (size_t)NS * Tile<HALF, HALF>::STAGE_BYTES;
+  const size_t lds_single = (size_t)NS * (Tile<HALF, QUAD>::STAGE_BYTES > Tile<HALF, HALF>::STAGE_BYTES
+                                              ? Tile<HALF, QUAD>::STAGE_BYTES
+                                              : Tile<HALF, HALF>::STAGE_BYTES);
   static bool attr = false;
   if (!attr) {
     (void)hipFuncSetAttribute((const void*)syrk_main_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -614,22 +713,22 @@ hipError_t syrk_bf16(const uint16_t* X, int64_t n, int64_t k, int64_t ldx, float
                               (int)lds_single);
     attr = true;
   }
+  // Order: first launch, second launch (singles and tail pieces), then the
+  // reductions, since a strip pair's tiles sum the tail pieces too.
   const int items = p.per_range * p.qsplit;
   hipLaunchKernelGGL(syrk_main_kernel, dim3(items), dim3(256), lds_main, s, X, n, k, ldx, H, partial, p.per_range,
-                     p.qsplit, p.qtokens);
-  size_t slot = 0;
-  if (p.qsplit > 1) {
+                     p.qsplit, p.qtokens, p.tail);
+  const size_t single_base = p.qsplit > 1 ? (size_t)p.per_range * p.qsplit : 0;
+  const int second = p.nsingle * p.ssplit + p.tail.npairs * p.qsplit * p.tail.tsplit;
+  if (second > 0)
+    hipLaunchKernelGGL(syrk_single_kernel, dim3(second), dim3(256), lds_single, s, X, n, k, ldx, H, partial,
+                       p.nsingle, p.ssplit, p.stokens, single_base, p.qtokens, p.tail);
+  if (p.qsplit > 1)
     hipLaunchKernelGGL(syrk_reduce_kernel, dim3(p.per_range, 16), dim3(256), 0, s, k, H, partial, 0, p.qsplit,
-                       p.per_range, (size_t)0);
-    slot += (size_t)p.per_range * p.qsplit;
-  }
-  if (p.nsingle > 0) {
-    hipLaunchKernelGGL(syrk_single_kernel, dim3(p.nsingle, p.ssplit), dim3(256), lds_single, s, X, n, k, ldx, H,
-                       partial, p.ssplit, p.stokens, slot);
-    if (p.ssplit > 1)
-      hipLaunchKernelGGL(syrk_reduce_kernel, dim3(p.nsingle, 4), dim3(256), 0, s, k, H, partial, 1, p.ssplit, 0,
-                         slot);
-  }
+                       p.per_range, (size_t)0, p.tail);
+  if (p.nsingle > 0 && p.ssplit > 1)
+    hipLaunchKernelGGL(syrk_reduce_kernel, dim3(p.nsingle, 4), dim3(256), 0, s, k, H, partial, 1, p.ssplit, 0,
+                       single_base, p.tail);
   return hipGetLastError();
 }
 
