@@ -65,10 +65,15 @@ __device__ __forceinline__ int unswz(int pc, int r) {
   return y ^ ((y & 2) << 2);
 }
 
-template <int TM, int TN>
+// A TM x TN tile of H: a stage holds ST token rows of the A operand (TM
+// channels) and then of the B operand (TN channels).  A diagonal tile (D:
+// rows and columns start at the same channel, TM <= TN) loads only B and
+// reads A from B's first TM channels.
+template <int TM, int TN, bool D = false>
 struct Tile {
-  static constexpr int A_ROWB = TM * 2, B_ROWB = TN * 2;    // bytes per token row
-  static constexpr int A_BYTES = ST * A_ROWB, B_BYTES = ST * B_ROWB;
+  static_assert(!D || TM <= TN, "a diagonal tile's rows are a prefix of its columns");
+  static constexpr int A_ROWB = D ? TN * 2 : TM * 2, B_ROWB = TN * 2;   // bytes per token row of A's and B's region
+  static constexpr int A_BYTES = D ? 0 : ST * A_ROWB, B_BYTES = ST * B_ROWB;
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
   static constexpr int PER_WAVE = STAGE_BYTES / 4096;         // 1 KB direct-to-LDS loads per wave
   static constexpr int NI = TM / 64, NJ = TN / 64;            // 32x32 MFMA tiles per wave
@@ -92,11 +97,11 @@ __device__ __forceinline__ void issue_loads(char* dst, const void* src, int nrec
 }
 
 // Operand fragments of k-step kk (16 tokens) of the stage in buf.
-template <int TM, int TN>
-__device__ __forceinline__ void read_frags(const char* buf, int kk, const int (&aoff)[Tile<TM, TN>::NI][2],
-                                           const int (&boff)[Tile<TM, TN>::NJ][2], bf16x8 (&a)[Tile<TM, TN>::NI],
-                                           bf16x8 (&b)[Tile<TM, TN>::NJ]) {
-  using T = Tile<TM, TN>;
+template <int TM, int TN, bool D>
+__device__ __forceinline__ void read_frags(const char* buf, int kk, const int (&aoff)[Tile<TM, TN, D>::NI][2],
+                                           const int (&boff)[Tile<TM, TN, D>::NJ][2], bf16x8 (&a)[Tile<TM, TN, D>::NI],
+                                           bf16x8 (&b)[Tile<TM, TN, D>::NJ]) {
+  using T = Tile<TM, TN, D>;
 #pragma unroll
   for (int f = 0; f < T::NI; ++f) {
     s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(buf + aoff[f][0] + kk * 16 * T::A_ROWB));
@@ -111,23 +116,13 @@ __device__ __forceinline__ void read_frags(const char* buf, int kk, const int (&
   }
 }
 
-template <int TM, int TN>
-__device__ __forceinline__ void mfma_block(const bf16x8 (&a)[Tile<TM, TN>::NI], const bf16x8 (&b)[Tile<TM, TN>::NJ],
-                                           f32x16 (&acc)[Tile<TM, TN>::NI][Tile<TM, TN>::NJ]) {
-#pragma unroll
-  for (int i = 0; i < Tile<TM, TN>::NI; ++i)
-#pragma unroll
-    for (int f = 0; f < Tile<TM, TN>::NJ; ++f)
-      acc[i][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[f], acc[i][f], 0, 0, 0);
-}
-
 // Fragment f of k-step kk of the stage in buf: f < NI is A fragment f,
 // otherwise B fragment f - NI.
-template <int TM, int TN>
-__device__ __forceinline__ void read_one(const char* buf, int kk, int f, const int (&aoff)[Tile<TM, TN>::NI][2],
-                                         const int (&boff)[Tile<TM, TN>::NJ][2], bf16x8 (&a)[Tile<TM, TN>::NI],
-                                         bf16x8 (&b)[Tile<TM, TN>::NJ]) {
-  using T = Tile<TM, TN>;
+template <int TM, int TN, bool D>
+__device__ __forceinline__ void read_one(const char* buf, int kk, int f, const int (&aoff)[Tile<TM, TN, D>::NI][2],
+                                         const int (&boff)[Tile<TM, TN, D>::NJ][2], bf16x8 (&a)[Tile<TM, TN, D>::NI],
+                                         bf16x8 (&b)[Tile<TM, TN, D>::NJ]) {
+  using T = Tile<TM, TN, D>;
   if (f < T::NI) {
     s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(buf + aoff[f][0] + kk * 16 * T::A_ROWB));
     s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(buf + aoff[f][1] + kk * 16 * T::A_ROWB));
@@ -162,15 +157,15 @@ __device__ __forceinline__ void issue_load_one(char* dst, const void* src, int n
 // cores are never left waiting behind a burst of memory instructions.
 // `slot` and `nxt` are distinct, which the restrict qualifiers state: the
 // compiler then need not wait on the loads in flight before operand reads.
-template <int TM, int TN, int WAIT, bool has_next>
+template <int TM, int TN, bool D, int WAIT, bool has_next>
 __device__ __forceinline__ void pipe_step(char* __restrict__ slot, const char* __restrict__ nxt,
-                                          const void* src, int nrec, const uint32_t (&voff)[Tile<TM, TN>::PER_WAVE],
-                                          const int (&ldsoff)[Tile<TM, TN>::PER_WAVE],
-                                          const int (&aoff)[Tile<TM, TN>::NI][2],
-                                          const int (&boff)[Tile<TM, TN>::NJ][2], bf16x8 (&a0)[Tile<TM, TN>::NI],
-                                          bf16x8 (&b0)[Tile<TM, TN>::NJ],
-                                          f32x16 (&acc)[Tile<TM, TN>::NI][Tile<TM, TN>::NJ]) {
-  using T = Tile<TM, TN>;
+                                          const void* src, int nrec, const uint32_t (&voff)[Tile<TM, TN, D>::PER_WAVE],
+                                          const int (&ldsoff)[Tile<TM, TN, D>::PER_WAVE],
+                                          const int (&aoff)[Tile<TM, TN, D>::NI][2],
+                                          const int (&boff)[Tile<TM, TN, D>::NJ][2], bf16x8 (&a0)[Tile<TM, TN, D>::NI],
+                                          bf16x8 (&b0)[Tile<TM, TN, D>::NJ],
+                                          f32x16 (&acc)[Tile<TM, TN, D>::NI][Tile<TM, TN, D>::NJ]) {
+  using T = Tile<TM, TN, D>;
   static_assert(ST == 32, "two k-steps per stage");
   constexpr int NM = T::NI * T::NJ, NF = T::NI + T::NJ, NL = T::PER_WAVE;
   constexpr int N1 = NM > NF ? NM : NF;
@@ -178,7 +173,7 @@ __device__ __forceinline__ void pipe_step(char* __restrict__ slot, const char* _
   bf16x8 a1[T::NI], b1[T::NJ];
 #pragma unroll
   for (int m = 0; m < N1; ++m) {
-    if (m < NF) read_one<TM, TN>(slot, 1, m, aoff, boff, a1, b1);
+    if (m < NF) read_one<TM, TN, D>(slot, 1, m, aoff, boff, a1, b1);
     if (m < NM) acc[m / T::NJ][m % T::NJ] =
         __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[m / T::NJ], b0[m % T::NJ], acc[m / T::NJ][m % T::NJ], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
@@ -193,7 +188,7 @@ __device__ __forceinline__ void pipe_step(char* __restrict__ slot, const char* _
   for (int m = 0; m < N2; ++m) {
     if constexpr (has_next) {
       if (m < NL) issue_load_one(slot, src, nrec, voff[m], ldsoff[m]);
-      if (m < NF) read_one<TM, TN>(nxt, 0, m, aoff, boff, a0, b0);
+      if (m < NF) read_one<TM, TN, D>(nxt, 0, m, aoff, boff, a0, b0);
     }
     if (m < NM) acc[m / T::NJ][m % T::NJ] =
         __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[m / T::NJ], b1[m % T::NJ], acc[m / T::NJ][m % T::NJ], 0, 0, 0);
@@ -206,11 +201,11 @@ __device__ __forceinline__ void pipe_step(char* __restrict__ slot, const char* _
 // otherwise store the partial sums into P [TM x TN].  Channels at or past k
 // may be read (they only feed accumulators of rows/columns >= k, which are
 // never stored); reads stay inside X's rows thanks to the buffer bound.
-template <int TM, int TN>
+template <int TM, int TN, bool D>
 __device__ __forceinline__ void tile_job(char* lds, const uint16_t* __restrict__ X, int64_t k, int64_t ldx,
                                          int64_t rowc0, int64_t colc0, int64_t t_begin, int64_t t_end,
                                          float* __restrict__ H, float* __restrict__ P) {
-  using T = Tile<TM, TN>;
+  using T = Tile<TM, TN, D>;
   const int nstages = t_end > t_begin ? (int)((t_end - t_begin + ST - 1) / ST) : 0;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1;
@@ -276,19 +271,19 @@ __device__ __forceinline__ void tile_job(char* lds, const uint16_t* __restrict__
   bf16x8 a0[T::NI], b0[T::NJ];
   __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
   asm volatile("s_barrier" ::: "memory");
-  read_frags<TM, TN>(lds, 0, aoff, boff, a0, b0);
+  read_frags<TM, TN, D>(lds, 0, aoff, boff, a0, b0);
   // Every step issues one stage of loads, so while the wave waits for stage
   // s+1 the loads of stages s+2..s+NS-1 are the ones it leaves in flight.
   constexpr int kWait = (NS - 2) * T::PER_WAVE;
   static_assert(NS >= 2 && kWait < 64, "ring depth");
   for (int s = 0; s + 1 < nstages; ++s) {
     const int sn = s + NS;
-    pipe_step<TM, TN, kWait, true>(lds + (s % NS) * T::STAGE_BYTES, lds + ((s + 1) % NS) * T::STAGE_BYTES,
+    pipe_step<TM, TN, D, kWait, true>(lds + (s % NS) * T::STAGE_BYTES, lds + ((s + 1) % NS) * T::STAGE_BYTES,
                                    stage_src(sn), stage_nrec(sn), voff, ldsoff, aoff, boff, a0, b0, acc);
   }
   if (nstages > 0) {
     const int s = nstages - 1;
-    pipe_step<TM, TN, kWait, false>(lds + (s % NS) * T::STAGE_BYTES, lds, stage_src(s), 0, voff, ldsoff, aoff, boff,
+    pipe_step<TM, TN, D, kWait, false>(lds + (s % NS) * T::STAGE_BYTES, lds, stage_src(s), 0, voff, ldsoff, aoff, boff,
                                     a0, b0, acc);
   }
 
@@ -442,13 +437,13 @@ __global__ __launch_bounds__(256) void syrk_main_kernel(const uint16_t* __restri
   const int64_t t0 = (int64_t)sp * qtokens, t1 = min(n, t0 + qtokens);
   float* P = qsplit > 1 ? partial + (size_t)L * kSlotFloats : nullptr;
   if (kind == 0) {
-    tile_job<QUAD, QUAD>(lds, X, k, ldx, (int64_t)a * QUAD, (int64_t)b * QUAD, t0, t1, H, P);
+    tile_job<QUAD, QUAD, false>(lds, X, k, ldx, (int64_t)a * QUAD, (int64_t)b * QUAD, t0, t1, H, P);
   } else if (kind == 1) {
     const int64_t te = tail.npairs > 0 ? min(t1, t0 + tail.head) : t1;   // the rest is tail work
-    tile_job<HALF, QUAD>(lds, X, k, ldx, (int64_t)a * QUAD, (int64_t)a * QUAD, t0, te, H, P);
+    tile_job<HALF, QUAD, true>(lds, X, k, ldx, (int64_t)a * QUAD, (int64_t)a * QUAD, t0, te, H, P);
     if (b >= 0) {
       __syncthreads();   // the LDS ring is reused
-      tile_job<HALF, QUAD>(lds, X, k, ldx, (int64_t)b * QUAD, (int64_t)b * QUAD, t0, te, H,
+      tile_job<HALF, QUAD, true>(lds, X, k, ldx, (int64_t)b * QUAD, (int64_t)b * QUAD, t0, te, H,
                            P ? P + HALF * QUAD : nullptr);
     }
   }
@@ -469,7 +464,7 @@ __global__ __launch_bounds__(256) void syrk_single_kernel(const uint16_t* __rest
     const int64_t c0 = (int64_t)a * QUAD + HALF;
     const int64_t t0 = (int64_t)sp * stokens;
     float* P = nsplit > 1 ? partial + (slot_base + (size_t)a * nsplit + sp) * kSlotFloats : nullptr;
-    tile_job<HALF, HALF>(lds, X, k, ldx, c0, c0, t0, min(n, t0 + stokens), H, P);
+    tile_job<HALF, HALF, true>(lds, X, k, ldx, c0, c0, t0, min(n, t0 + stokens), H, P);
     return;
   }
   // Tail piece u: token range sp, strip pair p, piece t (an empty token range
@@ -483,10 +478,10 @@ __global__ __launch_bounds__(256) void syrk_single_kernel(const uint16_t* __rest
   const int64_t ts = min(r1, (int64_t)sp * qtokens + tail.head + (int64_t)t * tail.ttokens);
   const int64_t te = min(r1, ts + tail.ttokens);
   float* P = partial + ((size_t)tail.base + u) * kSlotFloats;
-  tile_job<HALF, QUAD>(lds, X, k, ldx, (int64_t)a * QUAD, (int64_t)a * QUAD, ts, te, H, P);
+  tile_job<HALF, QUAD, true>(lds, X, k, ldx, (int64_t)a * QUAD, (int64_t)a * QUAD, ts, te, H, P);
   if (b >= 0) {
     __syncthreads();   // the LDS ring is reused
-    tile_job<HALF, QUAD>(lds, X, k, ldx, (int64_t)b * QUAD, (int64_t)b * QUAD, ts, te, H, P + HALF * QUAD);
+    tile_job<HALF, QUAD, true>(lds, X, k, ldx, (int64_t)b * QUAD, (int64_t)b * QUAD, ts, te, H, P + HALF * QUAD);
   }
 }
 
