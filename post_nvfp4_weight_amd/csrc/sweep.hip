@@ -465,20 +465,29 @@ __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
         }
       }
       T sc = 0;
+      // Row j of the block's U is read while column j - 1 is encoded, so the
+      // LDS latency hides behind that work (one wave per SIMD runs here).
+      f32x4 un[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) un[q] = *(const f32x4*)&Ud[b][0][4 * q];
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
+        float urow[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          urow[4 * q] = un[q][0]; urow[4 * q + 1] = un[q][1]; urow[4 * q + 2] = un[q][2]; urow[4 * q + 3] = un[q][3];
+        }
+        if (j + 1 < 15) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) un[q] = *(const f32x4*)&Ud[b][j + 1][4 * q];
+          __builtin_amdgcn_sched_barrier(0x7);   // arithmetic may move across, memory accesses may not
+        }
         const int code = e2m1_encode(v[j], s, g);
         T ej;
         if constexpr (F64) ej = (v[j] - e2m1_dequant_f64(code, s, g)) / (T)Ud[b][j][j];
         else ej = (v[j] - e2m1_dequant(code, s, g)) * id_s[c0 + j];
         sc = fma(ej, ej, sc);
         if (j + 1 < 16) {
-          float urow[16];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            f32x4 t = *(const f32x4*)&Ud[b][j][4 * q];
-            urow[4 * q] = t[0]; urow[4 * q + 1] = t[1]; urow[4 * q + 2] = t[2]; urow[4 * q + 3] = t[3];
-          }
 #pragma unroll
           for (int l = j + 1; l < 16; ++l) v[l] = fma(-ej, (T)urow[l], v[l]);
         }
