@@ -248,6 +248,24 @@ __global__ void fill_kernel(float* p, int64_t n, float v) {
   if (i < n) p[i] = v;
 }
 
+// The E2M1 magnitude index e2m1_index returns, found by a three-level search
+// over the midpoints instead of seven tests: the first two levels test odd
+// midpoints (a tie rounds up to the even index), the last an even one (a tie
+// rounds down).  ts[i] = t_i * s for the midpoints t = 0.25, 0.75, 1.25,
+// 1.75, 2.5, 3.5, 5 (exact products); each test is the sign of an fma, as in
+// e2m1_index.
+// (The selections are bit masks: written as conditionals they became branches.)
+__device__ __forceinline__ float pick(uint32_t mask, float a, float b) {   // mask ? a : b, mask all ones or zero
+  return __uint_as_float((__float_as_uint(a) & mask) | (__float_as_uint(b) & ~mask));
+}
+__device__ __forceinline__ int e2m1_index_search(float aw, float g, const float (&ts)[7]) {
+  const uint32_t m2 = 0u - (uint32_t)(fmaf(-ts[3], g, aw) >= 0.0f);
+  const uint32_t m1 = 0u - (uint32_t)(fmaf(-pick(m2, ts[5], ts[1]), g, aw) >= 0.0f);
+  const float t0 = pick(m1, pick(m2, ts[6], ts[2]), pick(m2, ts[4], ts[0]));
+  const uint32_t b0 = fmaf(-t0, g, aw) > 0.0f;
+  return (int)((m2 & 4u) | (m1 & 2u) | b0);
+}
+
 // ---- the sweep of one lazy batch ---------------------------------------------------------
 constexpr int UT_LD = kBatch + 4;
 
@@ -452,6 +470,8 @@ __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
       const int lo = candidate_lo(e4m3_code_of_ratio_any(a, g, r6g), n_cand);
       cand = lo + (ci < n_cand ? ci : 0);
       const float s = e4m3_value(cand);
+      const float hs = 0.5f * s;
+      const float ts[7] = {0.25f * s, 0.75f * s, 1.25f * s, 1.75f * s, 2.5f * s, 3.5f * s, 5.0f * s};
       // Block-independent selection: the plain squared rounding error of the
       // block's weights at the block start, each rounded on its own.
       T isc = 0;
@@ -482,10 +502,24 @@ __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
           for (int q = 0; q < 4; ++q) un[q] = *(const f32x4*)&Ud[b][j + 1][4 * q];
           __builtin_amdgcn_sched_barrier(0x7);   // arithmetic may move across, memory accesses may not
         }
-        const int code = e2m1_encode(v[j], s, g);
+        int code;
         T ej;
-        if constexpr (F64) ej = (v[j] - e2m1_dequant_f64(code, s, g)) / (T)Ud[b][j][j];
-        else ej = (v[j] - e2m1_dequant(code, s, g)) * id_s[c0 + j];
+        if constexpr (F64) {
+          code = e2m1_encode(v[j], s, g);
+          ej = (v[j] - e2m1_dequant_f64(code, s, g)) / (T)Ud[b][j][j];
+        } else {
+          // The dequantized value e2m1_dequant gives, fl32(m * g) with the code's
+          // sign set by a bit operation (m * g >= 0), then the error.  The
+          // product and the difference are rounded separately (no contraction
+          // into one fma).
+#pragma clang fp contract(off)
+          const float aw = fabsf(v[j]);
+          const int idx = e2m1_index_search(aw, g, ts);
+          code = idx | (int)(((__float_as_uint(v[j]) >> 31) & (uint32_t)(idx != 0)) << 3);
+          const float mg = e2m1_twice_mag(idx) * hs * g;
+          const float dq = __uint_as_float(__float_as_uint(mg) | ((uint32_t)(code & 8) << 28));
+          ej = (v[j] - dq) * id_s[c0 + j];
+        }
         sc = fma(ej, ej, sc);
         if (j + 1 < 16) {
 #pragma unroll
