@@ -79,6 +79,24 @@ __device__ __forceinline__ int e2m1_index(float aw, float s, float g) {
   return idx;
 }
 
+// The E2M1 magnitude index e2m1_index returns, found by a three-level search
+// over the midpoints instead of seven tests: the first two levels test odd
+// midpoints (a tie rounds up to the even index), the last an even one (a tie
+// rounds down).  ts[i] = t_i * s for the midpoints t = 0.25, 0.75, 1.25,
+// 1.75, 2.5, 3.5, 5 (exact products); each test is the sign of an fma, as in
+// e2m1_index.
+// (The selections are bit masks: written as conditionals they became branches.)
+__device__ __forceinline__ float pick(uint32_t mask, float a, float b) {   // mask ? a : b, mask all ones or zero
+  return __uint_as_float((__float_as_uint(a) & mask) | (__float_as_uint(b) & ~mask));
+}
+__device__ __forceinline__ int e2m1_index_search(float aw, float g, const float (&ts)[7]) {
+  const uint32_t m2 = 0u - (uint32_t)(fmaf(-ts[3], g, aw) >= 0.0f);
+  const uint32_t m1 = 0u - (uint32_t)(fmaf(-pick(m2, ts[5], ts[1]), g, aw) >= 0.0f);
+  const float t0 = pick(m1, pick(m2, ts[6], ts[2]), pick(m2, ts[4], ts[0]));
+  const uint32_t b0 = fmaf(-t0, g, aw) > 0.0f;
+  return (int)((m2 & 4u) | (m1 & 2u) | b0);
+}
+
 // Twice the E2M1 magnitude of index idx: 0,1,2,3,4,6,8,12 packed in nibbles.
 __device__ __forceinline__ float e2m1_twice_mag(int idx) {
   return (float)((0xC8643210u >> (4 * idx)) & 0xFu);

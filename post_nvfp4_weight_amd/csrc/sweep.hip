@@ -172,12 +172,17 @@ __global__ __launch_bounds__(256) void rtn_kernel(const void* __restrict__ W, in
     for (int ci = 0; ci < n_cand; ++ci) {
       const int c = lo + ci;
       const float s = e4m3_value(c);
+      const float hs = 0.5f * s;
+      const float ts[7] = {0.25f * s, 0.75f * s, 1.25f * s, 1.75f * s, 2.5f * s, 3.5f * s, 5.0f * s};
       float score = 0.0f;
       uint32_t plo = 0, phi = 0;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        int code = e2m1_encode(w[j], s, g);
-        float e = __fsub_rn(w[j], e2m1_dequant(code, s, g));
+        // e2m1_encode and e2m1_dequant's values, with the sign set by bit operations
+        const int idx = e2m1_index_search(fabsf(w[j]), g, ts);
+        const int code = idx | (int)(((__float_as_uint(w[j]) >> 31) & (uint32_t)(idx != 0)) << 3);
+        const float dq = __uint_as_float(__float_as_uint(e2m1_twice_mag(idx) * hs * g) | ((uint32_t)(code & 8) << 28));
+        float e = __fsub_rn(w[j], dq);
         score = __fadd_rn(score, __fmul_rn(e, e));
         if (j < 8) plo |= (uint32_t)code << (4 * j); else phi |= (uint32_t)code << (4 * (j - 8));
       }
@@ -246,24 +251,6 @@ __global__ void row_sum_kernel(const float* __restrict__ P, int64_t m, int64_t n
 __global__ void fill_kernel(float* p, int64_t n, float v) {
   int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i < n) p[i] = v;
-}
-
-// The E2M1 magnitude index e2m1_index returns, found by a three-level search
-// over the midpoints instead of seven tests: the first two levels test odd
-// midpoints (a tie rounds up to the even index), the last an even one (a tie
-// rounds down).  ts[i] = t_i * s for the midpoints t = 0.25, 0.75, 1.25,
-// 1.75, 2.5, 3.5, 5 (exact products); each test is the sign of an fma, as in
-// e2m1_index.
-// (The selections are bit masks: written as conditionals they became branches.)
-__device__ __forceinline__ float pick(uint32_t mask, float a, float b) {   // mask ? a : b, mask all ones or zero
-  return __uint_as_float((__float_as_uint(a) & mask) | (__float_as_uint(b) & ~mask));
-}
-__device__ __forceinline__ int e2m1_index_search(float aw, float g, const float (&ts)[7]) {
-  const uint32_t m2 = 0u - (uint32_t)(fmaf(-ts[3], g, aw) >= 0.0f);
-  const uint32_t m1 = 0u - (uint32_t)(fmaf(-pick(m2, ts[5], ts[1]), g, aw) >= 0.0f);
-  const float t0 = pick(m1, pick(m2, ts[6], ts[2]), pick(m2, ts[4], ts[0]));
-  const uint32_t b0 = fmaf(-t0, g, aw) > 0.0f;
-  return (int)((m2 & 4u) | (m1 & 2u) | b0);
 }
 
 // ---- the sweep of one lazy batch ---------------------------------------------------------
