@@ -684,9 +684,21 @@ SyrkPlan plan(int64_t n, int64_t k, int cus) {
 
 }  // namespace
 
+// An upper bound of the plan's slots that does not decrease with n, since
+// callers size one workspace for several token counts (groups, chunks): the
+// singles' splits as if there were no tail pieces, plus every tail piece the
+// token splits allow.
 size_t syrk_bf16_workspace(int64_t n, int64_t k) {
-  SyrkPlan p = plan(n, k, num_cus());
-  return p.slots * kSlotFloats * sizeof(float);
+  const int cus = num_cus();
+  SyrkPlan p = plan(n, k, cus);
+  size_t slots = 0;
+  if (p.qsplit > 1) slots += ((size_t)p.per_range + (size_t)pairs_per_range(p.nb2) * TSPLIT) * p.qsplit;
+  if (p.nsingle > 0 && p.nsingle < cus) {
+    const int64_t nstages = n > ST ? (n + ST - 1) / ST : 1;
+    const int64_t sp = cus / p.nsingle < nstages ? cus / p.nsingle : nstages;
+    if (sp > 1) slots += (size_t)p.nsingle * sp;
+  }
+  return (slots > p.slots ? slots : p.slots) * kSlotFloats * sizeof(float);
 }
 
 hipError_t syrk_bf16(const uint16_t* X, int64_t n, int64_t k, int64_t ldx, float* H, void* ws, hipStream_t s) {

@@ -109,3 +109,18 @@ def test_workspace_queries_are_consistent():
     assert ws >= 2 * 1000 * 256 * 2 + lib.hessian_workspace_size(1000, 256, 1)
     assert lib.hessian_host_staging_size(1000, 256, 1) >= 2 * 1000 * 256 * 2
     assert lib.hessian_host_staging_size(1000, 256, 0) >= 2 * 1000 * 256 * 4
+
+
+def test_hessian_workspace_never_shrinks_as_tokens_grow():
+    """One workspace serves every smaller token count (groups of a grouped call,
+    the last chunk of a streamed one), so the bf16 Hessian's workspace size
+    must not decrease with n: checked over channel counts whose tile plans
+    switch strip-pair tail pieces on at different token counts."""
+    import post_nvfp4_weight_amd as nvq
+    lib = nvq.lib
+    for k in (128, 400, 1024, 2320, 2560, 3072, 4096, 4608, 6144):
+        prev = 0
+        for n in list(range(1, 2400, 13)) + [4096, 8191, 65536, 262144]:
+            ws = lib.hessian_workspace_size(n, k, 1)
+            assert ws >= prev, (k, n, ws, prev)
+            prev = ws
