@@ -178,7 +178,7 @@ def consumer_bench(nvq, Wd, Xd):
     codes, scales, g = res["codes"], res["scales"], res["g"]
     Wdq = nvq.nvfp4_dequantize(codes, scales, g, torch.bfloat16)
     out = []
-    for T in (16, 256, 2048, 8192):
+    for T in (1, 16, 32, 256, 2048, 8192):
         X = Xd[:T].contiguous()
 
         def timed(fn, reps=20):

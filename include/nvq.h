@@ -308,7 +308,10 @@ int nvfp4_dequantize(const uint8_t* codes, const uint8_t* scales, const float* g
  *   ws      device workspace of nvfp4_gemm_workspace_size(T, k, m) bytes
  *           (256-aligned; may be NULL when that is 0): for few tokens k is
  *           split over workgroups and the fp32 partial sums are added in
- *           split order, so results do not depend on timing.
+ *           split order, so results do not depend on timing.  (With at most
+ *           32 tokens, k % 128 == 0 and codes 16-byte aligned, one workgroup
+ *           sums all of k for 16 output channels and the workspace is not
+ *           touched.)
  */
 size_t nvfp4_gemm_workspace_size(int64_t T, int64_t k, int64_t m);
 int nvfp4_gemm(const void* X, int x_dtype, int64_t T, int64_t k, int64_t ldx, const uint8_t* codes,

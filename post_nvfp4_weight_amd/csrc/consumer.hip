@@ -182,6 +182,89 @@ __global__ void nvfp4_gemm_reduce_kernel(const float* __restrict__ P, int nsplit
   else ((float*)Y)[row * ldy + col] = v;
 }
 
+// ---- few tokens (T <= 32): decode-sized products ------------------------------
+// These are bound by reading the weights once, so the loads are spread wide
+// and issued together.  A workgroup of 16 waves takes 16 output channels over
+// all of k (k a multiple of 128); wave w takes chunks w, w + 16, ... of 128 k,
+// two at a time.  v_mfma_f32_16x16x32_bf16: A = 16 tokens x 32 k, B = 32 k x
+// 16 channels.  In a chunk, lane (c = l % 16, q = l / 16) supplies the 32
+// consecutive k 32 q .. 32 q + 31 of the chunk over its four MFMAs, 8 per
+// MFMA, for channel c (B) and token c of each 16-token group (A): both
+// operands take the same k, so the four MFMAs sum every k of the chunk once
+// (the order of the k inside a sum is free).  A lane's 32 codes are one
+// 16-byte load and its two block scales one 2-byte load.  The waves' 16 x 16
+// partial tiles are summed in wave order through LDS.
+constexpr int GV_W = 16;   // waves per workgroup
+typedef float f32x4c __attribute__((ext_vector_type(4)));
+template <int NTG, int OUT>
+__global__ __launch_bounds__(1024) void nvfp4_gemv_kernel(const uint16_t* __restrict__ X, int64_t T, int64_t k,
+                                                          int64_t ldx, const uint8_t* __restrict__ codes,
+                                                          const uint8_t* __restrict__ scales,
+                                                          const float* __restrict__ gptr, int64_t m,
+                                                          void* __restrict__ Y, int64_t ldy) {
+  __shared__ float red[GV_W][NTG][16][17];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = lane & 15, q = lane >> 4;
+  const int64_t o0 = (int64_t)blockIdx.x * 16;
+  const int64_t orow = min(o0 + c, m - 1);
+  const int64_t nch = k / 128;
+  f32x4c acc[NTG];
+#pragma unroll
+  for (int tg = 0; tg < NTG; ++tg) acc[tg] = f32x4c{0.f, 0.f, 0.f, 0.f};
+  for (int64_t base = wave; base < nch; base += 2 * GV_W) {
+    u32x4 cw[2], xa[2][NTG][4];
+    uint32_t sw[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int64_t ch = base + u * GV_W;
+      const bool ok = ch < nch;
+      const int64_t kk = (ok ? ch : 0) * 128 + 32 * q;   // the lane's first k in the chunk
+      cw[u] = ok ? *(const u32x4*)(codes + orow * (k / 2) + kk / 2) : u32x4{0u, 0u, 0u, 0u};
+      sw[u] = ok ? (uint32_t)*(const uint16_t*)(scales + orow * (k / 16) + kk / 16) : 0u;
+#pragma unroll
+      for (int tg = 0; tg < NTG; ++tg) {
+        const int64_t t = tg * 16 + c;
+        const bool tok = ok && t < T;
+        const uint16_t* xr = X + min(t, T - 1) * ldx + kk;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xa[u][tg][j] = tok ? *(const u32x4*)(xr + 8 * j) : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        // codes of k 8 j .. 8 j + 7 of the lane's 32, under the scale of their 16-block
+        const float sc = scale_value((j < 2 ? sw[u] : sw[u] >> 8) & 0x7F);
+        const uint32_t w = cw[u][j];
+        const u32x4 bq{dq_byte<0>(w, sc), dq_byte<1>(w, sc), dq_byte<2>(w, sc), dq_byte<3>(w, sc)};
+        const bf16x8 b = __builtin_bit_cast(bf16x8, bq);
+#pragma unroll
+        for (int tg = 0; tg < NTG; ++tg)
+          acc[tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, xa[u][tg][j]), b, acc[tg],
+                                                            0, 0, 0);
+      }
+  }
+  // Accumulator register r of lane l: token 4 (l / 16) + r, channel l % 16.
+#pragma unroll
+  for (int tg = 0; tg < NTG; ++tg)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[wave][tg][4 * q + r][c] = acc[tg][r];
+  __syncthreads();
+  if (tid < NTG * 256) {
+    const int tg = tid >> 8, rr = (tid >> 4) & 15, cc = tid & 15;
+    float sum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < GV_W; ++w) sum += red[w][tg][rr][cc];
+    const int64_t t = tg * 16 + rr, o = o0 + cc;
+    if (t < T && o < m) {
+      const float v = sum * *gptr;
+      if (OUT == 1) ((__bf16*)Y)[t * ldy + o] = (__bf16)v;
+      else ((float*)Y)[t * ldy + o] = v;
+    }
+  }
+}
+
 // ---- many tokens: 256 x 256 tiles ----------------------------------------------
 // 256 (tokens) x 256 (output channels) per workgroup, four waves of 128 x 128
 // (16 accumulators of 32 x 32), k in steps of 32 (k a multiple of 32).  A wave
@@ -390,6 +473,19 @@ hipError_t nvfp4_gemm_launch(const uint16_t* X, int64_t T, int64_t k, int64_t ld
                              const uint8_t* scales, const float* g, int64_t m, void* Y, int out_bf16, int64_t ldy,
                              float* ws, hipStream_t s) {
   if (T <= 0 || m <= 0) return hipSuccess;
+  if (T <= 32 && k % 128 == 0 && (uintptr_t)codes % 16 == 0 && (uintptr_t)scales % 2 == 0 &&
+      (uintptr_t)X % 16 == 0 && ldx % 8 == 0) {
+    // Decode-sized: one workgroup per 16 output channels (no workspace).
+    const dim3 grid((unsigned)((m + 15) / 16));
+    if (T <= 16) {
+      if (out_bf16) hipLaunchKernelGGL((nvfp4_gemv_kernel<1, 1>), grid, dim3(1024), 0, s, X, T, k, ldx, codes, scales, g, m, Y, ldy);
+      else hipLaunchKernelGGL((nvfp4_gemv_kernel<1, 0>), grid, dim3(1024), 0, s, X, T, k, ldx, codes, scales, g, m, Y, ldy);
+    } else {
+      if (out_bf16) hipLaunchKernelGGL((nvfp4_gemv_kernel<2, 1>), grid, dim3(1024), 0, s, X, T, k, ldx, codes, scales, g, m, Y, ldy);
+      else hipLaunchKernelGGL((nvfp4_gemv_kernel<2, 0>), grid, dim3(1024), 0, s, X, T, k, ldx, codes, scales, g, m, Y, ldy);
+    }
+    return hipGetLastError();
+  }
   if (k % BK == 0 && (uintptr_t)codes % 16 == 0 && (uintptr_t)scales % 2 == 0 &&
       ((T + BT - 1) / BT) * ((m + BT - 1) / BT) >= num_cus_consumer()) {
     // Enough 256 x 256 tiles for every CU (k a multiple of 32, codes 16-byte and

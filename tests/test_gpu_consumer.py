@@ -39,11 +39,15 @@ def _layer(m, k, T, seed):
     return X, packed, scales, g
 
 
-# The last three cases have a 256 x 256 tile per CU: the first two take the
-# many-token kernel (k a multiple of 32), aligned, and ragged in T and m with
-# an odd number of 32-deep k steps (k = 544); k = 528 takes the other kernel.
-@pytest.mark.parametrize("T,m,k", [(1, 64, 16), (37, 100, 48), (300, 256, 1024), (129, 130, 2064), (512, 512, 4096),
-                                   (4096, 4096, 512), (4000, 4100, 544), (4000, 4100, 528)])
+# Cases 2-6 (at most 32 tokens, k a multiple of 128) take the decode-sized
+# kernel: one and two 16-token groups, ragged T and m, one to 32 chunks of
+# 128 k.  The last three cases have a 256 x 256 tile per CU: the first two
+# take the many-token kernel (k a multiple of 32), aligned, and ragged in T
+# and m with an odd number of 32-deep k steps (k = 544); k = 528 takes the
+# general kernel, as do the rest.
+@pytest.mark.parametrize("T,m,k", [(1, 64, 16), (1, 64, 128), (16, 1024, 4096), (5, 100, 1024), (17, 130, 384),
+                                   (32, 48, 2048), (37, 100, 48), (300, 256, 1024), (129, 130, 2064),
+                                   (512, 512, 4096), (4096, 4096, 512), (4000, 4100, 544), (4000, 4100, 528)])
 def test_gemm_matches_oracle(nvq, T, m, k):
     X, packed, scales, g = _layer(m, k, T, seed=T)
     Xd = synth.to_bf16_tensor(X).to(DEV)
