@@ -9,10 +9,13 @@
 // Q = e2m1 * e4m3.  Against X fl32(Q g)^T this differs by at most 2^-24 of
 // each product.
 //
-// Tiles are 128 (tokens) x 128 (output channels), four waves of 64 x 64, k in
-// steps of 64 (four NVFP4 blocks); both operands are kept [row][k] in LDS
-// (k contiguous, rows padded to 72 elements) and double-buffered; the next
-// step's loads are in flight while the current step is multiplied.
+// Three kernels share this: a decode-sized one for at most 32 tokens, a
+// large-tile one when there is a 256 x 256 tile per CU (both further below),
+// and the general one.  Its tiles are 128 (tokens) x 128 (output channels),
+// four waves of 64 x 64, k in steps of 64 (four NVFP4 blocks); both operands
+// are kept [row][k] in LDS (k contiguous, rows padded to 72 elements) and
+// double-buffered; the next step's loads are in flight while the current
+// step is multiplied.
 #include <algorithm>
 
 #include "common.h"

@@ -9,14 +9,18 @@
 //           128-block plus the 128x128 block right of it; waves 64x128);
 //   single  128x128: the bottom-right diagonal 128-block of a diagonal
 //           256-block (waves 64x64).
-// A quad moves 512 channels per token for 65536 products, a strip 384 for
-// 32768: the big tile halves the load traffic per flop.  The first launch
-// runs quads and strip pairs (two strips one after the other: the same work
-// as a quad), split over token ranges until there is an item per CU (for a
-// 4096-channel layer: 2 ranges x (120 quads + 8 strip pairs) = 256 items).
-// Items are ordered so that each XCD holds one token range and a compact
-// group of tiles, which keeps most operand reads inside its L2.  The small
-// singles follow in a second launch, split over tokens.  Split tiles write
+// A quad moves 512 channels per token for 65536 products.  Strips and
+// singles lie on the diagonal (their rows are the first of their columns), so
+// they load only their columns' channels and read both operands from them:
+// 256 channels for 32768 products, and 128 for 16384.  The first launch runs
+// quads and strip pairs (two strips one after the other), split over token
+// ranges until there is an item per CU (for a 4096-channel layer: 2 ranges x
+// (120 quads + 8 strip pairs) = 256 items).  A strip pair still takes longer
+// than a quad (half its products per LDS read and per barrier), so it covers
+// only the head of its range there; the rest of the range runs as pieces in
+// the second launch, beside the singles, which are split over tokens.  Items
+// are ordered so that each XCD holds one token range and a compact group of
+// tiles, which keeps most operand reads inside its L2.  Split tiles write
 // partial sums to the workspace, summed in a fixed order by a reduction
 // kernel, so results are reproducible.
 //
@@ -379,10 +383,11 @@ __host__ __device__ inline int items_per_range(int nb2) {
 __host__ __device__ inline int pairs_per_range(int nb2) { return items_per_range(nb2) - nb2 * (nb2 - 1) / 2; }
 
 // Strip-pair tails.  With token splits every first-launch item covers one
-// token range, but a strip pair moves 1.5 times the bytes per product of a
-// quad and would finish last.  So it covers only the first `head` tokens of
-// its range there, and the rest of the range is cut into tsplit pieces that
-// run in the second launch beside the singles (npairs == 0: no tails).
+// token range, but a strip pair takes longer than a quad (half a quad's
+// products per LDS read and per barrier) and would finish last.  So it covers
+// only the first `head` tokens of its range there, and the rest of the range
+// is cut into tsplit pieces that run in the second launch beside the singles
+// (npairs == 0: no tails).
 struct TailArgs {
   int npairs;        // strip-pair items per range
   int tsplit;        // pieces per (range, pair)
@@ -420,8 +425,8 @@ __device__ __forceinline__ int xcd_logical(int id, int G) {
 }
 
 // Launch 1: G = qsplit * per_range items; logical item L covers token range
-// L / per_range and item L % per_range of the order above.  A quad over one
-// range and a strip pair over one range are equal work.  With qsplit > 1 the
+// L / per_range and item L % per_range of the order above (a strip pair only
+// the head of the range when there are tail pieces).  With qsplit > 1 the
 // item's partial sums go to slot L (a strip pair's two 128x256 strips fill
 // the two halves of the slot).
 __global__ __launch_bounds__(256) void syrk_main_kernel(const uint16_t* __restrict__ X, int64_t n, int64_t k,
