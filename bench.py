@@ -241,7 +241,8 @@ def main():
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: the per-layer path is a single-GPU workload here "
-              "(rows of W shard across ranks with no exchange; see DESIGN.md). Use --gpus 1.", file=sys.stderr)
+              "(several GPUs would split the tokens of the Hessian, all-reduce H, and split the rows of W, "
+              "which need no exchange). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
     import torch
