@@ -115,7 +115,10 @@ def _hessian_check(H_gpu, X, n):
     assert np.all(np.abs(H_gpu - ref) <= bound + 1e-30)
 
 
-@pytest.mark.parametrize("n,k", [(3000, 400), (700, 256), (64, 128), (5000, 1024), (1500, 2320), (777, 4096)])
+# (1500, 2320), (777, 4096), (4127, 3072) and (2000, 2048) split the strip
+# pairs' token ranges into tail pieces (with ragged and empty pieces).
+@pytest.mark.parametrize("n,k", [(3000, 400), (700, 256), (64, 128), (5000, 1024), (1500, 2320), (777, 4096),
+                                 (4127, 3072), (2000, 2048)])
 def test_hessian_bf16(nvq, n, k):
     X = synth.activations("attn_proj", n, k, massive=4)
     Xt = synth.to_bf16_tensor(X).to(DEV)
