@@ -395,22 +395,30 @@ struct TailArgs {
   int64_t ttokens;   // tokens per piece
   int64_t base;      // first partial slot of the pieces, ordered by (range, pair, piece)
 };
-// Item index (within a range) of the p-th strip pair, and the pair number of item r.
-__device__ inline int pair_item(int p, int nb2) {
-  const int per = items_per_range(nb2);
-  for (int r = 0, q = 0; r < per; ++r) {
-    int kind, a, b;
-    item_coords(r, nb2, kind, a, b);
-    if (kind == 1 && q++ == p) return r;
+// Item index (within a range) of the p-th strip pair, and the pair number of
+// item r (the number of pairs before it), from the order of item_coords: per
+// super-block, its quads, its pairs, then its quads against later ones.
+__host__ __device__ inline int pair_item(int p, int nb2) {
+  int base = 0;
+  for (int a0 = 0; a0 < nb2; a0 += SB) {
+    const int na = min(SB, nb2 - a0), nq = na * (na - 1) / 2, np = (na + 1) / 2;
+    if (p < np) return base + nq + p;
+    p -= np;
+    base += nq + np + na * (nb2 - a0 - na);
   }
   return 0;
 }
-__device__ inline int pair_of_item(int r, int nb2) {
-  int q = 0;
-  for (int i = 0; i < r; ++i) {
-    int kind, a, b;
-    item_coords(i, nb2, kind, a, b);
-    q += kind == 1;
+__host__ __device__ inline int pair_of_item(int r, int nb2) {
+  int q = 0, base = 0;
+  for (int a0 = 0; a0 < nb2; a0 += SB) {
+    const int na = min(SB, nb2 - a0), nq = na * (na - 1) / 2, np = (na + 1) / 2;
+    const int len = nq + np + na * (nb2 - a0 - na);
+    if (r < base + len) {
+      const int x = r - base - nq;
+      return q + (x < 0 ? 0 : min(x, np));
+    }
+    q += np;
+    base += len;
   }
   return q;
 }
