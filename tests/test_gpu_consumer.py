@@ -73,9 +73,27 @@ def test_gemm_strided_activations(nvq):
     assert np.all(np.abs(Y - ref) <= _bound(X, packed, scales, g) + 1e-30)
 
 
-def test_gemm_after_library_quantization(nvq):
-    # quantize a layer with the whole library path, then use it
-    m, k, n, T = 256, 512, 4096, 64
+def test_gemm_decode_strided_activations(nvq):
+    # The decode-sized kernel (at most 32 tokens, k a multiple of 128) with
+    # activation rows padded (ldx > k), ragged m, five 128-deep chunks.
+    T, m, k = 9, 96 + 7, 640
+    X, packed, scales, g = _layer(m, k, T, seed=7)
+    wide = torch.zeros(T, k + 64, dtype=torch.bfloat16)
+    wide[:, :k] = synth.to_bf16_tensor(X)
+    Xd = wide.to(DEV)[:, :k]
+    args = (torch.from_numpy(packed).to(DEV), torch.from_numpy(scales).to(DEV),
+            torch.tensor([g], dtype=torch.float32, device=DEV))
+    ref = consumer.weight_only_matmul(X, packed, scales, g)
+    Y = nvq.nvfp4_gemm(Xd, *args).cpu().numpy()
+    assert np.all(np.abs(Y - ref) <= _bound(X, packed, scales, g) + 1e-30)
+    Yb = nvq.nvfp4_gemm(Xd, *args, out_dtype=torch.bfloat16).float().cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(Yb - ref) <= _bound(X, packed, scales, g) + np.abs(ref) * 2.0 ** -8 + 1e-30)
+
+
+@pytest.mark.parametrize("T", [64, 8])
+def test_gemm_after_library_quantization(nvq, T):
+    # quantize a layer with the whole library path, then use it (8 tokens: the decode-sized kernel)
+    m, k, n = 256, 512, 4096
     W, Xc = synth.attn_proj_layer(m, k, n)
     res = nvq.quantize_layer(synth.to_bf16_tensor(W).to(DEV), synth.to_bf16_tensor(Xc).to(DEV), n_cand=16)
     X = Xc[:T]
