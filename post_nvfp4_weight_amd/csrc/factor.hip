@@ -26,8 +26,17 @@ __global__ __launch_bounds__(256) void damping_kernel(const float* __restrict__ 
                                                       float* __restrict__ lam_ws, float* __restrict__ lam_out,
                                                       int32_t* __restrict__ info) {
   __shared__ float red[256];
+  // Eight diagonal loads in flight at a time, added in the same order.
   float s = 0.0f;
-  for (int64_t i = threadIdx.x; i < k; i += 256) s += H[i * k + i];
+  int64_t i = threadIdx.x;
+  for (; i + 7 * 256 < k; i += 8 * 256) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = H[(i + u * 256) * k + (i + u * 256)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; i < k; i += 256) s += H[i * k + i];
   red[threadIdx.x] = s;
   __syncthreads();
   for (int w = 128; w > 0; w >>= 1) {
@@ -374,9 +383,10 @@ __global__ void flip_out_kernel(const float* __restrict__ Linv, int64_t k, float
   U[i * k + j] = (j >= i) ? Linv[(k - 1 - i) * k + (k - 1 - j)] : 0.0f;
 }
 
-__global__ void zero_kernel(float* p, int64_t n) {
+// p[0 .. 4 n4) = 0 in 16-byte stores (p 16-byte aligned).
+__global__ void zero_kernel(float* p, int64_t n4) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0.0f;
+  if (i < n4) ((f32x4*)p)[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 }
 
 }  // namespace
@@ -394,8 +404,9 @@ hipError_t factor_hinv_launch(const float* H, int64_t k, float damp_rel, float* 
   float* lam = T + (size_t)k * k / 2;
 
   hipLaunchKernelGGL(damping_kernel, dim3(1), dim3(256), 0, s, H, k, damp_rel, lam, lambda_out, info);
-  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)(((size_t)k * k + 255) / 256)), dim3(256), 0, s, Linv,
-                     (int64_t)k * k);
+  // k % 16 == 0, so k * k is a multiple of 4 (and Linv, k * k floats into the workspace, is 16-byte aligned).
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)(((size_t)k * k / 4 + 255) / 256)), dim3(256), 0, s, Linv,
+                     (int64_t)k * k / 4);
   hipLaunchKernelGGL(flip_damp_kernel, dim3((unsigned)((k + 255) / 256), (unsigned)k), dim3(256), 0, s, H, k,
                      lam, A);
   hipError_t e = hipGetLastError();
