@@ -107,8 +107,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
   else if (p.kmode == kGemmKLowerB) { tn = lin / mt; tm = lin % mt; }
   else if (p.kmode == kGemmKLowerA) { tm = mt - 1 - lin / nt; tn = lin % nt; }
   if (LOWER && tn > tm) return;
-  // [buffer][A | B] operand tiles; reused by the row-dot epilogue.
-  __shared__ __attribute__((aligned(16))) float smem[2 * 2 * OPER];
+  // [buffer][A | B] operand tiles; reused by the row-dot epilogue.  64-wide
+  // tiles have four buffers (see the short-k path below).
+  constexpr int NBUF = T == 64 ? 4 : 2;
+  __shared__ __attribute__((aligned(16))) float smem[NBUF * 2 * OPER];
   constexpr bool AK = !TA;   // A stored [M][K]: k contiguous
   constexpr bool BKM = TB;   // B stored [N][K]: k contiguous
 
@@ -173,22 +175,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
   if (p.kmode == kGemmKSymUpperB) khi = min(p.K, p.noff + n0 + BN);
   const int64_t c0 = klo / BK, nk = (khi + BK - 1) / BK;
   const bool sym = p.kmode == kGemmKSymUpperB;
-  f32x4 ra[LQ], rb[LQ];
-  if (c0 < nk) {
-    load_tile<T, AK>(A, p.lda, m0, p.M, c0 * BK, p.K, tid, ra);
-    load_tile<T, BKM>(B, p.ldb, n0, p.N, c0 * BK, p.K, tid, rb);
-    if (sym) sym_upper<T, BKM>(rb, tid, c0 * BK, p.noff + n0);
-    store_tile<T, AK>(smem, tid, ra, alpha_a);
-    store_tile<T, BKM>(smem + OPER, tid, rb);
-  }
-  __syncthreads();
-  for (int64_t c = c0; c < nk; ++c) {
-    const int cur = (int)((c - c0) & 1);
-    if (c + 1 < nk) {
-      load_tile<T, AK>(A, p.lda, m0, p.M, (c + 1) * BK, p.K, tid, ra);
-      load_tile<T, BKM>(B, p.ldb, n0, p.N, (c + 1) * BK, p.K, tid, rb);
-    }
-    const float* As = smem + cur * 2 * OPER;
+  // The products of one chunk of BK k-values from the operand tiles at As.
+  auto mma_chunk = [&](const float* As) {
     const float* Bs = As + OPER;
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 2) {
@@ -204,13 +192,61 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
         for (int j = 0; j < NI; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j], 0, 0, 0);
     }
-    if (c + 1 < nk) {
-      float* nxt = smem + (cur ^ 1) * 2 * OPER;
-      if (sym) sym_upper<T, BKM>(rb, tid, (c + 1) * BK, p.noff + n0);
-      store_tile<T, AK>(nxt, tid, ra, alpha_a);
-      store_tile<T, BKM>(nxt + OPER, tid, rb);
+  };
+  bool done = false;
+  if constexpr (T == 64) {
+    if (nk > c0 && nk - c0 <= NBUF) {
+      // At most four chunks (the lazy batch updates, K = 128): with one chunk
+      // of look-ahead each chunk would wait for its own loads, so all of them
+      // are loaded together (chunks past the end repeat the last, unused),
+      // stored, and then multiplied in chunk order, as in the loop below.
+      f32x4 ra4[NBUF][LQ], rb4[NBUF][LQ];
+#pragma unroll
+      for (int u = 0; u < NBUF; ++u) {
+        const int64_t cu = min(c0 + u, nk - 1);
+        load_tile<T, AK>(A, p.lda, m0, p.M, cu * BK, p.K, tid, ra4[u]);
+        load_tile<T, BKM>(B, p.ldb, n0, p.N, cu * BK, p.K, tid, rb4[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < NBUF; ++u)
+        if (c0 + u < nk) {
+          if (sym) sym_upper<T, BKM>(rb4[u], tid, (c0 + u) * BK, p.noff + n0);
+          store_tile<T, AK>(smem + u * 2 * OPER, tid, ra4[u], alpha_a);
+          store_tile<T, BKM>(smem + u * 2 * OPER + OPER, tid, rb4[u]);
+        }
+      __syncthreads();
+#pragma unroll
+      for (int u = 0; u < NBUF; ++u)
+        if (c0 + u < nk) mma_chunk(smem + u * 2 * OPER);
+      __syncthreads();
+      done = true;
+    }
+  }
+  f32x4 ra[LQ], rb[LQ];
+  if (!done) {
+    if (c0 < nk) {
+      load_tile<T, AK>(A, p.lda, m0, p.M, c0 * BK, p.K, tid, ra);
+      load_tile<T, BKM>(B, p.ldb, n0, p.N, c0 * BK, p.K, tid, rb);
+      if (sym) sym_upper<T, BKM>(rb, tid, c0 * BK, p.noff + n0);
+      store_tile<T, AK>(smem, tid, ra, alpha_a);
+      store_tile<T, BKM>(smem + OPER, tid, rb);
     }
     __syncthreads();
+    for (int64_t c = c0; c < nk; ++c) {
+      const int cur = (int)((c - c0) & 1);
+      if (c + 1 < nk) {
+        load_tile<T, AK>(A, p.lda, m0, p.M, (c + 1) * BK, p.K, tid, ra);
+        load_tile<T, BKM>(B, p.ldb, n0, p.N, (c + 1) * BK, p.K, tid, rb);
+      }
+      mma_chunk(smem + cur * 2 * OPER);
+      if (c + 1 < nk) {
+        float* nxt = smem + (cur ^ 1) * 2 * OPER;
+        if (sym) sym_upper<T, BKM>(rb, tid, (c + 1) * BK, p.noff + n0);
+        store_tile<T, AK>(nxt, tid, ra, alpha_a);
+        store_tile<T, BKM>(nxt + OPER, tid, rb);
+      }
+      __syncthreads();
+    }
   }
 
   if (EPI == kEpiAxpby) {
