@@ -52,13 +52,23 @@ __global__ __launch_bounds__(256) void damping_kernel(const float* __restrict__ 
 }
 
 // A[i][j] = H[k-1-i][k-1-j] + lam * (i == j), lower triangle (reads H's upper triangle).
+// Four columns j .. j+3 per thread, 16-byte loads and stores (k % 4 == 0):
+// H's elements (k-1-i, k-4-j .. k-1-j) in reverse order.
 __global__ void flip_damp_kernel(const float* __restrict__ H, int64_t k, const float* __restrict__ lam,
                                  float* __restrict__ A) {
-  int64_t i = blockIdx.y, j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t i = blockIdx.y, j = 4 * ((int64_t)blockIdx.x * blockDim.x + threadIdx.x);
   if (j > i || j >= k) return;
-  float v = H[(k - 1 - i) * k + (k - 1 - j)];
-  if (i == j) v += *lam;
-  A[i * k + j] = v;
+  const f32x4 h = *(const f32x4*)(H + (k - 1 - i) * k + (k - 4 - j));
+  f32x4 v = f32x4{h[3], h[2], h[1], h[0]};
+  if (j + 3 <= i) {
+    if (i < j + 4) v[i - j] += *lam;
+    *(f32x4*)(A + i * k + j) = v;
+  } else {
+    // the vector holding the diagonal: its columns up to i only
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (j + u <= i) A[i * k + j + u] = j + u == i ? v[u] + *lam : v[u];
+  }
 }
 
 // Lane n of each row of 16 lanes, broadcast to the row (DPP row_newbcast;
@@ -377,10 +387,17 @@ __global__ __launch_bounds__(64) void diag_inv_kernel(const float* __restrict__ 
 }
 
 // U[i][j] = Linv[k-1-i][k-1-j] for j >= i, 0 below the diagonal.
+// Four columns j .. j+3 per thread, 16-byte loads and stores (k % 4 == 0).
 __global__ void flip_out_kernel(const float* __restrict__ Linv, int64_t k, float* __restrict__ U) {
-  int64_t i = blockIdx.y, j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t i = blockIdx.y, j = 4 * ((int64_t)blockIdx.x * blockDim.x + threadIdx.x);
   if (j >= k) return;
-  U[i * k + j] = (j >= i) ? Linv[(k - 1 - i) * k + (k - 1 - j)] : 0.0f;
+  f32x4 v = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  if (j + 3 >= i) {
+    const f32x4 l = *(const f32x4*)(Linv + (k - 1 - i) * k + (k - 4 - j));
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = j + u >= i ? l[3 - u] : 0.0f;
+  }
+  *(f32x4*)(U + i * k + j) = v;
 }
 
 // p[0 .. 4 n4) = 0 in 16-byte stores (p 16-byte aligned).
@@ -407,7 +424,7 @@ hipError_t factor_hinv_launch(const float* H, int64_t k, float damp_rel, float* 
   // k % 16 == 0, so k * k is a multiple of 4 (and Linv, k * k floats into the workspace, is 16-byte aligned).
   hipLaunchKernelGGL(zero_kernel, dim3((unsigned)(((size_t)k * k / 4 + 255) / 256)), dim3(256), 0, s, Linv,
                      (int64_t)k * k / 4);
-  hipLaunchKernelGGL(flip_damp_kernel, dim3((unsigned)((k + 255) / 256), (unsigned)k), dim3(256), 0, s, H, k,
+  hipLaunchKernelGGL(flip_damp_kernel, dim3((unsigned)((k / 4 + 255) / 256), (unsigned)k), dim3(256), 0, s, H, k,
                      lam, A);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -471,7 +488,7 @@ hipError_t factor_hinv_launch(const float* H, int64_t k, float damp_rel, float* 
       if (e != hipSuccess) return e;
     }
   }
-  hipLaunchKernelGGL(flip_out_kernel, dim3((unsigned)((k + 255) / 256), (unsigned)k), dim3(256), 0, s, Linv, k,
+  hipLaunchKernelGGL(flip_out_kernel, dim3((unsigned)((k / 4 + 255) / 256), (unsigned)k), dim3(256), 0, s, Linv, k,
                      U);
   return hipGetLastError();
 }
