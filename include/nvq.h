@@ -75,6 +75,18 @@ extern "C" {
  * committed with its replayed GPTQ updates as usual.  For the scale-selection
  * ablation; ignored with RTN. */
 #define NVQ_FLAG_INDEP  8u
+/* Reject non-finite input instead of quantizing it: a NaN or infinity in W,
+ * or a g that is not a finite positive number, has no NVFP4 encoding
+ * ("Replay the Curvature", Abstract: E2M1 codes under an E4M3 scale).  Every row of W that holds a non-finite value among its
+ * first k columns -- every row, if *g is not finite and positive -- is
+ * written as: codes 0, all of its scale bytes 0x7F (the E4M3FN NaN code, so
+ * that nvfp4_dequantize gives NaN for the row), row_err and row_loss NaN.
+ * Other rows are unaffected (rows are independent throughout the sweep).
+ * The check reads W once more on the device and never synchronizes: the
+ * caller finds the rejected rows by reading row_err (or the scales) back.
+ * Without the flag a non-finite weight still gives deterministic outputs
+ * (NaN scores lose every arg-min), but they mean nothing. */
+#define NVQ_FLAG_CHECK_FINITE 16u
 
 /*
  * hessian_accumulate -- second-order state of the layer ("Replay the
@@ -177,8 +189,9 @@ int hessian_accumulate_grouped(const void* X, int x_dtype, int64_t n, int64_t k,
  *              to 0.  U must not overlap H.
  *   lambda_out device, 1 float: lambda.
  *   info       device, 1 int32: 0 on success; j > 0 if the trailing principal
- *              submatrix of H + lambda I of order j is not positive definite
- *              (U then holds no meaningful values).
+ *              submatrix of H + lambda I of order j is not positive definite;
+ *              -1 if the upper triangle of H or lambda holds a NaN or an
+ *              infinity (U then holds no meaningful values).
  *   ws         device workspace of factor_hinv_workspace_size(k) bytes.
  * Computed in fp32: a blocked Cholesky factorization of the index-reversed
  * damped matrix followed by a blocked triangular inverse.
@@ -317,6 +330,24 @@ size_t nvfp4_gemm_workspace_size(int64_t T, int64_t k, int64_t m);
 int nvfp4_gemm(const void* X, int x_dtype, int64_t T, int64_t k, int64_t ldx, const uint8_t* codes,
                const uint8_t* scales, const float* g, int64_t m, void* Y, int y_dtype, int64_t ldy, void* ws,
                size_t ws_bytes, void* stream);
+
+/*
+ * nvq_check_finite -- device-side scan for NaN and infinity, for the inputs
+ * the quantizer cannot represent (W) or that would poison the second-order
+ * state (X, before hessian_accumulate; "Replay the Curvature", Abstract:
+ * the calibration activations and weights of the layer solve).
+ *
+ *   A       device [rows x ld], element type dtype (bf16 or fp32); only the
+ *           first cols values of each row are read.
+ *   rows    0 <= rows < 2^31 - 1; cols > 0; ld >= cols.
+ *   status  device, 1 int32 output: 0 if every value is finite, otherwise
+ *           1 + the lowest row index holding a NaN or infinity.  The value
+ *           does not depend on timing.  Written asynchronously; the library
+ *           does not read it back.
+ * A NaN in X makes H non-finite, which factor_hinv reports as info = -1.
+ */
+int nvq_check_finite(const void* A, int dtype, int64_t rows, int64_t cols, int64_t ld, int32_t* status,
+                     void* stream);
 
 /* Text of a status code; never NULL. */
 const char* nvq_status_string(int status);

@@ -207,9 +207,13 @@ def rtn(W, g, n_cand=1):
 
 
 def weighted_error(W, deq, H):
-    """Per-row E_r = dW_r H dW_r^T with dW = W - deq, in fp64."""
+    """Per-row E_r = dW_r H dW_r^T with dW = W - deq, in fp64.
+
+    Evaluated as the row sums of (dW H) * dW: the product dW H is one library
+    matrix product, then each row is dotted with its own dW row.
+    """
     dW = np.asarray(W, dtype=np.float64) - np.asarray(deq, dtype=np.float64)
-    return np.einsum("rk,kl,rl->r", dW, np.asarray(H, dtype=np.float64), dW)
+    return np.sum((dW @ np.asarray(H, dtype=np.float64)) * dW, axis=1)
 
 
 def quantize_layer(W, X=None, H=None, n_cand=16, damp_rel=DAMP_REL, g=None, dtype=np.float64):

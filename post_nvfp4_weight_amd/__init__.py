@@ -24,6 +24,7 @@ FLAG_RTN = 1
 FLAG_NO_ERR = 2
 FLAG_FP64 = 4
 FLAG_INDEP = 8
+FLAG_CHECK_FINITE = 16
 
 EXPORTS = [
     "hessian_workspace_size", "hessian_accumulate",
@@ -32,7 +33,8 @@ EXPORTS = [
     "factor_hinv_workspace_size", "factor_hinv", "factor_hinv_batched",
     "nvfp4_global_scale_workspace_size", "nvfp4_global_scale",
     "gptq_nvfp4_workspace_size", "gptq_nvfp4_quantize", "gptq_nvfp4_quantize_batched",
-    "nvfp4_dequantize", "nvfp4_gemm_workspace_size", "nvfp4_gemm", "nvq_status_string", "nvq_last_error",
+    "nvfp4_dequantize", "nvfp4_gemm_workspace_size", "nvfp4_gemm", "nvq_check_finite",
+    "nvq_status_string", "nvq_last_error",
 ]
 
 
@@ -68,6 +70,7 @@ def _load():
         "nvfp4_dequantize": (I32, [P, P, P, I64, I64, P, I32, P]),
         "nvfp4_gemm_workspace_size": (SZ, [I64, I64, I64]),
         "nvfp4_gemm": (I32, [P, I32, I64, I64, I64, P, P, P, I64, P, I32, I64, P, SZ, P]),
+        "nvq_check_finite": (I32, [P, I32, I64, I64, I64, P, P]),
         "nvq_status_string": (ctypes.c_char_p, [I32]),
         "nvq_last_error": (ctypes.c_char_p, []),
     }
@@ -301,6 +304,14 @@ def gptq_nvfp4_quantize_batched(W, U, H, g, n_cand=16, flags=0):
         _ptr(H), 0 if H is None else H.stride(0), _ptr(g), int(n_cand), int(flags), _ptr(out["codes"]),
         _ptr(out["scales"]), _ptr(out["row_err"]), _ptr(out["row_loss"]), _ptr(ws), need, _stream()))
     return out
+
+
+def check_finite(A):
+    """Device int32 tensor [1]: 0 if every value of A [rows, cols] is finite, else 1 + the first bad row."""
+    rows, cols, ld = _rows(A, "A")
+    status = torch.empty(1, dtype=torch.int32, device=A.device)
+    _check("nvq_check_finite", lib.nvq_check_finite(_ptr(A), _dtype_code(A), rows, cols, ld, _ptr(status), _stream()))
+    return status
 
 
 def quantize_layer(W, X, n_cand=16, damp_rel=0.01, flags=0):

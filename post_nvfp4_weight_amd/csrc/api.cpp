@@ -90,7 +90,7 @@ int quant_check(const char* fn, const void* W, int w_dtype, int64_t m, int64_t k
                 const uint8_t* scales, const float* row_err, const void* ws, size_t ws_bytes) {
   const bool rtn = flags & NVQ_FLAG_RTN;
   const bool want_err = !(flags & NVQ_FLAG_NO_ERR);
-  if (flags & ~(NVQ_FLAG_RTN | NVQ_FLAG_NO_ERR | NVQ_FLAG_FP64 | NVQ_FLAG_INDEP))
+  if (flags & ~(NVQ_FLAG_RTN | NVQ_FLAG_NO_ERR | NVQ_FLAG_FP64 | NVQ_FLAG_INDEP | NVQ_FLAG_CHECK_FINITE))
     return failp(NVQ_ERR_VALUE, fn, "unknown flags 0x%x", flags);
   if (!W || !g || !codes || !scales) return failp(NVQ_ERR_NULL, fn, "W, g, codes and scales are required");
   if (!rtn && !U) return failp(NVQ_ERR_NULL, fn, "U is required without NVQ_FLAG_RTN");
@@ -205,6 +205,8 @@ hipError_t quant_run(const void* W, int w_dtype, int64_t m, int64_t k, int64_t l
     if (e == hipSuccess) e = sweep_f32(m, k, U, g, n_cand, indep, codes, scales, row_loss, Wp, Eslab, invd, s);
   }
   if (e == hipSuccess && want_err) e = weighted_error_all(W, bf, m, k, ldw, H, g, codes, scales, row_err, Wp, part, s);
+  if (e == hipSuccess && (flags & NVQ_FLAG_CHECK_FINITE))
+    e = reject_nonfinite_rows_launch(W, bf, m, k, ldw, g, codes, scales, want_err ? row_err : nullptr, row_loss, s);
   return e;
 }
 
@@ -514,6 +516,20 @@ int gptq_nvfp4_quantize_batched(const void* W, int w_dtype, int64_t batch, int64
                     row_err ? row_err + (size_t)e * m : nullptr, row_loss ? row_loss + (size_t)e * m : nullptr,
                     (char*)ws, (hipStream_t)stream);
   return hip_status(err, "gptq_nvfp4_quantize_batched");
+}
+
+// ---------------------------------------------------------------------------
+int nvq_check_finite(const void* A, int dtype, int64_t rows, int64_t cols, int64_t ld, int32_t* status,
+                     void* stream) {
+  const char* fn = "nvq_check_finite";
+  if (!status) return failp(NVQ_ERR_NULL, fn, "status is NULL");
+  if (!dtype_ok(dtype)) return failp(NVQ_ERR_DTYPE, fn, "dtype %d", dtype);
+  if (rows < 0 || cols <= 0 || ld < cols || rows > 0x7FFFFFFE)
+    return failp(NVQ_ERR_SHAPE, fn, "rows=%lld cols=%lld ld=%lld (need 0<=rows<2^31-1, cols>0, ld>=cols)",
+                 (long long)rows, (long long)cols, (long long)ld);
+  if (rows > 0 && !A) return failp(NVQ_ERR_NULL, fn, "A is NULL");
+  if (!aligned(status, 4)) return failp(NVQ_ERR_ALIGN, fn, "status must be 4-byte aligned");
+  return hip_status(nonfinite_scan_launch(A, dtype == NVQ_DTYPE_BF16, rows, cols, ld, status, (hipStream_t)stream), fn);
 }
 
 // ---------------------------------------------------------------------------

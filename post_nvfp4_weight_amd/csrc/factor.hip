@@ -47,19 +47,24 @@ __global__ __launch_bounds__(256) void damping_kernel(const float* __restrict__ 
     float lam = damp_rel * (red[0] / (float)k);
     *lam_ws = lam;
     *lam_out = lam;
-    *info = 0;
+    *info = __builtin_isfinite(lam) ? 0 : -1;
   }
 }
 
 // A[i][j] = H[k-1-i][k-1-j] + lam * (i == j), lower triangle (reads H's upper triangle).
 // Four columns j .. j+3 per thread, 16-byte loads and stores (k % 4 == 0):
-// H's elements (k-1-i, k-4-j .. k-1-j) in reverse order.
+// H's elements (k-1-i, k-4-j .. k-1-j) in reverse order.  A non-finite value
+// in the upper triangle of H sets *info = -1 (every writer writes the same).
 __global__ void flip_damp_kernel(const float* __restrict__ H, int64_t k, const float* __restrict__ lam,
-                                 float* __restrict__ A) {
+                                 float* __restrict__ A, int32_t* __restrict__ info) {
   const int64_t i = blockIdx.y, j = 4 * ((int64_t)blockIdx.x * blockDim.x + threadIdx.x);
   if (j > i || j >= k) return;
   const f32x4 h = *(const f32x4*)(H + (k - 1 - i) * k + (k - 4 - j));
   f32x4 v = f32x4{h[3], h[2], h[1], h[0]};
+  bool bad = false;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) bad |= j + u <= i && !__builtin_isfinite(v[u]);
+  if (bad) *info = -1;
   if (j + 3 <= i) {
     if (i < j + 4) v[i - j] += *lam;
     *(f32x4*)(A + i * k + j) = v;
@@ -126,15 +131,18 @@ __device__ __forceinline__ void chol16(float (&c)[16], float (&x)[16], float lf,
 // transpose, and the step's contribution is subtracted from the columns to
 // its right, both as 16 x 16 tiles on the matrix cores
 // (v_mfma_f32_16x16x4f32, one tile per wave at a time).  Workgroup 0 stores
-// L11 and, on a non-positive pivot, sets *info (once) to the order of the
+// L11 into Ld (the same block of the inverse's buffer, zeroed beforehand,
+// which diag_inv_kernel later inverts in place): A's diagonal block is read by
+// every workgroup of the launch, so no workgroup may write it.  On a
+// non-positive pivot workgroup 0 also sets *info (once) to the order of the
 // failing leading minor of the reversed matrix, i.e. of the failing trailing
 // minor of H + lam I.
 //
 // 16x16x4 operand layout: lane l supplies A[l % 16][l / 16] and
 // B[l / 16][l % 16]; accumulator register r of lane l is D[4 (l / 16) + r][l % 16].
 constexpr int SP = NB + 4;   // LDS row stride: the tiles' operand and accumulator accesses are conflict free
-__global__ __launch_bounds__(256) void panel_kernel(float* __restrict__ A, int64_t k, int64_t p,
-                                                    int32_t* __restrict__ info) {
+__global__ __launch_bounds__(256) void panel_kernel(float* __restrict__ A, float* __restrict__ Ld, int64_t k,
+                                                    int64_t p, int32_t* __restrict__ info) {
   // Rows 0..63: the diagonal block (lower part; -> L11); rows 64..127: this
   // workgroup's panel rows (-> L21 rows).
   __shared__ __attribute__((aligned(16))) float V[2 * NB][SP];
@@ -265,7 +273,7 @@ __global__ __launch_bounds__(256) void panel_kernel(float* __restrict__ A, int64
 #pragma unroll
     for (int u = 0; u < 4; ++u)
       if (q < 4 && j4 + u > i) v[u] = 0.0f;
-    *(f32x4*)(A + (q < 4 ? p + i : p + nb + r0 + i) * k + p + j4) = v;
+    *(f32x4*)((q < 4 ? Ld + (p + i) * k : A + (p + nb + r0 + i) * k) + p + j4) = v;
   }
 }
 
@@ -352,12 +360,13 @@ __global__ __launch_bounds__(256) void chol_update_kernel(float* __restrict__ A,
   }
 }
 
-// Inverses of the diagonal 64-blocks of L (one wave each) into Linv: lane c
-// solves L x = e_c by forward substitution (column c of the inverse), with
-// the block in LDS so that row i of L reaches every lane as broadcast reads
-// (the same address in every lane), four values at a time.
-__global__ __launch_bounds__(64) void diag_inv_kernel(const float* __restrict__ A, int64_t k,
-                                                      float* __restrict__ Linv) {
+// Inverses of the diagonal 64-blocks of L (one wave each), in place in Linv,
+// where the panel launches stored them: lane c solves L x = e_c by forward
+// substitution (column c of the inverse), with the block in LDS so that row i
+// of L reaches every lane as broadcast reads (the same address in every
+// lane), four values at a time.  The block is read whole before it is
+// overwritten, and only by its own workgroup.
+__global__ __launch_bounds__(64) void diag_inv_kernel(float* __restrict__ Linv, int64_t k) {
   __shared__ __attribute__((aligned(16))) float Ls[NB][NB];
   const int lane = threadIdx.x;
   const int64_t p = (int64_t)blockIdx.x * NB;
@@ -366,7 +375,7 @@ __global__ __launch_bounds__(64) void diag_inv_kernel(const float* __restrict__ 
 #pragma unroll 8
   for (int i = 0; i < NB; ++i) {
     float v = (i == lane) ? 1.0f : 0.0f;
-    if (i < nb && lane < nb && lane <= i) v = A[(p + i) * k + p + lane];
+    if (i < nb && lane < nb && lane <= i) v = Linv[(p + i) * k + p + lane];
     Ls[i][lane] = v;
   }
   __syncthreads();
@@ -425,7 +434,7 @@ hipError_t factor_hinv_launch(const float* H, int64_t k, float damp_rel, float* 
   hipLaunchKernelGGL(zero_kernel, dim3((unsigned)(((size_t)k * k / 4 + 255) / 256)), dim3(256), 0, s, Linv,
                      (int64_t)k * k / 4);
   hipLaunchKernelGGL(flip_damp_kernel, dim3((unsigned)((k / 4 + 255) / 256), (unsigned)k), dim3(256), 0, s, H, k,
-                     lam, A);
+                     lam, A, info);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
@@ -437,7 +446,7 @@ hipError_t factor_hinv_launch(const float* H, int64_t k, float damp_rel, float* 
   for (int64_t p = 0; p < k; p += NB) {
     const int64_t rest = k - p - NB;
     const unsigned groups = rest > 0 ? (unsigned)((rest + NB - 1) / NB) : 1u;
-    hipLaunchKernelGGL(panel_kernel, dim3(groups), dim3(256), 0, s, A, k, p, info);
+    hipLaunchKernelGGL(panel_kernel, dim3(groups), dim3(256), 0, s, A, Linv, k, p, info);
     if (rest <= 0) break;
     const int64_t s0 = p / SW * SW, send = min(s0 + SW, k);
     if (p + NB < send) {
@@ -450,7 +459,7 @@ hipError_t factor_hinv_launch(const float* H, int64_t k, float damp_rel, float* 
                          rest2, (int)(send - s0), -1);
     }
   }
-  hipLaunchKernelGGL(diag_inv_kernel, dim3((unsigned)((k + NB - 1) / NB)), dim3(64), 0, s, A, k, Linv);
+  hipLaunchKernelGGL(diag_inv_kernel, dim3((unsigned)((k + NB - 1) / NB)), dim3(64), 0, s, Linv, k);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
 

@@ -88,6 +88,16 @@ hipError_t delta_w_launch(const void* W, int bf16, int64_t m, int64_t k, int64_t
                           float* dW, hipStream_t s, int64_t c0 = 0, int64_t c1 = -1);
 hipError_t row_sum_launch(const float* P, int64_t m, int64_t nparts, float* out, hipStream_t s);
 hipError_t fill_f32(float* p, int64_t n, float v, hipStream_t s);
+// *status = 0 if every A[r][c] (r < rows, c < cols; bf16 or fp32, row stride
+// ld) is finite, else 1 + the lowest row holding a non-finite value.
+hipError_t nonfinite_scan_launch(const void* A, int bf16, int64_t rows, int64_t cols, int64_t ld, int32_t* status,
+                                 hipStream_t s);
+// Rejects the rows of W holding a non-finite value (all rows if g is not a
+// finite positive number): codes 0, scales 0x7F, row_err and row_loss NaN.
+hipError_t reject_nonfinite_rows_launch(const void* W, int bf16, int64_t m, int64_t k, int64_t ldw, const float* g,
+                                        uint8_t* codes, uint8_t* scales, float* row_err, float* row_loss,
+                                        hipStream_t s);
+
 
 // NVFP4 weight-only GEMM: Y [T x m] = g (X Q^T), X bf16 [T x k] (row stride ldx),
 // Q = e2m1 * e4m3 from codes [m x k/2] and scales [m x k/16]; Y fp32 or bf16 (row stride ldy).

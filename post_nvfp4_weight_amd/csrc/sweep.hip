@@ -97,7 +97,8 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
   if (hb >= nhalf) return;
   const float g = *gptr;
   const uint8_t sc = scales[hb >> 1];
-  const float s = e4m3_value(sc & 0x7F);
+  // 0x7F / 0xFF is E4M3FN's NaN (the code of a row rejected by the finite check).
+  const float s = (sc & 0x7F) == 0x7F ? __builtin_nanf("") : e4m3_value(sc & 0x7F);
   const bool neg_scale = sc & 0x80;
   const uint32_t c = *(const uint32_t*)(codes + hb * 4);
   float v[8];
@@ -193,6 +194,75 @@ __global__ __launch_bounds__(256) void rtn_kernel(const void* __restrict__ W, in
   scales[row * nbk + blk] = (uint8_t)best_c;
 }
 
+// ---- finite checks ------------------------------------------------------------------
+// Whether row r of A (cols values of type bf16 or fp32, row stride ld) holds a
+// non-finite value (exponent field all ones), decided by the whole workgroup.
+// vec: rows start 16-byte aligned and hold a multiple of 16 bytes.
+template <int BF16>
+__device__ __forceinline__ bool row_nonfinite(const void* __restrict__ A, int64_t r, int64_t cols, int64_t ld,
+                                              bool vec) {
+  uint32_t bad = 0;
+  if (vec) {
+    const int64_t nv = cols * (BF16 ? 2 : 4) / 16;
+    const u32x4* row = (const u32x4*)((const char*)A + r * ld * (BF16 ? 2 : 4));
+    for (int64_t v = threadIdx.x; v < nv; v += blockDim.x) {
+      const u32x4 u = row[v];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (BF16) bad |= ((u[q] & 0x7F80u) == 0x7F80u) | ((u[q] & 0x7F800000u) == 0x7F800000u);
+        else bad |= (u[q] & 0x7F800000u) == 0x7F800000u;
+      }
+    }
+  } else {
+    for (int64_t c = threadIdx.x; c < cols; c += blockDim.x) {
+      if (BF16) bad |= (((const uint16_t*)A)[r * ld + c] & 0x7F80u) == 0x7F80u;
+      else bad |= (__float_as_uint(((const float*)A)[r * ld + c]) & 0x7F800000u) == 0x7F800000u;
+    }
+  }
+  return __syncthreads_or((int)bad) != 0;
+}
+
+__global__ void status_init_kernel(int32_t* __restrict__ status) { *status = 0x7FFFFFFF; }
+__global__ void status_finish_kernel(int32_t* __restrict__ status) {
+  const int32_t v = *status;
+  *status = v == 0x7FFFFFFF ? 0 : v + 1;
+}
+// *status = min(*status, the first row holding a non-finite value); a
+// workgroup visits its rows in increasing order, so it stops at its first.
+template <int BF16>
+__global__ __launch_bounds__(256) void nonfinite_scan_kernel(const void* __restrict__ A, int64_t rows, int64_t cols,
+                                                             int64_t ld, bool vec, int32_t* __restrict__ status) {
+  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+    if (row_nonfinite<BF16>(A, r, cols, ld, vec)) {
+      if (threadIdx.x == 0) atomicMin(status, (int32_t)r);
+      return;
+    }
+  }
+}
+
+// Rows of W that hold a non-finite value, or every row if g is not a finite
+// positive number, are rejected: codes 0, scales 0x7F (E4M3FN's NaN), and NaN
+// row_err / row_loss.  Runs after everything else has written the outputs.
+template <int BF16>
+__global__ __launch_bounds__(256) void reject_nonfinite_rows_kernel(const void* __restrict__ W, int64_t m, int64_t k,
+                                                                    int64_t ldw, bool vec, const float* __restrict__ gptr,
+                                                                    uint8_t* __restrict__ codes,
+                                                                    uint8_t* __restrict__ scales,
+                                                                    float* __restrict__ row_err,
+                                                                    float* __restrict__ row_loss) {
+  const float g = *gptr;
+  const bool g_bad = !(g > 0.0f) || __builtin_isinf(g);
+  for (int64_t r = blockIdx.x; r < m; r += gridDim.x) {
+    if (!g_bad && !row_nonfinite<BF16>(W, r, k, ldw, vec)) continue;
+    for (int64_t c = threadIdx.x; c < k / 2; c += blockDim.x) codes[r * (k / 2) + c] = 0;
+    for (int64_t c = threadIdx.x; c < k / kBlock; c += blockDim.x) scales[r * (k / kBlock) + c] = 0x7F;
+    if (threadIdx.x == 0) {
+      if (row_err) row_err[r] = __builtin_nanf("");
+      if (row_loss) row_loss[r] = __builtin_nanf("");
+    }
+  }
+}
+
 // ---- sweep helpers ------------------------------------------------------------------
 template <int BF16>
 __global__ void load_working_f64_kernel(const void* __restrict__ W, int64_t m, int64_t k, int64_t ldw,
@@ -262,13 +332,21 @@ struct SweepCfg {
   static constexpr int THREADS = ROWS * G;
 };
 
-// One butterfly step of the candidate arg-min inside groups of G lanes
-// (ties to the lower candidate index).  DPP moves within 16-lane rows.
+// One butterfly step of the candidate arg-min inside groups of G lanes.
+// DPP moves within 16-lane rows.  The order is total, so every lane of a
+// group ends with the same winner: the least score, ties to the lower
+// candidate index, a NaN score (a non-finite weight in the row) above every
+// number and NaN ties again to the lower index.
+template <typename T>
+__device__ __forceinline__ bool argmin_takes(T so, int io, T s, int i) {
+  const bool sn = s != s, on = so != so;
+  return (!on && (sn || so < s)) || ((so == s || (sn && on)) && io < i);
+}
 template <int CTRL>
 __device__ __forceinline__ void argmin_step(float& s, int& i) {
   const float so = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s), CTRL, 0xF, 0xF, false));
   const int io = __builtin_amdgcn_mov_dpp(i, CTRL, 0xF, 0xF, false);
-  if (so < s || (so == s && io < i)) { s = so; i = io; }
+  if (argmin_takes(so, io, s, i)) { s = so; i = io; }
 }
 template <int CTRL>
 __device__ __forceinline__ float sum_step(float s) {
@@ -289,7 +367,7 @@ template <int CTRL>
 __device__ __forceinline__ void argmin_step(double& s, int& i) {
   const double so = dpp_f64<CTRL>(s);
   const int io = __builtin_amdgcn_mov_dpp(i, CTRL, 0xF, 0xF, false);
-  if (so < s || (so == s && io < i)) { s = so; i = io; }
+  if (argmin_takes(so, io, s, i)) { s = so; i = io; }
 }
 template <int CTRL>
 __device__ __forceinline__ double sum_step(double s) {
@@ -677,6 +755,43 @@ hipError_t delta_w_launch(const void* W, int bf16, int64_t m, int64_t k, int64_t
 
 hipError_t row_sum_launch(const float* P, int64_t m, int64_t np, float* out, hipStream_t s) {
   hipLaunchKernelGGL(row_sum_kernel, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, s, P, m, np, out);
+  return hipGetLastError();
+}
+
+namespace {
+int scan_grid(int64_t rows) { return (int)(rows < 4096 ? (rows < 1 ? 1 : rows) : 4096); }
+bool rows_vectorizable(const void* A, int bf16, int64_t cols, int64_t ld) {
+  const int64_t es = bf16 ? 2 : 4;
+  return (uintptr_t)A % 16 == 0 && (cols * es) % 16 == 0 && (ld * es) % 16 == 0;
+}
+}  // namespace
+
+hipError_t nonfinite_scan_launch(const void* A, int bf16, int64_t rows, int64_t cols, int64_t ld, int32_t* status,
+                                 hipStream_t s) {
+  hipLaunchKernelGGL(status_init_kernel, dim3(1), dim3(1), 0, s, status);
+  if (rows > 0) {
+    const bool vec = rows_vectorizable(A, bf16, cols, ld);
+    if (bf16)
+      hipLaunchKernelGGL(nonfinite_scan_kernel<1>, dim3(scan_grid(rows)), dim3(256), 0, s, A, rows, cols, ld, vec,
+                         status);
+    else
+      hipLaunchKernelGGL(nonfinite_scan_kernel<0>, dim3(scan_grid(rows)), dim3(256), 0, s, A, rows, cols, ld, vec,
+                         status);
+  }
+  hipLaunchKernelGGL(status_finish_kernel, dim3(1), dim3(1), 0, s, status);
+  return hipGetLastError();
+}
+
+hipError_t reject_nonfinite_rows_launch(const void* W, int bf16, int64_t m, int64_t k, int64_t ldw, const float* g,
+                                        uint8_t* codes, uint8_t* scales, float* row_err, float* row_loss,
+                                        hipStream_t s) {
+  const bool vec = rows_vectorizable(W, bf16, k, ldw);
+  if (bf16)
+    hipLaunchKernelGGL(reject_nonfinite_rows_kernel<1>, dim3(scan_grid(m)), dim3(256), 0, s, W, m, k, ldw, vec, g,
+                       codes, scales, row_err, row_loss);
+  else
+    hipLaunchKernelGGL(reject_nonfinite_rows_kernel<0>, dim3(scan_grid(m)), dim3(256), 0, s, W, m, k, ldw, vec, g,
+                       codes, scales, row_err, row_loss);
   return hipGetLastError();
 }
 

@@ -90,6 +90,16 @@ def test_host_validation_rejects_bad_arguments():
     assert lib.hessian_accumulate_host(fake, 1, 10, 32, 32, fake, 8, P(1 << 20), 16, None, 0, None, None) == -5
     assert lib.hessian_accumulate_host(fake, 1, 10, 32, 32, fake, 8, P(1 << 20), 1 << 30, fake, 16, None,
                                        None) == -5
+    # finite check: status required, dtype, shape (rows, cols, ld); unknown quantize flag
+    assert lib.nvq_check_finite(fake, 1, 4, 32, 32, None, None) == -1
+    assert lib.nvq_check_finite(fake, 2, 4, 32, 32, fake, None) == -3
+    assert lib.nvq_check_finite(fake, 1, 4, 0, 32, fake, None) == -2
+    assert lib.nvq_check_finite(fake, 1, 4, 32, 16, fake, None) == -2
+    assert lib.nvq_check_finite(fake, 1, -1, 32, 32, fake, None) == -2
+    assert lib.nvq_check_finite(None, 1, 4, 32, 32, fake, None) == -1
+    rc = lib.gptq_nvfp4_quantize(fake, 1, 16, 32, 32, fake, fake, fake, 16, 32, fake, fake, fake, None,
+                                 fake, 1 << 30, None)
+    assert rc == -6 and b"flags" in lib.nvq_last_error()
     for s in (0, -1, -2, -3, -4, -5, -6, -7, -8, 99):
         assert lib.nvq_status_string(s)
 

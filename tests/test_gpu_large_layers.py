@@ -149,3 +149,50 @@ def test_sparse_down_projection_28672(nvq):
     synth.activations("sparse", n, k, kind="sparse", out=Xh)
     W = synth.weights("sparse", m, k, 0.01, outlier_frac=0.0005)
     _check_layer(nvq, Xh, Xh.to(DEV), W, rng, n_rows=64)
+
+
+def test_factor_panel_launch_larger_than_resident_workgroups(nvq):
+    """k = 33,024: the first panel launches (k - 64) / 64 = 515 workgroups, more
+    than fit on the device at once (2 per CU on 256 CUs), so some start only
+    after others have finished.  Every workgroup reads the panel's diagonal
+    block, so none may overwrite it.  The last workgroups' panel rows feed the
+    first rows of U (U is the index-reversed inverse factor), which are checked
+    by a property that holds at any size: with R = U^-1, U (H + lam I) = R^T is
+    lower triangular, so in fp64 the strictly upper part of the first 256 rows
+    of U (H + lam I) must vanish to the factor's rounding, and its diagonal is
+    1 / U_ii.  H is made well conditioned (N(0, 1) tokens, cond(H + lam I) ~
+    900).  There the factor's fp32 arithmetic (blocked Cholesky, then the
+    recursive-doubling triangular inverse, whose left residual is the larger
+    one: an fp32 emulation of the same recursion gives 2.4e-5 where an exact
+    inverse of the same L gives 7e-7) leaves, relative to the diagonal, up to
+    ~4e-5 above it and ~3e-4 on it -- the same at k = 16,384, where every
+    launch fits on the device, and in U's middle rows.  The bounds are 5e-4
+    and 2e-3; a panel row factored from the wrong diagonal block is off by
+    order one.  The trailing 2048 x 2048 block of U is also compared with the
+    fp64 oracle."""
+    k, n, s = 33024, 8192, 256
+    X = synth.to_bf16_tensor(synth.rng("small", 60).standard_normal((n, k), dtype=np.float32))
+    H = nvq.hessian_accumulate(X.to(DEV))
+    U, lam_t, info = nvq.factor_hinv(H)
+    torch.cuda.synchronize()
+    assert int(info.item()) == 0
+    lam = float(lam_t.item())
+    Us = U[:s].double().cpu().numpy()
+    T = np.zeros((s, k))
+    for c0 in range(0, k, 2048):
+        Hc = H[:, c0:c0 + 2048].double().cpu().numpy()
+        Hc[np.arange(c0, min(c0 + 2048, k)), np.arange(Hc.shape[1])] += lam
+        T[:, c0:c0 + 2048] = Us @ Hc
+    diag = T[np.arange(s), np.arange(s)]
+    dev_diag = np.abs(diag * Us[np.arange(s), np.arange(s)] - 1.0)
+    dev_up = np.array([np.max(np.abs(T[i, i + 1:])) / abs(diag[i]) for i in range(s)])
+    print(f"first {s} rows of U (H + lam I): diagonal within {dev_diag.max():.2e} of 1 / U_ii, "
+          f"upper part up to {dev_up.max():.2e} of the diagonal")
+    assert np.all(dev_diag <= 2e-3), int(np.argmax(dev_diag))
+    assert np.all(dev_up <= 5e-4), int(np.argmax(dev_up))
+    del T, Us
+    t = T_BLOCK
+    Ht = H[k - t:, k - t:].cpu().numpy().astype(np.float64)
+    Ut_ref = np.linalg.cholesky(np.linalg.inv(Ht + lam * np.eye(t))).T
+    Ut = U[k - t:, k - t:].cpu().numpy()
+    assert np.max(np.abs(Ut - Ut_ref)) <= 1e-4 * np.max(np.abs(Ut_ref))
