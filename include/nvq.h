@@ -332,6 +332,28 @@ int nvfp4_gemm(const void* X, int x_dtype, int64_t T, int64_t k, int64_t ldx, co
                size_t ws_bytes, void* stream);
 
 /*
+ * nvfp4_gemm_noalloc -- nvfp4_gemm for callers that cannot allocate memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same computation, kernels and results, bit for bit, with
+ * no workspace argument.  Its k-split partial sums use a fixed array of
+ * 32 MiB (33554432 bytes) of device memory inside the library, one per device
+ * that runs the call, held until the process ends (its address is looked up
+ * on the first call on each device).
+ *
+ *   Arguments as for nvfp4_gemm, without ws.  Shapes whose
+ *   nvfp4_gemm_workspace_size(T, k, m) exceeds 33554432 bytes are rejected
+ *   with NVQ_ERR_WORKSPACE (nothing is enqueued).  The call allocates and
+ *   frees nothing.
+ *   Every call on one device shares that device's array, which keeps the last
+ *   call's contents: calls that overlap on one device (concurrent streams,
+ *   host threads) race and must be serialized by the caller.  Nothing in the
+ *   array needs to start at zero: each call writes every partial sum it reads.
+ */
+int nvfp4_gemm_noalloc(const void* X, int x_dtype, int64_t T, int64_t k, int64_t ldx, const uint8_t* codes,
+                       const uint8_t* scales, const float* g, int64_t m, void* Y, int y_dtype, int64_t ldy,
+                       void* stream);
+
+/*
  * nvq_check_finite -- device-side scan for NaN and infinity, for the inputs
  * the quantizer cannot represent (W) or that would poison the second-order
  * state (X, before hessian_accumulate; "Replay the Curvature", Abstract:

@@ -33,7 +33,7 @@ EXPORTS = [
     "factor_hinv_workspace_size", "factor_hinv", "factor_hinv_batched",
     "nvfp4_global_scale_workspace_size", "nvfp4_global_scale",
     "gptq_nvfp4_workspace_size", "gptq_nvfp4_quantize", "gptq_nvfp4_quantize_batched",
-    "nvfp4_dequantize", "nvfp4_gemm_workspace_size", "nvfp4_gemm", "nvq_check_finite",
+    "nvfp4_dequantize", "nvfp4_gemm_workspace_size", "nvfp4_gemm", "nvfp4_gemm_noalloc", "nvq_check_finite",
     "nvq_status_string", "nvq_last_error",
 ]
 
@@ -70,6 +70,7 @@ def _load():
         "nvfp4_dequantize": (I32, [P, P, P, I64, I64, P, I32, P]),
         "nvfp4_gemm_workspace_size": (SZ, [I64, I64, I64]),
         "nvfp4_gemm": (I32, [P, I32, I64, I64, I64, P, P, P, I64, P, I32, I64, P, SZ, P]),
+        "nvfp4_gemm_noalloc": (I32, [P, I32, I64, I64, I64, P, P, P, I64, P, I32, I64, P]),
         "nvq_check_finite": (I32, [P, I32, I64, I64, I64, P, P]),
         "nvq_status_string": (ctypes.c_char_p, [I32]),
         "nvq_last_error": (ctypes.c_char_p, []),
@@ -143,6 +144,16 @@ def nvfp4_gemm(X, codes, scales, g, out_dtype=torch.float32, Y=None):
     ws = _workspace(need, X.device) if need else None
     _check("nvfp4_gemm", lib.nvfp4_gemm(_ptr(X), _dtype_code(X), T, k, ldx, _ptr(codes), _ptr(scales), _ptr(g), m,
                                         _ptr(Y), _dtype_code(Y), Y.stride(0), _ptr(ws), need, _stream()))
+    return Y
+
+
+def nvfp4_gemm_noalloc(X, codes, scales, g, Y):
+    """Y = X dequant(W)^T into a preallocated Y [T, m] (fp32 or bf16); the library allocates nothing."""
+    T, k, ldx = _rows(X, "X")
+    m = codes.shape[0]
+    _check("nvfp4_gemm_noalloc", lib.nvfp4_gemm_noalloc(_ptr(X), _dtype_code(X), T, k, ldx, _ptr(codes),
+                                                        _ptr(scales), _ptr(g), m, _ptr(Y), _dtype_code(Y),
+                                                        Y.stride(0), _stream()))
     return Y
 
 

@@ -359,24 +359,60 @@ int hessian_accumulate_host(const void* X_host, int x_dtype, int64_t n, int64_t 
 // ---- consumer: NVFP4 weight-only GEMM ------------------------------------------
 size_t nvfp4_gemm_workspace_size(int64_t T, int64_t k, int64_t m) { return align_up(nvfp4_gemm_workspace(T, k, m)); }
 
-int nvfp4_gemm(const void* X, int x_dtype, int64_t T, int64_t k, int64_t ldx, const uint8_t* codes,
-               const uint8_t* scales, const float* g, int64_t m, void* Y, int y_dtype, int64_t ldy, void* ws,
-               size_t ws_bytes, void* stream) {
-  const char* fn = "nvfp4_gemm";
+namespace {
+// Arguments of nvfp4_gemm and its no-allocation variant; *empty is set when
+// there is nothing to compute.
+int gemm_check(const char* fn, const void* X, int x_dtype, int64_t T, int64_t k, int64_t ldx, const uint8_t* codes,
+               const uint8_t* scales, const float* g, int64_t m, const void* Y, int y_dtype, int64_t ldy, bool* empty) {
+  *empty = false;
   if (x_dtype != NVQ_DTYPE_BF16) return failp(NVQ_ERR_DTYPE, fn, "x_dtype %d (activations must be bf16)", x_dtype);
   if (!dtype_ok(y_dtype)) return failp(NVQ_ERR_DTYPE, fn, "y_dtype %d", y_dtype);
   if (T < 0 || m < 0 || k <= 0 || k % 16 != 0 || ldx < k || ldx % 8 != 0 || ldy < m)
     return failp(NVQ_ERR_SHAPE, fn, "T=%lld m=%lld k=%lld ldx=%lld ldy=%lld (need k%%16==0, ldx>=k, ldx%%8==0, ldy>=m)",
                  (long long)T, (long long)m, (long long)k, (long long)ldx, (long long)ldy);
-  if (T == 0 || m == 0) return NVQ_OK;
+  if (T == 0 || m == 0) {
+    *empty = true;
+    return NVQ_OK;
+  }
   if (!X || !codes || !scales || !g || !Y) return failp(NVQ_ERR_NULL, fn, "X, codes, scales, g and Y are required");
   if (!aligned(X, 16)) return failp(NVQ_ERR_ALIGN, fn, "X must be 16-byte aligned");
   if (!aligned(codes, 8)) return failp(NVQ_ERR_ALIGN, fn, "codes must be 8-byte aligned");
+  return NVQ_OK;
+}
+}  // namespace
+
+int nvfp4_gemm(const void* X, int x_dtype, int64_t T, int64_t k, int64_t ldx, const uint8_t* codes,
+               const uint8_t* scales, const float* g, int64_t m, void* Y, int y_dtype, int64_t ldy, void* ws,
+               size_t ws_bytes, void* stream) {
+  const char* fn = "nvfp4_gemm";
+  bool empty = false;
+  const int rc = gemm_check(fn, X, x_dtype, T, k, ldx, codes, scales, g, m, Y, y_dtype, ldy, &empty);
+  if (rc != NVQ_OK || empty) return rc;
   const size_t need = nvfp4_gemm_workspace(T, k, m);
   if (need && (!ws || ws_bytes < need || !aligned(ws, kAlign)))
     return failp(NVQ_ERR_WORKSPACE, fn, "workspace needs %zu bytes (256-aligned), got %zu", need, ws_bytes);
   return hip_status(nvfp4_gemm_launch((const uint16_t*)X, T, k, ldx, codes, scales, g, m, Y,
                                       y_dtype == NVQ_DTYPE_BF16, ldy, (float*)ws, (hipStream_t)stream), fn);
+}
+
+int nvfp4_gemm_noalloc(const void* X, int x_dtype, int64_t T, int64_t k, int64_t ldx, const uint8_t* codes,
+                       const uint8_t* scales, const float* g, int64_t m, void* Y, int y_dtype, int64_t ldy,
+                       void* stream) {
+  const char* fn = "nvfp4_gemm_noalloc";
+  bool empty = false;
+  const int rc = gemm_check(fn, X, x_dtype, T, k, ldx, codes, scales, g, m, Y, y_dtype, ldy, &empty);
+  if (rc != NVQ_OK || empty) return rc;
+  const size_t need = nvfp4_gemm_workspace(T, k, m);
+  if (need > kNoAllocScratchBytes)
+    return failp(NVQ_ERR_WORKSPACE, fn,
+                 "T=%lld k=%lld m=%lld needs %zu bytes of partial sums; this variant holds at most %zu "
+                 "(use nvfp4_gemm with a workspace)",
+                 (long long)T, (long long)k, (long long)m, need, kNoAllocScratchBytes);
+  float* scr = nullptr;
+  hipError_t e = noalloc_scratch(&scr);
+  if (e != hipSuccess) return hip_status(e, fn);
+  return hip_status(nvfp4_gemm_launch((const uint16_t*)X, T, k, ldx, codes, scales, g, m, Y,
+                                      y_dtype == NVQ_DTYPE_BF16, ldy, scr, (hipStream_t)stream), fn);
 }
 
 size_t hessian_grouped_workspace_size(const int64_t* grp_off, int64_t G, int64_t k, int x_dtype) {

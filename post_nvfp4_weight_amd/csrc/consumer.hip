@@ -18,6 +18,8 @@
 // step is multiplied.
 #include <algorithm>
 
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -465,6 +467,37 @@ int nvfp4_gemm_splits(int64_t T, int64_t k, int64_t m) {
 }
 
 }  // namespace
+
+// ---- the no-allocation variant's scratch ---------------------------------------
+// The k-split partial sums of nvfp4_gemm_noalloc live in this array instead of
+// a caller workspace: each device that runs the call holds its own copy until
+// the process ends.  Host code never passes the array's name to a kernel (on
+// the host it is only a stand-in for the symbol): the device address comes
+// from hipGetSymbolAddress, taken once per device with that device current.
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t noalloc_scratch(float** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = (float*)p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 size_t nvfp4_gemm_workspace(int64_t T, int64_t k, int64_t m) {
   if (T <= 0 || m <= 0 || k <= 0) return 0;

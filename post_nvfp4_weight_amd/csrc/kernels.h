@@ -103,6 +103,11 @@ hipError_t reject_nonfinite_rows_launch(const void* W, int bf16, int64_t m, int6
 // Q = e2m1 * e4m3 from codes [m x k/2] and scales [m x k/16]; Y fp32 or bf16 (row stride ldy).
 // Small token counts split k over workspace partials (nvfp4_gemm_workspace bytes, 0 if unsplit).
 size_t nvfp4_gemm_workspace(int64_t T, int64_t k, int64_t m);
+// The no-allocation variant: its split partial sums use a fixed device array
+// of kNoAllocScratchBytes per device; noalloc_scratch gives this device's
+// address of it (looked up once per device).
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+hipError_t noalloc_scratch(float** out);
 hipError_t nvfp4_gemm_launch(const uint16_t* X, int64_t T, int64_t k, int64_t ldx, const uint8_t* codes,
                              const uint8_t* scales, const float* g, int64_t m, void* Y, int out_bf16, int64_t ldy,
                              float* ws, hipStream_t s);
