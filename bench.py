@@ -18,6 +18,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -219,12 +221,257 @@ def ablation(nvq, Wd, Xd):
                       "data": "synthetic"}))
 
 
+WORKLOADS = {
+    "attn_proj": "the attention-projection layer (headline)",
+    "mlp": "MLP pair of an 8B-class block: gate+up 28672x4096 (fp32 sweep) over X 131072x4096, down "
+           "4096x14336 (fp64 sweep) over its own SiLU(gate)*up activations",
+    "down_proj_70b": "70B-class down projection: W 8192x28672 bf16, X 65536x28672 bf16 60% zeros (fp64 sweep)",
+    "moe": "MoE layer: 256 experts, gate+up 2048x4096 each, 262144 tokens routed top-8 (Zipf 1.1)",
+}
+
+
+class LayerTimer:
+    """Times the per-layer C-ABI calls (zero H, Hessian, factor, global scale, quantize, dequantize) on
+    device-resident inputs with events on the library's stream; buffers allocated once, outside timing."""
+
+    STAGES = ["hessian", "factor", "gscale", "quantize", "dequant"]
+
+    def __init__(self, nvq, Wd, Xd, flags, n_cand=N_CAND):
+        import torch
+        self.nvq, self.lib, self.P, self.flags, self.n_cand = nvq, nvq.lib, nvq._ptr, flags, n_cand
+        self.Wd, self.Xd = Wd, Xd
+        self.m, self.k = Wd.shape
+        self.n = Xd.shape[0]
+        dev = Wd.device
+        m, k, n = self.m, self.k, self.n
+        self.H = torch.empty(k, k, dtype=torch.float32, device=dev)
+        self.U = torch.empty_like(self.H)
+        self.lam = torch.empty(1, dtype=torch.float32, device=dev)
+        self.info = torch.empty(1, dtype=torch.int32, device=dev)
+        self.g = torch.empty(1, dtype=torch.float32, device=dev)
+        self.codes = torch.empty(m, k // 2, dtype=torch.uint8, device=dev)
+        self.scales = torch.empty(m, k // 16, dtype=torch.uint8, device=dev)
+        self.row_err = torch.empty(m, dtype=torch.float32, device=dev)
+        self.row_loss = torch.empty(m, dtype=torch.float32, device=dev)
+        self.deq = torch.empty(m, k, dtype=torch.bfloat16, device=dev)
+        lib = self.lib
+        self.ws_n = {"h": lib.hessian_workspace_size(n, k, nvq.NVQ_DTYPE_BF16),
+                     "f": lib.factor_hinv_workspace_size(k),
+                     "g": lib.nvfp4_global_scale_workspace_size(m, k),
+                     "q": lib.gptq_nvfp4_workspace_size(m, k, flags)}
+        self.ws = {a: torch.empty(max(1, b), dtype=torch.uint8, device=dev) for a, b in self.ws_n.items()}
+
+    def _chk(self, name, rc):
+        if rc != 0:
+            raise RuntimeError(f"{name}: {self.lib.nvq_last_error().decode()}")
+
+    def step(self, ev=None):
+        lib, P, nvq, ws, wn = self.lib, self.P, self.nvq, self.ws, self.ws_n
+        s = nvq._stream()
+        m, k, n = self.m, self.k, self.n
+        self.H.zero_()
+        if ev: ev[0].record()
+        self._chk("hessian", lib.hessian_accumulate(P(self.Xd), nvq.NVQ_DTYPE_BF16, n, k, self.Xd.stride(0),
+                                                    P(self.H), P(ws["h"]), wn["h"], s))
+        if ev: ev[1].record()
+        self._chk("factor", lib.factor_hinv(P(self.H), k, 0.01, P(self.U), P(self.lam), P(self.info), P(ws["f"]),
+                                            wn["f"], s))
+        if ev: ev[2].record()
+        self._chk("gscale", lib.nvfp4_global_scale(P(self.Wd), nvq.NVQ_DTYPE_BF16, m, k, k, P(self.g), P(ws["g"]),
+                                                   wn["g"], s))
+        if ev: ev[3].record()
+        self._chk("quantize", lib.gptq_nvfp4_quantize(P(self.Wd), nvq.NVQ_DTYPE_BF16, m, k, k, P(self.U), P(self.H),
+                                                      P(self.g), self.n_cand, self.flags, P(self.codes),
+                                                      P(self.scales), P(self.row_err), P(self.row_loss),
+                                                      P(ws["q"]), wn["q"], s))
+        if ev: ev[4].record()
+        self._chk("dequant", lib.nvfp4_dequantize(P(self.codes), P(self.scales), P(self.g), m, k, P(self.deq),
+                                                  nvq.NVQ_DTYPE_BF16, s))
+        if ev: ev[5].record()
+
+    def run(self, steps, warmup):
+        import torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        assert int(self.info.item()) == 0, "factorization failed"
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.step(evs[i])
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        per = {st: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps for j, st in enumerate(self.STAGES)}
+        return ms, per
+
+
+def hessian_roofline(n, k, ms_h):
+    achieved = n * k * (k + 1) / (ms_h / 1e3) / 1e12
+    return {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": "hessian_accumulate",
+            "ms_per_call": round(ms_h, 4)}
+
+
+def workload_line(name, steps, warmup):
+    """One JSON line for a workload other than the headline: Mparam/s per layer including the Hessian."""
+    import torch
+    import post_nvfp4_weight_amd as nvq
+    import synth
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    layers = []
+    if name == "mlp":
+        n, d, f = 131072, 4096, 14336
+        log("generating inputs")
+        Xh = torch.empty(n, d, dtype=torch.bfloat16, pin_memory=True)
+        synth.activations("mlp", n, d, out=Xh)
+        Wg, Wu, Wdn = synth.mlp_block_weights(d, f)
+        Xd = Xh.to(dev)
+        del Xh
+        Xdown = synth.mlp_down_activations(Xd, Wg, Wu)
+        Wgu = synth.to_bf16_tensor(np.concatenate([Wg, Wu])).to(dev)
+        layers = [("gate_up", Wgu, Xd, 0), ("down", synth.to_bf16_tensor(Wdn).to(dev), Xdown, nvq.FLAG_FP64)]
+    elif name == "down_proj_70b":
+        m, k, n = 8192, 28672, 65536
+        log("generating inputs")
+        Xh = torch.empty(n, k, dtype=torch.bfloat16, pin_memory=True)
+        synth.activations("sparse", n, k, kind="sparse", out=Xh)
+        W = synth.weights("sparse", m, k, 0.01, outlier_frac=0.0005)
+        layers = [("down_proj", synth.to_bf16_tensor(W).to(dev), Xh.to(dev), nvq.FLAG_FP64)]
+        del Xh
+    else:
+        raise SystemExit(f"unknown workload {name}")
+    out = {"metric": "quantized weights/sec (Mparam/s) per layer incl. Hessian", "unit": "Mparam/s",
+           "n_gpus": 1, "steps": steps, "warmup": warmup, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16-mfma/fp32", "data": "synthetic",
+           "config": {"workload": WORKLOADS[name], "n_cand": N_CAND}, "layers": {}}
+    tot_ms, tot_params = 0.0, 0
+    for lname, Wd, Xd, flags in layers:
+        log(f"{lname}: warmup {warmup}, timing {steps} steps")
+        lt = LayerTimer(nvq, Wd, Xd, flags)
+        ms, per = lt.run(steps, warmup)
+        params = lt.m * lt.k
+        tot_ms += ms
+        tot_params += params
+        out["layers"][lname] = {
+            "d_out": lt.m, "d_in": lt.k, "tokens": lt.n, "sweep_precision": "fp64" if flags & nvq.FLAG_FP64 else "fp32",
+            "ms_per_step": round(ms, 3), "mparam_s": round(params / (ms / 1e3) / 1e6, 1),
+            "stages_ms": {a: round(b, 3) for a, b in per.items()},
+            "roofline": hessian_roofline(lt.n, lt.k, per["hessian"])}
+        del lt
+        torch.cuda.empty_cache()
+    out["ms_per_step"] = round(tot_ms, 3)
+    out["value"] = round(tot_params / (tot_ms / 1e3) / 1e6, 1)
+    print(json.dumps(out), flush=True)
+
+
+def moe_line(steps, warmup):
+    """The MoE layer: grouped Hessians over routed tokens, batched factors, per-expert global scales,
+    batched quantization (fp32 sweep) and dequantization of all 256 experts; Mparam/s over all experts."""
+    import torch
+    import post_nvfp4_weight_amd as nvq
+    import synth
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    E, n, k, m, top_k = 256, 262144, 4096, 2048, 8
+    log("generating inputs")
+    Xh = torch.empty(n, k, dtype=torch.bfloat16, pin_memory=True)
+    synth.activations("moe", n, k, out=Xh)
+    idx, off = synth.moe_routing(n, E, top_k)
+    Xd = Xh.to(dev)
+    del Xh
+    idx_d = torch.from_numpy(idx).to(dev)
+    Wt = torch.empty(E, m, k, dtype=torch.bfloat16, device=dev)
+    for e in range(E):
+        Wt[e] = synth.to_bf16_tensor(synth.moe_expert_weights(e, m, k)).to(dev)
+    lib, P = nvq.lib, nvq._ptr
+    import ctypes
+    offp = np.ascontiguousarray(off, dtype=np.int64)
+    offc = offp.ctypes.data_as(ctypes.c_void_p)
+    H = torch.empty(E, k, k, dtype=torch.float32, device=dev)
+    U = torch.empty_like(H)
+    lam = torch.empty(E, dtype=torch.float32, device=dev)
+    info = torch.empty(E, dtype=torch.int32, device=dev)
+    g = torch.empty(E, dtype=torch.float32, device=dev)
+    codes = torch.empty(E, m, k // 2, dtype=torch.uint8, device=dev)
+    scales = torch.empty(E, m, k // 16, dtype=torch.uint8, device=dev)
+    row_err = torch.empty(E, m, dtype=torch.float32, device=dev)
+    row_loss = torch.empty(E, m, dtype=torch.float32, device=dev)
+    deq = torch.empty(E, m, k, dtype=torch.bfloat16, device=dev)
+    # factors: 64 experts per pass (64 x 160 MiB); quantization: all 256 in one pass (256 x 36 MiB)
+    wn = {"h": lib.hessian_grouped_workspace_size(offc, E, k, nvq.NVQ_DTYPE_BF16),
+          "f": 64 * lib.factor_hinv_workspace_size(k), "g": lib.nvfp4_global_scale_workspace_size(m, k),
+          "q": E * lib.gptq_nvfp4_workspace_size(m, k, 0)}
+    ws = {a: torch.empty(max(1, b), dtype=torch.uint8, device=dev) for a, b in wn.items()}
+
+    def chk(name, rc):
+        if rc != 0:
+            raise RuntimeError(f"{name}: {lib.nvq_last_error().decode()}")
+
+    def step(ev=None):
+        s = nvq._stream()
+        H.zero_()
+        if ev: ev[0].record()
+        chk("hessian", lib.hessian_accumulate_grouped(P(Xd), nvq.NVQ_DTYPE_BF16, n, k, k, P(idx_d), offc, E, P(H),
+                                                      P(ws["h"]), wn["h"], s))
+        if ev: ev[1].record()
+        chk("factor", lib.factor_hinv_batched(P(H), k, E, k * k, 0.01, P(U), k * k, P(lam), P(info), P(ws["f"]),
+                                              wn["f"], s))
+        if ev: ev[2].record()
+        for e in range(E):
+            chk("gscale", lib.nvfp4_global_scale(P(Wt[e]), nvq.NVQ_DTYPE_BF16, m, k, k, P(g[e:]), P(ws["g"]),
+                                                 wn["g"], s))
+        if ev: ev[3].record()
+        chk("quantize", lib.gptq_nvfp4_quantize_batched(P(Wt), nvq.NVQ_DTYPE_BF16, E, m, k, k, m * k, P(U), k * k,
+                                                        P(H), k * k, P(g), N_CAND, 0, P(codes), P(scales),
+                                                        P(row_err), P(row_loss), P(ws["q"]), wn["q"], s))
+        if ev: ev[4].record()
+        for e in range(E):
+            chk("dequant", lib.nvfp4_dequantize(P(codes[e]), P(scales[e]), P(g[e:]), m, k, P(deq[e]),
+                                                nvq.NVQ_DTYPE_BF16, s))
+        if ev: ev[5].record()
+
+    log(f"warmup {warmup}")
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    assert bool(torch.all(info == 0)), "factorization failed"
+    log(f"timing {steps} steps")
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    per = {st: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps for j, st in enumerate(LayerTimer.STAGES)}
+    counts = np.diff(off)
+    flops = float(np.sum(counts.astype(np.float64) * k * (k + 1)))
+    ach = flops / (per["hessian"] / 1e3) / 1e12
+    out = {"metric": "quantized weights/sec (Mparam/s) per layer incl. Hessian",
+           "value": round(E * m * k / (ms / 1e3) / 1e6, 1), "unit": "Mparam/s", "n_gpus": 1, "steps": steps,
+           "warmup": warmup, "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16-mfma/fp32", "data": "synthetic",
+           "config": {"workload": WORKLOADS["moe"], "experts": E, "d_out": m, "d_in": k, "tokens": n,
+                      "top_k": top_k, "assignments": int(off[-1]), "tokens_per_expert_min": int(counts.min()),
+                      "tokens_per_expert_max": int(counts.max()), "n_cand": N_CAND, "sweep_precision": "fp32"},
+           "stages_ms": {a: round(b, 3) for a, b in per.items()},
+           "roofline": {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                        "kernel": "hessian_accumulate_grouped", "ms_per_call": round(per["hessian"], 4)}}
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", default="attn_proj", choices=sorted(WORKLOADS),
+                    help="attn_proj (default) is the headline line; the others print one line each for the "
+                         "larger layer shapes (their own default steps: 3, warmup 1)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the Hessian's measured HBM traffic from two rocprofv3 --pmc CSVs and exit")
     ap.add_argument("--streamed", action="store_true",
@@ -244,6 +491,15 @@ def main():
               "(several GPUs would split the tokens of the Hessian, all-reduce H, and split the rows of W, "
               "which need no exchange). Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload != "attn_proj":
+        steps = args.steps if "--steps" in sys.argv else 3
+        warmup = args.warmup if "--warmup" in sys.argv else 1
+        if args.workload == "moe":
+            moe_line(steps, warmup)
+        else:
+            workload_line(args.workload, steps, warmup)
+        return
 
     import torch
     import post_nvfp4_weight_amd as nvq

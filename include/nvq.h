@@ -202,12 +202,16 @@ int factor_hinv(const float* H, int64_t k, float damp_rel, float* U, float* lamb
 
 /*
  * factor_hinv_batched -- factor_hinv of `batch` matrices (one per expert of a
- * mixture-of-experts layer), one after the other on the stream:
- * H + e*stride_h -> U + e*stride_u, lambda_out[e], info[e].
- * Strides count floats, are >= k*k and multiples of 4; the U and H ranges
- * must not overlap.  ws: factor_hinv_workspace_size(k) bytes (reused).
- * batch = 0 is a no-op.  Arguments are checked as for factor_hinv; the first
- * failing element's status is returned (elements before it are enqueued).
+ * mixture-of-experts layer): H + e*stride_h -> U + e*stride_u,
+ * lambda_out[e], info[e].  Strides count floats, are >= k*k and multiples of
+ * 4; the U and H ranges must not overlap.
+ *   ws  at least factor_hinv_workspace_size(k) bytes; a workspace of
+ *       c * factor_hinv_workspace_size(k) bytes lets one pass factor c
+ *       matrices together: every launch of the blocked factorization (panel,
+ *       trailing update, inverse) covers all matrices of the pass, so the
+ *       serial chain of panels is walked once per pass instead of once per
+ *       matrix.  Results do not depend on c.
+ * batch = 0 is a no-op; nothing is enqueued when an argument is rejected.
  */
 int factor_hinv_batched(const float* H, int64_t k, int64_t batch, int64_t stride_h, float damp_rel, float* U,
                         int64_t stride_u, float* lambda_out, int32_t* info, void* ws, size_t ws_bytes,
@@ -280,9 +284,12 @@ int gptq_nvfp4_quantize(const void* W, int w_dtype, int64_t m, int64_t k, int64_
  * w_dtype), U + e*stride_u, H + e*stride_h (floats; U and H are not read when
  * the flags say so) and g[e], and writes codes + e*m*(k/2),
  * scales + e*m*(k/16), row_err + e*m and row_loss + e*m.  Strides: stride_w
- * >= m*ldw; stride_u and stride_h >= k*k and multiples of 4.  ws:
- * gptq_nvfp4_workspace_size(m, k, flags) bytes (reused).  batch = 0 is a
- * no-op; arguments are checked as for gptq_nvfp4_quantize.
+ * >= m*ldw; stride_u and stride_h >= k*k and multiples of 4.
+ *   ws  at least gptq_nvfp4_workspace_size(m, k, flags) bytes; a workspace
+ *       of c times that size quantizes c matrices per pass, every launch
+ *       (sweep batches, lazy updates, weighted error) covering all of them.
+ *       Results do not depend on c.
+ * batch = 0 is a no-op; arguments are checked as for gptq_nvfp4_quantize.
  */
 int gptq_nvfp4_quantize_batched(const void* W, int w_dtype, int64_t batch, int64_t m, int64_t k, int64_t ldw,
                                 int64_t stride_w, const float* U, int64_t stride_u, const float* H,

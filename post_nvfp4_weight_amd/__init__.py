@@ -282,13 +282,18 @@ def hessian_accumulate_grouped(X, tok_idx, grp_off, H=None):
     return H
 
 
-def factor_hinv_batched(H, damp_rel=0.01):
-    """H: [B, k, k] -> (U [B, k, k], lam [B], info [B]) as device tensors."""
+def factor_hinv_batched(H, damp_rel=0.01, max_ws_bytes=8 << 30):
+    """H: [B, k, k] -> (U [B, k, k], lam [B], info [B]) as device tensors.
+
+    The workspace holds as many matrices' buffers as fit in max_ws_bytes (at
+    least one, at most B): the library factors that many matrices per pass,
+    every launch covering all of them."""
     B, k = H.shape[0], H.shape[1]
     U = torch.empty_like(H)
     lam = torch.empty(B, dtype=torch.float32, device=H.device)
     info = torch.empty(B, dtype=torch.int32, device=H.device)
-    need = lib.factor_hinv_workspace_size(k)
+    one = lib.factor_hinv_workspace_size(k)
+    need = one * max(1, min(B, max_ws_bytes // one))
     ws = _workspace(need, H.device)
     _check("factor_hinv_batched", lib.factor_hinv_batched(_ptr(H), k, B, H.stride(0), float(damp_rel), _ptr(U),
                                                           U.stride(0), _ptr(lam), _ptr(info), _ptr(ws), need,
@@ -296,8 +301,11 @@ def factor_hinv_batched(H, damp_rel=0.01):
     return U, lam, info
 
 
-def gptq_nvfp4_quantize_batched(W, U, H, g, n_cand=16, flags=0):
-    """W: [B, m, k]; U, H: [B, k, k] (or None as the flags allow); g: device fp32 [B]."""
+def gptq_nvfp4_quantize_batched(W, U, H, g, n_cand=16, flags=0, max_ws_bytes=8 << 30):
+    """W: [B, m, k]; U, H: [B, k, k] (or None as the flags allow); g: device fp32 [B].
+
+    The workspace holds as many matrices' working buffers as fit in
+    max_ws_bytes (at least one): that many are quantized per pass."""
     B, m, k = W.shape
     dev = W.device
     if W.stride(2) != 1:
@@ -308,7 +316,8 @@ def gptq_nvfp4_quantize_batched(W, U, H, g, n_cand=16, flags=0):
         "row_err": None if (flags & FLAG_NO_ERR) else torch.empty(B, m, dtype=torch.float32, device=dev),
         "row_loss": torch.empty(B, m, dtype=torch.float32, device=dev),
     }
-    need = lib.gptq_nvfp4_workspace_size(m, k, flags)
+    one = lib.gptq_nvfp4_workspace_size(m, k, flags)
+    need = one * max(1, min(B, max_ws_bytes // one))
     ws = _workspace(need, dev)
     _check("gptq_nvfp4_quantize_batched", lib.gptq_nvfp4_quantize_batched(
         _ptr(W), _dtype_code(W), B, m, k, W.stride(1), W.stride(0), _ptr(U), 0 if U is None else U.stride(0),

@@ -108,27 +108,36 @@ int quant_check(const char* fn, const void* W, int w_dtype, int64_t m, int64_t k
   return NVQ_OK;
 }
 
-// Weighted error of output columns [c0, c1) given dW for every column < c1:
-// dW H' dW^T restricted to those columns, H' = 2 triu(H, 1) + diag(H), into
-// the per-column-tile partial sums.
-hipError_t error_tiles(const float* H, float* dW, float* part, int64_t m, int64_t k, int64_t c0, int64_t c1,
-                       hipStream_t s) {
-  GemmArgs a{};
-  a.A = dW; a.lda = k;
-  a.B = H + c0; a.ldb = k;
-  a.D = dW + c0; a.ldd = k;
-  a.P = part + c0 / kGemmTile; a.ldp = (k + kGemmTile - 1) / kGemmTile;
-  a.M = m; a.N = c1 - c0; a.K = c1; a.batch = 1; a.alpha = 1.0f; a.beta = 0.0f;
-  a.kmode = kGemmKSymUpperB; a.noff = c0;
-  return gemm_f32(a, false, false, false, kEpiRowDot, s);
-}
+// A batch of nb equal-shape matrices for the quantizer: matrix e reads W + e
+// * stride_w (elements of its dtype), U + e * stride_u, H + e * stride_h,
+// g[e], writes codes + e*m*k/2, scales + e*m*k/16, row_err + e*m,
+// row_loss + e*m, and uses its own workspace block at base + e * ws_stride
+// bytes (the QuantWs layout).  Every launch covers all nb matrices.
+struct QBatch {
+  int64_t nb = 1, stride_w = 0, stride_u = 0, stride_h = 0;
+  size_t ws_stride = 0;
+};
 
+// Weighted error dW H' dW^T, H' = 2 triu(H, 1) + diag(H), into the
+// per-column-tile partial sums, then summed per row.
 hipError_t weighted_error_all(const void* W, int bf, int64_t m, int64_t k, int64_t ldw, const float* H,
                               const float* g, const uint8_t* codes, const uint8_t* scales, float* row_err, float* dW,
-                              float* part, hipStream_t s) {
-  hipError_t e = delta_w_launch(W, bf, m, k, ldw, codes, scales, g, dW, s);
-  if (e == hipSuccess) e = error_tiles(H, dW, part, m, k, 0, k, s);
-  if (e == hipSuccess) e = row_sum_launch(part, m, (k + kGemmTile - 1) / kGemmTile, row_err, s);
+                              float* part, const QBatch& qb, hipStream_t s) {
+  const int64_t wsf = (int64_t)(qb.ws_stride / sizeof(float));
+  const int64_t np = (k + kGemmTile - 1) / kGemmTile;
+  hipError_t e = delta_w_launch(W, bf, m, k, ldw, codes, scales, g, dW, s, 0, -1, qb.nb, qb.stride_w, wsf);
+  if (e == hipSuccess) {
+    GemmArgs a{};
+    a.A = dW; a.lda = k;
+    a.B = H; a.ldb = k;
+    a.D = dW; a.ldd = k;
+    a.P = part; a.ldp = np;
+    a.M = m; a.N = k; a.K = k; a.batch = (int)qb.nb; a.bi = 1; a.alpha = 1.0f; a.beta = 0.0f;
+    a.sA2 = wsf; a.sB2 = qb.stride_h; a.sD2 = wsf; a.sP2 = wsf;
+    a.kmode = kGemmKSymUpperB; a.noff = 0;
+    e = gemm_f32(a, false, false, false, kEpiRowDot, s);
+  }
+  if (e == hipSuccess) e = row_sum_launch(part, m, np, row_err, s, qb.nb, wsf);
   return e;
 }
 
@@ -137,13 +146,18 @@ hipError_t weighted_error_all(const void* W, int bf, int64_t m, int64_t k, int64
 // 512-column block at once, and a finished block's error slab updates every
 // later column.
 hipError_t sweep_f32(int64_t m, int64_t k, const float* U, const float* g, int n_cand, bool indep, uint8_t* codes,
-                     uint8_t* scales, float* row_loss, float* Wp, float* Eslab, const float* invd, hipStream_t s) {
+                     uint8_t* scales, float* row_loss, float* Wp, float* Eslab, const float* invd, const QBatch& qb,
+                     hipStream_t s) {
+  const int64_t wsf = (int64_t)(qb.ws_stride / sizeof(float));
+  SweepStrides bs;
+  bs.wp = wsf; bs.u = qb.stride_u; bs.invd = wsf; bs.e = wsf;
   auto rank_update = [&](const float* Eb, int64_t r0, int64_t c0, int64_t kk, int64_t ncol) {
     GemmArgs a{};
     a.A = Eb; a.lda = kSuperBatch;
     a.B = U + r0 * k + c0; a.ldb = k;
     a.C = Wp + c0; a.ldc = k;
-    a.M = m; a.N = ncol; a.K = kk; a.batch = 1; a.alpha = -1.0f; a.beta = 1.0f;
+    a.M = m; a.N = ncol; a.K = kk; a.batch = (int)qb.nb; a.bi = 1; a.alpha = -1.0f; a.beta = 1.0f;
+    a.sA2 = wsf; a.sB2 = qb.stride_u; a.sC2 = wsf;
     return gemm_f32(a, false, false, false, kEpiAxpby, s);
   };
   hipError_t e = hipSuccess;
@@ -152,7 +166,7 @@ hipError_t sweep_f32(int64_t m, int64_t k, const float* U, const float* g, int n
     for (int64_t i1 = s0; e == hipSuccess && i1 < s1; i1 += kBatch) {
       const int ncols = (int)std::min<int64_t>(kBatch, s1 - i1);
       e = sweep_batch_launch(Wp, U, invd, g, m, k, (int)i1, ncols, n_cand, indep, codes, scales, Eslab + (i1 - s0),
-                             kSuperBatch, row_loss, s);
+                             kSuperBatch, row_loss, s, qb.nb, bs);
       const int64_t i2 = i1 + ncols;
       if (e == hipSuccess && i2 < s1) e = rank_update(Eslab + (i1 - s0), i1, i2, ncols, s1 - i2);
     }
@@ -161,15 +175,16 @@ hipError_t sweep_f32(int64_t m, int64_t k, const float* U, const float* g, int n
   return e;
 }
 
-// The quantization of one weight matrix (arguments already checked).
+// The quantization of nb matrices (arguments already checked).
 hipError_t quant_run(const void* W, int w_dtype, int64_t m, int64_t k, int64_t ldw, const float* U, const float* H,
                      const float* g, int n_cand, unsigned flags, uint8_t* codes, uint8_t* scales, float* row_err,
-                     float* row_loss, char* base, hipStream_t s) {
+                     float* row_loss, char* base, hipStream_t s, QBatch qb = QBatch()) {
   const bool rtn = flags & NVQ_FLAG_RTN;
   const bool want_err = !(flags & NVQ_FLAG_NO_ERR);
   const bool f64 = (flags & NVQ_FLAG_FP64) && !rtn;
   const bool indep = flags & NVQ_FLAG_INDEP;
   QuantWs L = quant_ws(m, k, f64);
+  if (qb.ws_stride == 0) qb.ws_stride = L.total;
   float* Wp = (float*)(base + L.wp);
   float* Eslab = (float*)(base + L.eslab);
   float* invd = (float*)(base + L.invd);
@@ -178,35 +193,43 @@ hipError_t quant_run(const void* W, int w_dtype, int64_t m, int64_t k, int64_t l
   hipError_t e = hipSuccess;
 
   if (rtn) {
-    e = rtn_launch(W, bf, m, k, ldw, g, n_cand, codes, scales, row_loss, s);
+    e = rtn_launch(W, bf, m, k, ldw, g, n_cand, codes, scales, row_loss, s, qb.nb, qb.stride_w);
   } else if (f64) {
-    // The same sweep and two-level updates with fp64 working weights and errors.
+    // The same sweep and two-level lazy updates with fp64 working weights and errors.
     double* Wd = (double*)(base + L.wp);
     double* Ed = (double*)(base + L.eslab);
-    e = load_working_copy_f64(W, bf, m, k, ldw, Wd, s);
-    if (e == hipSuccess && row_loss) e = fill_f32(row_loss, m, 0.0f, s);
+    const int64_t wsd = (int64_t)(qb.ws_stride / sizeof(double));
+    SweepStrides bs;
+    bs.wp = wsd; bs.u = qb.stride_u; bs.e = wsd;
+    e = load_working_copy_f64(W, bf, m, k, ldw, Wd, s, qb.nb, qb.stride_w, wsd);
+    if (e == hipSuccess && row_loss) e = fill_f32(row_loss, qb.nb * m, 0.0f, s);
     for (int64_t s0 = 0; e == hipSuccess && s0 < k; s0 += kSuperBatch) {
       const int64_t s1 = std::min<int64_t>(k, s0 + kSuperBatch);
       for (int64_t i1 = s0; e == hipSuccess && i1 < s1; i1 += kBatch) {
         const int ncols = (int)std::min<int64_t>(kBatch, s1 - i1);
         e = sweep_batch_launch_f64(Wd, U, g, m, k, (int)i1, ncols, n_cand, indep, codes, scales, Ed + (i1 - s0),
-                                   kSuperBatch, row_loss, s);
+                                   kSuperBatch, row_loss, s, qb.nb, bs);
         const int64_t i2 = i1 + ncols;
         if (e == hipSuccess && i2 < s1)
-          e = rank_update_f64(Ed + (i1 - s0), kSuperBatch, U + i1 * k + i2, k, Wd + i2, k, m, s1 - i2, ncols, s);
+          e = rank_update_f64(Ed + (i1 - s0), kSuperBatch, U + i1 * k + i2, k, Wd + i2, k, m, s1 - i2, ncols, s,
+                              qb.nb, wsd, qb.stride_u, wsd);
       }
       if (e == hipSuccess && s1 < k)
-        e = rank_update_f64(Ed, kSuperBatch, U + s0 * k + s1, k, Wd + s1, k, m, k - s1, s1 - s0, s);
+        e = rank_update_f64(Ed, kSuperBatch, U + s0 * k + s1, k, Wd + s1, k, m, k - s1, s1 - s0, s, qb.nb, wsd,
+                            qb.stride_u, wsd);
     }
   } else {
-    e = inv_diag_launch(U, k, invd, s);
-    if (e == hipSuccess) e = load_working_copy(W, bf, m, k, ldw, Wp, s);
-    if (e == hipSuccess && row_loss) e = fill_f32(row_loss, m, 0.0f, s);
-    if (e == hipSuccess) e = sweep_f32(m, k, U, g, n_cand, indep, codes, scales, row_loss, Wp, Eslab, invd, s);
+    const int64_t wsf = (int64_t)(qb.ws_stride / sizeof(float));
+    e = inv_diag_launch(U, k, invd, s, qb.nb, qb.stride_u, wsf);
+    if (e == hipSuccess) e = load_working_copy(W, bf, m, k, ldw, Wp, s, qb.nb, qb.stride_w, wsf);
+    if (e == hipSuccess && row_loss) e = fill_f32(row_loss, qb.nb * m, 0.0f, s);
+    if (e == hipSuccess) e = sweep_f32(m, k, U, g, n_cand, indep, codes, scales, row_loss, Wp, Eslab, invd, qb, s);
   }
-  if (e == hipSuccess && want_err) e = weighted_error_all(W, bf, m, k, ldw, H, g, codes, scales, row_err, Wp, part, s);
+  if (e == hipSuccess && want_err)
+    e = weighted_error_all(W, bf, m, k, ldw, H, g, codes, scales, row_err, Wp, part, qb, s);
   if (e == hipSuccess && (flags & NVQ_FLAG_CHECK_FINITE))
-    e = reject_nonfinite_rows_launch(W, bf, m, k, ldw, g, codes, scales, want_err ? row_err : nullptr, row_loss, s);
+    e = reject_nonfinite_rows_launch(W, bf, m, k, ldw, g, codes, scales, want_err ? row_err : nullptr, row_loss, s,
+                                     qb.nb, qb.stride_w);
   return e;
 }
 
@@ -473,24 +496,29 @@ int factor_hinv(const float* H, int64_t k, float damp_rel, float* U, float* lamb
   size_t need = factor_hinv_workspace_size(k);
   if (!ws || ws_bytes < need || !aligned(ws, kAlign))
     return fail(NVQ_ERR_WORKSPACE, "factor_hinv: workspace needs %zu bytes (256-aligned), got %zu", need, ws_bytes);
-  return hip_status(factor_hinv_launch(H, k, damp_rel, U, lambda_out, info, ws, (hipStream_t)stream), "factor_hinv");
+  return hip_status(factor_hinv_launch(H, k, 1, k * k, damp_rel, U, k * k, lambda_out, info, ws, 1,
+                                       (hipStream_t)stream), "factor_hinv");
 }
 
 int factor_hinv_batched(const float* H, int64_t k, int64_t batch, int64_t stride_h, float damp_rel, float* U,
                         int64_t stride_u, float* lambda_out, int32_t* info, void* ws, size_t ws_bytes, void* stream) {
-  if (batch < 0) return fail(NVQ_ERR_SHAPE, "factor_hinv_batched: batch=%lld", (long long)batch);
+  const char* fn = "factor_hinv_batched";
+  if (batch < 0) return failp(NVQ_ERR_SHAPE, fn, "batch=%lld", (long long)batch);
   if (batch == 0) return NVQ_OK;
+  if (!H || !U || !lambda_out || !info) return failp(NVQ_ERR_NULL, fn, "H, U, lambda_out and info are required");
+  if (k <= 0 || k % 16 != 0) return failp(NVQ_ERR_SHAPE, fn, "k=%lld (need k>0, k%%16==0)", (long long)k);
   if (stride_h < k * k || stride_u < k * k || stride_h % 4 != 0 || stride_u % 4 != 0)
-    return fail(NVQ_ERR_SHAPE, "factor_hinv_batched: strides must be >= k*k and multiples of 4");
-  if (H && U && (const float*)U < H + (size_t)stride_h * batch && H < (const float*)U + (size_t)stride_u * batch)
-    return fail(NVQ_ERR_VALUE, "factor_hinv_batched: U must not overlap H");
-  for (int64_t e = 0; e < batch; ++e) {
-    const int rc = factor_hinv(H ? H + (size_t)e * stride_h : nullptr, k, damp_rel,
-                               U ? U + (size_t)e * stride_u : nullptr, lambda_out ? lambda_out + e : nullptr,
-                               info ? info + e : nullptr, ws, ws_bytes, stream);
-    if (rc != NVQ_OK) return rc;
-  }
-  return NVQ_OK;
+    return failp(NVQ_ERR_SHAPE, fn, "strides must be >= k*k and multiples of 4");
+  if (!(damp_rel >= 0.0f) || !std::isfinite(damp_rel)) return failp(NVQ_ERR_VALUE, fn, "damp_rel must be finite and >= 0");
+  if ((const float*)U < H + (size_t)stride_h * batch && H < (const float*)U + (size_t)stride_u * batch)
+    return failp(NVQ_ERR_VALUE, fn, "U must not overlap H");
+  if (!aligned(H, 16) || !aligned(U, 16)) return failp(NVQ_ERR_ALIGN, fn, "H and U must be 16-byte aligned");
+  const size_t one = factor_hinv_workspace_size(k);
+  if (!ws || ws_bytes < one || !aligned(ws, kAlign))
+    return failp(NVQ_ERR_WORKSPACE, fn, "workspace needs at least %zu bytes (256-aligned), got %zu", one, ws_bytes);
+  const int64_t chunk = std::min<int64_t>((int64_t)(ws_bytes / one), batch);
+  return hip_status(factor_hinv_launch(H, k, batch, stride_h, damp_rel, U, stride_u, lambda_out, info, ws, chunk,
+                                       (hipStream_t)stream), fn);
 }
 
 // ---------------------------------------------------------------------------
@@ -543,14 +571,21 @@ int gptq_nvfp4_quantize_batched(const void* W, int w_dtype, int64_t batch, int64
       (want_err && (stride_h < k * k || stride_h % 4 != 0)))
     return fail(NVQ_ERR_SHAPE, "gptq_nvfp4_quantize_batched: strides must cover one element (W: m*ldw, U and H: k*k, "
                                "multiples of 4)");
+  // As many matrices per pass as the workspace holds (each launch covers all of them).
+  const QuantWs L = quant_ws(m, k, (flags & NVQ_FLAG_FP64) && !rtn);
+  const int64_t chunk = std::max<int64_t>(1, std::min<int64_t>({batch, (int64_t)(ws_bytes / L.total), 65535}));
   const size_t es = w_dtype == NVQ_DTYPE_BF16 ? 2 : 4;
+  QBatch qb;
+  qb.stride_w = stride_w; qb.stride_u = stride_u; qb.stride_h = stride_h; qb.ws_stride = L.total;
   hipError_t err = hipSuccess;
-  for (int64_t e = 0; err == hipSuccess && e < batch; ++e)
+  for (int64_t e = 0; err == hipSuccess && e < batch; e += chunk) {
+    qb.nb = std::min<int64_t>(chunk, batch - e);
     err = quant_run((const char*)W + (size_t)e * stride_w * es, w_dtype, m, k, ldw,
                     U ? U + (size_t)e * stride_u : nullptr, H ? H + (size_t)e * stride_h : nullptr, g + e, n_cand,
                     flags, codes + (size_t)e * m * (k / 2), scales + (size_t)e * m * (k / kBlock),
                     row_err ? row_err + (size_t)e * m : nullptr, row_loss ? row_loss + (size_t)e * m : nullptr,
-                    (char*)ws, (hipStream_t)stream);
+                    (char*)ws, (hipStream_t)stream, qb);
+  }
   return hip_status(err, "gptq_nvfp4_quantize_batched");
 }
 

@@ -22,10 +22,13 @@ namespace {
 constexpr int NB = 64;
 constexpr int SW = 8 * NB;   // super-panel width of the trailing updates
 
-__global__ __launch_bounds__(256) void damping_kernel(const float* __restrict__ H, int64_t k, float damp_rel,
-                                                      float* __restrict__ lam_ws, float* __restrict__ lam_out,
-                                                      int32_t* __restrict__ info) {
+// Matrix b = blockIdx.x of a batch: H + b * stride_h, lam_ws[b], lam_out[b], info[b].
+__global__ __launch_bounds__(256) void damping_kernel(const float* __restrict__ H, int64_t k, int64_t stride_h,
+                                                      float damp_rel, float* __restrict__ lam_ws,
+                                                      float* __restrict__ lam_out, int32_t* __restrict__ info) {
   __shared__ float red[256];
+  const int64_t b = blockIdx.x;
+  H += b * stride_h;
   // Eight diagonal loads in flight at a time, added in the same order.
   float s = 0.0f;
   int64_t i = threadIdx.x;
@@ -45,9 +48,9 @@ __global__ __launch_bounds__(256) void damping_kernel(const float* __restrict__ 
   }
   if (threadIdx.x == 0) {
     float lam = damp_rel * (red[0] / (float)k);
-    *lam_ws = lam;
-    *lam_out = lam;
-    *info = __builtin_isfinite(lam) ? 0 : -1;
+    lam_ws[b] = lam;
+    lam_out[b] = lam;
+    info[b] = __builtin_isfinite(lam) ? 0 : -1;
   }
 }
 
@@ -55,10 +58,16 @@ __global__ __launch_bounds__(256) void damping_kernel(const float* __restrict__ 
 // Four columns j .. j+3 per thread, 16-byte loads and stores (k % 4 == 0):
 // H's elements (k-1-i, k-4-j .. k-1-j) in reverse order.  A non-finite value
 // in the upper triangle of H sets *info = -1 (every writer writes the same).
-__global__ void flip_damp_kernel(const float* __restrict__ H, int64_t k, const float* __restrict__ lam,
-                                 float* __restrict__ A, int32_t* __restrict__ info) {
+// Matrix b = blockIdx.z: H + b * stride_h -> A + b * k^2 (lam[b], info[b]).
+__global__ void flip_damp_kernel(const float* __restrict__ H, int64_t k, int64_t stride_h,
+                                 const float* __restrict__ lam, float* __restrict__ A, int32_t* __restrict__ info) {
   const int64_t i = blockIdx.y, j = 4 * ((int64_t)blockIdx.x * blockDim.x + threadIdx.x);
+  const int64_t b = blockIdx.z;
   if (j > i || j >= k) return;
+  H += b * stride_h;
+  A += b * k * k;
+  lam += b;
+  info += b;
   const f32x4 h = *(const f32x4*)(H + (k - 1 - i) * k + (k - 4 - j));
   f32x4 v = f32x4{h[3], h[2], h[1], h[0]};
   bool bad = false;
@@ -144,8 +153,15 @@ constexpr int SP = NB + 4;   // LDS row stride: the tiles' operand and accumulat
 __global__ __launch_bounds__(256) void panel_kernel(float* __restrict__ A, float* __restrict__ Ld, int64_t k,
                                                     int64_t p, int32_t* __restrict__ info) {
   // Rows 0..63: the diagonal block (lower part; -> L11); rows 64..127: this
-  // workgroup's panel rows (-> L21 rows).
+  // workgroup's panel rows (-> L21 rows).  Matrix b = blockIdx.y of a batch
+  // (A, Ld: k^2 floats per matrix; info[b]).
   __shared__ __attribute__((aligned(16))) float V[2 * NB][SP];
+  {
+    const int64_t b = blockIdx.y;
+    A += b * k * k;
+    Ld += b * k * k;
+    info += b;
+  }
   __shared__ float Li[16][17];   // inverse of the current 16 x 16 diagonal sub-block
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lq = lane >> 4;
@@ -292,6 +308,7 @@ constexpr int UP = NB + 2;   // LDS row stride: a lane's (row, k) reads hit 64 d
 __global__ __launch_bounds__(256) void chol_update_kernel(float* __restrict__ A, int64_t k, int64_t p,
                                                           int64_t rest, int kw, int lim) {
   __shared__ float Pi[NB][UP], Pj[NB][UP];
+  A += (int64_t)blockIdx.y * k * k;   // matrix of a batch
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t t = blockIdx.x;
   int64_t ti, tj;
@@ -367,6 +384,7 @@ __global__ __launch_bounds__(256) void chol_update_kernel(float* __restrict__ A,
 // lane), four values at a time.  The block is read whole before it is
 // overwritten, and only by its own workgroup.
 __global__ __launch_bounds__(64) void diag_inv_kernel(float* __restrict__ Linv, int64_t k) {
+  Linv += (int64_t)blockIdx.y * k * k;   // matrix of a batch
   __shared__ __attribute__((aligned(16))) float Ls[NB][NB];
   const int lane = threadIdx.x;
   const int64_t p = (int64_t)blockIdx.x * NB;
@@ -397,9 +415,12 @@ __global__ __launch_bounds__(64) void diag_inv_kernel(float* __restrict__ Linv, 
 
 // U[i][j] = Linv[k-1-i][k-1-j] for j >= i, 0 below the diagonal.
 // Four columns j .. j+3 per thread, 16-byte loads and stores (k % 4 == 0).
-__global__ void flip_out_kernel(const float* __restrict__ Linv, int64_t k, float* __restrict__ U) {
+// Matrix b = blockIdx.z: Linv + b * k^2 -> U + b * stride_u.
+__global__ void flip_out_kernel(const float* __restrict__ Linv, int64_t k, float* __restrict__ U, int64_t stride_u) {
   const int64_t i = blockIdx.y, j = 4 * ((int64_t)blockIdx.x * blockDim.x + threadIdx.x);
   if (j >= k) return;
+  Linv += (int64_t)blockIdx.z * k * k;
+  U += (int64_t)blockIdx.z * stride_u;
   f32x4 v = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   if (j + 3 >= i) {
     const f32x4 l = *(const f32x4*)(Linv + (k - 1 - i) * k + (k - 4 - j));
@@ -418,23 +439,36 @@ __global__ void zero_kernel(float* p, int64_t n4) {
 }  // namespace
 
 size_t factor_workspace(int64_t k) {
-  // A (k^2), Linv (k^2), T (k^2 / 2), lam (64 floats)
+  // per matrix: A (k^2), Linv (k^2), T (k^2 / 2), lam (64 floats)
   return ((size_t)k * k * 2 + (size_t)k * k / 2 + 64) * sizeof(float);
 }
 
-hipError_t factor_hinv_launch(const float* H, int64_t k, float damp_rel, float* U, float* lambda_out,
-                              int32_t* info, void* ws, hipStream_t s) {
-  float* A = (float*)ws;
-  float* Linv = A + (size_t)k * k;
-  float* T = Linv + (size_t)k * k;
-  float* lam = T + (size_t)k * k / 2;
+int64_t factor_max_chunk(int64_t k) {
+  // grid.z of the batched GEMMs: (pairs of 64-blocks, at most k / 128) x matrices <= 65535
+  const int64_t pairs = k / 128 > 0 ? k / 128 : 1;
+  return 65535 / pairs > 0 ? 65535 / pairs : 1;
+}
 
-  hipLaunchKernelGGL(damping_kernel, dim3(1), dim3(256), 0, s, H, k, damp_rel, lam, lambda_out, info);
-  // k % 16 == 0, so k * k is a multiple of 4 (and Linv, k * k floats into the workspace, is 16-byte aligned).
-  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)(((size_t)k * k / 4 + 255) / 256)), dim3(256), 0, s, Linv,
-                     (int64_t)k * k / 4);
-  hipLaunchKernelGGL(flip_damp_kernel, dim3((unsigned)((k / 4 + 255) / 256), (unsigned)k), dim3(256), 0, s, H, k,
-                     lam, A, info);
+// nb matrices of one pass: the workspace holds `chunk` per-matrix buffers in
+// four regions (A: chunk x k^2, Linv: chunk x k^2, T: chunk x k^2 / 2, lam),
+// so a matrix's buffers sit at the same offsets whatever nb is.
+static hipError_t factor_pass(const float* H, int64_t k, int64_t nb, int64_t stride_h, float damp_rel, float* U,
+                              int64_t stride_u, float* lambda_out, int32_t* info, float* ws, int64_t chunk,
+                              hipStream_t s) {
+  const size_t kk = (size_t)k * k;
+  float* A = ws;
+  float* Linv = A + chunk * kk;
+  float* T = Linv + chunk * kk;
+  float* lam = T + chunk * kk / 2;
+  const unsigned nbu = (unsigned)nb;
+
+  hipLaunchKernelGGL(damping_kernel, dim3(nbu), dim3(256), 0, s, H, k, stride_h, damp_rel, lam, lambda_out, info);
+  // k % 16 == 0, so k * k is a multiple of 4 (and Linv, a multiple of k * k floats into the workspace, is
+  // 16-byte aligned).
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((nb * kk / 4 + 255) / 256)), dim3(256), 0, s, Linv,
+                     (int64_t)(nb * kk / 4));
+  hipLaunchKernelGGL(flip_damp_kernel, dim3((unsigned)((k / 4 + 255) / 256), (unsigned)k, nbu), dim3(256), 0, s, H,
+                     k, stride_h, lam, A, info);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
@@ -442,38 +476,41 @@ hipError_t factor_hinv_launch(const float* H, int64_t k, float damp_rel, float* 
   // the rest of its super-panel is updated (the columns the next panels
   // factor); the columns right of the super-panel take all of its panels in
   // one update after its last panel, so they are read and written once per
-  // SW columns instead of once per panel.
+  // SW columns instead of once per panel.  Every launch covers the nb
+  // matrices of the pass (grid.y).
   for (int64_t p = 0; p < k; p += NB) {
     const int64_t rest = k - p - NB;
     const unsigned groups = rest > 0 ? (unsigned)((rest + NB - 1) / NB) : 1u;
-    hipLaunchKernelGGL(panel_kernel, dim3(groups), dim3(256), 0, s, A, Linv, k, p, info);
+    hipLaunchKernelGGL(panel_kernel, dim3(groups, nbu), dim3(256), 0, s, A, Linv, k, p, info);
     if (rest <= 0) break;
     const int64_t s0 = p / SW * SW, send = min(s0 + SW, k);
     if (p + NB < send) {
       const int64_t tiles = (rest + NB - 1) / NB, lim = (send - p - NB + NB - 1) / NB;
-      hipLaunchKernelGGL(chol_update_kernel, dim3((unsigned)(lim * tiles)), dim3(256), 0, s, A, k, p, rest, NB,
+      hipLaunchKernelGGL(chol_update_kernel, dim3((unsigned)(lim * tiles), nbu), dim3(256), 0, s, A, k, p, rest, NB,
                          (int)lim);
     } else if (send < k) {
       const int64_t rest2 = k - send, tiles = (rest2 + NB - 1) / NB;
-      hipLaunchKernelGGL(chol_update_kernel, dim3((unsigned)(tiles * (tiles + 1) / 2)), dim3(256), 0, s, A, k, s0,
-                         rest2, (int)(send - s0), -1);
+      hipLaunchKernelGGL(chol_update_kernel, dim3((unsigned)(tiles * (tiles + 1) / 2), nbu), dim3(256), 0, s, A, k,
+                         s0, rest2, (int)(send - s0), -1);
     }
   }
-  hipLaunchKernelGGL(diag_inv_kernel, dim3((unsigned)((k + NB - 1) / NB)), dim3(64), 0, s, Linv, k);
+  hipLaunchKernelGGL(diag_inv_kernel, dim3((unsigned)((k + NB - 1) / NB), nbu), dim3(64), 0, s, Linv, k);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  // Triangular inverse by recursive doubling over diagonal blocks of size bs.
+  // Triangular inverse by recursive doubling over diagonal blocks of size bs;
+  // the GEMMs of a level run over (pairs of one matrix) x (nb matrices).
   for (int64_t bs = NB; bs < k; bs *= 2) {
     int64_t full = k / (2 * bs);  // pairs whose both halves are complete
-    auto pair_step = [&](int64_t base, int64_t n1, int64_t n2, int batch) -> hipError_t {
+    auto pair_step = [&](int64_t base, int64_t n1, int64_t n2, int pairs) -> hipError_t {
       // T = L21 * L11^-1   (n2 x n1)
       GemmArgs a{};
       a.A = A + (base + bs) * k + base; a.lda = k;
       a.B = Linv + base * k + base; a.ldb = k;
       a.C = T; a.ldc = n1;
-      a.M = n2; a.N = n1; a.K = n1; a.batch = batch;
+      a.M = n2; a.N = n1; a.K = n1; a.batch = pairs * (int)nb; a.bi = pairs;
       a.sA = 2 * bs * k + 2 * bs; a.sB = 2 * bs * k + 2 * bs; a.sC = n1 * n2;
+      a.sA2 = (int64_t)kk; a.sB2 = (int64_t)kk; a.sC2 = (int64_t)kk / 2;
       a.alpha = 1.0f; a.beta = 0.0f; a.kmode = kGemmKLowerB;   // L11^-1 is lower triangular
       hipError_t err = gemm_f32(a, false, false, false, kEpiAxpby, s);
       if (err != hipSuccess) return err;
@@ -482,8 +519,9 @@ hipError_t factor_hinv_launch(const float* H, int64_t k, float damp_rel, float* 
       b.A = Linv + (base + bs) * k + (base + bs); b.lda = k;
       b.B = T; b.ldb = n1;
       b.C = Linv + (base + bs) * k + base; b.ldc = k;
-      b.M = n2; b.N = n1; b.K = n2; b.batch = batch;
+      b.M = n2; b.N = n1; b.K = n2; b.batch = pairs * (int)nb; b.bi = pairs;
       b.sA = 2 * bs * k + 2 * bs; b.sB = n1 * n2; b.sC = 2 * bs * k + 2 * bs;
+      b.sA2 = (int64_t)kk; b.sB2 = (int64_t)kk / 2; b.sC2 = (int64_t)kk;
       b.alpha = -1.0f; b.beta = 0.0f; b.kmode = kGemmKLowerA;  // L22^-1 is lower triangular
       return gemm_f32(b, false, false, false, kEpiAxpby, s);
     };
@@ -497,9 +535,23 @@ hipError_t factor_hinv_launch(const float* H, int64_t k, float damp_rel, float* 
       if (e != hipSuccess) return e;
     }
   }
-  hipLaunchKernelGGL(flip_out_kernel, dim3((unsigned)((k / 4 + 255) / 256), (unsigned)k), dim3(256), 0, s, Linv, k,
-                     U);
+  hipLaunchKernelGGL(flip_out_kernel, dim3((unsigned)((k / 4 + 255) / 256), (unsigned)k, nbu), dim3(256), 0, s,
+                     Linv, k, U, stride_u);
   return hipGetLastError();
+}
+
+hipError_t factor_hinv_launch(const float* H, int64_t k, int64_t batch, int64_t stride_h, float damp_rel, float* U,
+                              int64_t stride_u, float* lambda_out, int32_t* info, void* ws, int64_t chunk,
+                              hipStream_t s) {
+  if (chunk < 1) chunk = 1;
+  chunk = min(chunk, factor_max_chunk(k));
+  for (int64_t b0 = 0; b0 < batch; b0 += chunk) {
+    const int64_t nb = min(chunk, batch - b0);
+    hipError_t e = factor_pass(H + b0 * stride_h, k, nb, stride_h, damp_rel, U + b0 * stride_u, stride_u,
+                               lambda_out + b0, info + b0, (float*)ws, chunk, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace nvq

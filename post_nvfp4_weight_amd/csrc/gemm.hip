@@ -119,9 +119,12 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
   const int wr = wave >> 1, wc = wave & 1;
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   const int64_t z = blockIdx.z;
-  const float* A = p.A + z * p.sA;
-  const float* B = p.B + z * p.sB;
-  float* C = p.C + z * p.sC;
+  const int64_t zi = p.bi > 0 ? z % p.bi : z, zo = p.bi > 0 ? z / p.bi : 0;
+  const float* A = p.A + zi * p.sA + zo * p.sA2;
+  const float* B = p.B + zi * p.sB + zo * p.sB2;
+  float* C = p.C + zi * p.sC + zo * p.sC2;
+  const float* Dz = EPI == kEpiRowDot ? p.D + zi * p.sD + zo * p.sD2 : nullptr;
+  float* Pz = EPI == kEpiRowDot ? p.P + zi * p.sP + zo * p.sP2 : nullptr;
 
   // Accumulator layout of a 32x32 MFMA tile: lane l, register r holds
   // row 8*(r/4) + 4*(l/32) + r%4, column l%32.  With beta != 0 the tile of C
@@ -275,7 +278,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
 #pragma unroll
         for (int j = 0; j < NI; ++j) {
           int64_t gj = n0 + wc * WT + j * 32 + (lane & 31);
-          const float d = p.D[min(gi, p.M - 1) * p.ldd + min(gj, p.N - 1)];
+          const float d = Dz[min(gi, p.M - 1) * p.ldd + min(gj, p.N - 1)];
           s = fmaf(p.alpha * acc[i][j][r], (gi < p.M && gj < p.N) ? d : 0.0f, s);
         }
         part[i][r] = s;
@@ -297,7 +300,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
       float s = 0.0f;
       for (int c2 = 0; c2 < 32; ++c2) s += red[tid][c2];
       int64_t gi = m0 + tid;
-      if (gi < p.M) p.P[gi * p.ldp + tn] = s;
+      if (gi < p.M) Pz[gi * p.ldp + tn] = s;
     }
   }
 }
@@ -359,9 +362,12 @@ __global__ __launch_bounds__(256) void gemm_x6_kernel(GemmArgs p) {
   const int wr = wave >> 1, wc = wave & 1;
   const int64_t m0 = (int64_t)tm * X6_T, n0 = (int64_t)tn * X6_T;
   const int64_t z = blockIdx.z;
-  const float* A = p.A + z * p.sA;
-  const float* B = p.B + z * p.sB;
-  float* C = p.C + z * p.sC;
+  const int64_t zi = p.bi > 0 ? z % p.bi : z, zo = p.bi > 0 ? z / p.bi : 0;
+  const float* A = p.A + zi * p.sA + zo * p.sA2;
+  const float* B = p.B + zi * p.sB + zo * p.sB2;
+  float* C = p.C + zi * p.sC + zo * p.sC2;
+  const float* Dz = EPI == kEpiRowDot ? p.D + zi * p.sD + zo * p.sD2 : nullptr;
+  float* Pz = EPI == kEpiRowDot ? p.P + zi * p.sP + zo * p.sP2 : nullptr;
 
   f32x16 acc[2][2];
   const bool load_c = EPI == kEpiAxpby && p.beta != 0.0f;
@@ -591,7 +597,7 @@ __global__ __launch_bounds__(256) void gemm_x6_kernel(GemmArgs p) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           int64_t gj = n0 + wc * WT + j * 32 + (lane & 31);
-          const float d = p.D[min(gi, p.M - 1) * p.ldd + min(gj, p.N - 1)];
+          const float d = Dz[min(gi, p.M - 1) * p.ldd + min(gj, p.N - 1)];
           sacc = fmaf(p.alpha * acc[i][j][r], (gi < p.M && gj < p.N) ? d : 0.0f, sacc);
         }
         part[i][r] = sacc;
@@ -613,7 +619,7 @@ __global__ __launch_bounds__(256) void gemm_x6_kernel(GemmArgs p) {
       float sacc = 0.0f;
       for (int c2 = 0; c2 < 32; ++c2) sacc += red[tid][c2];
       int64_t gi = m0 + tid;
-      if (gi < p.M) p.P[gi * p.ldp + tn] = sacc;
+      if (gi < p.M) Pz[gi * p.ldp + tn] = sacc;
     }
   }
 }
@@ -639,10 +645,13 @@ hipError_t launch_t(const GemmArgs& a, hipStream_t s) {
 // 64-wide fp32 tiles when 128-wide ones would give fewer than one per two CUs
 // (the row-dot keeps 128: its partial sums are laid out per 128 columns);
 // otherwise the split-bf16 kernel for A [M][K] times B [K][N].  Measured on
-// the 4096-column layer: the crossover between 1/4 and 1 tile per CU.
+// the 4096-column layer: the crossover between 1/4 and 1 tile per CU.  The
+// choice counts the tiles of one outer batch item only, so a matrix of a
+// batch gets the same kernel, and the same bits, as when it is alone.
 template <bool TA, bool TB, bool LOWER, int EPI>
 hipError_t launch(const GemmArgs& a, hipStream_t s) {
-  const int64_t tiles128 = ((a.N + 127) / 128) * ((a.M + 127) / 128) * a.batch;
+  const int64_t inner = a.bi > 0 ? a.bi : a.batch;
+  const int64_t tiles128 = ((a.N + 127) / 128) * ((a.M + 127) / 128) * inner;
   if (EPI == kEpiAxpby && 2 * tiles128 < gemm_num_cus()) return launch_t<64, TA, TB, LOWER, EPI>(a, s);
   if (!TA && !TB && !LOWER) {
     dim3 grid((unsigned)((a.N + X6_T - 1) / X6_T), (unsigned)((a.M + X6_T - 1) / X6_T), (unsigned)a.batch);
@@ -660,8 +669,12 @@ constexpr int F64_T = 64, F64_BK = 16;
 __global__ __launch_bounds__(256) void rank_update_f64_kernel(const double* __restrict__ A, int64_t lda,
                                                               const float* __restrict__ B, int64_t ldb,
                                                               double* __restrict__ C, int64_t ldc, int64_t M,
-                                                              int64_t N, int64_t K) {
+                                                              int64_t N, int64_t K, int64_t sA, int64_t sB,
+                                                              int64_t sC) {
   __shared__ double As[F64_T][F64_BK + 1];   // -A tile, [row][k]
+  A += (int64_t)blockIdx.z * sA;   // matrix of a batch
+  B += (int64_t)blockIdx.z * sB;
+  C += (int64_t)blockIdx.z * sC;
   __shared__ double Bs[F64_BK][F64_T + 1];   // B tile, [k][column]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1;
@@ -728,10 +741,11 @@ __global__ __launch_bounds__(256) void rank_update_f64_kernel(const double* __re
 }  // namespace
 
 hipError_t rank_update_f64(const double* A, int64_t lda, const float* B, int64_t ldb, double* C, int64_t ldc,
-                           int64_t M, int64_t N, int64_t K, hipStream_t s) {
-  if (M <= 0 || N <= 0 || K <= 0) return hipSuccess;
-  dim3 grid((unsigned)((N + F64_T - 1) / F64_T), (unsigned)((M + F64_T - 1) / F64_T));
-  hipLaunchKernelGGL(rank_update_f64_kernel, grid, dim3(256), 0, s, A, lda, B, ldb, C, ldc, M, N, K);
+                           int64_t M, int64_t N, int64_t K, hipStream_t s, int64_t nb, int64_t sA, int64_t sB,
+                           int64_t sC) {
+  if (M <= 0 || N <= 0 || K <= 0 || nb <= 0) return hipSuccess;
+  dim3 grid((unsigned)((N + F64_T - 1) / F64_T), (unsigned)((M + F64_T - 1) / F64_T), (unsigned)nb);
+  hipLaunchKernelGGL(rank_update_f64_kernel, grid, dim3(256), 0, s, A, lda, B, ldb, C, ldc, M, N, K, sA, sB, sC);
   return hipGetLastError();
 }
 

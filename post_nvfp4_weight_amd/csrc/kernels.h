@@ -19,7 +19,14 @@ struct GemmArgs {
   int64_t M, N, K;
   int64_t lda, ldb, ldc, ldd, ldp;
   int64_t sA, sB, sC;   // batch strides (elements)
-  int batch;
+  int batch;            // grid.z: batch items (inner x outer when bi > 1)
+  // Two-level batch (e.g. pairs of blocks within each of several matrices):
+  // with bi > 0, item z is inner z % bi and outer z / bi, and the outer
+  // strides sA2.. are added per outer index (bi = 0: one level).  sD, sP (and sD2, sP2) move the
+  // row-dot epilogue's D and P the same way.
+  int bi;
+  int64_t sA2, sB2, sC2;
+  int64_t sD, sP, sD2, sP2;
   float alpha, beta;
   int kmode;            // GemmK: which part of the k range each output tile needs
   int64_t noff;         // column of C (and of B) 0 within the whole matrix, for kmode's triangle
@@ -38,8 +45,10 @@ hipError_t gemm_f32(const GemmArgs& a, bool trans_a, bool trans_b, bool lower, G
                     hipStream_t s);
 constexpr int kGemmTile = 128;
 // C -= A B with A [M x K] and C [M x N] fp64, B [K x N] fp32 (all row-major).
+// nb matrices: item e at A + e * sA, B + e * sB, C + e * sC.
 hipError_t rank_update_f64(const double* A, int64_t lda, const float* B, int64_t ldb, double* C, int64_t ldc,
-                           int64_t M, int64_t N, int64_t K, hipStream_t s);
+                           int64_t M, int64_t N, int64_t K, hipStream_t s, int64_t nb = 1, int64_t sA = 0,
+                           int64_t sB = 0, int64_t sC = 0);
 
 // ---- Hessian -------------------------------------------------------------
 size_t syrk_bf16_workspace(int64_t n, int64_t k);
@@ -51,11 +60,26 @@ hipError_t gather_rows(const void* X, int esize, int64_t ldx, const int32_t* idx
                        int64_t k, void* out, hipStream_t s);
 
 // ---- factor ----------------------------------------------------------------
+// Workspace of one matrix; a workspace of c such sizes factors c matrices per pass.
 size_t factor_workspace(int64_t k);
-hipError_t factor_hinv_launch(const float* H, int64_t k, float damp_rel, float* U,
-                              float* lambda_out, int32_t* info, void* ws, hipStream_t s);
+// The largest number of matrices one pass takes (a grid-size limit).
+int64_t factor_max_chunk(int64_t k);
+// batch matrices H + b * stride_h -> U + b * stride_u, lambda_out[b], info[b],
+// `chunk` matrices per pass (ws holds chunk per-matrix workspaces).
+hipError_t factor_hinv_launch(const float* H, int64_t k, int64_t batch, int64_t stride_h, float damp_rel, float* U,
+                              int64_t stride_u, float* lambda_out, int32_t* info, void* ws, int64_t chunk,
+                              hipStream_t s);
 
 // ---- codec / sweep -----------------------------------------------------------
+// Batched launches (nb matrices, grid.y = matrix e) take per-matrix strides:
+// W in elements of its dtype; g, codes, scales, row_err and row_loss advance
+// by 1, m*k/2, m*k/16, m and m per matrix.
+struct SweepStrides {
+  int64_t wp = 0;     // working weights (elements of the working type)
+  int64_t u = 0;      // U (floats)
+  int64_t invd = 0;   // 1 / U_jj (floats)
+  int64_t e = 0;      // error slab (elements of the working type)
+};
 hipError_t global_scale_launch(const void* W, int bf16, int64_t m, int64_t k, int64_t ldw,
                                float* g, float* partial, int nparts, hipStream_t s);
 int global_scale_parts(int64_t m, int64_t k);
@@ -63,30 +87,34 @@ hipError_t dequant_launch(const uint8_t* codes, const uint8_t* scales, const flo
                           int64_t m, int64_t k, void* out, int out_bf16, hipStream_t s);
 hipError_t rtn_launch(const void* W, int bf16, int64_t m, int64_t k, int64_t ldw,
                       const float* g, int n_cand, uint8_t* codes, uint8_t* scales,
-                      float* row_loss, hipStream_t s);
+                      float* row_loss, hipStream_t s, int64_t nb = 1, int64_t stride_w = 0);
 hipError_t load_working_copy(const void* W, int bf16, int64_t m, int64_t k, int64_t ldw,
-                             float* Wp, hipStream_t s);
-hipError_t inv_diag_launch(const float* U, int64_t k, float* invd, hipStream_t s);
+                             float* Wp, hipStream_t s, int64_t nb = 1, int64_t stride_w = 0, int64_t stride_wp = 0);
+hipError_t inv_diag_launch(const float* U, int64_t k, float* invd, hipStream_t s, int64_t nb = 1,
+                           int64_t stride_u = 0, int64_t stride_invd = 0);
 // indep: choose each block's scale by the block-independent squared rounding
 // error instead of the replay score (the committed block is still replayed).
 hipError_t sweep_batch_launch(float* Wp, const float* U, const float* invd, const float* g,
                               int64_t m, int64_t k, int i1, int ncols, int n_cand, bool indep,
                               uint8_t* codes, uint8_t* scales, float* Eslab, int64_t lde, float* row_loss,
-                              hipStream_t s);
+                              hipStream_t s, int64_t nb = 1, const SweepStrides& bs = SweepStrides());
 // The same sweep with fp64 working weights and errors (U read as fp32).
 hipError_t sweep_batch_launch_f64(double* Wp, const float* U, const float* g, int64_t m, int64_t k, int i1,
                                   int ncols, int n_cand, bool indep, uint8_t* codes, uint8_t* scales, double* Eslab,
-                                  int64_t lde, float* row_loss, hipStream_t s);
+                                  int64_t lde, float* row_loss, hipStream_t s, int64_t nb = 1,
+                                  const SweepStrides& bs = SweepStrides());
 hipError_t load_working_copy_f64(const void* W, int bf16, int64_t m, int64_t k, int64_t ldw, double* Wp,
-                                 hipStream_t s);
+                                 hipStream_t s, int64_t nb = 1, int64_t stride_w = 0, int64_t stride_wp = 0);
 // Columns of the two-level lazy update: each 128-column batch updates the
 // rest of its 512-column block; each finished block updates every later
 // column with its whole error slab (m x 512).
 constexpr int kSuperBatch = 512;
 hipError_t delta_w_launch(const void* W, int bf16, int64_t m, int64_t k, int64_t ldw,
                           const uint8_t* codes, const uint8_t* scales, const float* g,
-                          float* dW, hipStream_t s, int64_t c0 = 0, int64_t c1 = -1);
-hipError_t row_sum_launch(const float* P, int64_t m, int64_t nparts, float* out, hipStream_t s);
+                          float* dW, hipStream_t s, int64_t c0 = 0, int64_t c1 = -1, int64_t nb = 1,
+                          int64_t stride_w = 0, int64_t stride_dw = 0);
+hipError_t row_sum_launch(const float* P, int64_t m, int64_t nparts, float* out, hipStream_t s, int64_t nb = 1,
+                          int64_t stride_p = 0);
 hipError_t fill_f32(float* p, int64_t n, float v, hipStream_t s);
 // *status = 0 if every A[r][c] (r < rows, c < cols; bf16 or fp32, row stride
 // ld) is finite, else 1 + the lowest row holding a non-finite value.
@@ -96,7 +124,7 @@ hipError_t nonfinite_scan_launch(const void* A, int bf16, int64_t rows, int64_t 
 // finite positive number): codes 0, scales 0x7F, row_err and row_loss NaN.
 hipError_t reject_nonfinite_rows_launch(const void* W, int bf16, int64_t m, int64_t k, int64_t ldw, const float* g,
                                         uint8_t* codes, uint8_t* scales, float* row_err, float* row_loss,
-                                        hipStream_t s);
+                                        hipStream_t s, int64_t nb = 1, int64_t stride_w = 0);
 
 
 // NVFP4 weight-only GEMM: Y [T x m] = g (X Q^T), X bf16 [T x k] (row stride ldx),

@@ -129,10 +129,17 @@ template <int BF16>
 __global__ __launch_bounds__(256) void rtn_kernel(const void* __restrict__ W, int64_t m, int64_t k, int64_t ldw,
                                                   const float* __restrict__ gptr, int n_cand,
                                                   uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-                                                  bool vec) {
+                                                  bool vec, int64_t stride_w) {
   const int64_t nbk = k / kBlock;
   const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (b >= m * nbk) return;
+  {   // matrix e = blockIdx.y of a batch: W + e * stride_w elements, g[e], its codes and scales
+    const int64_t e = blockIdx.y;
+    W = (const char*)W + e * stride_w * (BF16 ? 2 : 4);
+    gptr += e;
+    codes += e * m * (k / 2);
+    scales += e * m * nbk;
+  }
   const int64_t row = b / nbk, blk = b % nbk;
   const float g = *gptr;
   float w[16];
@@ -249,7 +256,16 @@ __global__ __launch_bounds__(256) void reject_nonfinite_rows_kernel(const void* 
                                                                     uint8_t* __restrict__ codes,
                                                                     uint8_t* __restrict__ scales,
                                                                     float* __restrict__ row_err,
-                                                                    float* __restrict__ row_loss) {
+                                                                    float* __restrict__ row_loss, int64_t stride_w) {
+  {   // matrix e = blockIdx.y of a batch
+    const int64_t e = blockIdx.y;
+    W = (const char*)W + e * stride_w * (BF16 ? 2 : 4);
+    gptr += e;
+    codes += e * m * (k / 2);
+    scales += e * m * (k / kBlock);
+    if (row_err) row_err += e * m;
+    if (row_loss) row_loss += e * m;
+  }
   const float g = *gptr;
   const bool g_bad = !(g > 0.0f) || __builtin_isinf(g);
   for (int64_t r = blockIdx.x; r < m; r += gridDim.x) {
@@ -266,17 +282,21 @@ __global__ __launch_bounds__(256) void reject_nonfinite_rows_kernel(const void* 
 // ---- sweep helpers ------------------------------------------------------------------
 template <int BF16>
 __global__ void load_working_f64_kernel(const void* __restrict__ W, int64_t m, int64_t k, int64_t ldw,
-                                        double* __restrict__ Wp) {
+                                        double* __restrict__ Wp, int64_t stride_w, int64_t stride_wp) {
   const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (e >= m * k) return;
+  W = (const char*)W + (int64_t)blockIdx.y * stride_w * (BF16 ? 2 : 4);   // matrix of a batch
+  Wp += (int64_t)blockIdx.y * stride_wp;
   Wp[e] = (double)load_w<BF16>(W, (e / k) * ldw + e % k);
 }
 
 template <int BF16>
 __global__ void load_working_kernel(const void* __restrict__ W, int64_t m, int64_t k, int64_t ldw,
-                                    float* __restrict__ Wp) {
+                                    float* __restrict__ Wp, int64_t stride_w, int64_t stride_wp) {
   int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (e >= m * k) return;
+  W = (const char*)W + (int64_t)blockIdx.y * stride_w * (BF16 ? 2 : 4);   // matrix of a batch
+  Wp += (int64_t)blockIdx.y * stride_wp;
   int64_t r = e / k, c = e % k;  // k % 4 == 0: the 4 elements share a row
   f32x4 v;
 #pragma unroll
@@ -284,8 +304,11 @@ __global__ void load_working_kernel(const void* __restrict__ W, int64_t m, int64
   *(f32x4*)(Wp + e) = v;
 }
 
-__global__ void inv_diag_kernel(const float* __restrict__ U, int64_t k, float* __restrict__ invd) {
+__global__ void inv_diag_kernel(const float* __restrict__ U, int64_t k, float* __restrict__ invd, int64_t stride_u,
+                                int64_t stride_invd) {
   int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  U += (int64_t)blockIdx.y * stride_u;   // matrix of a batch
+  invd += (int64_t)blockIdx.y * stride_invd;
   if (j < k) invd[j] = 1.0f / U[j * k + j];
 }
 
@@ -295,10 +318,19 @@ __global__ __launch_bounds__(256) void delta_w_kernel(const void* __restrict__ W
                                                       int64_t ldw, const uint8_t* __restrict__ codes,
                                                       const uint8_t* __restrict__ scales,
                                                       const float* __restrict__ gptr, float* __restrict__ dW,
-                                                      int64_t blk0, int64_t nblk) {
+                                                      int64_t blk0, int64_t nblk, int64_t stride_w,
+                                                      int64_t stride_dw) {
   const int64_t nbk = k / kBlock;
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (t >= m * nblk) return;
+  {   // matrix e = blockIdx.y of a batch
+    const int64_t e = blockIdx.y;
+    W = (const char*)W + e * stride_w * (BF16 ? 2 : 4);
+    codes += e * m * (k / 2);
+    scales += e * m * nbk;
+    gptr += e;
+    dW += e * stride_dw;
+  }
   const int64_t row = t / nblk, blk = blk0 + t % nblk, b = row * nbk + blk;
   const float g = *gptr;
   const float s = e4m3_value(scales[b] & 0x7F);
@@ -310,9 +342,12 @@ __global__ __launch_bounds__(256) void delta_w_kernel(const void* __restrict__ W
   }
 }
 
-__global__ void row_sum_kernel(const float* __restrict__ P, int64_t m, int64_t np, float* __restrict__ out) {
+__global__ void row_sum_kernel(const float* __restrict__ P, int64_t m, int64_t np, float* __restrict__ out,
+                               int64_t stride_p) {
   int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (r >= m) return;
+  P += (int64_t)blockIdx.y * stride_p;   // matrix of a batch
+  out += (int64_t)blockIdx.y * m;
   float s = 0.0f;
   for (int64_t t = 0; t < np; ++t) s += P[r * np + t];
   out[r] = s;
@@ -408,8 +443,19 @@ __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
     T* __restrict__ Wp, const float* __restrict__ U, const float* __restrict__ invd,
     const float* __restrict__ gptr, int64_t m, int64_t k, int i1, int ncols, int n_cand,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, T* __restrict__ Eslab, int64_t lde,
-    float* __restrict__ row_loss) {
+    float* __restrict__ row_loss, SweepStrides bs) {
   constexpr bool F64 = sizeof(T) == 8;
+  {   // matrix e = blockIdx.y of a batch
+    const int64_t e = blockIdx.y;
+    Wp += e * bs.wp;
+    U += e * bs.u;
+    invd += e * bs.invd;
+    gptr += e;
+    codes += e * m * (k / 2);
+    scales += e * m * (k / kBlock);
+    Eslab += e * bs.e;
+    if (row_loss) row_loss += e * m;
+  }
   constexpr int ROWS = SweepCfg<G>::ROWS;
   constexpr int NT = SweepCfg<G>::THREADS;
   __shared__ __attribute__((aligned(16))) float Ut[kBatch * UT_LD];      // Ut[c][r] = U[i1+r][i1+c]
@@ -637,26 +683,26 @@ __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
 template <int G, typename T>
 hipError_t sweep_launch_g(T* Wp, const float* U, const float* invd, const float* g, int64_t m, int64_t k,
                           int i1, int ncols, int n_cand, bool indep, uint8_t* codes, uint8_t* scales, T* Eslab,
-                          int64_t lde, float* row_loss, hipStream_t s) {
+                          int64_t lde, float* row_loss, hipStream_t s, int64_t nb, const SweepStrides& bs) {
   constexpr int ROWS = SweepCfg<G>::ROWS;
-  dim3 grid((unsigned)((m + ROWS - 1) / ROWS));
+  dim3 grid((unsigned)((m + ROWS - 1) / ROWS), (unsigned)nb);
   if (indep)
     hipLaunchKernelGGL((sweep_batch_kernel<G, T, true>), grid, dim3(SweepCfg<G>::THREADS), 0, s, Wp, U, invd, g, m,
-                       k, i1, ncols, n_cand, codes, scales, Eslab, lde, row_loss);
+                       k, i1, ncols, n_cand, codes, scales, Eslab, lde, row_loss, bs);
   else
     hipLaunchKernelGGL((sweep_batch_kernel<G, T, false>), grid, dim3(SweepCfg<G>::THREADS), 0, s, Wp, U, invd, g, m,
-                       k, i1, ncols, n_cand, codes, scales, Eslab, lde, row_loss);
+                       k, i1, ncols, n_cand, codes, scales, Eslab, lde, row_loss, bs);
   return hipGetLastError();
 }
 template <typename T>
 hipError_t sweep_launch_t(T* Wp, const float* U, const float* invd, const float* g, int64_t m, int64_t k, int i1,
                           int ncols, int n_cand, bool indep, uint8_t* codes, uint8_t* scales, T* Eslab, int64_t lde,
-                          float* row_loss, hipStream_t s) {
-  if (n_cand <= 1) return sweep_launch_g<1>(Wp, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s);
-  if (n_cand <= 2) return sweep_launch_g<2>(Wp, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s);
-  if (n_cand <= 4) return sweep_launch_g<4>(Wp, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s);
-  if (n_cand <= 8) return sweep_launch_g<8>(Wp, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s);
-  return sweep_launch_g<16>(Wp, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s);
+                          float* row_loss, hipStream_t s, int64_t nb, const SweepStrides& bs) {
+  if (n_cand <= 1) return sweep_launch_g<1>(Wp, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s, nb, bs);
+  if (n_cand <= 2) return sweep_launch_g<2>(Wp, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s, nb, bs);
+  if (n_cand <= 4) return sweep_launch_g<4>(Wp, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s, nb, bs);
+  if (n_cand <= 8) return sweep_launch_g<8>(Wp, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s, nb, bs);
+  return sweep_launch_g<16>(Wp, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s, nb, bs);
 }
 
 }  // namespace
@@ -692,69 +738,84 @@ hipError_t dequant_launch(const uint8_t* codes, const uint8_t* scales, const flo
 }
 
 hipError_t rtn_launch(const void* W, int bf16, int64_t m, int64_t k, int64_t ldw, const float* g, int n_cand,
-                      uint8_t* codes, uint8_t* scales, float* row_loss, hipStream_t s) {
+                      uint8_t* codes, uint8_t* scales, float* row_loss, hipStream_t s, int64_t nb, int64_t stride_w) {
   int64_t nblk = m * (k / kBlock);
-  dim3 grid((unsigned)((nblk + 255) / 256));
-  const bool vec = ((uintptr_t)W % 16 == 0) && (ldw % (bf16 ? 8 : 4) == 0);
+  dim3 grid((unsigned)((nblk + 255) / 256), (unsigned)nb);
+  const int64_t es = bf16 ? 2 : 4;
+  const bool vec = ((uintptr_t)W % 16 == 0) && (ldw % (bf16 ? 8 : 4) == 0) && ((stride_w * es) % 16 == 0);
   if (bf16)
-    hipLaunchKernelGGL(rtn_kernel<1>, grid, dim3(256), 0, s, W, m, k, ldw, g, n_cand, codes, scales, vec);
+    hipLaunchKernelGGL(rtn_kernel<1>, grid, dim3(256), 0, s, W, m, k, ldw, g, n_cand, codes, scales, vec, stride_w);
   else
-    hipLaunchKernelGGL(rtn_kernel<0>, grid, dim3(256), 0, s, W, m, k, ldw, g, n_cand, codes, scales, vec);
-  if (row_loss) hipLaunchKernelGGL(fill_kernel, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, s, row_loss, m, 0.0f);
+    hipLaunchKernelGGL(rtn_kernel<0>, grid, dim3(256), 0, s, W, m, k, ldw, g, n_cand, codes, scales, vec, stride_w);
+  if (row_loss)
+    hipLaunchKernelGGL(fill_kernel, dim3((unsigned)((nb * m + 255) / 256)), dim3(256), 0, s, row_loss, nb * m, 0.0f);
   return hipGetLastError();
 }
 
 hipError_t load_working_copy(const void* W, int bf16, int64_t m, int64_t k, int64_t ldw, float* Wp,
-                             hipStream_t s) {
-  dim3 grid((unsigned)((m * k / 4 + 255) / 256));
+                             hipStream_t s, int64_t nb, int64_t stride_w, int64_t stride_wp) {
+  dim3 grid((unsigned)((m * k / 4 + 255) / 256), (unsigned)nb);
   if (bf16)
-    hipLaunchKernelGGL(load_working_kernel<1>, grid, dim3(256), 0, s, W, m, k, ldw, Wp);
+    hipLaunchKernelGGL(load_working_kernel<1>, grid, dim3(256), 0, s, W, m, k, ldw, Wp, stride_w, stride_wp);
   else
-    hipLaunchKernelGGL(load_working_kernel<0>, grid, dim3(256), 0, s, W, m, k, ldw, Wp);
+    hipLaunchKernelGGL(load_working_kernel<0>, grid, dim3(256), 0, s, W, m, k, ldw, Wp, stride_w, stride_wp);
   return hipGetLastError();
 }
 
-hipError_t inv_diag_launch(const float* U, int64_t k, float* invd, hipStream_t s) {
-  hipLaunchKernelGGL(inv_diag_kernel, dim3((unsigned)((k + 255) / 256)), dim3(256), 0, s, U, k, invd);
+hipError_t inv_diag_launch(const float* U, int64_t k, float* invd, hipStream_t s, int64_t nb, int64_t stride_u,
+                           int64_t stride_invd) {
+  hipLaunchKernelGGL(inv_diag_kernel, dim3((unsigned)((k + 255) / 256), (unsigned)nb), dim3(256), 0, s, U, k, invd,
+                     stride_u, stride_invd);
   return hipGetLastError();
 }
 
 hipError_t load_working_copy_f64(const void* W, int bf16, int64_t m, int64_t k, int64_t ldw, double* Wp,
-                                 hipStream_t s) {
-  dim3 grid((unsigned)((m * k + 255) / 256));
+                                 hipStream_t s, int64_t nb, int64_t stride_w, int64_t stride_wp) {
+  dim3 grid((unsigned)((m * k + 255) / 256), (unsigned)nb);
   if (bf16)
-    hipLaunchKernelGGL(load_working_f64_kernel<1>, grid, dim3(256), 0, s, W, m, k, ldw, Wp);
+    hipLaunchKernelGGL(load_working_f64_kernel<1>, grid, dim3(256), 0, s, W, m, k, ldw, Wp, stride_w, stride_wp);
   else
-    hipLaunchKernelGGL(load_working_f64_kernel<0>, grid, dim3(256), 0, s, W, m, k, ldw, Wp);
+    hipLaunchKernelGGL(load_working_f64_kernel<0>, grid, dim3(256), 0, s, W, m, k, ldw, Wp, stride_w, stride_wp);
   return hipGetLastError();
 }
 
 hipError_t sweep_batch_launch(float* Wp, const float* U, const float* invd, const float* g, int64_t m, int64_t k,
                               int i1, int ncols, int n_cand, bool indep, uint8_t* codes, uint8_t* scales,
-                              float* Eslab, int64_t lde, float* row_loss, hipStream_t s) {
-  return sweep_launch_t<float>(Wp, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s);
+                              float* Eslab, int64_t lde, float* row_loss, hipStream_t s, int64_t nb,
+                              const SweepStrides& bs) {
+  return sweep_launch_t<float>(Wp, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s,
+                               nb, bs);
 }
 hipError_t sweep_batch_launch_f64(double* Wp, const float* U, const float* g, int64_t m, int64_t k, int i1,
                                   int ncols, int n_cand, bool indep, uint8_t* codes, uint8_t* scales, double* Eslab,
-                                  int64_t lde, float* row_loss, hipStream_t s) {
-  return sweep_launch_t<double>(Wp, U, U, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s);
+                                  int64_t lde, float* row_loss, hipStream_t s, int64_t nb, const SweepStrides& bs) {
+  // the fp64 sweep divides by U_jj itself: invd is not read (U is passed in its place)
+  SweepStrides b2 = bs;
+  b2.invd = bs.u;
+  return sweep_launch_t<double>(Wp, U, U, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s,
+                                nb, b2);
 }
 
 hipError_t delta_w_launch(const void* W, int bf16, int64_t m, int64_t k, int64_t ldw, const uint8_t* codes,
-                          const uint8_t* scales, const float* g, float* dW, hipStream_t s, int64_t c0, int64_t c1) {
+                          const uint8_t* scales, const float* g, float* dW, hipStream_t s, int64_t c0, int64_t c1,
+                          int64_t nb, int64_t stride_w, int64_t stride_dw) {
   if (c1 < 0) c1 = k;
   const int64_t blk0 = c0 / kBlock, nblk = (c1 - c0) / kBlock;
   if (m <= 0 || nblk <= 0) return hipSuccess;
-  dim3 grid((unsigned)((m * nblk + 255) / 256));
+  dim3 grid((unsigned)((m * nblk + 255) / 256), (unsigned)nb);
   if (bf16)
-    hipLaunchKernelGGL(delta_w_kernel<1>, grid, dim3(256), 0, s, W, m, k, ldw, codes, scales, g, dW, blk0, nblk);
+    hipLaunchKernelGGL(delta_w_kernel<1>, grid, dim3(256), 0, s, W, m, k, ldw, codes, scales, g, dW, blk0, nblk,
+                       stride_w, stride_dw);
   else
-    hipLaunchKernelGGL(delta_w_kernel<0>, grid, dim3(256), 0, s, W, m, k, ldw, codes, scales, g, dW, blk0, nblk);
+    hipLaunchKernelGGL(delta_w_kernel<0>, grid, dim3(256), 0, s, W, m, k, ldw, codes, scales, g, dW, blk0, nblk,
+                       stride_w, stride_dw);
   return hipGetLastError();
 }
 
-hipError_t row_sum_launch(const float* P, int64_t m, int64_t np, float* out, hipStream_t s) {
-  hipLaunchKernelGGL(row_sum_kernel, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, s, P, m, np, out);
+hipError_t row_sum_launch(const float* P, int64_t m, int64_t np, float* out, hipStream_t s, int64_t nb,
+                          int64_t stride_p) {
+  hipLaunchKernelGGL(row_sum_kernel, dim3((unsigned)((m + 255) / 256), (unsigned)nb), dim3(256), 0, s, P, m, np, out,
+                     stride_p);
   return hipGetLastError();
 }
 
@@ -784,14 +845,15 @@ hipError_t nonfinite_scan_launch(const void* A, int bf16, int64_t rows, int64_t 
 
 hipError_t reject_nonfinite_rows_launch(const void* W, int bf16, int64_t m, int64_t k, int64_t ldw, const float* g,
                                         uint8_t* codes, uint8_t* scales, float* row_err, float* row_loss,
-                                        hipStream_t s) {
-  const bool vec = rows_vectorizable(W, bf16, k, ldw);
+                                        hipStream_t s, int64_t nb, int64_t stride_w) {
+  const bool vec = rows_vectorizable(W, bf16, k, ldw) && (stride_w * (bf16 ? 2 : 4)) % 16 == 0;
+  const dim3 grid((unsigned)scan_grid(m), (unsigned)nb);
   if (bf16)
-    hipLaunchKernelGGL(reject_nonfinite_rows_kernel<1>, dim3(scan_grid(m)), dim3(256), 0, s, W, m, k, ldw, vec, g,
-                       codes, scales, row_err, row_loss);
+    hipLaunchKernelGGL(reject_nonfinite_rows_kernel<1>, grid, dim3(256), 0, s, W, m, k, ldw, vec, g, codes, scales,
+                       row_err, row_loss, stride_w);
   else
-    hipLaunchKernelGGL(reject_nonfinite_rows_kernel<0>, dim3(scan_grid(m)), dim3(256), 0, s, W, m, k, ldw, vec, g,
-                       codes, scales, row_err, row_loss);
+    hipLaunchKernelGGL(reject_nonfinite_rows_kernel<0>, grid, dim3(256), 0, s, W, m, k, ldw, vec, g, codes, scales,
+                       row_err, row_loss, stride_w);
   return hipGetLastError();
 }
 

@@ -43,18 +43,9 @@ namespace nvq {
 
 namespace {
 
-#ifndef NVQ_SYRK_ST
-#define NVQ_SYRK_ST 32
-#endif
-#ifndef NVQ_SYRK_NS
-#define NVQ_SYRK_NS 4
-#endif
-constexpr int ST = NVQ_SYRK_ST;   // tokens per stage
-constexpr int NS = NVQ_SYRK_NS;   // ring depth (stages in flight + the one being multiplied)
-#ifndef NVQ_SYRK_HEAD16
-#define NVQ_SYRK_HEAD16 13
-#endif
-constexpr int HEAD16 = NVQ_SYRK_HEAD16;   // sixteenths of a token range a strip pair covers in the first launch
+constexpr int ST = 32;       // tokens per stage
+constexpr int NS = 4;        // ring depth (stages in flight + the one being multiplied)
+constexpr int HEAD16 = 13;   // sixteenths of a token range a strip pair covers in the first launch
 constexpr int TSPLIT = 4;                 // tail pieces per (range, strip pair)
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));

@@ -146,6 +146,29 @@ def mlp_layer(m, k, n):
     return W, X
 
 
+def mlp_block_weights(d=4096, f=14336):
+    """Gate, up [f, d] and down [d, f] weights of one MLP block (bf16 values, N(0, 0.015^2))."""
+    Wg = weights("mlp", f, d, 0.015)
+    Wu = to_bf16_values(rng("mlp", 21).standard_normal((f, d)).astype(np.float32) * np.float32(0.015))
+    Wd = weights("mlp", d, f, 0.015)   # the same recipe, a [d x f] draw
+    return Wg, Wu, Wd
+
+
+def mlp_down_activations(Xd, Wg, Wu, chunk=8192):
+    """The down projection's inputs bf16(SiLU(X W_gate^T) * (X W_up^T)) from the block's own bf16
+    activations Xd (a torch tensor on any device; fp32 products, chunks of tokens).  A model forward
+    pass that makes inputs, not part of the quantization method."""
+    import torch
+    dev = Xd.device
+    Wg_t = torch.from_numpy(Wg).to(dev).t().contiguous()
+    Wu_t = torch.from_numpy(Wu).to(dev).t().contiguous()
+    out = torch.empty(Xd.shape[0], Wg.shape[0], dtype=torch.bfloat16, device=dev)
+    for c0 in range(0, Xd.shape[0], chunk):
+        xc = Xd[c0:c0 + chunk].float()
+        out[c0:c0 + chunk] = (torch.nn.functional.silu(xc @ Wg_t) * (xc @ Wu_t)).to(torch.bfloat16)
+    return out
+
+
 def sparse_layer(m, k, n):
     W = weights("sparse", m, k, 0.01, outlier_frac=0.0005)
     X = activations("sparse", n, k, kind="sparse")
