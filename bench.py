@@ -306,6 +306,60 @@ class LayerTimer:
         return ms, per
 
 
+PACK_M, PACK_K = 8192, 28672
+
+
+def pack_roofline(nvq, lib, P, dev, reps=20):
+    """RTN encode + pack (one candidate: the absmax scale) and bf16 dequantization of the 70B-class down
+    projection's W (8192 x 28672 bf16, synthetic): algorithmic HBM bytes 2.5625 per weight each way
+    (2 B of bf16 plus 0.5 B of codes and 1/16 B of scales), over the kernel time from events on the
+    library's stream."""
+    import torch
+    import synth
+    m, k = PACK_M, PACK_K
+    W = synth.to_bf16_tensor(synth.weights("sparse", m, k, 0.01, outlier_frac=0.0005)).to(dev)
+    g = torch.empty(1, dtype=torch.float32, device=dev)
+    codes = torch.empty(m, k // 2, dtype=torch.uint8, device=dev)
+    scales = torch.empty(m, k // 16, dtype=torch.uint8, device=dev)
+    out = torch.empty(m, k, dtype=torch.bfloat16, device=dev)
+    gws_n = lib.nvfp4_global_scale_workspace_size(m, k)
+    gws = torch.empty(max(1, gws_n), dtype=torch.uint8, device=dev)
+    qws_n = lib.gptq_nvfp4_workspace_size(m, k, nvq.FLAG_RTN)
+    qws = torch.empty(max(1, qws_n), dtype=torch.uint8, device=dev)
+    s = nvq._stream()
+    assert lib.nvfp4_global_scale(P(W), nvq.NVQ_DTYPE_BF16, m, k, k, P(g), P(gws), gws_n, s) == 0
+
+    def enc():
+        assert lib.gptq_nvfp4_quantize(P(W), nvq.NVQ_DTYPE_BF16, m, k, k, None, None, P(g), 1,
+                                       nvq.FLAG_RTN | nvq.FLAG_NO_ERR, P(codes), P(scales), None, None, P(qws),
+                                       qws_n, s) == 0
+
+    def dec():
+        assert lib.nvfp4_dequantize(P(codes), P(scales), P(g), m, k, P(out), nvq.NVQ_DTYPE_BF16, s) == 0
+
+    res = {}
+    for name, fn in (("rtn_encode", enc), ("dequant", dec)):
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = e0.elapsed_time(e1) / reps
+    nbytes = m * k * 2.5625
+    ach = {n: nbytes / (ms / 1e3) / 1e9 for n, ms in res.items()}
+    worst = min(ach, key=ach.get)
+    del W, codes, scales, out, qws
+    torch.cuda.empty_cache()
+    return {"bound": "hbm", "achieved": round(ach[worst], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(ach[worst] / PEAK_HBM_GBS, 4), "traffic": None,
+            "kernel": f"{worst} (the slower of rtn_encode and dequant)", "workload": f"W {m}x{k} bf16",
+            "bytes_per_call": int(nbytes),
+            "ms_per_call": {n: round(v, 4) for n, v in res.items()},
+            "gbs": {n: round(v, 1) for n, v in ach.items()}}
+
+
 def hessian_roofline(n, k, ms_h):
     achieved = n * k * (k + 1) / (ms_h / 1e3) / 1e12
     return {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -610,6 +664,10 @@ def main():
     torch.cuda.synchronize()
     rtn_ms = rtn_ev[0].elapsed_time(rtn_ev[1]) / reps
 
+    # The NVFP4 pack and unpack kernels at a size where HBM, not launch latency,
+    # bounds them: the 70B-class down projection's W (8192 x 28672 bf16).
+    roofline_pack = pack_roofline(nvq, lib, P, dev)
+
     # Untimed streaming kernel of known size (reads and writes CAL_COPY_BYTES):
     # the calibration dispatch for rocprofv3's HBM byte counters (see summarize_pmc).
     cal = torch.bitwise_not(Xd.view(torch.int32).reshape(-1)[:CAL_COPY_BYTES // 4])
@@ -624,6 +682,7 @@ def main():
         "config": {"workload": WORKLOAD,
                    "d_out": M, "d_in": K_IN, "tokens": N_TOK, "n_cand": N_CAND},
         "roofline": roofline,
+        "roofline_pack": roofline_pack,
         "stages_ms": {k: round(v, 3) for k, v in per_stage.items()},
         "rtn_encode_ms": round(rtn_ms, 4),
         "h2d_inputs_s": round(h2d_s, 3),

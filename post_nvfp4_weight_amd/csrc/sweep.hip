@@ -12,6 +12,8 @@
 // entries are read as wave-wide broadcasts), and after each block the row's G
 // lanes update the later columns of the batch.  Columns beyond the batch are
 // updated afterwards by one fp32 MFMA GEMM with the batch's error slab.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -85,44 +87,64 @@ __global__ __launch_bounds__(256) void gscale_finish_kernel(const float* __restr
 }
 
 // ---- dequantization ---------------------------------------------------------------
+// The codes [m][k/2], scales [m][k/16] and output [m][k] are dense, so they are
+// one stream of half blocks (8 weights: 4 bytes of codes, half a scale byte,
+// 16 bytes of bf16 or 32 of fp32 output).  A grid of a few workgroups per CU
+// strides over the stream; consecutive lanes take consecutive half blocks, so
+// a wave's loads and stores are contiguous, and a thread issues the loads of
+// DQ_U half blocks before any of their stores.
+constexpr int DQ_U = 4;
 template <int OUT_BF16>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict__ codes,
                                                       const uint8_t* __restrict__ scales,
-                                                      const float* __restrict__ gptr, int64_t m, int64_t k,
+                                                      const float* __restrict__ gptr, int64_t nhalf,
                                                       void* __restrict__ out) {
-  // One thread per half block (8 weights: 4 bytes of codes, 16 bytes of bf16
-  // out), so that a wave's loads and stores are contiguous.
-  const int64_t nhalf = m * (k / kBlock) * 2;
-  const int64_t hb = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (hb >= nhalf) return;
   const float g = *gptr;
-  const uint8_t sc = scales[hb >> 1];
-  // 0x7F / 0xFF is E4M3FN's NaN (the code of a row rejected by the finite check).
-  const float s = (sc & 0x7F) == 0x7F ? __builtin_nanf("") : e4m3_value(sc & 0x7F);
-  const bool neg_scale = sc & 0x80;
-  const uint32_t c = *(const uint32_t*)(codes + hb * 4);
-  float v[8];
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t h0 = (int64_t)blockIdx.x * 256 + threadIdx.x; h0 < nhalf; h0 += DQ_U * stride) {
+    uint32_t c[DQ_U];
+    uint32_t sc[DQ_U];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const float x = e2m1_dequant((int)((c >> (4 * j)) & 0xF), s, g);
-    v[j] = neg_scale ? -x : x;
-  }
-  if (OUT_BF16) {
-    u32x4 o;
+    for (int u = 0; u < DQ_U; ++u) {
+      const int64_t hb = min(h0 + u * stride, nhalf - 1);   // clamped: every load is valid
+      c[u] = *(const uint32_t*)(codes + hb * 4);
+      sc[u] = scales[hb >> 1];
+    }
 #pragma unroll
-    for (int w = 0; w < 4; ++w)
-      o[w] = (uint32_t)f32_to_bf16_bits(v[2 * w]) | ((uint32_t)f32_to_bf16_bits(v[2 * w + 1]) << 16);
-    *(u32x4*)((uint16_t*)out + hb * 8) = o;
-  } else {
-    f32x4* dst = (f32x4*)((float*)out + hb * 8);
-    dst[0] = f32x4{v[0], v[1], v[2], v[3]};
-    dst[1] = f32x4{v[4], v[5], v[6], v[7]};
+    for (int u = 0; u < DQ_U; ++u) {
+      const int64_t hb = h0 + u * stride;
+      if (hb >= nhalf) break;
+      // 0x7F / 0xFF is E4M3FN's NaN (the code of a row rejected by the finite check).
+      const float s = (sc[u] & 0x7F) == 0x7F ? __builtin_nanf("") : e4m3_value(sc[u] & 0x7F);
+      const bool neg_scale = sc[u] & 0x80;
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float x = e2m1_dequant((int)((c[u] >> (4 * j)) & 0xF), s, g);
+        v[j] = neg_scale ? -x : x;
+      }
+      if (OUT_BF16) {
+        u32x4 o;
+#pragma unroll
+        for (int w = 0; w < 4; ++w)
+          o[w] = (uint32_t)f32_to_bf16_bits(v[2 * w]) | ((uint32_t)f32_to_bf16_bits(v[2 * w + 1]) << 16);
+        *(u32x4*)((uint16_t*)out + hb * 8) = o;
+      } else {
+        f32x4* dst = (f32x4*)((float*)out + hb * 8);
+        dst[0] = f32x4{v[0], v[1], v[2], v[3]};
+        dst[1] = f32x4{v[4], v[5], v[6], v[7]};
+      }
+    }
   }
 }
 
 // ---- round to nearest (no GPTQ updates) ------------------------------------------
-// One thread per (row, block).  Candidate scores are sum_j (w_j - q_j)^2 with
-// separately rounded products and sums in column order.
+// One thread per (row, block) at a time, striding over the blocks of the
+// matrix (codes and scales are dense, so block b's codes are at 8 b and its
+// scale at b; W's block is at row * ldw + 16 * column block).  Candidate scores
+// are sum_j (w_j - q_j)^2 with separately rounded products and sums in column
+// order; with one candidate (the absmax scale) there is nothing to compare,
+// and no score is formed.
 // vec: every block starts 16-byte aligned (W aligned, ldw a multiple of 8
 // bf16 or 4 fp32 values), so it is read with 16-byte loads.
 template <int BF16>
@@ -130,75 +152,90 @@ __global__ __launch_bounds__(256) void rtn_kernel(const void* __restrict__ W, in
                                                   const float* __restrict__ gptr, int n_cand,
                                                   uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
                                                   bool vec, int64_t stride_w) {
-  const int64_t nbk = k / kBlock;
-  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (b >= m * nbk) return;
+  const int64_t nbk = k / kBlock, nblk = m * nbk;
   {   // matrix e = blockIdx.y of a batch: W + e * stride_w elements, g[e], its codes and scales
     const int64_t e = blockIdx.y;
     W = (const char*)W + e * stride_w * (BF16 ? 2 : 4);
     gptr += e;
     codes += e * m * (k / 2);
-    scales += e * m * nbk;
+    scales += e * nblk;
   }
-  const int64_t row = b / nbk, blk = b % nbk;
   const float g = *gptr;
-  float w[16];
-  const int64_t base = row * ldw + blk * 16;
-  if (vec) {
-    if (BF16) {
-      const u32x4* src = (const u32x4*)((const uint16_t*)W + base);
+  const float r6g = 1.0f / (6.0f * g);
+  const bool dense = ldw == k;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x; b < nblk; b += stride) {
+    const int64_t base = dense ? b * 16 : (b / nbk) * ldw + (b % nbk) * 16;
+    float w[16];
+    if (vec) {
+      if (BF16) {
+        const u32x4* src = (const u32x4*)((const uint16_t*)W + base);
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const u32x4 u = src[h];
+        for (int h = 0; h < 2; ++h) {
+          const u32x4 u = src[h];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            w[8 * h + 2 * q] = __uint_as_float(u[q] << 16);
+            w[8 * h + 2 * q + 1] = __uint_as_float(u[q] & 0xFFFF0000u);
+          }
+        }
+      } else {
+        const f32x4* src = (const f32x4*)((const float*)W + base);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          w[8 * h + 2 * q] = __uint_as_float(u[q] << 16);
-          w[8 * h + 2 * q + 1] = __uint_as_float(u[q] & 0xFFFF0000u);
+          const f32x4 u = src[q];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) w[4 * q + t] = u[t];
         }
       }
     } else {
-      const f32x4* src = (const f32x4*)((const float*)W + base);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const f32x4 u = src[q];
+      for (int j = 0; j < 16; ++j) w[j] = load_w<BF16>(W, base + j);
+    }
+    float a = 0.0f;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) w[4 * q + t] = u[t];
+    for (int j = 0; j < 16; ++j) a = fmaxf(a, fabsf(w[j]));
+    int best_c = 0;
+    uint32_t best_lo = 0, best_hi = 0;
+    if (a > 0.0f) {
+      const int lo = candidate_lo(e4m3_code_of_ratio_any(a, g, r6g), n_cand);
+      if (n_cand == 1) {
+        const float s = e4m3_value(lo);
+        const float ts[7] = {0.25f * s, 0.75f * s, 1.25f * s, 1.75f * s, 2.5f * s, 3.5f * s, 5.0f * s};
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int idx = e2m1_index_search(fabsf(w[j]), g, ts);
+          const int code = idx | (int)(((__float_as_uint(w[j]) >> 31) & (uint32_t)(idx != 0)) << 3);
+          if (j < 8) best_lo |= (uint32_t)code << (4 * j); else best_hi |= (uint32_t)code << (4 * (j - 8));
+        }
+        best_c = lo;
+      } else {
+        float best = __builtin_inff();
+        for (int ci = 0; ci < n_cand; ++ci) {
+          const int c = lo + ci;
+          const float s = e4m3_value(c);
+          const float hs = 0.5f * s;
+          const float ts[7] = {0.25f * s, 0.75f * s, 1.25f * s, 1.75f * s, 2.5f * s, 3.5f * s, 5.0f * s};
+          float score = 0.0f;
+          uint32_t plo = 0, phi = 0;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            // e2m1_encode and e2m1_dequant's values, with the sign set by bit operations
+            const int idx = e2m1_index_search(fabsf(w[j]), g, ts);
+            const int code = idx | (int)(((__float_as_uint(w[j]) >> 31) & (uint32_t)(idx != 0)) << 3);
+            const float dq =
+                __uint_as_float(__float_as_uint(e2m1_twice_mag(idx) * hs * g) | ((uint32_t)(code & 8) << 28));
+            float e = __fsub_rn(w[j], dq);
+            score = __fadd_rn(score, __fmul_rn(e, e));
+            if (j < 8) plo |= (uint32_t)code << (4 * j); else phi |= (uint32_t)code << (4 * (j - 8));
+          }
+          if (score < best) { best = score; best_c = c; best_lo = plo; best_hi = phi; }
+        }
       }
     }
-  } else {
-#pragma unroll
-    for (int j = 0; j < 16; ++j) w[j] = load_w<BF16>(W, base + j);
+    *(u32x2*)(codes + b * 8) = u32x2{best_lo, best_hi};
+    scales[b] = (uint8_t)best_c;
   }
-  float a = 0.0f;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) a = fmaxf(a, fabsf(w[j]));
-  int best_c = 0;
-  uint32_t best_lo = 0, best_hi = 0;
-  if (a > 0.0f) {
-    const int lo = candidate_lo(e4m3_code_of_ratio_any(a, g, 1.0f / (6.0f * g)), n_cand);
-    float best = __builtin_inff();
-    for (int ci = 0; ci < n_cand; ++ci) {
-      const int c = lo + ci;
-      const float s = e4m3_value(c);
-      const float hs = 0.5f * s;
-      const float ts[7] = {0.25f * s, 0.75f * s, 1.25f * s, 1.75f * s, 2.5f * s, 3.5f * s, 5.0f * s};
-      float score = 0.0f;
-      uint32_t plo = 0, phi = 0;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        // e2m1_encode and e2m1_dequant's values, with the sign set by bit operations
-        const int idx = e2m1_index_search(fabsf(w[j]), g, ts);
-        const int code = idx | (int)(((__float_as_uint(w[j]) >> 31) & (uint32_t)(idx != 0)) << 3);
-        const float dq = __uint_as_float(__float_as_uint(e2m1_twice_mag(idx) * hs * g) | ((uint32_t)(code & 8) << 28));
-        float e = __fsub_rn(w[j], dq);
-        score = __fadd_rn(score, __fmul_rn(e, e));
-        if (j < 8) plo |= (uint32_t)code << (4 * j); else phi |= (uint32_t)code << (4 * (j - 8));
-      }
-      if (score < best) { best = score; best_c = c; best_lo = plo; best_hi = phi; }
-    }
-  }
-  *(u32x2*)(codes + row * (k / 2) + blk * 8) = u32x2{best_lo, best_hi};
-  scales[row * nbk + blk] = (uint8_t)best_c;
 }
 
 // ---- finite checks ------------------------------------------------------------------
@@ -725,22 +762,29 @@ hipError_t global_scale_launch(const void* W, int bf16, int64_t m, int64_t k, in
   return hipGetLastError();
 }
 
+// Workgroups of a grid-stride streaming launch: enough for every CU several
+// times over, never more than the items need.
+static unsigned stream_grid(int64_t items_per_wg) {
+  const int64_t cap = 8 * 256;
+  return (unsigned)std::max<int64_t>(1, std::min<int64_t>(items_per_wg, cap));
+}
+
 hipError_t dequant_launch(const uint8_t* codes, const uint8_t* scales, const float* g, int64_t m, int64_t k,
                           void* out, int out_bf16, hipStream_t s) {
-  int64_t nblk = m * (k / kBlock);
-  if (nblk == 0) return hipSuccess;
-  dim3 grid((unsigned)((2 * nblk + 255) / 256));
+  const int64_t nhalf = 2 * m * (k / kBlock);
+  if (nhalf == 0) return hipSuccess;
+  const dim3 grid(stream_grid((nhalf + 256 * DQ_U - 1) / (256 * DQ_U)));
   if (out_bf16)
-    hipLaunchKernelGGL(dequant_kernel<1>, grid, dim3(256), 0, s, codes, scales, g, m, k, out);
+    hipLaunchKernelGGL(dequant_kernel<1>, grid, dim3(256), 0, s, codes, scales, g, nhalf, out);
   else
-    hipLaunchKernelGGL(dequant_kernel<0>, grid, dim3(256), 0, s, codes, scales, g, m, k, out);
+    hipLaunchKernelGGL(dequant_kernel<0>, grid, dim3(256), 0, s, codes, scales, g, nhalf, out);
   return hipGetLastError();
 }
 
 hipError_t rtn_launch(const void* W, int bf16, int64_t m, int64_t k, int64_t ldw, const float* g, int n_cand,
                       uint8_t* codes, uint8_t* scales, float* row_loss, hipStream_t s, int64_t nb, int64_t stride_w) {
   int64_t nblk = m * (k / kBlock);
-  dim3 grid((unsigned)((nblk + 255) / 256), (unsigned)nb);
+  dim3 grid(stream_grid((nblk + 255) / 256), (unsigned)nb);
   const int64_t es = bf16 ? 2 : 4;
   const bool vec = ((uintptr_t)W % 16 == 0) && (ldw % (bf16 ? 8 : 4) == 0) && ((stride_w * es) % 16 == 0);
   if (bf16)
