@@ -35,6 +35,9 @@ WORKLOAD = ("attention-projection layer W 4096x4096 bf16, X 262144x4096 bf16, 16
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hessian_accumulate_attn_proj_4096x4096_n262144_hbm_traffic.json")
 HESSIAN_SOURCES = [os.path.join(ROOT, "post_nvfp4_weight_amd", "csrc", f) for f in ("syrk.hip", "common.h")]
 CAL_COPY_BYTES = 512 << 20
+# Counter-measured bytes of the streaming kernels (sweep batch, RTN encode, dequantize), same passes.
+STREAM_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sweep_rtn_dequant_hbm_traffic.json")
+STREAM_SOURCES = [os.path.join(ROOT, "post_nvfp4_weight_amd", "csrc", f) for f in ("sweep.hip", "common.h")]
 
 
 def log(*a):
@@ -72,7 +75,17 @@ def cpu_baseline():
     gptq.weighted_error(W[:rows], deq, H_s)
     t_s = (time.perf_counter() - t0) * (M / rows)
     total = t_h + t_f + t_s
-    return {"value": M * K_IN / total / 1e6, "unit": "Mparam/s", "cores": cores, "kind": "oracle",
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": M * K_IN / total / 1e6, "unit": "Mparam/s", "cores": cores, "cpu_model": cpu_model,
+            "kind": "oracle",
             "sample": f"hessian on {n_s} of {N_TOK} tokens (x{N_TOK // n_s}), full {K_IN}x{K_IN} factor, "
                       f"sweep+error on {rows} of {M} rows (x{M // rows}); stage seconds "
                       f"H={t_h:.1f} factor={t_f:.1f} sweep={t_s:.1f}"}
@@ -85,6 +98,27 @@ def hessian_source_digest():
         with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def stream_source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for f in STREAM_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_stream_traffic(key):
+    """Measured HBM bytes per launch of a streaming kernel, or None if absent or taken on other sources."""
+    try:
+        with open(STREAM_TRAFFIC_FILE) as fh:
+            d = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if d.get("source_digest") != stream_source_digest():
+        return None
+    return d.get("kernels", {}).get(key, {}).get("hbm_bytes")
 
 
 def load_traffic():
@@ -137,6 +171,31 @@ def summarize_pmc(fetch_csv, write_csv):
     with open(TRAFFIC_FILE, "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps(out))
+    # The streaming kernels: per-launch bytes of the sweep (one 128-column
+    # batch of the benchmarked layer) and of the pack kernels on the 70B-class
+    # W (the largest launches of rtn_kernel and dequant_kernel in the run).
+    kinds = {"sweep_batch_kernel": "sweep_batch_kernel<16, float, false> (one 128-column batch, 4096 rows)",
+             "rtn_kernel": f"rtn_kernel<1> (W {PACK_M}x{PACK_K} bf16, one candidate)",
+             "dequant_kernel": f"dequant_kernel<1> (W {PACK_M}x{PACK_K}, bf16 out)"}
+    stream = {"commands": out["commands"], "workload": WORKLOAD, "unit": "bytes per launch",
+              "source_digest": stream_source_digest(),
+              "calibration_copy_bytes": CAL_COPY_BYTES, "kernels": {}}
+    for key, desc in kinds.items():
+        ent = {"kernel": desc}
+        for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+            rows = per_dispatch(path, name)
+            vals = [v for n, v in rows if key in n]
+            copies = [v for n, v in rows if "bitwise_not" in n]
+            factor = (CAL_COPY_BYTES / 1024.0) / max(copies)
+            kib = (sum(vals) / len(vals)) if key == "sweep_batch_kernel" else max(vals)
+            ent[name] = round(kib * 1024.0 * factor)
+        ent["hbm_bytes"] = ent["FETCH_SIZE"] + ent["WRITE_SIZE"]
+        if key != "sweep_batch_kernel":
+            ent["algorithmic_bytes"] = int(PACK_M * PACK_K * 2.5625)
+        stream["kernels"][key] = ent
+    with open(STREAM_TRAFFIC_FILE, "w") as fh:
+        json.dump(stream, fh, indent=1)
+    print(json.dumps(stream))
 
 
 def streamed(nvq, Xh, dev):
@@ -353,7 +412,8 @@ def pack_roofline(nvq, lib, P, dev, reps=20):
     del W, codes, scales, out, qws
     torch.cuda.empty_cache()
     return {"bound": "hbm", "achieved": round(ach[worst], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(ach[worst] / PEAK_HBM_GBS, 4), "traffic": None,
+            "frac": round(ach[worst] / PEAK_HBM_GBS, 4),
+            "traffic": load_stream_traffic("rtn_kernel" if worst == "rtn_encode" else "dequant_kernel"),
             "kernel": f"{worst} (the slower of rtn_encode and dequant)", "workload": f"W {m}x{k} bf16",
             "bytes_per_call": int(nbytes),
             "ms_per_call": {n: round(v, 4) for n, v in res.items()},
