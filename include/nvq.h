@@ -61,10 +61,22 @@ extern "C" {
 #define NVQ_FLAG_NO_ERR 2u
 /* fp64 working precision for the sweep: working weights, errors, scores and
  * the lazy updates are fp64 (U and H are read as fp32 inputs; the weighted
- * error is computed as without the flag).  For layers whose Hessian spans
- * many orders of magnitude, where fp32 rounding alone moves more than 0.1%
- * of the decisions of the exact computation.  Needs a larger workspace
- * (gptq_nvfp4_workspace_size with the same flags).  Ignored with RTN. */
+ * error is computed as without the flag).  Needs a larger workspace
+ * (gptq_nvfp4_workspace_size with the same flags).  Ignored with RTN.
+ * When to set it.  GPTQ's column coupling carries every flipped near-tie
+ * decision along its row, so the working precision decides how many
+ * decisions differ from the exact computation.  Measured against an fp64
+ * computation:
+ *   - layers fed by zero-mean activations (attention projections, MLP gate
+ *     and up projections) stay well inside 0.1% in fp32 (about 2e-5 of
+ *     codes and scales over a whole 4096 x 4096 layer): leave the flag off;
+ *   - layers fed by activations with a large common mean or heavy tails
+ *     (MLP down projections over gated activations; sparse non-negative
+ *     inputs), whose Hessians span about 8 orders of magnitude, move 0.1% to
+ *     0.7% of the decisions in fp32: set the flag (the lazy updates then run
+ *     on the fp64 matrix cores, whose dense peak is half the fp32 one).
+ * The library cannot inspect H's range without synchronizing, so the caller
+ * chooses per layer. */
 #define NVQ_FLAG_FP64   4u
 /* Block-independent scale selection, the baseline that Schur Replay corrects
  * ("Replay the Curvature", Abstract: scoring blocks independently can
