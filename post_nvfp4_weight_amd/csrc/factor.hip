@@ -140,7 +140,7 @@ __device__ __forceinline__ void chol16(float (&c)[16], float (&x)[16], float lf,
 // transpose, and the step's contribution is subtracted from the columns to
 // its right, both as 16 x 16 tiles on the matrix cores
 // (v_mfma_f32_16x16x4f32, one tile per wave at a time).  Workgroup 0 stores
-// L11 into Ld (the same block of the inverse's buffer, zeroed beforehand,
+// L11 into Ld (the same block of the inverse's buffer,
 // which diag_inv_kernel later inverts in place): A's diagonal block is read by
 // every workgroup of the launch, so no workgroup may write it.  On a
 // non-positive pivot workgroup 0 also sets *info (once) to the order of the
@@ -294,16 +294,13 @@ __global__ __launch_bounds__(256) void panel_kernel(float* __restrict__ A, float
 }
 
 // Trailing update by the kw panel columns starting at column p: C -= P P^T
-// on the lower triangle, where P is those columns' L21 (rest x kw, at
-// A + (p+kw) k + p) and C the block right of and below them (rest x rest, at
-// A + (p+kw)(k+1)).  With lim < 0 every lower tile is updated; otherwise only
-// the tiles in the first lim 64-column blocks of C (grid lim x tiles; the
-// workgroups of tiles above the diagonal exit).  One workgroup per 64 x 64
-// tile; each wave holds a 32 x 32 quadrant in MFMA accumulators initialized
-// from C, and multiplies -P_i by P_j^T (v_mfma_f32_32x32x2f32) in chunks of
-// 64 columns, in column order, so that C is read and written once for all kw
-// columns and every element sees the same sums in the same order as kw / 64
-// separate updates.
+// on the lower triangle of the tiles in the first lim 64-column blocks of C,
+// where P is those columns' L21 (rest x kw, at A + (p+kw) k + p) and C the
+// block right of and below them (rest x rest, at A + (p+kw)(k+1)).  Grid
+// lim x tiles; the workgroups of tiles above the diagonal exit.  One
+// workgroup per 64 x 64 tile; each wave holds a 32 x 32 quadrant in MFMA
+// accumulators initialized from C, and multiplies -P_i by P_j^T
+// (v_mfma_f32_32x32x2f32) in chunks of 64 columns.
 constexpr int UP = NB + 2;   // LDS row stride: a lane's (row, k) reads hit 64 distinct banks
 __global__ __launch_bounds__(256) void chol_update_kernel(float* __restrict__ A, int64_t k, int64_t p,
                                                           int64_t rest, int kw, int lim) {
@@ -311,19 +308,9 @@ __global__ __launch_bounds__(256) void chol_update_kernel(float* __restrict__ A,
   A += (int64_t)blockIdx.y * k * k;   // matrix of a batch
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t t = blockIdx.x;
-  int64_t ti, tj;
-  if (lim < 0) {
-    // Tile t -> (ti, tj), tj <= ti, row-major over the lower triangle of tiles.
-    ti = (int64_t)((sqrt(8.0 * (double)t + 1.0) - 1.0) * 0.5);
-    while (ti * (ti + 1) / 2 > t) --ti;
-    while ((ti + 1) * (ti + 2) / 2 <= t) ++ti;
-    tj = t - ti * (ti + 1) / 2;
-  } else {
-    const int64_t nt = (rest + NB - 1) / NB;
-    tj = t / nt;
-    ti = t % nt;
-    if (ti < tj) return;
-  }
+  const int64_t nt = (rest + NB - 1) / NB;
+  const int64_t tj = t / nt, ti = t % nt;
+  if (ti < tj || tj >= lim) return;
   const float* P = A + (p + kw) * k + p;
   float* C = A + (p + kw) * k + p + kw;
   const int wr = wave >> 1, wc = wave & 1;
@@ -382,7 +369,11 @@ __global__ __launch_bounds__(256) void chol_update_kernel(float* __restrict__ A,
 // substitution (column c of the inverse), with the block in LDS so that row i
 // of L reaches every lane as broadcast reads (the same address in every
 // lane), four values at a time.  The block is read whole before it is
-// overwritten, and only by its own workgroup.
+// overwritten, and only by its own workgroup.  An even block also zeroes the
+// 64 x 64 block right of it: the inverse's products read the upper triangle
+// of each 128-aligned diagonal block (as zeros), and nothing else writes that
+// part of Linv (the panels write their diagonal blocks' upper triangles as
+// zeros).
 __global__ __launch_bounds__(64) void diag_inv_kernel(float* __restrict__ Linv, int64_t k) {
   Linv += (int64_t)blockIdx.y * k * k;   // matrix of a batch
   __shared__ __attribute__((aligned(16))) float Ls[NB][NB];
@@ -411,6 +402,9 @@ __global__ __launch_bounds__(64) void diag_inv_kernel(float* __restrict__ Linv, 
 #pragma unroll
   for (int i = 0; i < NB; ++i)
     if (i < nb && lane < nb) Linv[(p + i) * k + p + lane] = x[i];
+  if ((blockIdx.x & 1) == 0 && p + NB + lane < k) {
+    for (int i = 0; i < nb; ++i) Linv[(p + i) * k + p + NB + lane] = 0.0f;
+  }
 }
 
 // U[i][j] = Linv[k-1-i][k-1-j] for j >= i, 0 below the diagonal.
@@ -428,12 +422,6 @@ __global__ void flip_out_kernel(const float* __restrict__ Linv, int64_t k, float
     for (int u = 0; u < 4; ++u) v[u] = j + u >= i ? l[3 - u] : 0.0f;
   }
   *(f32x4*)(U + i * k + j) = v;
-}
-
-// p[0 .. 4 n4) = 0 in 16-byte stores (p 16-byte aligned).
-__global__ void zero_kernel(float* p, int64_t n4) {
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n4) ((f32x4*)p)[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 }
 
 }  // namespace
@@ -463,10 +451,6 @@ static hipError_t factor_pass(const float* H, int64_t k, int64_t nb, int64_t str
   const unsigned nbu = (unsigned)nb;
 
   hipLaunchKernelGGL(damping_kernel, dim3(nbu), dim3(256), 0, s, H, k, stride_h, damp_rel, lam, lambda_out, info);
-  // k % 16 == 0, so k * k is a multiple of 4 (and Linv, a multiple of k * k floats into the workspace, is
-  // 16-byte aligned).
-  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((nb * kk / 4 + 255) / 256)), dim3(256), 0, s, Linv,
-                     (int64_t)(nb * kk / 4));
   hipLaunchKernelGGL(flip_damp_kernel, dim3((unsigned)((k / 4 + 255) / 256), (unsigned)k, nbu), dim3(256), 0, s, H,
                      k, stride_h, lam, A, info);
   hipError_t e = hipGetLastError();
@@ -489,9 +473,18 @@ static hipError_t factor_pass(const float* H, int64_t k, int64_t nb, int64_t str
       hipLaunchKernelGGL(chol_update_kernel, dim3((unsigned)(lim * tiles), nbu), dim3(256), 0, s, A, k, p, rest, NB,
                          (int)lim);
     } else if (send < k) {
-      const int64_t rest2 = k - send, tiles = (rest2 + NB - 1) / NB;
-      hipLaunchKernelGGL(chol_update_kernel, dim3((unsigned)(tiles * (tiles + 1) / 2), nbu), dim3(256), 0, s, A, k,
-                         s0, rest2, (int)(send - s0), -1);
+      // C -= P P^T over the super-panel's columns: P = its rows below it
+      // (rest2 x SW), C the trailing matrix (lower tiles).
+      const int64_t rest2 = k - send;
+      GemmArgs g{};
+      g.A = A + send * k + s0; g.lda = k;
+      g.B = g.A; g.ldb = k;
+      g.C = A + send * k + send; g.ldc = k;
+      g.M = rest2; g.N = rest2; g.K = send - s0;
+      g.batch = (int)nb; g.sA = (int64_t)kk; g.sB = (int64_t)kk; g.sC = (int64_t)kk;
+      g.alpha = -1.0f; g.beta = 1.0f; g.kmode = kGemmKFull;
+      e = gemm_f32(g, false, true, true, kEpiAxpby, s);
+      if (e != hipSuccess) return e;
     }
   }
   hipLaunchKernelGGL(diag_inv_kernel, dim3((unsigned)((k + NB - 1) / NB), nbu), dim3(64), 0, s, Linv, k);

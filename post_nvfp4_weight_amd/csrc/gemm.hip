@@ -312,11 +312,13 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
 // orders add up to at most four: x1y1, x1y2, x2y1, x1y3, x2y2, x3y1.  The
 // dropped terms are below 2^-24 of |x y|; bf16 products are exact in fp32 and
 // accumulate in fp32, so the result has fp32 accuracy at 6/16 of the fp32
-// matrix-core time.  A is [M][K] (k contiguous) and B is [K][N]; tiles are
-// 128 x 128, four waves of 64 x 64, k in chunks of 32.  In LDS every part is
-// kept [row][k] (k contiguous, rows padded to 40 elements), so that an MFMA
-// operand (8 consecutive k of one row or column) is one 16-byte read; B is
-// transposed on its way in, each thread turning a 4 x 4 block.
+// matrix-core time.  A is [M][K] (k contiguous) and B is [K][N], or with TB
+// stored [N][K]; tiles are 128 x 128, four waves of 64 x 64, k in chunks of
+// 32.  In LDS every part is kept [row][k] (k contiguous, rows padded to 40
+// elements), so that an MFMA operand (8 consecutive k of one row or column)
+// is one 16-byte read; a [K][N] B is transposed on its way in, each thread
+// turning a 4 x 4 block, and a [N][K] B is stored like A.  With LOWER the
+// workgroups of tiles wholly above the diagonal exit (square C).
 constexpr int X6_T = 128, X6_LD = BK + 8;                 // bf16 row stride of a part
 constexpr int X6_PART = X6_T * X6_LD;                     // bf16 elements of one part
 constexpr int X6_BUF = 6 * X6_PART;                       // A parts, then B parts
@@ -346,7 +348,7 @@ __device__ __forceinline__ void put4(uint16_t* base, int off, const f32x4& v) {
 // by (column / 16) % 4, which spreads the transposing writes over the banks.
 __device__ __forceinline__ int x6_boff(int n, int k) { return n * X6_LD + ((((k >> 3) ^ (n >> 4)) & 3) << 3) + (k & 7); }
 
-template <int EPI>
+template <int EPI, bool TB, bool LOWER>
 __global__ __launch_bounds__(256) void gemm_x6_kernel(GemmArgs p) {
   constexpr int WT = X6_T / 2;
   const int nt = (int)gridDim.x, mt = (int)gridDim.y;
@@ -361,6 +363,7 @@ __global__ __launch_bounds__(256) void gemm_x6_kernel(GemmArgs p) {
   const int lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1;
   const int64_t m0 = (int64_t)tm * X6_T, n0 = (int64_t)tn * X6_T;
+  if (LOWER && n0 >= m0 + X6_T) return;
   const int64_t z = blockIdx.z;
   const int64_t zi = p.bi > 0 ? z % p.bi : z, zo = p.bi > 0 ? z / p.bi : 0;
   const float* A = p.A + zi * p.sA + zo * p.sA2;
@@ -412,7 +415,7 @@ __global__ __launch_bounds__(256) void gemm_x6_kernel(GemmArgs p) {
   const bool sym = p.kmode == kGemmKSymUpperB;
 
   // Loads of one chunk: A rows (4 float4 along k per thread), B as a 4 x 4
-  // block (4 k x 4 columns) per thread, raw from clamped addresses so that
+  // block (4 k x 4 columns) per thread, or with TB as rows like A, raw from clamped addresses so that
   // all eight are in flight while the previous chunk is multiplied; masking,
   // alpha and the symmetric weights are applied when the chunk is stored.
   const int bk = (tid >> 5) * 4, bn = (tid & 31) * 4;
@@ -421,7 +424,12 @@ __global__ __launch_bounds__(256) void gemm_x6_kernel(GemmArgs p) {
     ra[q] = *(const f32x4*)(A + min(m0 + r, p.M - 1) * p.lda + min(k0 + kk, p.K - 4));
   };
   auto load_b = [&](int64_t k0, f32x4 (&rb)[4], int i) {
-    rb[i] = *(const f32x4*)(B + min(k0 + bk + i, p.K - 1) * p.ldb + min(n0 + bn, p.N - 4));
+    if (TB) {
+      const int e = i * 256 + tid, r = e >> 3, kk = (e & 7) * 4;
+      rb[i] = *(const f32x4*)(B + min(n0 + r, p.N - 1) * p.ldb + min(k0 + kk, p.K - 4));
+    } else {
+      rb[i] = *(const f32x4*)(B + min(k0 + bk + i, p.K - 1) * p.ldb + min(n0 + bn, p.N - 4));
+    }
   };
   auto load_chunk = [&](int64_t k0, f32x4 (&ra)[4], f32x4 (&rb)[4]) {
 #pragma unroll
@@ -438,6 +446,10 @@ __global__ __launch_bounds__(256) void gemm_x6_kernel(GemmArgs p) {
       const int q = idx, e = q * 256 + tid, r = e >> 3, kk = (e & 7) * 4;
       const bool ok = sm0 + r < sM && k0 + kk < sK;
       put4(buf, r * X6_LD + kk, ok ? ra[q] * alpha_a : f32x4{0.f, 0.f, 0.f, 0.f});
+    } else if (TB) {
+      const int q = idx - 4, e = q * 256 + tid, r = e >> 3, kk = (e & 7) * 4;
+      const bool ok = sn0 + r < sN && k0 + kk < sK;
+      put4(buf + 3 * X6_PART, x6_boff(r, kk), ok ? rb[q] : f32x4{0.f, 0.f, 0.f, 0.f});
     } else {
       const int j = idx - 4, gn = sn0 + bn;
       f32x4 v;
@@ -468,6 +480,9 @@ __global__ __launch_bounds__(256) void gemm_x6_kernel(GemmArgs p) {
     if (idx < 4) {
       const int e = idx * 256 + tid;
       base = buf; off = (e >> 3) * X6_LD + (e & 7) * 4;
+    } else if (TB) {
+      const int e = (idx - 4) * 256 + tid;
+      base = buf + 3 * X6_PART; off = x6_boff(e >> 3, (e & 7) * 4);
     } else {
       base = buf + 3 * X6_PART; off = x6_boff(bn + idx - 4, bk);
     }
@@ -476,6 +491,10 @@ __global__ __launch_bounds__(256) void gemm_x6_kernel(GemmArgs p) {
         const int q = idx, e = q * 256 + tid, rr = e >> 3, kk = (e & 7) * 4;
         const bool ok = sm0 + rr < sM && k0 + kk < sK;
         v = ok ? ra[q] * alpha_a : f32x4{0.f, 0.f, 0.f, 0.f};
+      } else if (TB) {
+        const int q = idx - 4, e = q * 256 + tid, rr = e >> 3, kk = (e & 7) * 4;
+        const bool ok = sn0 + rr < sN && k0 + kk < sK;
+        v = ok ? rb[q] : f32x4{0.f, 0.f, 0.f, 0.f};
       } else {
         const int j = idx - 4, gn = sn0 + bn;
 #pragma unroll
@@ -546,7 +565,8 @@ __global__ __launch_bounds__(256) void gemm_x6_kernel(GemmArgs p) {
     // vector instructions each, which run while the MFMA does); the first
     // k-step also reads the second one's fragments, and each load of chunk
     // c+3 follows the stage that last reads the registers it fills (A's row
-    // chunk q: piece q's first stage; B's rows: piece 7's).
+    // chunk q: piece q's first stage; B's rows: piece 7's, or with TB B's row
+    // chunk q: piece 4 + q's).
     f32x4 sv;
     uint32_t sh0, sh1, sm0_, sm1_;
     float sr[4];
@@ -560,7 +580,8 @@ __global__ __launch_bounds__(256) void gemm_x6_kernel(GemmArgs p) {
         const int g = 24 * h + m;
         store_stage(nbuf, kn, ra, rb, g / 6, g % 6, sv, sh0, sh1, sm0_, sm1_, sr);
         if (g % 6 == 1 && g < 24) load_a((c + 3) * BK, ra, g / 6);
-        if (g >= 43 && g < 47) load_b((c + 3) * BK, rb, g - 43);
+        if (TB && g % 6 == 1 && g >= 24) load_b((c + 3) * BK, rb, g / 6 - 4);
+        if (!TB && g >= 43 && g < 47) load_b((c + 3) * BK, rb, g - 43);
         __builtin_amdgcn_sched_barrier(0);
       }
   };
@@ -644,7 +665,7 @@ hipError_t launch_t(const GemmArgs& a, hipStream_t s) {
 
 // 64-wide fp32 tiles when 128-wide ones would give fewer than one per two CUs
 // (the row-dot keeps 128: its partial sums are laid out per 128 columns);
-// otherwise the split-bf16 kernel for A [M][K] times B [K][N].  Measured on
+// otherwise the split-bf16 kernel for A [M][K] times B [K][N] or [N][K].  Measured on
 // the 4096-column layer: the crossover between 1/4 and 1 tile per CU.  The
 // choice counts the tiles of one outer batch item only, so a matrix of a
 // batch gets the same kernel, and the same bits, as when it is alone.
@@ -653,10 +674,12 @@ hipError_t launch(const GemmArgs& a, hipStream_t s) {
   const int64_t inner = a.bi > 0 ? a.bi : a.batch;
   const int64_t tiles128 = ((a.N + 127) / 128) * ((a.M + 127) / 128) * inner;
   if (EPI == kEpiAxpby && 2 * tiles128 < gemm_num_cus()) return launch_t<64, TA, TB, LOWER, EPI>(a, s);
-  if (!TA && !TB && !LOWER) {
-    dim3 grid((unsigned)((a.N + X6_T - 1) / X6_T), (unsigned)((a.M + X6_T - 1) / X6_T), (unsigned)a.batch);
-    hipLaunchKernelGGL((gemm_x6_kernel<EPI>), grid, dim3(256), 0, s, a);
-    return hipGetLastError();
+  if constexpr (!TA && (TB || !LOWER) && (!TB || EPI == kEpiAxpby)) {
+    if (!TB || a.kmode == kGemmKFull) {
+      dim3 grid((unsigned)((a.N + X6_T - 1) / X6_T), (unsigned)((a.M + X6_T - 1) / X6_T), (unsigned)a.batch);
+      hipLaunchKernelGGL((gemm_x6_kernel<EPI, TB, LOWER>), grid, dim3(256), 0, s, a);
+      return hipGetLastError();
+    }
   }
   return launch_t<128, TA, TB, LOWER, EPI>(a, s);
 }
