@@ -3,9 +3,9 @@
 // With J the index reversal, A = J (H + lam I) J = L L^T (lower Cholesky), and
 // R = J L J is upper with H + lam I = R R^T, so U = R^-1 = J L^-1 J.  The
 // library therefore factors the reversed matrix with a right-looking blocked
-// Cholesky (64-column panels: one launch factors the diagonal block and
-// solves the panel below it, one launch applies the lower-triangular
-// trailing update), inverts the 64x64 diagonal blocks of L in one batched
+// Cholesky (64-column panels: one launch per panel factors the diagonal block,
+// solves the panel below it and applies the previous panel's trailing update,
+// with one lower-triangular update per 512 columns), inverts the 64x64 diagonal blocks of L in one batched
 // launch, completes L^-1 by recursive doubling (at each level, for every pair
 // of adjacent diagonal blocks, X21 = -L22^-1 L21 L11^-1 with two batched
 // GEMMs) and finally writes U[i][j] = L^-1[k-1-i][k-1-j].  Everything is
@@ -130,189 +130,20 @@ __device__ __forceinline__ void chol16(float (&c)[16], float (&x)[16], float lf,
   }(std::make_integer_sequence<int, 16>{});
 }
 
-// Panel p of the blocked Cholesky factorization (columns p .. p+nb-1 of the
-// lower factor).  Every workgroup factors the nb x nb diagonal block itself
-// (identical arithmetic, so identical results) and then solves its own 64
-// rows of the panel below it: L21 = A21 L11^-T.  Inside the workgroup the
-// block is factored in 16-column steps: one wave factors and inverts the
-// 16 x 16 diagonal sub-block in registers; then the rows below it (the
-// block's own rows and the panel rows) are multiplied by the inverse's
-// transpose, and the step's contribution is subtracted from the columns to
-// its right, both as 16 x 16 tiles on the matrix cores
-// (v_mfma_f32_16x16x4f32, one tile per wave at a time).  Workgroup 0 stores
-// L11 into Ld (the same block of the inverse's buffer,
-// which diag_inv_kernel later inverts in place): A's diagonal block is read by
-// every workgroup of the launch, so no workgroup may write it.  On a
-// non-positive pivot workgroup 0 also sets *info (once) to the order of the
-// failing leading minor of the reversed matrix, i.e. of the failing trailing
-// minor of H + lam I.
-//
-// 16x16x4 operand layout: lane l supplies A[l % 16][l / 16] and
-// B[l / 16][l % 16]; accumulator register r of lane l is D[4 (l / 16) + r][l % 16].
-constexpr int SP = NB + 4;   // LDS row stride: the tiles' operand and accumulator accesses are conflict free
-__global__ __launch_bounds__(256) void panel_kernel(float* __restrict__ A, float* __restrict__ Ld, int64_t k,
-                                                    int64_t p, int32_t* __restrict__ info) {
-  // Rows 0..63: the diagonal block (lower part; -> L11); rows 64..127: this
-  // workgroup's panel rows (-> L21 rows).  Matrix b = blockIdx.y of a batch
-  // (A, Ld: k^2 floats per matrix; info[b]).
-  __shared__ __attribute__((aligned(16))) float V[2 * NB][SP];
-  {
-    const int64_t b = blockIdx.y;
-    A += b * k * k;
-    Ld += b * k * k;
-    info += b;
-  }
-  __shared__ float Li[16][17];   // inverse of the current 16 x 16 diagonal sub-block
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l16 = lane & 15, lq = lane >> 4;
-  const int nb = (int)min((int64_t)NB, k - p);
-  const int64_t r0 = (int64_t)blockIdx.x * NB;
-  const int rows = (int)max((int64_t)0, min((int64_t)NB, k - p - nb - r0));
-  // All loads first (16-byte, clamped to valid rows), then the LDS writes.
-  f32x4 ld[8];
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int e = tid + 256 * (q & 3), i = e >> 4, j4 = (e & 15) * 4;
-    const int64_t row = q < 4 ? p + min(i, nb - 1) : p + nb + r0 + min(i, max(rows - 1, 0));
-    // nb is a multiple of 16: a 4-column group lies wholly inside or past it.
-    ld[q] = (q < 4 || rows > 0) ? *(const f32x4*)(A + row * k + p + min(j4, nb - 4)) : f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int e = tid + 256 * (q & 3), i = e >> 4, j4 = (e & 15) * 4;
-    f32x4 v;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int j = j4 + u;
-      if (q < 4) v[u] = (i < nb && j < nb) ? (j <= i ? ld[q][u] : 0.0f) : (i == j ? 1.0f : 0.0f);
-      else v[u] = (i < rows && j < nb) ? ld[q][u] : 0.0f;
-    }
-    *(f32x4*)&V[q < 4 ? i : NB + i][j4] = v;
-  }
-  __syncthreads();
-  int first_bad = 0;
-  // Wave 0 factors and inverts sub-block o (16 x 16 at rows/columns o).
-  auto factor_sub = [&](int o) {
-    // The lane index is made opaque here, so that the compiler forms what
-    // depends on it where it is used.
-    int lo = l16;
-    asm volatile("" : "+v"(lo));
-    const float lf = (float)lo;
-    float c[16], rsv[16], x[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      c[i] = V[o + max(i, lo)][o + min(i, lo)];
-      const float dl = lf - (float)i;
-      x[i] = fmaxf(fmaf(-dl, dl, 1.0f), 0.0f);   // delta(i, l)
-    }
-    int bad = -1;
-    chol16(c, x, lf, rsv, bad);
-    if (bad >= 0 && first_bad == 0 && o + bad < nb) first_bad = (int)(p + o + bad + 1);
-    // Lane l's scale 1 / L[l][l], through LDS (column 16 of Li is spare).
-    if (lane == 0) {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) Li[j][16] = rsv[j];
-    }
-    const float rsl = Li[lo][16];
-    // L into V (entries above the diagonal get values that nothing reads).
-    if (lane < 16) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) V[o + i][o + lane] = c[i] * rsl;
-    }
-    if (lane < 16) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) Li[i][lane] = x[i];
-    }
-  };
-  if (wave == 0) factor_sub(0);
-  __syncthreads();
-  for (int b = 0; b < NB / 16; ++b) {
-    const int o = 16 * b;
-    // Rows below the sub-block (o+16 .. 127): columns o..o+15 := V Li^T.
-    const int nrt = (2 * NB - o - 16) / 16;
-    for (int t = wave; t < nrt; t += 4) {
-      const int t0 = o + 16 + 16 * t;
-      float av[4], bv[4];
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        av[kk] = V[t0 + l16][o + 4 * kk + lq];
-        bv[kk] = Li[l16][4 * kk + lq];
-      }
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[kk], bv[kk], acc, 0, 0, 0);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) V[t0 + 4 * lq + r][o + l16] = acc[r];
-    }
-    __syncthreads();
-    // Columns right of the step (o+16 .. 63), every row below:
-    // V[r][j] -= V[r][o:o+16] . V[j][o:o+16].  Tiles wholly above the
-    // diagonal of the block are never read and are skipped.  Wave 0 updates
-    // the next diagonal sub-block (tile 0) and goes on to factor it while
-    // waves 1-3 update the other tiles.
-    const int nct = (NB - o - 16) / 16;
-    auto c_tile = [&](int t) {
-      const int ti = t / nct, tj = t % nct;
-      const int t0 = o + 16 + 16 * ti, j0 = o + 16 + 16 * tj;
-      if (t0 < j0) return;
-      float av[4], bv[4];
-      f32x4 acc;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[r] = V[t0 + 4 * lq + r][j0 + l16];
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        av[kk] = -V[t0 + l16][o + 4 * kk + lq];
-        bv[kk] = V[j0 + l16][o + 4 * kk + lq];
-      }
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[kk], bv[kk], acc, 0, 0, 0);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) V[t0 + 4 * lq + r][j0 + l16] = acc[r];
-    };
-    if (nct > 0) {
-      if (wave == 0) {
-        c_tile(0);
-        factor_sub(o + 16);
-      } else {
-        for (int t = wave; t < nrt * nct; t += 3) c_tile(t);
-      }
-    }
-    __syncthreads();
-  }
-  // 16-byte stores; the diagonal block's upper triangle is written as zeros.
-  if (blockIdx.x == 0 && tid == 0 && first_bad != 0 && *info == 0) *info = first_bad;
-#pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int e = tid + 256 * (q & 3), i = e >> 4, j4 = (e & 15) * 4;
-    if ((q < 4 ? (blockIdx.x != 0 || i >= nb) : i >= rows) || j4 >= nb) continue;
-    f32x4 v = *(const f32x4*)&V[q < 4 ? i : NB + i][j4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (q < 4 && j4 + u > i) v[u] = 0.0f;
-    *(f32x4*)((q < 4 ? Ld + (p + i) * k : A + (p + nb + r0 + i) * k) + p + j4) = v;
-  }
-}
-
-// Trailing update by the kw panel columns starting at column p: C -= P P^T
-// on the lower triangle of the tiles in the first lim 64-column blocks of C,
-// where P is those columns' L21 (rest x kw, at A + (p+kw) k + p) and C the
-// block right of and below them (rest x rest, at A + (p+kw)(k+1)).  Grid
-// lim x tiles; the workgroups of tiles above the diagonal exit.  One
-// workgroup per 64 x 64 tile; each wave holds a 32 x 32 quadrant in MFMA
-// accumulators initialized from C, and multiplies -P_i by P_j^T
-// (v_mfma_f32_32x32x2f32) in chunks of 64 columns.
+// Trailing update of one 64 x 64 tile (ti, tj) of C by the kw columns of L
+// starting at column pp: C -= P_i P_j^T on the tile's lower part, where P is
+// those columns' rows below them (rest x kw, at A + (pp+kw) k + pp) and C the
+// block right of and below them (rest x rest, at A + (pp+kw)(k+1)).  Each of
+// the four waves holds a 32 x 32 quadrant in MFMA accumulators initialized
+// from C, and multiplies -P_i by P_j^T (v_mfma_f32_32x32x2f32) in chunks of
+// 64 columns.  Pi and Pj are the workgroup's LDS operand tiles.
 constexpr int UP = NB + 2;   // LDS row stride: a lane's (row, k) reads hit 64 distinct banks
-__global__ __launch_bounds__(256) void chol_update_kernel(float* __restrict__ A, int64_t k, int64_t p,
-                                                          int64_t rest, int kw, int lim) {
-  __shared__ float Pi[NB][UP], Pj[NB][UP];
-  A += (int64_t)blockIdx.y * k * k;   // matrix of a batch
+__device__ __forceinline__ void update_tile(float* __restrict__ A, int64_t k, int64_t pp, int64_t rest, int kw,
+                                            int64_t ti, int64_t tj, float (*__restrict__ Pi)[UP],
+                                            float (*__restrict__ Pj)[UP]) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t t = blockIdx.x;
-  const int64_t nt = (rest + NB - 1) / NB;
-  const int64_t tj = t / nt, ti = t % nt;
-  if (ti < tj || tj >= lim) return;
-  const float* P = A + (p + kw) * k + p;
-  float* C = A + (p + kw) * k + p + kw;
+  const float* P = A + (pp + kw) * k + pp;
+  float* C = A + (pp + kw) * k + pp + kw;
   const int wr = wave >> 1, wc = wave & 1;
   const int64_t col = tj * NB + wc * 32 + (lane & 31);
   f32x16 acc;
@@ -361,6 +192,240 @@ __global__ __launch_bounds__(256) void chol_update_kernel(float* __restrict__ A,
   for (int r = 0; r < 16; ++r) {
     const int64_t row = ti * NB + wr * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
     if (row < rest && col < rest && col <= row) C[row * k + col] = acc[r];
+  }
+}
+
+// Panel p of the blocked Cholesky factorization (columns p .. p+nb-1 of the
+// lower factor).  The first `groups` workgroups form the panel: every one
+// factors the nb x nb diagonal block itself (identical arithmetic, so
+// identical results) and then solves its own 64 rows of the panel below it:
+// L21 = A21 L11^-T.  With PRE, the previous panel (columns p-64 .. p-1)
+// has not yet been subtracted from this panel's columns: each of these
+// workgroups first applies it to the rows it holds (the diagonal block and
+// its own rows: A -= P P_d^T, with P those rows of the previous panel and P_d
+// the diagonal block's rows of it).  The other workgroups of the launch apply
+// the previous panel to the rest of its super-panel, the 64 x 64 tiles of
+// column blocks 1 .. lim-1 right of p (grid (lim-1) x tiles; those above the
+// diagonal exit): columns that this launch's panel workgroups do not read.
+// Inside a panel workgroup the block is factored in 16-column steps: one wave
+// factors and inverts the 16 x 16 diagonal sub-block in registers; then the
+// rows below it (the block's own rows and the panel rows) are multiplied by
+// the inverse's transpose, and the step's contribution is subtracted from the
+// columns to its right, both as 16 x 16 tiles on the matrix cores
+// (v_mfma_f32_16x16x4f32, one tile per wave at a time).  Workgroup 0 stores
+// L11 into Ld (the same block of the inverse's buffer, which diag_inv_kernel
+// later inverts in place): A's diagonal block is read by every panel
+// workgroup of the launch, so no workgroup may write it.  On a non-positive
+// pivot workgroup 0 also sets *info (once) to the order of the failing
+// leading minor of the reversed matrix, i.e. of the failing trailing minor of
+// H + lam I.
+//
+// 16x16x4 operand layout: lane l supplies A[l % 16][l / 16] and
+// B[l / 16][l % 16]; accumulator register r of lane l is D[4 (l / 16) + r][l % 16].
+constexpr int SP = NB + 4;   // LDS row stride: the tiles' operand and accumulator accesses are conflict free
+template <bool PRE>
+__global__ __launch_bounds__(256, 2) void panel_kernel(float* __restrict__ A, float* __restrict__ Ld, int64_t k,
+                                                       int64_t p, int32_t* __restrict__ info, int groups) {
+  // Rows 0..63: the diagonal block (lower part; -> L11); rows 64..127: this
+  // workgroup's panel rows (-> L21 rows).  Ps: the same rows of the previous
+  // panel (pre-update), or an extra workgroup's operand tiles.  Matrix
+  // b = blockIdx.y of a batch (A, Ld: k^2 floats per matrix; info[b]).
+  __shared__ __attribute__((aligned(16))) float V[2 * NB][SP];
+  __shared__ __attribute__((aligned(16))) float Ps[PRE ? 2 * NB : 1][SP];
+  {
+    const int64_t b = blockIdx.y;
+    A += b * k * k;
+    Ld += b * k * k;
+    info += b;
+  }
+  if (PRE && (int)blockIdx.x >= groups) {
+    const int64_t rest = k - p, nt = (rest + NB - 1) / NB, t = (int64_t)blockIdx.x - groups;
+    const int64_t tj = 1 + t / nt, ti = t % nt;
+    if (ti < tj) return;
+    static_assert(2 * NB * UP <= 2 * NB * SP, "operand tiles fit in Ps");
+    update_tile(A, k, p - NB, rest, NB, ti, tj, (float (*)[UP]) & Ps[0][0], (float (*)[UP])(&Ps[0][0] + NB * UP));
+    return;
+  }
+  // Inverse of the current 16 x 16 diagonal sub-block (rows of 20: 16-byte
+  // aligned; column 16 carries the pivots' scales).
+  __shared__ __attribute__((aligned(16))) float Li[16][20];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, lq = lane >> 4;
+  const int nb = (int)min((int64_t)NB, k - p);
+  const int64_t r0 = (int64_t)blockIdx.x * NB;
+  const int rows = (int)max((int64_t)0, min((int64_t)NB, k - p - nb - r0));
+  // All loads first (16-byte, clamped to valid rows), then the LDS writes.
+  f32x4 ld[8], lp[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int e = tid + 256 * (q & 3), i = e >> 4, j4 = (e & 15) * 4;
+    const int64_t row = q < 4 ? p + min(i, nb - 1) : p + nb + r0 + min(i, max(rows - 1, 0));
+    // nb is a multiple of 16: a 4-column group lies wholly inside or past it.
+    ld[q] = (q < 4 || rows > 0) ? *(const f32x4*)(A + row * k + p + min(j4, nb - 4)) : f32x4{0.f, 0.f, 0.f, 0.f};
+    // The previous panel is whole (64 columns) whenever PRE is set.
+    if (PRE) lp[q] = (q < 4 || rows > 0) ? *(const f32x4*)(A + row * k + p - NB + j4) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int e = tid + 256 * (q & 3), i = e >> 4, j4 = (e & 15) * 4;
+    f32x4 v;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = j4 + u;
+      if (q < 4) v[u] = (i < nb && j < nb) ? (j <= i ? ld[q][u] : 0.0f) : (i == j ? 1.0f : 0.0f);
+      else v[u] = (i < rows && j < nb) ? ld[q][u] : 0.0f;
+    }
+    *(f32x4*)&V[q < 4 ? i : NB + i][j4] = v;
+    if (PRE) {
+      const bool ok = q < 4 ? i < nb : i < rows;
+      *(f32x4*)&Ps[q < 4 ? i : NB + i][j4] = ok ? lp[q] : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  __syncthreads();
+  // With PRE: V -= Ps Ps[0:64]^T on the diagonal block's lower 16 x 16 tiles
+  // (10) and the panel rows' tiles (16), 64 k-values each; a tile's upper part
+  // on the diagonal gets values that nothing reads.  Rows and columns past nb
+  // or rows hold zeros in Ps, so the identity and zero padding stay.  Wave 0
+  // takes tile 0 (the first diagonal sub-block) and factors it at once, while
+  // waves 1-3 update the other 25 tiles, two at a time.
+  auto pre_tiles = [&]<int NT>(int t0, int t1) {   // NT (1 or 2) tiles: t0 and t1
+    int ti[NT], tj[NT];
+#pragma unroll
+    for (int h = 0; h < NT; ++h) {
+      const int t = h ? t1 : t0;
+      if (t < 10) {
+        ti[h] = t < 1 ? 0 : (t < 3 ? 1 : (t < 6 ? 2 : 3));
+        tj[h] = t - ti[h] * (ti[h] + 1) / 2;
+      } else {
+        ti[h] = 4 + (t - 10) / 4;
+        tj[h] = (t - 10) % 4;
+      }
+    }
+    // Lane (l16, lq) supplies k = 16 lq .. 16 lq + 15 (step 4j + u: k = 16 lq
+    // + 4j + u), so that its operands are four 16-byte reads per tile side.
+    // The accumulators hold -V, so that no operand needs negating.
+    f32x4 acc[NT], a4[NT][4], b4[NT][4];
+#pragma unroll
+    for (int h = 0; h < NT; ++h) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        a4[h][j] = *(const f32x4*)&Ps[16 * ti[h] + l16][16 * lq + 4 * j];
+        b4[h][j] = *(const f32x4*)&Ps[16 * tj[h] + l16][16 * lq + 4 * j];
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[h][r] = -V[16 * ti[h] + 4 * lq + r][16 * tj[h] + l16];
+    }
+#pragma unroll
+    for (int kk = 0; kk < NB / 4; ++kk)
+#pragma unroll
+      for (int h = 0; h < NT; ++h)
+        acc[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[h][kk >> 2][kk & 3], b4[h][kk >> 2][kk & 3], acc[h], 0, 0, 0);
+#pragma unroll
+    for (int h = 0; h < NT; ++h)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) V[16 * ti[h] + 4 * lq + r][16 * tj[h] + l16] = -acc[h][r];
+  };
+  int first_bad = 0;
+  // Wave 0 factors and inverts sub-block o (16 x 16 at rows/columns o).
+  auto factor_sub = [&](int o) {
+    // The lane index is made opaque here, so that the compiler forms what
+    // depends on it where it is used.
+    int lo = l16;
+    asm volatile("" : "+v"(lo));
+    const float lf = (float)lo;
+    float c[16], rsv[16], x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      c[i] = V[o + max(i, lo)][o + min(i, lo)];
+      const float dl = lf - (float)i;
+      x[i] = fmaxf(fmaf(-dl, dl, 1.0f), 0.0f);   // delta(i, l)
+    }
+    int bad = -1;
+    chol16(c, x, lf, rsv, bad);
+    if (bad >= 0 && first_bad == 0 && o + bad < nb) first_bad = (int)(p + o + bad + 1);
+    // Lane l's scale 1 / L[l][l], through LDS (column 16 of Li is spare).
+    if (lane == 0) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) Li[j][16] = rsv[j];
+    }
+    const float rsl = Li[lo][16];
+    // L into V (entries above the diagonal get values that nothing reads).
+    if (lane < 16) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) V[o + i][o + lane] = c[i] * rsl;
+    }
+    if (lane < 16) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) Li[i][lane] = x[i];
+    }
+  };
+  if (wave == 0) {
+    if constexpr (PRE) pre_tiles.template operator()<1>(0, 0);
+    factor_sub(0);
+  } else if constexpr (PRE) {
+    // Wave w takes tiles w, w+3, ... (pairs w+6i, w+6i+3; wave 1's last tile, 25, alone).
+    for (int t = wave; t + 3 < 26; t += 6) pre_tiles.template operator()<2>(t, t + 3);
+    if (wave == 1) pre_tiles.template operator()<1>(25, 25);
+  }
+  __syncthreads();
+  for (int b = 0; b < NB / 16; ++b) {
+    const int o = 16 * b;
+    // Rows below the sub-block (o+16 .. 127): columns o..o+15 := V Li^T.
+    const int nrt = (2 * NB - o - 16) / 16;
+    for (int t = wave; t < nrt; t += 4) {
+      const int t0 = o + 16 + 16 * t;
+      // Lane (l16, lq) supplies k = 4 lq + kk: one 16-byte read per operand.
+      const f32x4 av = *(const f32x4*)&V[t0 + l16][o + 4 * lq];
+      const f32x4 bv = *(const f32x4*)&Li[l16][4 * lq];
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[kk], bv[kk], acc, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) V[t0 + 4 * lq + r][o + l16] = acc[r];
+    }
+    __syncthreads();
+    // Columns right of the step (o+16 .. 63), every row below:
+    // V[r][j] -= V[r][o:o+16] . V[j][o:o+16].  Tiles wholly above the
+    // diagonal of the block are never read and are skipped.  Wave 0 updates
+    // the next diagonal sub-block (tile 0) and goes on to factor it while
+    // waves 1-3 update the other tiles.
+    const int nct = (NB - o - 16) / 16;
+    auto c_tile = [&](int t) {
+      const int ti = t / nct, tj = t % nct;
+      const int t0 = o + 16 + 16 * ti, j0 = o + 16 + 16 * tj;
+      if (t0 < j0) return;
+      // Lane (l16, lq) supplies k = o + 4 lq + kk; the accumulator holds -V.
+      const f32x4 av = *(const f32x4*)&V[t0 + l16][o + 4 * lq];
+      const f32x4 bv = *(const f32x4*)&V[j0 + l16][o + 4 * lq];
+      f32x4 acc;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[r] = -V[t0 + 4 * lq + r][j0 + l16];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[kk], bv[kk], acc, 0, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) V[t0 + 4 * lq + r][j0 + l16] = -acc[r];
+    };
+    if (nct > 0) {
+      if (wave == 0) {
+        c_tile(0);
+        factor_sub(o + 16);
+      } else {
+        for (int t = wave; t < nrt * nct; t += 3) c_tile(t);
+      }
+    }
+    __syncthreads();
+  }
+  // 16-byte stores; the diagonal block's upper triangle is written as zeros.
+  if (blockIdx.x == 0 && tid == 0 && first_bad != 0 && *info == 0) *info = first_bad;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int e = tid + 256 * (q & 3), i = e >> 4, j4 = (e & 15) * 4;
+    if ((q < 4 ? (blockIdx.x != 0 || i >= nb) : i >= rows) || j4 >= nb) continue;
+    f32x4 v = *(const f32x4*)&V[q < 4 ? i : NB + i][j4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (q < 4 && j4 + u > i) v[u] = 0.0f;
+    *(f32x4*)((q < 4 ? Ld + (p + i) * k : A + (p + nb + r0 + i) * k) + p + j4) = v;
   }
 }
 
@@ -456,23 +521,31 @@ static hipError_t factor_pass(const float* H, int64_t k, int64_t nb, int64_t str
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  // Panels are grouped in super-panels of SW columns.  After each panel only
-  // the rest of its super-panel is updated (the columns the next panels
-  // factor); the columns right of the super-panel take all of its panels in
-  // one update after its last panel, so they are read and written once per
-  // SW columns instead of once per panel.  Every launch covers the nb
-  // matrices of the pass (grid.y).
+  // Panels are grouped in super-panels of SW columns.  Each panel's update of
+  // the rest of its super-panel (the columns the next panels factor) runs in
+  // the next panel's launch: its panel workgroups apply it to the columns they
+  // factor, extra workgroups to the columns right of them.  The columns right
+  // of the super-panel take all of its panels in one update after its last
+  // panel, so they are read and written once per SW columns instead of once
+  // per panel.  Every launch covers the nb matrices of the pass (grid.y).
   for (int64_t p = 0; p < k; p += NB) {
     const int64_t rest = k - p - NB;
-    const unsigned groups = rest > 0 ? (unsigned)((rest + NB - 1) / NB) : 1u;
-    hipLaunchKernelGGL(panel_kernel, dim3(groups, nbu), dim3(256), 0, s, A, Linv, k, p, info);
-    if (rest <= 0) break;
+    const int64_t groups = rest > 0 ? (rest + NB - 1) / NB : 1;
     const int64_t s0 = p / SW * SW, send = min(s0 + SW, k);
-    if (p + NB < send) {
-      const int64_t tiles = (rest + NB - 1) / NB, lim = (send - p - NB + NB - 1) / NB;
-      hipLaunchKernelGGL(chol_update_kernel, dim3((unsigned)(lim * tiles), nbu), dim3(256), 0, s, A, k, p, rest, NB,
-                         (int)lim);
-    } else if (send < k) {
+    const bool pre = p > s0;
+    int64_t extra = 0;
+    if (pre) {
+      const int64_t nt = (k - p + NB - 1) / NB, lim = (send - p + NB - 1) / NB;
+      extra = (lim - 1) * nt;
+    }
+    if (pre)
+      hipLaunchKernelGGL(panel_kernel<true>, dim3((unsigned)(groups + extra), nbu), dim3(256), 0, s, A, Linv, k, p,
+                         info, (int)groups);
+    else
+      hipLaunchKernelGGL(panel_kernel<false>, dim3((unsigned)groups, nbu), dim3(256), 0, s, A, Linv, k, p, info,
+                         (int)groups);
+    if (rest <= 0) break;
+    if (p + NB == send && send < k) {
       // C -= P P^T over the super-panel's columns: P = its rows below it
       // (rest2 x SW), C the trailing matrix (lower tiles).
       const int64_t rest2 = k - send;
