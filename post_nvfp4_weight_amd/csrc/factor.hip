@@ -565,10 +565,18 @@ static hipError_t factor_pass(const float* H, int64_t k, int64_t nb, int64_t str
   if (e != hipSuccess) return e;
 
   // Triangular inverse by recursive doubling over diagonal blocks of size bs;
-  // the GEMMs of a level run over (pairs of one matrix) x (nb matrices).
+  // the GEMMs of a level run over (pairs of one matrix) x (nb matrices).  At
+  // the levels whose tiles of one matrix do not fill the device, every
+  // tile's triangular k range is split in two halves (the second half's
+  // product into T2, added afterwards): the long tiles of those levels hold
+  // twice the average work, so the halves even the launch out.  The choice
+  // counts one matrix's tiles, so a matrix gets the same bits in any batch.
   for (int64_t bs = NB; bs < k; bs *= 2) {
     int64_t full = k / (2 * bs);  // pairs whose both halves are complete
     auto pair_step = [&](int64_t base, int64_t n1, int64_t n2, int pairs) -> hipError_t {
+      const int64_t tiles = (int64_t)pairs * ((n1 + 127) / 128) * ((n2 + 127) / 128);
+      const bool split = bs >= 1024 && tiles <= 256;
+      float* T2 = T + (int64_t)kk / 4;   // pairs * n1 * n2 <= k bs / 2 <= k^2 / 4 floats per matrix
       // T = L21 * L11^-1   (n2 x n1)
       GemmArgs a{};
       a.A = A + (base + bs) * k + base; a.lda = k;
@@ -578,7 +586,10 @@ static hipError_t factor_pass(const float* H, int64_t k, int64_t nb, int64_t str
       a.sA = 2 * bs * k + 2 * bs; a.sB = 2 * bs * k + 2 * bs; a.sC = n1 * n2;
       a.sA2 = (int64_t)kk; a.sB2 = (int64_t)kk; a.sC2 = (int64_t)kk / 2;
       a.alpha = 1.0f; a.beta = 0.0f; a.kmode = kGemmKLowerB;   // L11^-1 is lower triangular
+      if (split) { a.ksplit = 2; a.C2 = T2; a.ldc2 = n1; a.s2C = n1 * n2; a.s2C2 = (int64_t)kk / 2; }
       hipError_t err = gemm_f32(a, false, false, false, kEpiAxpby, s);
+      if (err == hipSuccess && split)
+        err = add_into(T, n1, T2, n1, (int64_t)pairs * n2, n1, s, nb, (int64_t)kk / 2, (int64_t)kk / 2);
       if (err != hipSuccess) return err;
       // X21 = -L22^-1 * T   (n2 x n1), written into Linv
       GemmArgs b{};
@@ -589,7 +600,17 @@ static hipError_t factor_pass(const float* H, int64_t k, int64_t nb, int64_t str
       b.sA = 2 * bs * k + 2 * bs; b.sB = n1 * n2; b.sC = 2 * bs * k + 2 * bs;
       b.sA2 = (int64_t)kk; b.sB2 = (int64_t)kk / 2; b.sC2 = (int64_t)kk;
       b.alpha = -1.0f; b.beta = 0.0f; b.kmode = kGemmKLowerA;  // L22^-1 is lower triangular
-      return gemm_f32(b, false, false, false, kEpiAxpby, s);
+      // With the split, the second half goes to T2 as [pair][n2][n1] (T itself
+      // stays intact: it is this product's B operand), then into X21.
+      if (split) { b.ksplit = 2; b.C2 = T2; b.ldc2 = n1; b.s2C = n1 * n2; b.s2C2 = (int64_t)kk / 2; }
+      err = gemm_f32(b, false, false, false, kEpiAxpby, s);
+      if (err != hipSuccess || !split) return err;
+      if (nb == 1)   // the pairs as one batch
+        return add_into(Linv + (base + bs) * k + base, k, T2, n1, n2, n1, s, pairs, 2 * bs * k + 2 * bs, n1 * n2);
+      for (int q = 0; err == hipSuccess && q < pairs; ++q)
+        err = add_into(Linv + (base + bs + q * 2 * bs) * k + base + q * 2 * bs, k, T2 + q * n1 * n2, n1, n2, n1, s, nb,
+                       (int64_t)kk, (int64_t)kk / 2);
+      return err;
     };
     if (full > 0) {
       e = pair_step(0, bs, bs, (int)full);

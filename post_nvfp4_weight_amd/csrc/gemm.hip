@@ -364,19 +364,21 @@ __global__ __launch_bounds__(256) void gemm_x6_kernel(GemmArgs p) {
   const int wr = wave >> 1, wc = wave & 1;
   const int64_t m0 = (int64_t)tm * X6_T, n0 = (int64_t)tn * X6_T;
   if (LOWER && n0 >= m0 + X6_T) return;
-  const int64_t z = blockIdx.z;
+  const int half = p.ksplit == 2 ? (int)(blockIdx.z & 1) : 0;
+  const int64_t z = p.ksplit == 2 ? blockIdx.z >> 1 : blockIdx.z;
   const int64_t zi = p.bi > 0 ? z % p.bi : z, zo = p.bi > 0 ? z / p.bi : 0;
   const float* A = p.A + zi * p.sA + zo * p.sA2;
   const float* B = p.B + zi * p.sB + zo * p.sB2;
-  float* C = p.C + zi * p.sC + zo * p.sC2;
+  float* C = half ? p.C2 + zi * p.s2C + zo * p.s2C2 : p.C + zi * p.sC + zo * p.sC2;
+  const int64_t ldc = half ? p.ldc2 : p.ldc;
   const float* Dz = EPI == kEpiRowDot ? p.D + zi * p.sD + zo * p.sD2 : nullptr;
   float* Pz = EPI == kEpiRowDot ? p.P + zi * p.sP + zo * p.sP2 : nullptr;
 
   f32x16 acc[2][2];
   const bool load_c = EPI == kEpiAxpby && p.beta != 0.0f;
   const int64_t wrow0 = m0 + wr * WT, wcol0 = n0 + wc * WT;
-  float* Cw = C + wrow0 * p.ldc + wcol0;
-  const int lane_off = 4 * (lane >> 5) * (int)p.ldc + (lane & 31);
+  float* Cw = C + wrow0 * ldc + wcol0;
+  const int lane_off = 4 * (lane >> 5) * (int)ldc + (lane & 31);
   const bool full = wrow0 + WT <= p.M && wcol0 + WT <= p.N;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -391,7 +393,7 @@ __global__ __launch_bounds__(256) void gemm_x6_kernel(GemmArgs p) {
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          acc[i][j][r] = p.beta * Cw[(i * 32 + 8 * (r >> 2) + (r & 3)) * p.ldc + j * 32 + lane_off];
+          acc[i][j][r] = p.beta * Cw[(i * 32 + 8 * (r >> 2) + (r & 3)) * ldc + j * 32 + lane_off];
   } else if (load_c) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -401,7 +403,7 @@ __global__ __launch_bounds__(256) void gemm_x6_kernel(GemmArgs p) {
         for (int r = 0; r < 16; ++r) {
           const int64_t gr = wrow0 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
           const int64_t gc = wcol0 + j * 32 + (lane & 31);
-          const float v = C[min(gr, p.M - 1) * p.ldc + min(gc, p.N - 1)];
+          const float v = C[min(gr, p.M - 1) * ldc + min(gc, p.N - 1)];
           acc[i][j][r] = (gr < p.M && gc < p.N) ? p.beta * v : 0.0f;
         }
   }
@@ -411,7 +413,11 @@ __global__ __launch_bounds__(256) void gemm_x6_kernel(GemmArgs p) {
   if (p.kmode == kGemmKLowerA) khi = min(p.K, m0 + X6_T);
   if (p.kmode == kGemmKLowerB) klo = p.noff + n0;
   if (p.kmode == kGemmKSymUpperB) khi = min(p.K, p.noff + n0 + X6_T);
-  const int64_t c0 = klo / BK, nk = (khi + BK - 1) / BK;
+  if (p.ksplit == 2) {   // halves of whole chunks: the first ends at mid, the second starts there
+    const int64_t mid = (klo / BK + ((khi + BK - 1) / BK - klo / BK) / 2) * BK;
+    if (half) klo = max(klo, mid); else khi = min(khi, mid);
+  }
+  const int64_t c0 = klo / BK, nk = max(c0, (khi + BK - 1) / BK);
   const bool sym = p.kmode == kGemmKSymUpperB;
 
   // Loads of one chunk: A rows (4 float4 along k per thread), B as a 4 x 4
@@ -604,7 +610,7 @@ __global__ __launch_bounds__(256) void gemm_x6_kernel(GemmArgs p) {
         for (int r = 0; r < 16; ++r) {
           const int row = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3), col = j * 32 + (lane & 31);
           if (full || (wrow0 + row < p.M && wcol0 + col < p.N))
-            Cw[(i * 32 + 8 * (r >> 2) + (r & 3)) * p.ldc + j * 32 + lane_off] = acc[i][j][r];
+            Cw[(i * 32 + 8 * (r >> 2) + (r & 3)) * ldc + j * 32 + lane_off] = acc[i][j][r];
         }
   } else {
     float (*red)[33] = (float (*)[33])smem;   // [128][33], operand tiles are dead here
@@ -645,6 +651,27 @@ __global__ __launch_bounds__(256) void gemm_x6_kernel(GemmArgs p) {
   }
 }
 
+// C += C2 elementwise over M x N (row strides ldc, ldc2), matrix z = blockIdx.y;
+// 4 columns per thread, as 16-byte vectors when both rows allow.
+__global__ __launch_bounds__(256) void add_into_kernel(float* __restrict__ C, int64_t ldc, const float* __restrict__ C2,
+                                                       int64_t ldc2, int64_t M, int64_t N, int64_t sC, int64_t sC2) {
+  C += (int64_t)blockIdx.y * sC;
+  C2 += (int64_t)blockIdx.y * sC2;
+  const int64_t n4 = (N + 3) / 4, items = M * n4;
+  const bool vec = ((ldc | ldc2 | sC | sC2) & 3) == 0 && ((uintptr_t)C & 15) == 0 && ((uintptr_t)C2 & 15) == 0;
+  for (int64_t it = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; it < items; it += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t i = it / n4, j = (it % n4) * 4;
+    if (vec && j + 4 <= N) {
+      f32x4 a = *(const f32x4*)(C + i * ldc + j);
+      const f32x4 b = *(const f32x4*)(C2 + i * ldc2 + j);
+      a += b;
+      *(f32x4*)(C + i * ldc + j) = a;
+    } else {
+      for (int64_t t = j; t < min(N, j + 4); ++t) C[i * ldc + t] += C2[i * ldc2 + t];
+    }
+  }
+}
+
 int gemm_num_cus() {
   static int cus = 0;
   if (!cus) {
@@ -673,10 +700,12 @@ template <bool TA, bool TB, bool LOWER, int EPI>
 hipError_t launch(const GemmArgs& a, hipStream_t s) {
   const int64_t inner = a.bi > 0 ? a.bi : a.batch;
   const int64_t tiles128 = ((a.N + 127) / 128) * ((a.M + 127) / 128) * inner;
-  if (EPI == kEpiAxpby && 2 * tiles128 < gemm_num_cus()) return launch_t<64, TA, TB, LOWER, EPI>(a, s);
+  if (a.ksplit == 2 && (TA || TB || LOWER || EPI != kEpiAxpby || a.beta != 0.0f)) return hipErrorInvalidValue;
+  if (a.ksplit != 2 && EPI == kEpiAxpby && 2 * tiles128 < gemm_num_cus()) return launch_t<64, TA, TB, LOWER, EPI>(a, s);
   if constexpr (!TA && (TB || !LOWER) && (!TB || EPI == kEpiAxpby)) {
     if (!TB || a.kmode == kGemmKFull) {
-      dim3 grid((unsigned)((a.N + X6_T - 1) / X6_T), (unsigned)((a.M + X6_T - 1) / X6_T), (unsigned)a.batch);
+      dim3 grid((unsigned)((a.N + X6_T - 1) / X6_T), (unsigned)((a.M + X6_T - 1) / X6_T),
+                (unsigned)(a.batch * (a.ksplit == 2 ? 2 : 1)));
       hipLaunchKernelGGL((gemm_x6_kernel<EPI, TB, LOWER>), grid, dim3(256), 0, s, a);
       return hipGetLastError();
     }
@@ -782,6 +811,15 @@ hipError_t gemm_f32(const GemmArgs& a, bool ta, bool tb, bool lower, GemmEpi epi
   if (!ta && tb) return lower ? launch<false, true, true, kEpiAxpby>(a, s) : launch<false, true, false, kEpiAxpby>(a, s);
   if (ta && !tb) return lower ? launch<true, false, true, kEpiAxpby>(a, s) : launch<true, false, false, kEpiAxpby>(a, s);
   return launch<true, true, false, kEpiAxpby>(a, s);
+}
+
+hipError_t add_into(float* C, int64_t ldc, const float* C2, int64_t ldc2, int64_t M, int64_t N, hipStream_t s,
+                    int64_t nb, int64_t sC, int64_t sC2) {
+  if (M <= 0 || N <= 0 || nb <= 0) return hipSuccess;
+  const int64_t items = M * ((N + 3) / 4);
+  const unsigned blocks = (unsigned)min((items + 255) / 256, (int64_t)2048);
+  hipLaunchKernelGGL(add_into_kernel, dim3(blocks, (unsigned)nb), dim3(256), 0, s, C, ldc, C2, ldc2, M, N, sC, sC2);
+  return hipGetLastError();
 }
 
 }  // namespace nvq

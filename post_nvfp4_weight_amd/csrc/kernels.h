@@ -30,6 +30,14 @@ struct GemmArgs {
   float alpha, beta;
   int kmode;            // GemmK: which part of the k range each output tile needs
   int64_t noff;         // column of C (and of B) 0 within the whole matrix, for kmode's triangle
+  // ksplit 2 (split-bf16 kernel, beta = 0): every tile's k range is cut in two
+  // halves of whole 32-chunks, the first half's product written to C, the
+  // second's to C2 (row stride ldc2, batch strides s2C, s2C2 like sC, sC2);
+  // the caller adds C2 into C.  This evens out tiles whose triangular k
+  // ranges differ in length.
+  int ksplit;
+  float* C2;
+  int64_t ldc2, s2C, s2C2;
 };
 // kmode: kGemmKFull; kGemmKLowerA (A lower triangular: row tile i needs
 // k < its last row); kGemmKLowerB (B lower triangular: column tile j needs
@@ -44,6 +52,9 @@ enum GemmK { kGemmKFull = 0, kGemmKLowerA = 1, kGemmKLowerB = 2, kGemmKSymUpperB
 hipError_t gemm_f32(const GemmArgs& a, bool trans_a, bool trans_b, bool lower, GemmEpi epi,
                     hipStream_t s);
 constexpr int kGemmTile = 128;
+// C[i][j] += C2[i][j] for i < M, j < N (row strides ldc, ldc2); nb matrices at C + e sC, C2 + e sC2.
+hipError_t add_into(float* C, int64_t ldc, const float* C2, int64_t ldc2, int64_t M, int64_t N, hipStream_t s,
+                    int64_t nb = 1, int64_t sC = 0, int64_t sC2 = 0);
 // C -= A B with A [M x K] and C [M x N] fp64, B [K x N] fp32 (all row-major).
 // nb matrices: item e at A + e * sA, B + e * sB, C + e * sC.
 hipError_t rank_update_f64(const double* A, int64_t lda, const float* B, int64_t ldb, double* C, int64_t ldc,
