@@ -142,9 +142,9 @@ hipError_t weighted_error_all(const void* W, int bf, int64_t m, int64_t k, int64
 }
 
 // The fp32 sweep with two-level lazy updates (the same sums as eager GPTQ
-// updates, in another order): within a 512-column block the batches' errors
-// reach the later batches of the block, and a finished block's error slab
-// updates every later column.
+// updates, in another order): a batch's errors update the rest of its
+// 512-column block at once, and a finished block's error slab updates every
+// later column.
 hipError_t sweep_f32(int64_t m, int64_t k, const float* U, const float* g, int n_cand, bool indep, uint8_t* codes,
                      uint8_t* scales, float* row_loss, float* Wp, float* Eslab, const float* invd, const QBatch& qb,
                      hipStream_t s) {
@@ -160,19 +160,15 @@ hipError_t sweep_f32(int64_t m, int64_t k, const float* U, const float* g, int n
     a.sA2 = wsf; a.sB2 = qb.stride_u; a.sC2 = wsf;
     return gemm_f32(a, false, false, false, kEpiAxpby, s);
   };
-  // With the left-looking sweep each batch subtracts the earlier batches of
-  // its block from its own staged rows; otherwise a batch's errors update the
-  // rest of its block at once.
-  const bool left = sweep_left_looking(n_cand);
   hipError_t e = hipSuccess;
   for (int64_t s0 = 0; e == hipSuccess && s0 < k; s0 += kSuperBatch) {
     const int64_t s1 = std::min<int64_t>(k, s0 + kSuperBatch);
     for (int64_t i1 = s0; e == hipSuccess && i1 < s1; i1 += kBatch) {
       const int ncols = (int)std::min<int64_t>(kBatch, s1 - i1);
       e = sweep_batch_launch(Wp, U, invd, g, m, k, (int)i1, ncols, n_cand, indep, codes, scales, Eslab + (i1 - s0),
-                             kSuperBatch, row_loss, s, qb.nb, bs, left ? (int)(i1 - s0) : 0);
+                             kSuperBatch, row_loss, s, qb.nb, bs);
       const int64_t i2 = i1 + ncols;
-      if (e == hipSuccess && !left && i2 < s1) e = rank_update(Eslab + (i1 - s0), i1, i2, ncols, s1 - i2);
+      if (e == hipSuccess && i2 < s1) e = rank_update(Eslab + (i1 - s0), i1, i2, ncols, s1 - i2);
     }
     if (e == hipSuccess && s1 < k) e = rank_update(Eslab, s0, s1, s1 - s0, k - s1);
   }

@@ -105,16 +105,10 @@ hipError_t inv_diag_launch(const float* U, int64_t k, float* invd, hipStream_t s
                            int64_t stride_u = 0, int64_t stride_invd = 0);
 // indep: choose each block's scale by the block-independent squared rounding
 // error instead of the replay score (the committed block is still replayed).
-// nprev > 0 (only where sweep_left_looking(n_cand)): the batch's columns have
-// not yet received the earlier batches of their block; the kernel subtracts
-// them from its staged rows, E[:, i1-nprev:i1] U[i1-nprev:i1, i1:i1+ncols]
-// (E at Eslab - nprev, the same row stride lde).
-bool sweep_left_looking(int n_cand);
 hipError_t sweep_batch_launch(float* Wp, const float* U, const float* invd, const float* g,
                               int64_t m, int64_t k, int i1, int ncols, int n_cand, bool indep,
                               uint8_t* codes, uint8_t* scales, float* Eslab, int64_t lde, float* row_loss,
-                              hipStream_t s, int64_t nb = 1, const SweepStrides& bs = SweepStrides(),
-                              int nprev = 0);
+                              hipStream_t s, int64_t nb = 1, const SweepStrides& bs = SweepStrides());
 // The same sweep with fp64 working weights and errors (U read as fp32).
 hipError_t sweep_batch_launch_f64(double* Wp, const float* U, const float* g, int64_t m, int64_t k, int i1,
                                   int ncols, int n_cand, bool indep, uint8_t* codes, uint8_t* scales, double* Eslab,

@@ -475,12 +475,12 @@ __device__ __forceinline__ void load16(const T* p, T (&v)[16]) {
   for (int q = 0; q < 16; ++q) v[q] = p[q];
 }
 
-template <int G, typename T, bool INDEP, bool LEFT>
+template <int G, typename T, bool INDEP>
 __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
     T* __restrict__ Wp, const float* __restrict__ U, const float* __restrict__ invd,
     const float* __restrict__ gptr, int64_t m, int64_t k, int i1, int ncols, int n_cand,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, T* __restrict__ Eslab, int64_t lde,
-    float* __restrict__ row_loss, SweepStrides bs, int nprev) {
+    float* __restrict__ row_loss, SweepStrides bs) {
   constexpr bool F64 = sizeof(T) == 8;
   {   // matrix e = blockIdx.y of a batch
     const int64_t e = blockIdx.y;
@@ -501,10 +501,6 @@ __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
   // Rows padded by 64 bytes: the four rows a wave touches fall on distinct banks.
   __shared__ __attribute__((aligned(16))) T slab[ROWS][kBatch + 64 / sizeof(T)];
   __shared__ __attribute__((aligned(16))) T eb_s[ROWS][16];
-  // Left-looking update: chunks of U's rows (row stride 144: the 16 columns x
-  // 4 rows of an operand read fall on 64 distinct banks) and of E's columns.
-  __shared__ __attribute__((aligned(16))) float Uc[LEFT ? 2 : 1][LEFT ? 32 : 1][144];
-  __shared__ __attribute__((aligned(16))) float Ec[LEFT ? 2 : 1][LEFT ? 16 : 1][36];
 
   const int tid = threadIdx.x;
   const int rl = tid / G, ci = tid % G;
@@ -592,74 +588,7 @@ __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
     slab_store(base, w);
   }
   __syncthreads();
-  if constexpr (LEFT) {
-    // The earlier batches of this block: slab -= E[:, -nprev:0] U[i1-nprev:i1, i1:i1+ncols]
-    // on v_mfma_f32_16x16x4f32 (16 rows x 16 columns per tile; wave w takes
-    // column tiles w and w + 4).  U's rows and E's columns pass through LDS
-    // in chunks of 32 k values (16-byte loads by the whole workgroup, issued
-    // two chunks ahead into registers, two LDS buffers).
-    static_assert(G == 16 && sizeof(T) == 4 && ROWS == 16 && NT == 256, "left-looking update shape");
-    if (nprev > 0) {
-      const int l16 = lane & 15, lq = lane >> 4, nch = nprev / 32;
-      const int t0 = wave, t1 = wave + 4;
-      const bool on0 = 16 * t0 < ncols, on1 = 16 * t1 < ncols;
-      // Chunk c: U rows i1-nprev+32c .. +31, columns i1 .. i1+127 (clamped
-      // to ncols), thread items e = tid + 256 q: row e / 32, columns 4 (e % 32);
-      // E rows row0 .. row0+15, columns -nprev+32c .. +31: thread tid < 128
-      // loads row tid / 8, columns 4 (tid % 8).
-      auto load_chunk = [&](int c, f32x4 (&u)[4], f32x4& ev) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int e = tid + 256 * q, r = e >> 5, c4 = (e & 31) * 4;
-          u[q] = *(const f32x4*)(U + (int64_t)(i1 - nprev + 32 * c + r) * k + i1 + min(c4, ncols - 4));
-        }
-        const int er = (tid & 127) >> 3, ec = (tid & 7) * 4;
-        ev = *(const f32x4*)(Eslab - nprev + 32 * c + min(row0 + er, m - 1) * lde + ec);
-      };
-      auto store_chunk = [&](int buf, const f32x4 (&u)[4], const f32x4& ev) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int e = tid + 256 * q, r = e >> 5, c4 = (e & 31) * 4;
-          *(f32x4*)&Uc[buf][r][c4] = u[q];
-        }
-        if (tid < 128) *(f32x4*)&Ec[buf][tid >> 3][(tid & 7) * 4] = ev;
-      };
-      f32x4 acc0, acc1;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {   // the accumulators hold -slab: E U adds, the store negates back
-        acc0[r] = on0 ? -slab[4 * lq + r][16 * t0 + l16] : 0.0f;
-        acc1[r] = on1 ? -slab[4 * lq + r][16 * t1 + l16] : 0.0f;
-      }
-      f32x4 ua[4], ub[4], ea, eb;
-      load_chunk(0, ua, ea);
-      if (nch > 1) load_chunk(1, ub, eb);
-      store_chunk(0, ua, ea);
-      __syncthreads();
-      for (int c = 0; c < nch; ++c) {
-        // Registers: chunk c+1 in (c even ? ub : ua); chunk c+2 goes into the other set.
-        f32x4 (&un)[4] = (c & 1) ? ub : ua;
-        f32x4& en = (c & 1) ? eb : ea;
-        if (c + 2 < nch) load_chunk(c + 2, un, en);
-        const int buf = c & 1;
-#pragma unroll
-        for (int s4 = 0; s4 < 8; ++s4) {
-          const float av = Ec[buf][l16][4 * s4 + lq];
-          const float b0 = Uc[buf][4 * s4 + lq][16 * t0 + l16], b1 = Uc[buf][4 * s4 + lq][16 * t1 + l16];
-          acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(av, b0, acc0, 0, 0, 0);
-          acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(av, b1, acc1, 0, 0, 0);
-        }
-        // Buffer (c+1) & 1 was last read for chunk c-1, before the previous barrier.
-        if (c + 1 < nch) store_chunk((c + 1) & 1, (c & 1) ? ua : ub, (c & 1) ? ea : eb);
-        __syncthreads();
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if (on0) slab[4 * lq + r][16 * t0 + l16] = -acc0[r];
-        if (on1) slab[4 * lq + r][16 * t1 + l16] = -acc1[r];
-      }
-      __syncthreads();
-    }
-  }
+
   T loss = 0;
   const int nblk = ncols / kBlock;
   for (int b = 0; b < nblk; ++b) {
@@ -791,28 +720,26 @@ __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
 template <int G, typename T>
 hipError_t sweep_launch_g(T* Wp, const float* U, const float* invd, const float* g, int64_t m, int64_t k,
                           int i1, int ncols, int n_cand, bool indep, uint8_t* codes, uint8_t* scales, T* Eslab,
-                          int64_t lde, float* row_loss, hipStream_t s, int64_t nb, const SweepStrides& bs, int nprev) {
+                          int64_t lde, float* row_loss, hipStream_t s, int64_t nb, const SweepStrides& bs) {
   constexpr int ROWS = SweepCfg<G>::ROWS;
-  constexpr bool L = G == 16 && sizeof(T) == 4;   // the left-looking update exists for this shape only
-  if (nprev > 0 && (!L || nprev % 32 != 0)) return hipErrorInvalidValue;
   dim3 grid((unsigned)((m + ROWS - 1) / ROWS), (unsigned)nb);
   if (indep)
-    hipLaunchKernelGGL((sweep_batch_kernel<G, T, true, L>), grid, dim3(SweepCfg<G>::THREADS), 0, s, Wp, U, invd, g, m,
-                       k, i1, ncols, n_cand, codes, scales, Eslab, lde, row_loss, bs, nprev);
+    hipLaunchKernelGGL((sweep_batch_kernel<G, T, true>), grid, dim3(SweepCfg<G>::THREADS), 0, s, Wp, U, invd, g, m,
+                       k, i1, ncols, n_cand, codes, scales, Eslab, lde, row_loss, bs);
   else
-    hipLaunchKernelGGL((sweep_batch_kernel<G, T, false, L>), grid, dim3(SweepCfg<G>::THREADS), 0, s, Wp, U, invd, g,
-                       m, k, i1, ncols, n_cand, codes, scales, Eslab, lde, row_loss, bs, nprev);
+    hipLaunchKernelGGL((sweep_batch_kernel<G, T, false>), grid, dim3(SweepCfg<G>::THREADS), 0, s, Wp, U, invd, g, m,
+                       k, i1, ncols, n_cand, codes, scales, Eslab, lde, row_loss, bs);
   return hipGetLastError();
 }
 template <typename T>
 hipError_t sweep_launch_t(T* Wp, const float* U, const float* invd, const float* g, int64_t m, int64_t k, int i1,
                           int ncols, int n_cand, bool indep, uint8_t* codes, uint8_t* scales, T* Eslab, int64_t lde,
-                          float* row_loss, hipStream_t s, int64_t nb, const SweepStrides& bs, int nprev) {
-  if (n_cand <= 1) return sweep_launch_g<1>(Wp, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s, nb, bs, nprev);
-  if (n_cand <= 2) return sweep_launch_g<2>(Wp, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s, nb, bs, nprev);
-  if (n_cand <= 4) return sweep_launch_g<4>(Wp, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s, nb, bs, nprev);
-  if (n_cand <= 8) return sweep_launch_g<8>(Wp, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s, nb, bs, nprev);
-  return sweep_launch_g<16>(Wp, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s, nb, bs, nprev);
+                          float* row_loss, hipStream_t s, int64_t nb, const SweepStrides& bs) {
+  if (n_cand <= 1) return sweep_launch_g<1>(Wp, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s, nb, bs);
+  if (n_cand <= 2) return sweep_launch_g<2>(Wp, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s, nb, bs);
+  if (n_cand <= 4) return sweep_launch_g<4>(Wp, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s, nb, bs);
+  if (n_cand <= 8) return sweep_launch_g<8>(Wp, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s, nb, bs);
+  return sweep_launch_g<16>(Wp, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s, nb, bs);
 }
 
 }  // namespace
@@ -896,14 +823,12 @@ hipError_t load_working_copy_f64(const void* W, int bf16, int64_t m, int64_t k, 
   return hipGetLastError();
 }
 
-bool sweep_left_looking(int n_cand) { return n_cand > 8; }
-
 hipError_t sweep_batch_launch(float* Wp, const float* U, const float* invd, const float* g, int64_t m, int64_t k,
                               int i1, int ncols, int n_cand, bool indep, uint8_t* codes, uint8_t* scales,
                               float* Eslab, int64_t lde, float* row_loss, hipStream_t s, int64_t nb,
-                              const SweepStrides& bs, int nprev) {
+                              const SweepStrides& bs) {
   return sweep_launch_t<float>(Wp, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s,
-                               nb, bs, nprev);
+                               nb, bs);
 }
 hipError_t sweep_batch_launch_f64(double* Wp, const float* U, const float* g, int64_t m, int64_t k, int i1,
                                   int ncols, int n_cand, bool indep, uint8_t* codes, uint8_t* scales, double* Eslab,
@@ -912,7 +837,7 @@ hipError_t sweep_batch_launch_f64(double* Wp, const float* U, const float* g, in
   SweepStrides b2 = bs;
   b2.invd = bs.u;
   return sweep_launch_t<double>(Wp, U, U, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s,
-                                nb, b2, 0);
+                                nb, b2);
 }
 
 hipError_t delta_w_launch(const void* W, int bf16, int64_t m, int64_t k, int64_t ldw, const uint8_t* codes,
