@@ -152,13 +152,14 @@ def summarize_pmc(fetch_csv, write_csv):
                         "python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline",
                         "python3 bench.py --summarize-pmc gpurun_out/pmcf/fetch_counter_collection.csv "
                         "gpurun_out/pmcw/write_counter_collection.csv"],
-           "kernel": "hessian_accumulate (syrk_main_kernel + syrk_single_kernel + syrk_reduce_kernel)",
+           "kernel": "hessian_accumulate (first launch syrk_k4_kernel, or syrk_main_kernel when k is not 16 "
+                     "segments of 256; syrk_single_kernel; the syrk_reduce kernels)",
            "workload": WORKLOAD, "source_digest": hessian_source_digest(), "unit": "bytes per call",
            "calibration_copy_bytes": CAL_COPY_BYTES}
     total = 0.0
     for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         rows = per_dispatch(path, name)
-        calls = sum(1 for n, _ in rows if "syrk_main_kernel" in n)
+        calls = sum(1 for n, _ in rows if "syrk_main_kernel" in n or "syrk_k4_kernel" in n)
         kib = sum(v for n, v in rows if "syrk_" in n) / max(1, calls)
         copies = [v for n, v in rows if "bitwise_not" in n]
         if not calls or not copies:

@@ -46,6 +46,7 @@ namespace {
 constexpr int ST = 32;       // tokens per stage
 constexpr int NS = 4;        // ring depth (stages in flight + the one being multiplied)
 constexpr int HEAD16 = 13;   // sixteenths of a token range a strip pair covers in the first launch
+constexpr int HEAD16_K4 = 10;   // the same beside four-group tiles
 constexpr int TSPLIT = 4;                 // tail pieces per (range, strip pair)
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -328,6 +329,334 @@ __device__ __forceinline__ void tile_job(char* lds, const uint16_t* __restrict__
   }
 }
 
+// ---- Four-group tiles (layers of 16 segments) ---------------------------------
+// A quad moves 4 groups of 128 channels per token for 4 group pairs.  A
+// workgroup that loads 4 groups can instead multiply all 6 of their pairs
+// (98304 products, 384 accumulator registers per lane), a third fewer bytes
+// per product.  For 16 segments of 256 channels (32 groups, segment m holding
+// groups 2m and 2m+1), the pairs of groups in different segments are covered
+// exactly once by 80 such tiles: a group divisible design with block size 4
+// and 16 groups of size 2 (Brouwer, Schrijver and Hanani, "Group divisible
+// designs with block-size four", Discrete Math. 1977, show that it exists).
+// This one was found by computer search as a design invariant under the shift
+// x -> x + 4 (mod 32) of group indices: nine base blocks give orbits of 8
+// blocks, and two blocks fixed by x -> x + 16 give orbits of 4.  The pairs
+// inside a segment (its diagonal 256-block) stay with the strips and singles.
+constexpr int K4_SEGS = 16, K4_TILES = 80, K4G = 128;
+struct K4Table { uint8_t g[K4_TILES][4]; };
+constexpr uint8_t kK4Base[9][4] = {{2, 12, 20, 29}, {0, 4, 7, 10}, {3, 11, 12, 24}, {0, 21, 27, 29}, {2, 4, 17, 30},
+                                   {1, 11, 21, 28}, {1, 22, 29, 30}, {3, 15, 21, 30}, {3, 10, 22, 31}};
+constexpr uint8_t kK4Fixed[2][4] = {{0, 2, 16, 18}, {1, 3, 17, 19}};
+constexpr K4Table make_k4_table() {
+  K4Table t{};
+  int n = 0;
+  for (int s = 0; s < 8; ++s)
+    for (int b = 0; b < 9; ++b, ++n)
+      for (int q = 0; q < 4; ++q) t.g[n][q] = (uint8_t)((kK4Base[b][q] + 4 * s) % 32);
+  for (int s = 0; s < 4; ++s)
+    for (int b = 0; b < 2; ++b, ++n)
+      for (int q = 0; q < 4; ++q) t.g[n][q] = (uint8_t)(kK4Fixed[b][q] + 4 * s);
+  for (int i = 0; i < K4_TILES; ++i)   // increasing group order within a tile
+    for (int a = 1; a < 4; ++a)
+      for (int c = a; c > 0 && t.g[i][c - 1] > t.g[i][c]; --c) {
+        const uint8_t x = t.g[i][c];
+        t.g[i][c] = t.g[i][c - 1];
+        t.g[i][c - 1] = x;
+      }
+  return t;
+}
+// Every pair of groups in different segments lies in exactly one tile, and no
+// tile holds both groups of a segment.
+constexpr bool k4_table_ok(const K4Table& t) {
+  int cnt[32][32] = {};
+  for (int i = 0; i < K4_TILES; ++i)
+    for (int a = 0; a < 4; ++a)
+      for (int b = a + 1; b < 4; ++b) {
+        if (t.g[i][a] / 2 == t.g[i][b] / 2 || t.g[i][a] >= t.g[i][b]) return false;
+        ++cnt[t.g[i][a]][t.g[i][b]];
+      }
+  for (int a = 0; a < 32; ++a)
+    for (int b = a + 1; b < 32; ++b)
+      if (cnt[a][b] != (a / 2 == b / 2 ? 0 : 1)) return false;
+  return true;
+}
+constexpr K4Table kK4Host = make_k4_table();
+static_assert(k4_table_ok(kK4Host), "the four-group tiles must cover every cross-segment group pair once");
+__constant__ K4Table kK4 = make_k4_table();
+
+// Index of the pair of regions (a, b), a < b, in a tile's partial sums.
+__host__ __device__ constexpr int k4_pair(int a, int b) { return a == 0 ? b - 1 : (a == 1 ? b + 1 : 5); }
+constexpr size_t kK4SlotFloats = (size_t)6 * K4G * K4G;   // 1.5 quad slots
+constexpr int K4_ROWB = K4G * 2;                          // bytes of a group's token row
+constexpr int K4_REGION = ST * K4_ROWB;                   // one group's rows of a stage
+constexpr int K4_STAGE = 4 * K4_REGION;
+static_assert(K4_STAGE == Tile<QUAD, QUAD>::STAGE_BYTES, "same LDS ring as a quad");
+
+// Wave roles.  A stage holds the tile's four groups as regions 0..3 (in
+// increasing channel order).  Each wave multiplies one whole 128x128 pair
+// block (rows region X, columns region Y) and half of another: in form A
+// (waves 0 and 1) rows X times columns 0..63 of region Z, in form B (waves 2
+// and 3) rows Z times columns 64..127 of region Y.  Blocks: wave 0 (0,1) and
+// the left half of (0,3); wave 1 (1,3) and the left half of (1,2); wave 2
+// (2,3) and the right half of (0,3); wave 3 (0,2) and the right half of
+// (1,2).  Every block has its rows before its columns, so it lies in H's
+// upper triangle.  A wave reads 10 (form A) or 12 (form B) operand fragments
+// per k-step for its 24 products.
+template <int W> struct K4Role;
+template <> struct K4Role<0> { static constexpr int X = 0, Y = 1, Z = 3, B = 0; };
+template <> struct K4Role<1> { static constexpr int X = 1, Y = 3, Z = 2, B = 0; };
+template <> struct K4Role<2> { static constexpr int X = 2, Y = 3, Z = 0, B = 1; };
+template <> struct K4Role<3> { static constexpr int X = 0, Y = 2, Z = 1, B = 1; };
+
+// Region layout: [32 token rows][128 channels], 16-byte chunk p of row r
+// stored at chunk p ^ 4 (r % 4).  A transposed fragment read (16 lanes: rows
+// T + j/4, 8 bytes at channel C + 4 (j % 4)) then hits 64 distinct banks per
+// 32 lanes, and since r % 4 is fixed per lane (T is a multiple of 4) a lane's
+// address for fragment f is its own base for f plus immediates for the
+// region, the half and the k-step.
+template <int W>
+__device__ __forceinline__ bf16x8 k4_frag(const char* buf, const int (&F)[4], int region, int f, int kk) {
+  const char* p = buf + F[f] + region * K4_REGION + kk * 16 * K4_ROWB;
+  s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)p);
+  s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(p + 4 * K4_ROWB));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+template <int W>
+struct K4Frags {
+  static constexpr int NZ = K4Role<W>::B ? 4 : 2;
+  bf16x8 x[4], y[4], z[NZ];
+};
+
+// Fragment m of k-step kk: m < 4 region X, m < 8 region Y, then region Z.
+template <int W>
+__device__ __forceinline__ void k4_read(const char* buf, const int (&F)[4], int m, int kk, K4Frags<W>& fr) {
+  using R = K4Role<W>;
+  if (m < 4) fr.x[m] = k4_frag<W>(buf, F, R::X, m, kk);
+  else if (m < 8) fr.y[m - 4] = k4_frag<W>(buf, F, R::Y, m - 4, kk);
+  else fr.z[m - 8] = k4_frag<W>(buf, F, R::Z, m - 8, kk);
+}
+
+// The half block's eight accumulators (128 registers) live in VGPRs, the
+// whole block's sixteen (256) in AGPRs: the compiler would put every product
+// of a builtin into AGPRs, which 384 accumulators overflow.  So the half
+// block's products are written as inline assembly with VGPR operands.  The
+// compiler tracks their registers but not the matrix unit's hazards, so
+// k4_mfma_fence waits out the longest pass count (16 passes plus the
+// margin, 24 wait states) between them and any other access to their
+// accumulators: after the zeroing and before the epilogue.
+__device__ __forceinline__ void k4_mfma_fence(f32x16 (&accH)[4][2]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+v"(accH[0][0]), "+v"(accH[0][1]), "+v"(accH[1][0]), "+v"(accH[1][1]), "+v"(accH[2][0]),
+                 "+v"(accH[2][1]), "+v"(accH[3][0]), "+v"(accH[3][1]));
+}
+
+// Product m: m < 16 the whole block's tile (m / 4, m % 4), then the half
+// block's tile ((m - 16) / 2, (m - 16) % 2).
+template <int W>
+__device__ __forceinline__ void k4_mfma(int m, const K4Frags<W>& fr, f32x16 (&accF)[4][4], f32x16 (&accH)[4][2]) {
+  if (m < 16) {
+    accF[m / 4][m % 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.x[m / 4], fr.y[m % 4], accF[m / 4][m % 4], 0, 0, 0);
+  } else {
+    const int q = m - 16;
+    if constexpr (K4Role<W>::B)
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(accH[q / 2][q % 2]) : "v"(fr.z[q / 2]), "v"(fr.y[2 + q % 2]));
+    else
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(accH[q / 2][q % 2]) : "v"(fr.x[q / 2]), "v"(fr.z[q % 2]));
+  }
+}
+
+// Load q (0..7) of wave W for the stage at src (nrec bytes to the end of the
+// token range, capped): token rows 4 (W + 4 (q % 2)) .. +3 of region q / 2,
+// into LDS bytes (W + 4q) * 1024 of the stage.  The buffer starts at the
+// region's first channel with its bound moved by the same bytes, so rows past
+// the range still read as zeros; voff[q % 2] is the lane's row and (swizzled)
+// chunk within the stage.
+template <int W, int q>
+__device__ __forceinline__ void k4_load(char* slot, const uint16_t* src, int nrec, const int64_t (&ch)[4],
+                                        const uint32_t (&voff)[2]) {
+#if __HIP_DEVICE_COMPILE__
+  const int left = nrec - 2 * (int)ch[q >> 1];
+  __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(src + ch[q >> 1]), (short)0, left > 0 ? left : 0, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (LDS_AS void*)(slot + (W + 4 * q) * 1024), 16, voff[q & 1], 0, 0, 0);
+#endif
+}
+
+template <int W>
+__device__ __forceinline__ void k4_loads(char* slot, const uint16_t* src, int nrec, const int64_t (&ch)[4],
+                                         const uint32_t (&voff)[2], int m) {
+  switch (m) {
+    case 0: k4_load<W, 0>(slot, src, nrec, ch, voff); break;
+    case 1: k4_load<W, 1>(slot, src, nrec, ch, voff); break;
+    case 2: k4_load<W, 2>(slot, src, nrec, ch, voff); break;
+    case 3: k4_load<W, 3>(slot, src, nrec, ch, voff); break;
+    case 4: k4_load<W, 4>(slot, src, nrec, ch, voff); break;
+    case 5: k4_load<W, 5>(slot, src, nrec, ch, voff); break;
+    case 6: k4_load<W, 6>(slot, src, nrec, ch, voff); break;
+    case 7: k4_load<W, 7>(slot, src, nrec, ch, voff); break;
+    default: break;
+  }
+}
+
+// One 32x32 accumulator tile at rows r0, columns c0 of pair block `pair`
+// (rows from channel rch, columns from cch): into H (add, and the mirror) or
+// into the tile's partial sums P [pair][128][128].
+__device__ __forceinline__ void k4_store(const f32x16& acc, int pair, int r0, int c0, int64_t rch, int64_t cch,
+                                         int64_t k, float* __restrict__ H, float* __restrict__ P) {
+  const int lane = threadIdx.x & 63, col = c0 + (lane & 31);
+  if (P) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = r0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      P[(size_t)pair * K4G * K4G + row * K4G + col] = acc[r];
+    }
+    return;
+  }
+  const int64_t gj = cch + col;
+  float old[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int64_t gi = rch + r0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+    old[r] = (gi < k && gj < k) ? H[gi * k + gj] : 0.0f;
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int64_t gi = rch + r0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+    if (gi < k && gj < k) {   // gi < gj: the groups differ and are in increasing order
+      const float v = old[r] + acc[r];
+      H[gi * k + gj] = v;
+      H[gj * k + gi] = v;
+    }
+  }
+}
+
+// One pipeline step over a four-group stage (the order of pipe_step): the
+// first k-step's 24 products interleaved with the second k-step's fragment
+// reads, then the wait for stage s+1 and the barrier, then the second
+// k-step's products interleaved with the refill of `slot` and the next
+// stage's first fragments.  `slot` and `nxt` are distinct, which the restrict
+// qualifiers state, so operand reads need not wait on the loads in flight.
+template <int W, bool has_next>
+__device__ __forceinline__ void k4_step(char* __restrict__ slot, const char* __restrict__ nxt, const uint16_t* src,
+                                        int nrec, const int64_t (&ch)[4], const uint32_t (&voff)[2],
+                                        const int (&F)[4], K4Frags<W>& f0, f32x16 (&accF)[4][4],
+                                        f32x16 (&accH)[4][2]) {
+  constexpr int NF = 8 + K4Frags<W>::NZ, NM = 24, NL = 8;
+  constexpr int kWait = (NS - 2) * NL;
+  static_assert(NS >= 2 && kWait < 64, "ring depth");
+  K4Frags<W> f1;
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    if (m < NF) k4_read<W>(slot, F, m, 1, f1);
+    k4_mfma<W>(m, f0, accF, accH);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if constexpr (has_next) {
+    __builtin_amdgcn_s_waitcnt((kWait & 15) | (7 << 4) | (0 << 8) | ((kWait >> 4) << 14));
+    asm volatile("s_barrier" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    if constexpr (has_next) {
+      if (m < NL) k4_loads<W>(slot, src, nrec, ch, voff, m);
+      if (m < NF) k4_read<W>(nxt, F, m, 0, f0);
+    }
+    k4_mfma<W>(m, f1, accF, accH);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <int W>
+__device__ __forceinline__ void k4_wave(char* lds, const uint16_t* __restrict__ X, int64_t k, int64_t ldx,
+                                        const int64_t (&ch)[4], int64_t t_begin, int64_t t_end,
+                                        float* __restrict__ H, float* __restrict__ P) {
+  using R = K4Role<W>;
+  constexpr int NF = 8 + K4Frags<W>::NZ, NL = 8;
+  const int nstages = t_end > t_begin ? (int)((t_end - t_begin + ST - 1) / ST) : 0;
+  const int lane = threadIdx.x & 63, g = lane >> 4, j = lane & 15, s4 = j >> 2;
+  int F[4];
+#pragma unroll
+  for (int f = 0; f < 4; ++f) F[f] = (8 * (g >> 1) + s4) * K4_ROWB + 64 * (f ^ s4) + 32 * (g & 1) + 8 * (j & 3);
+  uint32_t voff[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    voff[h] = (uint32_t)((4 * (W + 4 * h) + (lane >> 4)) * ldx * 2 + 16 * ((lane & 15) ^ (4 * (lane >> 4))));
+  auto stage_nrec = [&](int st) -> int {
+    return st < nstages ? (int)min((t_end - t_begin - (int64_t)st * ST) * ldx * 2, (int64_t)0x7FFFFFF0) : 0;
+  };
+  auto stage_src = [&](int st) -> const uint16_t* {
+    return X + (st < nstages ? t_begin + (int64_t)st * ST : t_begin) * ldx;
+  };
+
+  f32x16 accF[4][4], accH[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) accF[i][c][r] = 0.0f;
+      accH[i][0][r] = 0.0f;
+      accH[i][1][r] = 0.0f;
+    }
+
+  // Prologue: fill every slot (zero-length loads past the end), then read
+  // stage 0's first fragments.
+  for (int s = 0; s < NS; ++s)
+#pragma unroll
+    for (int m = 0; m < NL; ++m) k4_loads<W>(lds + s * K4_STAGE, stage_src(s), stage_nrec(s), ch, voff, m);
+  K4Frags<W> f0;
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
+  asm volatile("s_barrier" ::: "memory");
+#pragma unroll
+  for (int m = 0; m < NF; ++m) k4_read<W>(lds, F, m, 0, f0);
+  k4_mfma_fence(accH);
+  for (int s = 0; s + 1 < nstages; ++s)
+    k4_step<W, true>(lds + (s % NS) * K4_STAGE, lds + ((s + 1) % NS) * K4_STAGE, stage_src(s + NS),
+                     stage_nrec(s + NS), ch, voff, F, f0, accF, accH);
+  if (nstages > 0) {
+    const int s = nstages - 1;
+    k4_step<W, false>(lds + (s % NS) * K4_STAGE, lds, stage_src(s), 0, ch, voff, F, f0, accF, accH);
+  }
+  __builtin_amdgcn_s_waitcnt(0);   // the zero-length loads past the end write LDS too
+  k4_mfma_fence(accH);
+
+  const int pF = k4_pair(R::X, R::Y);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) k4_store(accF[i][c], pF, 32 * i, 32 * c, ch[R::X], ch[R::Y], k, H, P);
+  if constexpr (R::B) {
+    const int pH = k4_pair(R::Z, R::Y);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) k4_store(accH[i][c], pH, 32 * i, 64 + 32 * c, ch[R::Z], ch[R::Y], k, H, P);
+  } else {
+    const int pH = k4_pair(R::X, R::Z);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) k4_store(accH[i][c], pH, 32 * i, 32 * c, ch[R::X], ch[R::Z], k, H, P);
+  }
+}
+
+// Tile t of the table over tokens [t_begin, t_end): into H, or into its
+// partial sums P (kK4SlotFloats).
+__device__ __forceinline__ void k4_job(char* lds, const uint16_t* __restrict__ X, int64_t k, int64_t ldx, int t,
+                                       int64_t t_begin, int64_t t_end, float* __restrict__ H, float* __restrict__ P) {
+  int64_t ch[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) ch[q] = (int64_t)kK4.g[t][q] * K4G;
+  switch (threadIdx.x >> 6) {
+    case 0: k4_wave<0>(lds, X, k, ldx, ch, t_begin, t_end, H, P); break;
+    case 1: k4_wave<1>(lds, X, k, ldx, ch, t_begin, t_end, H, P); break;
+    case 2: k4_wave<2>(lds, X, k, ldx, ch, t_begin, t_end, H, P); break;
+    default: k4_wave<3>(lds, X, k, ldx, ch, t_begin, t_end, H, P); break;
+  }
+}
+
 // Order of the first launch's items within one token range.  256-blocks are
 // grouped into super-blocks of SB; for each super-block A in turn come the
 // quads inside A (row-major), then A's strips in pairs (2p, 2p+1), then the
@@ -423,34 +752,76 @@ __device__ __forceinline__ int xcd_logical(int id, int G) {
   return (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + i;
 }
 
-// Launch 1: G = qsplit * per_range items; logical item L covers token range
-// L / per_range and item L % per_range of the order above (a strip pair only
-// the head of the range when there are tail pieces).  With qsplit > 1 the
-// item's partial sums go to slot L (a strip pair's two 128x256 strips fill
-// the two halves of the slot).
+// First-launch parameters.  Without four-group tiles: qsplit * per_range
+// items; logical item L covers token range L / per_range and item L %
+// per_range of the order above (a strip pair only the head of the range when
+// there are tail pieces), and with qsplit > 1 writes its partial sums to slot
+// L (a strip pair's two 128x256 strips fill the two halves of the slot).  With
+// them (k4 = 1): first the K4_TILES * q4 tiles (tile L % K4_TILES over token
+// range L / K4_TILES of q4, partial sums at L * kK4SlotFloats when q4 > 1),
+// then qsplit * per_range strip pairs (per_range = the pairs; pair p of range
+// sp is item sp * per_range + p, partial slot pair_base + that).
+struct MainArgs {
+  int per_range, qsplit;
+  int64_t qtokens;
+  int k4, q4;
+  int64_t k4tokens, pair_base;
+};
+
+__device__ __forceinline__ void strip_pair_job(char* lds, const uint16_t* __restrict__ X, int64_t k, int64_t ldx,
+                                               int a, int b, int64_t t0, int64_t te, float* __restrict__ H,
+                                               float* __restrict__ P) {
+  tile_job<HALF, QUAD, true>(lds, X, k, ldx, (int64_t)a * QUAD, (int64_t)a * QUAD, t0, te, H, P);
+  if (b >= 0) {
+    __syncthreads();   // the LDS ring is reused
+    tile_job<HALF, QUAD, true>(lds, X, k, ldx, (int64_t)b * QUAD, (int64_t)b * QUAD, t0, te, H,
+                               P ? P + HALF * QUAD : nullptr);
+  }
+}
+
+// The strip pair of item L (its range and its pair), as the first launch runs it.
+__device__ __forceinline__ void first_launch_pair(char* lds, const uint16_t* __restrict__ X, int64_t n, int64_t k,
+                                                  int64_t ldx, float* __restrict__ H, float* __restrict__ partial,
+                                                  const MainArgs& m, const TailArgs& tail, int L, int a, int b) {
+  const int64_t t0 = (int64_t)(L / m.per_range) * m.qtokens, t1 = min(n, t0 + m.qtokens);
+  const int64_t te = tail.npairs > 0 ? min(t1, t0 + tail.head) : t1;   // the rest is tail work
+  strip_pair_job(lds, X, k, ldx, a, b, t0, te, H, m.qsplit > 1 ? partial + ((size_t)m.pair_base + L) * kSlotFloats : nullptr);
+}
+
 __global__ __launch_bounds__(256) void syrk_main_kernel(const uint16_t* __restrict__ X, int64_t n, int64_t k,
                                                         int64_t ldx, float* __restrict__ H,
-                                                        float* __restrict__ partial, int per_range, int qsplit,
-                                                        int64_t qtokens, TailArgs tail) {
+                                                        float* __restrict__ partial, MainArgs m, TailArgs tail) {
   extern __shared__ __attribute__((aligned(1024))) char lds[];
   const int nb2 = (int)((k + QUAD - 1) / QUAD);
   const int L = xcd_logical(blockIdx.x, gridDim.x);
-  const int sp = L / per_range;
   int kind, a, b;
-  item_coords(L % per_range, nb2, kind, a, b);
-  const int64_t t0 = (int64_t)sp * qtokens, t1 = min(n, t0 + qtokens);
-  float* P = qsplit > 1 ? partial + (size_t)L * kSlotFloats : nullptr;
+  item_coords(L % m.per_range, nb2, kind, a, b);
   if (kind == 0) {
-    tile_job<QUAD, QUAD, false>(lds, X, k, ldx, (int64_t)a * QUAD, (int64_t)b * QUAD, t0, t1, H, P);
+    const int64_t t0 = (int64_t)(L / m.per_range) * m.qtokens, t1 = min(n, t0 + m.qtokens);
+    tile_job<QUAD, QUAD, false>(lds, X, k, ldx, (int64_t)a * QUAD, (int64_t)b * QUAD, t0, t1, H,
+                                m.qsplit > 1 ? partial + (size_t)L * kSlotFloats : nullptr);
   } else if (kind == 1) {
-    const int64_t te = tail.npairs > 0 ? min(t1, t0 + tail.head) : t1;   // the rest is tail work
-    tile_job<HALF, QUAD, true>(lds, X, k, ldx, (int64_t)a * QUAD, (int64_t)a * QUAD, t0, te, H, P);
-    if (b >= 0) {
-      __syncthreads();   // the LDS ring is reused
-      tile_job<HALF, QUAD, true>(lds, X, k, ldx, (int64_t)b * QUAD, (int64_t)b * QUAD, t0, te, H,
-                           P ? P + HALF * QUAD : nullptr);
-    }
+    first_launch_pair(lds, X, n, k, ldx, H, partial, m, tail, L, a, b);
   }
+}
+
+// The first launch with four-group tiles: K4_TILES * q4 tiles, then the
+// strip pairs.
+__global__ __launch_bounds__(256) void syrk_k4_kernel(const uint16_t* __restrict__ X, int64_t n, int64_t k,
+                                                      int64_t ldx, float* __restrict__ H,
+                                                      float* __restrict__ partial, MainArgs m, TailArgs tail) {
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+  const int nb2 = (int)((k + QUAD - 1) / QUAD);
+  const int L = xcd_logical(blockIdx.x, gridDim.x);
+  const int nk = K4_TILES * m.q4;
+  if (L < nk) {
+    const int64_t t0 = (int64_t)(L / K4_TILES) * m.k4tokens, t1 = min(n, t0 + m.k4tokens);
+    k4_job(lds, X, k, ldx, L % K4_TILES, t0, t1, H, m.q4 > 1 ? partial + (size_t)L * kK4SlotFloats : nullptr);
+    return;
+  }
+  int kind, a, b;
+  item_coords(pair_item((L - nk) % m.per_range, nb2), nb2, kind, a, b);
+  first_launch_pair(lds, X, n, k, ldx, H, partial, m, tail, L - nk, a, b);
 }
 
 // Launch 2: singles (bottom-right diagonal 128-block of 256-block a), split
@@ -481,12 +852,7 @@ __global__ __launch_bounds__(256) void syrk_single_kernel(const uint16_t* __rest
   const int64_t r1 = min(n, (int64_t)sp * qtokens + qtokens);
   const int64_t ts = min(r1, (int64_t)sp * qtokens + tail.head + (int64_t)t * tail.ttokens);
   const int64_t te = min(r1, ts + tail.ttokens);
-  float* P = partial + ((size_t)tail.base + u) * kSlotFloats;
-  tile_job<HALF, QUAD, true>(lds, X, k, ldx, (int64_t)a * QUAD, (int64_t)a * QUAD, ts, te, H, P);
-  if (b >= 0) {
-    __syncthreads();   // the LDS ring is reused
-    tile_job<HALF, QUAD, true>(lds, X, k, ldx, (int64_t)b * QUAD, (int64_t)b * QUAD, ts, te, H, P + HALF * QUAD);
-  }
+  strip_pair_job(lds, X, k, ldx, a, b, ts, te, H, partial + ((size_t)tail.base + u) * kSlotFloats);
 }
 
 // Sum the token splits of one 64x64 piece of a tile in split order, add the
@@ -618,16 +984,53 @@ __global__ __launch_bounds__(256) void syrk_reduce_kernel(int64_t k, float* __re
   }
 }
 
+// With four-group tiles.  kind 0: blockIdx.x is tile t, whose split sp sits
+// at (sp * K4_TILES + t) * kK4SlotFloats; blockIdx.y (0..23) is a 64x64 piece
+// of its six 128x128 pair blocks (2x2 each).  kind 1: blockIdx.x is strip
+// pair p, whose split sp sits in slot slot_base + sp * per_range + p (then
+// its tail pieces); blockIdx.y (0..15) is a piece of its two 2x4.
+__global__ __launch_bounds__(256) void syrk_reduce_k4_kernel(int64_t k, float* __restrict__ H,
+                                                             const float* __restrict__ partial, int kind, int nsplit,
+                                                             int per_range, size_t slot_base, TailArgs tail) {
+  const int y = blockIdx.y;
+  if (kind == 0) {
+    const int t = blockIdx.x, pair = y / 4, pr = (y % 4) / 2, pc = y % 2;
+    const int ra = pair < 3 ? 0 : (pair < 5 ? 1 : 2), rb = pair < 3 ? pair + 1 : (pair < 5 ? pair - 1 : 3);
+    const float* P = partial + (size_t)t * kK4SlotFloats + (size_t)pair * K4G * K4G + pr * PIECE * K4G + pc * PIECE;
+    reduce_piece(k, H, P, (size_t)K4_TILES * kK4SlotFloats, nsplit, K4G,
+                 (int64_t)kK4.g[t][ra] * K4G + pr * PIECE, (int64_t)kK4.g[t][rb] * K4G + pc * PIECE);
+    return;
+  }
+  const int nb2 = (int)((k + QUAD - 1) / QUAD);
+  const int p = blockIdx.x;
+  int ik, a, b;
+  item_coords(pair_item(p, nb2), nb2, ik, a, b);
+  const int d = y < 8 ? a : b;
+  if (d < 0) return;
+  const int pr = (y & 7) / 4, pc = y % 4;
+  const size_t off = (y < 8 ? 0 : (size_t)HALF * QUAD) + (size_t)pr * PIECE * QUAD + pc * PIECE;
+  const float* P2 = nullptr;
+  int n2 = 0;
+  if (tail.npairs > 0) {   // then the pair's tail pieces, by range and piece
+    P2 = partial + ((size_t)tail.base + (size_t)p * tail.tsplit) * kSlotFloats + off;
+    n2 = nsplit * tail.tsplit;
+  }
+  reduce_piece(k, H, partial + (slot_base + p) * kSlotFloats + off, (size_t)per_range * kSlotFloats, nsplit, QUAD,
+               (int64_t)d * QUAD + pr * PIECE, (int64_t)d * QUAD + pc * PIECE, P2, n2, tail.tsplit,
+               (size_t)tail.npairs * tail.tsplit * kSlotFloats, kSlotFloats);
+}
+
 __global__ void symmetrize_kernel(float* H, int64_t k) {
   int64_t i = blockIdx.y, j = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (j < k && j < i) H[i * k + j] = H[j * k + i];
 }
 
 struct SyrkPlan {
-  int nb2, per_range, qsplit, nsingle, ssplit;
-  int64_t qtokens, stokens;
+  int nb2, nsingle, ssplit;
+  MainArgs m;        // per_range, qsplit, qtokens: the first launch's quads and strip pairs (or pairs alone)
+  int64_t stokens;
   TailArgs tail;
-  size_t slots;
+  size_t slots;      // partial slots of kSlotFloats
 };
 
 int num_cus() {
@@ -641,37 +1044,67 @@ int num_cus() {
   return cus;
 }
 
+// Token ranges of the four-group tiles: as many as give every tile range a CU
+// of its own.  The strip pairs split over the CUs left (at least one range).
+// Both counts grow with n up to their caps, never down.
+int k4_ranges(int64_t nstages, int cus) {
+  int64_t s = cus / K4_TILES;
+  if (s > nstages) s = nstages;
+  return s < 1 ? 1 : (int)s;
+}
+int k4_pair_ranges(int64_t nstages, int cus, int npairs) {
+  int64_t s = (cus - (int64_t)K4_TILES * (cus / K4_TILES)) / npairs;
+  if (s > nstages) s = nstages;
+  return s < 1 ? 1 : (int)s;
+}
+
 SyrkPlan plan(int64_t n, int64_t k, int cus) {
   SyrkPlan p;
   p.nb2 = (int)((k + QUAD - 1) / QUAD);
-  p.per_range = items_per_range(p.nb2);
   p.nsingle = 0;
   for (int a = 0; a < p.nb2; ++a)
     if ((int64_t)a * QUAD + HALF < k) ++p.nsingle;
   int64_t nstages = (n + ST - 1) / ST;
   if (nstages < 1) nstages = 1;
-  // Split the first launch's items over token ranges while they would not
-  // give every CU an item.
-  p.qsplit = 1;
-  if (p.per_range < cus) {
-    int64_t s = (cus + p.per_range - 1) / p.per_range;
-    if (s > nstages) s = nstages;
-    p.qsplit = (int)(s < 1 ? 1 : s);
-  }
-  p.qtokens = ((nstages + p.qsplit - 1) / p.qsplit) * ST;
-  // Strip-pair tails (only with token splits, whose partial sums the tails
-  // join): the pairs keep HEAD16/16 of each range, whole stages, when the
-  // pieces leave at least half the device to the singles.
-  p.tail = TailArgs{0, 1, 0, 0, 0};
-  if (p.qsplit > 1) {
-    const int npairs = pairs_per_range(p.nb2);
-    const int64_t head = p.qtokens * HEAD16 / 16 / ST * ST;
-    if (npairs > 0 && head > 0 && head < p.qtokens && (int64_t)npairs * p.qsplit * TSPLIT <= cus / 2) {
-      const int64_t per = (p.qtokens - head + TSPLIT - 1) / TSPLIT;
-      p.tail = TailArgs{npairs, TSPLIT, head, (per + ST - 1) / ST * ST, (int64_t)p.per_range * p.qsplit};
+  MainArgs& m = p.m;
+  m.k4 = p.nb2 == K4_SEGS;
+  m.q4 = 0;
+  m.k4tokens = 0;
+  m.pair_base = 0;
+  int head16 = HEAD16;
+  if (m.k4) {
+    // Four-group tiles for the quads, then the strip pairs alone.
+    m.q4 = k4_ranges(nstages, cus);
+    m.k4tokens = ((nstages + m.q4 - 1) / m.q4) * ST;
+    m.per_range = pairs_per_range(p.nb2);
+    m.qsplit = k4_pair_ranges(nstages, cus, m.per_range);
+    m.pair_base = m.q4 > 1 ? (int64_t)((K4_TILES * m.q4 * kK4SlotFloats + kSlotFloats - 1) / kSlotFloats) : 0;
+    head16 = HEAD16_K4;
+  } else {
+    // Split the first launch's items over token ranges while they would not
+    // give every CU an item.
+    m.per_range = items_per_range(p.nb2);
+    m.qsplit = 1;
+    if (m.per_range < cus) {
+      int64_t s = (cus + m.per_range - 1) / m.per_range;
+      if (s > nstages) s = nstages;
+      m.qsplit = (int)(s < 1 ? 1 : s);
     }
   }
-  const int tail_items = p.tail.npairs * p.qsplit * p.tail.tsplit;
+  m.qtokens = ((nstages + m.qsplit - 1) / m.qsplit) * ST;
+  // Strip-pair tails (only with token splits, whose partial sums the tails
+  // join): the pairs keep head16/16 of each range, whole stages, when the
+  // pieces leave at least half the device to the singles.
+  p.tail = TailArgs{0, 1, 0, 0, 0};
+  if (m.qsplit > 1) {
+    const int npairs = pairs_per_range(p.nb2);
+    const int64_t head = m.qtokens * head16 / 16 / ST * ST;
+    if (npairs > 0 && head > 0 && head < m.qtokens && (int64_t)npairs * m.qsplit * TSPLIT <= cus / 2) {
+      const int64_t per = (m.qtokens - head + TSPLIT - 1) / TSPLIT;
+      p.tail = TailArgs{npairs, TSPLIT, head, (per + ST - 1) / ST * ST, 0};
+    }
+  }
+  const int tail_items = p.tail.npairs * m.qsplit * p.tail.tsplit;
   p.ssplit = 1;
   if (p.nsingle > 0 && p.nsingle < cus - tail_items) {
     int64_t s = (cus - tail_items) / p.nsingle;
@@ -679,9 +1112,10 @@ SyrkPlan plan(int64_t n, int64_t k, int cus) {
     p.ssplit = (int)(s < 1 ? 1 : s);
   }
   p.stokens = ((nstages + p.ssplit - 1) / p.ssplit) * ST;
-  // Slots: first-launch items, then the singles' splits, then the tail pieces.
-  p.slots = (p.qsplit > 1 ? (size_t)p.per_range * p.qsplit : 0) + (p.ssplit > 1 ? (size_t)p.nsingle * p.ssplit : 0) +
-            (size_t)tail_items;
+  // Slots: the four-group tiles' splits, the first launch's other items, then
+  // the singles' splits, then the tail pieces.
+  p.slots = (size_t)m.pair_base + (m.qsplit > 1 ? (size_t)m.per_range * m.qsplit : 0) +
+            (p.ssplit > 1 ? (size_t)p.nsingle * p.ssplit : 0) + (size_t)tail_items;
   if (tail_items > 0) p.tail.base = (int64_t)(p.slots - tail_items);
   return p;
 }
@@ -695,8 +1129,8 @@ SyrkPlan plan(int64_t n, int64_t k, int cus) {
 size_t syrk_bf16_workspace(int64_t n, int64_t k) {
   const int cus = num_cus();
   SyrkPlan p = plan(n, k, cus);
-  size_t slots = 0;
-  if (p.qsplit > 1) slots += ((size_t)p.per_range + (size_t)pairs_per_range(p.nb2) * TSPLIT) * p.qsplit;
+  size_t slots = (size_t)p.m.pair_base;
+  if (p.m.qsplit > 1) slots += ((size_t)p.m.per_range + (size_t)pairs_per_range(p.nb2) * TSPLIT) * p.m.qsplit;
   if (p.nsingle > 0 && p.nsingle < cus) {
     const int64_t nstages = n > ST ? (n + ST - 1) / ST : 1;
     const int64_t sp = cus / p.nsingle < nstages ? cus / p.nsingle : nstages;
@@ -712,6 +1146,7 @@ hipError_t syrk_bf16(const uint16_t* X, int64_t n, int64_t k, int64_t ldx, float
   constexpr int main_stage = Tile<QUAD, QUAD>::STAGE_BYTES > Tile<HALF, QUAD>::STAGE_BYTES
                                  ? Tile<QUAD, QUAD>::STAGE_BYTES
                                  : Tile<HALF, QUAD>::STAGE_BYTES;
+  static_assert(K4_STAGE <= main_stage, "the first launch's LDS ring holds a four-group stage");
   const size_t lds_main = (size_t)NS * main_stage;
   const size_t lds_single = (size_t)NS * (Tile<HALF, QUAD>::STAGE_BYTES > Tile<HALF, HALF>::STAGE_BYTES
                                               ? Tile<HALF, QUAD>::STAGE_BYTES
@@ -720,23 +1155,35 @@ hipError_t syrk_bf16(const uint16_t* X, int64_t n, int64_t k, int64_t ldx, float
   if (!attr) {
     (void)hipFuncSetAttribute((const void*)syrk_main_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)lds_main);
+    (void)hipFuncSetAttribute((const void*)syrk_k4_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)lds_main);
     (void)hipFuncSetAttribute((const void*)syrk_single_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)lds_single);
     attr = true;
   }
+  const MainArgs& m = p.m;
   // Order: first launch, second launch (singles and tail pieces), then the
   // reductions, since a strip pair's tiles sum the tail pieces too.
-  const int items = p.per_range * p.qsplit;
-  hipLaunchKernelGGL(syrk_main_kernel, dim3(items), dim3(256), lds_main, s, X, n, k, ldx, H, partial, p.per_range,
-                     p.qsplit, p.qtokens, p.tail);
-  const size_t single_base = p.qsplit > 1 ? (size_t)p.per_range * p.qsplit : 0;
-  const int second = p.nsingle * p.ssplit + p.tail.npairs * p.qsplit * p.tail.tsplit;
+  if (m.k4)
+    hipLaunchKernelGGL(syrk_k4_kernel, dim3(K4_TILES * m.q4 + m.per_range * m.qsplit), dim3(256), lds_main, s, X, n,
+                       k, ldx, H, partial, m, p.tail);
+  else
+    hipLaunchKernelGGL(syrk_main_kernel, dim3(m.per_range * m.qsplit), dim3(256), lds_main, s, X, n, k, ldx, H,
+                       partial, m, p.tail);
+  const size_t single_base = (size_t)m.pair_base + (m.qsplit > 1 ? (size_t)m.per_range * m.qsplit : 0);
+  const int second = p.nsingle * p.ssplit + p.tail.npairs * m.qsplit * p.tail.tsplit;
   if (second > 0)
     hipLaunchKernelGGL(syrk_single_kernel, dim3(second), dim3(256), lds_single, s, X, n, k, ldx, H, partial,
-                       p.nsingle, p.ssplit, p.stokens, single_base, p.qtokens, p.tail);
-  if (p.qsplit > 1)
-    hipLaunchKernelGGL(syrk_reduce_kernel, dim3(p.per_range, 16), dim3(256), 0, s, k, H, partial, 0, p.qsplit,
-                       p.per_range, (size_t)0, p.tail);
+                       p.nsingle, p.ssplit, p.stokens, single_base, m.qtokens, p.tail);
+  if (m.k4 && m.q4 > 1)
+    hipLaunchKernelGGL(syrk_reduce_k4_kernel, dim3(K4_TILES, 24), dim3(256), 0, s, k, H, partial, 0, m.q4, 0,
+                       (size_t)0, p.tail);
+  if (m.k4 && m.qsplit > 1)
+    hipLaunchKernelGGL(syrk_reduce_k4_kernel, dim3(m.per_range, 16), dim3(256), 0, s, k, H, partial, 1, m.qsplit,
+                       m.per_range, (size_t)m.pair_base, p.tail);
+  if (!m.k4 && m.qsplit > 1)
+    hipLaunchKernelGGL(syrk_reduce_kernel, dim3(m.per_range, 16), dim3(256), 0, s, k, H, partial, 0, m.qsplit,
+                       m.per_range, (size_t)0, p.tail);
   if (p.nsingle > 0 && p.ssplit > 1)
     hipLaunchKernelGGL(syrk_reduce_kernel, dim3(p.nsingle, 4), dim3(256), 0, s, k, H, partial, 1, p.ssplit, 0,
                        single_base, p.tail);
