@@ -142,9 +142,19 @@ def summarize_pmc(fetch_csv, write_csv):
         with open(path) as fh:
             for r in csv.DictReader(fh):
                 if r["Counter_Name"] == counter:
-                    e = d.setdefault(r["Dispatch_Id"], [r["Kernel_Name"], 0.0])
+                    e = d.setdefault(int(r["Dispatch_Id"]), [r["Kernel_Name"], 0.0])
                     e[1] += float(r["Counter_Value"])
-        return list(d.values())
+        return [d[i] for i in sorted(d)]
+
+    def hessian_calls(rows):
+        # A call is a run of consecutive syrk_ dispatches (its launches and
+        # reductions); calls are separated by other kernels.
+        calls, prev = 0, False
+        for n, _ in rows:
+            cur = "syrk_" in n
+            calls += cur and not prev
+            prev = cur
+        return calls
 
     out = {"commands": ["rocprofv3 --pmc FETCH_SIZE --output-format csv -d gpurun_out/pmcf -o fetch -- "
                         "python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline",
@@ -152,14 +162,14 @@ def summarize_pmc(fetch_csv, write_csv):
                         "python3 bench.py --steps 1 --warmup 0 --no-cpu-baseline",
                         "python3 bench.py --summarize-pmc gpurun_out/pmcf/fetch_counter_collection.csv "
                         "gpurun_out/pmcw/write_counter_collection.csv"],
-           "kernel": "hessian_accumulate (first launch syrk_k4_kernel, or syrk_main_kernel when k is not 16 "
-                     "segments of 256; syrk_single_kernel; the syrk_reduce kernels)",
+           "kernel": "hessian_accumulate (at k = 4096 syrk_k4_kernel twice, then syrk_reduce_k4_kernel twice; "
+                     "otherwise syrk_main_kernel, syrk_single_kernel and syrk_reduce_kernel)",
            "workload": WORKLOAD, "source_digest": hessian_source_digest(), "unit": "bytes per call",
            "calibration_copy_bytes": CAL_COPY_BYTES}
     total = 0.0
     for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         rows = per_dispatch(path, name)
-        calls = sum(1 for n, _ in rows if "syrk_main_kernel" in n or "syrk_k4_kernel" in n)
+        calls = hessian_calls(rows)
         kib = sum(v for n, v in rows if "syrk_" in n) / max(1, calls)
         copies = [v for n, v in rows if "bitwise_not" in n]
         if not calls or not copies:

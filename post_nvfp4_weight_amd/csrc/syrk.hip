@@ -46,7 +46,6 @@ namespace {
 constexpr int ST = 32;       // tokens per stage
 constexpr int NS = 4;        // ring depth (stages in flight + the one being multiplied)
 constexpr int HEAD16 = 13;   // sixteenths of a token range a strip pair covers in the first launch
-constexpr int HEAD16_K4 = 10;   // the same beside four-group tiles
 constexpr int TSPLIT = 4;                 // tail pieces per (range, strip pair)
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -347,15 +346,27 @@ struct K4Table { uint8_t g[K4_TILES][4]; };
 constexpr uint8_t kK4Base[9][4] = {{2, 12, 20, 29}, {0, 4, 7, 10}, {3, 11, 12, 24}, {0, 21, 27, 29}, {2, 4, 17, 30},
                                    {1, 11, 21, 28}, {1, 22, 29, 30}, {3, 15, 21, 30}, {3, 10, 22, 31}};
 constexpr uint8_t kK4Fixed[2][4] = {{0, 2, 16, 18}, {1, 3, 17, 19}};
+// Order of the tiles in the launch: consecutive items go to one XCD (32 per
+// XCD, 80 per token range), so the order was chosen (by annealing) to keep
+// the groups that each XCD's run of tiles touches few: 27-28 of the 32 for
+// the runs of 32 and 20-21 for the runs of 16 (31-32 and 27-32 in orbit order).
+// Entry i is the orbit-order index (8 shifts of the nine base blocks, then 4
+// shifts of the two fixed ones) of tile i.
+constexpr uint8_t kK4Order[K4_TILES] = {
+    65, 8,  45, 61, 56, 49, 71, 38, 18, 36, 64, 11, 43, 1,  42, 74, 19, 40, 50, 79, 31, 75, 41, 52, 73, 51, 3,
+    47, 68, 21, 27, 34, 16, 33, 57, 59, 7,  26, 20, 72, 39, 30, 32, 2,  67, 17, 69, 14, 22, 10, 24, 76, 23, 63,
+    25, 37, 13, 44, 6,  15, 53, 28, 0,  9,  70, 5,  35, 12, 4,  77, 55, 48, 29, 46, 60, 78, 66, 58, 54, 62};
 constexpr K4Table make_k4_table() {
-  K4Table t{};
+  K4Table o{}, t{};
   int n = 0;
   for (int s = 0; s < 8; ++s)
     for (int b = 0; b < 9; ++b, ++n)
-      for (int q = 0; q < 4; ++q) t.g[n][q] = (uint8_t)((kK4Base[b][q] + 4 * s) % 32);
+      for (int q = 0; q < 4; ++q) o.g[n][q] = (uint8_t)((kK4Base[b][q] + 4 * s) % 32);
   for (int s = 0; s < 4; ++s)
     for (int b = 0; b < 2; ++b, ++n)
-      for (int q = 0; q < 4; ++q) t.g[n][q] = (uint8_t)(kK4Fixed[b][q] + 4 * s);
+      for (int q = 0; q < 4; ++q) o.g[n][q] = (uint8_t)(kK4Fixed[b][q] + 4 * s);
+  for (int i = 0; i < K4_TILES; ++i)
+    for (int q = 0; q < 4; ++q) t.g[i][q] = o.g[kK4Order[i]][q];
   for (int i = 0; i < K4_TILES; ++i)   // increasing group order within a tile
     for (int a = 1; a < 4; ++a)
       for (int c = a; c > 0 && t.g[i][c - 1] > t.g[i][c]; --c) {
@@ -393,20 +404,43 @@ constexpr int K4_STAGE = 4 * K4_REGION;
 static_assert(K4_STAGE == Tile<QUAD, QUAD>::STAGE_BYTES, "same LDS ring as a quad");
 
 // Wave roles.  A stage holds the tile's four groups as regions 0..3 (in
-// increasing channel order).  Each wave multiplies one whole 128x128 pair
-// block (rows region X, columns region Y) and half of another: in form A
-// (waves 0 and 1) rows X times columns 0..63 of region Z, in form B (waves 2
-// and 3) rows Z times columns 64..127 of region Y.  Blocks: wave 0 (0,1) and
-// the left half of (0,3); wave 1 (1,3) and the left half of (1,2); wave 2
-// (2,3) and the right half of (0,3); wave 3 (0,2) and the right half of
-// (1,2).  Every block has its rows before its columns, so it lies in H's
-// upper triangle.  A wave reads 10 (form A) or 12 (form B) operand fragments
-// per k-step for its 24 products.
-template <int W> struct K4Role;
-template <> struct K4Role<0> { static constexpr int X = 0, Y = 1, Z = 3, B = 0; };
-template <> struct K4Role<1> { static constexpr int X = 1, Y = 3, Z = 2, B = 0; };
-template <> struct K4Role<2> { static constexpr int X = 2, Y = 3, Z = 0, B = 1; };
-template <> struct K4Role<3> { static constexpr int X = 0, Y = 2, Z = 1, B = 1; };
+// increasing channel order).  Each wave multiplies one whole 128x128 block
+// (rows region X, columns region Y) and half of another: with HALF 0 rows X
+// times columns 0..63 of region Z, with HALF 1 rows Z times columns 64..127
+// of region Y, with HALF 2 rows Z times columns 64..127 of region Z.  FB and
+// HB number the two blocks in the tile's partial sums.
+//   Four-group tiles (blocks numbered by k4_pair): wave 0 (0,1) and the left
+//   half of (0,3); wave 1 (1,3) and the left half of (1,2); wave 2 (2,3) and
+//   the right half of (0,3); wave 3 (0,2) and the right half of (1,2).  They
+//   read 10, 10, 12 and 12 operand fragments per k-step for 24 products.
+//   Diagonal tiles (the diagonal 256-blocks of two segments: regions 0,1 are
+//   the first segment's groups, 2,3 the second's; blocks 0 (0,1), 1 (2,3),
+//   2..5 the diagonal 128-blocks of regions 0..3): wave 0 (0,1) and the left
+//   half of (0,0); wave 1 (2,3) and the left half of (2,2); wave 2 (1,1) and
+//   the right half of (0,0); wave 3 (3,3) and the right half of (2,2).  They
+//   read 8 fragments per k-step; a quarter of their products (those below
+//   the diagonal blocks' diagonals) are not needed.
+// Every block has its rows at or before its columns, so it lies in H's upper
+// triangle.
+template <int W_, int X_, int Y_, int Z_, int HALF_, int FB_, int HB_>
+struct Role {
+  static constexpr int W = W_, X = X_, Y = Y_, Z = Z_, HALF = HALF_, FB = FB_, HB = HB_;
+  static constexpr bool YX = X_ == Y_;                 // the whole block is diagonal: Y's fragments are X's
+  static constexpr bool ZX = HALF_ == 0 && Z_ == X_;   // the half block is diagonal: Z's fragments are X's
+  static constexpr int NY = YX ? 0 : 4, NZ = ZX ? 0 : (HALF_ == 0 ? 2 : 4), NF = 4 + NY + NZ;
+  static constexpr int HR = HALF_ == 0 ? X_ : Z_, HC = HALF_ == 1 ? Y_ : Z_, HC0 = HALF_ == 0 ? 0 : 64;
+};
+using K4W0 = Role<0, 0, 1, 3, 0, 0, 2>;
+using K4W1 = Role<1, 1, 3, 2, 0, 4, 3>;
+using K4W2 = Role<2, 2, 3, 0, 1, 5, 2>;
+using K4W3 = Role<3, 0, 2, 1, 1, 1, 3>;
+using DGW0 = Role<0, 0, 1, 0, 0, 0, 2>;
+using DGW1 = Role<1, 2, 3, 2, 0, 1, 4>;
+using DGW2 = Role<2, 1, 1, 0, 2, 3, 2>;
+using DGW3 = Role<3, 3, 3, 2, 2, 5, 4>;
+// Rows and columns region of block b of a diagonal tile.
+__host__ __device__ constexpr int dg_row(int b) { return b == 0 ? 0 : (b == 1 ? 2 : b - 2); }
+__host__ __device__ constexpr int dg_col(int b) { return b == 0 ? 1 : (b == 1 ? 3 : b - 2); }
 
 // Region layout: [32 token rows][128 channels], 16-byte chunk p of row r
 // stored at chunk p ^ 4 (r % 4).  A transposed fragment read (16 lanes: rows
@@ -414,7 +448,6 @@ template <> struct K4Role<3> { static constexpr int X = 0, Y = 2, Z = 1, B = 1; 
 // 32 lanes, and since r % 4 is fixed per lane (T is a multiple of 4) a lane's
 // address for fragment f is its own base for f plus immediates for the
 // region, the half and the k-step.
-template <int W>
 __device__ __forceinline__ bf16x8 k4_frag(const char* buf, const int (&F)[4], int region, int f, int kk) {
   const char* p = buf + F[f] + region * K4_REGION + kk * 16 * K4_ROWB;
   s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)p);
@@ -422,19 +455,20 @@ __device__ __forceinline__ bf16x8 k4_frag(const char* buf, const int (&F)[4], in
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-template <int W>
+template <class R>
 struct K4Frags {
-  static constexpr int NZ = K4Role<W>::B ? 4 : 2;
-  bf16x8 x[4], y[4], z[NZ];
+  bf16x8 x[4], y[R::NY > 0 ? R::NY : 1], z[R::NZ > 0 ? R::NZ : 1];
+  __device__ __forceinline__ const bf16x8& yf(int j) const { if constexpr (R::YX) return x[j]; else return y[j]; }
+  __device__ __forceinline__ const bf16x8& zf(int j) const { if constexpr (R::ZX) return x[j]; else return z[j]; }
 };
 
-// Fragment m of k-step kk: m < 4 region X, m < 8 region Y, then region Z.
-template <int W>
-__device__ __forceinline__ void k4_read(const char* buf, const int (&F)[4], int m, int kk, K4Frags<W>& fr) {
-  using R = K4Role<W>;
-  if (m < 4) fr.x[m] = k4_frag<W>(buf, F, R::X, m, kk);
-  else if (m < 8) fr.y[m - 4] = k4_frag<W>(buf, F, R::Y, m - 4, kk);
-  else fr.z[m - 8] = k4_frag<W>(buf, F, R::Z, m - 8, kk);
+// Fragment m of k-step kk: m < 4 region X, then region Y (unless it is X),
+// then region Z (unless it is X).
+template <class R>
+__device__ __forceinline__ void k4_read(const char* buf, const int (&F)[4], int m, int kk, K4Frags<R>& fr) {
+  if (m < 4) fr.x[m] = k4_frag(buf, F, R::X, m, kk);
+  else if (m < 4 + R::NY) fr.y[m - 4] = k4_frag(buf, F, R::Y, m - 4, kk);
+  else fr.z[m - 4 - R::NY] = k4_frag(buf, F, R::Z, m - 4 - R::NY, kk);
 }
 
 // The half block's eight accumulators (128 registers) live in VGPRs, the
@@ -451,18 +485,22 @@ __device__ __forceinline__ void k4_mfma_fence(f32x16 (&accH)[4][2]) {
                  "+v"(accH[2][1]), "+v"(accH[3][0]), "+v"(accH[3][1]));
 }
 
+__device__ __forceinline__ void k4_mfma_v(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+
 // Product m: m < 16 the whole block's tile (m / 4, m % 4), then the half
 // block's tile ((m - 16) / 2, (m - 16) % 2).
-template <int W>
-__device__ __forceinline__ void k4_mfma(int m, const K4Frags<W>& fr, f32x16 (&accF)[4][4], f32x16 (&accH)[4][2]) {
+template <class R>
+__device__ __forceinline__ void k4_mfma(int m, const K4Frags<R>& fr, f32x16 (&accF)[4][4], f32x16 (&accH)[4][2]) {
   if (m < 16) {
-    accF[m / 4][m % 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.x[m / 4], fr.y[m % 4], accF[m / 4][m % 4], 0, 0, 0);
+    accF[m / 4][m % 4] =
+        __builtin_amdgcn_mfma_f32_32x32x16_bf16(fr.x[m / 4], fr.yf(m % 4), accF[m / 4][m % 4], 0, 0, 0);
   } else {
     const int q = m - 16;
-    if constexpr (K4Role<W>::B)
-      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(accH[q / 2][q % 2]) : "v"(fr.z[q / 2]), "v"(fr.y[2 + q % 2]));
-    else
-      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(accH[q / 2][q % 2]) : "v"(fr.x[q / 2]), "v"(fr.z[q % 2]));
+    if constexpr (R::HALF == 0) k4_mfma_v(accH[q / 2][q % 2], fr.x[q / 2], fr.zf(q % 2));
+    else if constexpr (R::HALF == 1) k4_mfma_v(accH[q / 2][q % 2], fr.z[q / 2], fr.yf(2 + q % 2));
+    else k4_mfma_v(accH[q / 2][q % 2], fr.z[q / 2], fr.z[2 + q % 2]);
   }
 }
 
@@ -499,17 +537,19 @@ __device__ __forceinline__ void k4_loads(char* slot, const uint16_t* src, int nr
   }
 }
 
-// One 32x32 accumulator tile at rows r0, columns c0 of pair block `pair`
-// (rows from channel rch, columns from cch): into H (add, and the mirror) or
-// into the tile's partial sums P [pair][128][128].
-__device__ __forceinline__ void k4_store(const f32x16& acc, int pair, int r0, int c0, int64_t rch, int64_t cch,
+// One 32x32 accumulator tile at rows r0, columns c0 of block `blk` (rows
+// from channel rch, columns from cch): into the tile's partial sums P
+// [block][128][128], or added into H.  Off a diagonal block (rch < cch) every
+// element and its mirror are written; on one (rch == cch) the upper triangle
+// and the mirror of the strict upper triangle.
+__device__ __forceinline__ void k4_store(const f32x16& acc, int blk, int r0, int c0, int64_t rch, int64_t cch,
                                          int64_t k, float* __restrict__ H, float* __restrict__ P) {
   const int lane = threadIdx.x & 63, col = c0 + (lane & 31);
   if (P) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = r0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      P[(size_t)pair * K4G * K4G + row * K4G + col] = acc[r];
+      P[(size_t)blk * K4G * K4G + row * K4G + col] = acc[r];
     }
     return;
   }
@@ -518,15 +558,15 @@ __device__ __forceinline__ void k4_store(const f32x16& acc, int pair, int r0, in
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int64_t gi = rch + r0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-    old[r] = (gi < k && gj < k) ? H[gi * k + gj] : 0.0f;
+    old[r] = (gi < k && gj < k && gi <= gj) ? H[gi * k + gj] : 0.0f;
   }
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int64_t gi = rch + r0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-    if (gi < k && gj < k) {   // gi < gj: the groups differ and are in increasing order
+    if (gi < k && gj < k && gi <= gj) {
       const float v = old[r] + acc[r];
       H[gi * k + gj] = v;
-      H[gj * k + gi] = v;
+      if (gi != gj) H[gj * k + gi] = v;
     }
   }
 }
@@ -537,19 +577,19 @@ __device__ __forceinline__ void k4_store(const f32x16& acc, int pair, int r0, in
 // k-step's products interleaved with the refill of `slot` and the next
 // stage's first fragments.  `slot` and `nxt` are distinct, which the restrict
 // qualifiers state, so operand reads need not wait on the loads in flight.
-template <int W, bool has_next>
+template <class R, bool has_next>
 __device__ __forceinline__ void k4_step(char* __restrict__ slot, const char* __restrict__ nxt, const uint16_t* src,
                                         int nrec, const int64_t (&ch)[4], const uint32_t (&voff)[2],
-                                        const int (&F)[4], K4Frags<W>& f0, f32x16 (&accF)[4][4],
+                                        const int (&F)[4], K4Frags<R>& f0, f32x16 (&accF)[4][4],
                                         f32x16 (&accH)[4][2]) {
-  constexpr int NF = 8 + K4Frags<W>::NZ, NM = 24, NL = 8;
+  constexpr int NM = 24, NL = 8;
   constexpr int kWait = (NS - 2) * NL;
   static_assert(NS >= 2 && kWait < 64, "ring depth");
-  K4Frags<W> f1;
+  K4Frags<R> f1;
 #pragma unroll
   for (int m = 0; m < NM; ++m) {
-    if (m < NF) k4_read<W>(slot, F, m, 1, f1);
-    k4_mfma<W>(m, f0, accF, accH);
+    if (m < R::NF) k4_read<R>(slot, F, m, 1, f1);
+    k4_mfma<R>(m, f0, accF, accH);
     __builtin_amdgcn_sched_barrier(0);
   }
   if constexpr (has_next) {
@@ -560,20 +600,19 @@ __device__ __forceinline__ void k4_step(char* __restrict__ slot, const char* __r
 #pragma unroll
   for (int m = 0; m < NM; ++m) {
     if constexpr (has_next) {
-      if (m < NL) k4_loads<W>(slot, src, nrec, ch, voff, m);
-      if (m < NF) k4_read<W>(nxt, F, m, 0, f0);
+      if (m < NL) k4_loads<R::W>(slot, src, nrec, ch, voff, m);
+      if (m < R::NF) k4_read<R>(nxt, F, m, 0, f0);
     }
-    k4_mfma<W>(m, f1, accF, accH);
+    k4_mfma<R>(m, f1, accF, accH);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-template <int W>
+template <class R>
 __device__ __forceinline__ void k4_wave(char* lds, const uint16_t* __restrict__ X, int64_t k, int64_t ldx,
                                         const int64_t (&ch)[4], int64_t t_begin, int64_t t_end,
                                         float* __restrict__ H, float* __restrict__ P) {
-  using R = K4Role<W>;
-  constexpr int NF = 8 + K4Frags<W>::NZ, NL = 8;
+  constexpr int NL = 8;
   const int nstages = t_end > t_begin ? (int)((t_end - t_begin + ST - 1) / ST) : 0;
   const int lane = threadIdx.x & 63, g = lane >> 4, j = lane & 15, s4 = j >> 2;
   int F[4];
@@ -582,7 +621,7 @@ __device__ __forceinline__ void k4_wave(char* lds, const uint16_t* __restrict__ 
   uint32_t voff[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h)
-    voff[h] = (uint32_t)((4 * (W + 4 * h) + (lane >> 4)) * ldx * 2 + 16 * ((lane & 15) ^ (4 * (lane >> 4))));
+    voff[h] = (uint32_t)((4 * (R::W + 4 * h) + (lane >> 4)) * ldx * 2 + 16 * ((lane & 15) ^ (4 * (lane >> 4))));
   auto stage_nrec = [&](int st) -> int {
     return st < nstages ? (int)min((t_end - t_begin - (int64_t)st * ST) * ldx * 2, (int64_t)0x7FFFFFF0) : 0;
   };
@@ -605,55 +644,59 @@ __device__ __forceinline__ void k4_wave(char* lds, const uint16_t* __restrict__ 
   // stage 0's first fragments.
   for (int s = 0; s < NS; ++s)
 #pragma unroll
-    for (int m = 0; m < NL; ++m) k4_loads<W>(lds + s * K4_STAGE, stage_src(s), stage_nrec(s), ch, voff, m);
-  K4Frags<W> f0;
+    for (int m = 0; m < NL; ++m) k4_loads<R::W>(lds + s * K4_STAGE, stage_src(s), stage_nrec(s), ch, voff, m);
+  K4Frags<R> f0;
   __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
   asm volatile("s_barrier" ::: "memory");
 #pragma unroll
-  for (int m = 0; m < NF; ++m) k4_read<W>(lds, F, m, 0, f0);
+  for (int m = 0; m < R::NF; ++m) k4_read<R>(lds, F, m, 0, f0);
   k4_mfma_fence(accH);
   for (int s = 0; s + 1 < nstages; ++s)
-    k4_step<W, true>(lds + (s % NS) * K4_STAGE, lds + ((s + 1) % NS) * K4_STAGE, stage_src(s + NS),
+    k4_step<R, true>(lds + (s % NS) * K4_STAGE, lds + ((s + 1) % NS) * K4_STAGE, stage_src(s + NS),
                      stage_nrec(s + NS), ch, voff, F, f0, accF, accH);
   if (nstages > 0) {
     const int s = nstages - 1;
-    k4_step<W, false>(lds + (s % NS) * K4_STAGE, lds, stage_src(s), 0, ch, voff, F, f0, accF, accH);
+    k4_step<R, false>(lds + (s % NS) * K4_STAGE, lds, stage_src(s), 0, ch, voff, F, f0, accF, accH);
   }
   __builtin_amdgcn_s_waitcnt(0);   // the zero-length loads past the end write LDS too
   k4_mfma_fence(accH);
 
-  const int pF = k4_pair(R::X, R::Y);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) k4_store(accF[i][c], pF, 32 * i, 32 * c, ch[R::X], ch[R::Y], k, H, P);
-  if constexpr (R::B) {
-    const int pH = k4_pair(R::Z, R::Y);
+    for (int c = 0; c < 4; ++c) k4_store(accF[i][c], R::FB, 32 * i, 32 * c, ch[R::X], ch[R::Y], k, H, P);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int c = 0; c < 2; ++c) k4_store(accH[i][c], pH, 32 * i, 64 + 32 * c, ch[R::Z], ch[R::Y], k, H, P);
-  } else {
-    const int pH = k4_pair(R::X, R::Z);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int c = 0; c < 2; ++c) k4_store(accH[i][c], pH, 32 * i, 32 * c, ch[R::X], ch[R::Z], k, H, P);
-  }
+    for (int c = 0; c < 2; ++c)
+      k4_store(accH[i][c], R::HB, 32 * i, R::HC0 + 32 * c, ch[R::HR], ch[R::HC], k, H, P);
 }
 
-// Tile t of the table over tokens [t_begin, t_end): into H, or into its
-// partial sums P (kK4SlotFloats).
+// Tile t over tokens [t_begin, t_end), into H or into its partial sums P
+// (kK4SlotFloats): t < K4_TILES a four-group tile of the table, otherwise
+// diagonal tile t - K4_TILES (segments 2d and 2d + 1, groups 4d .. 4d + 3).
 __device__ __forceinline__ void k4_job(char* lds, const uint16_t* __restrict__ X, int64_t k, int64_t ldx, int t,
                                        int64_t t_begin, int64_t t_end, float* __restrict__ H, float* __restrict__ P) {
   int64_t ch[4];
+  const int wave = threadIdx.x >> 6;
+  if (t < K4_TILES) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q) ch[q] = (int64_t)kK4.g[t][q] * K4G;
-  switch (threadIdx.x >> 6) {
-    case 0: k4_wave<0>(lds, X, k, ldx, ch, t_begin, t_end, H, P); break;
-    case 1: k4_wave<1>(lds, X, k, ldx, ch, t_begin, t_end, H, P); break;
-    case 2: k4_wave<2>(lds, X, k, ldx, ch, t_begin, t_end, H, P); break;
-    default: k4_wave<3>(lds, X, k, ldx, ch, t_begin, t_end, H, P); break;
+    for (int q = 0; q < 4; ++q) ch[q] = (int64_t)kK4.g[t][q] * K4G;
+    switch (wave) {
+      case 0: k4_wave<K4W0>(lds, X, k, ldx, ch, t_begin, t_end, H, P); break;
+      case 1: k4_wave<K4W1>(lds, X, k, ldx, ch, t_begin, t_end, H, P); break;
+      case 2: k4_wave<K4W2>(lds, X, k, ldx, ch, t_begin, t_end, H, P); break;
+      default: k4_wave<K4W3>(lds, X, k, ldx, ch, t_begin, t_end, H, P); break;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ch[q] = (int64_t)(4 * (t - K4_TILES) + q) * K4G;
+    switch (wave) {
+      case 0: k4_wave<DGW0>(lds, X, k, ldx, ch, t_begin, t_end, H, P); break;
+      case 1: k4_wave<DGW1>(lds, X, k, ldx, ch, t_begin, t_end, H, P); break;
+      case 2: k4_wave<DGW2>(lds, X, k, ldx, ch, t_begin, t_end, H, P); break;
+      default: k4_wave<DGW3>(lds, X, k, ldx, ch, t_begin, t_end, H, P); break;
+    }
   }
 }
 
@@ -752,41 +795,15 @@ __device__ __forceinline__ int xcd_logical(int id, int G) {
   return (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + i;
 }
 
-// First-launch parameters.  Without four-group tiles: qsplit * per_range
-// items; logical item L covers token range L / per_range and item L %
-// per_range of the order above (a strip pair only the head of the range when
-// there are tail pieces), and with qsplit > 1 writes its partial sums to slot
-// L (a strip pair's two 128x256 strips fill the two halves of the slot).  With
-// them (k4 = 1): first the K4_TILES * q4 tiles (tile L % K4_TILES over token
-// range L / K4_TILES of q4, partial sums at L * kK4SlotFloats when q4 > 1),
-// then qsplit * per_range strip pairs (per_range = the pairs; pair p of range
-// sp is item sp * per_range + p, partial slot pair_base + that).
+// First-launch parameters of the quads: qsplit * per_range items; logical
+// item L covers token range L / per_range and item L % per_range of the order
+// above (a strip pair only the head of the range when there are tail
+// pieces), and with qsplit > 1 writes its partial sums to slot L (a strip
+// pair's two 128x256 strips fill the two halves of the slot).
 struct MainArgs {
   int per_range, qsplit;
   int64_t qtokens;
-  int k4, q4;
-  int64_t k4tokens, pair_base;
 };
-
-__device__ __forceinline__ void strip_pair_job(char* lds, const uint16_t* __restrict__ X, int64_t k, int64_t ldx,
-                                               int a, int b, int64_t t0, int64_t te, float* __restrict__ H,
-                                               float* __restrict__ P) {
-  tile_job<HALF, QUAD, true>(lds, X, k, ldx, (int64_t)a * QUAD, (int64_t)a * QUAD, t0, te, H, P);
-  if (b >= 0) {
-    __syncthreads();   // the LDS ring is reused
-    tile_job<HALF, QUAD, true>(lds, X, k, ldx, (int64_t)b * QUAD, (int64_t)b * QUAD, t0, te, H,
-                               P ? P + HALF * QUAD : nullptr);
-  }
-}
-
-// The strip pair of item L (its range and its pair), as the first launch runs it.
-__device__ __forceinline__ void first_launch_pair(char* lds, const uint16_t* __restrict__ X, int64_t n, int64_t k,
-                                                  int64_t ldx, float* __restrict__ H, float* __restrict__ partial,
-                                                  const MainArgs& m, const TailArgs& tail, int L, int a, int b) {
-  const int64_t t0 = (int64_t)(L / m.per_range) * m.qtokens, t1 = min(n, t0 + m.qtokens);
-  const int64_t te = tail.npairs > 0 ? min(t1, t0 + tail.head) : t1;   // the rest is tail work
-  strip_pair_job(lds, X, k, ldx, a, b, t0, te, H, m.qsplit > 1 ? partial + ((size_t)m.pair_base + L) * kSlotFloats : nullptr);
-}
 
 __global__ __launch_bounds__(256) void syrk_main_kernel(const uint16_t* __restrict__ X, int64_t n, int64_t k,
                                                         int64_t ldx, float* __restrict__ H,
@@ -796,32 +813,70 @@ __global__ __launch_bounds__(256) void syrk_main_kernel(const uint16_t* __restri
   const int L = xcd_logical(blockIdx.x, gridDim.x);
   int kind, a, b;
   item_coords(L % m.per_range, nb2, kind, a, b);
+  const int64_t t0 = (int64_t)(L / m.per_range) * m.qtokens, t1 = min(n, t0 + m.qtokens);
+  float* P = m.qsplit > 1 ? partial + (size_t)L * kSlotFloats : nullptr;
   if (kind == 0) {
-    const int64_t t0 = (int64_t)(L / m.per_range) * m.qtokens, t1 = min(n, t0 + m.qtokens);
-    tile_job<QUAD, QUAD, false>(lds, X, k, ldx, (int64_t)a * QUAD, (int64_t)b * QUAD, t0, t1, H,
-                                m.qsplit > 1 ? partial + (size_t)L * kSlotFloats : nullptr);
+    tile_job<QUAD, QUAD, false>(lds, X, k, ldx, (int64_t)a * QUAD, (int64_t)b * QUAD, t0, t1, H, P);
   } else if (kind == 1) {
-    first_launch_pair(lds, X, n, k, ldx, H, partial, m, tail, L, a, b);
+    const int64_t te = tail.npairs > 0 ? min(t1, t0 + tail.head) : t1;   // the rest is tail work
+    tile_job<HALF, QUAD, true>(lds, X, k, ldx, (int64_t)a * QUAD, (int64_t)a * QUAD, t0, te, H, P);
+    if (b >= 0) {
+      __syncthreads();   // the LDS ring is reused
+      tile_job<HALF, QUAD, true>(lds, X, k, ldx, (int64_t)b * QUAD, (int64_t)b * QUAD, t0, te, H,
+                                 P ? P + HALF * QUAD : nullptr);
+    }
   }
 }
 
-// The first launch with four-group tiles: K4_TILES * q4 tiles, then the
-// strip pairs.
+// Four-group and diagonal tiles (16 segments).  First launch: K4_TILES * q4
+// four-group tiles (tile L % K4_TILES over token range L / K4_TILES of
+// k4tokens), then K4_DTILES * qd diagonal tiles (tile d of range sp is item
+// sp * K4_DTILES + d over the first `head` tokens of its range of dtokens,
+// all of it without tail pieces).  Second launch: the diagonal tiles' tail
+// pieces, ts per (range, tile) of ttokens each, item u = (sp * K4_DTILES + d)
+// * ts + piece.  A diagonal tile costs what a four-group tile does, so with
+// head = k4tokens both kinds of first-launch item take the same time.
+// Partial sums (kK4SlotFloats each) at slot L for the four-group tiles,
+// dbase + that item for the diagonal heads, tbase + u for the tail pieces;
+// with direct = 1 (one token range for every tile, no tails) each tile adds
+// into H itself.
+constexpr int K4_DTILES = K4_SEGS / 2;
+constexpr int K4_TSPLIT = 16;
+struct K4Args {
+  int q4, qd, ts, direct;
+  int64_t k4tokens, dtokens, head, ttokens, dbase, tbase;
+};
+
 __global__ __launch_bounds__(256) void syrk_k4_kernel(const uint16_t* __restrict__ X, int64_t n, int64_t k,
                                                       int64_t ldx, float* __restrict__ H,
-                                                      float* __restrict__ partial, MainArgs m, TailArgs tail) {
+                                                      float* __restrict__ partial, K4Args a, int tails) {
   extern __shared__ __attribute__((aligned(1024))) char lds[];
-  const int nb2 = (int)((k + QUAD - 1) / QUAD);
   const int L = xcd_logical(blockIdx.x, gridDim.x);
-  const int nk = K4_TILES * m.q4;
-  if (L < nk) {
-    const int64_t t0 = (int64_t)(L / K4_TILES) * m.k4tokens, t1 = min(n, t0 + m.k4tokens);
-    k4_job(lds, X, k, ldx, L % K4_TILES, t0, t1, H, m.q4 > 1 ? partial + (size_t)L * kK4SlotFloats : nullptr);
-    return;
+  const int nk = K4_TILES * a.q4;
+  int t;
+  int64_t t0, t1;
+  size_t slot;
+  if (tails) {
+    const int sp = L / (K4_DTILES * a.ts), piece = L % a.ts;
+    const int64_t r0 = (int64_t)sp * a.dtokens, r1 = min(n, r0 + a.dtokens);
+    t = K4_TILES + (L / a.ts) % K4_DTILES;
+    t0 = min(r1, r0 + a.head + (int64_t)piece * a.ttokens);
+    t1 = min(r1, t0 + a.ttokens);
+    slot = (size_t)a.tbase + L;
+  } else if (L < nk) {
+    t = L % K4_TILES;
+    t0 = (int64_t)(L / K4_TILES) * a.k4tokens;
+    t1 = min(n, t0 + a.k4tokens);
+    slot = L;
+  } else {
+    const int e = L - nk;
+    t = K4_TILES + e % K4_DTILES;
+    t0 = (int64_t)(e / K4_DTILES) * a.dtokens;
+    t1 = min(n, t0 + a.dtokens);
+    if (a.ts > 0) t1 = min(t1, t0 + a.head);
+    slot = (size_t)a.dbase + e;
   }
-  int kind, a, b;
-  item_coords(pair_item((L - nk) % m.per_range, nb2), nb2, kind, a, b);
-  first_launch_pair(lds, X, n, k, ldx, H, partial, m, tail, L - nk, a, b);
+  k4_job(lds, X, k, ldx, t, t0, t1, H, a.direct ? nullptr : partial + slot * kK4SlotFloats);
 }
 
 // Launch 2: singles (bottom-right diagonal 128-block of 256-block a), split
@@ -852,7 +907,12 @@ __global__ __launch_bounds__(256) void syrk_single_kernel(const uint16_t* __rest
   const int64_t r1 = min(n, (int64_t)sp * qtokens + qtokens);
   const int64_t ts = min(r1, (int64_t)sp * qtokens + tail.head + (int64_t)t * tail.ttokens);
   const int64_t te = min(r1, ts + tail.ttokens);
-  strip_pair_job(lds, X, k, ldx, a, b, ts, te, H, partial + ((size_t)tail.base + u) * kSlotFloats);
+  float* P = partial + ((size_t)tail.base + u) * kSlotFloats;
+  tile_job<HALF, QUAD, true>(lds, X, k, ldx, (int64_t)a * QUAD, (int64_t)a * QUAD, ts, te, H, P);
+  if (b >= 0) {
+    __syncthreads();   // the LDS ring is reused
+    tile_job<HALF, QUAD, true>(lds, X, k, ldx, (int64_t)b * QUAD, (int64_t)b * QUAD, ts, te, H, P + HALF * QUAD);
+  }
 }
 
 // Sum the token splits of one 64x64 piece of a tile in split order, add the
@@ -984,40 +1044,29 @@ __global__ __launch_bounds__(256) void syrk_reduce_kernel(int64_t k, float* __re
   }
 }
 
-// With four-group tiles.  kind 0: blockIdx.x is tile t, whose split sp sits
-// at (sp * K4_TILES + t) * kK4SlotFloats; blockIdx.y (0..23) is a 64x64 piece
-// of its six 128x128 pair blocks (2x2 each).  kind 1: blockIdx.x is strip
-// pair p, whose split sp sits in slot slot_base + sp * per_range + p (then
-// its tail pieces); blockIdx.y (0..15) is a piece of its two 2x4.
+// Four-group and diagonal tiles.  kind 0: blockIdx.x is four-group tile t,
+// whose range sp sits at slot sp * K4_TILES + t; kind 1: blockIdx.x is
+// diagonal tile d, whose range sp sits at slot dbase + sp * K4_DTILES + d,
+// followed by its tail pieces (slot tbase + (sp * K4_DTILES + d) * ts +
+// piece), summed by range and piece.  blockIdx.y (0..23) is a 64x64 piece of
+// the tile's six 128x128 blocks (2x2 each); pieces wholly below a diagonal
+// block's diagonal are skipped.
 __global__ __launch_bounds__(256) void syrk_reduce_k4_kernel(int64_t k, float* __restrict__ H,
-                                                             const float* __restrict__ partial, int kind, int nsplit,
-                                                             int per_range, size_t slot_base, TailArgs tail) {
-  const int y = blockIdx.y;
+                                                             const float* __restrict__ partial, int kind,
+                                                             K4Args a) {
+  const int t = blockIdx.x, y = blockIdx.y, b = y / 4, pr = (y % 4) / 2, pc = y % 2;
+  const size_t off = (size_t)b * K4G * K4G + pr * PIECE * K4G + pc * PIECE;
   if (kind == 0) {
-    const int t = blockIdx.x, pair = y / 4, pr = (y % 4) / 2, pc = y % 2;
-    const int ra = pair < 3 ? 0 : (pair < 5 ? 1 : 2), rb = pair < 3 ? pair + 1 : (pair < 5 ? pair - 1 : 3);
-    const float* P = partial + (size_t)t * kK4SlotFloats + (size_t)pair * K4G * K4G + pr * PIECE * K4G + pc * PIECE;
-    reduce_piece(k, H, P, (size_t)K4_TILES * kK4SlotFloats, nsplit, K4G,
+    const int ra = b < 3 ? 0 : (b < 5 ? 1 : 2), rb = b < 3 ? b + 1 : (b < 5 ? b - 1 : 3);
+    reduce_piece(k, H, partial + (size_t)t * kK4SlotFloats + off, (size_t)K4_TILES * kK4SlotFloats, a.q4, K4G,
                  (int64_t)kK4.g[t][ra] * K4G + pr * PIECE, (int64_t)kK4.g[t][rb] * K4G + pc * PIECE);
     return;
   }
-  const int nb2 = (int)((k + QUAD - 1) / QUAD);
-  const int p = blockIdx.x;
-  int ik, a, b;
-  item_coords(pair_item(p, nb2), nb2, ik, a, b);
-  const int d = y < 8 ? a : b;
-  if (d < 0) return;
-  const int pr = (y & 7) / 4, pc = y % 4;
-  const size_t off = (y < 8 ? 0 : (size_t)HALF * QUAD) + (size_t)pr * PIECE * QUAD + pc * PIECE;
-  const float* P2 = nullptr;
-  int n2 = 0;
-  if (tail.npairs > 0) {   // then the pair's tail pieces, by range and piece
-    P2 = partial + ((size_t)tail.base + (size_t)p * tail.tsplit) * kSlotFloats + off;
-    n2 = nsplit * tail.tsplit;
-  }
-  reduce_piece(k, H, partial + (slot_base + p) * kSlotFloats + off, (size_t)per_range * kSlotFloats, nsplit, QUAD,
-               (int64_t)d * QUAD + pr * PIECE, (int64_t)d * QUAD + pc * PIECE, P2, n2, tail.tsplit,
-               (size_t)tail.npairs * tail.tsplit * kSlotFloats, kSlotFloats);
+  const float* P2 = a.ts > 0 ? partial + ((size_t)a.tbase + (size_t)t * a.ts) * kK4SlotFloats + off : nullptr;
+  reduce_piece(k, H, partial + ((size_t)a.dbase + t) * kK4SlotFloats + off, (size_t)K4_DTILES * kK4SlotFloats,
+               a.qd, K4G, (int64_t)(4 * t + dg_row(b)) * K4G + pr * PIECE,
+               (int64_t)(4 * t + dg_col(b)) * K4G + pc * PIECE, P2, a.qd * a.ts, a.ts > 0 ? a.ts : 1,
+               (size_t)K4_DTILES * a.ts * kK4SlotFloats, kK4SlotFloats);
 }
 
 __global__ void symmetrize_kernel(float* H, int64_t k) {
@@ -1026,8 +1075,9 @@ __global__ void symmetrize_kernel(float* H, int64_t k) {
 }
 
 struct SyrkPlan {
-  int nb2, nsingle, ssplit;
-  MainArgs m;        // per_range, qsplit, qtokens: the first launch's quads and strip pairs (or pairs alone)
+  int nb2, k4, nsingle, ssplit;
+  MainArgs m;        // quads and strip pairs (k4 = 0)
+  K4Args a;          // four-group and diagonal tiles (k4 = 1)
   int64_t stokens;
   TailArgs tail;
   size_t slots;      // partial slots of kSlotFloats
@@ -1044,61 +1094,73 @@ int num_cus() {
   return cus;
 }
 
-// Token ranges of the four-group tiles: as many as give every tile range a CU
-// of its own.  The strip pairs split over the CUs left (at least one range).
-// Both counts grow with n up to their caps, never down.
-int k4_ranges(int64_t nstages, int cus) {
-  int64_t s = cus / K4_TILES;
-  if (s > nstages) s = nstages;
-  return s < 1 ? 1 : (int)s;
+// Four-group and diagonal tiles: as many token ranges of the four-group
+// tiles as give each (tile, range) a CU; the diagonal tiles split over the
+// CUs left (at least one range), their heads as long as a four-group item
+// and the rest of each range in K4_TSPLIT tail pieces.  The range counts
+// grow with n up to their caps and never shrink.
+K4Args k4_plan(int64_t nstages, int cus) {
+  K4Args a{};
+  int64_t q4 = cus / K4_TILES;
+  a.q4 = (int)(q4 > nstages ? nstages : (q4 < 1 ? 1 : q4));
+  int64_t qd = (cus - (int64_t)K4_TILES * (cus / K4_TILES)) / K4_DTILES;
+  a.qd = (int)(qd > nstages ? nstages : (qd < 1 ? 1 : qd));
+  a.k4tokens = ((nstages + a.q4 - 1) / a.q4) * ST;
+  a.dtokens = ((nstages + a.qd - 1) / a.qd) * ST;
+  a.head = a.k4tokens < a.dtokens ? a.k4tokens : a.dtokens;
+  a.ts = 0;
+  a.ttokens = 0;
+  if (a.head < a.dtokens) {
+    a.ts = K4_TSPLIT;
+    const int64_t per = (a.dtokens - a.head + a.ts - 1) / a.ts;
+    a.ttokens = (per + ST - 1) / ST * ST;
+  }
+  a.direct = a.q4 == 1 && a.qd == 1 && a.ts == 0;
+  a.dbase = (int64_t)K4_TILES * a.q4;
+  a.tbase = a.dbase + (int64_t)K4_DTILES * a.qd;
+  return a;
 }
-int k4_pair_ranges(int64_t nstages, int cus, int npairs) {
-  int64_t s = (cus - (int64_t)K4_TILES * (cus / K4_TILES)) / npairs;
-  if (s > nstages) s = nstages;
-  return s < 1 ? 1 : (int)s;
+// Partial slots (of kSlotFloats) the four-group plan uses: every tile range,
+// diagonal head and tail piece (the tails at their cap, so that the count
+// never shrinks as n grows).
+size_t k4_slots(const K4Args& a) {
+  if (a.direct) return 0;
+  const size_t k4s = (size_t)a.tbase + (size_t)K4_DTILES * a.qd * K4_TSPLIT;
+  return (k4s * kK4SlotFloats + kSlotFloats - 1) / kSlotFloats;
 }
 
 SyrkPlan plan(int64_t n, int64_t k, int cus) {
-  SyrkPlan p;
+  SyrkPlan p{};
   p.nb2 = (int)((k + QUAD - 1) / QUAD);
+  int64_t nstages = (n + ST - 1) / ST;
+  if (nstages < 1) nstages = 1;
+  p.k4 = p.nb2 == K4_SEGS;
+  if (p.k4) {
+    p.a = k4_plan(nstages, cus);
+    p.slots = k4_slots(p.a);
+    return p;
+  }
   p.nsingle = 0;
   for (int a = 0; a < p.nb2; ++a)
     if ((int64_t)a * QUAD + HALF < k) ++p.nsingle;
-  int64_t nstages = (n + ST - 1) / ST;
-  if (nstages < 1) nstages = 1;
   MainArgs& m = p.m;
-  m.k4 = p.nb2 == K4_SEGS;
-  m.q4 = 0;
-  m.k4tokens = 0;
-  m.pair_base = 0;
-  int head16 = HEAD16;
-  if (m.k4) {
-    // Four-group tiles for the quads, then the strip pairs alone.
-    m.q4 = k4_ranges(nstages, cus);
-    m.k4tokens = ((nstages + m.q4 - 1) / m.q4) * ST;
-    m.per_range = pairs_per_range(p.nb2);
-    m.qsplit = k4_pair_ranges(nstages, cus, m.per_range);
-    m.pair_base = m.q4 > 1 ? (int64_t)((K4_TILES * m.q4 * kK4SlotFloats + kSlotFloats - 1) / kSlotFloats) : 0;
-    head16 = HEAD16_K4;
-  } else {
-    // Split the first launch's items over token ranges while they would not
-    // give every CU an item.
-    m.per_range = items_per_range(p.nb2);
-    m.qsplit = 1;
-    if (m.per_range < cus) {
-      int64_t s = (cus + m.per_range - 1) / m.per_range;
-      if (s > nstages) s = nstages;
-      m.qsplit = (int)(s < 1 ? 1 : s);
-    }
+  // Split the first launch's items over token ranges while they would not
+  // give every CU an item.
+  m.per_range = items_per_range(p.nb2);
+  m.qsplit = 1;
+  if (m.per_range < cus) {
+    int64_t s = (cus + m.per_range - 1) / m.per_range;
+    if (s > nstages) s = nstages;
+    m.qsplit = (int)(s < 1 ? 1 : s);
   }
   m.qtokens = ((nstages + m.qsplit - 1) / m.qsplit) * ST;
   // Strip-pair tails (only with token splits, whose partial sums the tails
-  // join): the pairs keep head16/16 of each range, whole stages, when the
+  // join): the pairs keep HEAD16/16 of each range, whole stages, when the
   // pieces leave at least half the device to the singles.
   p.tail = TailArgs{0, 1, 0, 0, 0};
   if (m.qsplit > 1) {
     const int npairs = pairs_per_range(p.nb2);
-    const int64_t head = m.qtokens * head16 / 16 / ST * ST;
+    const int64_t head = m.qtokens * HEAD16 / 16 / ST * ST;
     if (npairs > 0 && head > 0 && head < m.qtokens && (int64_t)npairs * m.qsplit * TSPLIT <= cus / 2) {
       const int64_t per = (m.qtokens - head + TSPLIT - 1) / TSPLIT;
       p.tail = TailArgs{npairs, TSPLIT, head, (per + ST - 1) / ST * ST, 0};
@@ -1112,10 +1174,9 @@ SyrkPlan plan(int64_t n, int64_t k, int cus) {
     p.ssplit = (int)(s < 1 ? 1 : s);
   }
   p.stokens = ((nstages + p.ssplit - 1) / p.ssplit) * ST;
-  // Slots: the four-group tiles' splits, the first launch's other items, then
-  // the singles' splits, then the tail pieces.
-  p.slots = (size_t)m.pair_base + (m.qsplit > 1 ? (size_t)m.per_range * m.qsplit : 0) +
-            (p.ssplit > 1 ? (size_t)p.nsingle * p.ssplit : 0) + (size_t)tail_items;
+  // Slots: first-launch items, then the singles' splits, then the tail pieces.
+  p.slots = (m.qsplit > 1 ? (size_t)m.per_range * m.qsplit : 0) + (p.ssplit > 1 ? (size_t)p.nsingle * p.ssplit : 0) +
+            (size_t)tail_items;
   if (tail_items > 0) p.tail.base = (int64_t)(p.slots - tail_items);
   return p;
 }
@@ -1129,7 +1190,8 @@ SyrkPlan plan(int64_t n, int64_t k, int cus) {
 size_t syrk_bf16_workspace(int64_t n, int64_t k) {
   const int cus = num_cus();
   SyrkPlan p = plan(n, k, cus);
-  size_t slots = (size_t)p.m.pair_base;
+  if (p.k4) return p.slots * kSlotFloats * sizeof(float);
+  size_t slots = 0;
   if (p.m.qsplit > 1) slots += ((size_t)p.m.per_range + (size_t)pairs_per_range(p.nb2) * TSPLIT) * p.m.qsplit;
   if (p.nsingle > 0 && p.nsingle < cus) {
     const int64_t nstages = n > ST ? (n + ST - 1) / ST : 1;
@@ -1161,27 +1223,32 @@ hipError_t syrk_bf16(const uint16_t* X, int64_t n, int64_t k, int64_t ldx, float
                               (int)lds_single);
     attr = true;
   }
+  if (p.k4) {
+    // Tiles, tail pieces, then the reductions (a diagonal tile sums its tail
+    // pieces too).
+    const K4Args& a = p.a;
+    hipLaunchKernelGGL(syrk_k4_kernel, dim3(K4_TILES * a.q4 + K4_DTILES * a.qd), dim3(256), lds_main, s, X, n, k,
+                       ldx, H, partial, a, 0);
+    if (a.ts > 0)
+      hipLaunchKernelGGL(syrk_k4_kernel, dim3(K4_DTILES * a.qd * a.ts), dim3(256), lds_main, s, X, n, k, ldx, H,
+                         partial, a, 1);
+    if (!a.direct) {
+      hipLaunchKernelGGL(syrk_reduce_k4_kernel, dim3(K4_TILES, 24), dim3(256), 0, s, k, H, partial, 0, a);
+      hipLaunchKernelGGL(syrk_reduce_k4_kernel, dim3(K4_DTILES, 24), dim3(256), 0, s, k, H, partial, 1, a);
+    }
+    return hipGetLastError();
+  }
   const MainArgs& m = p.m;
   // Order: first launch, second launch (singles and tail pieces), then the
   // reductions, since a strip pair's tiles sum the tail pieces too.
-  if (m.k4)
-    hipLaunchKernelGGL(syrk_k4_kernel, dim3(K4_TILES * m.q4 + m.per_range * m.qsplit), dim3(256), lds_main, s, X, n,
-                       k, ldx, H, partial, m, p.tail);
-  else
-    hipLaunchKernelGGL(syrk_main_kernel, dim3(m.per_range * m.qsplit), dim3(256), lds_main, s, X, n, k, ldx, H,
-                       partial, m, p.tail);
-  const size_t single_base = (size_t)m.pair_base + (m.qsplit > 1 ? (size_t)m.per_range * m.qsplit : 0);
+  hipLaunchKernelGGL(syrk_main_kernel, dim3(m.per_range * m.qsplit), dim3(256), lds_main, s, X, n, k, ldx, H,
+                     partial, m, p.tail);
+  const size_t single_base = m.qsplit > 1 ? (size_t)m.per_range * m.qsplit : 0;
   const int second = p.nsingle * p.ssplit + p.tail.npairs * m.qsplit * p.tail.tsplit;
   if (second > 0)
     hipLaunchKernelGGL(syrk_single_kernel, dim3(second), dim3(256), lds_single, s, X, n, k, ldx, H, partial,
                        p.nsingle, p.ssplit, p.stokens, single_base, m.qtokens, p.tail);
-  if (m.k4 && m.q4 > 1)
-    hipLaunchKernelGGL(syrk_reduce_k4_kernel, dim3(K4_TILES, 24), dim3(256), 0, s, k, H, partial, 0, m.q4, 0,
-                       (size_t)0, p.tail);
-  if (m.k4 && m.qsplit > 1)
-    hipLaunchKernelGGL(syrk_reduce_k4_kernel, dim3(m.per_range, 16), dim3(256), 0, s, k, H, partial, 1, m.qsplit,
-                       m.per_range, (size_t)m.pair_base, p.tail);
-  if (!m.k4 && m.qsplit > 1)
+  if (m.qsplit > 1)
     hipLaunchKernelGGL(syrk_reduce_kernel, dim3(m.per_range, 16), dim3(256), 0, s, k, H, partial, 0, m.qsplit,
                        m.per_range, (size_t)0, p.tail);
   if (p.nsingle > 0 && p.ssplit > 1)
