@@ -1097,21 +1097,27 @@ int num_cus() {
 // Four-group and diagonal tiles: as many token ranges of the four-group
 // tiles as give each (tile, range) a CU; the diagonal tiles split over the
 // CUs left (at least one range), their heads as long as a four-group item
-// and the rest of each range in K4_TSPLIT tail pieces.  The range counts
+// and the rest of each range in up to K4_TSPLIT tail pieces.  Each split
+// writes a partial slot (384 KB) that the reduction reads again, so ranges
+// and tail pieces keep at least K4_MIN_STAGES stages each.  The range counts
 // grow with n up to their caps and never shrink.
+constexpr int K4_MIN_STAGES = 16;
 K4Args k4_plan(int64_t nstages, int cus) {
   K4Args a{};
+  const int64_t most = nstages / K4_MIN_STAGES < 1 ? 1 : nstages / K4_MIN_STAGES;
   int64_t q4 = cus / K4_TILES;
-  a.q4 = (int)(q4 > nstages ? nstages : (q4 < 1 ? 1 : q4));
+  a.q4 = (int)(q4 > most ? most : (q4 < 1 ? 1 : q4));
   int64_t qd = (cus - (int64_t)K4_TILES * (cus / K4_TILES)) / K4_DTILES;
-  a.qd = (int)(qd > nstages ? nstages : (qd < 1 ? 1 : qd));
+  a.qd = (int)(qd > most ? most : (qd < 1 ? 1 : qd));
   a.k4tokens = ((nstages + a.q4 - 1) / a.q4) * ST;
   a.dtokens = ((nstages + a.qd - 1) / a.qd) * ST;
   a.head = a.k4tokens < a.dtokens ? a.k4tokens : a.dtokens;
   a.ts = 0;
   a.ttokens = 0;
   if (a.head < a.dtokens) {
-    a.ts = K4_TSPLIT;
+    const int64_t tail_stages = (a.dtokens - a.head) / ST;
+    const int64_t ts = tail_stages / K4_MIN_STAGES;
+    a.ts = (int)(ts > K4_TSPLIT ? K4_TSPLIT : (ts < 1 ? 1 : ts));
     const int64_t per = (a.dtokens - a.head + a.ts - 1) / a.ts;
     a.ttokens = (per + ST - 1) / ST * ST;
   }

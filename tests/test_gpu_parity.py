@@ -117,12 +117,13 @@ def _hessian_check(H_gpu, X, n):
 
 # (1500, 2320), (777, 4096), (4127, 3072) and (2000, 2048) split the strip
 # pairs' token ranges into tail pieces (with ragged and empty pieces).  Layers
-# of 16 256-channel segments (k in (3840, 4096]) take the four-group tiles:
-# (777, 4096) and (3000, 4096) with token splits, (20, 4096) in one stage
-# straight into H, (100, 3968) with channels past k in the last group and an
-# empty token range.
+# of 16 256-channel segments (k in (3840, 4096]) take the four-group and
+# diagonal tiles: (777, 4096), (20, 4096) and (100, 3968) add into H directly
+# (the last with channels past k in the last group), (3000, 4096) splits the
+# tokens in 3 and 2 ranges with one tail piece per diagonal tile, (7000, 4096)
+# with two ragged tail pieces.
 @pytest.mark.parametrize("n,k", [(3000, 400), (700, 256), (64, 128), (5000, 1024), (1500, 2320), (777, 4096),
-                                 (4127, 3072), (2000, 2048), (3000, 4096), (20, 4096), (100, 3968)])
+                                 (4127, 3072), (2000, 2048), (3000, 4096), (20, 4096), (100, 3968), (7000, 4096)])
 def test_hessian_bf16(nvq, n, k):
     X = synth.activations("attn_proj", n, k, massive=4)
     Xt = synth.to_bf16_tensor(X).to(DEV)
@@ -142,7 +143,7 @@ def test_hessian_accumulates_over_chunks(nvq):
 def test_hessian_accumulates_over_chunks_four_group_tiles(nvq):
     # The first chunk (one stage) adds into H directly, the second through
     # token splits and the reduction.
-    n, k = 1300, 4096
+    n, k = 1600, 4096
     X = synth.activations("attn_proj", n, k)
     Xt = synth.to_bf16_tensor(X).to(DEV)
     H = nvq.hessian_accumulate(Xt[:30])
