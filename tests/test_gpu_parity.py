@@ -162,8 +162,10 @@ def test_hessian_fp32_small_layer(nvq):
 
 
 # ------------------------------------------------------------------ factor
-# k = 2048 reaches the inverse level whose products split their k ranges.
-@pytest.mark.parametrize("k,n", [(256, 2048), (448, 4000), (1024, 8192), (2048, 6144)])
+# k = 2048 reaches the inverse level whose products split their k ranges;
+# k = 4608 (nine super-panels of 512) runs the trailing updates split over two
+# streams.
+@pytest.mark.parametrize("k,n", [(256, 2048), (448, 4000), (1024, 8192), (2048, 6144), (4608, 9216)])
 def test_factor_matches_oracle(nvq, k, n):
     X = synth.activations("attn_proj", n, k, massive=4)
     H = gptq.hessian(X)
