@@ -26,6 +26,12 @@
  *     the last failure on the calling thread is given by nvq_last_error().
  *   - Calls on different streams may run concurrently when their output and
  *     workspace buffers do not overlap.
+ *   - A call may run part of its work on an internal stream of the library
+ *     (one per device, default priority; factor_hinv above k = 4096): that
+ *     work starts after the work enqueued on "stream" before the call, and
+ *     the work enqueued on "stream" after the call waits for it (HIP events),
+ *     so the call is ordered on "stream" as if it ran there alone, also under
+ *     stream capture.
  */
 #ifndef NVQ_H
 #define NVQ_H
