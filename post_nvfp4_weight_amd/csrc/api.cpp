@@ -160,15 +160,19 @@ hipError_t sweep_f32(int64_t m, int64_t k, const float* U, const float* g, int n
     a.sA2 = wsf; a.sB2 = qb.stride_u; a.sC2 = wsf;
     return gemm_f32(a, false, false, false, kEpiAxpby, s);
   };
+  // With larger candidate groups the sweep launch itself applies the earlier
+  // batches' errors of the block to its rows (pre columns); else a GEMM after
+  // each batch updates the rest of the block.
+  const bool inblock = sweep_applies_inblock(n_cand);
   hipError_t e = hipSuccess;
   for (int64_t s0 = 0; e == hipSuccess && s0 < k; s0 += kSuperBatch) {
     const int64_t s1 = std::min<int64_t>(k, s0 + kSuperBatch);
     for (int64_t i1 = s0; e == hipSuccess && i1 < s1; i1 += kBatch) {
       const int ncols = (int)std::min<int64_t>(kBatch, s1 - i1);
       e = sweep_batch_launch(Wp, U, invd, g, m, k, (int)i1, ncols, n_cand, indep, codes, scales, Eslab + (i1 - s0),
-                             kSuperBatch, row_loss, s, qb.nb, bs);
+                             kSuperBatch, row_loss, s, qb.nb, bs, inblock ? (int)(i1 - s0) : 0);
       const int64_t i2 = i1 + ncols;
-      if (e == hipSuccess && i2 < s1) e = rank_update(Eslab + (i1 - s0), i1, i2, ncols, s1 - i2);
+      if (e == hipSuccess && !inblock && i2 < s1) e = rank_update(Eslab + (i1 - s0), i1, i2, ncols, s1 - i2);
     }
     if (e == hipSuccess && s1 < k) e = rank_update(Eslab, s0, s1, s1 - s0, k - s1);
   }

@@ -105,10 +105,15 @@ hipError_t inv_diag_launch(const float* U, int64_t k, float* invd, hipStream_t s
                            int64_t stride_u = 0, int64_t stride_invd = 0);
 // indep: choose each block's scale by the block-independent squared rounding
 // error instead of the replay score (the committed block is still replayed).
+// pre (a multiple of 128, with sweep_applies_inblock(n_cand)): the batch's
+// columns have not yet received the errors of the pre columns before it in
+// its 512-column block, which the error slab holds just before Eslab; the
+// launch applies them to its rows first.  Otherwise pre must be 0.
 hipError_t sweep_batch_launch(float* Wp, const float* U, const float* invd, const float* g,
                               int64_t m, int64_t k, int i1, int ncols, int n_cand, bool indep,
                               uint8_t* codes, uint8_t* scales, float* Eslab, int64_t lde, float* row_loss,
-                              hipStream_t s, int64_t nb = 1, const SweepStrides& bs = SweepStrides());
+                              hipStream_t s, int64_t nb = 1, const SweepStrides& bs = SweepStrides(), int pre = 0);
+bool sweep_applies_inblock(int n_cand);
 // The same sweep with fp64 working weights and errors (U read as fp32).
 hipError_t sweep_batch_launch_f64(double* Wp, const float* U, const float* g, int64_t m, int64_t k, int i1,
                                   int ncols, int n_cand, bool indep, uint8_t* codes, uint8_t* scales, double* Eslab,

@@ -11,7 +11,10 @@
 // eight 16x16 diagonal blocks and 1/U_jj live in LDS (the in-block factor
 // entries are read as wave-wide broadcasts), and after each block the row's G
 // lanes update the later columns of the batch.  Columns beyond the batch are
-// updated afterwards by one fp32 MFMA GEMM with the batch's error slab.
+// updated by fp32 MFMA products with the error slab: with G >= 8 the batch's
+// own rows first take the errors of the earlier batches of their 512-column
+// block inside the sweep launch (one 16 x 128 product per workgroup), else a
+// GEMM after each batch updates the rest of the block.
 #include <algorithm>
 
 #include "common.h"
@@ -402,6 +405,9 @@ template <int G>
 struct SweepCfg {
   static constexpr int ROWS = (64 / G) > 16 ? (64 / G) : 16;
   static constexpr int THREADS = ROWS * G;
+  // With two or more waves per workgroup the launch applies the earlier
+  // batches' errors of the 512-column block to its rows itself.
+  static constexpr bool INBLOCK = G >= 8;
 };
 
 // One butterfly step of the candidate arg-min inside groups of G lanes.
@@ -480,7 +486,7 @@ __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
     T* __restrict__ Wp, const float* __restrict__ U, const float* __restrict__ invd,
     const float* __restrict__ gptr, int64_t m, int64_t k, int i1, int ncols, int n_cand,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, T* __restrict__ Eslab, int64_t lde,
-    float* __restrict__ row_loss, SweepStrides bs) {
+    float* __restrict__ row_loss, SweepStrides bs, int pre) {
   constexpr bool F64 = sizeof(T) == 8;
   {   // matrix e = blockIdx.y of a batch
     const int64_t e = blockIdx.y;
@@ -588,6 +594,79 @@ __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
     slab_store(base, w);
   }
   __syncthreads();
+
+  // The earlier batches of this 512-column block (pre columns, whose errors
+  // sit just before this batch's in the error slab) have not yet updated the
+  // batch's columns: slab[r][c] -= sum_q E[r][q] U[i1-pre+q][i1+c], on
+  // v_mfma_f32_16x16x4f32 tiles of 16 rows x 16 columns, each wave taking
+  // 128 / NW columns.  Lane (l16, lq) supplies q = kc + 4 lq + s at step s of
+  // a 16-value chunk: one 16-byte read of its row's errors, and U rows read
+  // as 64-byte row pieces.  Rows past m read row m-1 (results unused);
+  // columns past ncols are neither read nor written.
+  if constexpr (!F64 && SweepCfg<G>::INBLOCK) {
+    if (pre > 0) {
+      static_assert(ROWS == 16, "one 16-row tile per workgroup");
+      constexpr int TPW = kBatch / 16 / NW;   // column tiles per wave
+      const int l16 = lane & 15, lq = lane >> 4;
+      const float* ep = Eslab - pre + min(row0 + l16, m - 1) * lde + 4 * lq;
+      const float* up = U + (int64_t)(i1 - pre + 4 * lq) * k + i1;
+      int col[TPW];
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) col[t] = min((wave * TPW + t) * 16 + l16, ncols - 1);
+      f32x4 acc[TPW];
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // Stages of 64 k-values in two buffers: one stage's loads are in flight
+      // during the other's products (pre is a multiple of 128; the last load
+      // repeats the last stage, unused).  The scheduling barriers keep the
+      // loads ahead of the products they overlap.
+      constexpr int CU = 4;
+      struct Stage {
+        f32x4 a[CU];
+        float b[CU][4][TPW];
+      };
+      auto load_stage = [&](int kc, Stage& o) {
+#pragma unroll
+        for (int c = 0; c < CU; ++c) {
+          o.a[c] = *(const f32x4*)(ep + kc + 16 * c);
+#pragma unroll
+          for (int st = 0; st < 4; ++st)
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) o.b[c][st][t] = up[(int64_t)(kc + 16 * c + st) * k + col[t]];
+        }
+      };
+      auto mfma_stage = [&](const Stage& o) {
+#pragma unroll
+        for (int c = 0; c < CU; ++c)
+#pragma unroll
+          for (int st = 0; st < 4; ++st)
+#pragma unroll
+            for (int t = 0; t < TPW; ++t)
+              acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(o.a[c][st], o.b[c][st][t], acc[t], 0, 0, 0);
+      };
+      Stage sa, sb;
+      load_stage(0, sa);
+      for (int kc = 0; kc < pre; kc += 32 * CU) {
+        load_stage(kc + 16 * CU, sb);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_stage(sa);
+        __builtin_amdgcn_sched_barrier(0);
+        load_stage(min(kc + 32 * CU, pre - 16 * CU), sa);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_stage(sb);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        const int c = (wave * TPW + t) * 16 + l16;
+        if (c < ncols) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) slab[4 * lq + r][c] -= acc[t][r];
+        }
+      }
+      __syncthreads();
+    }
+  }
 
   T loss = 0;
   const int nblk = ncols / kBlock;
@@ -720,26 +799,27 @@ __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
 template <int G, typename T>
 hipError_t sweep_launch_g(T* Wp, const float* U, const float* invd, const float* g, int64_t m, int64_t k,
                           int i1, int ncols, int n_cand, bool indep, uint8_t* codes, uint8_t* scales, T* Eslab,
-                          int64_t lde, float* row_loss, hipStream_t s, int64_t nb, const SweepStrides& bs) {
+                          int64_t lde, float* row_loss, hipStream_t s, int64_t nb, const SweepStrides& bs, int pre) {
   constexpr int ROWS = SweepCfg<G>::ROWS;
+  if (!SweepCfg<G>::INBLOCK || sizeof(T) != 4) pre = 0;
   dim3 grid((unsigned)((m + ROWS - 1) / ROWS), (unsigned)nb);
   if (indep)
     hipLaunchKernelGGL((sweep_batch_kernel<G, T, true>), grid, dim3(SweepCfg<G>::THREADS), 0, s, Wp, U, invd, g, m,
-                       k, i1, ncols, n_cand, codes, scales, Eslab, lde, row_loss, bs);
+                       k, i1, ncols, n_cand, codes, scales, Eslab, lde, row_loss, bs, pre);
   else
     hipLaunchKernelGGL((sweep_batch_kernel<G, T, false>), grid, dim3(SweepCfg<G>::THREADS), 0, s, Wp, U, invd, g, m,
-                       k, i1, ncols, n_cand, codes, scales, Eslab, lde, row_loss, bs);
+                       k, i1, ncols, n_cand, codes, scales, Eslab, lde, row_loss, bs, pre);
   return hipGetLastError();
 }
 template <typename T>
 hipError_t sweep_launch_t(T* Wp, const float* U, const float* invd, const float* g, int64_t m, int64_t k, int i1,
                           int ncols, int n_cand, bool indep, uint8_t* codes, uint8_t* scales, T* Eslab, int64_t lde,
-                          float* row_loss, hipStream_t s, int64_t nb, const SweepStrides& bs) {
-  if (n_cand <= 1) return sweep_launch_g<1>(Wp, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s, nb, bs);
-  if (n_cand <= 2) return sweep_launch_g<2>(Wp, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s, nb, bs);
-  if (n_cand <= 4) return sweep_launch_g<4>(Wp, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s, nb, bs);
-  if (n_cand <= 8) return sweep_launch_g<8>(Wp, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s, nb, bs);
-  return sweep_launch_g<16>(Wp, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s, nb, bs);
+                          float* row_loss, hipStream_t s, int64_t nb, const SweepStrides& bs, int pre) {
+  if (n_cand <= 1) return sweep_launch_g<1>(Wp, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s, nb, bs, pre);
+  if (n_cand <= 2) return sweep_launch_g<2>(Wp, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s, nb, bs, pre);
+  if (n_cand <= 4) return sweep_launch_g<4>(Wp, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s, nb, bs, pre);
+  if (n_cand <= 8) return sweep_launch_g<8>(Wp, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s, nb, bs, pre);
+  return sweep_launch_g<16>(Wp, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s, nb, bs, pre);
 }
 
 }  // namespace
@@ -826,10 +906,11 @@ hipError_t load_working_copy_f64(const void* W, int bf16, int64_t m, int64_t k, 
 hipError_t sweep_batch_launch(float* Wp, const float* U, const float* invd, const float* g, int64_t m, int64_t k,
                               int i1, int ncols, int n_cand, bool indep, uint8_t* codes, uint8_t* scales,
                               float* Eslab, int64_t lde, float* row_loss, hipStream_t s, int64_t nb,
-                              const SweepStrides& bs) {
+                              const SweepStrides& bs, int pre) {
   return sweep_launch_t<float>(Wp, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s,
-                               nb, bs);
+                               nb, bs, pre);
 }
+bool sweep_applies_inblock(int n_cand) { return n_cand > 4; }
 hipError_t sweep_batch_launch_f64(double* Wp, const float* U, const float* g, int64_t m, int64_t k, int i1,
                                   int ncols, int n_cand, bool indep, uint8_t* codes, uint8_t* scales, double* Eslab,
                                   int64_t lde, float* row_loss, hipStream_t s, int64_t nb, const SweepStrides& bs) {
@@ -837,7 +918,7 @@ hipError_t sweep_batch_launch_f64(double* Wp, const float* U, const float* g, in
   SweepStrides b2 = bs;
   b2.invd = bs.u;
   return sweep_launch_t<double>(Wp, U, U, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s,
-                                nb, b2);
+                                nb, b2, 0);
 }
 
 hipError_t delta_w_launch(const void* W, int bf16, int64_t m, int64_t k, int64_t ldw, const uint8_t* codes,
