@@ -588,6 +588,74 @@ def moe_line(steps, warmup):
     print(json.dumps(out), flush=True)
 
 
+def device_peaks():
+    """Micro-benchmarked device peaks from libnvq_peaks.so, printed as one JSON line: the bf16 and fp32
+    MFMA issue rates and the fp32 FMA rate (register operands only, 4 workgroups of 256 per CU, each
+    launch about 30 ms at the nominal peak; the third of three launches, after the clock has settled),
+    and HBM bandwidth of a 16-byte-vector copy of 1 GiB (read + write bytes over its time; the best of 1, 4
+    or 8 vectors in flight per thread and 1024 to 16384 workgroups, with torch's copy beside it)."""
+    import ctypes
+    import torch
+    here = os.path.dirname(os.path.abspath(__file__))
+    lib = ctypes.CDLL(os.path.join(here, "post_nvfp4_weight_amd", "libnvq_peaks.so"))
+    lib.nvq_peak_compute.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.nvq_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int,
+                                  ctypes.c_void_p]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    grid = 1024
+    out = torch.empty(grid * 256, dtype=torch.float32, device=dev)
+
+    def timed(fn, reps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ms = []
+        for _ in range(3):
+            ev[0].record()
+            for _ in range(reps):
+                fn()
+            ev[1].record()
+            torch.cuda.synchronize()
+            ms.append(ev[0].elapsed_time(ev[1]) / reps)
+        return ms[-1]
+
+    def chk(rc):
+        if rc != 0:
+            raise RuntimeError(f"peak kernel launch failed: hipError {rc}")
+
+    # (name, kind, flops per iteration of the whole grid, iterations, nominal TFLOP/s)
+    kinds = [("bf16_mfma", 0, grid * 4 * 4 * 32768, 131072, PEAK_BF16_TFLOPS),
+             ("fp32_mfma", 1, grid * 4 * 4 * 4096, 65536, 157.3),
+             ("fp32_fma_nonpacked", 2, grid * 256 * 16 * 2, 262144, 78.6)]
+    res = {}
+    for name, kind, fpi, iters, nominal in kinds:
+        ms = timed(lambda: chk(lib.nvq_peak_compute(kind, grid, iters, ctypes.c_void_p(out.data_ptr()), s)), 1)
+        tf = fpi * iters / (ms / 1e3) / 1e12
+        res[name] = {"tflops": round(tf, 1), "nominal": nominal, "frac_of_nominal": round(tf / nominal, 4),
+                     "implied_clock_ghz": round(2.4 * tf / nominal, 3), "ms": round(ms, 3)}
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    best = None
+    sweep = {}
+    for unroll in (1, 4, 8):
+        for cgrid in (1024, 2048, 4096, 8192, 16384):
+            ms = timed(lambda: chk(lib.nvq_peak_copy(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()),
+                                                     nbytes, cgrid, unroll, s)), 10)
+            sweep[f"u{unroll}_g{cgrid}"] = round(2 * nbytes / (ms / 1e3) / 1e9, 1)
+            if best is None or ms < best[0]:
+                best = (ms, unroll, cgrid)
+    ms, unroll, cgrid = best
+    gbs = 2 * nbytes / (ms / 1e3) / 1e9
+    res["hbm_copy"] = {"gbs": round(gbs, 1), "nominal": PEAK_HBM_GBS, "frac_of_nominal": round(gbs / PEAK_HBM_GBS, 4),
+                       "bytes_per_copy": 2 * nbytes, "ms": round(ms, 4), "unroll": unroll, "grid": cgrid,
+                       "sweep_gbs": sweep}
+    ms = timed(lambda: dst.copy_(src), 10)
+    res["torch_copy_gbs"] = round(2 * nbytes / (ms / 1e3) / 1e9, 1)
+    print(json.dumps({"device_peaks": res}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -607,7 +675,12 @@ def main():
     ap.add_argument("--ablation", action="store_true",
                     help="instead of timing, print the layer's total weighted error under four scale-selection "
                          "configurations (RTN absmax, GPTQ absmax, GPTQ block-independent, GPTQ Schur Replay)")
+    ap.add_argument("--peaks", action="store_true",
+                    help="instead of the layer step, micro-benchmark the device's MFMA, FMA and HBM copy peaks")
     args = ap.parse_args()
+    if args.peaks:
+        device_peaks()
+        return
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
         return

@@ -12,6 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libnvq.so")
+PEAKS_LIB = os.path.join(HERE, "libnvq_peaks.so")
 SOURCES = ["api.cpp", "gemm.hip", "syrk.hip", "factor.hip", "sweep.hip", "consumer.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -52,6 +53,14 @@ def build(verbose=False, jobs=None):
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout.decode(errors="replace"))
     os.replace(LIB + ".tmp", LIB)
+    # The device-peak micro-benchmarks: a separate library that only the
+    # benchmark loads.
+    src = os.path.join(CSRC, "peaks.hip")
+    r = subprocess.run([HIPCC] + common + device_flags + ["-shared", src, "-o", PEAKS_LIB + ".tmp"],
+                       stdout=subprocess.PIPE, stderr=subprocess.STDOUT)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed on peaks.hip:\n" + r.stdout.decode(errors="replace"))
+    os.replace(PEAKS_LIB + ".tmp", PEAKS_LIB)
     return LIB
 
 
