@@ -46,6 +46,16 @@ __device__ __forceinline__ float e4m3_value(int c) {
   int e = c >> 3, m = c & 7;
   return e == 0 ? (float)m * 0x1p-9f : __uint_as_float((uint32_t)(e + 120) << 23 | (uint32_t)m << 20);
 }
+// The same value with both forms evaluated and one selected: c 2^-9 for the
+// subnormal codes c < 8, else the float bits (c << 20) + (120 << 23).  Where
+// it is evaluated per block ahead of the element loop (the scale search and
+// encode) this compiles without branches; the dequantization kernel keeps
+// the form above, which schedules better there.
+__device__ __forceinline__ float e4m3_value_sel(int c) {
+  const float nrm = __uint_as_float(((uint32_t)c << 20) + (120u << 23));
+  const float sub = (float)c * 0x1p-9f;
+  return c < 8 ? sub : nrm;
+}
 
 // Code of the E4M3 value nearest to the real quotient a / (6 g), ties to the
 // even code, saturating at 0x7E.  a >= 0.  Binary search over the 126
@@ -57,7 +67,7 @@ __device__ __forceinline__ int e4m3_code_of_ratio(float a, float g) {
   for (int it = 0; it < 7; ++it) {
     int mid = (lo + hi) >> 1;              // test midpoint between mid and mid+1
     if (lo >= hi) break;
-    float six_m = 3.0f * (e4m3_value(mid) + e4m3_value(mid + 1));   // 6 * m_i, exact
+    float six_m = 3.0f * (e4m3_value_sel(mid) + e4m3_value_sel(mid + 1));   // 6 * m_i, exact
     float d = fmaf(-six_m, g, a);
     bool pass = (mid & 1) ? (d >= 0.0f) : (d > 0.0f);
     if (pass) lo = mid + 1; else hi = mid;
@@ -97,6 +107,29 @@ __device__ __forceinline__ int e2m1_index_search(float aw, float g, const float 
   return (int)((m2 & 4u) | (m1 & 2u) | b0);
 }
 
+// The same index from one exact test.  q2 ~ 2 aw / (s g) (any relative
+// error under 10% will do) picks the midpoint t_j nearest to aw / (s g):
+// j = floor(min(q2, q2 / 2 + 2, 6.5)) switches from j to j + 1 at 0.5, 1,
+// 1.5, 2, 3 and 4, each well inside the gap between t_j and t_{j+1}
+// (midpoints 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5).  So aw / (s g) lies
+// between t_{j-1} and t_{j+1}, and the index is j, or j + 1 when aw passes
+// t_j: the sign of fma(-t_j s, g, aw) as in e2m1_index (t_j s is exact:
+// 8 t_j = 2, 6, 10, 14, 20, 28, 40 from a byte table, times s8 = s / 8).
+// (The byte is selected by j alone: the other result bytes are ignored.)
+// The tie rule rides on the integer view of that difference d: a positive
+// float is an integer >= 1, +0 is 0 and every negative float (-0 too) is
+// negative, so "d > 0" is int(d) > 0 and "d >= 0" (odd midpoints, ties round
+// up) is int(d) > -1: both are int(d) > -(j & 1), in signed arithmetic.
+__device__ __forceinline__ int e2m1_index_nearest(float aw, float q2, float g, float s8) {
+  const int j = (int)fminf(fminf(q2, fmaf(0.5f, q2, 2.0f)), 6.5f);
+  const float t8 = (float)(__builtin_amdgcn_perm(0x00281C14u, 0x0E0A0602u, (uint32_t)j) & 0xFFu);
+  const float d = fmaf(-(t8 * s8), g, aw);
+  return j + (int)(__float_as_int(d) > -(j & 1));
+}
+// q2 = aw * r2 with r2 = 2 / (s g) needs that quotient finite: g at least
+// this for every scale s >= 2^-9 (below it the search above is used).
+constexpr float kNearestMinG = 0x1p-100f;
+
 // Twice the E2M1 magnitude of index idx: 0,1,2,3,4,6,8,12 packed in nibbles.
 __device__ __forceinline__ float e2m1_twice_mag(int idx) {
   return (float)((0xC8643210u >> (4 * idx)) & 0xFu);
@@ -123,7 +156,7 @@ __device__ __forceinline__ int e4m3_code_of_ratio(double a, float g) {
   for (int it = 0; it < 7; ++it) {
     int mid = (lo + hi) >> 1;
     if (lo >= hi) break;
-    double thr = (double)(3.0f * (e4m3_value(mid) + e4m3_value(mid + 1))) * (double)g;
+    double thr = (double)(3.0f * (e4m3_value_sel(mid) + e4m3_value_sel(mid + 1))) * (double)g;
     bool pass = (mid & 1) ? (a >= thr) : (a > thr);
     if (pass) lo = mid + 1; else hi = mid;
   }
@@ -166,35 +199,31 @@ __device__ __forceinline__ void lds_barrier() {
 // search's test above); never past the last code.
 // (Branch-free: i <= 126, and e4m3_value is defined on 127.)
 __device__ __forceinline__ bool e4m3_passes(float a, float g, int i) {
-  const float d = fmaf(-3.0f * (e4m3_value(i) + e4m3_value(i + 1)), g, a);
+  const float d = fmaf(-3.0f * (e4m3_value_sel(i) + e4m3_value_sel(i + 1)), g, a);
   return i < kE4m3MaxCode && ((i & 1) ? d >= 0.0f : d > 0.0f);
 }
 __device__ __forceinline__ bool e4m3_passes(double a, float g, int i) {
-  const double thr = (double)(3.0f * (e4m3_value(i) + e4m3_value(i + 1))) * (double)g;
+  const double thr = (double)(3.0f * (e4m3_value_sel(i) + e4m3_value_sel(i + 1))) * (double)g;
   return i < kE4m3MaxCode && ((i & 1) ? a >= thr : a > thr);
 }
 // E4M3 code whose value is at or just below q >= 0, from q's bits (q may be
 // approximate or infinite; clamped to [0, 126]).
+// (Both forms are evaluated and one selected; the product is clamped before
+// its conversion, so that it stays in range for every q.)
 __device__ __forceinline__ int e4m3_code_below(float q) {
-  int c;
-  if (q < 0x1p-6f) {
-    c = (int)(q * 512.0f);
-  } else {
-    const uint32_t u = __float_as_uint(q);
-    c = ((int)(u >> 23) - 120) * 8 + (int)((u >> 20) & 7);
-  }
-  return min(max(c, 0), kE4m3MaxCode);
+  const int sub = (int)fminf(q * 512.0f, 8.0f);
+  const int nrm = (int)(__float_as_uint(q) >> 20) - 960;   // (exponent - 120) * 8 + top mantissa bits
+  return min(max(q < 0x1p-6f ? sub : nrm, 0), kE4m3MaxCode);
 }
-// The code e4m3_code_of_ratio returns, located by an approximate quotient
-// (r6g ~ 1 / (6 g), a few ulps off): the grid floor of the exact quotient is
-// within one code of the approximate quotient's (grid steps are >= 1/16
-// relative), and the nearest code is that floor or the next one, so the true
-// code lies in [lo, lo + 3] for lo = below - 1.  Every midpoint under lo is
-// passed and none past lo + 2; the three in between are tested exactly.
+// The code e4m3_code_of_ratio returns, from one exact test.  The grid code
+// i at or below an approximate quotient q = a r6g (r6g ~ 1 / (6 g), a few
+// ulps off) names the midpoint m_i nearest to q; grid steps are >= 1/16
+// relative, so the exact quotient lies between m_{i-1} and m_{i+1}, and the
+// code is i, or i + 1 when a passes m_i (never past the last code).
 template <typename T>
 __device__ __forceinline__ int e4m3_code_of_ratio_fast(T a, float g, float r6g) {
-  const int lo = max(e4m3_code_below((float)a * r6g) - 1, 0);
-  return lo + (int)e4m3_passes(a, g, lo) + (int)e4m3_passes(a, g, lo + 1) + (int)e4m3_passes(a, g, lo + 2);
+  const int i = e4m3_code_below((float)a * r6g);
+  return i + (int)e4m3_passes(a, g, i);
 }
 // The quotient above is only that close while 1 / (6 g) is a finite normal
 // float; below this g (weights under ~1e-35) the binary search is used.

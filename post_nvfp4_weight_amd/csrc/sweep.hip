@@ -165,6 +165,9 @@ __global__ __launch_bounds__(256) void rtn_kernel(const void* __restrict__ W, in
   }
   const float g = *gptr;
   const float r6g = 1.0f / (6.0f * g);
+  // The one-test E2M1 index needs 2 / (s g) finite for every scale s >= 2^-9.
+  const bool nearest = g >= kNearestMinG;
+  const float rg = 1.0f / g;
   const bool dense = ldw == k;
   const int64_t stride = (int64_t)gridDim.x * 256;
   for (int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x; b < nblk; b += stride) {
@@ -202,8 +205,33 @@ __global__ __launch_bounds__(256) void rtn_kernel(const void* __restrict__ W, in
     uint32_t best_lo = 0, best_hi = 0;
     if (a > 0.0f) {
       const int lo = candidate_lo(e4m3_code_of_ratio_any(a, g, r6g), n_cand);
-      if (n_cand == 1) {
-        const float s = e4m3_value(lo);
+      if (n_cand == 1 && nearest) {
+        // Magnitude indices and sign bits gather into the two code words
+        // separately; a sign is kept where its nibble's index is non-zero
+        // (zero is always +0).
+        const float s = e4m3_value_sel(lo);
+        const float r2 = 2.0f * __builtin_amdgcn_rcpf(s) * rg, s8 = 0.125f * s;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const float* x = &w[8 * h];
+          uint32_t mag = 0;
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            mag |= (uint32_t)e2m1_index_nearest(fabsf(x[j]), fabsf(x[j]) * r2, g, s8) << (4 * j);
+          // Code byte q holds elements 2q (bits 0-3) and 2q+1 (bits 4-7): byte
+          // permutes gather byte 3 (the sign's byte) of the odd elements into
+          // bytes 0-3 (sign at bit 7) and of the even ones (shifted to bit 3).
+          auto b3 = [&](int a, int c) {   // byte 3 of x[a] and x[c] into bytes 0, 1 | of x[a+4], x[c+4] into 2, 3
+            return __builtin_amdgcn_perm(__float_as_uint(x[c]), __float_as_uint(x[a]), 0x0C0C0703u) |
+                   __builtin_amdgcn_perm(__float_as_uint(x[c + 4]), __float_as_uint(x[a + 4]), 0x07030C0Cu);
+          };
+          const uint32_t sgn = (b3(1, 3) & 0x80808080u) | ((b3(0, 2) >> 4) & 0x08080808u);
+          const uint32_t nz = mag | (mag >> 1) | (mag >> 2);   // bit 4j: nibble j is non-zero
+          (h ? best_hi : best_lo) = mag | (sgn & (nz << 3));
+        }
+        best_c = lo;
+      } else if (n_cand == 1) {
+        const float s = e4m3_value_sel(lo);
         const float ts[7] = {0.25f * s, 0.75f * s, 1.25f * s, 1.75f * s, 2.5f * s, 3.5f * s, 5.0f * s};
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
@@ -216,7 +244,7 @@ __global__ __launch_bounds__(256) void rtn_kernel(const void* __restrict__ W, in
         float best = __builtin_inff();
         for (int ci = 0; ci < n_cand; ++ci) {
           const int c = lo + ci;
-          const float s = e4m3_value(c);
+          const float s = e4m3_value_sel(c);
           const float hs = 0.5f * s;
           const float ts[7] = {0.25f * s, 0.75f * s, 1.25f * s, 1.75f * s, 2.5f * s, 3.5f * s, 5.0f * s};
           float score = 0.0f;
@@ -696,7 +724,7 @@ __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
     if (a > T(0)) {
       const int lo = candidate_lo(e4m3_code_of_ratio_any(a, g, r6g), n_cand);
       cand = lo + (ci < n_cand ? ci : 0);
-      const float s = e4m3_value(cand);
+      const float s = e4m3_value_sel(cand);
       const float hs = 0.5f * s;
       const float ts[7] = {0.25f * s, 0.75f * s, 1.25f * s, 1.75f * s, 2.5f * s, 3.5f * s, 5.0f * s};
       // Block-independent selection: the plain squared rounding error of the
