@@ -95,6 +95,26 @@ def test_rtn_one_candidate_bit_exact(nvq, dtype):
     assert np.array_equal(out["scales"].cpu().numpy(), ref["scales"])
 
 
+@pytest.mark.parametrize("K", [1, 4])
+@pytest.mark.parametrize("gexp", [-9, -6, 0])
+def test_rtn_exact_ties_bit_exact(nvq, K, gexp):
+    # Weights on a 1/8 grid and a power-of-two global scale: many weights sit
+    # exactly on an E2M1 midpoint t * s * g (and block maxima on E4M3
+    # midpoints), where the rounding rule decides (ties to the even index).
+    rng = np.random.default_rng(11 + gexp)
+    W = (rng.integers(-64, 65, size=(64, 512)) * 0.125).astype(np.float32)
+    W[3, :16] = 0.0
+    g = np.float32(2.0 ** gexp)
+    ref = gptq.sweep(W, np.eye(512, dtype=np.float32), g, K, dtype=np.float32)
+    s = np.repeat(codec.e4m3_decode(ref["scales"]).astype(np.float64), 16, axis=1) * float(g)
+    ratio = np.divide(np.abs(W), s, out=np.zeros(W.shape), where=s > 0)
+    assert np.any(np.isin(ratio, [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]))
+    out = nvq.gptq_nvfp4_quantize(_to_dev(W), None, None, _to_dev(np.array([g])), K,
+                                  nvq.FLAG_RTN | nvq.FLAG_NO_ERR)
+    assert np.array_equal(out["scales"].cpu().numpy(), ref["scales"])
+    assert np.array_equal(out["codes"].cpu().numpy(), codec.pack_codes(ref["codes"]))
+
+
 @pytest.mark.parametrize("K", [4, 8, 16])
 def test_rtn_candidates_bit_exact_fp32_scores(nvq, K):
     W = synth.weights("attn_proj", 64, 256, 0.02, outlier_frac=0.01, bf16=False)
