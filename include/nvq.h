@@ -27,7 +27,8 @@
  *   - Calls on different streams may run concurrently when their output and
  *     workspace buffers do not overlap.
  *   - A call may run part of its work on an internal stream of the library
- *     (one per device, default priority; factor_hinv above k = 4096): that
+ *     (one per device, default priority; factor_hinv and factor_chol above
+ *     k = 4096): that
  *     work starts after the work enqueued on "stream" before the call, and
  *     the work enqueued on "stream" after the call waits for it (HIP events),
  *     so the call is ordered on "stream" as if it ran there alone, also under
@@ -105,6 +106,21 @@ extern "C" {
  * Without the flag a non-finite weight still gives deterministic outputs
  * (NaN scores lose every arg-min), but they mean nothing. */
 #define NVQ_FLAG_CHECK_FINITE 16u
+/* The U argument is the V that factor_chol writes (the Cholesky factor R of
+ * H + lambda I = R R^T, scaled) instead of the U that factor_hinv writes
+ * (U = R^-1).  The sweep is the same GPTQ computation ("Replay the
+ * Curvature", Abstract: quantizing one column updates those that follow)
+ * taken in the factor's own form: a committed column j propagates its raw
+ * error w_j - q_j (against its input value) through V_jl = -R_jl / R_ll, the
+ * later columns receive w'_l = w_l + sum_{j<l} (w_j - q_j) R_jl / R_ll,
+ * and the score term of column j is ((w'_j - q_j) R_jj)^2.  With exact
+ * arithmetic these are the updates and scores of the inverse form, term by
+ * term (e_j U_jl = (w_j - q_j) R_jl / R_ll summed over j); in fp32 they
+ * differ by rounding.  The candidate window, decisions, codes, scales,
+ * row_loss and row_err are defined as without the flag.  Needs a larger
+ * workspace (gptq_nvfp4_workspace_size with the same flags: one more copy of
+ * W in the working precision).  Ignored with RTN. */
+#define NVQ_FLAG_CHOL_FACTOR 32u
 
 /*
  * hessian_accumulate -- second-order state of the layer ("Replay the
@@ -219,6 +235,31 @@ int factor_hinv(const float* H, int64_t k, float damp_rel, float* U, float* lamb
                 int32_t* info, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * factor_chol -- the damped Cholesky factor in the form the sweep takes with
+ * NVQ_FLAG_CHOL_FACTOR, without the triangular inverse that factor_hinv
+ * forms ("Replay the Curvature", Abstract: GPTQ, in which quantizing one
+ * column updates those that follow).
+ *
+ *   lambda = damp_rel * mean(diag H) as in factor_hinv; R is the
+ *   upper-triangular matrix with positive diagonal such that
+ *   H + lambda I = R R^T (so R = U^-1 for factor_hinv's U).
+ *   V          device fp32 [k x k] output: V[i][j] = -R[i][j] / R[j][j] for
+ *              j > i, V[i][i] = R[i][i], 0 below the diagonal.  V must not
+ *              overlap H.
+ *   H, k, damp_rel, lambda_out, info: as for factor_hinv (info > 0 names the
+ *              order of the trailing principal submatrix that is not positive
+ *              definite; V then holds no meaningful values).
+ *   ws         device workspace of factor_chol_workspace_size(k) bytes.
+ * Computed in fp32 by the same blocked Cholesky factorization of the
+ * index-reversed damped matrix as factor_hinv (R = J L J for L = chol(J (H +
+ * lambda I) J), J the index reversal); the same internal stream above k =
+ * 4096.
+ */
+size_t factor_chol_workspace_size(int64_t k);
+int factor_chol(const float* H, int64_t k, float damp_rel, float* V, float* lambda_out, int32_t* info, void* ws,
+                size_t ws_bytes, void* stream);
+
+/*
  * factor_hinv_batched -- factor_hinv of `batch` matrices (one per expert of a
  * mixture-of-experts layer): H + e*stride_h -> U + e*stride_u,
  * lambda_out[e], info[e].  Strides count floats, are >= k*k and multiples of
@@ -274,7 +315,8 @@ int nvfp4_global_scale(const void* W, int w_dtype, int64_t m, int64_t k, int64_t
  *
  *   W        device [m x ldw], element type w_dtype (bf16 or fp32); not
  *            modified.  m > 0, k > 0, k % 16 == 0, ldw >= k, ldw % 4 == 0.
- *   U        device fp32 [k x k] from factor_hinv (read unless NVQ_FLAG_RTN).
+ *   U        device fp32 [k x k] from factor_hinv, or from factor_chol with
+ *            NVQ_FLAG_CHOL_FACTOR (read unless NVQ_FLAG_RTN).
  *   H        device fp32 [k x k] symmetric (the undamped Hessian), read only
  *            for the weighted error; may be NULL with NVQ_FLAG_NO_ERR.
  *   g        device, 1 float: the per-tensor scale (e.g. nvfp4_global_scale).

@@ -25,12 +25,14 @@ FLAG_NO_ERR = 2
 FLAG_FP64 = 4
 FLAG_INDEP = 8
 FLAG_CHECK_FINITE = 16
+FLAG_CHOL_FACTOR = 32
 
 EXPORTS = [
     "hessian_workspace_size", "hessian_accumulate",
     "hessian_grouped_workspace_size", "hessian_accumulate_grouped",
     "hessian_host_workspace_size", "hessian_host_staging_size", "hessian_accumulate_host",
     "factor_hinv_workspace_size", "factor_hinv", "factor_hinv_batched",
+    "factor_chol_workspace_size", "factor_chol",
     "nvfp4_global_scale_workspace_size", "nvfp4_global_scale",
     "gptq_nvfp4_workspace_size", "gptq_nvfp4_quantize", "gptq_nvfp4_quantize_batched",
     "nvfp4_dequantize", "nvfp4_gemm_workspace_size", "nvfp4_gemm", "nvfp4_gemm_noalloc", "nvq_check_finite",
@@ -63,6 +65,8 @@ def _load():
                                                P, P, P, SZ, P]),
         "factor_hinv_workspace_size": (SZ, [I64]),
         "factor_hinv": (I32, [P, I64, F32, P, P, P, P, SZ, P]),
+        "factor_chol_workspace_size": (SZ, [I64]),
+        "factor_chol": (I32, [P, I64, F32, P, P, P, P, SZ, P]),
         "nvfp4_global_scale_workspace_size": (SZ, [I64, I64]),
         "nvfp4_global_scale": (I32, [P, I32, I64, I64, I64, P, P, SZ, P]),
         "gptq_nvfp4_workspace_size": (SZ, [I64, I64, U32]),
@@ -334,10 +338,30 @@ def check_finite(A):
     return status
 
 
-def quantize_layer(W, X, n_cand=16, damp_rel=0.01, flags=0):
-    """Whole layer: H = X^T X, U, g, the sweep and the weighted error (all on the GPU)."""
+def factor_chol(H, damp_rel=0.01, V=None, ws=None):
+    """Returns (V, lam, info) as device tensors: H + lam I = R R^T with R upper triangular,
+    V = -R_ij / R_jj above the diagonal, R_ii on it, 0 below (for FLAG_CHOL_FACTOR)."""
+    k = H.shape[0]
+    V = torch.empty_like(H) if V is None else V
+    lam = torch.empty(1, dtype=torch.float32, device=H.device)
+    info = torch.empty(1, dtype=torch.int32, device=H.device)
+    need = lib.factor_chol_workspace_size(k)
+    if ws is None or ws.numel() < need:
+        ws = _workspace(need, H.device)
+    _check("factor_chol", lib.factor_chol(_ptr(H), k, float(damp_rel), _ptr(V), _ptr(lam), _ptr(info), _ptr(ws),
+                                          need, _stream()))
+    return V, lam, info
+
+
+def quantize_layer(W, X, n_cand=16, damp_rel=0.01, flags=0, chol=False):
+    """Whole layer: H = X^T X, the factor (U from factor_hinv, or with chol V from factor_chol and
+    FLAG_CHOL_FACTOR), g, the sweep and the weighted error (all on the GPU)."""
     H = hessian_accumulate(X)
-    U, lam, info = factor_hinv(H, damp_rel)
+    if chol:
+        U, lam, info = factor_chol(H, damp_rel)
+        flags |= FLAG_CHOL_FACTOR
+    else:
+        U, lam, info = factor_hinv(H, damp_rel)
     g = nvfp4_global_scale(W)
     res = gptq_nvfp4_quantize(W, U, H, g, n_cand, flags)
     res.update(H=H, U=U, lam=lam, info=info, g=g)

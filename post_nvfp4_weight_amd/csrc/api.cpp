@@ -41,16 +41,20 @@ size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 struct QuantWs {
-  size_t wp, eslab, invd, part, total;
+  size_t wp, w0, eslab, invd, mb, part, total;
 };
 
-QuantWs quant_ws(int64_t m, int64_t k, bool f64) {
+// chol: the Cholesky-factor form also keeps the input weights in the working
+// precision (w0) and the diagonal blocks' M - I (mb, k * 16 floats).
+QuantWs quant_ws(int64_t m, int64_t k, bool f64, bool chol = false) {
   QuantWs w;
   const size_t es = f64 ? sizeof(double) : sizeof(float);
   size_t off = 0;
   w.wp = off;   off += align_up((size_t)m * k * es);
+  w.w0 = off;   if (chol) off += align_up((size_t)m * k * es);
   w.eslab = off; off += align_up((size_t)m * kSuperBatch * es);
   w.invd = off;  off += align_up((size_t)k * sizeof(float));
+  w.mb = off;    if (chol) off += align_up((size_t)k * kBlock * sizeof(float));
   w.part = off;  off += align_up((size_t)m * ((k + kGemmTile - 1) / kGemmTile) * sizeof(float));
   w.total = off;
   return w;
@@ -90,7 +94,8 @@ int quant_check(const char* fn, const void* W, int w_dtype, int64_t m, int64_t k
                 const uint8_t* scales, const float* row_err, const void* ws, size_t ws_bytes) {
   const bool rtn = flags & NVQ_FLAG_RTN;
   const bool want_err = !(flags & NVQ_FLAG_NO_ERR);
-  if (flags & ~(NVQ_FLAG_RTN | NVQ_FLAG_NO_ERR | NVQ_FLAG_FP64 | NVQ_FLAG_INDEP | NVQ_FLAG_CHECK_FINITE))
+  if (flags & ~(NVQ_FLAG_RTN | NVQ_FLAG_NO_ERR | NVQ_FLAG_FP64 | NVQ_FLAG_INDEP | NVQ_FLAG_CHECK_FINITE |
+                NVQ_FLAG_CHOL_FACTOR))
     return failp(NVQ_ERR_VALUE, fn, "unknown flags 0x%x", flags);
   if (!W || !g || !codes || !scales) return failp(NVQ_ERR_NULL, fn, "W, g, codes and scales are required");
   if (!rtn && !U) return failp(NVQ_ERR_NULL, fn, "U is required without NVQ_FLAG_RTN");
@@ -102,7 +107,7 @@ int quant_check(const char* fn, const void* W, int w_dtype, int64_t m, int64_t k
   if (n_cand < 1 || n_cand > 16) return failp(NVQ_ERR_NCAND, fn, "n_cand=%d", n_cand);
   if (!aligned(codes, 8)) return failp(NVQ_ERR_ALIGN, fn, "codes must be 8-byte aligned");
   if ((U && !aligned(U, 16)) || (H && !aligned(H, 16))) return failp(NVQ_ERR_ALIGN, fn, "U and H must be 16-byte aligned");
-  QuantWs L = quant_ws(m, k, (flags & NVQ_FLAG_FP64) && !rtn);
+  QuantWs L = quant_ws(m, k, (flags & NVQ_FLAG_FP64) && !rtn, (flags & NVQ_FLAG_CHOL_FACTOR) && !rtn);
   if (!ws || ws_bytes < L.total || !aligned(ws, kAlign))
     return failp(NVQ_ERR_WORKSPACE, fn, "workspace needs %zu bytes (256-aligned), got %zu", L.total, ws_bytes);
   return NVQ_OK;
@@ -147,10 +152,10 @@ hipError_t weighted_error_all(const void* W, int bf, int64_t m, int64_t k, int64
 // later column.
 hipError_t sweep_f32(int64_t m, int64_t k, const float* U, const float* g, int n_cand, bool indep, uint8_t* codes,
                      uint8_t* scales, float* row_loss, float* Wp, float* Eslab, const float* invd, const QBatch& qb,
-                     hipStream_t s) {
+                     hipStream_t s, const float* W0, const float* Mb) {
   const int64_t wsf = (int64_t)(qb.ws_stride / sizeof(float));
   SweepStrides bs;
-  bs.wp = wsf; bs.u = qb.stride_u; bs.invd = wsf; bs.e = wsf;
+  bs.wp = wsf; bs.u = qb.stride_u; bs.invd = wsf; bs.e = wsf; bs.mb = wsf;
   auto rank_update = [&](const float* Eb, int64_t r0, int64_t c0, int64_t kk, int64_t ncol) {
     GemmArgs a{};
     a.A = Eb; a.lda = kSuperBatch;
@@ -170,7 +175,7 @@ hipError_t sweep_f32(int64_t m, int64_t k, const float* U, const float* g, int n
     for (int64_t i1 = s0; e == hipSuccess && i1 < s1; i1 += kBatch) {
       const int ncols = (int)std::min<int64_t>(kBatch, s1 - i1);
       e = sweep_batch_launch(Wp, U, invd, g, m, k, (int)i1, ncols, n_cand, indep, codes, scales, Eslab + (i1 - s0),
-                             kSuperBatch, row_loss, s, qb.nb, bs, inblock ? (int)(i1 - s0) : 0);
+                             kSuperBatch, row_loss, s, qb.nb, bs, inblock ? (int)(i1 - s0) : 0, W0, Mb);
       const int64_t i2 = i1 + ncols;
       if (e == hipSuccess && !inblock && i2 < s1) e = rank_update(Eslab + (i1 - s0), i1, i2, ncols, s1 - i2);
     }
@@ -187,11 +192,13 @@ hipError_t quant_run(const void* W, int w_dtype, int64_t m, int64_t k, int64_t l
   const bool want_err = !(flags & NVQ_FLAG_NO_ERR);
   const bool f64 = (flags & NVQ_FLAG_FP64) && !rtn;
   const bool indep = flags & NVQ_FLAG_INDEP;
-  QuantWs L = quant_ws(m, k, f64);
+  const bool chol = (flags & NVQ_FLAG_CHOL_FACTOR) && !rtn;
+  QuantWs L = quant_ws(m, k, f64, chol);
   if (qb.ws_stride == 0) qb.ws_stride = L.total;
   float* Wp = (float*)(base + L.wp);
   float* Eslab = (float*)(base + L.eslab);
   float* invd = (float*)(base + L.invd);
+  float* Mb = chol ? (float*)(base + L.mb) : nullptr;
   float* part = (float*)(base + L.part);
   const int bf = w_dtype == NVQ_DTYPE_BF16;
   hipError_t e = hipSuccess;
@@ -201,18 +208,21 @@ hipError_t quant_run(const void* W, int w_dtype, int64_t m, int64_t k, int64_t l
   } else if (f64) {
     // The same sweep and two-level lazy updates with fp64 working weights and errors.
     double* Wd = (double*)(base + L.wp);
+    double* W0d = chol ? (double*)(base + L.w0) : nullptr;
     double* Ed = (double*)(base + L.eslab);
     const int64_t wsd = (int64_t)(qb.ws_stride / sizeof(double));
     SweepStrides bs;
-    bs.wp = wsd; bs.u = qb.stride_u; bs.e = wsd;
+    bs.wp = wsd; bs.u = qb.stride_u; bs.e = wsd; bs.mb = (int64_t)(qb.ws_stride / sizeof(float));
     e = load_working_copy_f64(W, bf, m, k, ldw, Wd, s, qb.nb, qb.stride_w, wsd);
+    if (e == hipSuccess && chol) e = chol_block_m_launch(U, k, Mb, s, qb.nb, qb.stride_u, bs.mb);
+    if (e == hipSuccess && chol) e = load_working_copy_f64(W, bf, m, k, ldw, W0d, s, qb.nb, qb.stride_w, wsd);
     if (e == hipSuccess && row_loss) e = fill_f32(row_loss, qb.nb * m, 0.0f, s);
     for (int64_t s0 = 0; e == hipSuccess && s0 < k; s0 += kSuperBatch) {
       const int64_t s1 = std::min<int64_t>(k, s0 + kSuperBatch);
       for (int64_t i1 = s0; e == hipSuccess && i1 < s1; i1 += kBatch) {
         const int ncols = (int)std::min<int64_t>(kBatch, s1 - i1);
         e = sweep_batch_launch_f64(Wd, U, g, m, k, (int)i1, ncols, n_cand, indep, codes, scales, Ed + (i1 - s0),
-                                   kSuperBatch, row_loss, s, qb.nb, bs);
+                                   kSuperBatch, row_loss, s, qb.nb, bs, W0d, Mb);
         const int64_t i2 = i1 + ncols;
         if (e == hipSuccess && i2 < s1)
           e = rank_update_f64(Ed + (i1 - s0), kSuperBatch, U + i1 * k + i2, k, Wd + i2, k, m, s1 - i2, ncols, s,
@@ -224,10 +234,14 @@ hipError_t quant_run(const void* W, int w_dtype, int64_t m, int64_t k, int64_t l
     }
   } else {
     const int64_t wsf = (int64_t)(qb.ws_stride / sizeof(float));
-    e = inv_diag_launch(U, k, invd, s, qb.nb, qb.stride_u, wsf);
+    float* W0 = chol ? (float*)(base + L.w0) : nullptr;
+    e = inv_diag_launch(U, k, invd, s, qb.nb, qb.stride_u, wsf, chol);
+    if (e == hipSuccess && chol) e = chol_block_m_launch(U, k, Mb, s, qb.nb, qb.stride_u, wsf);
     if (e == hipSuccess) e = load_working_copy(W, bf, m, k, ldw, Wp, s, qb.nb, qb.stride_w, wsf);
+    if (e == hipSuccess && chol) e = load_working_copy(W, bf, m, k, ldw, W0, s, qb.nb, qb.stride_w, wsf);
     if (e == hipSuccess && row_loss) e = fill_f32(row_loss, qb.nb * m, 0.0f, s);
-    if (e == hipSuccess) e = sweep_f32(m, k, U, g, n_cand, indep, codes, scales, row_loss, Wp, Eslab, invd, qb, s);
+    if (e == hipSuccess)
+      e = sweep_f32(m, k, U, g, n_cand, indep, codes, scales, row_loss, Wp, Eslab, invd, qb, s, W0, Mb);
   }
   if (e == hipSuccess && want_err)
     e = weighted_error_all(W, bf, m, k, ldw, H, g, codes, scales, row_err, Wp, part, qb, s);
@@ -525,6 +539,23 @@ int factor_hinv_batched(const float* H, int64_t k, int64_t batch, int64_t stride
                                        (hipStream_t)stream), fn);
 }
 
+size_t factor_chol_workspace_size(int64_t k) { return factor_hinv_workspace_size(k); }
+
+int factor_chol(const float* H, int64_t k, float damp_rel, float* V, float* lambda_out, int32_t* info, void* ws,
+                size_t ws_bytes, void* stream) {
+  const char* fn = "factor_chol";
+  if (!H || !V || !lambda_out || !info) return failp(NVQ_ERR_NULL, fn, "H, V, lambda_out and info are required");
+  if (k <= 0 || k % 16 != 0) return failp(NVQ_ERR_SHAPE, fn, "k=%lld (need k>0, k%%16==0)", (long long)k);
+  if (!(damp_rel >= 0.0f) || !std::isfinite(damp_rel)) return failp(NVQ_ERR_VALUE, fn, "damp_rel must be finite and >= 0");
+  if (H == V) return failp(NVQ_ERR_VALUE, fn, "V must not overlap H");
+  if (!aligned(H, 16) || !aligned(V, 16)) return failp(NVQ_ERR_ALIGN, fn, "H and V must be 16-byte aligned");
+  const size_t need = factor_chol_workspace_size(k);
+  if (!ws || ws_bytes < need || !aligned(ws, kAlign))
+    return failp(NVQ_ERR_WORKSPACE, fn, "workspace needs %zu bytes (256-aligned), got %zu", need, ws_bytes);
+  return hip_status(factor_hinv_launch(H, k, 1, k * k, damp_rel, V, k * k, lambda_out, info, ws, 1,
+                                       (hipStream_t)stream, true), fn);
+}
+
 // ---------------------------------------------------------------------------
 size_t nvfp4_global_scale_workspace_size(int64_t m, int64_t k) {
   return (m > 0 && k > 0) ? align_up((size_t)global_scale_parts(m, k) * sizeof(float)) : 0;
@@ -547,7 +578,8 @@ int nvfp4_global_scale(const void* W, int w_dtype, int64_t m, int64_t k, int64_t
 // ---------------------------------------------------------------------------
 size_t gptq_nvfp4_workspace_size(int64_t m, int64_t k, unsigned flags) {
   if (m <= 0 || k <= 0) return 0;
-  return quant_ws(m, k, (flags & NVQ_FLAG_FP64) && !(flags & NVQ_FLAG_RTN)).total;
+  const bool rtn = flags & NVQ_FLAG_RTN;
+  return quant_ws(m, k, (flags & NVQ_FLAG_FP64) && !rtn, (flags & NVQ_FLAG_CHOL_FACTOR) && !rtn).total;
 }
 
 int gptq_nvfp4_quantize(const void* W, int w_dtype, int64_t m, int64_t k, int64_t ldw, const float* U,
@@ -576,7 +608,7 @@ int gptq_nvfp4_quantize_batched(const void* W, int w_dtype, int64_t batch, int64
     return fail(NVQ_ERR_SHAPE, "gptq_nvfp4_quantize_batched: strides must cover one element (W: m*ldw, U and H: k*k, "
                                "multiples of 4)");
   // As many matrices per pass as the workspace holds (each launch covers all of them).
-  const QuantWs L = quant_ws(m, k, (flags & NVQ_FLAG_FP64) && !rtn);
+  const QuantWs L = quant_ws(m, k, (flags & NVQ_FLAG_FP64) && !rtn, (flags & NVQ_FLAG_CHOL_FACTOR) && !rtn);
   const int64_t chunk = std::max<int64_t>(1, std::min<int64_t>({batch, (int64_t)(ws_bytes / L.total), 65535}));
   const size_t es = w_dtype == NVQ_DTYPE_BF16 ? 2 : 4;
   QBatch qb;

@@ -490,6 +490,39 @@ __global__ void flip_out_kernel(const float* __restrict__ Linv, int64_t k, float
   *(f32x4*)(U + i * k + j) = v;
 }
 
+// The Cholesky factor itself, for the sweep's form without the inverse:
+// L = chol(J H_d J) is stored by the panel launches with its diagonal 64-blocks
+// in Ld and the rest of its lower part in A; R = J L J is upper triangular
+// with H_d = R R^T (R = U^-1).  V[i][j] = -R[i][j] / R[j][j] above the
+// diagonal, V[i][i] = R[i][i], 0 below.  Four columns j .. j+3 per thread
+// (they lie in one 64-block of L: k % 4 == 0), 16-byte loads and stores.
+// Matrix b = blockIdx.z: A + b * k^2, Ld + b * k^2 -> V + b * stride_v.
+__global__ void chol_out_kernel(const float* __restrict__ A, const float* __restrict__ Ld, int64_t k,
+                                float* __restrict__ V, int64_t stride_v) {
+  const int64_t i = blockIdx.y, j = 4 * ((int64_t)blockIdx.x * blockDim.x + threadIdx.x);
+  if (j >= k) return;
+  A += (int64_t)blockIdx.z * k * k;
+  Ld += (int64_t)blockIdx.z * k * k;
+  V += (int64_t)blockIdx.z * stride_v;
+  f32x4 v = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  if (j + 3 >= i) {
+    const int64_t r = k - 1 - i, c0 = k - 4 - j;   // L[r][c0 + 3 - u] = R[i][j + u]
+    const float* src = r / NB == c0 / NB ? Ld : A;
+    const f32x4 l = *(const f32x4*)(src + r * k + c0);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t jj = j + u;
+      if (jj == i) {
+        v[u] = l[3 - u];
+      } else if (jj > i) {
+        const int64_t d = k - 1 - jj;
+        v[u] = -l[3 - u] / Ld[d * k + d];
+      }
+    }
+  }
+  *(f32x4*)(V + i * k + j) = v;
+}
+
 }  // namespace
 
 size_t factor_workspace(int64_t k) {
@@ -526,7 +559,7 @@ static hipError_t helper_stream(hipStream_t* out) {
 // so a matrix's buffers sit at the same offsets whatever nb is.
 static hipError_t factor_pass(const float* H, int64_t k, int64_t nb, int64_t stride_h, float damp_rel, float* U,
                               int64_t stride_u, float* lambda_out, int32_t* info, float* ws, int64_t chunk,
-                              hipStream_t s) {
+                              bool chol, hipStream_t s) {
   const size_t kk = (size_t)k * k;
   float* A = ws;
   float* Linv = A + chunk * kk;
@@ -622,6 +655,11 @@ static hipError_t factor_pass(const float* H, int64_t k, int64_t nb, int64_t str
   if (rest_pending) e = hipStreamWaitEvent(s, ev_rest, 0);
   release();
   if (e != hipSuccess) return e;
+  if (chol) {   // the factor itself (scaled as the sweep takes it), no inverse
+    hipLaunchKernelGGL(chol_out_kernel, dim3((unsigned)((k / 4 + 255) / 256), (unsigned)k, nbu), dim3(256), 0, s, A,
+                       Linv, k, U, stride_u);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(diag_inv_kernel, dim3((unsigned)((k + NB - 1) / NB), nbu), dim3(64), 0, s, Linv, k);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -691,13 +729,13 @@ static hipError_t factor_pass(const float* H, int64_t k, int64_t nb, int64_t str
 
 hipError_t factor_hinv_launch(const float* H, int64_t k, int64_t batch, int64_t stride_h, float damp_rel, float* U,
                               int64_t stride_u, float* lambda_out, int32_t* info, void* ws, int64_t chunk,
-                              hipStream_t s) {
+                              hipStream_t s, bool chol) {
   if (chunk < 1) chunk = 1;
   chunk = min(chunk, factor_max_chunk(k));
   for (int64_t b0 = 0; b0 < batch; b0 += chunk) {
     const int64_t nb = min(chunk, batch - b0);
     hipError_t e = factor_pass(H + b0 * stride_h, k, nb, stride_h, damp_rel, U + b0 * stride_u, stride_u,
-                               lambda_out + b0, info + b0, (float*)ws, chunk, s);
+                               lambda_out + b0, info + b0, (float*)ws, chunk, chol, s);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

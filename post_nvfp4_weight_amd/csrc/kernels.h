@@ -76,10 +76,13 @@ size_t factor_workspace(int64_t k);
 // The largest number of matrices one pass takes (a grid-size limit).
 int64_t factor_max_chunk(int64_t k);
 // batch matrices H + b * stride_h -> U + b * stride_u, lambda_out[b], info[b],
-// `chunk` matrices per pass (ws holds chunk per-matrix workspaces).
+// `chunk` matrices per pass (ws holds chunk per-matrix workspaces).  With
+// chol, the output is V (the Cholesky factor R of H_d = R R^T with its
+// strictly upper part scaled to -R_ij / R_jj and R_ii on the diagonal)
+// instead of U = R^-1: no triangular inverse is formed.
 hipError_t factor_hinv_launch(const float* H, int64_t k, int64_t batch, int64_t stride_h, float damp_rel, float* U,
                               int64_t stride_u, float* lambda_out, int32_t* info, void* ws, int64_t chunk,
-                              hipStream_t s);
+                              hipStream_t s, bool chol = false);
 
 // ---- codec / sweep -----------------------------------------------------------
 // Batched launches (nb matrices, grid.y = matrix e) take per-matrix strides:
@@ -90,6 +93,7 @@ struct SweepStrides {
   int64_t u = 0;      // U (floats)
   int64_t invd = 0;   // 1 / U_jj (floats)
   int64_t e = 0;      // error slab (elements of the working type)
+  int64_t mb = 0;     // Cholesky-factor form: the diagonal blocks' M - I (floats)
 };
 hipError_t global_scale_launch(const void* W, int bf16, int64_t m, int64_t k, int64_t ldw,
                                float* g, float* partial, int nparts, hipStream_t s);
@@ -101,24 +105,37 @@ hipError_t rtn_launch(const void* W, int bf16, int64_t m, int64_t k, int64_t ldw
                       float* row_loss, hipStream_t s, int64_t nb = 1, int64_t stride_w = 0);
 hipError_t load_working_copy(const void* W, int bf16, int64_t m, int64_t k, int64_t ldw,
                              float* Wp, hipStream_t s, int64_t nb = 1, int64_t stride_w = 0, int64_t stride_wp = 0);
+// invd[j] = 1 / U_jj, or U_jj itself with copy (the Cholesky-factor form).
 hipError_t inv_diag_launch(const float* U, int64_t k, float* invd, hipStream_t s, int64_t nb = 1,
-                           int64_t stride_u = 0, int64_t stride_invd = 0);
+                           int64_t stride_u = 0, int64_t stride_invd = 0, bool copy = false);
 // indep: choose each block's scale by the block-independent squared rounding
 // error instead of the replay score (the committed block is still replayed).
 // pre (a multiple of 128, with sweep_applies_inblock(n_cand)): the batch's
 // columns have not yet received the errors of the pre columns before it in
 // its 512-column block, which the error slab holds just before Eslab; the
 // launch applies them to its rows first.  Otherwise pre must be 0.
+// W0 (non-null): the Cholesky-factor form.  U then holds V (-R_ij / R_jj
+// above the diagonal of the factor R of H_d = R R^T, R_jj on it), invd
+// holds R_jj, W0 the input weights in the working layout (as Wp before any
+// update) and Mb the blocks' M - I (chol_block_m_launch, stride bs.mb); a
+// committed column propagates w0_j - q_j and scores ((w'_j - q_j) R_jj)^2.
 hipError_t sweep_batch_launch(float* Wp, const float* U, const float* invd, const float* g,
                               int64_t m, int64_t k, int i1, int ncols, int n_cand, bool indep,
                               uint8_t* codes, uint8_t* scales, float* Eslab, int64_t lde, float* row_loss,
-                              hipStream_t s, int64_t nb = 1, const SweepStrides& bs = SweepStrides(), int pre = 0);
+                              hipStream_t s, int64_t nb = 1, const SweepStrides& bs = SweepStrides(), int pre = 0,
+                              const float* W0 = nullptr, const float* Mb = nullptr);
 bool sweep_applies_inblock(int n_cand);
 // The same sweep with fp64 working weights and errors (U read as fp32).
 hipError_t sweep_batch_launch_f64(double* Wp, const float* U, const float* g, int64_t m, int64_t k, int i1,
                                   int ncols, int n_cand, bool indep, uint8_t* codes, uint8_t* scales, double* Eslab,
                                   int64_t lde, float* row_loss, hipStream_t s, int64_t nb = 1,
-                                  const SweepStrides& bs = SweepStrides());
+                                  const SweepStrides& bs = SweepStrides(), const double* W0 = nullptr,
+                                  const float* Mb = nullptr);
+// Cholesky-factor form: for each diagonal 16x16 block of V, Mb[16 j + i] (j
+// the block's column, i < j) = (M - I)_ij with M = (I - N)^-1 and N the
+// block's strictly upper part (0 for i >= j); k * 16 floats per matrix.
+hipError_t chol_block_m_launch(const float* V, int64_t k, float* Mb, hipStream_t s, int64_t nb = 1,
+                               int64_t stride_v = 0, int64_t stride_m = 0);
 hipError_t load_working_copy_f64(const void* W, int bf16, int64_t m, int64_t k, int64_t ldw, double* Wp,
                                  hipStream_t s, int64_t nb = 1, int64_t stride_w = 0, int64_t stride_wp = 0);
 // Columns of the two-level lazy update: each 128-column batch updates the

@@ -372,12 +372,40 @@ __global__ void load_working_kernel(const void* __restrict__ W, int64_t m, int64
   *(f32x4*)(Wp + e) = v;
 }
 
+// invd[j] = 1 / U[j][j], or U[j][j] itself (copy: the diagonal of the
+// Cholesky-factor form, R_jj, by which the sweep multiplies).
 __global__ void inv_diag_kernel(const float* __restrict__ U, int64_t k, float* __restrict__ invd, int64_t stride_u,
-                                int64_t stride_invd) {
+                                int64_t stride_invd, int copy) {
   int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
   U += (int64_t)blockIdx.y * stride_u;   // matrix of a batch
   invd += (int64_t)blockIdx.y * stride_invd;
-  if (j < k) invd[j] = 1.0f / U[j * k + j];
+  if (j < k) invd[j] = copy ? U[j * k + j] : 1.0f / U[j * k + j];
+}
+
+// Cholesky-factor form: for each diagonal 16x16 block of V (N its strictly
+// upper part, N_ij = -R_ij / R_jj), M = (I - N)^-1, unit upper triangular,
+// found column by column by substitution (no divisions) in fp64.  Thread t
+// (block t / 16, column c = t % 16) writes Mt[t][i] = M_ic for i < c and 0
+// for i >= c: the transposed strictly upper part the sweep reads by columns.
+__global__ void chol_block_m_kernel(const float* __restrict__ V, int64_t k, float* __restrict__ Mt, int64_t stride_v,
+                                    int64_t stride_m) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  V += (int64_t)blockIdx.y * stride_v;
+  Mt += (int64_t)blockIdx.y * stride_m;
+  if (t >= k) return;
+  const int c = (int)(t % 16);
+  const float* vb = V + (t - c) * k + (t - c);   // the block's top-left element
+  double x[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) x[i] = i == c ? 1.0 : 0.0;
+  // (I - N) x = e_c: x_i = sum_{j > i} N_ij x_j, taking j downwards (x_j is
+  // final once every later column has added its part; x_j = 0 for j > c).
+#pragma unroll
+  for (int j = 15; j >= 1; --j)
+#pragma unroll
+    for (int i = 0; i < j; ++i) x[i] = fma((double)vb[(int64_t)i * k + j], x[j], x[i]);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) Mt[t * 16 + i] = i < c ? (float)x[i] : 0.0f;
 }
 
 // dW = W - dequant(codes, scales, g) as fp32 [m x k].
@@ -487,6 +515,22 @@ __device__ __forceinline__ void group_argmin(T& s, int& i) {
   if (G >= 8) argmin_step<kDppHalfMirror>(s, i);
   if (G >= 16) argmin_step<kDppMirror>(s, i);
 }
+template <int CTRL>
+__device__ __forceinline__ float max_step(float s) {
+  return fmaxf(s, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(s), CTRL, 0xF, 0xF, false)));
+}
+template <int CTRL>
+__device__ __forceinline__ double max_step(double s) {
+  return fmax(s, dpp_f64<CTRL>(s));
+}
+template <int G, typename T>
+__device__ __forceinline__ T group_max(T s) {
+  if (G >= 2) s = max_step<kDppXor1>(s);
+  if (G >= 4) s = max_step<kDppXor2>(s);
+  if (G >= 8) s = max_step<kDppHalfMirror>(s);
+  if (G >= 16) s = max_step<kDppMirror>(s);
+  return s;
+}
 template <int G, typename T>
 __device__ __forceinline__ T group_sum(T s) {
   if (G >= 2) s = sum_step<kDppXor1>(s);
@@ -509,16 +553,34 @@ __device__ __forceinline__ void load16(const T* p, T (&v)[16]) {
   for (int q = 0; q < 16; ++q) v[q] = p[q];
 }
 
-template <int G, typename T, bool INDEP>
+// CHOL: U holds V from the Cholesky factor R of H_d = R R^T (V_ij = -R_ij /
+// R_jj above the diagonal, V_jj = R_jj, so invd holds R_jj), and W0 the
+// weights as input.  The same updates are then taken as w'_l = w_l +
+// sum_{j<l} (w_j - q_j) R_jl / R_ll: a committed column propagates its raw
+// error w_j - q_j (against its input value) through V where the inverse form
+// propagates e_j = (w'_j - q_j) / U_jj through U, and its score term is
+// e_j = (w'_j - q_j) R_jj (U_jj = 1 / R_jj).  The error slab holds the
+// propagated values, so the lazy updates are unchanged.  Mid-block the two
+// forms hold different values for the columns not yet reached, and the
+// candidate window is set by the absmax of the inverse form's block-start
+// values a = w + P_{<c0} R_{<c0,B} U_BB.  With b the values held here and
+// U_BB = R_BB^-1 = D^-1 (I - N)^-1 (D = diag R_BB, N the strictly upper part
+// of V's diagonal block), a = b + (b - w)(M - I) with M = (I - N)^-1; Mb holds
+// each block's M - I transposed (chol_block_m_kernel), and the candidate
+// lanes of a row share the 16 columns of a before a group max.  A block whose
+// a is all zero takes q = 0 and propagates its input weights.
+template <int G, typename T, bool INDEP, bool CHOL>
 __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
-    T* __restrict__ Wp, const float* __restrict__ U, const float* __restrict__ invd,
+    T* __restrict__ Wp, const T* __restrict__ W0, const float* __restrict__ U, const float* __restrict__ invd,
     const float* __restrict__ gptr, int64_t m, int64_t k, int i1, int ncols, int n_cand,
     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, T* __restrict__ Eslab, int64_t lde,
-    float* __restrict__ row_loss, SweepStrides bs, int pre) {
+    float* __restrict__ row_loss, SweepStrides bs, int pre, const float* __restrict__ Mb) {
   constexpr bool F64 = sizeof(T) == 8;
   {   // matrix e = blockIdx.y of a batch
     const int64_t e = blockIdx.y;
     Wp += e * bs.wp;
+    if (CHOL) W0 += e * bs.wp;
+    if (CHOL) Mb += e * bs.mb;
     U += e * bs.u;
     invd += e * bs.invd;
     gptr += e;
@@ -532,6 +594,7 @@ __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
   __shared__ __attribute__((aligned(16))) float Ut[kBatch * UT_LD];      // Ut[c][r] = U[i1+r][i1+c]
   __shared__ __attribute__((aligned(16))) float Ud[kBatch / kBlock][kBlock][kBlock];  // diagonal 16x16 blocks
   __shared__ __attribute__((aligned(16))) float id_s[kBatch];
+  __shared__ __attribute__((aligned(16))) float Mt_s[CHOL ? kBatch / kBlock : 1][kBlock][kBlock];  // CHOL: M - I
   // Rows padded by 64 bytes: the four rows a wave touches fall on distinct banks.
   __shared__ __attribute__((aligned(16))) T slab[ROWS][kBatch + 64 / sizeof(T)];
   __shared__ __attribute__((aligned(16))) T eb_s[ROWS][16];
@@ -564,16 +627,16 @@ __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
   float idv[IDN];
 #pragma unroll
   for (int j = 0; j < IDN; ++j) idv[j] = invd[i1 + min(tid + j * NT, ncols - 1)];
-  auto slab_load = [&](int base, tvec (&w)[SCH]) {
+  auto slab_load_from = [&](const T* src, int base, tvec (&w)[SCH]) {
 #pragma unroll
     for (int it = 0; it < SCH; ++it) {
       const int idx = base + it * NT + tid;
       const int64_t gr = min(row0 + idx / (kBatch / VT), m - 1);
       const int c = min((idx % (kBatch / VT)) * VT, ncols - VT);
-      w[it] = *(const tvec*)(Wp + gr * k + i1 + c);
+      w[it] = *(const tvec*)(src + gr * k + i1 + c);
     }
   };
-  auto slab_store = [&](int base, const tvec (&w)[SCH]) {
+  auto slab_store_to = [&](T (*dst)[kBatch + 64 / sizeof(T)], int base, const tvec (&w)[SCH]) {
 #pragma unroll
     for (int it = 0; it < SCH; ++it) {
       const int idx = base + it * NT + tid;
@@ -582,9 +645,11 @@ __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
       tvec v;
 #pragma unroll
       for (int t = 0; t < VT; ++t) v[t] = ok ? w[it][t] : T(0);
-      *(tvec*)&slab[r][c] = v;
+      *(tvec*)&dst[r][c] = v;
     }
   };
+  auto slab_load = [&](int base, tvec (&w)[SCH]) { slab_load_from(Wp, base, w); };
+  auto slab_store = [&](int base, const tvec (&w)[SCH]) { slab_store_to(slab, base, w); };
   tvec w0[SCH];
   slab_load(0, w0);
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
@@ -616,6 +681,10 @@ __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
 #pragma unroll
   for (int j = 0; j < IDN; ++j)
     if (tid + j * NT < kBatch) id_s[tid + j * NT] = tid + j * NT < ncols ? idv[j] : 0.0f;
+  if constexpr (CHOL) {   // the batch's ncols / 16 blocks of M - I, 256 floats each
+    const f32x4* src = (const f32x4*)(Mb + (int64_t)i1 * kBlock);
+    for (int idx = tid; idx < ncols * (kBlock / 4); idx += NT) ((f32x4*)&Mt_s[0][0][0])[idx] = src[idx];
+  }
   for (int base = NT * SCH; base < SV; base += NT * SCH) {
     tvec w[SCH];
     slab_load(base, w);
@@ -698,6 +767,19 @@ __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
 
   T loss = 0;
   const int nblk = ncols / kBlock;
+  // CHOL: the row's input weights of a block, read one block ahead (16-byte
+  // loads; rows past m read row m-1, unused).
+  const T* w0row = CHOL ? W0 + min(row, m - 1) * k + i1 : nullptr;
+  auto load_w0 = [&](int c0, T (&o)[16]) {
+#pragma unroll
+    for (int q = 0; q < 16 / VT; ++q) {
+      const tvec t = *(const tvec*)(w0row + c0 + VT * q);
+#pragma unroll
+      for (int u = 0; u < VT; ++u) o[VT * q + u] = t[u];
+    }
+  };
+  T o_next[16];
+  if constexpr (CHOL) load_w0(0, o_next);
   for (int b = 0; b < nblk; ++b) {
     const int c0 = b * kBlock;
     T v[16];
@@ -710,13 +792,56 @@ __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
         v[4 * q] = t[0]; v[4 * q + 1] = t[1]; v[4 * q + 2] = t[2]; v[4 * q + 3] = t[3];
       }
     }
-    T a = 0;
+    T o[16];   // CHOL: the block's input weights
+    if constexpr (CHOL) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) a = fmax(a, fabs(v[j]));
+      for (int j = 0; j < 16; ++j) o[j] = o_next[j];
+      load_w0(min(c0 + kBlock, ncols - kBlock), o_next);
+    }
+    // The block-start values the candidate window (and the block-independent
+    // score) is taken on: v itself, or with CHOL a = v + (v - w)(M - I).
+    T a = 0;
+    T av[INDEP ? 16 : 1];
+    if constexpr (!CHOL) {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) a = fmax(a, fabs(v[j]));
+      if constexpr (INDEP) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) av[j] = v[j];
+      }
+    } else {
+      T d[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) d[j] = v[j] - o[j];
+      auto column = [&](int c, T vc) {   // a_c (Mt_s[b][c][j] = 0 for j >= c)
+        T acc = vc;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 m4 = *(const f32x4*)&Mt_s[b][c][4 * q];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) acc = fma(d[4 * q + u], (T)m4[u], acc);
+        }
+        return acc;
+      };
+      if constexpr (INDEP) {
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+          av[c] = column(c, v[c]);
+          a = fmax(a, fabs(av[c]));
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < 16 / G; ++t) {
+          const int c = ci + G * t;
+          a = fmax(a, fabs(column(c, slab[rl][c0 + c])));
+        }
+        a = group_max<G>(a);
+      }
+    }
 
     T e[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) e[j] = 0;
+    for (int j = 0; j < 16; ++j) e[j] = CHOL ? o[j] : T(0);   // CHOL: the propagated values when a = 0
     uint32_t plo = 0, phi = 0;
     int cand = 0;
     T score = F64 ? T(__builtin_inf()) : T(__builtin_inff());
@@ -734,8 +859,8 @@ __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           T dj;
-          if constexpr (F64) dj = v[j] - e2m1_dequant_f64(e2m1_encode(v[j], s, g), s, g);
-          else dj = v[j] - e2m1_dequant(e2m1_encode(v[j], s, g), s, g);
+          if constexpr (F64) dj = av[j] - e2m1_dequant_f64(e2m1_encode(av[j], s, g), s, g);
+          else dj = av[j] - e2m1_dequant(e2m1_encode(av[j], s, g), s, g);
           isc = fma(dj, dj, isc);
         }
       }
@@ -758,10 +883,12 @@ __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
           __builtin_amdgcn_sched_barrier(0x7);   // arithmetic may move across, memory accesses may not
         }
         int code;
-        T ej;
+        T ej, pj;   // the score term and the propagated value
         if constexpr (F64) {
           code = e2m1_encode(v[j], s, g);
-          ej = (v[j] - e2m1_dequant_f64(code, s, g)) / (T)Ud[b][j][j];
+          const T dq = e2m1_dequant_f64(code, s, g);
+          ej = CHOL ? (v[j] - dq) * (T)Ud[b][j][j] : (v[j] - dq) / (T)Ud[b][j][j];
+          pj = CHOL ? o[j] - dq : ej;
         } else {
           // The dequantized value e2m1_dequant gives, fl32(m * g) with the code's
           // sign set by a bit operation (m * g >= 0), then the error.  The
@@ -774,13 +901,14 @@ __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
           const float mg = e2m1_twice_mag(idx) * hs * g;
           const float dq = __uint_as_float(__float_as_uint(mg) | ((uint32_t)(code & 8) << 28));
           ej = (v[j] - dq) * id_s[c0 + j];
+          pj = CHOL ? o[j] - dq : ej;
         }
         sc = fma(ej, ej, sc);
         if (j + 1 < 16) {
 #pragma unroll
-          for (int l = j + 1; l < 16; ++l) v[l] = fma(-ej, (T)urow[l], v[l]);
+          for (int l = j + 1; l < 16; ++l) v[l] = fma(-pj, (T)urow[l], v[l]);
         }
-        e[j] = ej;
+        e[j] = pj;
         if (j < 8) plo |= (uint32_t)code << (4 * j); else phi |= (uint32_t)code << (4 * (j - 8));
       }
       rsc = sc;
@@ -825,29 +953,36 @@ __global__ __launch_bounds__(SweepCfg<G>::THREADS) void sweep_batch_kernel(
 }
 
 template <int G, typename T>
-hipError_t sweep_launch_g(T* Wp, const float* U, const float* invd, const float* g, int64_t m, int64_t k,
-                          int i1, int ncols, int n_cand, bool indep, uint8_t* codes, uint8_t* scales, T* Eslab,
-                          int64_t lde, float* row_loss, hipStream_t s, int64_t nb, const SweepStrides& bs, int pre) {
+hipError_t sweep_launch_g(T* Wp, const T* W0, const float* U, const float* invd, const float* g, int64_t m,
+                          int64_t k, int i1, int ncols, int n_cand, bool indep, uint8_t* codes, uint8_t* scales,
+                          T* Eslab, int64_t lde, float* row_loss, hipStream_t s, int64_t nb, const SweepStrides& bs,
+                          int pre, const float* Mb) {
   constexpr int ROWS = SweepCfg<G>::ROWS;
   if (!SweepCfg<G>::INBLOCK || sizeof(T) != 4) pre = 0;
   dim3 grid((unsigned)((m + ROWS - 1) / ROWS), (unsigned)nb);
-  if (indep)
-    hipLaunchKernelGGL((sweep_batch_kernel<G, T, true>), grid, dim3(SweepCfg<G>::THREADS), 0, s, Wp, U, invd, g, m,
-                       k, i1, ncols, n_cand, codes, scales, Eslab, lde, row_loss, bs, pre);
-  else
-    hipLaunchKernelGGL((sweep_batch_kernel<G, T, false>), grid, dim3(SweepCfg<G>::THREADS), 0, s, Wp, U, invd, g, m,
-                       k, i1, ncols, n_cand, codes, scales, Eslab, lde, row_loss, bs, pre);
+  const dim3 blk(SweepCfg<G>::THREADS);
+#define NVQ_SWEEP_LAUNCH(IND, CH)                                                                                  \
+  hipLaunchKernelGGL((sweep_batch_kernel<G, T, IND, CH>), grid, blk, 0, s, Wp, W0, U, invd, g, m, k, i1, ncols,     \
+                     n_cand, codes, scales, Eslab, lde, row_loss, bs, pre, Mb)
+  if (W0) {
+    if (indep) NVQ_SWEEP_LAUNCH(true, true); else NVQ_SWEEP_LAUNCH(false, true);
+  } else {
+    if (indep) NVQ_SWEEP_LAUNCH(true, false); else NVQ_SWEEP_LAUNCH(false, false);
+  }
+#undef NVQ_SWEEP_LAUNCH
   return hipGetLastError();
 }
 template <typename T>
-hipError_t sweep_launch_t(T* Wp, const float* U, const float* invd, const float* g, int64_t m, int64_t k, int i1,
+hipError_t sweep_launch_t(T* Wp, const T* W0, const float* U, const float* invd, const float* g, int64_t m, int64_t k, int i1,
                           int ncols, int n_cand, bool indep, uint8_t* codes, uint8_t* scales, T* Eslab, int64_t lde,
-                          float* row_loss, hipStream_t s, int64_t nb, const SweepStrides& bs, int pre) {
-  if (n_cand <= 1) return sweep_launch_g<1>(Wp, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s, nb, bs, pre);
-  if (n_cand <= 2) return sweep_launch_g<2>(Wp, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s, nb, bs, pre);
-  if (n_cand <= 4) return sweep_launch_g<4>(Wp, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s, nb, bs, pre);
-  if (n_cand <= 8) return sweep_launch_g<8>(Wp, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s, nb, bs, pre);
-  return sweep_launch_g<16>(Wp, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s, nb, bs, pre);
+                          float* row_loss, hipStream_t s, int64_t nb, const SweepStrides& bs, int pre,
+                          const float* Mb) {
+  if (W0 && !Mb) return hipErrorInvalidValue;
+  if (n_cand <= 1) return sweep_launch_g<1>(Wp, W0, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s, nb, bs, pre, Mb);
+  if (n_cand <= 2) return sweep_launch_g<2>(Wp, W0, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s, nb, bs, pre, Mb);
+  if (n_cand <= 4) return sweep_launch_g<4>(Wp, W0, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s, nb, bs, pre, Mb);
+  if (n_cand <= 8) return sweep_launch_g<8>(Wp, W0, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s, nb, bs, pre, Mb);
+  return sweep_launch_g<16>(Wp, W0, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s, nb, bs, pre, Mb);
 }
 
 }  // namespace
@@ -915,9 +1050,17 @@ hipError_t load_working_copy(const void* W, int bf16, int64_t m, int64_t k, int6
 }
 
 hipError_t inv_diag_launch(const float* U, int64_t k, float* invd, hipStream_t s, int64_t nb, int64_t stride_u,
-                           int64_t stride_invd) {
+                           int64_t stride_invd, bool copy) {
   hipLaunchKernelGGL(inv_diag_kernel, dim3((unsigned)((k + 255) / 256), (unsigned)nb), dim3(256), 0, s, U, k, invd,
-                     stride_u, stride_invd);
+                     stride_u, stride_invd, (int)copy);
+  return hipGetLastError();
+}
+
+hipError_t chol_block_m_launch(const float* V, int64_t k, float* Mb, hipStream_t s, int64_t nb, int64_t stride_v,
+                               int64_t stride_m) {
+  if (k % kBlock) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(chol_block_m_kernel, dim3((unsigned)((k + 255) / 256), (unsigned)nb), dim3(256), 0, s, V, k, Mb,
+                     stride_v, stride_m);
   return hipGetLastError();
 }
 
@@ -934,19 +1077,20 @@ hipError_t load_working_copy_f64(const void* W, int bf16, int64_t m, int64_t k, 
 hipError_t sweep_batch_launch(float* Wp, const float* U, const float* invd, const float* g, int64_t m, int64_t k,
                               int i1, int ncols, int n_cand, bool indep, uint8_t* codes, uint8_t* scales,
                               float* Eslab, int64_t lde, float* row_loss, hipStream_t s, int64_t nb,
-                              const SweepStrides& bs, int pre) {
-  return sweep_launch_t<float>(Wp, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s,
-                               nb, bs, pre);
+                              const SweepStrides& bs, int pre, const float* W0, const float* Mb) {
+  return sweep_launch_t<float>(Wp, W0, U, invd, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde,
+                               row_loss, s, nb, bs, pre, Mb);
 }
 bool sweep_applies_inblock(int n_cand) { return n_cand > 4; }
 hipError_t sweep_batch_launch_f64(double* Wp, const float* U, const float* g, int64_t m, int64_t k, int i1,
                                   int ncols, int n_cand, bool indep, uint8_t* codes, uint8_t* scales, double* Eslab,
-                                  int64_t lde, float* row_loss, hipStream_t s, int64_t nb, const SweepStrides& bs) {
+                                  int64_t lde, float* row_loss, hipStream_t s, int64_t nb, const SweepStrides& bs,
+                                  const double* W0, const float* Mb) {
   // the fp64 sweep divides by U_jj itself: invd is not read (U is passed in its place)
   SweepStrides b2 = bs;
   b2.invd = bs.u;
-  return sweep_launch_t<double>(Wp, U, U, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss, s,
-                                nb, b2, 0);
+  return sweep_launch_t<double>(Wp, W0, U, U, g, m, k, i1, ncols, n_cand, indep, codes, scales, Eslab, lde, row_loss,
+                                s, nb, b2, 0, Mb);
 }
 
 hipError_t delta_w_launch(const void* W, int bf16, int64_t m, int64_t k, int64_t ldw, const uint8_t* codes,

@@ -62,6 +62,17 @@ def test_host_validation_rejects_bad_arguments():
     # factor: negative damping, overlapping U
     assert lib.factor_hinv(fake, 32, ctypes.c_float(-1.0), P(8192), fake, fake, fake, 1 << 30, None) == -6
     assert lib.factor_hinv(fake, 32, ctypes.c_float(0.01), fake, fake, fake, fake, 1 << 30, None) == -6
+    # the Cholesky-factor form: the same checks, and a workspace too small
+    assert lib.factor_chol(fake, 32, ctypes.c_float(-1.0), P(8192), fake, fake, fake, 1 << 30, None) == -6
+    assert lib.factor_chol(fake, 32, ctypes.c_float(0.01), fake, fake, fake, fake, 1 << 30, None) == -6
+    assert lib.factor_chol(fake, 24, ctypes.c_float(0.01), P(8192), fake, fake, fake, 1 << 30, None) == -2
+    assert lib.factor_chol(fake, 32, ctypes.c_float(0.01), P(8192), fake, fake, P(1 << 20), 16, None) == -5
+    # with FLAG_CHOL_FACTOR the quantizer needs one more working copy of W
+    need = lib.gptq_nvfp4_workspace_size(16, 32, nvq.FLAG_CHOL_FACTOR)
+    assert need > lib.gptq_nvfp4_workspace_size(16, 32, 0)
+    rc = lib.gptq_nvfp4_quantize(fake, 1, 16, 32, 32, fake, fake, fake, 16, nvq.FLAG_CHOL_FACTOR, fake, fake, fake,
+                                 None, P(1 << 20), need - 256, None)
+    assert rc == -5
     # dequantize: bad k, bad dtype, empty is fine
     assert lib.nvfp4_dequantize(fake, fake, fake, 4, 8, fake, 0, None) == -2
     assert lib.nvfp4_dequantize(fake, fake, fake, 4, 32, fake, 5, None) == -3
@@ -97,7 +108,7 @@ def test_host_validation_rejects_bad_arguments():
     assert lib.nvq_check_finite(fake, 1, 4, 32, 16, fake, None) == -2
     assert lib.nvq_check_finite(fake, 1, -1, 32, 32, fake, None) == -2
     assert lib.nvq_check_finite(None, 1, 4, 32, 32, fake, None) == -1
-    rc = lib.gptq_nvfp4_quantize(fake, 1, 16, 32, 32, fake, fake, fake, 16, 32, fake, fake, fake, None,
+    rc = lib.gptq_nvfp4_quantize(fake, 1, 16, 32, 32, fake, fake, fake, 16, 64, fake, fake, fake, None,
                                  fake, 1 << 30, None)
     assert rc == -6 and b"flags" in lib.nvq_last_error()
     for s in (0, -1, -2, -3, -4, -5, -6, -7, -8, 99):
