@@ -185,7 +185,8 @@ def summarize_pmc(fetch_csv, write_csv):
     # The streaming kernels: per-launch bytes of the sweep (one 128-column
     # batch of the benchmarked layer) and of the pack kernels on the 70B-class
     # W (the largest launches of rtn_kernel and dequant_kernel in the run).
-    kinds = {"sweep_batch_kernel": "sweep_batch_kernel<16, float, false> (one 128-column batch, 4096 rows)",
+    kinds = {"sweep_batch_kernel": "sweep_batch_kernel<16, float, false, true> (Cholesky-factor form; one "
+                                   "128-column batch, 4096 rows)",
              "rtn_kernel": f"rtn_kernel<1> (W {PACK_M}x{PACK_K} bf16, one candidate)",
              "dequant_kernel": f"dequant_kernel<1> (W {PACK_M}x{PACK_K}, bf16 out)"}
     stream = {"commands": out["commands"], "workload": WORKLOAD, "unit": "bytes per launch",
@@ -740,9 +741,11 @@ def main():
     row_loss = torch.empty(M, dtype=torch.float32, device=dev)
     deq = torch.empty(M, K_IN, dtype=torch.bfloat16, device=dev)
     ws_h_n = lib.hessian_workspace_size(N_TOK, K_IN, nvq.NVQ_DTYPE_BF16)
-    ws_f_n = lib.factor_hinv_workspace_size(K_IN)
+    # The Cholesky-factor form: factor_chol (no triangular inverse) and the sweep on V.
+    qflags = nvq.FLAG_CHOL_FACTOR
+    ws_f_n = lib.factor_chol_workspace_size(K_IN)
     ws_g_n = lib.nvfp4_global_scale_workspace_size(M, K_IN)
-    ws_q_n = lib.gptq_nvfp4_workspace_size(M, K_IN, 0)
+    ws_q_n = lib.gptq_nvfp4_workspace_size(M, K_IN, qflags)
     ws = {n: torch.empty(max(1, b), dtype=torch.uint8, device=dev)
           for n, b in [("h", ws_h_n), ("f", ws_f_n), ("g", ws_g_n), ("q", ws_q_n)]}
 
@@ -759,12 +762,12 @@ def main():
         chk("hessian", lib.hessian_accumulate(P(Xd), nvq.NVQ_DTYPE_BF16, N_TOK, K_IN, K_IN, P(H), P(ws["h"]),
                                               ws_h_n, s))
         if ev: ev[1].record()
-        chk("factor", lib.factor_hinv(P(H), K_IN, 0.01, P(U), P(lam), P(info), P(ws["f"]), ws_f_n, s))
+        chk("factor", lib.factor_chol(P(H), K_IN, 0.01, P(U), P(lam), P(info), P(ws["f"]), ws_f_n, s))
         if ev: ev[2].record()
         chk("gscale", lib.nvfp4_global_scale(P(Wd), nvq.NVQ_DTYPE_BF16, M, K_IN, K_IN, P(g), P(ws["g"]), ws_g_n, s))
         if ev: ev[3].record()
         chk("quantize", lib.gptq_nvfp4_quantize(P(Wd), nvq.NVQ_DTYPE_BF16, M, K_IN, K_IN, P(U), P(H), P(g), N_CAND,
-                                                0, P(codes), P(scales), P(row_err), P(row_loss), P(ws["q"]),
+                                                qflags, P(codes), P(scales), P(row_err), P(row_loss), P(ws["q"]),
                                                 ws_q_n, s))
         if ev: ev[4].record()
         chk("dequant", lib.nvfp4_dequantize(P(codes), P(scales), P(g), M, K_IN, P(deq), nvq.NVQ_DTYPE_BF16, s))
@@ -824,7 +827,7 @@ def main():
         "ms_per_step": round(ms_per_step, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16-mfma/fp32", "data": "synthetic",
         "config": {"workload": WORKLOAD,
-                   "d_out": M, "d_in": K_IN, "tokens": N_TOK, "n_cand": N_CAND},
+                   "d_out": M, "d_in": K_IN, "tokens": N_TOK, "n_cand": N_CAND, "factor": "cholesky"},
         "roofline": roofline,
         "roofline_pack": roofline_pack,
         "stages_ms": {k: round(v, 3) for k, v in per_stage.items()},

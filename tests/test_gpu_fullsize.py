@@ -21,6 +21,11 @@ oracle recomputes what it can in seconds:
     weighted error agrees within 1e-3, and every row that diverges does so
     first at a near tie of the oracle's own decisions;
   * a second GPU run of the whole layer is bitwise identical to the first.
+The same holds for the Cholesky-factor form (factor_chol and
+NVQ_FLAG_CHOL_FACTOR, the calls the benchmark times): its V from the GPU's H
+matches the oracle's U inverted in fp64 to 1e-4, R R^T meets the fp32
+Cholesky backward-error bound against H + lam I, and its whole layer meets
+the same end-to-end bars against the same oracle sweep, reproducibly.
 """
 
 import numpy as np
@@ -63,6 +68,13 @@ def full():
     same = {key: bool(torch.equal(res[key].view(torch.uint8), again[key].view(torch.uint8)))
             for key in ("H", "U", "lam", "info", "g", "codes", "scales", "row_err", "row_loss")}
     del again
+    chol = nvq.quantize_layer(Wd, Xd, n_cand=N_CAND, chol=True)
+    torch.cuda.synchronize()
+    again = nvq.quantize_layer(Wd, Xd, n_cand=N_CAND, chol=True)
+    torch.cuda.synchronize()
+    same_chol = {key: bool(torch.equal(chol[key].view(torch.uint8), again[key].view(torch.uint8)))
+                 for key in ("H", "U", "lam", "info", "codes", "scales", "row_err", "row_loss")}
+    del again
     out = {
         "X": X, "W": W,
         "H": res["H"].cpu().numpy(), "U": res["U"].cpu().numpy(),
@@ -72,8 +84,12 @@ def full():
         "deq": deq.view(torch.int16).cpu().numpy(),
         "rtn_codes": rtn["codes"].cpu().numpy(), "rtn_scales": rtn["scales"].cpu().numpy(),
         "same": same,
+        "chol": {"V": chol["U"].cpu().numpy(), "H": chol["H"].cpu().numpy(), "lam": float(chol["lam"].item()),
+                 "info": int(chol["info"].item()), "codes": codec.unpack_codes(chol["codes"].cpu().numpy()),
+                 "scales": chol["scales"].cpu().numpy(),
+                 "row_err": chol["row_err"].cpu().numpy().astype(np.float64), "same": same_chol},
     }
-    del Xd, Wd, res
+    del Xd, Wd, res, chol
     torch.cuda.empty_cache()
     return out
 
@@ -103,6 +119,28 @@ def test_full_factor(full):
     U = full["U"]
     assert np.all(np.tril(U, -1) == 0)
     assert np.max(np.abs(U - Uref)) <= 1e-4 * np.max(np.abs(Uref))
+
+
+def test_full_factor_chol(full):
+    c = full["chol"]
+    assert c["info"] == 0
+    assert np.array_equal(c["H"], full["H"])
+    H = c["H"].astype(np.float64)
+    Uref, lam = gptq.hinv_factor(H)
+    assert c["lam"] == pytest.approx(lam, rel=1e-5)
+    Rref = np.triu(np.linalg.inv(Uref))
+    dref = np.diag(Rref)
+    V = c["V"].astype(np.float64)
+    assert np.all(np.tril(V, -1) == 0)
+    d = np.diag(V)
+    assert np.max(np.abs(d - dref)) <= 1e-4 * np.max(dref)
+    off, offref = np.triu(V, 1), np.triu(-Rref / dref[None, :], 1)
+    assert np.max(np.abs(off - offref)) <= 1e-4 * np.max(np.abs(offref))
+    R = off * (-d[None, :]) + np.diag(d)
+    Hd = H + np.float64(np.float32(c["lam"])) * np.eye(K_IN)
+    gamma = (K_IN + 1) * 2.0 ** -24 / (1 - (K_IN + 1) * 2.0 ** -24)
+    bound = 2.0 * gamma * (np.abs(R) @ np.abs(R).T) + 4 * 2.0 ** -24 * np.abs(Hd)
+    assert np.all(np.abs(R @ R.T - Hd) <= bound)
 
 
 def test_full_global_scale_and_rtn(full):
@@ -142,6 +180,7 @@ def test_full_dequant_bf16_sampled_rows(full):
 
 def test_full_layer_bitwise_reproducible(full):
     assert all(full["same"].values()), full["same"]
+    assert all(full["chol"]["same"].values()), full["chol"]["same"]
 
 
 MIDPOINTS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
@@ -183,20 +222,21 @@ def test_full_layer_matches_oracle_end_to_end(full):
     Uref, lam = gptq.hinv_factor(Href)
     assert full["lam"] == pytest.approx(lam, rel=1e-5)
     ref = gptq.sweep(W, Uref, g, N_CAND, dtype=np.float64)
-    codes, scales = full["codes"], full["scales"]
-    cm = _mismatch(codes, ref["codes"])
-    sm = _mismatch(scales, ref["scales"])
     deq_ref = codec.dequantize(codec.pack_codes(ref["codes"]), ref["scales"], g)
     E_ref = gptq.weighted_error(W, deq_ref, Href).sum()
-    E_gpu = full["row_err"].sum()
-    print(f"whole layer: code mismatch {cm:.2e}, scale mismatch {sm:.2e}, E gpu {E_gpu:.8g} oracle {E_ref:.8g} "
-          f"(rel {abs(E_gpu - E_ref) / E_ref:.2e})")
-    assert cm <= 1e-3 and sm <= 1e-3
-    assert abs(E_gpu - E_ref) <= 1e-3 * E_ref
-    # every diverging row starts at a near tie of the oracle's decisions
-    div = np.nonzero(np.any(codes != ref["codes"], axis=1) | np.any(scales != ref["scales"], axis=1))[0]
-    print(f"{len(div)} of {M} rows diverge")
-    if len(div):
-        tr = gptq.sweep(W[div], Uref, g, N_CAND, dtype=np.float64, trace=True)
-        for i, r in enumerate(div):
-            _first_divergence_is_near_tie(codes[r], scales[r], tr, i, g)
+    for form, out in (("inverse", full), ("cholesky", full["chol"])):
+        codes, scales = out["codes"], out["scales"]
+        cm = _mismatch(codes, ref["codes"])
+        sm = _mismatch(scales, ref["scales"])
+        E_gpu = out["row_err"].sum()
+        print(f"whole layer ({form} form): code mismatch {cm:.2e}, scale mismatch {sm:.2e}, E gpu {E_gpu:.8g} "
+              f"oracle {E_ref:.8g} (rel {abs(E_gpu - E_ref) / E_ref:.2e})")
+        assert cm <= 1e-3 and sm <= 1e-3, form
+        assert abs(E_gpu - E_ref) <= 1e-3 * E_ref, form
+        # every diverging row starts at a near tie of the oracle's decisions
+        div = np.nonzero(np.any(codes != ref["codes"], axis=1) | np.any(scales != ref["scales"], axis=1))[0]
+        print(f"{len(div)} of {M} rows diverge ({form} form)")
+        if len(div):
+            tr = gptq.sweep(W[div], Uref, g, N_CAND, dtype=np.float64, trace=True)
+            for i, r in enumerate(div):
+                _first_divergence_is_near_tie(codes[r], scales[r], tr, i, g)
