@@ -218,10 +218,13 @@ def test_full_layer_matches_oracle_end_to_end(full):
     bound = absX * ((N_TOK / 16 + 64) * 2.0 ** -23)
     assert np.all(np.abs(full["H"].astype(np.float64) - Href) <= bound + 1e-30)
     del absX, bound
+    print("oracle H over all tokens: every GPU entry within the bound", flush=True)
     # its own factor and its own sweep of every row
     Uref, lam = gptq.hinv_factor(Href)
     assert full["lam"] == pytest.approx(lam, rel=1e-5)
+    print("oracle factor done; oracle sweep of every row", flush=True)
     ref = gptq.sweep(W, Uref, g, N_CAND, dtype=np.float64)
+    print("oracle sweep done", flush=True)
     deq_ref = codec.dequantize(codec.pack_codes(ref["codes"]), ref["scales"], g)
     E_ref = gptq.weighted_error(W, deq_ref, Href).sum()
     for form, out in (("inverse", full), ("cholesky", full["chol"])):
@@ -235,7 +238,7 @@ def test_full_layer_matches_oracle_end_to_end(full):
         assert abs(E_gpu - E_ref) <= 1e-3 * E_ref, form
         # every diverging row starts at a near tie of the oracle's decisions
         div = np.nonzero(np.any(codes != ref["codes"], axis=1) | np.any(scales != ref["scales"], axis=1))[0]
-        print(f"{len(div)} of {M} rows diverge ({form} form)")
+        print(f"{len(div)} of {M} rows diverge ({form} form)", flush=True)
         if len(div):
             tr = gptq.sweep(W[div], Uref, g, N_CAND, dtype=np.float64, trace=True)
             for i, r in enumerate(div):
