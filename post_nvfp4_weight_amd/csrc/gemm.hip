@@ -319,9 +319,17 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
 // is one 16-byte read; a [K][N] B is transposed on its way in, each thread
 // turning a 4 x 4 block, and a [N][K] B is stored like A.  With LOWER the
 // workgroups of tiles wholly above the diagonal exit (square C).
+// With NP = 2 the operands are split into two parts, x = x1 + x2 + r with
+// |r| <= 2^-16 |x|, and a product sums the three part products x1y1, x1y2,
+// x2y1 (the dropped x2y2 is below 2^-16 of |x y|): half the products and
+// two thirds of the operand stores of NP = 3.  Only the weighted error
+// (the row-dot epilogue) takes it: an error of about 2^-16 per product there
+// moves a row's dW H' dW^T by a few parts in a million, and no quantization
+// decision depends on it.
 constexpr int X6_T = 128, X6_LD = BK + 8;                 // bf16 row stride of a part
 constexpr int X6_PART = X6_T * X6_LD;                     // bf16 elements of one part
-constexpr int X6_BUF = 6 * X6_PART;                       // A parts, then B parts
+template <int NP>
+constexpr int x6_buf() { return 2 * NP * X6_PART; }     // A parts, then B parts
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -335,21 +343,24 @@ __device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& h, uint
   l = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{s0, s1}, bf16x2));
 }
 // Four consecutive-k values of one row -> 8 bytes at element offset off of
-// each of the three parts.
+// each of the NP parts (the two-part split is the first two of the three).
+template <int NP>
 __device__ __forceinline__ void put4(uint16_t* base, int off, const f32x4& v) {
   uint32_t h0, m0, l0, h1, m1, l1;
   split_pair(v[0], v[1], h0, m0, l0);
   split_pair(v[2], v[3], h1, m1, l1);
   *(u32x2*)(base + off) = u32x2{h0, h1};
   *(u32x2*)(base + X6_PART + off) = u32x2{m0, m1};
-  *(u32x2*)(base + 2 * X6_PART + off) = u32x2{l0, l1};
+  if (NP == 3) *(u32x2*)(base + 2 * X6_PART + off) = u32x2{l0, l1};
 }
 // B is stored transposed, [column][k]; its 16-byte k chunks are XOR-swizzled
 // by (column / 16) % 4, which spreads the transposing writes over the banks.
 __device__ __forceinline__ int x6_boff(int n, int k) { return n * X6_LD + ((((k >> 3) ^ (n >> 4)) & 3) << 3) + (k & 7); }
 
-template <int EPI, bool TB, bool LOWER>
+template <int EPI, bool TB, bool LOWER, int NP>
 __global__ __launch_bounds__(256) void gemm_x6_kernel(GemmArgs p) {
+  static_assert(NP == 2 || NP == 3, "two or three bf16 parts");
+  constexpr int X6_BUF = x6_buf<NP>();
   constexpr int WT = X6_T / 2;
   const int nt = (int)gridDim.x, mt = (int)gridDim.y;
   const int lin = (int)blockIdx.y * nt + (int)blockIdx.x;
@@ -451,11 +462,11 @@ __global__ __launch_bounds__(256) void gemm_x6_kernel(GemmArgs p) {
     if (idx < 4) {
       const int q = idx, e = q * 256 + tid, r = e >> 3, kk = (e & 7) * 4;
       const bool ok = sm0 + r < sM && k0 + kk < sK;
-      put4(buf, r * X6_LD + kk, ok ? ra[q] * alpha_a : f32x4{0.f, 0.f, 0.f, 0.f});
+      put4<NP>(buf, r * X6_LD + kk, ok ? ra[q] * alpha_a : f32x4{0.f, 0.f, 0.f, 0.f});
     } else if (TB) {
       const int q = idx - 4, e = q * 256 + tid, r = e >> 3, kk = (e & 7) * 4;
       const bool ok = sn0 + r < sN && k0 + kk < sK;
-      put4(buf + 3 * X6_PART, x6_boff(r, kk), ok ? rb[q] : f32x4{0.f, 0.f, 0.f, 0.f});
+      put4<NP>(buf + NP * X6_PART, x6_boff(r, kk), ok ? rb[q] : f32x4{0.f, 0.f, 0.f, 0.f});
     } else {
       const int j = idx - 4, gn = sn0 + bn;
       f32x4 v;
@@ -469,7 +480,7 @@ __global__ __launch_bounds__(256) void gemm_x6_kernel(GemmArgs p) {
         }
         v[i] = x;
       }
-      put4(buf + 3 * X6_PART, x6_boff(bn + j, bk), v);
+      put4<NP>(buf + NP * X6_PART, x6_boff(bn + j, bk), v);
     }
   };
   auto store_chunk = [&](uint16_t* buf, int k0, const f32x4 (&ra)[4], const f32x4 (&rb)[4]) {
@@ -488,9 +499,9 @@ __global__ __launch_bounds__(256) void gemm_x6_kernel(GemmArgs p) {
       base = buf; off = (e >> 3) * X6_LD + (e & 7) * 4;
     } else if (TB) {
       const int e = (idx - 4) * 256 + tid;
-      base = buf + 3 * X6_PART; off = x6_boff(e >> 3, (e & 7) * 4);
+      base = buf + NP * X6_PART; off = x6_boff(e >> 3, (e & 7) * 4);
     } else {
-      base = buf + 3 * X6_PART; off = x6_boff(bn + idx - 4, bk);
+      base = buf + NP * X6_PART; off = x6_boff(bn + idx - 4, bk);
     }
     if (st == 0) {
       if (idx < 4) {
@@ -524,6 +535,8 @@ __global__ __launch_bounds__(256) void gemm_x6_kernel(GemmArgs p) {
       mm0 = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{r[0], r[1]}, bf16x2));
       mm1 = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{r[2], r[3]}, bf16x2));
       *(u32x2*)(base + off) = u32x2{h0, h1};
+    } else if (NP == 2) {   // stage 4 stores the second (last) parts; stage 5 has nothing left
+      if (st == 4) *(u32x2*)(base + X6_PART + off) = u32x2{mm0, mm1};
     } else if (st == 4) {
       r[0] -= __uint_as_float(mm0 << 16); r[1] -= __uint_as_float(mm0 & 0xFFFF0000u);
       r[2] -= __uint_as_float(mm1 << 16); r[3] -= __uint_as_float(mm1 & 0xFFFF0000u);
@@ -548,23 +561,28 @@ __global__ __launch_bounds__(256) void gemm_x6_kernel(GemmArgs p) {
   __syncthreads();
   // Lane l reads rows (l % 32) and k offset 8 (l / 32) of each 32-row block.
   const int arow = wr * WT + (lane & 31), brow = wc * WT + (lane & 31), koff = 8 * (lane >> 5);
-  constexpr int PA[6] = {2, 1, 0, 1, 0, 0}, PB[6] = {0, 1, 2, 0, 1, 0};   // part products, smallest first
+  // Part products, smallest first: NPR of them per 32 x 32 accumulator and
+  // k-step, 4 NPR MFMAs per k-step, each followed by SPS of the 48 store
+  // stages of the next chunk (8 pieces of 6).
+  constexpr int NPR = NP == 3 ? 6 : 3, SPS = 48 / (8 * NPR);
+  constexpr int PA[6] = {NP == 3 ? 2 : 1, NP == 3 ? 1 : 0, 0, 1, 0, 0};
+  constexpr int PB[6] = {0, 1, NP == 3 ? 2 : 0, 0, 1, 0};
   static_assert(BK == 32, "two 16-deep k-steps per chunk");
   // As (the buffer being multiplied) and nbuf (the idle one) are distinct,
   // which the restrict qualifiers state: the stores into nbuf need not wait
   // for the fragment reads from As.
   auto body = [&](const uint16_t* __restrict__ As, uint16_t* __restrict__ nbuf, int64_t c, f32x4 (&ra)[4],
                   f32x4 (&rb)[4]) {
-    const uint16_t* Bs = As + 3 * X6_PART;
+    const uint16_t* Bs = As + NP * X6_PART;
     const int kn = (int)((c + 1) * BK);
-    bf16x8 a[2][3][2], b[2][3][2];   // [k-step][part][32-row block]
-    auto read = [&](int h, int f) {   // fragment f (0..11) of k-step h
+    bf16x8 a[2][NP][2], b[2][NP][2];   // [k-step][part][32-row block]
+    auto read = [&](int h, int f) {   // fragment f (0..4 NP - 1) of k-step h
       const int pt = f >> 2, t = (f >> 1) & 1, ks = 16 * h;
       if (f & 1) b[h][pt][t] = *(const bf16x8*)(Bs + pt * X6_PART + x6_boff(brow + 32 * t, ks + koff));
       else a[h][pt][t] = *(const bf16x8*)(As + pt * X6_PART + (arow + 32 * t) * X6_LD + ks + koff);
     };
 #pragma unroll
-    for (int f = 0; f < 12; ++f) read(0, f);
+    for (int f = 0; f < 4 * NP; ++f) read(0, f);
     // Per k-step: 24 products (the four accumulators take turns, so that no
     // MFMA waits for the one before it).  Behind each product comes one stage
     // of the next chunk's store (6 stages for each of its 8 pieces, a few
@@ -579,15 +597,18 @@ __global__ __launch_bounds__(256) void gemm_x6_kernel(GemmArgs p) {
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int m = 0; m < 24; ++m) {
+      for (int m = 0; m < 4 * NPR; ++m) {
         const int pp = m >> 2, i = (m >> 1) & 1, j = m & 1;
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[h][PA[pp]][i], b[h][PB[pp]][j], acc[i][j], 0, 0, 0);
-        if (h == 0 && m < 12) read(1, m);
-        const int g = 24 * h + m;
-        store_stage(nbuf, kn, ra, rb, g / 6, g % 6, sv, sh0, sh1, sm0_, sm1_, sr);
-        if (g % 6 == 1 && g < 24) load_a((c + 3) * BK, ra, g / 6);
-        if (TB && g % 6 == 1 && g >= 24) load_b((c + 3) * BK, rb, g / 6 - 4);
-        if (!TB && g >= 43 && g < 47) load_b((c + 3) * BK, rb, g - 43);
+        if (h == 0 && m < 4 * NP) read(1, m);
+#pragma unroll
+        for (int u = 0; u < SPS; ++u) {
+          const int g = SPS * (4 * NPR * h + m) + u;
+          store_stage(nbuf, kn, ra, rb, g / 6, g % 6, sv, sh0, sh1, sm0_, sm1_, sr);
+          if (g % 6 == 1 && g < 24) load_a((c + 3) * BK, ra, g / 6);
+          if (TB && g % 6 == 1 && g >= 24) load_b((c + 3) * BK, rb, g / 6 - 4);
+          if (!TB && g >= 43 && g < 47) load_b((c + 3) * BK, rb, g - 43);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
   };
@@ -706,7 +727,7 @@ hipError_t launch(const GemmArgs& a, hipStream_t s) {
     if (!TB || a.kmode == kGemmKFull) {
       dim3 grid((unsigned)((a.N + X6_T - 1) / X6_T), (unsigned)((a.M + X6_T - 1) / X6_T),
                 (unsigned)(a.batch * (a.ksplit == 2 ? 2 : 1)));
-      hipLaunchKernelGGL((gemm_x6_kernel<EPI, TB, LOWER>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((gemm_x6_kernel<EPI, TB, LOWER, EPI == kEpiRowDot ? 2 : 3>), grid, dim3(256), 0, s, a);
       return hipGetLastError();
     }
   }
