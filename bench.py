@@ -493,8 +493,9 @@ def workload_line(name, steps, warmup):
 
 
 def moe_line(steps, warmup):
-    """The MoE layer: grouped Hessians over routed tokens, batched factors, per-expert global scales,
-    batched quantization (fp32 sweep) and dequantization of all 256 experts; Mparam/s over all experts."""
+    """The MoE layer: grouped Hessians over routed tokens, batched Cholesky factors (factor_chol_batched,
+    no triangular inverse), per-expert global scales, batched quantization (fp32 sweep on V) and
+    dequantization of all 256 experts; Mparam/s over all experts."""
     import torch
     import post_nvfp4_weight_amd as nvq
     import synth
@@ -525,10 +526,11 @@ def moe_line(steps, warmup):
     row_err = torch.empty(E, m, dtype=torch.float32, device=dev)
     row_loss = torch.empty(E, m, dtype=torch.float32, device=dev)
     deq = torch.empty(E, m, k, dtype=torch.bfloat16, device=dev)
-    # factors: 64 experts per pass (64 x 160 MiB); quantization: all 256 in one pass (256 x 36 MiB)
+    # factors: 64 experts per pass (64 x 160 MiB); quantization: all 256 in one pass (256 x 68 MiB)
+    qflags = nvq.FLAG_CHOL_FACTOR
     wn = {"h": lib.hessian_grouped_workspace_size(offc, E, k, nvq.NVQ_DTYPE_BF16),
-          "f": 64 * lib.factor_hinv_workspace_size(k), "g": lib.nvfp4_global_scale_workspace_size(m, k),
-          "q": E * lib.gptq_nvfp4_workspace_size(m, k, 0)}
+          "f": 64 * lib.factor_chol_workspace_size(k), "g": lib.nvfp4_global_scale_workspace_size(m, k),
+          "q": E * lib.gptq_nvfp4_workspace_size(m, k, qflags)}
     ws = {a: torch.empty(max(1, b), dtype=torch.uint8, device=dev) for a, b in wn.items()}
 
     def chk(name, rc):
@@ -542,7 +544,7 @@ def moe_line(steps, warmup):
         chk("hessian", lib.hessian_accumulate_grouped(P(Xd), nvq.NVQ_DTYPE_BF16, n, k, k, P(idx_d), offc, E, P(H),
                                                       P(ws["h"]), wn["h"], s))
         if ev: ev[1].record()
-        chk("factor", lib.factor_hinv_batched(P(H), k, E, k * k, 0.01, P(U), k * k, P(lam), P(info), P(ws["f"]),
+        chk("factor", lib.factor_chol_batched(P(H), k, E, k * k, 0.01, P(U), k * k, P(lam), P(info), P(ws["f"]),
                                               wn["f"], s))
         if ev: ev[2].record()
         for e in range(E):
@@ -550,7 +552,7 @@ def moe_line(steps, warmup):
                                                  wn["g"], s))
         if ev: ev[3].record()
         chk("quantize", lib.gptq_nvfp4_quantize_batched(P(Wt), nvq.NVQ_DTYPE_BF16, E, m, k, k, m * k, P(U), k * k,
-                                                        P(H), k * k, P(g), N_CAND, 0, P(codes), P(scales),
+                                                        P(H), k * k, P(g), N_CAND, qflags, P(codes), P(scales),
                                                         P(row_err), P(row_loss), P(ws["q"]), wn["q"], s))
         if ev: ev[4].record()
         for e in range(E):

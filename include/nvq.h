@@ -277,6 +277,23 @@ int factor_hinv_batched(const float* H, int64_t k, int64_t batch, int64_t stride
                         void* stream);
 
 /*
+ * factor_chol_batched -- factor_chol of `batch` matrices (one per expert of a
+ * mixture-of-experts layer; "Replay the Curvature", Abstract: GPTQ, in which
+ * quantizing one column updates those that follow): H + e*stride_h ->
+ * V + e*stride_v, lambda_out[e], info[e], each as factor_chol gives it.
+ * Strides count floats, are >= k*k and multiples of 4; the V and H ranges
+ * must not overlap.
+ *   ws  at least factor_chol_workspace_size(k) bytes; c times that lets one
+ *       pass factor c matrices together (every launch covers all matrices of
+ *       the pass).  Results do not depend on c: each matrix gets the bits
+ *       factor_chol gives it alone.
+ * batch = 0 is a no-op; nothing is enqueued when an argument is rejected.
+ */
+int factor_chol_batched(const float* H, int64_t k, int64_t batch, int64_t stride_h, float damp_rel, float* V,
+                        int64_t stride_v, float* lambda_out, int32_t* info, void* ws, size_t ws_bytes,
+                        void* stream);
+
+/*
  * nvfp4_global_scale -- per-tensor fp32 scale applied on top of the E4M3 block
  * scales: g = fl32(max|W| / 2688) (2688 = 6 * 448, the largest E2M1 magnitude
  * times the largest finite E4M3 value), or g = 1 when W is all zero.

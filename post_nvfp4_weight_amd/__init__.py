@@ -32,7 +32,7 @@ EXPORTS = [
     "hessian_grouped_workspace_size", "hessian_accumulate_grouped",
     "hessian_host_workspace_size", "hessian_host_staging_size", "hessian_accumulate_host",
     "factor_hinv_workspace_size", "factor_hinv", "factor_hinv_batched",
-    "factor_chol_workspace_size", "factor_chol",
+    "factor_chol_workspace_size", "factor_chol", "factor_chol_batched",
     "nvfp4_global_scale_workspace_size", "nvfp4_global_scale",
     "gptq_nvfp4_workspace_size", "gptq_nvfp4_quantize", "gptq_nvfp4_quantize_batched",
     "nvfp4_dequantize", "nvfp4_gemm_workspace_size", "nvfp4_gemm", "nvfp4_gemm_noalloc", "nvq_check_finite",
@@ -67,6 +67,7 @@ def _load():
         "factor_hinv": (I32, [P, I64, F32, P, P, P, P, SZ, P]),
         "factor_chol_workspace_size": (SZ, [I64]),
         "factor_chol": (I32, [P, I64, F32, P, P, P, P, SZ, P]),
+        "factor_chol_batched": (I32, [P, I64, I64, I64, F32, P, I64, P, P, P, SZ, P]),
         "nvfp4_global_scale_workspace_size": (SZ, [I64, I64]),
         "nvfp4_global_scale": (I32, [P, I32, I64, I64, I64, P, P, SZ, P]),
         "gptq_nvfp4_workspace_size": (SZ, [I64, I64, U32]),
@@ -303,6 +304,23 @@ def factor_hinv_batched(H, damp_rel=0.01, max_ws_bytes=8 << 30):
                                                           U.stride(0), _ptr(lam), _ptr(info), _ptr(ws), need,
                                                           _stream()))
     return U, lam, info
+
+
+def factor_chol_batched(H, damp_rel=0.01, max_ws_bytes=8 << 30):
+    """H: [B, k, k] -> (V [B, k, k], lam [B], info [B]) as device tensors, each V as
+    factor_chol gives it (for FLAG_CHOL_FACTOR); passes of as many matrices as
+    fit in max_ws_bytes of workspace."""
+    B, k = H.shape[0], H.shape[1]
+    V = torch.empty_like(H)
+    lam = torch.empty(B, dtype=torch.float32, device=H.device)
+    info = torch.empty(B, dtype=torch.int32, device=H.device)
+    one = lib.factor_chol_workspace_size(k)
+    need = one * max(1, min(B, max_ws_bytes // one))
+    ws = _workspace(need, H.device)
+    _check("factor_chol_batched", lib.factor_chol_batched(_ptr(H), k, B, H.stride(0), float(damp_rel), _ptr(V),
+                                                          V.stride(0), _ptr(lam), _ptr(info), _ptr(ws), need,
+                                                          _stream()))
+    return V, lam, info
 
 
 def gptq_nvfp4_quantize_batched(W, U, H, g, n_cand=16, flags=0, max_ws_bytes=8 << 30):

@@ -518,25 +518,40 @@ int factor_hinv(const float* H, int64_t k, float damp_rel, float* U, float* lamb
                                        (hipStream_t)stream), "factor_hinv");
 }
 
-int factor_hinv_batched(const float* H, int64_t k, int64_t batch, int64_t stride_h, float damp_rel, float* U,
-                        int64_t stride_u, float* lambda_out, int32_t* info, void* ws, size_t ws_bytes, void* stream) {
-  const char* fn = "factor_hinv_batched";
+// factor_hinv_batched and factor_chol_batched: the same checks, the U form or
+// the Cholesky-factor form over passes of as many matrices as the workspace
+// holds.
+static int factor_batched(const char* fn, bool chol, const float* H, int64_t k, int64_t batch, int64_t stride_h,
+                          float damp_rel, float* U, int64_t stride_u, float* lambda_out, int32_t* info, void* ws,
+                          size_t ws_bytes, void* stream) {
   if (batch < 0) return failp(NVQ_ERR_SHAPE, fn, "batch=%lld", (long long)batch);
   if (batch == 0) return NVQ_OK;
-  if (!H || !U || !lambda_out || !info) return failp(NVQ_ERR_NULL, fn, "H, U, lambda_out and info are required");
+  if (!H || !U || !lambda_out || !info) return failp(NVQ_ERR_NULL, fn, "H, the output, lambda_out and info are required");
   if (k <= 0 || k % 16 != 0) return failp(NVQ_ERR_SHAPE, fn, "k=%lld (need k>0, k%%16==0)", (long long)k);
   if (stride_h < k * k || stride_u < k * k || stride_h % 4 != 0 || stride_u % 4 != 0)
     return failp(NVQ_ERR_SHAPE, fn, "strides must be >= k*k and multiples of 4");
   if (!(damp_rel >= 0.0f) || !std::isfinite(damp_rel)) return failp(NVQ_ERR_VALUE, fn, "damp_rel must be finite and >= 0");
   if ((const float*)U < H + (size_t)stride_h * batch && H < (const float*)U + (size_t)stride_u * batch)
-    return failp(NVQ_ERR_VALUE, fn, "U must not overlap H");
-  if (!aligned(H, 16) || !aligned(U, 16)) return failp(NVQ_ERR_ALIGN, fn, "H and U must be 16-byte aligned");
+    return failp(NVQ_ERR_VALUE, fn, "the output must not overlap H");
+  if (!aligned(H, 16) || !aligned(U, 16)) return failp(NVQ_ERR_ALIGN, fn, "H and the output must be 16-byte aligned");
   const size_t one = factor_hinv_workspace_size(k);
   if (!ws || ws_bytes < one || !aligned(ws, kAlign))
     return failp(NVQ_ERR_WORKSPACE, fn, "workspace needs at least %zu bytes (256-aligned), got %zu", one, ws_bytes);
   const int64_t chunk = std::min<int64_t>((int64_t)(ws_bytes / one), batch);
   return hip_status(factor_hinv_launch(H, k, batch, stride_h, damp_rel, U, stride_u, lambda_out, info, ws, chunk,
-                                       (hipStream_t)stream), fn);
+                                       (hipStream_t)stream, chol), fn);
+}
+
+int factor_hinv_batched(const float* H, int64_t k, int64_t batch, int64_t stride_h, float damp_rel, float* U,
+                        int64_t stride_u, float* lambda_out, int32_t* info, void* ws, size_t ws_bytes, void* stream) {
+  return factor_batched("factor_hinv_batched", false, H, k, batch, stride_h, damp_rel, U, stride_u, lambda_out, info,
+                        ws, ws_bytes, stream);
+}
+
+int factor_chol_batched(const float* H, int64_t k, int64_t batch, int64_t stride_h, float damp_rel, float* V,
+                        int64_t stride_v, float* lambda_out, int32_t* info, void* ws, size_t ws_bytes, void* stream) {
+  return factor_batched("factor_chol_batched", true, H, k, batch, stride_h, damp_rel, V, stride_v, lambda_out, info,
+                        ws, ws_bytes, stream);
 }
 
 size_t factor_chol_workspace_size(int64_t k) { return factor_hinv_workspace_size(k); }

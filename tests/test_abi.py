@@ -90,6 +90,16 @@ def test_host_validation_rejects_bad_arguments():
                                    None) == 0
     assert lib.factor_hinv_batched(fake, 32, 2, 100, ctypes.c_float(0.01), P(1 << 24), 1024, fake, fake, fake,
                                    1 << 30, None) == -2
+    assert lib.factor_chol_batched(None, 32, 0, 1024, ctypes.c_float(0.01), None, 1024, None, None, None, 0,
+                                   None) == 0
+    assert lib.factor_chol_batched(fake, 32, 2, 100, ctypes.c_float(0.01), P(1 << 24), 1024, fake, fake, fake,
+                                   1 << 30, None) == -2
+    assert lib.factor_chol_batched(fake, 24, 2, 1024, ctypes.c_float(0.01), P(1 << 24), 1024, fake, fake, fake,
+                                   1 << 30, None) == -2
+    assert lib.factor_chol_batched(fake, 32, 2, 1024, ctypes.c_float(-1.0), P(1 << 24), 1024, fake, fake, fake,
+                                   1 << 30, None) == -6
+    assert lib.factor_chol_batched(fake, 32, 2, 1024, ctypes.c_float(0.01), P(1 << 24), 1024, fake, fake, fake,
+                                   16, None) == -5
     rc = lib.gptq_nvfp4_quantize_batched(fake, 1, 2, 16, 32, 32, 100, fake, 1024, fake, 1024, fake, 16, 0,
                                          fake, fake, fake, None, fake, 1 << 30, None)
     assert rc == -2

@@ -52,6 +52,21 @@ def test_batched_factor_equals_single(nvq, k):
             assert torch.equal(lam[e:e + 1], single[e][1]), (per_pass, e)
 
 
+@pytest.mark.parametrize("k", [592, 1040])
+def test_batched_chol_factor_equals_single(nvq, k):
+    E = 5
+    H, _ = _experts(E, 16, k, 2 * k)
+    one = nvq.lib.factor_chol_workspace_size(k)
+    single = [nvq.factor_chol(H[e]) for e in range(E)]
+    for per_pass in (1, 2, E):
+        V, lam, info = nvq.factor_chol_batched(H, max_ws_bytes=per_pass * one)
+        torch.cuda.synchronize()
+        assert torch.all(info == 0)
+        for e in range(E):
+            assert torch.equal(V[e], single[e][0]), (per_pass, e)
+            assert torch.equal(lam[e:e + 1], single[e][1]), (per_pass, e)
+
+
 @pytest.mark.parametrize("flags,n_cand", [(0, 16), (4, 16), (8, 16), (1, 4), (16, 8), (2, 16)])
 def test_batched_quantize_equals_single(nvq, flags, n_cand):
     E, m, k = 4, 40, 400

@@ -1,6 +1,7 @@
 """GPU parity of the mixture-of-experts calls: grouped Hessians over routed
-token rows, batched factors and batched quantization, against the CPU oracle
-applied expert by expert (each expert is a linear layer of its own).
+token rows, batched factors (the U form and the Cholesky-factor form) and
+batched quantization, against the CPU oracle applied expert by expert (each
+expert is a linear layer of its own).
 
 The small case checks every expert.  The full case is the MoE workload at its
 real shape (256 experts with gate and up stacked as 2048 x 4096, 262,144
@@ -72,6 +73,53 @@ def test_moe_small_every_expert(nvq):
         assert np.allclose(row_err[e], E_own, rtol=1e-4, atol=1e-6 * E_own.max()), e
 
 
+def _v_from_u(U):
+    """V of the oracle's U (the form FLAG_CHOL_FACTOR takes): R = U^-1 in fp64, V = -R_ij / R_jj above
+    the diagonal, R_ii on it, 0 below."""
+    R = np.triu(np.linalg.inv(U))
+    d = np.diag(R)
+    return np.triu(-R / d[None, :], 1) + np.diag(d)
+
+
+def _v_close(V, Vref):
+    d, dref = np.diag(V), np.diag(Vref)
+    off, offref = np.triu(V, 1), np.triu(Vref, 1)
+    return (np.all(np.tril(V, -1) == 0) and np.max(np.abs(d - dref)) <= 1e-4 * np.max(dref)
+            and np.max(np.abs(off - offref)) <= 1e-4 * np.max(np.abs(offref)))
+
+
+def test_moe_small_every_expert_cholesky_form(nvq):
+    """The same layer through factor_chol_batched and the sweep on V (FLAG_CHOL_FACTOR): every expert's V
+    against the oracle's factor, and its codes, scales and errors against the oracle's fp64 sweep with its
+    own U."""
+    E, n, k, m, top_k = 6, 3000, 256, 48, 2
+    X = synth.activations("moe", n, k)
+    idx, off = synth.moe_routing(n, E, top_k)
+    Xt = synth.to_bf16_tensor(X).to(DEV)
+    Hg = nvq.hessian_accumulate_grouped(Xt, torch.from_numpy(idx).to(DEV), off)
+    V, lam, info = nvq.factor_chol_batched(Hg)
+    W = np.stack([synth.moe_expert_weights(e, m, k) for e in range(E)])
+    Wt = synth.to_bf16_tensor(W.reshape(E * m, k)).reshape(E, m, k).to(DEV)
+    g = torch.stack([nvq.nvfp4_global_scale(Wt[e]) for e in range(E)]).reshape(E)
+    out = nvq.gptq_nvfp4_quantize_batched(Wt, V, Hg, g, 16, nvq.FLAG_CHOL_FACTOR)
+    torch.cuda.synchronize()
+    assert np.all(info.cpu().numpy() == 0)
+    Hc, Vc, gc = Hg.cpu().numpy(), V.cpu().numpy().astype(np.float64), g.cpu().numpy()
+    codes, scales = out["codes"].cpu().numpy(), out["scales"].cpu().numpy()
+    row_err = out["row_err"].cpu().numpy().astype(np.float64)
+    for e in range(E):
+        Uref, lam_ref = gptq.hinv_factor(Hc[e].astype(np.float64))
+        assert float(lam[e].item()) == pytest.approx(lam_ref, rel=1e-5)
+        assert _v_close(Vc[e], _v_from_u(Uref)), e
+        ref = gptq.sweep(W[e], Uref, gc[e], 16)
+        ce = codec.unpack_codes(codes[e])
+        assert _mismatch(ce, ref["codes"]) <= 1e-3, e
+        assert _mismatch(scales[e], ref["scales"]) <= 1e-3, e
+        deq = codec.dequantize(codes[e], scales[e], gc[e])
+        E_own = gptq.weighted_error(W[e], deq, Hc[e])
+        assert np.allclose(row_err[e], E_own, rtol=1e-4, atol=1e-6 * E_own.max()), e
+
+
 def test_moe_empty_group_leaves_its_hessian(nvq):
     k = 64
     X = synth.to_bf16_tensor(synth.activations("moe", 100, k)).to(DEV)
@@ -97,8 +145,12 @@ def test_moe_full_shape_sampled_experts(nvq):
         Wt[e] = synth.to_bf16_tensor(synth.moe_expert_weights(e, m, k)).to(DEV)
     g = torch.stack([nvq.nvfp4_global_scale(Wt[e]) for e in range(E)]).reshape(E)
     out = nvq.gptq_nvfp4_quantize_batched(Wt, U, Hg, g, 16)
+    # the Cholesky-factor form, as the MoE benchmark runs it
+    V, _, info_c = nvq.factor_chol_batched(Hg)
+    out_c = nvq.gptq_nvfp4_quantize_batched(Wt, V, Hg, g, 16, nvq.FLAG_CHOL_FACTOR)
     torch.cuda.synchronize()
     assert np.all(info.cpu().numpy() == 0)
+    assert np.all(info_c.cpu().numpy() == 0)
     order = np.argsort(counts)
     rng = np.random.default_rng(7)
     for e in (int(order[0]), int(order[E // 2]), int(order[-1])):
@@ -129,4 +181,15 @@ def test_moe_full_shape_sampled_experts(nvq):
         deq = codec.dequantize(codec.pack_codes(ce), se, ge)
         E_own = gptq.weighted_error(We[rows], deq, He)
         E_gpu = out["row_err"][e][rows].cpu().numpy().astype(np.float64)
+        assert np.allclose(E_gpu, E_own, rtol=1e-4, atol=1e-6 * E_own.max()), e
+        # Cholesky-factor form: V against the oracle's factor, the sampled rows against its fp64 sweep
+        assert _v_close(V[e].cpu().numpy().astype(np.float64), _v_from_u(Uref)), e
+        ref_c = gptq.sweep(We[rows], Uref, ge, 16)
+        cc = codec.unpack_codes(out_c["codes"][e][rows].cpu().numpy())
+        sc = out_c["scales"][e][rows].cpu().numpy()
+        assert _mismatch(cc, ref_c["codes"]) <= 1e-3, e
+        assert _mismatch(sc, ref_c["scales"]) <= 1e-3, e
+        deq = codec.dequantize(codec.pack_codes(cc), sc, ge)
+        E_own = gptq.weighted_error(We[rows], deq, He)
+        E_gpu = out_c["row_err"][e][rows].cpu().numpy().astype(np.float64)
         assert np.allclose(E_gpu, E_own, rtol=1e-4, atol=1e-6 * E_own.max()), e
