@@ -302,13 +302,15 @@ WORKLOADS = {
 
 
 class LayerTimer:
-    """Times the per-layer C-ABI calls (zero H, Hessian, factor, global scale, quantize, dequantize) on
-    device-resident inputs with events on the library's stream; buffers allocated once, outside timing."""
+    """Times the per-layer C-ABI calls (zero H, Hessian, factor_chol, global scale, quantize on V,
+    dequantize) on device-resident inputs with events on the library's stream; buffers allocated once,
+    outside timing."""
 
     STAGES = ["hessian", "factor", "gscale", "quantize", "dequant"]
 
     def __init__(self, nvq, Wd, Xd, flags, n_cand=N_CAND):
         import torch
+        flags |= nvq.FLAG_CHOL_FACTOR   # factor_chol: V, no triangular inverse
         self.nvq, self.lib, self.P, self.flags, self.n_cand = nvq, nvq.lib, nvq._ptr, flags, n_cand
         self.Wd, self.Xd = Wd, Xd
         self.m, self.k = Wd.shape
@@ -327,7 +329,7 @@ class LayerTimer:
         self.deq = torch.empty(m, k, dtype=torch.bfloat16, device=dev)
         lib = self.lib
         self.ws_n = {"h": lib.hessian_workspace_size(n, k, nvq.NVQ_DTYPE_BF16),
-                     "f": lib.factor_hinv_workspace_size(k),
+                     "f": lib.factor_chol_workspace_size(k),
                      "g": lib.nvfp4_global_scale_workspace_size(m, k),
                      "q": lib.gptq_nvfp4_workspace_size(m, k, flags)}
         self.ws = {a: torch.empty(max(1, b), dtype=torch.uint8, device=dev) for a, b in self.ws_n.items()}
@@ -345,7 +347,7 @@ class LayerTimer:
         self._chk("hessian", lib.hessian_accumulate(P(self.Xd), nvq.NVQ_DTYPE_BF16, n, k, self.Xd.stride(0),
                                                     P(self.H), P(ws["h"]), wn["h"], s))
         if ev: ev[1].record()
-        self._chk("factor", lib.factor_hinv(P(self.H), k, 0.01, P(self.U), P(self.lam), P(self.info), P(ws["f"]),
+        self._chk("factor", lib.factor_chol(P(self.H), k, 0.01, P(self.U), P(self.lam), P(self.info), P(ws["f"]),
                                             wn["f"], s))
         if ev: ev[2].record()
         self._chk("gscale", lib.nvfp4_global_scale(P(self.Wd), nvq.NVQ_DTYPE_BF16, m, k, k, P(self.g), P(ws["g"]),
@@ -471,7 +473,7 @@ def workload_line(name, steps, warmup):
     out = {"metric": "quantized weights/sec (Mparam/s) per layer incl. Hessian", "unit": "Mparam/s",
            "n_gpus": 1, "steps": steps, "warmup": warmup, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "bf16-mfma/fp32", "data": "synthetic",
-           "config": {"workload": WORKLOADS[name], "n_cand": N_CAND}, "layers": {}}
+           "config": {"workload": WORKLOADS[name], "n_cand": N_CAND, "factor": "cholesky"}, "layers": {}}
     tot_ms, tot_params = 0.0, 0
     for lname, Wd, Xd, flags in layers:
         log(f"{lname}: warmup {warmup}, timing {steps} steps")

@@ -23,6 +23,9 @@ What is checked against the fp64 oracle:
     These layers' Hessians span up to 8 orders of magnitude: in fp32, rounding
     alone (in the oracle as much as on the GPU) moves 0.1-0.7% of the
     decisions of the exact computation, all of them at near ties.
+  * the Cholesky-factor form (factor_chol and the fp64 sweep on V, as the
+    layer benchmark runs it) on the same H: V's trailing block against the
+    oracle's, and the same sampled rows to the same bars.
 """
 
 import numpy as np
@@ -128,8 +131,36 @@ def _check_layer(nvq, Xh, Xd, W, rng, n_rows=32, fp32_too=False):
         del r32
     deq = codec.dequantize(codec.pack_codes(codes), scales, g)
     dW = W[rows].astype(np.float64) - deq.astype(np.float64)
-    E_own = np.einsum("rk,rk->r", dW @ H.cpu().numpy().astype(np.float64), dW)
+    Hh = H.cpu().numpy().astype(np.float64)
+    E_own = np.einsum("rk,rk->r", dW @ Hh, dW)
     E_gpu = res["row_err"][rows_t].cpu().numpy().astype(np.float64)
+    assert np.allclose(E_gpu, E_own, rtol=1e-4, atol=1e-6 * E_own.max())
+    # The Cholesky-factor form (factor_chol, the sweep on V; what the layer benchmark times): V's
+    # trailing block against the oracle's (R = U^-1 is upper triangular, so its trailing block is the
+    # inverse of U's), and the sampled rows of the fp64 sweep on V to the same bars.
+    V, lam_c, info_c = nvq.factor_chol(H)
+    rc = nvq.gptq_nvfp4_quantize(Wd, V, H, res["g"], 16, nvq.FLAG_FP64 | nvq.FLAG_CHOL_FACTOR)
+    torch.cuda.synchronize()
+    assert int(info_c.item()) == 0
+    assert float(lam_c.item()) == float(res["lam"].item())
+    Rt = np.triu(np.linalg.inv(Ut_ref))
+    dt = np.diag(Rt)
+    Vt_ref = np.triu(-Rt / dt[None, :], 1) + np.diag(dt)
+    Vt = V[k - t:, k - t:].cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(np.diag(Vt) - dt)) <= 1e-4 * np.max(dt)
+    assert np.max(np.abs(np.triu(Vt, 1) - np.triu(Vt_ref, 1))) <= 1e-4 * np.max(np.abs(np.triu(Vt_ref, 1)))
+    cc = codec.unpack_codes(rc["codes"][rows_t].cpu().numpy())
+    sc = rc["scales"][rows_t].cpu().numpy()
+    print(f"Cholesky-factor form, {len(rows)} rows: code mismatch {_mismatch(cc, ref_s['codes']):.2e}, "
+          f"scale mismatch {_mismatch(sc, ref_s['scales']):.2e} against the fp64 oracle")
+    assert _mismatch(cc, ref_s["codes"]) <= 1e-3
+    assert _mismatch(sc, ref_s["scales"]) <= 1e-3
+    for i in range(len(rows)):
+        _first_divergence_is_near_tie(cc[i], sc[i], ref_s, i, g)
+    deq = codec.dequantize(codec.pack_codes(cc), sc, g)
+    dW = W[rows].astype(np.float64) - deq.astype(np.float64)
+    E_own = np.einsum("rk,rk->r", dW @ Hh, dW)
+    E_gpu = rc["row_err"][rows_t].cpu().numpy().astype(np.float64)
     assert np.allclose(E_gpu, E_own, rtol=1e-4, atol=1e-6 * E_own.max())
 
 
