@@ -456,13 +456,40 @@ int nvfp4_gemm_noalloc(const void* X, int x_dtype, int64_t T, int64_t k, int64_t
                                       y_dtype == NVQ_DTYPE_BF16, ldy, scr, (hipStream_t)stream), fn);
 }
 
+// Grouped Hessians: experts of at least kGroupedLarge tokens (or every expert
+// when the grouped k = 4096 launch does not apply) are gathered and
+// accumulated one at a time; the others are gathered one after another into
+// the same row buffer and accumulated K4G_EXP at a time by one grouped launch
+// each (a launch also ends when the buffer is full).  The buffer holds the
+// largest expert's rows, and at least min(the small experts' rows, 2 GiB).
+constexpr int64_t kGroupedLarge = 16384;
+constexpr size_t kGroupedRowBytes = (size_t)2 << 30;
+
+static bool grouped_launch_applies(int64_t k, int x_dtype) {
+  return x_dtype == NVQ_DTYPE_BF16 && syrk_k4_grouped_applies(k);
+}
+
+static int64_t grouped_rows_cap(const int64_t* grp_off, int64_t G, int64_t k, int x_dtype, int64_t* nmax_out) {
+  int64_t nmax = 0, small = 0;
+  const bool grouped = grouped_launch_applies(k, x_dtype);
+  for (int64_t e = 0; e < G; ++e) {
+    const int64_t ne = grp_off[e + 1] - grp_off[e];
+    nmax = std::max<int64_t>(nmax, ne);
+    if (grouped && ne < kGroupedLarge) small += ne;
+  }
+  *nmax_out = nmax;
+  const size_t esize = x_dtype == NVQ_DTYPE_BF16 ? 2 : 4;
+  const int64_t cap = (int64_t)(kGroupedRowBytes / ((size_t)k * esize));
+  return std::max<int64_t>(nmax, std::min<int64_t>(small, cap));
+}
+
 size_t hessian_grouped_workspace_size(const int64_t* grp_off, int64_t G, int64_t k, int x_dtype) {
   if (!grp_off || G <= 0 || k <= 0 || !dtype_ok(x_dtype)) return 0;
   int64_t nmax = 0;
-  for (int64_t e = 0; e < G; ++e) nmax = std::max<int64_t>(nmax, grp_off[e + 1] - grp_off[e]);
+  const int64_t rows = grouped_rows_cap(grp_off, G, k, x_dtype, &nmax);
   if (nmax <= 0) return 0;
   const size_t esize = x_dtype == NVQ_DTYPE_BF16 ? 2 : 4;
-  return align_up((size_t)nmax * k * esize) + hessian_workspace_size(nmax, k, x_dtype);
+  return align_up((size_t)rows * k * esize) + hessian_workspace_size(nmax, k, x_dtype);
 }
 
 int hessian_accumulate_grouped(const void* X, int x_dtype, int64_t n, int64_t k, int64_t ldx, const int32_t* tok_idx,
@@ -487,15 +514,37 @@ int hessian_accumulate_grouped(const void* X, int x_dtype, int64_t n, int64_t k,
   hipStream_t s = (hipStream_t)stream;
   const int esize = x_dtype == NVQ_DTYPE_BF16 ? 2 : 4;
   int64_t nmax = 0;
-  for (int64_t e = 0; e < G; ++e) nmax = std::max<int64_t>(nmax, grp_off[e + 1] - grp_off[e]);
+  const int64_t cap = grouped_rows_cap(grp_off, G, k, x_dtype, &nmax);
+  const bool grouped = grouped_launch_applies(k, x_dtype);
   char* rows = (char*)ws;
-  void* hws = rows + align_up((size_t)nmax * k * esize);
+  void* hws = rows + align_up((size_t)cap * k * esize);
   hipError_t err = hipSuccess;
   for (int64_t e = 0; err == hipSuccess && e < G; ++e) {
     const int64_t ne = grp_off[e + 1] - grp_off[e];
-    if (ne == 0) continue;
+    if (ne == 0 || (grouped && ne < kGroupedLarge)) continue;
     err = gather_rows(X, esize, ldx, tok_idx + grp_off[e], n, ne, k, rows, s);
     if (err == hipSuccess) err = hessian_run(rows, x_dtype, ne, k, k, H + (size_t)e * k * k, hws, s);
+  }
+  if (grouped) {
+    K4Grouped g{};
+    int nexp = 0;
+    int64_t used = 0;
+    for (int64_t e = 0; err == hipSuccess && e <= G; ++e) {
+      const int64_t ne = e < G ? grp_off[e + 1] - grp_off[e] : 0;
+      if (e < G && (ne == 0 || ne >= kGroupedLarge)) continue;
+      if (nexp > 0 && (e == G || nexp == K4G_EXP || used + ne > cap)) {
+        err = syrk_bf16_grouped((const uint16_t*)rows, k, g, nexp, H, s);
+        nexp = 0;
+        used = 0;
+      }
+      if (e == G || err != hipSuccess) break;
+      err = gather_rows(X, esize, ldx, tok_idx + grp_off[e], n, ne, k, rows + (size_t)used * k * esize, s);
+      g.beg[nexp] = (int32_t)used;
+      g.cnt[nexp] = (int32_t)ne;
+      g.hexp[nexp] = (int32_t)e;
+      ++nexp;
+      used += ne;
+    }
   }
   return hip_status(err, "hessian_accumulate_grouped");
 }

@@ -66,6 +66,17 @@ size_t syrk_bf16_workspace(int64_t n, int64_t k);
 hipError_t syrk_bf16(const uint16_t* X, int64_t n, int64_t k, int64_t ldx, float* H, void* ws,
                      hipStream_t s);
 hipError_t symmetrize_from_upper(float* H, int64_t k, hipStream_t s);
+// Grouped Hessians of small experts at k = 4096 (see syrk_k4_grouped_kernel):
+// expert j of a group has cnt[j] gathered bf16 rows (ld k) from row beg[j] and
+// adds into H + hexp[j] * k * k (upper triangle, then mirrored into the lower
+// one).  syrk_bf16_grouped fills nx and xe itself.
+constexpr int K4G_EXP = 128, K4G_PER_XCD = 32;
+struct K4Grouped {
+  int32_t beg[K4G_EXP], cnt[K4G_EXP], hexp[K4G_EXP];
+  uint8_t nx[8], xe[8][K4G_PER_XCD];
+};
+bool syrk_k4_grouped_applies(int64_t k);
+hipError_t syrk_bf16_grouped(const uint16_t* rows, int64_t k, K4Grouped& g, int nexp, float* H, hipStream_t s);
 // out[t] = row clamp(idx[t], 0, nsrc-1) of X (rows of k elements of esize bytes, ld ldx).
 hipError_t gather_rows(const void* X, int esize, int64_t ldx, const int32_t* idx, int64_t nsrc, int64_t n,
                        int64_t k, void* out, hipStream_t s);

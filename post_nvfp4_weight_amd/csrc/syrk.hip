@@ -34,6 +34,7 @@
 // and lane i receives channel C + i for tokens T..T+3.  16-byte chunks of a
 // row are XOR-swizzled by the row index so that the transposed reads of 32
 // lanes hit 64 distinct banks.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
@@ -543,7 +544,8 @@ __device__ __forceinline__ void k4_loads(char* slot, const uint16_t* src, int nr
 // element and its mirror are written; on one (rch == cch) the upper triangle
 // and the mirror of the strict upper triangle.
 __device__ __forceinline__ void k4_store(const f32x16& acc, int blk, int r0, int c0, int64_t rch, int64_t cch,
-                                         int64_t k, float* __restrict__ H, float* __restrict__ P) {
+                                         int64_t k, float* __restrict__ H, float* __restrict__ P,
+                                         bool mirror = true) {
   const int lane = threadIdx.x & 63, col = c0 + (lane & 31);
   if (P) {
 #pragma unroll
@@ -566,7 +568,7 @@ __device__ __forceinline__ void k4_store(const f32x16& acc, int blk, int r0, int
     if (gi < k && gj < k && gi <= gj) {
       const float v = old[r] + acc[r];
       H[gi * k + gj] = v;
-      if (gi != gj) H[gj * k + gi] = v;
+      if (mirror && gi != gj) H[gj * k + gi] = v;
     }
   }
 }
@@ -611,7 +613,7 @@ __device__ __forceinline__ void k4_step(char* __restrict__ slot, const char* __r
 template <class R>
 __device__ __forceinline__ void k4_wave(char* lds, const uint16_t* __restrict__ X, int64_t k, int64_t ldx,
                                         const int64_t (&ch)[4], int64_t t_begin, int64_t t_end,
-                                        float* __restrict__ H, float* __restrict__ P) {
+                                        float* __restrict__ H, float* __restrict__ P, bool mirror) {
   constexpr int NL = 8;
   const int nstages = t_end > t_begin ? (int)((t_end - t_begin + ST - 1) / ST) : 0;
   const int lane = threadIdx.x & 63, g = lane >> 4, j = lane & 15, s4 = j >> 2;
@@ -664,38 +666,39 @@ __device__ __forceinline__ void k4_wave(char* lds, const uint16_t* __restrict__ 
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) k4_store(accF[i][c], R::FB, 32 * i, 32 * c, ch[R::X], ch[R::Y], k, H, P);
+    for (int c = 0; c < 4; ++c) k4_store(accF[i][c], R::FB, 32 * i, 32 * c, ch[R::X], ch[R::Y], k, H, P, mirror);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int c = 0; c < 2; ++c)
-      k4_store(accH[i][c], R::HB, 32 * i, R::HC0 + 32 * c, ch[R::HR], ch[R::HC], k, H, P);
+      k4_store(accH[i][c], R::HB, 32 * i, R::HC0 + 32 * c, ch[R::HR], ch[R::HC], k, H, P, mirror);
 }
 
 // Tile t over tokens [t_begin, t_end), into H or into its partial sums P
 // (kK4SlotFloats): t < K4_TILES a four-group tile of the table, otherwise
 // diagonal tile t - K4_TILES (segments 2d and 2d + 1, groups 4d .. 4d + 3).
 __device__ __forceinline__ void k4_job(char* lds, const uint16_t* __restrict__ X, int64_t k, int64_t ldx, int t,
-                                       int64_t t_begin, int64_t t_end, float* __restrict__ H, float* __restrict__ P) {
+                                       int64_t t_begin, int64_t t_end, float* __restrict__ H, float* __restrict__ P,
+                                       bool mirror = true) {
   int64_t ch[4];
   const int wave = threadIdx.x >> 6;
   if (t < K4_TILES) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) ch[q] = (int64_t)kK4.g[t][q] * K4G;
     switch (wave) {
-      case 0: k4_wave<K4W0>(lds, X, k, ldx, ch, t_begin, t_end, H, P); break;
-      case 1: k4_wave<K4W1>(lds, X, k, ldx, ch, t_begin, t_end, H, P); break;
-      case 2: k4_wave<K4W2>(lds, X, k, ldx, ch, t_begin, t_end, H, P); break;
-      default: k4_wave<K4W3>(lds, X, k, ldx, ch, t_begin, t_end, H, P); break;
+      case 0: k4_wave<K4W0>(lds, X, k, ldx, ch, t_begin, t_end, H, P, mirror); break;
+      case 1: k4_wave<K4W1>(lds, X, k, ldx, ch, t_begin, t_end, H, P, mirror); break;
+      case 2: k4_wave<K4W2>(lds, X, k, ldx, ch, t_begin, t_end, H, P, mirror); break;
+      default: k4_wave<K4W3>(lds, X, k, ldx, ch, t_begin, t_end, H, P, mirror); break;
     }
   } else {
 #pragma unroll
     for (int q = 0; q < 4; ++q) ch[q] = (int64_t)(4 * (t - K4_TILES) + q) * K4G;
     switch (wave) {
-      case 0: k4_wave<DGW0>(lds, X, k, ldx, ch, t_begin, t_end, H, P); break;
-      case 1: k4_wave<DGW1>(lds, X, k, ldx, ch, t_begin, t_end, H, P); break;
-      case 2: k4_wave<DGW2>(lds, X, k, ldx, ch, t_begin, t_end, H, P); break;
-      default: k4_wave<DGW3>(lds, X, k, ldx, ch, t_begin, t_end, H, P); break;
+      case 0: k4_wave<DGW0>(lds, X, k, ldx, ch, t_begin, t_end, H, P, mirror); break;
+      case 1: k4_wave<DGW1>(lds, X, k, ldx, ch, t_begin, t_end, H, P, mirror); break;
+      case 2: k4_wave<DGW2>(lds, X, k, ldx, ch, t_begin, t_end, H, P, mirror); break;
+      default: k4_wave<DGW3>(lds, X, k, ldx, ch, t_begin, t_end, H, P, mirror); break;
     }
   }
 }
@@ -847,6 +850,9 @@ struct K4Args {
   int64_t k4tokens, dtokens, head, ttokens, dbase, tbase;
 };
 
+constexpr int K4_ALL = K4_TILES + K4_DTILES;   // tiles of one k = 4096 Hessian
+static_assert(sizeof(K4Grouped::nx) == kXcds, "one expert list per XCD");
+
 __global__ __launch_bounds__(256) void syrk_k4_kernel(const uint16_t* __restrict__ X, int64_t n, int64_t k,
                                                       int64_t ldx, float* __restrict__ H,
                                                       float* __restrict__ partial, K4Args a, int tails) {
@@ -877,6 +883,63 @@ __global__ __launch_bounds__(256) void syrk_k4_kernel(const uint16_t* __restrict
     slot = (size_t)a.dbase + e;
   }
   k4_job(lds, X, k, ldx, t, t0, t1, H, a.direct ? nullptr : partial + slot * kK4SlotFloats);
+}
+
+// Grouped Hessians of small experts (one H per expert, k = 4096 layout): one
+// launch runs every four-group and diagonal tile of every expert of the
+// group, each over its expert's whole token range (rows gathered one expert
+// after another), adding straight into that expert's H.  Workgroup b runs on
+// XCD b % 8 (ids are dealt round-robin), item (b / 8) of that XCD's list:
+// expert xe[x][(b / 8) / K4_ALL], tile (b / 8) % K4_ALL.  The host gives each
+// XCD whole experts, largest first and balanced by tokens, so an expert's rows
+// are read into one XCD's L2 and the XCDs finish together; workgroups past
+// an XCD's list exit.  No tile of an expert shares an H entry with another,
+// so the direct stores do not race.
+__global__ __launch_bounds__(256) void syrk_k4_grouped_kernel(const uint16_t* __restrict__ X, int64_t k,
+                                                              float* __restrict__ H, K4Grouped g) {
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+  const int x = (int)(blockIdx.x % kXcds), i = (int)(blockIdx.x / kXcds);
+  const int j = i / K4_ALL, t = i % K4_ALL;
+  if (j >= g.nx[x]) return;
+  const int e = g.xe[x][j];
+  k4_job(lds, X + (int64_t)g.beg[e] * k, k, k, t, 0, g.cnt[e], H + (int64_t)g.hexp[e] * k * k, nullptr, false);
+}
+
+// The lower triangle of each grouped expert's H from its upper triangle (the
+// grouped tiles add into the upper triangle only: their column-strided mirror
+// stores would touch a cache line per element).  One 64 x 64 tile per
+// workgroup: tile (bi, bj), bi >= bj, of expert blockIdx.y is the transpose of
+// upper tile (bj, bi), read by rows into LDS and written by rows; a diagonal
+// tile writes only below its diagonal.  k % 64 == 0.
+__global__ __launch_bounds__(256) void k4_mirror_kernel(float* __restrict__ H, int64_t k, K4Grouped g) {
+  __shared__ float T[64][65];
+  const int64_t t = blockIdx.x;
+  int64_t bi = (int64_t)((sqrt(8.0 * (double)t + 1.0) - 1.0) / 2.0);
+  while (bi * (bi + 1) / 2 > t) --bi;
+  while ((bi + 1) * (bi + 2) / 2 <= t) ++bi;
+  const int64_t bj = t - bi * (bi + 1) / 2;
+  float* He = H + (int64_t)g.hexp[blockIdx.y] * k * k;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = q * 256 + tid, r = e >> 4, c4 = (e & 15) * 4;
+    const f32x4 v = *(const f32x4*)(He + (bj * 64 + r) * k + bi * 64 + c4);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) T[r][c4 + u] = v[u];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = q * 256 + tid, r = e >> 4, c4 = (e & 15) * 4;
+    float* dst = He + (bi * 64 + r) * k + bj * 64 + c4;
+    if (bi != bj) {
+      *(f32x4*)dst = f32x4{T[c4][r], T[c4 + 1][r], T[c4 + 2][r], T[c4 + 3][r]};
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (c4 + u < r) dst[u] = T[c4 + u][r];
+    }
+  }
 }
 
 // Launch 2: singles (bottom-right diagonal 128-block of 256-block a), split
@@ -1260,6 +1323,42 @@ hipError_t syrk_bf16(const uint16_t* X, int64_t n, int64_t k, int64_t ldx, float
   if (p.nsingle > 0 && p.ssplit > 1)
     hipLaunchKernelGGL(syrk_reduce_kernel, dim3(p.nsingle, 4), dim3(256), 0, s, k, H, partial, 1, p.ssplit, 0,
                        single_base, p.tail);
+  return hipGetLastError();
+}
+
+bool syrk_k4_applies(int64_t k) { return (k + QUAD - 1) / QUAD == K4_SEGS; }
+bool syrk_k4_grouped_applies(int64_t k) { return syrk_k4_applies(k) && k % 64 == 0; }
+
+// Experts on XCDs: largest first, each to the XCD with the fewest tokens so far
+// (among those with room), so every XCD's list is in decreasing size.
+hipError_t syrk_bf16_grouped(const uint16_t* rows, int64_t k, K4Grouped& g, int nexp, float* H, hipStream_t s) {
+  if (nexp <= 0) return hipSuccess;
+  if (nexp > K4G_EXP || !syrk_k4_grouped_applies(k)) return hipErrorInvalidValue;
+  int order[K4G_EXP];
+  for (int j = 0; j < nexp; ++j) order[j] = j;
+  std::sort(order, order + nexp, [&](int a, int b) { return g.cnt[a] != g.cnt[b] ? g.cnt[a] > g.cnt[b] : a < b; });
+  int64_t load[kXcds] = {};
+  for (int x = 0; x < kXcds; ++x) g.nx[x] = 0;
+  for (int q = 0; q < nexp; ++q) {
+    int best = -1;
+    for (int x = 0; x < kXcds; ++x)
+      if (g.nx[x] < K4G_PER_XCD && (best < 0 || load[x] < load[best])) best = x;
+    g.xe[best][g.nx[best]++] = (uint8_t)order[q];
+    load[best] += g.cnt[order[q]];
+  }
+  int most = 0;
+  for (int x = 0; x < kXcds; ++x) most = std::max<int>(most, g.nx[x]);
+  static bool attr = false;
+  const size_t lds = (size_t)NS * K4_STAGE;
+  if (!attr) {
+    (void)hipFuncSetAttribute((const void*)syrk_k4_grouped_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)lds);
+    attr = true;
+  }
+  hipLaunchKernelGGL(syrk_k4_grouped_kernel, dim3((unsigned)(kXcds * most * K4_ALL)), dim3(256), lds, s, rows, k, H,
+                     g);
+  const int64_t nt = k / 64;
+  hipLaunchKernelGGL(k4_mirror_kernel, dim3((unsigned)(nt * (nt + 1) / 2), (unsigned)nexp), dim3(256), 0, s, H, k, g);
   return hipGetLastError();
 }
 

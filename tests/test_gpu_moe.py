@@ -120,6 +120,33 @@ def test_moe_small_every_expert_cholesky_form(nvq):
         assert np.allclose(row_err[e], E_own, rtol=1e-4, atol=1e-6 * E_own.max()), e
 
 
+def test_moe_grouped_launch_k4096(nvq):
+    """At k = 4096 the experts under 16384 tokens share grouped launches (every tile of every such expert
+    over its whole token range, adding into its own H) and the larger ones take the one-expert path:
+    experts of 0 to 20000 tokens, ragged counts, an H that already holds values; every H_e within the
+    fp32 summation bound of H0_e + X_e^T X_e in fp64, exactly symmetric."""
+    k = 4096
+    counts = [777, 0, 1, 16384, 31, 100, 5000, 2048, 20000, 3, 9999]
+    n = 24000
+    X = synth.activations("moe", n, k)
+    rng = np.random.default_rng(11)
+    idx = np.concatenate([rng.choice(n, size=c, replace=False) for c in counts]).astype(np.int32)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    E = len(counts)
+    H0 = np.zeros((E, k, k), dtype=np.float32)
+    H0[4] = 3.0   # an H that already holds values: the grouped tiles add into it
+    Hg = nvq.hessian_accumulate_grouped(synth.to_bf16_tensor(X).to(DEV), torch.from_numpy(idx).to(DEV), off,
+                                        torch.from_numpy(H0).to(DEV))
+    torch.cuda.synchronize()
+    Hc = Hg.cpu().numpy()
+    for e in range(E):
+        Xe = X[idx[off[e]:off[e + 1]]].astype(np.float64)
+        ref = H0[e].astype(np.float64) + Xe.T @ Xe
+        bound = np.abs(Xe).T @ np.abs(Xe) * ((len(Xe) / 16 + 64) * 2.0 ** -23) + 4 * 2.0 ** -24 * np.abs(H0[e])
+        assert np.array_equal(Hc[e], Hc[e].T), e
+        assert np.all(np.abs(Hc[e] - ref) <= bound + 1e-30), e
+
+
 def test_moe_empty_group_leaves_its_hessian(nvq):
     k = 64
     X = synth.to_bf16_tensor(synth.activations("moe", 100, k)).to(DEV)
