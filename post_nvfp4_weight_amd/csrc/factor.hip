@@ -497,26 +497,37 @@ __global__ void flip_out_kernel(const float* __restrict__ Linv, int64_t k, float
 // diagonal, V[i][i] = R[i][i], 0 below.  Four columns j .. j+3 per thread
 // (they lie in one 64-block of L: k % 4 == 0), 16-byte loads and stores.
 // Matrix b = blockIdx.z: A + b * k^2, Ld + b * k^2 -> V + b * stride_v.
+// dv[c] = L[c][c] (from the diagonal blocks in Ld) for each matrix z of the
+// pass (dv + z * stride_d), so that chol_out_kernel reads the pivots as
+// contiguous vectors instead of one strided element per output.
+__global__ void diag_vec_kernel(const float* __restrict__ Ld, int64_t k, float* __restrict__ dv, int64_t stride_d) {
+  const int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= k) return;
+  dv[(int64_t)blockIdx.y * stride_d + c] = Ld[(int64_t)blockIdx.y * k * k + c * k + c];
+}
+
 __global__ void chol_out_kernel(const float* __restrict__ A, const float* __restrict__ Ld, int64_t k,
-                                float* __restrict__ V, int64_t stride_v) {
+                                float* __restrict__ V, int64_t stride_v, const float* __restrict__ dv,
+                                int64_t stride_d) {
   const int64_t i = blockIdx.y, j = 4 * ((int64_t)blockIdx.x * blockDim.x + threadIdx.x);
   if (j >= k) return;
   A += (int64_t)blockIdx.z * k * k;
   Ld += (int64_t)blockIdx.z * k * k;
   V += (int64_t)blockIdx.z * stride_v;
+  dv += (int64_t)blockIdx.z * stride_d;
   f32x4 v = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   if (j + 3 >= i) {
     const int64_t r = k - 1 - i, c0 = k - 4 - j;   // L[r][c0 + 3 - u] = R[i][j + u]
     const float* src = r / NB == c0 / NB ? Ld : A;
     const f32x4 l = *(const f32x4*)(src + r * k + c0);
+    const f32x4 dd = *(const f32x4*)(dv + c0);   // dd[3 - u] = L[d][d], d = k - 1 - (j + u)
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int64_t jj = j + u;
       if (jj == i) {
         v[u] = l[3 - u];
       } else if (jj > i) {
-        const int64_t d = k - 1 - jj;
-        v[u] = -l[3 - u] / Ld[d * k + d];
+        v[u] = -l[3 - u] / dd[3 - u];
       }
     }
   }
@@ -655,9 +666,11 @@ static hipError_t factor_pass(const float* H, int64_t k, int64_t nb, int64_t str
   if (rest_pending) e = hipStreamWaitEvent(s, ev_rest, 0);
   release();
   if (e != hipSuccess) return e;
-  if (chol) {   // the factor itself (scaled as the sweep takes it), no inverse
+  if (chol) {   // the factor itself (scaled as the sweep takes it), no inverse; T holds the pivots
+    hipLaunchKernelGGL(diag_vec_kernel, dim3((unsigned)((k + 255) / 256), nbu), dim3(256), 0, s, Linv, k, T,
+                       (int64_t)(kk / 2));
     hipLaunchKernelGGL(chol_out_kernel, dim3((unsigned)((k / 4 + 255) / 256), (unsigned)k, nbu), dim3(256), 0, s, A,
-                       Linv, k, U, stride_u);
+                       Linv, k, U, stride_u, T, (int64_t)(kk / 2));
     return hipGetLastError();
   }
   hipLaunchKernelGGL(diag_inv_kernel, dim3((unsigned)((k + NB - 1) / NB), nbu), dim3(64), 0, s, Linv, k);
