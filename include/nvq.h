@@ -200,9 +200,16 @@ int hessian_accumulate_host(const void* X_host, int x_dtype, int64_t n, int64_t 
  *   H        device fp32 [G][k][k]; each H[e] as in hessian_accumulate (upper
  *            triangle read, full symmetric matrix written).
  *   ws       device workspace of hessian_grouped_workspace_size(grp_off, G, k,
- *            x_dtype) bytes: the largest group's gathered rows plus the
- *            Hessian workspace for that many tokens.
- * Groups are processed in order on the stream (gather, then the contraction).
+ *            x_dtype) bytes: a gathered-row buffer (the largest group's rows,
+ *            and for bf16 X with k = 4096 at least the smaller groups' rows up
+ *            to 2 GiB) plus the Hessian workspace for the largest group.
+ * Groups of at least 16384 rows, and every group unless X is bf16 and k is
+ * 4096, are gathered and accumulated one at a time, in order, on the stream.
+ * With bf16 X and k = 4096 the smaller groups are gathered one after another
+ * into the row buffer and accumulated together, up to 128 groups per launch
+ * (each H[e] entry then sums its group's rows in one fixed order, so results
+ * are bitwise reproducible; they may differ in rounding from a
+ * hessian_accumulate call on the same rows, within the same fp32 bound).
  */
 size_t hessian_grouped_workspace_size(const int64_t* grp_off, int64_t G, int64_t k, int x_dtype);
 int hessian_accumulate_grouped(const void* X, int x_dtype, int64_t n, int64_t k, int64_t ldx, const int32_t* tok_idx,
