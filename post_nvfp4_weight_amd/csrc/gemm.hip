@@ -325,7 +325,11 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
 // two thirds of the operand stores of NP = 3.  Only the weighted error
 // (the row-dot epilogue) takes it: an error of about 2^-16 per product there
 // moves a row's dW H' dW^T by a few parts in a million, and no quantization
-// decision depends on it.
+// decision depends on it.  NP = 2 reads the second k-step's fragments after
+// the first k-step's products instead of among them, which keeps it within
+// 256 registers: with its 80 KB of LDS two workgroups share a CU, and each
+// hides the other's fragment reads and split stages (same products, same
+// order, same bits; the weighted error 381 -> 290 us at 4096 x 4096).
 constexpr int X6_T = 128, X6_LD = BK + 8;                 // bf16 row stride of a part
 constexpr int X6_PART = X6_T * X6_LD;                     // bf16 elements of one part
 template <int NP>
@@ -358,7 +362,7 @@ __device__ __forceinline__ void put4(uint16_t* base, int off, const f32x4& v) {
 __device__ __forceinline__ int x6_boff(int n, int k) { return n * X6_LD + ((((k >> 3) ^ (n >> 4)) & 3) << 3) + (k & 7); }
 
 template <int EPI, bool TB, bool LOWER, int NP>
-__global__ __launch_bounds__(256) void gemm_x6_kernel(GemmArgs p) {
+__global__ __launch_bounds__(256, NP == 2 ? 2 : 1) void gemm_x6_kernel(GemmArgs p) {
   static_assert(NP == 2 || NP == 3, "two or three bf16 parts");
   constexpr int X6_BUF = x6_buf<NP>();
   constexpr int WT = X6_T / 2;
@@ -598,9 +602,13 @@ __global__ __launch_bounds__(256) void gemm_x6_kernel(GemmArgs p) {
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int m = 0; m < 4 * NPR; ++m) {
+        if (NP == 2 && h == 1 && m == 0) {
+#pragma unroll
+          for (int f = 0; f < 4 * NP; ++f) read(1, f);
+        }
         const int pp = m >> 2, i = (m >> 1) & 1, j = m & 1;
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[h][PA[pp]][i], b[h][PB[pp]][j], acc[i][j], 0, 0, 0);
-        if (h == 0 && m < 4 * NP) read(1, m);
+        if (NP == 3 && h == 0 && m < 4 * NP) read(1, m);
 #pragma unroll
         for (int u = 0; u < SPS; ++u) {
           const int g = SPS * (4 * NPR * h + m) + u;
