@@ -329,7 +329,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs p) {
 // the first k-step's products instead of among them, which keeps it within
 // 256 registers: with its 80 KB of LDS two workgroups share a CU, and each
 // hides the other's fragment reads and split stages (same products, same
-// order, same bits; the weighted error 381 -> 290 us at 4096 x 4096).
+// order, same bits; the weighted error 381 -> 295 us at 4096 x 4096).
 constexpr int X6_T = 128, X6_LD = BK + 8;                 // bf16 row stride of a part
 constexpr int X6_PART = X6_T * X6_LD;                     // bf16 elements of one part
 template <int NP>
