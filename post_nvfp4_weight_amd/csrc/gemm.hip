@@ -361,8 +361,8 @@ __device__ __forceinline__ void put4(uint16_t* base, int off, const f32x4& v) {
 // by (column / 16) % 4, which spreads the transposing writes over the banks.
 __device__ __forceinline__ int x6_boff(int n, int k) { return n * X6_LD + ((((k >> 3) ^ (n >> 4)) & 3) << 3) + (k & 7); }
 
-template <int EPI, bool TB, bool LOWER, int NP>
-__global__ __launch_bounds__(256, NP == 2 ? 2 : 1) void gemm_x6_kernel(GemmArgs p) {
+template <int EPI, bool TB, bool LOWER, int NP, bool ONEBUF>
+__global__ __launch_bounds__(256, (NP == 2 || ONEBUF) ? 2 : 1) void gemm_x6_kernel(GemmArgs p) {
   static_assert(NP == 2 || NP == 3, "two or three bf16 parts");
   constexpr int X6_BUF = x6_buf<NP>();
   constexpr int WT = X6_T / 2;
@@ -372,7 +372,7 @@ __global__ __launch_bounds__(256, NP == 2 ? 2 : 1) void gemm_x6_kernel(GemmArgs 
   if (p.kmode == kGemmKSymUpperB) { tn = nt - 1 - lin / mt; tm = lin % mt; }
   else if (p.kmode == kGemmKLowerB) { tn = lin / mt; tm = lin % mt; }
   else if (p.kmode == kGemmKLowerA) { tm = mt - 1 - lin / nt; tn = lin % nt; }
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * X6_BUF];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[(ONEBUF ? 1 : 2) * X6_BUF];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -557,77 +557,114 @@ __global__ __launch_bounds__(256, NP == 2 ? 2 : 1) void gemm_x6_kernel(GemmArgs 
   // pieces placed among the products, and then the loads of chunk c+3 take
   // its registers.  Loads past the end read clamped addresses and stores past
   // the end go to the idle buffer, so no step branches.
-  f32x4 ra0[4], rb0[4], ra1[4], rb1[4];
-  load_chunk(c0 * BK, ra0, rb0);
-  store_chunk(smem, (int)(c0 * BK), ra0, rb0);
-  load_chunk((c0 + 1) * BK, ra0, rb0);
-  load_chunk((c0 + 2) * BK, ra1, rb1);
-  __syncthreads();
-  // Lane l reads rows (l % 32) and k offset 8 (l / 32) of each 32-row block.
-  const int arow = wr * WT + (lane & 31), brow = wc * WT + (lane & 31), koff = 8 * (lane >> 5);
-  // Part products, smallest first: NPR of them per 32 x 32 accumulator and
-  // k-step, 4 NPR MFMAs per k-step, each followed by SPS of the 48 store
-  // stages of the next chunk (8 pieces of 6).
-  constexpr int NPR = NP == 3 ? 6 : 3, SPS = 48 / (8 * NPR);
-  constexpr int PA[6] = {NP == 3 ? 2 : 1, NP == 3 ? 1 : 0, 0, 1, 0, 0};
-  constexpr int PB[6] = {0, 1, NP == 3 ? 2 : 0, 0, 1, 0};
-  static_assert(BK == 32, "two 16-deep k-steps per chunk");
-  // As (the buffer being multiplied) and nbuf (the idle one) are distinct,
-  // which the restrict qualifiers state: the stores into nbuf need not wait
-  // for the fragment reads from As.
-  auto body = [&](const uint16_t* __restrict__ As, uint16_t* __restrict__ nbuf, int64_t c, f32x4 (&ra)[4],
-                  f32x4 (&rb)[4]) {
-    const uint16_t* Bs = As + NP * X6_PART;
-    const int kn = (int)((c + 1) * BK);
-    bf16x8 a[2][NP][2], b[2][NP][2];   // [k-step][part][32-row block]
-    auto read = [&](int h, int f) {   // fragment f (0..4 NP - 1) of k-step h
-      const int pt = f >> 2, t = (f >> 1) & 1, ks = 16 * h;
-      if (f & 1) b[h][pt][t] = *(const bf16x8*)(Bs + pt * X6_PART + x6_boff(brow + 32 * t, ks + koff));
-      else a[h][pt][t] = *(const bf16x8*)(As + pt * X6_PART + (arow + 32 * t) * X6_LD + ks + koff);
-    };
+  if constexpr (ONEBUF) {
+    // One LDS buffer (two workgroups share a CU): per chunk, the split parts
+    // are stored, the next chunk's loads issued into the same registers, and
+    // after a barrier both k-steps are multiplied; another barrier frees the
+    // buffer.  The other workgroup on the CU runs its products while this one
+    // splits and stores.
+    f32x4 ra[4], rb[4];
+    load_chunk(c0 * BK, ra, rb);
+    const int arow = wr * WT + (lane & 31), brow = wc * WT + (lane & 31), koff = 8 * (lane >> 5);
+    constexpr int NPR = NP == 3 ? 6 : 3;
+    constexpr int PA[6] = {NP == 3 ? 2 : 1, NP == 3 ? 1 : 0, 0, 1, 0, 0};
+    constexpr int PB[6] = {0, 1, NP == 3 ? 2 : 0, 0, 1, 0};
+    static_assert(BK == 32, "two 16-deep k-steps per chunk");
+    const uint16_t* Bs = smem + NP * X6_PART;
+    for (int64_t c = c0; c < nk; ++c) {
+      store_chunk(smem, (int)(c * BK), ra, rb);
+      load_chunk((c + 1) * BK, ra, rb);   // clamped addresses past the end
+      lds_barrier();
 #pragma unroll
-    for (int f = 0; f < 4 * NP; ++f) read(0, f);
-    // Per k-step: 24 products (the four accumulators take turns, so that no
-    // MFMA waits for the one before it).  Behind each product comes one stage
-    // of the next chunk's store (6 stages for each of its 8 pieces, a few
-    // vector instructions each, which run while the MFMA does); the first
-    // k-step also reads the second one's fragments, and each load of chunk
-    // c+3 follows the stage that last reads the registers it fills (A's row
-    // chunk q: piece q's first stage; B's rows: piece 7's, or with TB B's row
-    // chunk q: piece 4 + q's).
-    f32x4 sv;
-    uint32_t sh0, sh1, sm0_, sm1_;
-    float sr[4];
+      for (int h = 0; h < 2; ++h) {
+        bf16x8 a[NP][2], b[NP][2];
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int m = 0; m < 4 * NPR; ++m) {
-        if (NP == 2 && h == 1 && m == 0) {
-#pragma unroll
-          for (int f = 0; f < 4 * NP; ++f) read(1, f);
+        for (int f = 0; f < 4 * NP; ++f) {
+          const int pt = f >> 2, t = (f >> 1) & 1, ks = 16 * h;
+          if (f & 1) b[pt][t] = *(const bf16x8*)(Bs + pt * X6_PART + x6_boff(brow + 32 * t, ks + koff));
+          else a[pt][t] = *(const bf16x8*)(smem + pt * X6_PART + (arow + 32 * t) * X6_LD + ks + koff);
         }
-        const int pp = m >> 2, i = (m >> 1) & 1, j = m & 1;
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[h][PA[pp]][i], b[h][PB[pp]][j], acc[i][j], 0, 0, 0);
-        if (NP == 3 && h == 0 && m < 4 * NP) read(1, m);
 #pragma unroll
-        for (int u = 0; u < SPS; ++u) {
-          const int g = SPS * (4 * NPR * h + m) + u;
-          store_stage(nbuf, kn, ra, rb, g / 6, g % 6, sv, sh0, sh1, sm0_, sm1_, sr);
-          if (g % 6 == 1 && g < 24) load_a((c + 3) * BK, ra, g / 6);
-          if (TB && g % 6 == 1 && g >= 24) load_b((c + 3) * BK, rb, g / 6 - 4);
-          if (!TB && g >= 43 && g < 47) load_b((c + 3) * BK, rb, g - 43);
+        for (int m = 0; m < 4 * NPR; ++m) {
+          const int pp = m >> 2, i = (m >> 1) & 1, j = m & 1;
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[PA[pp]][i], b[PB[pp]][j], acc[i][j], 0, 0, 0);
         }
-        __builtin_amdgcn_sched_barrier(0);
       }
-  };
-  auto step = [&](int64_t c, f32x4 (&ra)[4], f32x4 (&rb)[4]) {
-    const int cur = (int)((c - c0) & 1);
-    body(smem + cur * X6_BUF, smem + (cur ^ 1) * X6_BUF, c, ra, rb);
-    lds_barrier();
-  };
-  for (int64_t c = c0; c < nk; c += 2) {
-    step(c, ra0, rb0);
-    if (c + 1 < nk) step(c + 1, ra1, rb1);
+      lds_barrier();
+    }
+  } else {
+    f32x4 ra0[4], rb0[4], ra1[4], rb1[4];
+    load_chunk(c0 * BK, ra0, rb0);
+    store_chunk(smem, (int)(c0 * BK), ra0, rb0);
+    load_chunk((c0 + 1) * BK, ra0, rb0);
+    load_chunk((c0 + 2) * BK, ra1, rb1);
+    __syncthreads();
+    // Lane l reads rows (l % 32) and k offset 8 (l / 32) of each 32-row block.
+    const int arow = wr * WT + (lane & 31), brow = wc * WT + (lane & 31), koff = 8 * (lane >> 5);
+    // Part products, smallest first: NPR of them per 32 x 32 accumulator and
+    // k-step, 4 NPR MFMAs per k-step, each followed by SPS of the 48 store
+    // stages of the next chunk (8 pieces of 6).
+    constexpr int NPR = NP == 3 ? 6 : 3, SPS = 48 / (8 * NPR);
+    constexpr int PA[6] = {NP == 3 ? 2 : 1, NP == 3 ? 1 : 0, 0, 1, 0, 0};
+    constexpr int PB[6] = {0, 1, NP == 3 ? 2 : 0, 0, 1, 0};
+    static_assert(BK == 32, "two 16-deep k-steps per chunk");
+    // As (the buffer being multiplied) and nbuf (the idle one) are distinct,
+    // which the restrict qualifiers state: the stores into nbuf need not wait
+    // for the fragment reads from As.
+    auto body = [&](const uint16_t* __restrict__ As, uint16_t* __restrict__ nbuf, int64_t c, f32x4 (&ra)[4],
+                    f32x4 (&rb)[4]) {
+      const uint16_t* Bs = As + NP * X6_PART;
+      const int kn = (int)((c + 1) * BK);
+      bf16x8 a[2][NP][2], b[2][NP][2];   // [k-step][part][32-row block]
+      auto read = [&](int h, int f) {   // fragment f (0..4 NP - 1) of k-step h
+        const int pt = f >> 2, t = (f >> 1) & 1, ks = 16 * h;
+        if (f & 1) b[h][pt][t] = *(const bf16x8*)(Bs + pt * X6_PART + x6_boff(brow + 32 * t, ks + koff));
+        else a[h][pt][t] = *(const bf16x8*)(As + pt * X6_PART + (arow + 32 * t) * X6_LD + ks + koff);
+      };
+  #pragma unroll
+      for (int f = 0; f < 4 * NP; ++f) read(0, f);
+      // Per k-step: 24 products (the four accumulators take turns, so that no
+      // MFMA waits for the one before it).  Behind each product comes one stage
+      // of the next chunk's store (6 stages for each of its 8 pieces, a few
+      // vector instructions each, which run while the MFMA does); the first
+      // k-step also reads the second one's fragments, and each load of chunk
+      // c+3 follows the stage that last reads the registers it fills (A's row
+      // chunk q: piece q's first stage; B's rows: piece 7's, or with TB B's row
+      // chunk q: piece 4 + q's).
+      f32x4 sv;
+      uint32_t sh0, sh1, sm0_, sm1_;
+      float sr[4];
+  #pragma unroll
+      for (int h = 0; h < 2; ++h)
+  #pragma unroll
+        for (int m = 0; m < 4 * NPR; ++m) {
+          if (NP == 2 && h == 1 && m == 0) {
+  #pragma unroll
+            for (int f = 0; f < 4 * NP; ++f) read(1, f);
+          }
+          const int pp = m >> 2, i = (m >> 1) & 1, j = m & 1;
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[h][PA[pp]][i], b[h][PB[pp]][j], acc[i][j], 0, 0, 0);
+          if (NP == 3 && h == 0 && m < 4 * NP) read(1, m);
+  #pragma unroll
+          for (int u = 0; u < SPS; ++u) {
+            const int g = SPS * (4 * NPR * h + m) + u;
+            store_stage(nbuf, kn, ra, rb, g / 6, g % 6, sv, sh0, sh1, sm0_, sm1_, sr);
+            if (g % 6 == 1 && g < 24) load_a((c + 3) * BK, ra, g / 6);
+            if (TB && g % 6 == 1 && g >= 24) load_b((c + 3) * BK, rb, g / 6 - 4);
+            if (!TB && g >= 43 && g < 47) load_b((c + 3) * BK, rb, g - 43);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    auto step = [&](int64_t c, f32x4 (&ra)[4], f32x4 (&rb)[4]) {
+      const int cur = (int)((c - c0) & 1);
+      body(smem + cur * X6_BUF, smem + (cur ^ 1) * X6_BUF, c, ra, rb);
+      lds_barrier();
+    };
+    for (int64_t c = c0; c < nk; c += 2) {
+      step(c, ra0, rb0);
+      if (c + 1 < nk) step(c + 1, ra1, rb1);
+    }
   }
 
   if (EPI == kEpiAxpby) {
@@ -735,7 +772,8 @@ hipError_t launch(const GemmArgs& a, hipStream_t s) {
     if (!TB || a.kmode == kGemmKFull) {
       dim3 grid((unsigned)((a.N + X6_T - 1) / X6_T), (unsigned)((a.M + X6_T - 1) / X6_T),
                 (unsigned)(a.batch * (a.ksplit == 2 ? 2 : 1)));
-      hipLaunchKernelGGL((gemm_x6_kernel<EPI, TB, LOWER, EPI == kEpiRowDot ? 2 : 3>), grid, dim3(256), 0, s, a);
+      hipLaunchKernelGGL((gemm_x6_kernel<EPI, TB, LOWER, EPI == kEpiRowDot ? 2 : 3, EPI != kEpiRowDot>), grid,
+                         dim3(256), 0, s, a);
       return hipGetLastError();
     }
   }
