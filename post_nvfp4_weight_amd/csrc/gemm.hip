@@ -772,8 +772,22 @@ hipError_t launch(const GemmArgs& a, hipStream_t s) {
     if (!TB || a.kmode == kGemmKFull) {
       dim3 grid((unsigned)((a.N + X6_T - 1) / X6_T), (unsigned)((a.M + X6_T - 1) / X6_T),
                 (unsigned)(a.batch * (a.ksplit == 2 ? 2 : 1)));
-      hipLaunchKernelGGL((gemm_x6_kernel<EPI, TB, LOWER, EPI == kEpiRowDot ? 2 : 3, EPI != kEpiRowDot>), grid,
-                         dim3(256), 0, s, a);
+      // Three parts: the one-buffer kernel (two workgroups per CU) once there
+      // are more live tiles than CUs; below that it has no partner on the CU
+      // and the double-buffered kernel is faster.  Both give the same bits.
+      const int64_t mt = (a.M + X6_T - 1) / X6_T, nt = (a.N + X6_T - 1) / X6_T;
+      int64_t live = mt * nt;
+      if (LOWER) {   // tiles wholly above the diagonal exit
+        live = 0;
+        for (int64_t t = 0; t < mt; ++t) live += std::min<int64_t>(nt, t + 1);
+      }
+      live *= a.batch * (a.ksplit == 2 ? 2 : 1);
+      if (EPI == kEpiRowDot)
+        hipLaunchKernelGGL((gemm_x6_kernel<EPI, TB, LOWER, 2, false>), grid, dim3(256), 0, s, a);
+      else if (live > gemm_num_cus())
+        hipLaunchKernelGGL((gemm_x6_kernel<EPI, TB, LOWER, 3, true>), grid, dim3(256), 0, s, a);
+      else
+        hipLaunchKernelGGL((gemm_x6_kernel<EPI, TB, LOWER, 3, false>), grid, dim3(256), 0, s, a);
       return hipGetLastError();
     }
   }
